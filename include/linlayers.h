@@ -1,0 +1,177 @@
+/*
+ * linlayers.h -- C ABI of the MI355X (gfx950) GEMM and RecSys linear-compression
+ * library (liblinlayers.so).
+ *
+ * Operations (definitions from the pages this library follows):
+ *
+ *  - gemm_*   : C = A.B with bf16 A and B, fp32 accumulation, fp32 or bf16 C.
+ *               The problem is stated as on the page "Triton 3.7 permite
+ *               extender el compilador de GPU sin forks" (listings in the
+ *               sections "NVIDIA H100 (Hopper): GEMM persistente" and
+ *               "AMD MI350: GEMM segmentado"): pointers a/b/c, sizes M, N, K and
+ *               the element strides stride_am, stride_ak, stride_bk, stride_bn,
+ *               stride_cm, stride_cn.  The tile sizes and stage count those
+ *               listings take as compile-time constants are chosen inside the
+ *               plan here.
+ *  - lincomp_*: the RecSys linear-compression layer named on the page "Meta
+ *               accelere un noyau GPU d'un facteur 4 avec TLX" (section on what
+ *               a four-fold speed-up means).  For request r and candidate c the
+ *               layer input X is the request's user rows stacked above the
+ *               candidate's item rows, and Y[r][c] = W^T . X.  The user rows are
+ *               identical across a request's candidates (section on how data
+ *               loading holds back compute), so this entry point takes them
+ *               once per request and computes their contribution once per
+ *               request, not once per candidate.
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Pointers named A, B, C, user, item, W, Y and workspace are DEVICE
+ *    pointers on the device the plan (or call) runs on; descriptors and plans
+ *    are host memory.  The caller owns every buffer, including the workspace;
+ *    the library never allocates device memory.  It owns only host plan
+ *    objects (released by gemm_plan_destroy).
+ *  - bf16 values are passed as their 16-bit patterns.  All strides are in
+ *    ELEMENTS, not bytes.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Run calls only
+ *    enqueue work and return; results are ready when the stream is.  Errors
+ *    raised by the device (faults) surface at the caller's next
+ *    synchronisation, not as a return value.
+ *  - No exceptions cross this ABI.  Every call returns an ll_status.
+ *  - Plans are immutable and may be shared between host threads; concurrent
+ *    runs need distinct workspaces.
+ */
+#ifndef LINLAYERS_H
+#define LINLAYERS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LL_OK = 0,
+  LL_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad stride, overlap, wrong device */
+  LL_ERR_UNSUPPORTED = 2,  /* dtype, layout or device (not gfx950) this library does not handle */
+  LL_ERR_WORKSPACE = 3,    /* workspace smaller than the queried size */
+  LL_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+  LL_ERR_NO_DEVICE = 5     /* no HIP device is visible */
+} ll_status;
+
+typedef enum { LL_BF16 = 0, LL_F32 = 1 } ll_dtype;
+
+/* gemm_desc.flags */
+#define LL_FLAG_PACK_A 0x1u /* always copy A into an aligned workspace layout first */
+#define LL_FLAG_PACK_B 0x2u /* same for B */
+#define LL_FLAG_PRODUCER_CONSUMER 0x4u /* force the wave-specialised (producer/consumer) kernel */
+#define LL_FLAG_COOPERATIVE 0x8u       /* force the kernel in which every wave loads and computes */
+
+/*
+ * GEMM problem.  A[i][k] = A[i*stride_am + k*stride_ak] (0 <= i < M, 0 <= k < K),
+ * B[k][j] = B[k*stride_bk + j*stride_bn], C[i][j] = C[i*stride_cm + j*stride_cn].
+ * a_type and b_type must be LL_BF16; c_type is LL_BF16 or LL_F32.
+ * For A and for B, one of the two strides must be 1 (row- or column-major, any
+ * leading dimension); C may use any positive strides.  bf16 C is rounded to
+ * nearest even.
+ */
+typedef struct {
+  int64_t M, N, K;
+  int64_t stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn;
+  int32_t a_type, b_type, c_type; /* ll_dtype values */
+  uint32_t flags;                 /* LL_FLAG_* ; unknown bits -> LL_ERR_INVALID_ARG */
+} gemm_desc;
+
+typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
+
+/*
+ * Validate `desc` and choose the kernel configuration (tile shape, stage
+ * count, wave roles, split-K factor, grid) for the CURRENT HIP device.
+ * On success *out receives a new plan.
+ * Errors: LL_ERR_INVALID_ARG (null out/desc, negative size, zero or negative
+ * stride, unknown flag bits), LL_ERR_UNSUPPORTED (dtype, neither stride of A
+ * or of B equal to 1, device not gfx950), LL_ERR_NO_DEVICE, LL_ERR_HIP.
+ * Argument checks run before any device query.
+ */
+ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* desc);
+
+/* Bytes of device workspace gemm_run needs for this plan (may be 0). */
+ll_status gemm_plan_workspace_size(const gemm_plan* plan, size_t* bytes);
+
+/*
+ * Writes a one-line, NUL-terminated description of the plan's choices
+ * (kernel, tile, stages, roles, split-K, grid) into buf[0..len).
+ */
+ll_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
+
+/*
+ * C = A.B on `stream`.  A, B: bf16 device buffers; C: device buffer of
+ * c_type.  Unless the plan packs an operand (LL_FLAG_PACK_*, or a layout that
+ * needs it: leading dimension not a multiple of 8, K-contiguous operand with
+ * K not a multiple of 8, M- or N-contiguous operand whose M or N is not a
+ * multiple of 8), that operand's pointer must be 16-byte aligned.
+ * M == 0 or N == 0: nothing is written.  K == 0: C is set to zero.
+ * Errors: LL_ERR_INVALID_ARG (null plan/pointer with a non-empty problem,
+ * misaligned operand, C overlapping A or B, current device differs from the
+ * plan's), LL_ERR_WORKSPACE (ws_bytes below gemm_plan_workspace_size or a
+ * null workspace with a non-zero requirement), LL_ERR_HIP (launch failure).
+ */
+ll_status gemm_run(const gemm_plan* plan, const void* A, const void* B, void* C,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+ll_status gemm_plan_destroy(gemm_plan* plan);
+
+/*
+ * Linear compression.  Sizes: R requests, C candidates per request, Nu user
+ * rows, Ni item rows, D columns (embedding width), Mo compressed rows.
+ *   user[r][n][d] = user[r*su_r + n*su_n + d]            (0 <= n < Nu), bf16
+ *   item[r][c][n][d] = item[r*si_r + c*si_c + n*si_n + d] (0 <= n < Ni), bf16
+ *   W[n][m] = W[n*sw_n + m]                               (0 <= n < Nu+Ni), bf16
+ *   Y[r][c][m][d] = Y[r*sy_r + c*sy_c + m*sy_m + d], y_type LL_BF16 or LL_F32
+ * Y[r][c][m][d] = sum_{n<Nu} W[n][m] user[r][n][d] + sum_{n<Ni} W[Nu+n][m] item[r][c][n][d],
+ * accumulated in fp32; the first sum is computed once per request and kept
+ * in fp32 (never rounded to bf16) until the final result is rounded.
+ * The last dimension of every tensor is contiguous; user, item and W must be
+ * 16-byte aligned and su_n, si_n, sw_n multiples of 8; D and Mo multiples
+ * of 8.
+ * flags: 0 = user block once per request (default); LL_LINCOMP_NO_DEDUP =
+ * treat the user rows as if they were repeated for every candidate (each
+ * candidate recomputes the user contribution; the result is the same sum).
+ */
+#define LL_LINCOMP_NO_DEDUP 0x1u
+
+typedef struct {
+  int64_t R, C, Nu, Ni, D, Mo;
+  int64_t su_r, su_n;
+  int64_t si_r, si_c, si_n;
+  int64_t sw_n;
+  int64_t sy_r, sy_c, sy_m;
+  int32_t y_type; /* ll_dtype */
+  uint32_t flags;
+} lincomp_desc;
+
+/* Bytes of device workspace lincomp_run needs for `desc` (may be 0).
+ * Errors as for the argument checks of lincomp_run; no device is queried. */
+ll_status lincomp_workspace_size(const lincomp_desc* desc, size_t* bytes);
+
+/*
+ * Y = linear compression of (user, item) by W, on `stream` (current device,
+ * must be gfx950).  R == 0 or C == 0: nothing is written.
+ * Errors: LL_ERR_INVALID_ARG (null desc/pointer, negative size, stride or
+ * alignment rule above broken, Y overlapping an input), LL_ERR_UNSUPPORTED
+ * (y_type, device), LL_ERR_WORKSPACE, LL_ERR_NO_DEVICE, LL_ERR_HIP.
+ */
+ll_status lincomp_run(const lincomp_desc* desc, const void* user, const void* item,
+                      const void* W, void* Y, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* Static, human-readable name of a status code ("LL_OK", ...). */
+const char* ll_status_string(ll_status s);
+
+/* Message of the most recent failing call on this host thread ("" if none). */
+const char* ll_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LINLAYERS_H */

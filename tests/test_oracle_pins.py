@@ -1,0 +1,294 @@
+"""Pins of the fp64 oracle against things other than itself: exact rational
+arithmetic on tiny inputs, numpy's float64 matmul, closed forms, integer
+exactness, layout identities and the invariance of the user-once rewrite.
+All CPU-only."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import acceptance
+
+U53 = 2.0 ** -53
+
+
+def _mixed_bf16(rng, n):
+    """bf16 patterns with random sign, exponent in [-12, 12] and mantissa."""
+    m = rng.random(n, dtype=np.float32) + np.float32(1.0)
+    e = rng.integers(-12, 13, n).astype(np.float32)
+    s = np.where(rng.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+    return synth.f32_to_bf16_rne(s * m * np.exp2(e))
+
+
+def _frac(bits):
+    return [Fraction(float(v)) for v in synth.bf16_to_f32(bits)]
+
+
+def _layout(rng, rows, cols, which):
+    """Returns (buffer_size, row_stride, col_stride) for a rows x cols operand."""
+    if which == "row":
+        ld = cols + int(rng.integers(0, 3))
+        return rows * ld, ld, 1
+    ld = rows + int(rng.integers(0, 3))
+    return cols * ld, 1, ld
+
+
+def test_bruteforce_exact_rationals_all_shapes_1_to_8():
+    rng = np.random.default_rng(1234)
+    for M in range(1, 9):
+        for N in range(1, 9):
+            for K in range(1, 9):
+                la, lb = rng.choice(["row", "col"]), rng.choice(["row", "col"])
+                na, sam, sak = _layout(rng, M, K, la)
+                nb, sbk, sbn = _layout(rng, K, N, lb)
+                A = _mixed_bf16(rng, na)
+                B = _mixed_bf16(rng, nb)
+                C, S = oracle.gemm(M, N, K, A, sam, sak, B, sbk, sbn)
+                fa, fb = _frac(A), _frac(B)
+                for i in range(M):
+                    for j in range(N):
+                        terms = [fa[i * sam + k * sak] * fb[k * sbk + j * sbn] for k in range(K)]
+                        exact = sum(terms, Fraction(0))
+                        sabs = sum((abs(t) for t in terms), Fraction(0))
+                        tol = K * U53 * float(sabs) * 1.0001
+                        assert abs(Fraction(C[i, j]) - exact) <= Fraction(tol), (M, N, K, i, j)
+                        assert abs(Fraction(S[i, j]) - sabs) <= Fraction(tol), (M, N, K, i, j)
+
+
+def test_matches_numpy_float64_matmul():
+    rng = np.random.default_rng(7)
+    for (M, N, K) in [(33, 17, 129), (64, 64, 64), (5, 300, 77)]:
+        c = synth.gemm_case(M, N, K, seed=int(rng.integers(1 << 30)), dist=("normal", 0, 1.0))
+        C, S = oracle.gemm_case(c)
+        A = synth.bf16_to_f32(c.A).astype(np.float64).reshape(M, K)
+        B = synth.bf16_to_f32(c.B).astype(np.float64).reshape(K, N)
+        ref = A @ B
+        Sref = np.abs(A) @ np.abs(B)
+        assert np.all(np.abs(C - ref) <= 2 * K * U53 * Sref + 1e-300)
+        assert np.allclose(S, Sref, rtol=4 * K * U53, atol=0)
+
+
+def test_identity_and_permutation_exact():
+    rng = np.random.default_rng(3)
+    n = 40
+    X = _mixed_bf16(rng, n * n)
+    I = synth.f32_to_bf16_rne(np.eye(n, dtype=np.float32)).reshape(-1)
+    Xf = synth.bf16_to_f32(X).astype(np.float64).reshape(n, n)
+    C, _ = oracle.gemm(n, n, n, X, n, 1, I, n, 1)
+    assert np.array_equal(C, Xf)
+    C, _ = oracle.gemm(n, n, n, I, n, 1, X, n, 1)
+    assert np.array_equal(C, Xf)
+    perm = rng.permutation(n)
+    P = np.zeros((n, n), dtype=np.float32)
+    P[np.arange(n), perm] = 1.0
+    C, _ = oracle.gemm(n, n, n, synth.f32_to_bf16_rne(P).reshape(-1), n, 1, X, n, 1)
+    assert np.array_equal(C, Xf[perm])
+    # A.I with I column-major and A column-major
+    C, _ = oracle.gemm(n, n, n, X, 1, n, I, 1, n)
+    assert np.array_equal(C, Xf.T)
+
+
+def test_rank1_closed_forms():
+    rng = np.random.default_rng(5)
+    M, N, K = 12, 9, 64
+    u = _mixed_bf16(rng, M)
+    v = _mixed_bf16(rng, N)
+    one = synth.f32_to_bf16_rne(np.ones(1, dtype=np.float32))[0]
+    A = np.repeat(u, K)                      # A[i][k] = u[i]
+    B = np.tile(v, K)                        # B[k][j] = v[j]
+    C, _ = oracle.gemm(M, N, K, A, K, 1, B, N, 1)
+    uf = synth.bf16_to_f32(u).astype(np.float64)
+    vf = synth.bf16_to_f32(v).astype(np.float64)
+    assert np.array_equal(C, K * np.outer(uf, vf))
+    # A = u a^T, B = b v^T  ->  C = (a.b) u v^T
+    a = _mixed_bf16(rng, K)
+    b = _mixed_bf16(rng, K)
+    ua = synth.f32_to_bf16_rne((np.outer(uf, synth.bf16_to_f32(a))).astype(np.float32))
+    # choose u = 1 so that u a^T stays exactly representable
+    A = np.tile(a, M)                        # A[i][k] = a[k]
+    B = np.repeat(b, N)                      # B[k][j] = b[k]
+    C, S = oracle.gemm(M, N, K, A, K, 1, B, N, 1)
+    fa, fb = _frac(a), _frac(b)
+    dot = sum((x * y for x, y in zip(fa, fb)), Fraction(0))
+    sabs = sum((abs(x * y) for x, y in zip(fa, fb)), Fraction(0))
+    assert np.all(np.abs(C - float(dot)) <= K * U53 * float(sabs))
+    assert one == 0x3F80 and ua.size == M * K
+
+
+def test_integer_valued_inputs_are_exact():
+    for (M, N, K) in [(16, 16, 16), (31, 45, 257), (8, 8, 4096)]:
+        c = synth.gemm_case(M, N, K, dist=("int", -4, 4), seed=M * N + K)
+        C, _ = oracle.gemm_case(c)
+        A = synth.bf16_to_f32(c.A).astype(np.int64).reshape(M, K)
+        B = synth.bf16_to_f32(c.B).astype(np.int64).reshape(K, N)
+        assert np.array_equal(C, (A @ B).astype(np.float64))
+
+
+def test_column_major_b_equals_row_major_copy():
+    M, N, K = 23, 31, 70
+    c = synth.gemm_case(M, N, K, seed=9, b_col_major=True, lda=K + 3, ldb=K + 5)
+    C1, S1 = oracle.gemm_case(c)
+    Bt = c.B.reshape(N, K + 5)[:, :K]          # [N][K]
+    Brow = np.ascontiguousarray(Bt.T).reshape(-1)  # [K][N]
+    C2, S2 = oracle.gemm(M, N, K, c.A, K + 3, 1, Brow, N, 1)
+    assert np.array_equal(C1, C2) and np.array_equal(S1, S2)
+
+
+def test_entries_and_row_strips_agree_with_full():
+    c = synth.gemm_case(50, 60, 300, seed=4, dist=("normal", 0, 1.0))
+    C, S = oracle.gemm_case(c)
+    Cs, Ss = oracle.gemm_case(c, rows=(17, 9))
+    assert np.array_equal(Cs, C[17:26]) and np.array_equal(Ss, S[17:26])
+    rng = np.random.default_rng(0)
+    r = rng.integers(0, 50, 200)
+    col = rng.integers(0, 60, 200)
+    e, es = oracle.gemm_case_entries(c, r, col)
+    assert np.array_equal(e, C[r, col]) and np.array_equal(es, S[r, col])
+
+
+def _lc_dense(R, C, Nu, Ni, D, Mo, rng, dist):
+    if dist == "int":
+        mk = lambda n: synth.f32_to_bf16_rne(rng.integers(-3, 4, n).astype(np.float32))
+    else:
+        mk = lambda n: _mixed_bf16(rng, n)
+    return mk(R * Nu * D), mk(R * C * Ni * D), mk((Nu + Ni) * Mo)
+
+
+def _lc_strides(R, C, Nu, Ni, D, Mo):
+    return dict(su_r=Nu * D, su_n=D, si_r=C * Ni * D, si_c=Ni * D, si_n=D, sw_n=Mo)
+
+
+def test_lincomp_naive_matches_numpy_on_stacked_input():
+    rng = np.random.default_rng(11)
+    R, C, Nu, Ni, D, Mo = 3, 4, 5, 7, 6, 3
+    user, item, W = _lc_dense(R, C, Nu, Ni, D, Mo, rng, "mixed")
+    st = _lc_strides(R, C, Nu, Ni, D, Mo)
+    pairs = [(r, c) for r in range(R) for c in range(C)]
+    Y, S = oracle.lincomp_naive((R, C, Nu, Ni, D, Mo), user, item, W, st, pairs)
+    u = synth.bf16_to_f32(user).astype(np.float64).reshape(R, Nu, D)
+    it = synth.bf16_to_f32(item).astype(np.float64).reshape(R, C, Ni, D)
+    w = synth.bf16_to_f32(W).astype(np.float64).reshape(Nu + Ni, Mo)
+    for p, (r, c) in enumerate(pairs):
+        X = np.concatenate([u[r], it[r, c]], axis=0)
+        ref = w.T @ X
+        Sref = np.abs(w.T) @ np.abs(X)
+        assert np.all(np.abs(Y[p] - ref) <= 2 * (Nu + Ni) * U53 * Sref)
+        assert np.allclose(S[p], Sref, rtol=4 * (Nu + Ni) * U53, atol=0)
+    # exact rationals for one candidate
+    fu, fi, fw = _frac(user), _frac(item), _frac(W)
+    r, c = 2, 1
+    for m in range(Mo):
+        for d in range(D):
+            terms = [fw[n * Mo + m] * fu[r * Nu * D + n * D + d] for n in range(Nu)]
+            terms += [fw[(Nu + n) * Mo + m] * fi[r * C * Ni * D + c * Ni * D + n * D + d]
+                      for n in range(Ni)]
+            ex = sum(terms, Fraction(0))
+            sa = sum((abs(t) for t in terms), Fraction(0))
+            p = pairs.index((r, c))
+            assert abs(Fraction(Y[p, m, d]) - ex) <= Fraction((Nu + Ni) * U53 * float(sa))
+
+
+def test_lincomp_dedup_invariance():
+    rng = np.random.default_rng(12)
+    R, C, Nu, Ni, D, Mo = 2, 3, 16, 24, 8, 5
+    st = _lc_strides(R, C, Nu, Ni, D, Mo)
+    pairs = [(r, c) for r in range(R) for c in range(C)]
+    user, item, W = _lc_dense(R, C, Nu, Ni, D, Mo, rng, "mixed")
+    Yn, S = oracle.lincomp_naive((R, C, Nu, Ni, D, Mo), user, item, W, st, pairs)
+    Yd = oracle.lincomp_dedup((R, C, Nu, Ni, D, Mo), user, item, W, st, pairs)
+    assert np.all(np.abs(Yn - Yd) <= 2 * (Nu + Ni) * U53 * S)
+    user, item, W = _lc_dense(R, C, Nu, Ni, D, Mo, rng, "int")
+    Yn = oracle.lincomp_naive((R, C, Nu, Ni, D, Mo), user, item, W, st, pairs, bound=False)
+    Yd = oracle.lincomp_dedup((R, C, Nu, Ni, D, Mo), user, item, W, st, pairs)
+    assert np.array_equal(Yn, Yd)
+
+
+def test_lincomp_selector_special_cases():
+    rng = np.random.default_rng(13)
+    R, C, Nu, Ni, D, Mo = 2, 3, 6, 4, 5, 4
+    st = _lc_strides(R, C, Nu, Ni, D, Mo)
+    pairs = [(r, c) for r in range(R) for c in range(C)]
+    user, item, _ = _lc_dense(R, C, Nu, Ni, D, Mo, rng, "mixed")
+    uf = synth.bf16_to_f32(user).astype(np.float64).reshape(R, Nu, D)
+    itf = synth.bf16_to_f32(item).astype(np.float64).reshape(R, C, Ni, D)
+    # W = [E; 0] with E selecting user rows sel_u[m]
+    sel_u = [5, 0, 3, 3]
+    Wf = np.zeros((Nu + Ni, Mo), dtype=np.float32)
+    for m, n in enumerate(sel_u):
+        Wf[n, m] = 1.0
+    Y = oracle.lincomp_naive((R, C, Nu, Ni, D, Mo), user, item, synth.f32_to_bf16_rne(Wf), st,
+                             pairs, bound=False)
+    for p, (r, c) in enumerate(pairs):
+        assert np.array_equal(Y[p], uf[r][sel_u])
+    # W = [0; E] selecting item rows
+    sel_i = [1, 3, 0, 2]
+    Wf[:] = 0
+    for m, n in enumerate(sel_i):
+        Wf[Nu + n, m] = 1.0
+    Y = oracle.lincomp_naive((R, C, Nu, Ni, D, Mo), user, item, synth.f32_to_bf16_rne(Wf), st,
+                             pairs, bound=False)
+    for p, (r, c) in enumerate(pairs):
+        assert np.array_equal(Y[p], itf[r, c][sel_i])
+    # zero user block: the user rows contribute exactly nothing
+    _, _, W = _lc_dense(R, C, Nu, Ni, D, Mo, rng, "mixed")
+    zu = np.zeros_like(user)
+    Y = oracle.lincomp_naive((R, C, Nu, Ni, D, Mo), zu, item, W, st, pairs, bound=False)
+    Wi = W.reshape(Nu + Ni, Mo)[Nu:].reshape(-1)
+    for p, (r, c) in enumerate(pairs):
+        it = item.reshape(R, C, Ni * D)[r, c]
+        ref, _ = oracle.gemm(Mo, D, Ni, Wi, 1, Mo, it, D, 1)   # A = Wi^T (column-major view)
+        assert np.array_equal(Y[p], ref)
+
+
+def test_acceptance_rne_passes_truncation_fails():
+    # values needing rounding to 8 significant bits; K = 1 so S = |ref|
+    x = np.array([1 + 2 ** -7 - 2 ** -20, -(3 + 0.9 * 2 ** -6), 1000.9, 2 ** -10 * 1.99],
+                 dtype=np.float32)
+    ref = x.astype(np.float64)
+    S = np.abs(ref)
+    rne = synth.bf16_to_f32(synth.f32_to_bf16_rne(x)).astype(np.float64)
+    trunc = synth.bf16_to_f32((x.view(np.uint32) >> 16).astype(np.uint16)).astype(np.float64)
+    assert acceptance.check(rne, ref, S, "bf16")[0]
+    assert not acceptance.check(trunc, ref, S, "bf16")[0]
+    # fp32 bound
+    z = np.zeros_like(ref)
+    assert acceptance.check(z + 0.9e-6, z, z, "f32")[0]
+    assert not acceptance.check(z + 2e-6, z, z, "f32")[0]
+    assert acceptance.check(ref + 0.9e-3 * S, ref, S, "f32")[0]
+    assert not acceptance.check(ref + 1.1e-3 * S + 1e-6, ref, S, "f32")[0]
+    bad = ref.copy()
+    bad[1] = np.nan
+    assert not acceptance.check(bad, ref, S, "f32")[0]
+
+
+def test_synth_rne_and_determinism():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -7 - 2 ** -20, -2.0, 0.0],
+                 dtype=np.float32)
+    assert list(synth.f32_to_bf16_rne(x)) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC000, 0]
+    a = synth.bf16_tensor(3 * synth.CHUNK + 17, "normal", 0, 1.0, seed=42, tensor=3)
+    b = synth.bf16_tensor(3 * synth.CHUNK + 17, "normal", 0, 1.0, seed=42, tensor=3)
+    assert np.array_equal(a, b)
+    c = synth.bf16_tensor(synth.CHUNK + 5, "normal", 0, 1.0, seed=42, tensor=3)
+    assert np.array_equal(c, a[: synth.CHUNK + 5])
+    d = synth.bf16_tensor(100, "int", -4, 4, seed=1)
+    f = synth.bf16_to_f32(d)
+    assert f.min() >= -4 and f.max() <= 4 and np.all(f == np.round(f))
+
+
+def test_golden_fixture():
+    """tests/golden/gemm_int_7x5x9.txt: written by tests/golden/make_golden.py from
+    the oracle; integer inputs, so the closed form (int64 matmul) must agree too."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "gemm_int_7x5x9.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    M, N, K = (int(v) for v in rows[0])
+    A = np.array([int(v) for v in rows[1]], dtype=np.int64).reshape(M, K)
+    B = np.array([int(v) for v in rows[2]], dtype=np.int64).reshape(K, N)
+    C = np.array([float(v) for v in rows[3]]).reshape(M, N)
+    assert np.array_equal(A @ B, C.astype(np.int64))
+    Ab = synth.f32_to_bf16_rne(A.astype(np.float32)).reshape(-1)
+    Bb = synth.f32_to_bf16_rne(B.astype(np.float32)).reshape(-1)
+    Co, _ = oracle.gemm(M, N, K, Ab, K, 1, Bb, N, 1)
+    assert np.array_equal(Co, C)
