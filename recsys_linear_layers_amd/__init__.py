@@ -1,0 +1,245 @@
+"""bf16 GEMM and RecSys linear-compression layer for MI355X (gfx950).
+
+Thin Python binding over liblinlayers.so, whose C ABI is declared in
+include/linlayers.h.  The functions named like the C entry points
+(gemm_plan_create, gemm_run, lincomp_run, ...) only marshal arguments; every
+step of the computation runs in the library's HIP kernels.  ``gemm`` and
+``lincomp`` are torch conveniences over them (torch supplies device memory and
+the current stream).
+
+Importing this module fails if the library has not been built
+(``python recsys_linear_layers_amd/build.py``); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinlayers.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python {os.path.join(_HERE, 'build.py')}` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+LL_OK, LL_ERR_INVALID_ARG, LL_ERR_UNSUPPORTED, LL_ERR_WORKSPACE, LL_ERR_HIP, LL_ERR_NO_DEVICE = range(6)
+LL_BF16, LL_F32 = 0, 1
+LL_FLAG_PACK_A = 0x1
+LL_FLAG_PACK_B = 0x2
+LL_FLAG_PRODUCER_CONSUMER = 0x4
+LL_FLAG_COOPERATIVE = 0x8
+LL_LINCOMP_NO_DEDUP = 0x1
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class GemmDesc(ctypes.Structure):
+    _fields_ = [("M", _i64), ("N", _i64), ("K", _i64),
+                ("stride_am", _i64), ("stride_ak", _i64), ("stride_bk", _i64), ("stride_bn", _i64),
+                ("stride_cm", _i64), ("stride_cn", _i64),
+                ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32), ("c_type", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class LincompDesc(ctypes.Structure):
+    _fields_ = [("R", _i64), ("C", _i64), ("Nu", _i64), ("Ni", _i64), ("D", _i64), ("Mo", _i64),
+                ("su_r", _i64), ("su_n", _i64),
+                ("si_r", _i64), ("si_c", _i64), ("si_n", _i64),
+                ("sw_n", _i64),
+                ("sy_r", _i64), ("sy_c", _i64), ("sy_m", _i64),
+                ("y_type", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_lib.ll_status_string.restype = ctypes.c_char_p
+_lib.ll_status_string.argtypes = [ctypes.c_int]
+_lib.ll_last_error.restype = ctypes.c_char_p
+_lib.ll_last_error.argtypes = []
+_lib.gemm_plan_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(GemmDesc)]
+_lib.gemm_plan_workspace_size.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
+_lib.gemm_plan_describe.argtypes = [_vp, ctypes.c_char_p, ctypes.c_size_t]
+_lib.gemm_run.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.gemm_plan_destroy.argtypes = [_vp]
+_lib.lincomp_workspace_size.argtypes = [ctypes.POINTER(LincompDesc), ctypes.POINTER(ctypes.c_size_t)]
+_lib.lincomp_run.argtypes = [ctypes.POINTER(LincompDesc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+for _f in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run",
+           "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class LLError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {ll_status_string(status)}: {ll_last_error()}")
+
+
+def ll_status_string(status: int) -> str:
+    return _lib.ll_status_string(int(status)).decode()
+
+
+def ll_last_error() -> str:
+    return _lib.ll_last_error().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != LL_OK:
+        raise LLError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# C-ABI mirrors (pointers are ints; stream is a hipStream_t value or 0)
+# ---------------------------------------------------------------------------
+
+def gemm_plan_create(desc: GemmDesc) -> int:
+    h = _vp()
+    _check(_lib.gemm_plan_create(ctypes.byref(h), ctypes.byref(desc)), "gemm_plan_create")
+    return h.value
+
+
+def gemm_plan_workspace_size(plan: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.gemm_plan_workspace_size(plan, ctypes.byref(n)), "gemm_plan_workspace_size")
+    return n.value
+
+
+def gemm_plan_describe(plan: int) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(_lib.gemm_plan_describe(plan, buf, 512), "gemm_plan_describe")
+    return buf.value.decode()
+
+
+def gemm_run(plan: int, A: int, B: int, C: int, workspace: int, ws_bytes: int, stream: int) -> None:
+    _check(_lib.gemm_run(plan, A, B, C, workspace, ws_bytes, stream), "gemm_run")
+
+
+def gemm_plan_destroy(plan: int) -> None:
+    _check(_lib.gemm_plan_destroy(plan), "gemm_plan_destroy")
+
+
+def lincomp_workspace_size(desc: LincompDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.lincomp_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "lincomp_workspace_size")
+    return n.value
+
+
+def lincomp_run(desc: LincompDesc, user: int, item: int, W: int, Y: int, workspace: int, ws_bytes: int,
+                stream: int) -> None:
+    _check(_lib.lincomp_run(ctypes.byref(desc), user, item, W, Y, workspace, ws_bytes, stream), "lincomp_run")
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences: build descriptors from tensor shapes/strides, keep plans
+# and workspaces, launch on torch's current stream.
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return LL_BF16
+    if dt == torch.float32:
+        return LL_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+class GemmPlan:
+    """Owns one gemm_plan and a workspace tensor on the plan's device."""
+
+    def __init__(self, desc: GemmDesc, device):
+        self.desc = desc
+        self.handle = gemm_plan_create(desc)
+        self.ws_bytes = gemm_plan_workspace_size(self.handle)
+        torch = _torch()
+        self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+
+    def describe(self) -> str:
+        return gemm_plan_describe(self.handle)
+
+    def run(self, A, B, C, stream: int | None = None) -> None:
+        if stream is None:
+            stream = _torch().cuda.current_stream(A.device).cuda_stream
+        gemm_run(self.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), self.workspace.data_ptr(),
+                 self.ws_bytes, stream)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.gemm_plan_destroy(h)
+            self.handle = None
+
+
+_plans: dict = {}
+
+
+def gemm_desc_for(A, B, C, flags: int = 0) -> GemmDesc:
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    sa, sb, sc = A.stride(), B.stride(), C.stride()
+    return GemmDesc(M, N, K, sa[0], sa[1], sb[0], sb[1], sc[0], sc[1],
+                    _dtype_code(A.dtype), _dtype_code(B.dtype), _dtype_code(C.dtype), flags)
+
+
+def plan_for(A, B, C, flags: int = 0) -> GemmPlan:
+    desc = gemm_desc_for(A, B, C, flags)
+    key = (A.device.index, tuple(getattr(desc, f) for f, _ in GemmDesc._fields_))
+    plan = _plans.get(key)
+    if plan is None:
+        plan = GemmPlan(desc, A.device)
+        _plans[key] = plan
+    return plan
+
+
+def gemm(A, B, out=None, out_dtype=None, flags: int = 0):
+    """C = A @ B for 2-D bf16 CUDA (HIP) tensors with any row/column-major strides."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((A.shape[0], B.shape[1]), dtype=out_dtype or torch.bfloat16, device=A.device)
+    plan_for(A, B, out, flags).run(A, B, out)
+    return out
+
+
+def lincomp_desc_for(user, item, W, Y, flags: int = 0) -> LincompDesc:
+    R, Nu, D = user.shape
+    R2, C, Ni, D2 = item.shape
+    Nin, Mo = W.shape
+    if R2 != R or D2 != D or Nin != Nu + Ni or tuple(Y.shape) != (R, C, Mo, D):
+        raise ValueError("lincomp shape mismatch")
+    for t in (user, item, W, Y):
+        if t.stride(-1) != 1:
+            raise ValueError("last dimension must be contiguous")
+    su, si, sw, sy = user.stride(), item.stride(), W.stride(), Y.stride()
+    return LincompDesc(R, C, Nu, Ni, D, Mo, su[0], su[1], si[0], si[1], si[2], sw[0],
+                       sy[0], sy[1], sy[2], _dtype_code(Y.dtype), flags)
+
+
+_lc_ws: dict = {}
+
+
+def lincomp(user, item, W, out=None, out_dtype=None, flags: int = 0):
+    """Y[r, c] = W^T . [user[r]; item[r, c]] for bf16 tensors user [R][Nu][D],
+    item [R][C][Ni][D], W [Nu+Ni][Mo]; returns Y [R][C][Mo][D]."""
+    torch = _torch()
+    R, Nu, D = user.shape
+    C = item.shape[1]
+    Mo = W.shape[1]
+    if out is None:
+        out = torch.empty((R, C, Mo, D), dtype=out_dtype or torch.bfloat16, device=user.device)
+    desc = lincomp_desc_for(user, item, W, out, flags)
+    need = lincomp_workspace_size(desc)
+    key = user.device.index
+    ws = _lc_ws.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=user.device)
+        _lc_ws[key] = ws
+    stream = torch.cuda.current_stream(user.device).cuda_stream
+    lincomp_run(desc, user.data_ptr(), item.data_ptr(), W.data_ptr(), out.data_ptr(), ws.data_ptr(),
+                ws.numel(), stream)
+    return out

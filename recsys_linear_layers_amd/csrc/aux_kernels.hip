@@ -1,0 +1,120 @@
+// Auxiliary kernels: operand packing, split-K reduction, zero fill, and the
+// launch table over the per-layout instantiation units.
+#include "kernels.hpp"
+
+namespace ll {
+
+hipError_t launch_gemm_kk(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_kn(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_mk(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_mn(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+
+hipError_t launch_gemm(int layout, int kind, const GemmKArgs& args, int grid, hipStream_t stream) {
+  switch (layout) {
+    case 0: return launch_gemm_kk(kind, args, grid, stream);
+    case 1: return launch_gemm_kn(kind, args, grid, stream);
+    case 2: return launch_gemm_mk(kind, args, grid, stream);
+    case 3: return launch_gemm_mn(kind, args, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+const KindInfo& kind_info(int kind) {
+  static const KindInfo table[KIND_COUNT] = {
+      {256, 128, 512, 3 * (256 + 128) * kBK * 2, 3, 4, "wide_pc_256x128x64_s3_4c4p"},
+      {256, 128, 256, 3 * (256 + 128) * kBK * 2, 3, 0, "wide_coop_256x128x64_s3_4w"},
+      {128, 256, 512, 3 * (128 + 256) * kBK * 2, 3, 4, "tall_pc_128x256x64_s3_4c4p"},
+      {128, 128, 256, 3 * (128 + 128) * kBK * 2, 3, 0, "small_coop_128x128x64_s3_4w"},
+      {64, 256, 512, 3 * (64 + 256) * kBK * 2, 3, 4, "lincomp_pc_64x256x64_s3_4c4p"},
+  };
+  return table[kind];
+}
+
+// dst[r][k] = src[r*s_r + k*s_k] for k < K, 0 for K <= k < ldp.  One thread per
+// 8-element (16-byte) chunk of dst.
+__global__ void __launch_bounds__(256) pack_kmajor_kernel(const uint16_t* __restrict__ src, int64_t s_r,
+                                                          int64_t s_k, int64_t rows, int64_t K,
+                                                          uint16_t* __restrict__ dst, int64_t ldp) {
+  const int64_t chunks_per_row = ldp / 8;
+  const int64_t total = rows * chunks_per_row;
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = c / chunks_per_row;
+    const int64_t k0 = (c - r * chunks_per_row) * 8;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < K) ? src[r * s_r + (k0 + e) * s_k] : (uint16_t)0;
+    uint4 o;
+    o.x = v[0] | ((uint32_t)v[1] << 16);
+    o.y = v[2] | ((uint32_t)v[3] << 16);
+    o.z = v[4] | ((uint32_t)v[5] << 16);
+    o.w = v[6] | ((uint32_t)v[7] << 16);
+    *(uint4*)(dst + r * ldp + k0) = o;
+  }
+}
+
+hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
+                              uint16_t* dst, int64_t ldp, hipStream_t stream) {
+  const int64_t total = rows * (ldp / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  const int grid = (int)(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(pack_kmajor_kernel, dim3(grid), dim3(256), 0, stream, src, s_r, s_k, rows, K, dst,
+                     ldp);
+  return hipGetLastError();
+}
+
+// C[i][j] = sum over s = 0..splits-1 (ascending) of partial[s][i][j].
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ P, int splits,
+                                                            int64_t M, int64_t N, void* __restrict__ C,
+                                                            int64_t ldcm, int64_t ldcn, int c_bf16) {
+  const int64_t total = M * N;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    float acc = P[e];
+    for (int s = 1; s < splits; ++s) acc += P[(int64_t)s * total + e];
+    const int64_t i = e / N, j = e - i * N;
+    const int64_t o = i * ldcm + j * ldcn;
+    if (c_bf16)
+      ((uint16_t*)C)[o] = f32_to_bf16_bits(acc);
+    else
+      ((float*)C)[o] = acc;
+  }
+}
+
+hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int64_t N, void* C,
+                                int64_t ldcm, int64_t ldcn, int c_bf16, hipStream_t stream) {
+  const int64_t total = M * N;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  const int grid = (int)(blocks < 16384 ? blocks : 16384);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, partial, splits, M, N, C,
+                     ldcm, ldcn, c_bf16);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(void* __restrict__ C, int64_t M, int64_t N,
+                                                        int64_t ldcm, int64_t ldcn, int c_bf16) {
+  const int64_t total = M * N;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / N, j = e - i * N;
+    const int64_t o = i * ldcm + j * ldcn;
+    if (c_bf16)
+      ((uint16_t*)C)[o] = 0;
+    else
+      ((float*)C)[o] = 0.f;
+  }
+}
+
+hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_bf16,
+                            hipStream_t stream) {
+  const int64_t total = M * N;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  const int grid = (int)(blocks < 16384 ? blocks : 16384);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldcm, ldcn, c_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace ll

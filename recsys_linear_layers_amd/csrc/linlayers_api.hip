@@ -1,0 +1,539 @@
+// C ABI of liblinlayers.so: argument checks, plan selection (tile shape,
+// wave roles, split-K, packing, grid), workspace layout and launches.
+// The declarations and their contracts are in include/linlayers.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/linlayers.h"
+#include "kernels.hpp"
+
+using namespace ll;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ll_status fail(ll_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ll_status fail(ll_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ll_status ok() {
+  g_last_error.clear();
+  return LL_OK;
+}
+
+ll_status hip_fail(hipError_t e, const char* what) {
+  return fail(LL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct DeviceInfo {
+  bool probed = false;
+  bool gfx950 = false;
+  int cus = 0;
+  char arch[64] = {0};
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+// Current device, its CU count, and whether it is gfx950.
+ll_status current_device(int* dev, const DeviceInfo** info) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) return fail(LL_ERR_NO_DEVICE, "no HIP device visible");
+  e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (*dev < 0 || *dev >= 64) return fail(LL_ERR_UNSUPPORTED, "device index %d out of range", *dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[*dev];
+  if (!d.probed) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, *dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    d.cus = prop.multiProcessorCount;
+    snprintf(d.arch, sizeof d.arch, "%s", prop.gcnArchName);
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.probed = true;
+  }
+  *info = &d;
+  if (!d.gfx950) return fail(LL_ERR_UNSUPPORTED, "device %d is %s; this library targets gfx950", *dev, d.arch);
+  return LL_OK;
+}
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Byte extent [lo, hi) touched by a 2-D strided view of `rows` x `cols` elements.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span_of(const void* p, int64_t rows, int64_t cols, int64_t sr, int64_t sc, int64_t esize) {
+  const uintptr_t b = (uintptr_t)p;
+  const int64_t last = (rows - 1) * sr + (cols - 1) * sc;
+  return {b, b + (uintptr_t)((last + 1) * esize)};
+}
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// One operand as the kernel sees it.
+struct OperandPlan {
+  bool kmajor;      // K-contiguous in memory (after packing, always true)
+  bool pack;        // copied into the workspace as K-major [rows][Kp]
+  int64_t ld;       // leading dimension of the direct view
+  int64_t s_r, s_k; // original strides (rows = M or N)
+  size_t ws_off;    // workspace offset of the packed copy
+};
+
+}  // namespace
+
+struct gemm_plan {
+  gemm_desc d;
+  int device;
+  int cus;
+  int kind;
+  int layout;
+  OperandPlan a, b;
+  int64_t Kp;       // K rounded up to a multiple of 8
+  int splits;
+  int kiters, kps;
+  int tiles_m, tiles_n, total, grid, group_m;
+  size_t ws_partial_off;
+  size_t ws_bytes;
+};
+
+namespace {
+
+// Decide how an operand with logical extent rows x K and strides (s_r, s_k) is fed.
+ll_status plan_operand(const char* name, int64_t rows, int64_t K, int64_t s_r, int64_t s_k, bool force_pack,
+                       OperandPlan* op) {
+  op->s_r = s_r;
+  op->s_k = s_k;
+  if (s_k == 1) {
+    op->kmajor = true;
+    op->ld = s_r;
+  } else if (s_r == 1) {
+    op->kmajor = false;
+    op->ld = s_k;
+  } else {
+    return fail(LL_ERR_UNSUPPORTED, "%s: neither stride is 1 (strides %lld, %lld)", name, (long long)s_r,
+                (long long)s_k);
+  }
+  bool direct = !force_pack && op->ld % 8 == 0;
+  if (op->kmajor)
+    direct = direct && K % 8 == 0 && op->ld * 2 * 256 < (1ll << 31);
+  else
+    direct = direct && rows % 8 == 0 && op->ld * 2 * kBK < (1ll << 31);
+  op->pack = !direct;
+  if (op->pack) op->kmajor = true;
+  return LL_OK;
+}
+
+int occupancy_for(int kind) {
+  const KindInfo& k = kind_info(kind);
+  int occ = (160 * 1024) / k.lds;
+  const int waves = k.threads / 64;
+  const int by_waves = 32 / waves;  // 8 waves per SIMD x 4 SIMDs upper bound
+  if (occ > by_waves) occ = by_waves;
+  return occ < 1 ? 1 : occ;
+}
+
+void fill_operand_args(OperandArgs* oa, const void* ptr, const OperandPlan& op, int64_t rows, int64_t K,
+                       int64_t Kp, const void* ws) {
+  if (op.pack) {
+    oa->ptr = (const uint16_t*)((const char*)ws + op.ws_off);
+    oa->ld = Kp;
+    oa->kvalid = (int32_t)Kp;
+    oa->extent = rows * Kp;
+  } else {
+    oa->ptr = (const uint16_t*)ptr;
+    oa->ld = op.ld;
+    oa->kvalid = (int32_t)(op.kmajor ? K : K);
+    oa->extent = op.kmajor ? (rows - 1) * op.ld + K : (K - 1) * op.ld + rows;
+  }
+  oa->rows = (int32_t)rows;
+  oa->bo = 0;
+  oa->bi = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ll_status_string(ll_status s) {
+  switch (s) {
+    case LL_OK: return "LL_OK";
+    case LL_ERR_INVALID_ARG: return "LL_ERR_INVALID_ARG";
+    case LL_ERR_UNSUPPORTED: return "LL_ERR_UNSUPPORTED";
+    case LL_ERR_WORKSPACE: return "LL_ERR_WORKSPACE";
+    case LL_ERR_HIP: return "LL_ERR_HIP";
+    case LL_ERR_NO_DEVICE: return "LL_ERR_NO_DEVICE";
+  }
+  return "LL_ERR_UNKNOWN";
+}
+
+const char* ll_last_error(void) { return g_last_error.c_str(); }
+
+ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
+  if (!out || !d) return fail(LL_ERR_INVALID_ARG, "gemm_plan_create: null argument");
+  *out = nullptr;
+  if (d->M < 0 || d->N < 0 || d->K < 0) return fail(LL_ERR_INVALID_ARG, "negative size");
+  if (d->stride_am < 1 || d->stride_ak < 1 || d->stride_bk < 1 || d->stride_bn < 1 || d->stride_cm < 1 ||
+      d->stride_cn < 1)
+    return fail(LL_ERR_INVALID_ARG, "strides must be >= 1");
+  const uint32_t known = LL_FLAG_PACK_A | LL_FLAG_PACK_B | LL_FLAG_PRODUCER_CONSUMER | LL_FLAG_COOPERATIVE;
+  if (d->flags & ~known) return fail(LL_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~known);
+  if ((d->flags & LL_FLAG_PRODUCER_CONSUMER) && (d->flags & LL_FLAG_COOPERATIVE))
+    return fail(LL_ERR_INVALID_ARG, "LL_FLAG_PRODUCER_CONSUMER and LL_FLAG_COOPERATIVE are exclusive");
+  if (d->a_type != LL_BF16 || d->b_type != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "A and B must be LL_BF16");
+  if (d->c_type != LL_BF16 && d->c_type != LL_F32) return fail(LL_ERR_UNSUPPORTED, "C must be LL_BF16 or LL_F32");
+  if (d->M >= (1ll << 31) || d->N >= (1ll << 31) || d->K >= (1ll << 31))
+    return fail(LL_ERR_UNSUPPORTED, "dimensions must be below 2^31");
+
+  gemm_plan p;
+  memset(&p, 0, sizeof p);
+  p.d = *d;
+  ll_status s = plan_operand("A", d->M, d->K, d->stride_am, d->stride_ak, d->flags & LL_FLAG_PACK_A, &p.a);
+  if (s != LL_OK) return s;
+  s = plan_operand("B", d->N, d->K, d->stride_bn, d->stride_bk, d->flags & LL_FLAG_PACK_B, &p.b);
+  if (s != LL_OK) return s;
+  // Any K-contiguous operand needs K padded to a multiple of 8; packed copies carry zeros there.
+  p.Kp = round_up(d->K, 8);
+  if (p.Kp * 2 * 256 >= (1ll << 31)) return fail(LL_ERR_UNSUPPORTED, "K too large");
+  p.layout = layout_index(p.a.kmajor, p.b.kmajor);
+
+  const DeviceInfo* info = nullptr;
+  s = current_device(&p.device, &info);
+  if (s != LL_OK) return s;
+  p.cus = info->cus;
+
+  // Tile shape: skinny M uses 128-row tiles; tiny problems use 128x128 tiles.
+  const int64_t M = d->M, N = d->N;
+  int kind;
+  if (M <= 128 && N >= 1024)
+    kind = KIND_TALL_PC;
+  else if (M * N <= 1024ll * 1024)
+    kind = KIND_SMALL_COOP;
+  else
+    kind = KIND_WIDE_PC;
+  if (d->flags & LL_FLAG_COOPERATIVE) {
+    if (kind == KIND_WIDE_PC || kind == KIND_TALL_PC) kind = KIND_WIDE_COOP;
+  } else if (d->flags & LL_FLAG_PRODUCER_CONSUMER) {
+    if (kind == KIND_SMALL_COOP || kind == KIND_WIDE_COOP) kind = KIND_WIDE_PC;
+  }
+  p.kind = kind;
+  const KindInfo& ki = kind_info(kind);
+  p.tiles_m = (int)((M + ki.bm - 1) / ki.bm);
+  p.tiles_n = (int)((N + ki.bn - 1) / ki.bn);
+  p.kiters = (int)((p.Kp + kBK - 1) / kBK);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  if (tiles >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "too many tiles");
+  const int occ = occupancy_for(kind);
+  const int64_t slots = (int64_t)p.cus * occ;
+  // Split K when the tiles alone cannot fill the chip and K is long enough to share.
+  int splits = 1;
+  if (tiles > 0 && tiles * 2 <= slots && p.kiters >= 16) {
+    int64_t want = slots / tiles;
+    int64_t by_k = p.kiters / 8;
+    splits = (int)(want < by_k ? want : by_k);
+    if (splits < 1) splits = 1;
+    if (splits > 64) splits = 64;
+  }
+  p.kps = (p.kiters + splits - 1) / splits;
+  splits = p.kiters > 0 ? (p.kiters + p.kps - 1) / p.kps : 1;  // every split gets >= 1 k-step
+  p.splits = splits;
+  p.total = (int)(tiles * splits);
+  p.grid = (int)(p.total < slots ? p.total : slots);
+  if (p.grid < 1) p.grid = 1;
+  p.group_m = 8;
+
+  size_t off = 0;
+  if (p.a.pack) {
+    p.a.ws_off = off;
+    off = align256(off + (size_t)(M * p.Kp * 2));
+  }
+  if (p.b.pack) {
+    p.b.ws_off = off;
+    off = align256(off + (size_t)(N * p.Kp * 2));
+  }
+  p.ws_partial_off = off;
+  if (splits > 1) off = align256(off + (size_t)splits * M * N * 4);
+  p.ws_bytes = off;
+
+  gemm_plan* h = new (std::nothrow) gemm_plan(p);
+  if (!h) return fail(LL_ERR_INVALID_ARG, "out of host memory");
+  *out = h;
+  return ok();
+}
+
+ll_status gemm_plan_workspace_size(const gemm_plan* p, size_t* bytes) {
+  if (!p || !bytes) return fail(LL_ERR_INVALID_ARG, "null argument");
+  *bytes = p->ws_bytes;
+  return ok();
+}
+
+ll_status gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
+  if (!p || !buf || len == 0) return fail(LL_ERR_INVALID_ARG, "null argument");
+  const KindInfo& k = kind_info(p->kind);
+  static const char* lay[4] = {"A:K-major,B:K-major", "A:K-major,B:N-major", "A:M-major,B:K-major",
+                               "A:M-major,B:N-major"};
+  snprintf(buf, len,
+           "kernel=%s layout=%s packA=%d packB=%d tiles=%dx%d splitk=%d kiters=%d grid=%d cus=%d "
+           "group_m=%d ws=%zu",
+           k.name, lay[p->layout], (int)p->a.pack, (int)p->b.pack, p->tiles_m, p->tiles_n, p->splits,
+           p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes);
+  return ok();
+}
+
+ll_status gemm_plan_destroy(gemm_plan* p) {
+  delete p;
+  return ok();
+}
+
+ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (!p) return fail(LL_ERR_INVALID_ARG, "null plan");
+  const gemm_desc& d = p->d;
+  if (d.M == 0 || d.N == 0) return ok();
+  if (!C) return fail(LL_ERR_INVALID_ARG, "null C");
+  if (d.K > 0 && (!A || !B)) return fail(LL_ERR_INVALID_ARG, "null A or B");
+  if (ws_bytes < p->ws_bytes || (p->ws_bytes > 0 && !ws))
+    return fail(LL_ERR_WORKSPACE, "workspace %zu bytes, plan needs %zu", ws_bytes, p->ws_bytes);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device) return fail(LL_ERR_INVALID_ARG, "plan made for device %d, current is %d", p->device, dev);
+  const int64_t csz = d.c_type == LL_BF16 ? 2 : 4;
+  const Span sc = span_of(C, d.M, d.N, d.stride_cm, d.stride_cn, csz);
+  if (d.K > 0) {
+    if (overlaps(sc, span_of(A, d.M, d.K, d.stride_am, d.stride_ak, 2)) ||
+        overlaps(sc, span_of(B, d.K, d.N, d.stride_bk, d.stride_bn, 2)))
+      return fail(LL_ERR_INVALID_ARG, "C overlaps A or B");
+  }
+  if (p->ws_bytes > 0 && overlaps(sc, Span{(uintptr_t)ws, (uintptr_t)ws + p->ws_bytes}))
+    return fail(LL_ERR_INVALID_ARG, "C overlaps the workspace");
+  hipStream_t st = (hipStream_t)stream;
+  const int cbf = d.c_type == LL_BF16;
+  if (d.K == 0) {
+    e = launch_fill_zero(C, d.M, d.N, d.stride_cm, d.stride_cn, cbf, st);
+    return e == hipSuccess ? ok() : hip_fail(e, "fill_zero launch");
+  }
+  if ((!p->a.pack && ((uintptr_t)A & 15)) || (!p->b.pack && ((uintptr_t)B & 15)))
+    return fail(LL_ERR_INVALID_ARG, "A and B must be 16-byte aligned unless packed (LL_FLAG_PACK_A/B)");
+  if (p->a.pack) {
+    e = launch_pack_kmajor((const uint16_t*)A, p->a.s_r, p->a.s_k, d.M, d.K,
+                           (uint16_t*)((char*)ws + p->a.ws_off), p->Kp, st);
+    if (e != hipSuccess) return hip_fail(e, "pack A launch");
+  }
+  if (p->b.pack) {
+    e = launch_pack_kmajor((const uint16_t*)B, p->b.s_r, p->b.s_k, d.N, d.K,
+                           (uint16_t*)((char*)ws + p->b.ws_off), p->Kp, st);
+    if (e != hipSuccess) return hip_fail(e, "pack B launch");
+  }
+  GemmKArgs k;
+  memset(&k, 0, sizeof k);
+  fill_operand_args(&k.a, A, p->a, d.M, d.K, p->Kp, ws);
+  fill_operand_args(&k.b, B, p->b, d.N, d.K, p->Kp, ws);
+  k.M = (int32_t)d.M;
+  k.N = (int32_t)d.N;
+  k.c_bf16 = cbf;
+  k.bdiv = 1;
+  k.batches = 1;
+  k.splits = p->splits;
+  k.kiters = p->kiters;
+  k.kps = p->kps;
+  k.tiles_m = p->tiles_m;
+  k.tiles_n = p->tiles_n;
+  k.group_m = p->group_m;
+  k.total = p->total;
+  if (p->splits > 1) {
+    k.partial = (float*)((char*)ws + p->ws_partial_off);
+  } else {
+    k.c = C;
+    k.ldcm = d.stride_cm;
+    k.ldcn = d.stride_cn;
+  }
+  e = launch_gemm(p->layout, p->kind, k, p->grid, st);
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  if (p->splits > 1) {
+    e = launch_splitk_reduce(k.partial, p->splits, d.M, d.N, C, d.stride_cm, d.stride_cn, cbf, st);
+    if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Linear compression
+// ---------------------------------------------------------------------------
+
+static ll_status lincomp_check(const lincomp_desc* d) {
+  if (!d) return fail(LL_ERR_INVALID_ARG, "null desc");
+  if (d->R < 0 || d->C < 0 || d->Nu < 0 || d->Ni < 0 || d->D < 0 || d->Mo < 0)
+    return fail(LL_ERR_INVALID_ARG, "negative size");
+  if (d->flags & ~(uint32_t)LL_LINCOMP_NO_DEDUP) return fail(LL_ERR_INVALID_ARG, "unknown flag bits");
+  if (d->y_type != LL_BF16 && d->y_type != LL_F32) return fail(LL_ERR_UNSUPPORTED, "Y must be LL_BF16 or LL_F32");
+  if (d->D % 8 || d->Mo % 8) return fail(LL_ERR_INVALID_ARG, "D and Mo must be multiples of 8");
+  if (d->su_n % 8 || d->si_n % 8 || d->sw_n % 8 || d->su_r % 8 || d->si_r % 8 || d->si_c % 8)
+    return fail(LL_ERR_INVALID_ARG, "su_r, su_n, si_r, si_c, si_n, sw_n must be multiples of 8");
+  if (d->su_n < d->D || d->si_n < d->D || d->sw_n < d->Mo || d->sy_m < d->D)
+    return fail(LL_ERR_INVALID_ARG, "row strides shorter than the rows");
+  if (d->su_r < 0 || d->si_r < 0 || d->si_c < 0 || d->sy_r < 0 || d->sy_c < 0)
+    return fail(LL_ERR_INVALID_ARG, "negative stride");
+  if (d->Mo > 256 || d->D >= (1 << 30) || d->R * d->C >= (1ll << 30))
+    return fail(LL_ERR_UNSUPPORTED, "Mo must be <= 256 and R*C below 2^30");
+  if (d->su_n * 2 * kBK >= (1ll << 31) || d->si_n * 2 * kBK >= (1ll << 31) || d->sw_n * 2 * kBK >= (1ll << 31))
+    return fail(LL_ERR_UNSUPPORTED, "row strides too large");
+  return LL_OK;
+}
+
+ll_status lincomp_workspace_size(const lincomp_desc* d, size_t* bytes) {
+  ll_status s = lincomp_check(d);
+  if (s != LL_OK) return s;
+  if (!bytes) return fail(LL_ERR_INVALID_ARG, "null bytes");
+  // fp32 user contribution, one [Mo][D] block per request (or per candidate without dedup).
+  const int64_t blocks = (d->flags & LL_LINCOMP_NO_DEDUP) ? d->R * d->C : d->R;
+  *bytes = (d->Nu > 0) ? align256((size_t)blocks * d->Mo * d->D * 4) : 0;
+  return ok();
+}
+
+ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item, const void* W, void* Y,
+                      void* ws, size_t ws_bytes, void* stream) {
+  ll_status s = lincomp_check(d);
+  if (s != LL_OK) return s;
+  if (d->R == 0 || d->C == 0 || d->Mo == 0 || d->D == 0) return ok();
+  if (!Y || !W || (d->Nu > 0 && !user) || (d->Ni > 0 && !item)) return fail(LL_ERR_INVALID_ARG, "null pointer");
+  if (((uintptr_t)user & 15) || ((uintptr_t)item & 15) || ((uintptr_t)W & 15))
+    return fail(LL_ERR_INVALID_ARG, "user, item and W must be 16-byte aligned");
+  size_t need = 0;
+  lincomp_workspace_size(d, &need);
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(LL_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  const DeviceInfo* info = nullptr;
+  int dev = 0;
+  s = current_device(&dev, &info);
+  if (s != LL_OK) return s;
+  const int64_t ysz = d->y_type == LL_BF16 ? 2 : 4;
+  const Span sy = {(uintptr_t)Y, (uintptr_t)Y + (uintptr_t)(((d->R - 1) * d->sy_r + (d->C - 1) * d->sy_c +
+                                                              (d->Mo - 1) * d->sy_m + d->D) * ysz)};
+  if (overlaps(sy, Span{(uintptr_t)W, (uintptr_t)W + (uintptr_t)((d->Nu + d->Ni - 1) * d->sw_n + d->Mo) * 2}) ||
+      (d->Nu > 0 && overlaps(sy, Span{(uintptr_t)user, (uintptr_t)user + (uintptr_t)(((d->R - 1) * d->su_r +
+                                                                                      (d->Nu - 1) * d->su_n + d->D) * 2)})) ||
+      (d->Ni > 0 && overlaps(sy, Span{(uintptr_t)item, (uintptr_t)item + (uintptr_t)(((d->R - 1) * d->si_r +
+                                                                                      (d->C - 1) * d->si_c +
+                                                                                      (d->Ni - 1) * d->si_n + d->D) * 2)})) ||
+      (need > 0 && overlaps(sy, Span{(uintptr_t)ws, (uintptr_t)ws + need})))
+    return fail(LL_ERR_INVALID_ARG, "Y overlaps an input or the workspace");
+
+  hipStream_t st = (hipStream_t)stream;
+  const bool dedup = !(d->flags & LL_LINCOMP_NO_DEDUP);
+  const int kind = KIND_LINCOMP_PC;
+  const KindInfo& ki = kind_info(kind);
+  const int tiles_m = (int)((d->Mo + ki.bm - 1) / ki.bm);
+  const int tiles_n = (int)((d->D + ki.bn - 1) / ki.bn);
+  const int64_t slots = (int64_t)info->cus * occupancy_for(kind);
+  float* U = (float*)ws;
+  hipError_t e;
+
+  // Phase 1: the user rows' contribution U = W[0:Nu]^T . user, once per request
+  // (or, without dedup, once per candidate, as if the rows were repeated).
+  if (d->Nu > 0) {
+    GemmKArgs k;
+    memset(&k, 0, sizeof k);
+    k.a.ptr = (const uint16_t*)W;  // A[m][n] = W[n][m]: M-contiguous
+    k.a.ld = d->sw_n;
+    k.a.rows = (int32_t)d->Mo;
+    k.a.kvalid = (int32_t)d->Nu;
+    k.a.extent = (d->Nu - 1) * d->sw_n + d->Mo;
+    k.b.ptr = (const uint16_t*)user;  // B[n][dd] = user[r][n][dd]: N-contiguous
+    k.b.ld = d->su_n;
+    k.b.rows = (int32_t)d->D;
+    k.b.kvalid = (int32_t)d->Nu;
+    k.b.bo = d->su_r;
+    k.b.bi = 0;
+    k.b.extent = (d->R - 1) * d->su_r + (d->Nu - 1) * d->su_n + d->D;
+    k.c = U;
+    k.ldcm = d->D;
+    k.ldcn = 1;
+    k.cbo = dedup ? d->Mo * d->D : d->C * d->Mo * d->D;
+    k.cbi = dedup ? 0 : d->Mo * d->D;
+    k.M = (int32_t)d->Mo;
+    k.N = (int32_t)d->D;
+    k.bdiv = dedup ? 1 : (int32_t)d->C;
+    k.batches = (int32_t)(dedup ? d->R : d->R * d->C);
+    k.splits = 1;
+    k.kiters = (int32_t)((d->Nu + kBK - 1) / kBK);
+    k.kps = k.kiters;
+    k.tiles_m = tiles_m;
+    k.tiles_n = tiles_n;
+    k.group_m = 1;
+    k.total = k.batches * tiles_m * tiles_n;
+    const int grid = (int)(k.total < slots ? k.total : slots);
+    e = launch_gemm(layout_index(false, false), kind, k, grid, st);
+    if (e != hipSuccess) return hip_fail(e, "lincomp user-phase launch");
+  }
+
+  // Phase 2: Y[r][c] = U + W[Nu:]^T . item[r][c]; U enters as the epilogue's fp32 bias.
+  GemmKArgs k;
+  memset(&k, 0, sizeof k);
+  k.a.ptr = (const uint16_t*)W + d->Nu * d->sw_n;
+  k.a.ld = d->sw_n;
+  k.a.rows = (int32_t)d->Mo;
+  k.a.kvalid = (int32_t)d->Ni;
+  k.a.extent = d->Ni > 0 ? (d->Ni - 1) * d->sw_n + d->Mo : 0;
+  k.b.ptr = (const uint16_t*)item;
+  k.b.ld = d->si_n;
+  k.b.rows = (int32_t)d->D;
+  k.b.kvalid = (int32_t)d->Ni;
+  k.b.bo = d->si_r;
+  k.b.bi = d->si_c;
+  k.b.extent = d->Ni > 0 ? (d->R - 1) * d->si_r + (d->C - 1) * d->si_c + (d->Ni - 1) * d->si_n + d->D : 0;
+  k.c = Y;
+  k.ldcm = d->sy_m;
+  k.ldcn = 1;
+  k.cbo = d->sy_r;
+  k.cbi = d->sy_c;
+  k.c_bf16 = d->y_type == LL_BF16;
+  if (d->Nu > 0) {
+    k.bias = U;
+    k.bias_m = d->D;
+    k.bias_n = 1;
+    k.bias_bo = dedup ? d->Mo * d->D : d->C * d->Mo * d->D;
+    k.bias_bi = dedup ? 0 : d->Mo * d->D;
+  }
+  k.M = (int32_t)d->Mo;
+  k.N = (int32_t)d->D;
+  k.bdiv = (int32_t)d->C;
+  k.batches = (int32_t)(d->R * d->C);
+  k.splits = 1;
+  k.kiters = (int32_t)((d->Ni + kBK - 1) / kBK);
+  k.kps = k.kiters;
+  k.tiles_m = tiles_m;
+  k.tiles_n = tiles_n;
+  k.group_m = 1;
+  k.total = k.batches * tiles_m * tiles_n;
+  if (k.kiters == 0) {
+    // No item rows: Y = U (rounded).  A zero-iteration tile still runs its epilogue.
+    k.kiters = 1;
+    k.kps = 1;
+    k.a.kvalid = 0;
+    k.b.kvalid = 0;
+    k.a.ptr = (const uint16_t*)W;
+    k.b.ptr = (const uint16_t*)W;
+    k.a.extent = 0;
+    k.b.extent = 0;
+  }
+  const int grid = (int)(k.total < slots ? k.total : slots);
+  e = launch_gemm(layout_index(false, false), kind, k, grid, st);
+  if (e != hipSuccess) return hip_fail(e, "lincomp candidate-phase launch");
+  return ok();
+}
+
+}  // extern "C"

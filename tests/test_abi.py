@@ -1,0 +1,123 @@
+"""The C ABI library loads, exports every entry point its header declares, and
+rejects bad arguments on the host (no GPU needed for these checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linlayers.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:ll_status|const char\s*\*)\s*(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for n in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run",
+              "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "ll_status_string",
+              "ll_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import recsys_linear_layers_amd as ll
+    lib = ctypes.CDLL(ll.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    import recsys_linear_layers_amd as ll
+    assert ll.ll_status_string(ll.LL_OK) == "LL_OK"
+    assert ll.ll_status_string(ll.LL_ERR_WORKSPACE) == "LL_ERR_WORKSPACE"
+    assert ll.ll_status_string(ll.LL_ERR_NO_DEVICE) == "LL_ERR_NO_DEVICE"
+    assert ll.ll_status_string(99) == "LL_ERR_UNKNOWN"
+
+
+def _desc(**kw):
+    import recsys_linear_layers_amd as ll
+    base = dict(M=64, N=64, K=64, stride_am=64, stride_ak=1, stride_bk=64, stride_bn=1, stride_cm=64,
+                stride_cn=1, a_type=ll.LL_BF16, b_type=ll.LL_BF16, c_type=ll.LL_F32, flags=0)
+    base.update(kw)
+    return ll.GemmDesc(**base)
+
+
+def _create_status(desc):
+    import recsys_linear_layers_amd as ll
+    h = ctypes.c_void_p()
+    st = ll._lib.gemm_plan_create(ctypes.byref(h), ctypes.byref(desc))
+    if h.value:
+        ll._lib.gemm_plan_destroy(h)
+    return st
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(M=-1), "LL_ERR_INVALID_ARG"),
+    (dict(K=-5), "LL_ERR_INVALID_ARG"),
+    (dict(stride_am=0), "LL_ERR_INVALID_ARG"),
+    (dict(stride_cn=-1), "LL_ERR_INVALID_ARG"),
+    (dict(flags=0x100), "LL_ERR_INVALID_ARG"),
+    (dict(flags=0x4 | 0x8), "LL_ERR_INVALID_ARG"),
+    (dict(a_type=1), "LL_ERR_UNSUPPORTED"),
+    (dict(c_type=7), "LL_ERR_UNSUPPORTED"),
+    (dict(stride_am=64, stride_ak=2), "LL_ERR_UNSUPPORTED"),
+    (dict(stride_bk=3, stride_bn=5), "LL_ERR_UNSUPPORTED"),
+    (dict(M=1 << 31), "LL_ERR_UNSUPPORTED"),
+])
+def test_plan_argument_checks(kw, expect):
+    import recsys_linear_layers_amd as ll
+    assert ll.ll_status_string(_create_status(_desc(**kw))) == expect
+
+
+def test_plan_null_arguments():
+    import recsys_linear_layers_amd as ll
+    assert ll._lib.gemm_plan_create(None, None) == ll.LL_ERR_INVALID_ARG
+    assert "null" in ll.ll_last_error()
+    h = ctypes.c_void_p()
+    assert ll._lib.gemm_plan_create(ctypes.byref(h), None) == ll.LL_ERR_INVALID_ARG
+    assert ll._lib.gemm_run(None, None, None, None, None, 0, None) == ll.LL_ERR_INVALID_ARG
+    assert ll._lib.gemm_plan_workspace_size(None, None) == ll.LL_ERR_INVALID_ARG
+
+
+def test_valid_plan_needs_a_device():
+    import recsys_linear_layers_amd as ll
+    st = _create_status(_desc())
+    if _has_gpu():
+        assert st == ll.LL_OK
+    else:
+        assert st == ll.LL_ERR_NO_DEVICE
+
+
+def _lc(**kw):
+    import recsys_linear_layers_amd as ll
+    R, C, Nu, Ni, D, Mo = 2, 3, 256, 256, 256, 64
+    base = dict(R=R, C=C, Nu=Nu, Ni=Ni, D=D, Mo=Mo, su_r=Nu * D, su_n=D, si_r=C * Ni * D, si_c=Ni * D,
+                si_n=D, sw_n=Mo, sy_r=C * Mo * D, sy_c=Mo * D, sy_m=D, y_type=ll.LL_BF16, flags=0)
+    base.update(kw)
+    return ll.LincompDesc(**base)
+
+
+def test_lincomp_workspace_and_checks():
+    import recsys_linear_layers_amd as ll
+    assert ll.lincomp_workspace_size(_lc()) == 2 * 64 * 256 * 4
+    assert ll.lincomp_workspace_size(_lc(flags=ll.LL_LINCOMP_NO_DEDUP)) == 2 * 3 * 64 * 256 * 4
+    assert ll.lincomp_workspace_size(_lc(Nu=0)) == 0
+    n = ctypes.c_size_t()
+    for kw in (dict(R=-1), dict(D=12), dict(su_n=12), dict(flags=8), dict(y_type=5), dict(si_c=4),
+               dict(sw_n=8)):
+        st = ll._lib.lincomp_workspace_size(ctypes.byref(_lc(**kw)), ctypes.byref(n))
+        assert st != ll.LL_OK, kw
+    st = ll._lib.lincomp_run(None, None, None, None, None, None, 0, None)
+    assert st == ll.LL_ERR_INVALID_ARG

@@ -1,0 +1,184 @@
+"""GEMM parity on the GPU: the HIP path (through the C ABI) against the fp64
+oracle, element by element within the acceptance bound, and bit-exact where
+integer-valued inputs make every fp32 partial sum exact."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import gemm_operands, sample_indices, to_f64
+from oracle import acceptance
+
+pytestmark = pytest.mark.gpu
+
+
+def _ll():
+    import recsys_linear_layers_amd as ll
+    return ll
+
+
+def _run(case, flags=0, c_layout="row", out=None):
+    import torch
+    ll = _ll()
+    A, B = gemm_operands(case)
+    dt = torch.float32 if case.out_dtype == "f32" else torch.bfloat16
+    if out is None:
+        if c_layout == "row":
+            C = torch.full((case.M, case.N), float("nan"), dtype=dt, device="cuda")
+        else:
+            C = torch.full((case.N, case.M), float("nan"), dtype=dt, device="cuda").t()
+    else:
+        C = out
+    ll.gemm(A, B, out=C, flags=flags)
+    torch.cuda.synchronize()
+    return C
+
+
+def _full_check(case, flags=0, c_layout="row"):
+    C = _run(case, flags, c_layout)
+    ref, S = oracle.gemm_case(case)
+    acceptance.assert_close(to_f64(C), ref, S, case.out_dtype,
+                            f"{case.name} M={case.M} N={case.N} K={case.K} flags={flags}")
+    return C, ref
+
+
+def test_gemm_256_fp32_out_full():
+    case = synth.gemm_workload("gemm_256")
+    _full_check(case)
+
+
+SHAPES = [(1, 1, 1), (7, 9, 13), (33, 65, 129), (128, 128, 64), (200, 136, 72), (257, 263, 300),
+          (64, 520, 8), (300, 8, 1000), (130, 1030, 520)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("la,lb", [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")])
+def test_small_shapes_every_layout(M, N, K, la, lb):
+    seed = M * 1000003 + N * 1009 + K
+    c = synth.gemm_case(M, N, K, seed=seed, b_col_major=(lb == "col"), out_dtype="f32")
+    if la == "col":  # re-describe A column-major: buffer is [K][M]
+        c.A = synth.bf16_tensor(M * K, "uniform", -1.0, 1.0, seed=seed, tensor=5)
+        c.sam, c.sak = 1, M
+    _full_check(c)
+    c.out_dtype = "bf16"
+    _full_check(c)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (257, 263, 300), (520, 264, 1992)])
+def test_integer_inputs_bit_exact(M, N, K):
+    c = synth.gemm_case(M, N, K, dist=("int", -4, 4), seed=M + N + K)
+    C = _run(c)
+    ref, _ = oracle.gemm_case(c)
+    assert np.array_equal(to_f64(C), ref)
+
+
+def test_bf16_epilogue_rounds_to_nearest_even():
+    # Integer-valued results up to ~2^12 are exact in fp32 and mostly need rounding to 8 bits.
+    c = synth.gemm_case(256, 256, 256, dist=("int", -4, 4), seed=99, out_dtype="bf16")
+    C = _run(c)
+    ref, _ = oracle.gemm_case(c)
+    want = synth.f32_to_bf16_rne(ref.astype(np.float32))
+    import torch
+    got = C.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_k_zero_and_empty():
+    import torch
+    ll = _ll()
+    A = torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((0, 7), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((5, 7), 3.0, dtype=torch.float32, device="cuda")
+    ll.gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 0)
+    A = torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((16, 7), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((0, 7), dtype=torch.float32, device="cuda")
+    ll.gemm(A, B, out=C)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("flags", [0, 0x1, 0x2, 0x3, 0x4, 0x8])
+def test_modes_agree(flags):
+    c = synth.gemm_case(520, 1032, 264, dist=("int", -4, 4), seed=5)
+    C = _run(c, flags=flags)
+    ref, _ = oracle.gemm_case(c)
+    assert np.array_equal(to_f64(C), ref)
+    c2 = synth.gemm_case(333, 555, 777, seed=6, dist=("normal", 0, 1.0), out_dtype="bf16")
+    _full_check(c2, flags=flags)
+
+
+def test_column_major_c():
+    c = synth.gemm_case(200, 300, 136, seed=8)
+    _full_check(c, c_layout="col")
+
+
+def test_misaligned_operand_is_rejected_without_pack():
+    import torch
+    ll = _ll()
+    base = torch.zeros(64 * 64 + 1, dtype=torch.bfloat16, device="cuda")
+    A = base[1:].view(64, 64)
+    B = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(ll.LLError) as e:
+        ll.gemm(A, B, out=C)
+    assert e.value.status == ll.LL_ERR_INVALID_ARG
+    ll.gemm(A, B, out=C, flags=ll.LL_FLAG_PACK_A)
+    torch.cuda.synchronize()
+
+
+def _sampled_check(case, n=4096, strip_rows=8, seed=1, flags=0):
+    C = _run(case, flags=flags)
+    got = to_f64(C)
+    rows, cols = sample_indices(case.M, case.N, n, seed)
+    ref, S = oracle.gemm_case_entries(case, rows, cols)
+    acceptance.assert_close(got[rows, cols], ref, S, case.out_dtype, f"{case.name} samples")
+    for r0 in (0, case.M - strip_rows):
+        ref, S = oracle.gemm_case(case, rows=(r0, strip_rows))
+        acceptance.assert_close(got[r0:r0 + strip_rows], ref, S, case.out_dtype, f"{case.name} strip {r0}")
+    return got
+
+
+def test_gemm_4096_bf16_out():
+    _sampled_check(synth.gemm_workload("gemm_4096"), strip_rows=16)
+
+
+@pytest.mark.parametrize("name", ["ffn_up", "ffn_down"])
+def test_ffn_shapes(name):
+    _sampled_check(synth.gemm_workload(name), n=2048, strip_rows=2)
+
+
+def test_edge_shape_column_major_b():
+    _sampled_check(synth.gemm_workload("edge"), strip_rows=4)
+
+
+def test_edge_shape_integer_exact_samples():
+    M, N, K, kw = synth.GEMM_WORKLOADS["edge"]
+    kw = dict(kw, dist=("int", -4, 4))
+    c = synth.gemm_case(M, N, K, name="edge_int", **kw)
+    got = to_f64(_run(c))
+    rows, cols = sample_indices(M, N, 4096, 3)
+    ref, _ = oracle.gemm_case_entries(c, rows, cols)
+    assert np.array_equal(got[rows, cols], ref)
+
+
+def test_skinny_split_k():
+    import torch
+    ll = _ll()
+    c = synth.gemm_workload("skinny_splitk")
+    A, B = gemm_operands(c)
+    assert "splitk=1 " not in ll.plan_for(A, B, torch.empty((c.M, c.N), device="cuda")).describe()
+    got = _sampled_check(c, strip_rows=2)
+    again = to_f64(_run(c))
+    assert np.array_equal(got, again), "split-K result must be run-to-run deterministic"
+
+
+def test_skinny_split_k_integer_exact():
+    M, N, K, kw = synth.GEMM_WORKLOADS["skinny_splitk"]
+    kw = dict(kw, dist=("int", -1, 1))
+    c = synth.gemm_case(M, N, K, name="skinny_int", **kw)
+    got = to_f64(_run(c))
+    rows, cols = sample_indices(M, N, 2048, 4)
+    ref, _ = oracle.gemm_case_entries(c, rows, cols)
+    assert np.array_equal(got[rows, cols], ref)
