@@ -1,0 +1,243 @@
+"""Benchmark: bf16 GEMM TFLOP/s (fraction of dense MFMA peak) and
+linear-compression requests/s (fraction of HBM bandwidth) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one call of the library on the headline workload (default: the
+4096^3 GEMM with bf16 output).  Inputs are seeded synthetic bf16 (the
+``synth`` module), resident in HBM before timing starts.  W untimed warm-up
+steps, then K timed steps between two device synchronisations; the kernel's
+average duration comes from HIP events recorded around every launch on the
+stream the library launches on.  Prints ONE JSON line.  The other
+configurations are reported in the same line under "also".
+
+CPU baseline: the fp64 oracle, timed on a bounded sample of the headline
+workload (rows of C) on this host's cores; it is a reported baseline, not the
+target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256"}
+LINCOMP_NAMES = {"lincomp_256x128"}
+
+
+def _kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recsys_linear_layers_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profiles(workload: str):
+    """HBM bytes per launch recorded by the rocprofv3 counter runs in profiles/,
+    or None if there is no record or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != _kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def _log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _time_launches(fn, steps: int, warmup: int, stream):
+    """Returns (wall ms per step, average event-measured ms per launch)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    return wall, ev
+
+
+def bench_gemm(name: str, steps: int, warmup: int):
+    import torch
+    import recsys_linear_layers_amd as ll
+    import synth
+    from synth.device import gemm_operands
+    _log(f"{name}: generating inputs")
+    case = synth.gemm_workload(name)
+    A, B = gemm_operands(case)
+    _log(f"{name}: timing")
+    dt = torch.bfloat16 if case.out_dtype == "bf16" else torch.float32
+    C = torch.empty((case.M, case.N), dtype=dt, device="cuda")
+    plan = ll.plan_for(A, B, C)
+    stream = torch.cuda.current_stream()
+    wall, ev = _time_launches(lambda: plan.run(A, B, C, stream.cuda_stream), steps, warmup, stream)
+    tflops = case.flops / (ev * 1e-3) / 1e12
+    return dict(case=case, wall_ms=wall, kernel_ms=ev, tflops=tflops, plan=plan.describe())
+
+
+def bench_lincomp(name: str, steps: int, warmup: int):
+    import torch
+    import recsys_linear_layers_amd as ll
+    import synth
+    from synth.device import lincomp_operands
+    _log(f"{name}: generating inputs")
+    c = synth.lincomp_workload(name)
+    user, item, W = lincomp_operands(c)
+    _log(f"{name}: timing")
+    Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    wall, ev = _time_launches(lambda: ll.lincomp(user, item, W, out=Y), steps, warmup, stream)
+    gbs = c.algorithmic_bytes / (ev * 1e-3) / 1e9
+    return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3), gbs=gbs,
+                tflops=c.flops / (ev * 1e-3) / 1e12)
+
+
+def cpu_baseline_gemm(name: str, target_s: float = 12.0):
+    """The oracle on the first rows of C, sized to about target_s of CPU time."""
+    import oracle
+    import synth
+    case = synth.gemm_workload(name)
+    rows, dt = 1, 0.0
+    while rows < case.M:
+        t0 = time.perf_counter()
+        oracle.gemm_case(case, rows=(0, rows), bound=False)
+        dt = time.perf_counter() - t0
+        if dt > 0.5:
+            break
+        rows *= 2
+    rows = int(max(1, min(case.M, rows * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm_case(case, rows=(0, rows), bound=False)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * case.N * case.K
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=oracle.get_threads(), kind="oracle",
+                sample=f"fp64 oracle, rows 0..{rows - 1} of C ({rows}x{case.N}x{case.K}), {dt:.1f} s")
+
+
+def cpu_baseline_lincomp(name: str, target_s: float = 12.0):
+    import oracle
+    import synth
+    c = synth.lincomp_workload(name)
+    n, dt = 1, 0.0
+    while n < c.R * c.C:
+        t0 = time.perf_counter()
+        oracle.lincomp_case(c, [(i // c.C, i % c.C) for i in range(n)], bound=False)
+        dt = time.perf_counter() - t0
+        if dt > 0.5:
+            break
+        n *= 2
+    n = int(max(1, min(c.R * c.C, n * target_s / max(dt, 1e-6))))
+    pairs = [(i // c.C, i % c.C) for i in range(n)]
+    t0 = time.perf_counter()
+    oracle.lincomp_case(c, pairs, bound=False)
+    dt = time.perf_counter() - t0
+    # requests/s at this candidate rate
+    return dict(value=(n / c.C) / dt, unit="requests/s", cores=oracle.get_threads(), kind="oracle",
+                sample=f"fp64 per-candidate oracle, first {n} candidates, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gemm_4096",
+                    choices=sorted(GEMM_NAMES | LINCOMP_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true", help="time only the headline workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    head = args.workload
+    if head in LINCOMP_NAMES:
+        r = bench_lincomp(head, args.steps, args.warmup)
+        c = r["case"]
+        metric, unit, value = "linear-compression requests/s", "requests/s", r["req_s"]
+        roof = dict(bound="hbm", achieved=r["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=r["gbs"] / PEAK_HBM_GBS, traffic=_traffic_from_profiles(head))
+        config = dict(workload=head, requests=c.R, candidates_per_request=c.C, user_rows=c.Nu,
+                      item_rows=c.Ni, dim=c.D, out_rows=c.Mo, y_dtype="bf16",
+                      algorithmic_bytes=c.algorithmic_bytes)
+        plan = "two launches: user block per request, then per-candidate GEMM with fp32 bias"
+    else:
+        r = bench_gemm(head, args.steps, args.warmup)
+        c = r["case"]
+        metric, unit, value = "bf16 GEMM TFLOP/s", "TFLOP/s", r["tflops"]
+        roof = dict(bound="mfma", achieved=r["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=r["tflops"] / PEAK_BF16_TFLOPS, traffic=_traffic_from_profiles(head))
+        config = dict(workload=head, M=c.M, N=c.N, K=c.K, a_layout="row-major",
+                      b_layout="column-major" if c.sbk == 1 else "row-major",
+                      c_dtype=c.out_dtype, flops=c.flops)
+        plan = r["plan"]
+
+    also = []
+    if not args.no_also:
+        for name in ["ffn_up", "ffn_down", "lincomp_256x128", "edge", "skinny_splitk", "gemm_4096"]:
+            if name == head:
+                continue
+            torch.cuda.empty_cache()
+            if name in LINCOMP_NAMES:
+                x = bench_lincomp(name, args.steps, args.warmup)
+                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
+                                 unit="requests/s", hbm_gbs=round(x["gbs"], 1),
+                                 hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4)))
+            else:
+                x = bench_gemm(name, args.steps, args.warmup)
+                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["tflops"], 1),
+                                 unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                 plan=x["plan"]))
+            del x
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("cpu baseline (oracle)")
+        cpu = cpu_baseline_lincomp(head) if head in LINCOMP_NAMES else cpu_baseline_gemm(head)
+
+    out = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": config, "roofline": roof, "cpu_baseline": cpu,
+        "kernel_ms": round(r["kernel_ms"], 4), "plan": plan, "also": also,
+        "kernel_source_hash": _kernel_source_hash(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

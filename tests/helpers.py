@@ -1,25 +1,10 @@
-"""Shared test helpers: move seeded bf16 storage buffers to the GPU and read
-results back as float64.  No arithmetic of the method lives here."""
+"""Shared test helpers (sampling of output entries); device movement comes from
+synth.device.  No arithmetic of the method lives here."""
 from __future__ import annotations
 
 import numpy as np
 
-
-def to_device(buf: np.ndarray, shape, strides, device="cuda"):
-    """A bf16 tensor viewing `buf` (uint16 bf16 patterns) with element strides."""
-    import torch
-    flat = torch.from_numpy(np.ascontiguousarray(buf).view(np.int16)).to(device).view(torch.bfloat16)
-    return flat.as_strided(tuple(shape), tuple(strides))
-
-
-def to_f64(t) -> np.ndarray:
-    return t.float().cpu().numpy().astype(np.float64)
-
-
-def gemm_operands(case, device="cuda"):
-    A = to_device(case.A, (case.M, case.K), (case.sam, case.sak), device)
-    B = to_device(case.B, (case.K, case.N), (case.sbk, case.sbn), device)
-    return A, B
+from synth.device import gemm_operands, lincomp_operands, to_device, to_f64  # noqa: F401
 
 
 def sample_indices(M, N, n, seed, tile=256):

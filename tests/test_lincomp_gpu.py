@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import to_device, to_f64
+from helpers import lincomp_operands, to_f64
 from oracle import acceptance
 
 pytestmark = pytest.mark.gpu
@@ -14,10 +14,8 @@ pytestmark = pytest.mark.gpu
 def _run(case, y_dtype="bf16", flags=0):
     import torch
     import recsys_linear_layers_amd as ll
-    R, C, Nu, Ni, D, Mo = case.R, case.C, case.Nu, case.Ni, case.D, case.Mo
-    user = to_device(case.user if Nu else np.zeros(8, np.uint16), (R, Nu, D), (Nu * D, D, 1))
-    item = to_device(case.item if Ni else np.zeros(8, np.uint16), (R, C, Ni, D), (C * Ni * D, Ni * D, D, 1))
-    W = to_device(case.W, (Nu + Ni, Mo), (Mo, 1))
+    R, C, D, Mo = case.R, case.C, case.D, case.Mo
+    user, item, W = lincomp_operands(case)
     dt = torch.bfloat16 if y_dtype == "bf16" else torch.float32
     Y = torch.full((R, C, Mo, D), float("nan"), dtype=dt, device="cuda")
     ll.lincomp(user, item, W, out=Y, flags=flags)
