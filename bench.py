@@ -170,6 +170,9 @@ def main():
                     choices=sorted(GEMM_NAMES | LINCOMP_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="time only the headline workload")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, --steps times "
+                         "(calibrates the HBM byte counters of a profiler run); prints its own line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -182,6 +185,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        stream = torch.cuda.current_stream()
+        wall, ev = _time_launches(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+        print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ev, 4),
+                          "GB/s": round(2 * n / (ev * 1e-3) / 1e9, 1)}))
+        return
 
     head = args.workload
     if head in LINCOMP_NAMES:

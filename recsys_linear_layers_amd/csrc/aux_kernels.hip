@@ -20,13 +20,10 @@ hipError_t launch_gemm(int layout, int kind, const GemmKArgs& args, int grid, hi
 }
 
 const KindInfo& kind_info(int kind) {
-  static const KindInfo table[KIND_COUNT] = {
-      {256, 128, 512, 3 * (256 + 128) * kBK * 2, 3, 4, "wide_pc_256x128x64_s3_4c4p"},
-      {256, 128, 256, 3 * (256 + 128) * kBK * 2, 3, 0, "wide_coop_256x128x64_s3_4w"},
-      {128, 256, 512, 3 * (128 + 256) * kBK * 2, 3, 4, "tall_pc_128x256x64_s3_4c4p"},
-      {128, 128, 256, 3 * (128 + 128) * kBK * 2, 3, 0, "small_coop_128x128x64_s3_4w"},
-      {64, 256, 512, 3 * (64 + 256) * kBK * 2, 3, 4, "lincomp_pc_64x256x64_s3_4c4p"},
-  };
+#define LL_KIND_INFO(name, bm, bn, kt, wm, wn, np, st) \
+  {bm, bn, kt, (wm * wn + np) * 64, st * (bm + bn) * kt * 2, st, np, #name},
+  static const KindInfo table[KIND_COUNT] = {LL_GEMM_KINDS(LL_KIND_INFO)};
+#undef LL_KIND_INFO
   return table[kind];
 }
 

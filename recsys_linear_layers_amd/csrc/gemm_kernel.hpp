@@ -4,26 +4,29 @@
 // listings on "Triton 3.7 permite extender el compilador de GPU sin forks"
 // state the problem (sections "NVIDIA H100 (Hopper): GEMM persistente" and
 // "AMD MI350: GEMM segmentado"), optionally batched, split along K, and with a
-// per-batch fp32 bias added in the epilogue (used by the linear-compression
-// layer).
+// per-batch fp32 addend in the epilogue (used by the linear-compression layer).
 //
 // How (gfx950-specific design; the pages' TMA/WGMMA and register-staged
 // mechanisms are not used):
-//  * A ring of STAGES LDS slots.  Each slot holds one BK=64 k-slice of the A
-//    tile and of the B tile.  Producer waves fill slots straight from HBM with
+//  * A ring of STAGES LDS slots.  Each slot holds one KT-deep k-slice of the
+//    A tile and of the B tile.  Loading waves fill slots straight from HBM with
 //    `buffer_load_dwordx4 ... lds` (no VGPR staging): each instruction moves
-//    64 lanes x 16 B = 1 KB into a contiguous LDS block.  Out-of-range lanes get
-//    an offset beyond the buffer's num_records, so the hardware writes zeros.
-//  * Consumer waves read MFMA operand fragments from the slot computed STAGES-1
-//    steps earlier and run v_mfma_f32_32x32x16_bf16.  A K-contiguous operand
-//    is stored as [rows][64] (128-byte rows, 16-byte chunks XOR-swizzled) and
-//    read with ds_read_b128; an M/N-contiguous operand is stored as it sits in
-//    memory, [64][rows], and read with ds_read_b64_tr_b16, which transposes
-//    16-bit elements across each group of 16 lanes.
-//  * Handoff: one workgroup barrier per k-step.  Before it, producers wait
-//    (vmcnt) until their loads for the slot about to be consumed have landed;
-//    after it, producers refill the slot consumed in the previous step.  With
-//    NPROD > 0 the roles are separate waves; with NPROD == 0 every wave does
+//    64 lanes x 16 B = 1 KB into a contiguous LDS block.  Lanes outside the
+//    matrix get an offset beyond the buffer's num_records, so the hardware
+//    writes zeros.
+//  * Computing waves read MFMA operand fragments from LDS and run
+//    v_mfma_f32_32x32x16_bf16.  A K-contiguous operand is stored [rows][KT]
+//    (16-byte chunks XOR-swizzled by row) and read with ds_read_b128; an
+//    M/N-contiguous operand is stored as it sits in memory, [KT][rows], and
+//    read with ds_read_b64_tr_b16, which transposes 16-bit elements across
+//    each group of 16 lanes.
+//  * Handoff: one workgroup barrier per k-slice, placed before the slice's
+//    last k16 step.  Before it, loading waves wait (vmcnt) until their share of
+//    the NEXT slice has landed; after it, every wave has finished reading the
+//    current slice's LDS (its last fragments are already in registers), so the
+//    slice's slot is refilled at once and the next slice's first fragments are
+//    read while the last k16 step's MFMAs run.  With NPROD > 0 the loading
+//    and computing roles are separate waves; with NPROD == 0 every wave does
 //    both.  The ring runs across tile boundaries of the persistent loop.
 //  * Persistent grid over (batch, k-split, tile) work items in grouped
 //    (GROUP_M) order, with workgroup ids remapped so that the consecutive
@@ -39,11 +42,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LL_LDS __attribute__((address_space(3)))
 
-constexpr int kBK = 64;                    // k elements per pipeline stage
+constexpr int kBK = 64;                    // k granularity the host plans in (largest KT)
 constexpr uint32_t kOOB = 0x80000000u;     // byte offset beyond every num_records used here
-constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
 struct OperandArgs {
   const uint16_t* ptr;  // element (0, 0) of batch 0
@@ -64,15 +68,23 @@ struct GemmKArgs {
   int32_t M, N;
   int32_t c_bf16;
   int32_t bdiv;
-  int32_t batches, splits, kiters, kps;
+  int32_t batches, splits, kiters, kps;  // kiters, kps in units of KT
   int32_t tiles_m, tiles_n, group_m;
   int32_t total;
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_>
+template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,
+          bool BATCHED_ = false>
 struct GemmCfg {
+  // BATCHED: work items run over batches (operand/C batch offsets) and the
+  // epilogue may add an fp32 addend; otherwise work items run over k-splits
+  // and the epilogue may write split-K partials.  Kernel arguments a kind does
+  // not use are never read, which keeps them out of scalar registers.
+  static constexpr bool BATCHED = BATCHED_;
   static constexpr int BM = BM_, BN = BN_;
-  static constexpr int WM = WM_, WN = WN_;   // consumer-wave grid
+  static constexpr int KT = KT_;              // k elements per ring slot (32 or 64)
+  static constexpr int KS = KT / 16;          // k16 MFMA steps per slot
+  static constexpr int WM = WM_, WN = WN_;    // computing-wave grid
   static constexpr int NCONS = WM * WN;
   static constexpr int NPROD = NPROD_;        // 0: every wave loads and computes
   static constexpr int STAGES = STAGES_;
@@ -81,27 +93,41 @@ struct GemmCfg {
   static constexpr int WAVES = NCONS + NPROD;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 32x32 blocks per wave
-  static constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
+  static constexpr int A_BYTES = BM * KT * 2, B_BYTES = BN * KT * 2;
   static constexpr int SLOT = A_BYTES + B_BYTES;
   static constexpr int LDS = STAGES * SLOT;
   static constexpr int LOADERS = NPROD ? NPROD : NCONS;
-  static constexpr int QA = BM / 8, QB = BN / 8;           // 1-KB load instructions per stage
-  static constexpr int LPW = (QA + QB) / LOADERS;           // per loading wave
+  static constexpr int QA = A_BYTES / 1024, QB = B_BYTES / 1024;  // 1-KB loads per slot
+  static constexpr int LPW = (QA + QB) / LOADERS;                  // per loading wave
+  static_assert(KT == 32 || KT == 64, "KT");
   static_assert(QA % LOADERS == 0 && QB % LOADERS == 0, "load split");
   static_assert(FM >= 1 && FN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(STAGES >= 2, "stages");
+  static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
+  // Accumulators beyond what fits beside the fragments in 256 VGPRs are kept in
+  // AGPRs explicitly: the MFMAs are then written as inline asm with AGPR
+  // accumulator operands (the compiler otherwise places fragments in AGPRs and
+  // spills accumulators).
+  static constexpr bool AGPR_ACC = FM * FN * 16 > 128;
 };
 
 // ---------------------------------------------------------------------------
-// LDS layouts.  K-major tile: [rows][64] bf16, 128-byte rows of eight 16-byte
-// chunks; chunk c of row r sits at c ^ swz_k(r), which makes the 8 (or 16)
-// rows one ds_read_b128 pass touches hit distinct banks.  MN-major tile:
-// [64][rows] bf16; chunk c of k-row r sits at c ^ swz_mn(r), which spreads the
-// 4 k-rows one ds_read_b64_tr_b16 lane group reads over different banks.
+// LDS layouts.
+//  K-major tile: [rows][KT] bf16, rows of CPR = KT/8 16-byte chunks; chunk c of
+//  row r sits at c ^ swz_k(r).  For CPR = 8 the 8 (or 16) rows one
+//  ds_read_b128 pass touches fall in distinct bank groups; for CPR = 4 (two
+//  rows per 128-byte bank line) likewise for 8- and 16-lane passes.
+//  MN-major tile: [KT][rows] bf16; chunk c of k-row r sits at c ^ swz_mn(r),
+//  which spreads the 4 k-rows one ds_read_b64_tr_b16 lane group reads over
+//  different banks.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (CPR == 8) return (row ^ (row >> 3)) & 7;
+  else return ((row >> 1) ^ (row >> 2)) & 3;
+}
 template <int CH>
 __device__ __forceinline__ int swz_mn(int k) { return ((k & 3) << 2) & (CH - 1); }
 
@@ -121,51 +147,110 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nrec) {
   r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
   r[2] = __builtin_amdgcn_readfirstlane((int)nrec);
-  r[3] = (int)kRsrcWord3;
+  r[3] = kRsrcWord3;
   return r;
 }
 
 // One direct-to-LDS load: lane l's 16 bytes at rsrc.base + voff land at LDS
-// byte lds_addr + 16*l.  Written as inline asm so that the compiler does not
-// treat every later LDS access as dependent on it (it would otherwise insert
-// s_waitcnt vmcnt(0) before each ds_read and barrier).  Completion is tracked
-// by the explicit vmcnt waits of the pipeline instead.
+// byte address m0 + 16*l.  Written as inline asm (M0 passed as an operand) so
+// that the compiler does not order every later LDS access and barrier behind
+// it with s_waitcnt vmcnt(0); completion is tracked by the explicit vmcnt
+// waits of the pipeline instead.
+//
+// The compiler does not see a vector-memory instruction inside the asm, so it
+// cannot pad the gfx9 hazards in front of it: a VALU write of an SGPR
+// (v_readfirstlane building the descriptor, v_readlane restoring a spilled
+// SGPR) needs 5 wait states before a VMEM instruction reads that SGPR, and an
+// SALU write of M0 needs 1 before an LDS-DMA load.  The s_nop 4 covers both.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const char LL_LDS* p) { return (uint32_t)(uintptr_t)p; }
 
+// One direct-to-LDS load with a wave-uniform byte offset added (soffset);
+// same hazard padding as dma16.
+__device__ __forceinline__ void dma16s(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+               : "memory");
+}
+
 // Issue this wave's share of the 1-KB direct-to-LDS loads of one operand tile
-// (R rows along M or N, one BK slice).  q0/qstep select the instructions.
-template <int R, bool KMAJ>
-__device__ __forceinline__ void load_tile(const OperandArgs& op, int64_t boff, int mn0, int k0,
-                                          char LL_LDS* dst, int q0, int qstep, int lane) {
-  const int64_t base = KMAJ ? boff + (int64_t)mn0 * op.ld + k0 : boff + (int64_t)k0 * op.ld + mn0;
-  const i32x4 rsrc = make_rsrc(op.ptr + base, clamp_records(op.extent - base));
-  constexpr int NQ = R / 8;
-  const int ld = (int)op.ld;
-  const uint32_t dst0 = lds_u32(dst);
-#pragma unroll
-  for (int q = q0; q < NQ; q += qstep) {
-    uint32_t voff;
-    if (KMAJ) {
-      const int row = q * 8 + (lane >> 3);
-      const int lc = (lane & 7) ^ swz_k(row);
-      const bool ok = (mn0 + row < op.rows) && (k0 + lc * 8 < op.kvalid);
-      voff = ok ? (uint32_t)(row * ld + lc * 8) * 2u : kOOB;
+// (R rows along M or N, one KT slice): instructions q = lw, lw + NL, ...
+//
+// Instruction q covers tile rows (K-major) or k-rows (MN-major) q*RPQ ..
+// q*RPQ + RPQ - 1.  In the fast path its byte offset splits into a
+// wave-uniform part (slice offset + q*RPQ*ld*2, passed as soffset) and a
+// per-lane part that depends on q only through q mod PER, the period of the
+// swizzle pattern, so one or two offset registers serve all instructions.
+// Tiles that reach past the matrix (last row/column tile, a k tail) take the
+// masked path, where lanes outside the matrix get an offset beyond
+// num_records and the hardware writes zeros.
+template <int R, int KT, bool KMAJ>
+struct TileGeom {
+  static constexpr int NQ = R * KT * 2 / 1024;   // 1-KB instructions per tile
+  static constexpr int CPR = KT / 8;             // K-major: 16-byte chunks per row
+  static constexpr int CH = R / 8;               // MN-major: 16-byte chunks per k-row
+  static constexpr int RPQ = KMAJ ? 64 / CPR : 64 / CH;
+  static constexpr int PER = KMAJ ? (CPR == 8 ? 8 : 1) : (RPQ >= 4 ? 1 : 4 / RPQ);
+  static_assert(KMAJ || CH <= 64, "MN-major tile too wide");
+  // Per-lane byte offset of instruction q (q mod PER) relative to its first row.
+  __device__ static __forceinline__ uint32_t lane_off(int q, int lane, int ld) {
+    const int qq = PER == 1 ? 0 : q % PER;
+    int rl, lc;
+    if constexpr (KMAJ) {
+      rl = lane / CPR;
+      lc = (lane % CPR) ^ swz_k<CPR>(qq * RPQ + rl);
     } else {
-      constexpr int CH = R / 8;
-      const int lin = q * 64 + lane;
-      const int kr = lin / CH;
-      const int lc = (lin % CH) ^ swz_mn<CH>(kr);
-      const bool ok = (k0 + kr < op.kvalid) && (mn0 + lc * 8 < op.rows);
-      voff = ok ? (uint32_t)(kr * ld + lc * 8) * 2u : kOOB;
+      rl = lane / CH;
+      lc = (lane % CH) ^ swz_mn<CH>(qq * RPQ + rl);
     }
-    dma16(rsrc, __builtin_amdgcn_readfirstlane(dst0 + q * 1024), voff);
+    return (uint32_t)(rl * ld + lc * 8) * 2u;
+  }
+};
+
+template <int R, int KT, bool KMAJ, int NL, class Stream>
+__device__ __forceinline__ void load_tile(const OperandArgs& op, const Stream& o, bool fast, int mn0, int k0,
+                                          char LL_LDS* dst, int lw, int lane, uint32_t vfast) {
+  using G = TileGeom<R, KT, KMAJ>;
+  static_assert(G::NQ % NL == 0, "load split");
+  const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_u32(dst));
+  const int ld = (int)op.ld;
+  if (fast) {
+#pragma unroll
+    for (int i = 0; i < G::NQ / NL; ++i) {
+      const int q = lw + i * NL;
+      // vfast is lane_off(lw); other residues are recomputed (PER > NL only).
+      const uint32_t voff = (NL % G::PER == 0) ? vfast : G::lane_off(q, lane, ld);
+      const uint32_t soff = o.soff + (uint32_t)(q * G::RPQ) * (uint32_t)ld * 2u;
+      dma16s(o.rs, dst0 + q * 1024, voff, soff);
+    }
+  } else {
+    // Lanes outside the matrix: offset beyond num_records (the whole offset
+    // sits in voff here, soffset is 0, so it cannot wrap back into range).
+#pragma unroll
+    for (int i = 0; i < G::NQ / NL; ++i) {
+      const int q = lw + i * NL;
+      uint32_t voff;
+      if constexpr (KMAJ) {
+        const int row = q * G::RPQ + lane / G::CPR;
+        const int lc = (lane % G::CPR) ^ swz_k<G::CPR>(row);
+        const bool ok = (mn0 + row < op.rows) && (k0 + lc * 8 < op.kvalid);
+        voff = ok ? o.soff + (uint32_t)(row * ld + lc * 8) * 2u : kOOB;
+      } else {
+        const int lin = q * 64 + lane;
+        const int kr = lin / G::CH;
+        const int lc = (lin % G::CH) ^ swz_mn<G::CH>(kr);
+        const bool ok = (k0 + kr < op.kvalid) && (mn0 + lc * 8 < op.rows);
+        voff = ok ? o.soff + (uint32_t)(kr * ld + lc * 8) * 2u : kOOB;
+      }
+      dma16(o.rs, dst0 + q * 1024, voff);
+    }
   }
 }
 
@@ -177,11 +262,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // MFMA operand fragment: lane l holds rows/cols (r0 + l%32) and k = kk*16 + 8*(l/32) + j, j<8.
-template <int R>
+template <int KT>
 __device__ __forceinline__ bf16x8 frag_kmajor(const char LL_LDS* tile, int r0, int kk, int lane) {
+  constexpr int CPR = KT / 8;
   const int row = r0 + (lane & 31);
   const int lc = kk * 2 + (lane >> 5);
-  return *(const bf16x8 LL_LDS*)(tile + row * 128 + ((lc ^ swz_k(row)) << 4));
+  return *(const bf16x8 LL_LDS*)(tile + row * (KT * 2) + ((lc ^ swz_k<CPR>(row)) << 4));
 }
 
 // Same fragment from an MN-major tile.  ds_read_b64_tr_b16 gives lane i of each
@@ -214,23 +300,30 @@ struct TileInfo {
   int b, ks, m0, n0, kb, ke;
 };
 
-template <int BM, int BN>
+template <class Cfg>
 __device__ __forceinline__ TileInfo decode_tile(const GemmKArgs& p, int t) {
   const int tiles = p.tiles_m * p.tiles_n;
   const int tin = t % tiles;
   const int rest = t / tiles;
   TileInfo ti;
-  ti.ks = rest % p.splits;
-  ti.b = rest / p.splits;
+  if constexpr (Cfg::BATCHED) {
+    ti.ks = 0;
+    ti.b = rest;
+    ti.kb = 0;
+    ti.ke = p.kiters;
+  } else {
+    ti.ks = rest;
+    ti.b = 0;
+    ti.kb = rest * p.kps;
+    ti.ke = min(ti.kb + p.kps, p.kiters);
+  }
   const int per_group = p.group_m * p.tiles_n;
   const int gid = tin / per_group;
   const int first_m = gid * p.group_m;
   const int gsz = min(p.tiles_m - first_m, p.group_m);
   const int w = tin - gid * per_group;
-  ti.m0 = (first_m + w % gsz) * BM;
-  ti.n0 = (w / gsz) * BN;
-  ti.kb = ti.ks * p.kps;
-  ti.ke = min(ti.kb + p.kps, p.kiters);
+  ti.m0 = (first_m + w % gsz) * Cfg::BM;
+  ti.n0 = (w / gsz) * Cfg::BN;
   return ti;
 }
 
@@ -241,75 +334,157 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   return (bid & 7) * (grid >> 3) + (bid >> 3);
 }
 
-template <int BM, int BN>
-struct Cursor {
-  int t, k;
-  TileInfo ti;
-  __device__ __forceinline__ void init(const GemmKArgs& p, int first) {
-    t = first;
-    if (t < p.total) {
-      ti = decode_tile<BM, BN>(p, t);
-      k = ti.kb;
-    }
-  }
-  __device__ __forceinline__ bool valid(const GemmKArgs& p) const { return t < p.total; }
-  __device__ __forceinline__ void advance(const GemmKArgs& p, int stride) {
-    if (++k == ti.ke) {
-      t += stride;
-      if (t < p.total) {
-        ti = decode_tile<BM, BN>(p, t);
-        k = ti.kb;
-      }
-    }
-  }
-};
-
 __device__ __forceinline__ int64_t batch_off(int b, int bdiv, int64_t bo, int64_t bi) {
   return (int64_t)(b / bdiv) * bo + (int64_t)(b % bdiv) * bi;
 }
 
+// Loading side of the pipeline.  Per operand: a buffer descriptor based at
+// the work item's tile origin at slice `k0s` and a running wave-uniform byte
+// offset along k, so that each slice costs one scalar add per operand.  The
+// descriptor is re-based (opened again at the current slice) before the
+// offset could leave the 32-bit range.
+struct OpStream {
+  i32x4 rs;
+  uint32_t soff;  // byte offset of the next slice from the descriptor base
+  int32_t k0s;    // slice (units of KT) at the descriptor base
+};
+
 template <class Cfg>
-__device__ __forceinline__ void issue_stage(const GemmKArgs& p, const TileInfo& ti, int k,
-                                            char LL_LDS* slot, int lw, int lane) {
-  const int k0 = k * kBK;
-  load_tile<Cfg::BM, Cfg::A_KMAJOR>(p.a, batch_off(ti.b, p.bdiv, p.a.bo, p.a.bi), ti.m0, k0, slot,
-                                    lw, Cfg::LOADERS, lane);
-  load_tile<Cfg::BN, Cfg::B_KMAJOR>(p.b, batch_off(ti.b, p.bdiv, p.b.bo, p.b.bi), ti.n0, k0,
-                                    slot + Cfg::A_BYTES, lw, Cfg::LOADERS, lane);
-}
+struct Loader {
+  int t, k, ke;  // work item, next slice, end slice (units of KT)
+  int b, m0, n0;
+  bool rows_in;  // both operand tiles lie inside the matrix along M and N
+  OpStream a, bo;
+
+  template <int R, bool KMAJ>
+  __device__ static __forceinline__ void open(OpStream& o, const OperandArgs& op, int b, int bdiv, int mn0,
+                                              int ks) {
+    int64_t origin = KMAJ ? (int64_t)mn0 * op.ld + (int64_t)ks * Cfg::KT
+                          : (int64_t)ks * Cfg::KT * op.ld + mn0;
+    if constexpr (Cfg::BATCHED) origin += batch_off(b, bdiv, op.bo, op.bi);
+    o.rs = make_rsrc(op.ptr + origin, clamp_records(op.extent - origin));
+    o.soff = 0;
+    o.k0s = ks;
+  }
+
+  __device__ __forceinline__ void start(const GemmKArgs& p, int t_) {
+    t = t_;
+    if (t >= p.total) return;
+    const TileInfo ti = decode_tile<Cfg>(p, t);
+    k = ti.kb;
+    ke = ti.ke;
+    b = ti.b;
+    m0 = ti.m0;
+    n0 = ti.n0;
+    rows_in = m0 + Cfg::BM <= p.a.rows && n0 + Cfg::BN <= p.b.rows;
+    open<Cfg::BM, Cfg::A_KMAJOR>(a, p.a, b, p.bdiv, m0, k);
+    open<Cfg::BN, Cfg::B_KMAJOR>(bo, p.b, b, p.bdiv, n0, k);
+  }
+
+  __device__ __forceinline__ bool valid(const GemmKArgs& p) const { return t < p.total; }
+
+  // Issue this wave's share of slice k into `slot`.
+  __device__ __forceinline__ void issue(const GemmKArgs& p, char LL_LDS* slot, int lw, int lane, uint32_t va,
+                                        uint32_t vb) const {
+    const int k0 = k * Cfg::KT;
+    const bool fast = rows_in && k0 + Cfg::KT <= p.a.kvalid;  // kvalid is the same for both operands
+    load_tile<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR, Cfg::LOADERS>(p.a, a, fast, m0, k0, slot, lw, lane, va);
+    load_tile<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR, Cfg::LOADERS>(p.b, bo, fast, n0, k0, slot + Cfg::A_BYTES, lw,
+                                                              lane, vb);
+  }
+
+  __device__ __forceinline__ void advance(const GemmKArgs& p, int stride) {
+    if (++k == ke) {
+      start(p, t + stride);
+      return;
+    }
+    a.soff += Cfg::A_KMAJOR ? Cfg::KT * 2u : (uint32_t)(Cfg::KT * 2) * (uint32_t)p.a.ld;
+    bo.soff += Cfg::B_KMAJOR ? Cfg::KT * 2u : (uint32_t)(Cfg::KT * 2) * (uint32_t)p.b.ld;
+    if (a.soff >= (1u << 30)) open<Cfg::BM, Cfg::A_KMAJOR>(a, p.a, b, p.bdiv, m0, k);
+    if (bo.soff >= (1u << 30)) open<Cfg::BN, Cfg::B_KMAJOR>(bo, p.b, b, p.bdiv, n0, k);
+  }
+};
+
+template <class Cfg>
+struct Frags {
+  bf16x8 a[Cfg::FM], b[Cfg::FN];
+};
 
 template <class Cfg>
 __device__ __forceinline__ void load_frags(const char LL_LDS* slot, int kk, int wm0, int wn0, int lane,
-                                           bf16x8 (&a)[Cfg::FM], bf16x8 (&b)[Cfg::FN]) {
+                                           Frags<Cfg>& f) {
   const char LL_LDS* sA = slot;
   const char LL_LDS* sB = slot + Cfg::A_BYTES;
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i)
-    a[i] = Cfg::A_KMAJOR ? frag_kmajor<Cfg::BM>(sA, wm0 + 32 * i, kk, lane)
-                         : frag_mnmajor<Cfg::BM>(sA, wm0 + 32 * i, kk, lane);
+    f.a[i] = Cfg::A_KMAJOR ? frag_kmajor<Cfg::KT>(sA, wm0 + 32 * i, kk, lane)
+                           : frag_mnmajor<Cfg::BM>(sA, wm0 + 32 * i, kk, lane);
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j)
-    b[j] = Cfg::B_KMAJOR ? frag_kmajor<Cfg::BN>(sB, wn0 + 32 * j, kk, lane)
-                         : frag_mnmajor<Cfg::BN>(sB, wn0 + 32 * j, kk, lane);
+    f.b[j] = Cfg::B_KMAJOR ? frag_kmajor<Cfg::KT>(sB, wn0 + 32 * j, kk, lane)
+                           : frag_mnmajor<Cfg::BN>(sB, wn0 + 32 * j, kk, lane);
 }
 
-// One BK slice: four k16 steps; fragments of step kk+1 are requested before
-// the MFMAs of step kk so that LDS latency overlaps matrix-core work.
+// One k16 step over the wave's FM x FN blocks.  `first` (wave-uniform) starts
+// the tile's sums: the MFMA then takes 0 as its C operand instead of acc.
+// AGPR_ACC: the MFMAs are volatile inline asm on AGPR accumulators, so they
+// keep program order with the other volatile asm of the kernel (DMA issue,
+// the hazard padding before the epilogue); fragments are VGPR operands
+// written by LDS reads, whose results the compiler waits for.  Back-to-back
+// MFMAs accumulating into the same registers need no padding.
 template <class Cfg>
-__device__ __forceinline__ void compute_stage(const char LL_LDS* slot, f32x16 (&acc)[Cfg::FM][Cfg::FN],
-                                              int wm0, int wn0, int lane) {
-  bf16x8 a[2][Cfg::FM], b[2][Cfg::FN];
-  load_frags<Cfg>(slot, 0, wm0, wn0, lane, a[0], b[0]);
+__device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN], bool first) {
+  if constexpr (Cfg::AGPR_ACC) {
+    if (first) {
 #pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    const int cur = kk & 1;
-    if (kk + 1 < kBK / 16) load_frags<Cfg>(slot, kk + 1, wm0, wn0, lane, a[cur ^ 1], b[cur ^ 1]);
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc[i][j]) : "v"(f.a[i]), "v"(f.b[j]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(f.a[i]), "v"(f.b[j]));
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   }
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// Accumulator element r of block (i, j) as a VGPR value.  AGPR_ACC: read with
+// an ordered asm v_accvgpr_read after acc_hazard_pad().
+template <class Cfg>
+__device__ __forceinline__ float acc_get(const f32x16& a, int r) {
+  if constexpr (Cfg::AGPR_ACC) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a[r]));
+    return v;
+  } else {
+    return a[r];
+  }
+}
+
+// Wait states between the last MFMA of a tile and VALU reads of its result
+// (the longest MFMA-write -> VALU-read requirement is below 20 cycles).
+template <class Cfg>
+__device__ __forceinline__ void acc_hazard_pad() {
+  if constexpr (Cfg::AGPR_ACC) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
@@ -324,7 +499,7 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
                                          int lane) {
   const int colb = ti.n0 + wn0 + (lane & 31);
   const int rowb = ti.m0 + wm0 + 4 * (lane >> 5);
-  if (p.partial) {
+  if (!Cfg::BATCHED && p.partial) {
     float* P = p.partial + (int64_t)ti.ks * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
@@ -334,12 +509,14 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
         for (int r = 0; r < 16; ++r) {
           const int row = rowb + 32 * i + 8 * (r >> 2) + (r & 3);
           const int col = colb + 32 * j;
-          if (row < p.M && col < p.N) P[(int64_t)row * p.N + col] = acc[i][j][r];
+          const float v = acc_get<Cfg>(acc[i][j], r);
+          if (row < p.M && col < p.N) P[(int64_t)row * p.N + col] = v;
         }
     return;
   }
-  const int64_t coff = batch_off(ti.b, p.bdiv, p.cbo, p.cbi);
-  const int64_t boff = p.bias ? batch_off(ti.b, p.bdiv, p.bias_bo, p.bias_bi) : 0;
+  const int64_t coff = Cfg::BATCHED ? batch_off(ti.b, p.bdiv, p.cbo, p.cbi) : 0;
+  const float* bias = Cfg::BATCHED ? p.bias : nullptr;
+  const int64_t boff = bias ? batch_off(ti.b, p.bdiv, p.bias_bo, p.bias_bi) : 0;
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
@@ -347,13 +524,13 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
       const int col = colb + 32 * j;
       float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = acc[i][j][r];
-      if (p.bias) {
+      for (int r = 0; r < 16; ++r) v[r] = acc_get<Cfg>(acc[i][j], r);
+      if (bias) {
         float bv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rowb + 32 * i + 8 * (r >> 2) + (r & 3);
-          bv[r] = (row < p.M && col < p.N) ? p.bias[boff + row * p.bias_m + col * p.bias_n] : 0.f;
+          bv[r] = (row < p.M && col < p.N) ? bias[boff + row * p.bias_m + col * p.bias_n] : 0.f;
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] += bv[r];
@@ -372,13 +549,27 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
     }
 }
 
+// s_waitcnt vmcnt(n * LPW) for a wave-uniform n in [0, S-2].
+template <class Cfg>
+__device__ __forceinline__ void wait_slices(int n) {
+  if constexpr (Cfg::STAGES <= 2) {
+    wait_vmcnt<0>();
+  } else {
+    if (n <= 0) wait_vmcnt<0>();
+    else if (n == 1 || Cfg::STAGES == 3) wait_vmcnt<Cfg::LPW>();
+    else wait_vmcnt<(Cfg::STAGES - 2) * Cfg::LPW>();
+  }
+}
+
 template <class Cfg>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_EU, Cfg::WAVES_PER_EU)))
     gemm_persistent(const GemmKArgs p) {
+  static_assert(Cfg::STAGES <= 4, "wait_slices covers up to 4 stages");
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS];
   char LL_LDS* smem = (char LL_LDS*)smem_raw;
   constexpr int S = Cfg::STAGES;
+  constexpr int KS = Cfg::KS;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const bool is_cons = Cfg::NPROD == 0 || wave < Cfg::NCONS;
@@ -387,63 +578,84 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   const int cw = is_cons ? wave : 0;
   const int wm0 = (cw / Cfg::WN) * (Cfg::BM / Cfg::WM);
   const int wn0 = (cw % Cfg::WN) * (Cfg::BN / Cfg::WN);
+  const uint32_t va = TileGeom<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR>::lane_off(lw, lane, (int)p.a.ld);
+  const uint32_t vb = TileGeom<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR>::lane_off(lw, lane, (int)p.b.ld);
 
   const int stride = gridDim.x;
   const int first = xcd_remap(blockIdx.x, gridDim.x);
-  Cursor<Cfg::BM, Cfg::BN> lc, cc;
-  lc.init(p, first);
-  cc.init(p, first);
+  if (first >= p.total) return;  // uniform over the workgroup
 
+  Loader<Cfg> ld;
+  ld.start(p, first);
+
+  // Prologue: fill every slot of the ring.
   int issued = 0;
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) {
-    if (lc.valid(p)) {
-      if (is_prod) issue_stage<Cfg>(p, lc.ti, lc.k, smem + s * Cfg::SLOT, lw, lane);
-      lc.advance(p, stride);
+  for (int s = 0; s < S; ++s) {
+    if (ld.valid(p)) {
+      if (is_prod) ld.issue(p, smem + s * Cfg::SLOT, lw, lane, va, vb);
+      ld.advance(p, stride);
       ++issued;
     }
   }
+  if (is_prod) wait_slices<Cfg>(issued - 1);
+  lds_barrier();
 
   f32x16 acc[Cfg::FM][Cfg::FN];
-#pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+  Frags<Cfg> f[2];
+  if (is_cons) load_frags<Cfg>(smem, 0, wm0, wn0, lane, f[0]);
 
   bool drain = false;  // this wave issued global stores since its last full wait
-  int j = 0;
-  while (cc.valid(p)) {
-    const int slot = j % S;
-    if (is_prod) {
-      if (!drain && issued - j - 1 >= S - 2)
-        wait_vmcnt<(S - 2) * Cfg::LPW>();
-      else
-        wait_vmcnt<0>();
-      drain = false;
+  int j = 0;           // slices consumed so far
+  int slot = 0;        // ring slot of slice j
+  int ct = first;      // work item being computed
+  TileInfo cti = decode_tile<Cfg>(p, ct);
+  int ck = cti.kb;
+  while (true) {
+    char LL_LDS* cur = smem + slot * Cfg::SLOT;
+    const bool tile_first = ck == cti.kb;
+    const bool tile_end = ck + 1 == cti.ke;
+    const bool has_next = !tile_end || ct + stride < p.total;
+    const int nslot = slot + 1 == S ? 0 : slot + 1;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) {
+        if (is_cons) load_frags<Cfg>(cur, kk + 1, wm0, wn0, lane, f[(kk + 1) & 1]);
+      } else {
+        // Slice boundary: slice j+1 must have landed; slice j's LDS is free.
+        if (is_prod && has_next) {
+          wait_slices<Cfg>(drain ? 0 : issued - j - 2);
+          drain = false;
+        }
+        lds_barrier();
+        if (ld.valid(p)) {
+          if (is_prod) ld.issue(p, cur, lw, lane, va, vb);
+          ld.advance(p, stride);
+          ++issued;
+        }
+        if (is_cons && has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
+      }
+      if (is_cons) mfma_step<Cfg>(f[kk & 1], acc, Cfg::AGPR_ACC && kk == 0 && tile_first);
     }
-    lds_barrier();
-    if (lc.valid(p)) {
-      if (is_prod) issue_stage<Cfg>(p, lc.ti, lc.k, smem + ((j + S - 1) % S) * Cfg::SLOT, lw, lane);
-      lc.advance(p, stride);
-      ++issued;
-    }
-    if (is_cons) compute_stage<Cfg>(smem + slot * Cfg::SLOT, acc, wm0, wn0, lane);
-    if (cc.k + 1 == cc.ti.ke) {
+    if (tile_end) {
       if (is_cons) {
-        epilogue<Cfg>(p, cc.ti, acc, wm0, wn0, lane);
+        acc_hazard_pad<Cfg>();
+        epilogue<Cfg>(p, cti, acc, wm0, wn0, lane);
         drain = true;
       }
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < Cfg::FN; ++jj)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+      if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
     }
-    cc.advance(p, stride);
+    if (!has_next) break;
+    if (tile_end) {
+      ct += stride;
+      cti = decode_tile<Cfg>(p, ct);
+      ck = cti.kb;
+    } else {
+      ++ck;
+    }
     ++j;
+    slot = nslot;
   }
 }
 

@@ -1,6 +1,8 @@
-// Instantiations of the persistent GEMM for A K-contiguous,
-// B K-contiguous.
+// Instantiations of the persistent GEMM for A K-contiguous, B K-contiguous.
 #include "kernels.hpp"
+
+#define LL_AK true
+#define LL_BK true
 
 namespace ll {
 
@@ -12,10 +14,7 @@ static hipError_t launch_cfg(const GemmKArgs& a, int grid, hipStream_t s) {
 
 hipError_t launch_gemm_kk(int kind, const GemmKArgs& a, int grid, hipStream_t s) {
   switch (kind) {
-    case KIND_WIDE_PC: return launch_cfg<GemmCfg<256, 128, 2, 2, 4, 3, true, true>>(a, grid, s);
-    case KIND_WIDE_COOP: return launch_cfg<GemmCfg<256, 128, 2, 2, 0, 3, true, true>>(a, grid, s);
-    case KIND_TALL_PC: return launch_cfg<GemmCfg<128, 256, 2, 2, 4, 3, true, true>>(a, grid, s);
-    case KIND_SMALL_COOP: return launch_cfg<GemmCfg<128, 128, 2, 2, 0, 3, true, true>>(a, grid, s);
+    LL_GEMM_KINDS(LL_KIND_CASE)
     default: return hipErrorInvalidValue;
   }
 }

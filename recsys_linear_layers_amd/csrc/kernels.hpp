@@ -8,24 +8,40 @@
 
 namespace ll {
 
-// Tile configurations (indices into the launch tables).
+// Tile configurations: X(name, BM, BN, KT, WM, WN, NPROD, STAGES).  WM x WN
+// computing waves each own a (BM/WM) x (BN/WN) block of the tile; NPROD > 0
+// adds that many loading waves, NPROD == 0 makes every wave load and compute.
+// KT is the k depth of one ring slot.
+#define LL_GEMM_KINDS(X)                                                                              \
+  X(KIND_SQ4_K64, 256, 256, 64, 2, 2, 0, 2)    /* 4 waves (1 per SIMD) 128x128 each, 2 x 64 KB */    \
+  X(KIND_SQ4_K32, 256, 256, 32, 2, 2, 0, 4)    /* same, 4 x 32 KB slots */                          \
+  X(KIND_SQ8_K64, 256, 256, 64, 2, 4, 0, 2)    /* 8 waves (2 per SIMD) 128x64 each */               \
+  X(KIND_SQ8_K32, 256, 256, 32, 2, 4, 0, 4)    /* same, 4 x 32 KB slots */                          \
+  X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 3)    /* 4 computing 128x64 + 4 loading waves */           \
+  X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 3)  /* 4 waves 128x64, load + compute */                 \
+  X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 3)    /* skinny M: 4 computing 64x128 + 4 loading */       \
+  X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 3) /* small problems: 4 waves 64x64 */                  \
+  X(KIND_LINCOMP_PC, 64, 256, 64, 1, 4, 4, 3)  /* one 64xD candidate block: 4 + 4 waves */
+
 enum KernelKind {
-  KIND_WIDE_PC = 0,   // 256x128 tile, 4 consumer waves (2x2, 128x64 each) + 4 producer waves, 3 stages
-  KIND_WIDE_COOP,     // 256x128 tile, 4 waves that load and compute, 3 stages
-  KIND_TALL_PC,       // 128x256 tile (skinny M), 4 consumers (2x2, 64x128) + 4 producers, 3 stages
-  KIND_SMALL_COOP,    // 128x128 tile, 4 waves that load and compute (64x64 each), 3 stages
-  KIND_LINCOMP_PC,    // 64x256 tile (one candidate's 64xD output), 4 consumers (1x4) + 4 producers
+#define LL_KIND_ENUM(name, ...) name,
+  LL_GEMM_KINDS(LL_KIND_ENUM)
+#undef LL_KIND_ENUM
   KIND_COUNT
 };
 
 struct KindInfo {
-  int bm, bn, threads, lds, stages, nprod;
+  int bm, bn, kt, threads, lds, stages, nprod;
   const char* name;
 };
 const KindInfo& kind_info(int kind);
 
 // Layout index: bit 1 = A is M-contiguous, bit 0 = B is N-contiguous.
 inline int layout_index(bool a_kmajor, bool b_kmajor) { return (a_kmajor ? 0 : 2) | (b_kmajor ? 0 : 1); }
+
+// Launch switch over every kind for one operand layout (instantiated once per layout).
+#define LL_KIND_CASE(name, bm, bn, kt, wm, wn, np, st) \
+  case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK, name == KIND_LINCOMP_PC>>(a, grid, s);
 
 // Launch `kind` for layout `layout` on `grid` workgroups.  Returns the launch status.
 hipError_t launch_gemm(int layout, int kind, const GemmKArgs& args, int grid, hipStream_t stream);

@@ -3,6 +3,7 @@
 // The declarations and their contracts are in include/linlayers.h.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -216,7 +217,8 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   if (s != LL_OK) return s;
   p.cus = info->cus;
 
-  // Tile shape: skinny M uses 128-row tiles; tiny problems use 128x128 tiles.
+  // Tile shape: skinny M uses 128-row tiles; tiny problems use 128x128 tiles;
+  // everything else 256x256 tiles.
   const int64_t M = d->M, N = d->N;
   int kind;
   if (M <= 128 && N >= 1024)
@@ -224,26 +226,32 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   else if (M * N <= 1024ll * 1024)
     kind = KIND_SMALL_COOP;
   else
-    kind = KIND_WIDE_PC;
+    kind = KIND_SQ8_K32;
   if (d->flags & LL_FLAG_COOPERATIVE) {
-    if (kind == KIND_WIDE_PC || kind == KIND_TALL_PC) kind = KIND_WIDE_COOP;
+    if (kind_info(kind).nprod > 0) kind = KIND_WIDE_COOP;
   } else if (d->flags & LL_FLAG_PRODUCER_CONSUMER) {
-    if (kind == KIND_SMALL_COOP || kind == KIND_WIDE_COOP) kind = KIND_WIDE_PC;
+    if (kind_info(kind).nprod == 0) kind = KIND_WIDE_PC;
+  }
+  // LL_GEMM_KIND=<kind name or index> overrides the choice (configuration sweeps).
+  if (const char* env = getenv("LL_GEMM_KIND")) {
+    for (int i = 0; i < KIND_COUNT; ++i)
+      if (strcmp(env, kind_info(i).name) == 0) kind = i;
+    if (env[0] >= '0' && env[0] <= '9' && atoi(env) < KIND_COUNT) kind = atoi(env);
   }
   p.kind = kind;
   const KindInfo& ki = kind_info(kind);
   p.tiles_m = (int)((M + ki.bm - 1) / ki.bm);
   p.tiles_n = (int)((N + ki.bn - 1) / ki.bn);
-  p.kiters = (int)((p.Kp + kBK - 1) / kBK);
+  p.kiters = (int)((p.Kp + ki.kt - 1) / ki.kt);
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   if (tiles >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "too many tiles");
   const int occ = occupancy_for(kind);
   const int64_t slots = (int64_t)p.cus * occ;
   // Split K when the tiles alone cannot fill the chip and K is long enough to share.
   int splits = 1;
-  if (tiles > 0 && tiles * 2 <= slots && p.kiters >= 16) {
+  if (tiles > 0 && tiles * 2 <= slots && p.Kp >= 1024) {
     int64_t want = slots / tiles;
-    int64_t by_k = p.kiters / 8;
+    int64_t by_k = p.Kp / 512;
     splits = (int)(want < by_k ? want : by_k);
     if (splits < 1) splits = 1;
     if (splits > 64) splits = 64;
@@ -469,7 +477,7 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
     k.bdiv = dedup ? 1 : (int32_t)d->C;
     k.batches = (int32_t)(dedup ? d->R : d->R * d->C);
     k.splits = 1;
-    k.kiters = (int32_t)((d->Nu + kBK - 1) / kBK);
+    k.kiters = (int32_t)((d->Nu + ki.kt - 1) / ki.kt);
     k.kps = k.kiters;
     k.tiles_m = tiles_m;
     k.tiles_n = tiles_n;
@@ -513,7 +521,7 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
   k.bdiv = (int32_t)d->C;
   k.batches = (int32_t)(d->R * d->C);
   k.splits = 1;
-  k.kiters = (int32_t)((d->Ni + kBK - 1) / kBK);
+  k.kiters = (int32_t)((d->Ni + ki.kt - 1) / ki.kt);
   k.kps = k.kiters;
   k.tiles_m = tiles_m;
   k.tiles_n = tiles_n;
