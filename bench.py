@@ -63,23 +63,27 @@ def _log(msg: str) -> None:
 
 
 def _time_launches(fn, steps: int, warmup: int, stream):
-    """Returns (wall ms per step, average event-measured ms per launch)."""
+    """Returns (wall ms per step, event-measured ms per step).
+
+    The K timed steps are enqueued back to back between one pair of HIP
+    events recorded on `stream` (the stream the library launches on), so the
+    per-step figure is the kernels' average duration plus any gap between
+    them; the host stays ahead of the device for kernels this long.
+    """
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         fn()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
-    return wall, ev
+    return wall, start.elapsed_time(end) / steps
 
 
 def bench_gemm(name: str, steps: int, warmup: int):

@@ -106,11 +106,7 @@ struct GemmCfg {
   static_assert(STAGES >= 2, "stages");
   static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
-  // Accumulators beyond what fits beside the fragments in 256 VGPRs are kept in
-  // AGPRs explicitly: the MFMAs are then written as inline asm with AGPR
-  // accumulator operands (the compiler otherwise places fragments in AGPRs and
-  // spills accumulators).
-  static constexpr bool AGPR_ACC = FM * FN * 16 > 128;
+  static_assert(FM * FN * 16 <= 128, "accumulators must fit beside the fragments in 256 VGPRs");
 };
 
 // ---------------------------------------------------------------------------
@@ -425,36 +421,14 @@ __device__ __forceinline__ void load_frags(const char LL_LDS* slot, int kk, int 
                            : frag_mnmajor<Cfg::BN>(sB, wn0 + 32 * j, kk, lane);
 }
 
-// One k16 step over the wave's FM x FN blocks.  `first` (wave-uniform) starts
-// the tile's sums: the MFMA then takes 0 as its C operand instead of acc.
-// AGPR_ACC: the MFMAs are volatile inline asm on AGPR accumulators, so they
-// keep program order with the other volatile asm of the kernel (DMA issue,
-// the hazard padding before the epilogue); fragments are VGPR operands
-// written by LDS reads, whose results the compiler waits for.  Back-to-back
-// MFMAs accumulating into the same registers need no padding.
+// One k16 step over the wave's FM x FN blocks of 32x32.
 template <class Cfg>
-__device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN], bool first) {
-  if constexpr (Cfg::AGPR_ACC) {
-    if (first) {
+__device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
+  for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc[i][j]) : "v"(f.a[i]), "v"(f.b[j]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(f.a[i]), "v"(f.b[j]));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-  }
+    for (int j = 0; j < Cfg::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 template <int FM, int FN>
@@ -465,26 +439,6 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-}
-
-// Accumulator element r of block (i, j) as a VGPR value.  AGPR_ACC: read with
-// an ordered asm v_accvgpr_read after acc_hazard_pad().
-template <class Cfg>
-__device__ __forceinline__ float acc_get(const f32x16& a, int r) {
-  if constexpr (Cfg::AGPR_ACC) {
-    float v;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a[r]));
-    return v;
-  } else {
-    return a[r];
-  }
-}
-
-// Wait states between the last MFMA of a tile and VALU reads of its result
-// (the longest MFMA-write -> VALU-read requirement is below 20 cycles).
-template <class Cfg>
-__device__ __forceinline__ void acc_hazard_pad() {
-  if constexpr (Cfg::AGPR_ACC) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
@@ -509,7 +463,7 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
         for (int r = 0; r < 16; ++r) {
           const int row = rowb + 32 * i + 8 * (r >> 2) + (r & 3);
           const int col = colb + 32 * j;
-          const float v = acc_get<Cfg>(acc[i][j], r);
+          const float v = acc[i][j][r];
           if (row < p.M && col < p.N) P[(int64_t)row * p.N + col] = v;
         }
     return;
@@ -524,7 +478,7 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
       const int col = colb + 32 * j;
       float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = acc_get<Cfg>(acc[i][j], r);
+      for (int r = 0; r < 16; ++r) v[r] = acc[i][j][r];
       if (bias) {
         float bv[16];
 #pragma unroll
@@ -602,7 +556,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   lds_barrier();
 
   f32x16 acc[Cfg::FM][Cfg::FN];
-  if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+  zero_acc(acc);
   Frags<Cfg> f[2];
   if (is_cons) load_frags<Cfg>(smem, 0, wm0, wn0, lane, f[0]);
 
@@ -614,7 +568,6 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   int ck = cti.kb;
   while (true) {
     char LL_LDS* cur = smem + slot * Cfg::SLOT;
-    const bool tile_first = ck == cti.kb;
     const bool tile_end = ck + 1 == cti.ke;
     const bool has_next = !tile_end || ct + stride < p.total;
     const int nslot = slot + 1 == S ? 0 : slot + 1;
@@ -636,15 +589,14 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         }
         if (is_cons && has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
       }
-      if (is_cons) mfma_step<Cfg>(f[kk & 1], acc, Cfg::AGPR_ACC && kk == 0 && tile_first);
+      if (is_cons) mfma_step<Cfg>(f[kk & 1], acc);
     }
     if (tile_end) {
       if (is_cons) {
-        acc_hazard_pad<Cfg>();
         epilogue<Cfg>(p, cti, acc, wm0, wn0, lane);
         drain = true;
       }
-      if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+      zero_acc(acc);
     }
     if (!has_next) break;
     if (tile_end) {

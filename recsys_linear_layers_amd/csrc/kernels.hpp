@@ -13,8 +13,6 @@ namespace ll {
 // adds that many loading waves, NPROD == 0 makes every wave load and compute.
 // KT is the k depth of one ring slot.
 #define LL_GEMM_KINDS(X)                                                                              \
-  X(KIND_SQ4_K64, 256, 256, 64, 2, 2, 0, 2)    /* 4 waves (1 per SIMD) 128x128 each, 2 x 64 KB */    \
-  X(KIND_SQ4_K32, 256, 256, 32, 2, 2, 0, 4)    /* same, 4 x 32 KB slots */                          \
   X(KIND_SQ8_K64, 256, 256, 64, 2, 4, 0, 2)    /* 8 waves (2 per SIMD) 128x64 each */               \
   X(KIND_SQ8_K32, 256, 256, 32, 2, 4, 0, 4)    /* same, 4 x 32 KB slots */                          \
   X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 3)    /* 4 computing 128x64 + 4 loading waves */           \

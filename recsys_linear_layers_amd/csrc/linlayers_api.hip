@@ -226,7 +226,7 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   else if (M * N <= 1024ll * 1024)
     kind = KIND_SMALL_COOP;
   else
-    kind = KIND_SQ8_K32;
+    kind = KIND_SQ8_K64;
   if (d->flags & LL_FLAG_COOPERATIVE) {
     if (kind_info(kind).nprod > 0) kind = KIND_WIDE_COOP;
   } else if (d->flags & LL_FLAG_PRODUCER_CONSUMER) {
