@@ -44,6 +44,15 @@ inline int layout_index(bool a_kmajor, bool b_kmajor) { return (a_kmajor ? 0 : 2
 // Launch `kind` for layout `layout` on `grid` workgroups.  Returns the launch status.
 hipError_t launch_gemm(int layout, int kind, const GemmKArgs& args, int grid, hipStream_t stream);
 
+// Fused linear-compression kernel (lincomp_kernel.hpp).
+struct LincompKArgs;
+struct LincompKind {
+  int bm, bn, kt, threads;
+  const char* name;
+};
+const LincompKind& lincomp_kind();
+hipError_t launch_lincomp(const LincompKArgs& args, int grid, hipStream_t stream);
+
 // Auxiliary kernels.
 hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
                               uint16_t* dst, int64_t ldp, hipStream_t stream);

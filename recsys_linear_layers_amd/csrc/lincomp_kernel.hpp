@@ -1,0 +1,348 @@
+// Fused, persistent RecSys linear-compression kernel for gfx950 (MI355X).
+//
+// What is computed (page "Meta accélère un noyau GPU d'un facteur 4 avec TLX",
+// sections "Comment le chargement des données gêne le calcul" and "Ce que
+// signifie une accélération d'un facteur quatre"): for request r and
+// candidate c the layer input is the request's user rows stacked above the
+// candidate's item rows, X = [user[r]; item[r][c]], and the output is
+// Y[r][c] = W^T . X.  The user rows are the same for every candidate of a
+// request, so their product U[r] = W[0:Nu]^T . user[r] is formed once per
+// request and reused, instead of once per candidate.
+//
+// How:
+//  * Work item = (Mo tile, D tile, request, range of candidates).  Per item
+//    the ring carries first the Nu/KT "user" slices (A = W[0:Nu] rows,
+//    B = user[r]) and then Ni/KT slices per candidate (A = W[Nu:] rows,
+//    B = item[r][c]).  The consumer waves keep U[r] in registers at the end
+//    of the user slices and start every candidate's accumulators from it, so
+//    U never goes through memory and is never rounded.
+//    Without dedup the user slices are repeated before every candidate and
+//    the accumulators start from zero (the stacked-input form).
+//  * Loading waves (NPROD) only stream slices HBM -> LDS with direct-to-LDS
+//    loads; computing waves only read fragments, run MFMAs and store Y.  The
+//    two roles run separate loops that meet at one workgroup barrier per
+//    slice, so the computing waves' global stores never enter the loading
+//    waves' vmcnt and never stall the ring.
+//  * bf16 Y is stored as bf16 pairs: a DPP swap between neighbouring lanes
+//    gives each lane two adjacent d values, so every store instruction
+//    writes whole 128-byte lines.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace ll {
+
+struct LincompKArgs {
+  const uint16_t* user;
+  const uint16_t* item;
+  const uint16_t* W;
+  void* Y;
+  int64_t su_r, su_n, si_r, si_c, si_n, sw_n, sy_r, sy_c, sy_m;
+  int64_t user_extent, item_extent, w_extent;  // elements addressable from each base pointer
+  int32_t R, C, Nu, Ni, D, Mo;
+  int32_t tiles_m, tiles_n, chunk, nchunks;    // candidates per work item, work items per request
+  int32_t nu_sl, ni_sl;                        // slices per user / per candidate phase (>= 1 for Ni)
+  int32_t total;                               // work items
+  int32_t y_bf16, dedup;
+};
+
+template <int BM_, int BN_, int KT_, int WN_, int NPROD_, int STAGES_>
+struct LincompCfg {
+  static constexpr int BM = BM_, BN = BN_, KT = KT_, KS = KT / 16;
+  static constexpr int WM = 1, WN = WN_;
+  static constexpr int NCONS = WN, NPROD = NPROD_, STAGES = STAGES_;
+  static constexpr int WAVES = NCONS + NPROD, THREADS = WAVES * 64;
+  static constexpr int FM = BM / 32, FN = BN / WN / 32;
+  static constexpr bool A_KMAJOR = false, B_KMAJOR = false;  // W^T and X are both MN-major in LDS
+  static constexpr int A_BYTES = BM * KT * 2, B_BYTES = BN * KT * 2;
+  static constexpr int SLOT = A_BYTES + B_BYTES;
+  static constexpr int LDS = STAGES * SLOT;
+  static constexpr int LOADERS = NPROD;
+  static constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / NPROD;
+  static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
+  static_assert(NPROD > 0, "the fused kernel uses separate loading waves");
+  static_assert((A_BYTES / 1024) % NPROD == 0 && (B_BYTES / 1024) % NPROD == 0, "load split");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(FM * FN * 16 * 2 <= 160, "accumulators + U must leave room for fragments");
+};
+
+// Position in a work item's slice sequence.  Both roles walk the same
+// sequence with their own copy.
+struct LcPos {
+  int t;        // work item
+  int r, c, c1; // request, current candidate, end of the item's candidates
+  int m0, n0;   // output tile origin (Mo, D)
+  bool user;    // current slice belongs to the user phase
+  int ks;       // slice index within the phase
+
+  __device__ __forceinline__ void start(const LincompKArgs& p, int t_) {
+    t = t_;
+    if (t >= p.total) return;
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int tin = t % tiles;
+    const int rc = t / tiles;
+    r = rc / p.nchunks;
+    const int ch = rc - r * p.nchunks;
+    c = ch * p.chunk;
+    c1 = min(c + p.chunk, p.C);
+    m0 = tin / p.tiles_n;  // tile indices along Mo and D
+    n0 = tin - m0 * p.tiles_n;
+    ks = 0;
+    user = p.nu_sl > 0;
+  }
+  __device__ __forceinline__ bool valid(const LincompKArgs& p) const { return t < p.total; }
+  // Last slice of the user phase (dedup: U is complete after it).
+  __device__ __forceinline__ bool user_end(const LincompKArgs& p) const { return user && ks + 1 == p.nu_sl; }
+  // Last slice of a candidate (its result is complete after it).
+  __device__ __forceinline__ bool cand_end(const LincompKArgs& p) const { return !user && ks + 1 == p.ni_sl; }
+  __device__ __forceinline__ bool item_end(const LincompKArgs& p) const { return cand_end(p) && c + 1 == c1; }
+  __device__ __forceinline__ void advance(const LincompKArgs& p, int stride) {
+    if (user) {
+      if (++ks == p.nu_sl) {
+        user = false;
+        ks = 0;
+      }
+      return;
+    }
+    if (++ks < p.ni_sl) return;
+    ks = 0;
+    if (++c < c1) {
+      user = !p.dedup && p.nu_sl > 0;
+      return;
+    }
+    start(p, t + stride);
+  }
+};
+
+// Slice origin (elements from the base pointers) and operand descriptions for
+// one slice.  rows/kvalid feed the masked path of load_tile.
+struct SliceStream {
+  i32x4 rs;
+  uint32_t soff;
+};
+
+template <class Cfg>
+__device__ __forceinline__ void lc_issue(const LincompKArgs& p, const LcPos& s, char LL_LDS* slot, int lw,
+                                         int lane, uint32_t va, uint32_t vb) {
+  const int k0 = s.ks * Cfg::KT;
+  const int kvalid = s.user ? p.Nu : p.Ni;
+  const int m0 = s.m0 * Cfg::BM, n0 = s.n0 * Cfg::BN;
+  // A = W^T: A[m][n] = W[wrow0 + n][m], MN-major with ld = sw_n.
+  OperandArgs oa;
+  oa.ld = p.sw_n;
+  oa.rows = p.Mo;
+  oa.kvalid = kvalid;
+  const int64_t wrow0 = s.user ? 0 : p.Nu;
+  const int64_t aorg = (wrow0 + k0) * p.sw_n + m0;
+  SliceStream sa;
+  sa.rs = make_rsrc(p.W + aorg, clamp_records(p.w_extent - aorg));
+  sa.soff = 0;
+  // B = X rows: user[r] or item[r][c], MN-major with ld = su_n / si_n.
+  OperandArgs ob;
+  ob.rows = p.D;
+  ob.kvalid = kvalid;
+  SliceStream sb;
+  sb.soff = 0;
+  if (s.user) {
+    ob.ld = p.su_n;
+    const int64_t borg = (int64_t)s.r * p.su_r + (int64_t)k0 * p.su_n + n0;
+    sb.rs = make_rsrc(p.user + borg, clamp_records(p.user_extent - borg));
+  } else {
+    ob.ld = p.si_n;
+    const int64_t borg = (int64_t)s.r * p.si_r + (int64_t)s.c * p.si_c + (int64_t)k0 * p.si_n + n0;
+    sb.rs = make_rsrc(p.item + borg, clamp_records(p.item_extent - borg));
+  }
+  const bool kin = k0 + Cfg::KT <= kvalid;
+  const bool fa = kin && m0 + Cfg::BM <= p.Mo;
+  const bool fb = kin && n0 + Cfg::BN <= p.D;
+  load_tile<Cfg::BM, Cfg::KT, false, Cfg::LOADERS>(oa, sa, fa, m0, k0, slot, lw, lane, va);
+  load_tile<Cfg::BN, Cfg::KT, false, Cfg::LOADERS>(ob, sb, fb, n0, k0, slot + Cfg::A_BYTES, lw, lane, vb);
+}
+
+// Swap with the neighbouring lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ float swap_pair(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF,
+                                                               false));
+}
+
+// Store the wave's FM x FN blocks of Y for candidate (r, c).  Accumulator
+// layout of v_mfma_f32_32x32x16: register q of lane l holds row
+// 8*(q/4) + 4*(l/32) + q%4, column l%32 of the 32x32 block.
+template <class Cfg>
+__device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& s,
+                                            const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wn0, int lane) {
+  const int64_t yoff = (int64_t)s.r * p.sy_r + (int64_t)s.c * p.sy_c;
+  const int mb = s.m0 * Cfg::BM + 4 * (lane >> 5);
+  const int db = s.n0 * Cfg::BN + wn0 + (lane & 31);
+  if (p.y_bf16) {
+    // Lane pair (2i, 2i+1) holds columns d, d+1 of the same rows.  After the
+    // swap the even lane owns rows q%4 in {0,1} and the odd lane rows {2,3},
+    // each as a (d, d+1) pair.
+    uint16_t* Y = (uint16_t*)p.Y + yoff;
+    const bool odd = lane & 1;
+    const int d = db - (lane & 1);
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          // even lane sends rows 2,3, odd lane sends rows 0,1
+          // The even lane sends rows 2, 3 and receives the odd lane's rows 0, 1
+          // (column d+1); the odd lane sends rows 0, 1 and receives rows 2, 3
+          // (column d).
+          const float s0 = swap_pair(odd ? v0 : v2);
+          const float s1 = swap_pair(odd ? v1 : v3);
+          float a0, a1, b0, b1;  // row ra: (a0 at d, a1 at d+1); row ra+1: (b0, b1)
+          if (!odd) {
+            a0 = v0; a1 = s0;
+            b0 = v1; b1 = s1;
+          } else {
+            a0 = s0; a1 = v2;
+            b0 = s1; b1 = v3;
+          }
+          const int ra = mb + 32 * i + 8 * g + (odd ? 2 : 0);
+          const int dd = d + 32 * j;
+          const uint32_t pa = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
+          const uint32_t pb = (uint32_t)f32_to_bf16_bits(b0) | ((uint32_t)f32_to_bf16_bits(b1) << 16);
+          if (dd < p.D) {  // D is a multiple of 8, so dd < D implies dd + 1 < D
+            if (ra < p.Mo) *(uint32_t*)(Y + (int64_t)ra * p.sy_m + dd) = pa;
+            if (ra + 1 < p.Mo) *(uint32_t*)(Y + (int64_t)(ra + 1) * p.sy_m + dd) = pb;
+          }
+        }
+  } else {
+    float* Y = (float*)p.Y + yoff;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = mb + 32 * i + 8 * (q >> 2) + (q & 3);
+          const int d = db + 32 * j;
+          if (m < p.Mo && d < p.D) Y[(int64_t)m * p.sy_m + d] = acc[i][j][q];
+        }
+  }
+}
+
+template <class Cfg>
+__device__ __forceinline__ void lc_wait(int n) {
+  if constexpr (Cfg::STAGES <= 2) {
+    wait_vmcnt<0>();
+  } else {
+    if (n <= 0) wait_vmcnt<0>();
+    else if (n == 1 || Cfg::STAGES == 3) wait_vmcnt<Cfg::LPW>();
+    else wait_vmcnt<(Cfg::STAGES - 2) * Cfg::LPW>();
+  }
+}
+
+template <class Cfg>
+__global__ void __launch_bounds__(Cfg::THREADS)
+    __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_EU, Cfg::WAVES_PER_EU)))
+    lincomp_fused(const LincompKArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS];
+  char LL_LDS* smem = (char LL_LDS*)smem_raw;
+  constexpr int S = Cfg::STAGES;
+  constexpr int KS = Cfg::KS;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int stride = gridDim.x;
+  const int first = xcd_remap(blockIdx.x, gridDim.x);
+  if (first >= p.total) return;  // uniform over the workgroup
+
+  if (wave >= Cfg::NCONS) {
+    // ---------------- loading waves ----------------
+    const int lw = wave - Cfg::NCONS;
+    const uint32_t va = TileGeom<Cfg::BM, Cfg::KT, false>::lane_off(lw, lane, (int)p.sw_n);
+    const uint32_t vbu = TileGeom<Cfg::BN, Cfg::KT, false>::lane_off(lw, lane, (int)p.su_n);
+    const uint32_t vbi = TileGeom<Cfg::BN, Cfg::KT, false>::lane_off(lw, lane, (int)p.si_n);
+    LcPos ld, cc;
+    ld.start(p, first);
+    cc.start(p, first);
+    int issued = 0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (ld.valid(p)) {
+        lc_issue<Cfg>(p, ld, smem + s * Cfg::SLOT, lw, lane, va, ld.user ? vbu : vbi);
+        ld.advance(p, stride);
+        ++issued;
+      }
+    }
+    lc_wait<Cfg>(issued - 1);
+    lds_barrier();
+    int j = 0, slot = 0;
+    while (true) {
+      const bool has_next = !cc.item_end(p) || cc.t + stride < p.total;
+      if (has_next) lc_wait<Cfg>(issued - j - 2);
+      lds_barrier();
+      if (ld.valid(p)) {
+        lc_issue<Cfg>(p, ld, smem + slot * Cfg::SLOT, lw, lane, va, ld.user ? vbu : vbi);
+        ld.advance(p, stride);
+        ++issued;
+      }
+      if (!has_next) break;
+      cc.advance(p, stride);
+      ++j;
+      slot = slot + 1 == S ? 0 : slot + 1;
+    }
+    return;
+  }
+
+  // ---------------- computing waves ----------------
+  const int wn0 = wave * (Cfg::BN / Cfg::WN);
+  f32x16 acc[Cfg::FM][Cfg::FN], u[Cfg::FM][Cfg::FN];
+  zero_acc(acc);
+  zero_acc(u);
+  Frags<Cfg> f[2];
+  lds_barrier();
+  load_frags<Cfg>(smem, 0, 0, wn0, lane, f[0]);
+  LcPos cc;
+  cc.start(p, first);
+  int slot = 0;
+  while (true) {
+    char LL_LDS* cur = smem + slot * Cfg::SLOT;
+    const bool item_end = cc.item_end(p);
+    const bool has_next = !item_end || cc.t + stride < p.total;
+    const int nslot = slot + 1 == S ? 0 : slot + 1;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) {
+        load_frags<Cfg>(cur, kk + 1, 0, wn0, lane, f[(kk + 1) & 1]);
+      } else {
+        lds_barrier();
+        if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, 0, wn0, lane, f[0]);
+      }
+      mfma_step<Cfg>(f[kk & 1], acc);
+    }
+    if (p.dedup && cc.user_end(p)) {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < Cfg::FN; ++jj) u[i][jj] = acc[i][jj];
+    }
+    if (cc.cand_end(p)) {
+      lc_epilogue<Cfg>(p, cc, acc, wn0, lane);
+      if (p.dedup) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < Cfg::FN; ++jj) acc[i][jj] = u[i][jj];
+      } else {
+        zero_acc(acc);
+      }
+    }
+    if (item_end) {
+      zero_acc(acc);
+      zero_acc(u);
+    }
+    if (!has_next) break;
+    cc.advance(p, stride);
+    slot = nslot;
+  }
+}
+
+}  // namespace ll

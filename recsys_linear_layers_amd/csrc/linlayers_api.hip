@@ -6,11 +6,13 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
 #include "../../include/linlayers.h"
 #include "kernels.hpp"
+#include "lincomp_kernel.hpp"
 
 using namespace ll;
 
@@ -390,14 +392,15 @@ static ll_status lincomp_check(const lincomp_desc* d) {
   if (d->flags & ~(uint32_t)LL_LINCOMP_NO_DEDUP) return fail(LL_ERR_INVALID_ARG, "unknown flag bits");
   if (d->y_type != LL_BF16 && d->y_type != LL_F32) return fail(LL_ERR_UNSUPPORTED, "Y must be LL_BF16 or LL_F32");
   if (d->D % 8 || d->Mo % 8) return fail(LL_ERR_INVALID_ARG, "D and Mo must be multiples of 8");
-  if (d->su_n % 8 || d->si_n % 8 || d->sw_n % 8 || d->su_r % 8 || d->si_r % 8 || d->si_c % 8)
-    return fail(LL_ERR_INVALID_ARG, "su_r, su_n, si_r, si_c, si_n, sw_n must be multiples of 8");
+  if (d->su_n % 8 || d->si_n % 8 || d->sw_n % 8 || d->su_r % 8 || d->si_r % 8 || d->si_c % 8 ||
+      d->sy_r % 8 || d->sy_c % 8 || d->sy_m % 8)
+    return fail(LL_ERR_INVALID_ARG, "every row and batch stride must be a multiple of 8");
   if (d->su_n < d->D || d->si_n < d->D || d->sw_n < d->Mo || d->sy_m < d->D)
     return fail(LL_ERR_INVALID_ARG, "row strides shorter than the rows");
   if (d->su_r < 0 || d->si_r < 0 || d->si_c < 0 || d->sy_r < 0 || d->sy_c < 0)
     return fail(LL_ERR_INVALID_ARG, "negative stride");
-  if (d->Mo > 256 || d->D >= (1 << 30) || d->R * d->C >= (1ll << 30))
-    return fail(LL_ERR_UNSUPPORTED, "Mo must be <= 256 and R*C below 2^30");
+  if (d->Mo >= (1 << 30) || d->D >= (1 << 30) || d->R * d->C >= (1ll << 30))
+    return fail(LL_ERR_UNSUPPORTED, "Mo, D and R*C must be below 2^30");
   if (d->su_n * 2 * kBK >= (1ll << 31) || d->si_n * 2 * kBK >= (1ll << 31) || d->sw_n * 2 * kBK >= (1ll << 31))
     return fail(LL_ERR_UNSUPPORTED, "row strides too large");
   return LL_OK;
@@ -407,23 +410,20 @@ ll_status lincomp_workspace_size(const lincomp_desc* d, size_t* bytes) {
   ll_status s = lincomp_check(d);
   if (s != LL_OK) return s;
   if (!bytes) return fail(LL_ERR_INVALID_ARG, "null bytes");
-  // fp32 user contribution, one [Mo][D] block per request (or per candidate without dedup).
-  const int64_t blocks = (d->flags & LL_LINCOMP_NO_DEDUP) ? d->R * d->C : d->R;
-  *bytes = (d->Nu > 0) ? align256((size_t)blocks * d->Mo * d->D * 4) : 0;
+  *bytes = 0;  // the fused kernel keeps the per-request user contribution in registers
   return ok();
 }
 
 ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item, const void* W, void* Y,
                       void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
   ll_status s = lincomp_check(d);
   if (s != LL_OK) return s;
   if (d->R == 0 || d->C == 0 || d->Mo == 0 || d->D == 0) return ok();
   if (!Y || !W || (d->Nu > 0 && !user) || (d->Ni > 0 && !item)) return fail(LL_ERR_INVALID_ARG, "null pointer");
-  if (((uintptr_t)user & 15) || ((uintptr_t)item & 15) || ((uintptr_t)W & 15))
-    return fail(LL_ERR_INVALID_ARG, "user, item and W must be 16-byte aligned");
-  size_t need = 0;
-  lincomp_workspace_size(d, &need);
-  if (ws_bytes < need || (need > 0 && !ws)) return fail(LL_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  if (((uintptr_t)user & 15) || ((uintptr_t)item & 15) || ((uintptr_t)W & 15) || ((uintptr_t)Y & 15))
+    return fail(LL_ERR_INVALID_ARG, "user, item, W and Y must be 16-byte aligned");
   const DeviceInfo* info = nullptr;
   int dev = 0;
   s = current_device(&dev, &info);
@@ -436,111 +436,56 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
                                                                                       (d->Nu - 1) * d->su_n + d->D) * 2)})) ||
       (d->Ni > 0 && overlaps(sy, Span{(uintptr_t)item, (uintptr_t)item + (uintptr_t)(((d->R - 1) * d->si_r +
                                                                                       (d->C - 1) * d->si_c +
-                                                                                      (d->Ni - 1) * d->si_n + d->D) * 2)})) ||
-      (need > 0 && overlaps(sy, Span{(uintptr_t)ws, (uintptr_t)ws + need})))
-    return fail(LL_ERR_INVALID_ARG, "Y overlaps an input or the workspace");
+                                                                                      (d->Ni - 1) * d->si_n + d->D) * 2)})))
+    return fail(LL_ERR_INVALID_ARG, "Y overlaps an input");
 
-  hipStream_t st = (hipStream_t)stream;
-  const bool dedup = !(d->flags & LL_LINCOMP_NO_DEDUP);
-  const int kind = KIND_LINCOMP_PC;
-  const KindInfo& ki = kind_info(kind);
-  const int tiles_m = (int)((d->Mo + ki.bm - 1) / ki.bm);
-  const int tiles_n = (int)((d->D + ki.bn - 1) / ki.bn);
-  const int64_t slots = (int64_t)info->cus * occupancy_for(kind);
-  float* U = (float*)ws;
-  hipError_t e;
-
-  // Phase 1: the user rows' contribution U = W[0:Nu]^T . user, once per request
-  // (or, without dedup, once per candidate, as if the rows were repeated).
-  if (d->Nu > 0) {
-    GemmKArgs k;
-    memset(&k, 0, sizeof k);
-    k.a.ptr = (const uint16_t*)W;  // A[m][n] = W[n][m]: M-contiguous
-    k.a.ld = d->sw_n;
-    k.a.rows = (int32_t)d->Mo;
-    k.a.kvalid = (int32_t)d->Nu;
-    k.a.extent = (d->Nu - 1) * d->sw_n + d->Mo;
-    k.b.ptr = (const uint16_t*)user;  // B[n][dd] = user[r][n][dd]: N-contiguous
-    k.b.ld = d->su_n;
-    k.b.rows = (int32_t)d->D;
-    k.b.kvalid = (int32_t)d->Nu;
-    k.b.bo = d->su_r;
-    k.b.bi = 0;
-    k.b.extent = (d->R - 1) * d->su_r + (d->Nu - 1) * d->su_n + d->D;
-    k.c = U;
-    k.ldcm = d->D;
-    k.ldcn = 1;
-    k.cbo = dedup ? d->Mo * d->D : d->C * d->Mo * d->D;
-    k.cbi = dedup ? 0 : d->Mo * d->D;
-    k.M = (int32_t)d->Mo;
-    k.N = (int32_t)d->D;
-    k.bdiv = dedup ? 1 : (int32_t)d->C;
-    k.batches = (int32_t)(dedup ? d->R : d->R * d->C);
-    k.splits = 1;
-    k.kiters = (int32_t)((d->Nu + ki.kt - 1) / ki.kt);
-    k.kps = k.kiters;
-    k.tiles_m = tiles_m;
-    k.tiles_n = tiles_n;
-    k.group_m = 1;
-    k.total = k.batches * tiles_m * tiles_n;
-    const int grid = (int)(k.total < slots ? k.total : slots);
-    e = launch_gemm(layout_index(false, false), kind, k, grid, st);
-    if (e != hipSuccess) return hip_fail(e, "lincomp user-phase launch");
-  }
-
-  // Phase 2: Y[r][c] = U + W[Nu:]^T . item[r][c]; U enters as the epilogue's fp32 bias.
-  GemmKArgs k;
+  const LincompKind& lk = lincomp_kind();
+  LincompKArgs k;
   memset(&k, 0, sizeof k);
-  k.a.ptr = (const uint16_t*)W + d->Nu * d->sw_n;
-  k.a.ld = d->sw_n;
-  k.a.rows = (int32_t)d->Mo;
-  k.a.kvalid = (int32_t)d->Ni;
-  k.a.extent = d->Ni > 0 ? (d->Ni - 1) * d->sw_n + d->Mo : 0;
-  k.b.ptr = (const uint16_t*)item;
-  k.b.ld = d->si_n;
-  k.b.rows = (int32_t)d->D;
-  k.b.kvalid = (int32_t)d->Ni;
-  k.b.bo = d->si_r;
-  k.b.bi = d->si_c;
-  k.b.extent = d->Ni > 0 ? (d->R - 1) * d->si_r + (d->C - 1) * d->si_c + (d->Ni - 1) * d->si_n + d->D : 0;
-  k.c = Y;
-  k.ldcm = d->sy_m;
-  k.ldcn = 1;
-  k.cbo = d->sy_r;
-  k.cbi = d->sy_c;
-  k.c_bf16 = d->y_type == LL_BF16;
-  if (d->Nu > 0) {
-    k.bias = U;
-    k.bias_m = d->D;
-    k.bias_n = 1;
-    k.bias_bo = dedup ? d->Mo * d->D : d->C * d->Mo * d->D;
-    k.bias_bi = dedup ? 0 : d->Mo * d->D;
-  }
-  k.M = (int32_t)d->Mo;
-  k.N = (int32_t)d->D;
-  k.bdiv = (int32_t)d->C;
-  k.batches = (int32_t)(d->R * d->C);
-  k.splits = 1;
-  k.kiters = (int32_t)((d->Ni + ki.kt - 1) / ki.kt);
-  k.kps = k.kiters;
-  k.tiles_m = tiles_m;
-  k.tiles_n = tiles_n;
-  k.group_m = 1;
-  k.total = k.batches * tiles_m * tiles_n;
-  if (k.kiters == 0) {
-    // No item rows: Y = U (rounded).  A zero-iteration tile still runs its epilogue.
-    k.kiters = 1;
-    k.kps = 1;
-    k.a.kvalid = 0;
-    k.b.kvalid = 0;
-    k.a.ptr = (const uint16_t*)W;
-    k.b.ptr = (const uint16_t*)W;
-    k.a.extent = 0;
-    k.b.extent = 0;
-  }
-  const int grid = (int)(k.total < slots ? k.total : slots);
-  e = launch_gemm(layout_index(false, false), kind, k, grid, st);
-  if (e != hipSuccess) return hip_fail(e, "lincomp candidate-phase launch");
+  k.user = (const uint16_t*)user;
+  k.item = (const uint16_t*)item;
+  k.W = (const uint16_t*)W;
+  k.Y = Y;
+  k.su_r = d->su_r;
+  k.su_n = d->su_n;
+  k.si_r = d->si_r;
+  k.si_c = d->si_c;
+  k.si_n = d->si_n;
+  k.sw_n = d->sw_n;
+  k.sy_r = d->sy_r;
+  k.sy_c = d->sy_c;
+  k.sy_m = d->sy_m;
+  k.user_extent = d->Nu > 0 ? (d->R - 1) * d->su_r + (d->Nu - 1) * d->su_n + d->D : 0;
+  k.item_extent = d->Ni > 0 ? (d->R - 1) * d->si_r + (d->C - 1) * d->si_c + (d->Ni - 1) * d->si_n + d->D : 0;
+  k.w_extent = (d->Nu + d->Ni - 1) * d->sw_n + d->Mo;
+  k.R = (int32_t)d->R;
+  k.C = (int32_t)d->C;
+  k.Nu = (int32_t)d->Nu;
+  k.Ni = (int32_t)d->Ni;
+  k.D = (int32_t)d->D;
+  k.Mo = (int32_t)d->Mo;
+  k.tiles_m = (int32_t)((d->Mo + lk.bm - 1) / lk.bm);
+  k.tiles_n = (int32_t)((d->D + lk.bn - 1) / lk.bn);
+  k.nu_sl = (int32_t)((d->Nu + lk.kt - 1) / lk.kt);
+  // A candidate with no item rows still needs one (all-zero) slice so that its
+  // result (the user contribution alone) is written.
+  k.ni_sl = d->Ni > 0 ? (int32_t)((d->Ni + lk.kt - 1) / lk.kt) : 1;
+  // Candidates per work item: one workgroup per CU, and the user block is
+  // recomputed only once per work item.
+  const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n;
+  const int64_t per_req = std::max<int64_t>(1, (info->cus + d->R * tiles - 1) / (d->R * tiles));
+  int64_t chunk = (d->C + per_req - 1) / per_req;
+  if (chunk < 1) chunk = 1;
+  k.chunk = (int32_t)chunk;
+  k.nchunks = (int32_t)((d->C + chunk - 1) / chunk);
+  const int64_t total = tiles * d->R * k.nchunks;
+  if (total >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "too many work items");
+  k.total = (int32_t)total;
+  k.y_bf16 = d->y_type == LL_BF16;
+  k.dedup = !(d->flags & LL_LINCOMP_NO_DEDUP);
+  const int grid = (int)std::min<int64_t>(total, info->cus);
+  hipError_t e = launch_lincomp(k, grid, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "lincomp launch");
   return ok();
 }
 

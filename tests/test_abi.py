@@ -111,12 +111,13 @@ def _lc(**kw):
 
 def test_lincomp_workspace_and_checks():
     import recsys_linear_layers_amd as ll
-    assert ll.lincomp_workspace_size(_lc()) == 2 * 64 * 256 * 4
-    assert ll.lincomp_workspace_size(_lc(flags=ll.LL_LINCOMP_NO_DEDUP)) == 2 * 3 * 64 * 256 * 4
+    # the fused kernel keeps the per-request user contribution in registers
+    assert ll.lincomp_workspace_size(_lc()) == 0
+    assert ll.lincomp_workspace_size(_lc(flags=ll.LL_LINCOMP_NO_DEDUP)) == 0
     assert ll.lincomp_workspace_size(_lc(Nu=0)) == 0
     n = ctypes.c_size_t()
     for kw in (dict(R=-1), dict(D=12), dict(su_n=12), dict(flags=8), dict(y_type=5), dict(si_c=4),
-               dict(sw_n=8)):
+               dict(sw_n=8), dict(sy_m=260)):
         st = ll._lib.lincomp_workspace_size(ctypes.byref(_lc(**kw)), ctypes.byref(n))
         assert st != ll.LL_OK, kw
     st = ll._lib.lincomp_run(None, None, None, None, None, None, 0, None)
