@@ -3,8 +3,8 @@
 // What is computed: C = A.B (fp32 accumulation) over strided operands, as the
 // listings on "Triton 3.7 permite extender el compilador de GPU sin forks"
 // state the problem (sections "NVIDIA H100 (Hopper): GEMM persistente" and
-// "AMD MI350: GEMM segmentado"), optionally batched, split along K, and with a
-// per-batch fp32 addend in the epilogue (used by the linear-compression layer).
+// "AMD MI350: GEMM segmentado"), optionally split along K when the tiles
+// alone cannot fill the chip.
 //
 // How (gfx950-specific design; the pages' TMA/WGMMA and register-staged
 // mechanisms are not used):
@@ -28,7 +28,7 @@
 //    read while the last k16 step's MFMAs run.  With NPROD > 0 the loading
 //    and computing roles are separate waves; with NPROD == 0 every wave does
 //    both.  The ring runs across tile boundaries of the persistent loop.
-//  * Persistent grid over (batch, k-split, tile) work items in grouped
+//  * Persistent grid over (k-split, tile) work items in grouped
 //    (GROUP_M) order, with workgroup ids remapped so that the consecutive
 //    work items that share operand panels land on the same XCD (and its L2).
 #pragma once
@@ -50,37 +50,27 @@ constexpr uint32_t kOOB = 0x80000000u;     // byte offset beyond every num_recor
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
 struct OperandArgs {
-  const uint16_t* ptr;  // element (0, 0) of batch 0
+  const uint16_t* ptr;  // element (0, 0)
   int64_t ld;           // K-major: elements between MN rows; MN-major: elements between k rows
   int32_t rows;         // extent along M (A) or N (B)
   int32_t kvalid;       // k extent holding data; K-major operands: a multiple of 8
-  int64_t bo, bi;       // batch offset of item b: (b / bdiv) * bo + (b % bdiv) * bi
   int64_t extent;       // elements addressable from ptr (clamps num_records)
 };
 
 struct GemmKArgs {
   OperandArgs a, b;
   void* c;
-  int64_t ldcm, ldcn, cbo, cbi;
-  const float* bias;  // optional fp32 addend, same batch/row/col indexing scheme as C
-  int64_t bias_m, bias_n, bias_bo, bias_bi;
+  int64_t ldcm, ldcn;
   float* partial;     // split-K partials [splits][M][N], or null
   int32_t M, N;
   int32_t c_bf16;
-  int32_t bdiv;
-  int32_t batches, splits, kiters, kps;  // kiters, kps in units of KT
+  int32_t splits, kiters, kps;  // kiters, kps in units of KT
   int32_t tiles_m, tiles_n, group_m;
   int32_t total;
 };
 
-template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,
-          bool BATCHED_ = false>
+template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_>
 struct GemmCfg {
-  // BATCHED: work items run over batches (operand/C batch offsets) and the
-  // epilogue may add an fp32 addend; otherwise work items run over k-splits
-  // and the epilogue may write split-K partials.  Kernel arguments a kind does
-  // not use are never read, which keeps them out of scalar registers.
-  static constexpr bool BATCHED = BATCHED_;
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int KT = KT_;              // k elements per ring slot (32 or 64)
   static constexpr int KS = KT / 16;          // k16 MFMA steps per slot
@@ -158,22 +148,37 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nrec) {
 // (v_readfirstlane building the descriptor, v_readlane restoring a spilled
 // SGPR) needs 5 wait states before a VMEM instruction reads that SGPR, and an
 // SALU write of M0 needs 1 before an LDS-DMA load.  The s_nop 4 covers both.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
+  if constexpr (NT)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+                 : "memory");
+  else
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+                 : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const char LL_LDS* p) { return (uint32_t)(uintptr_t)p; }
 
 // One direct-to-LDS load with a wave-uniform byte offset added (soffset);
-// same hazard padding as dma16.
+// same hazard padding as dma16.  NT marks data that is read once (the
+// non-temporal cache hint), so that it does not displace reused data in L2.
+template <bool NT = false>
 __device__ __forceinline__ void dma16s(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
-               : "memory");
+  if constexpr (NT)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
+  else
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
 }
 
 // Issue this wave's share of the 1-KB direct-to-LDS loads of one operand tile
@@ -210,7 +215,7 @@ struct TileGeom {
   }
 };
 
-template <int R, int KT, bool KMAJ, int NL, class Stream>
+template <int R, int KT, bool KMAJ, int NL, class Stream, bool NT = false>
 __device__ __forceinline__ void load_tile(const OperandArgs& op, const Stream& o, bool fast, int mn0, int k0,
                                           char LL_LDS* dst, int lw, int lane, uint32_t vfast) {
   using G = TileGeom<R, KT, KMAJ>;
@@ -224,7 +229,7 @@ __device__ __forceinline__ void load_tile(const OperandArgs& op, const Stream& o
       // vfast is lane_off(lw); other residues are recomputed (PER > NL only).
       const uint32_t voff = (NL % G::PER == 0) ? vfast : G::lane_off(q, lane, ld);
       const uint32_t soff = o.soff + (uint32_t)(q * G::RPQ) * (uint32_t)ld * 2u;
-      dma16s(o.rs, dst0 + q * 1024, voff, soff);
+      dma16s<NT>(o.rs, dst0 + q * 1024, voff, soff);
     }
   } else {
     // Lanes outside the matrix: offset beyond num_records (the whole offset
@@ -245,7 +250,7 @@ __device__ __forceinline__ void load_tile(const OperandArgs& op, const Stream& o
         const bool ok = (k0 + kr < op.kvalid) && (mn0 + lc * 8 < op.rows);
         voff = ok ? o.soff + (uint32_t)(kr * ld + lc * 8) * 2u : kOOB;
       }
-      dma16(o.rs, dst0 + q * 1024, voff);
+      dma16<NT>(o.rs, dst0 + q * 1024, voff);
     }
   }
 }
@@ -293,7 +298,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 struct TileInfo {
-  int b, ks, m0, n0, kb, ke;
+  int ks, m0, n0, kb, ke;
 };
 
 template <class Cfg>
@@ -302,17 +307,9 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmKArgs& p, int t) {
   const int tin = t % tiles;
   const int rest = t / tiles;
   TileInfo ti;
-  if constexpr (Cfg::BATCHED) {
-    ti.ks = 0;
-    ti.b = rest;
-    ti.kb = 0;
-    ti.ke = p.kiters;
-  } else {
-    ti.ks = rest;
-    ti.b = 0;
-    ti.kb = rest * p.kps;
-    ti.ke = min(ti.kb + p.kps, p.kiters);
-  }
+  ti.ks = rest;
+  ti.kb = rest * p.kps;
+  ti.ke = min(ti.kb + p.kps, p.kiters);
   const int per_group = p.group_m * p.tiles_n;
   const int gid = tin / per_group;
   const int first_m = gid * p.group_m;
@@ -330,10 +327,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   return (bid & 7) * (grid >> 3) + (bid >> 3);
 }
 
-__device__ __forceinline__ int64_t batch_off(int b, int bdiv, int64_t bo, int64_t bi) {
-  return (int64_t)(b / bdiv) * bo + (int64_t)(b % bdiv) * bi;
-}
-
 // Loading side of the pipeline.  Per operand: a buffer descriptor based at
 // the work item's tile origin at slice `k0s` and a running wave-uniform byte
 // offset along k, so that each slice costs one scalar add per operand.  The
@@ -348,16 +341,14 @@ struct OpStream {
 template <class Cfg>
 struct Loader {
   int t, k, ke;  // work item, next slice, end slice (units of KT)
-  int b, m0, n0;
+  int m0, n0;
   bool rows_in;  // both operand tiles lie inside the matrix along M and N
   OpStream a, bo;
 
   template <int R, bool KMAJ>
-  __device__ static __forceinline__ void open(OpStream& o, const OperandArgs& op, int b, int bdiv, int mn0,
-                                              int ks) {
-    int64_t origin = KMAJ ? (int64_t)mn0 * op.ld + (int64_t)ks * Cfg::KT
-                          : (int64_t)ks * Cfg::KT * op.ld + mn0;
-    if constexpr (Cfg::BATCHED) origin += batch_off(b, bdiv, op.bo, op.bi);
+  __device__ static __forceinline__ void open(OpStream& o, const OperandArgs& op, int mn0, int ks) {
+    const int64_t origin = KMAJ ? (int64_t)mn0 * op.ld + (int64_t)ks * Cfg::KT
+                                : (int64_t)ks * Cfg::KT * op.ld + mn0;
     o.rs = make_rsrc(op.ptr + origin, clamp_records(op.extent - origin));
     o.soff = 0;
     o.k0s = ks;
@@ -369,12 +360,11 @@ struct Loader {
     const TileInfo ti = decode_tile<Cfg>(p, t);
     k = ti.kb;
     ke = ti.ke;
-    b = ti.b;
     m0 = ti.m0;
     n0 = ti.n0;
     rows_in = m0 + Cfg::BM <= p.a.rows && n0 + Cfg::BN <= p.b.rows;
-    open<Cfg::BM, Cfg::A_KMAJOR>(a, p.a, b, p.bdiv, m0, k);
-    open<Cfg::BN, Cfg::B_KMAJOR>(bo, p.b, b, p.bdiv, n0, k);
+    open<Cfg::BM, Cfg::A_KMAJOR>(a, p.a, m0, k);
+    open<Cfg::BN, Cfg::B_KMAJOR>(bo, p.b, n0, k);
   }
 
   __device__ __forceinline__ bool valid(const GemmKArgs& p) const { return t < p.total; }
@@ -396,8 +386,8 @@ struct Loader {
     }
     a.soff += Cfg::A_KMAJOR ? Cfg::KT * 2u : (uint32_t)(Cfg::KT * 2) * (uint32_t)p.a.ld;
     bo.soff += Cfg::B_KMAJOR ? Cfg::KT * 2u : (uint32_t)(Cfg::KT * 2) * (uint32_t)p.b.ld;
-    if (a.soff >= (1u << 30)) open<Cfg::BM, Cfg::A_KMAJOR>(a, p.a, b, p.bdiv, m0, k);
-    if (bo.soff >= (1u << 30)) open<Cfg::BN, Cfg::B_KMAJOR>(bo, p.b, b, p.bdiv, n0, k);
+    if (a.soff >= (1u << 30)) open<Cfg::BM, Cfg::A_KMAJOR>(a, p.a, m0, k);
+    if (bo.soff >= (1u << 30)) open<Cfg::BN, Cfg::B_KMAJOR>(bo, p.b, n0, k);
   }
 };
 
@@ -453,7 +443,7 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
                                          int lane) {
   const int colb = ti.n0 + wn0 + (lane & 31);
   const int rowb = ti.m0 + wm0 + 4 * (lane >> 5);
-  if (!Cfg::BATCHED && p.partial) {
+  if (p.partial) {
     float* P = p.partial + (int64_t)ti.ks * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
@@ -468,42 +458,25 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
         }
     return;
   }
-  const int64_t coff = Cfg::BATCHED ? batch_off(ti.b, p.bdiv, p.cbo, p.cbi) : 0;
-  const float* bias = Cfg::BATCHED ? p.bias : nullptr;
-  const int64_t boff = bias ? batch_off(ti.b, p.bdiv, p.bias_bo, p.bias_bi) : 0;
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int col = colb + 32 * j;
-      float v[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = acc[i][j][r];
-      if (bias) {
-        float bv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rowb + 32 * i + 8 * (r >> 2) + (r & 3);
-          bv[r] = (row < p.M && col < p.N) ? bias[boff + row * p.bias_m + col * p.bias_n] : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] += bv[r];
-      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = rowb + 32 * i + 8 * (r >> 2) + (r & 3);
         if (row < p.M && col < p.N) {
-          const int64_t o = coff + (int64_t)row * p.ldcm + (int64_t)col * p.ldcn;
+          const int64_t o = (int64_t)row * p.ldcm + (int64_t)col * p.ldcn;
           if (p.c_bf16)
-            ((uint16_t*)p.c)[o] = f32_to_bf16_bits(v[r]);
+            ((uint16_t*)p.c)[o] = f32_to_bf16_bits(acc[i][j][r]);
           else
-            ((float*)p.c)[o] = v[r];
+            ((float*)p.c)[o] = acc[i][j][r];
         }
       }
     }
 }
 
-// s_waitcnt vmcnt(n * LPW) for a wave-uniform n in [0, S-2].
 template <class Cfg>
 __device__ __forceinline__ void wait_slices(int n) {
   if constexpr (Cfg::STAGES <= 2) {

@@ -18,8 +18,7 @@ namespace ll {
   X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 3)    /* 4 computing 128x64 + 4 loading waves */           \
   X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 3)  /* 4 waves 128x64, load + compute */                 \
   X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 3)    /* skinny M: 4 computing 64x128 + 4 loading */       \
-  X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 3) /* small problems: 4 waves 64x64 */                  \
-  X(KIND_LINCOMP_PC, 64, 256, 64, 1, 4, 4, 3)  /* one 64xD candidate block: 4 + 4 waves */
+  X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 3) /* small problems: 4 waves 64x64 */
 
 enum KernelKind {
 #define LL_KIND_ENUM(name, ...) name,
@@ -39,7 +38,7 @@ inline int layout_index(bool a_kmajor, bool b_kmajor) { return (a_kmajor ? 0 : 2
 
 // Launch switch over every kind for one operand layout (instantiated once per layout).
 #define LL_KIND_CASE(name, bm, bn, kt, wm, wn, np, st) \
-  case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK, name == KIND_LINCOMP_PC>>(a, grid, s);
+  case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK>>(a, grid, s);
 
 // Launch `kind` for layout `layout` on `grid` workgroups.  Returns the launch status.
 hipError_t launch_gemm(int layout, int kind, const GemmKArgs& args, int grid, hipStream_t stream);

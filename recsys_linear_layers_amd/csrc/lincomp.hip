@@ -1,21 +1,52 @@
 // Instantiation and launch of the fused linear-compression kernel.
+#include <stdlib.h>
+
 #include "kernels.hpp"
 #include "lincomp_kernel.hpp"
 
 namespace ll {
 
-// 64 (Mo) x 256 (D) output tile, 64-deep slices, 4 computing waves (64 x 64
-// each) + 4 loading waves, 3 ring slots (120 KB of LDS).
-using LincompMain = LincompCfg<64, 256, 64, 4, 4, 3>;
+// Default: 64 (Mo) x 256 (D) output tile, 64-deep slices, 4 computing waves
+// (64 x 64 each) + 4 loading waves, 3 ring slots (120 KB of LDS).
+// Configurations X(BM, BN, KT, computing waves, loading waves, ring slots); the
+// first is the default, LL_LINCOMP_CFG=<index> selects another (sweeps).
+#define LL_LINCOMP_CFGS(X) \
+  X(64, 256, 64, 4, 4, 3)  \
+  X(64, 256, 64, 4, 4, 4)  \
+  X(64, 256, 32, 4, 4, 4)  \
+  X(64, 256, 32, 4, 4, 6)  \
+  X(64, 256, 64, 4, 2, 3)  \
+  X(64, 256, 32, 4, 2, 7)
+
+static int cfg_index() {
+  static const int idx = [] {
+    const char* e = getenv("LL_LINCOMP_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  return idx;
+}
 
 const LincompKind& lincomp_kind() {
-  static const LincompKind k = {LincompMain::BM, LincompMain::BN, LincompMain::KT, LincompMain::THREADS,
-                                "lincomp_fused_64x256x64_s3_4c4p"};
-  return k;
+#define LL_LC_KIND(bm, bn, kt, nc, np, st) {bm, bn, kt, (nc + np) * 64, "lincomp_" #bm "x" #bn "x" #kt "_s" #st "_" #nc "c" #np "p"},
+  static const LincompKind kinds[] = {LL_LINCOMP_CFGS(LL_LC_KIND)};
+#undef LL_LC_KIND
+  const int n = (int)(sizeof kinds / sizeof kinds[0]);
+  const int i = cfg_index();
+  return kinds[i >= 0 && i < n ? i : 0];
 }
 
 hipError_t launch_lincomp(const LincompKArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(lincomp_fused<LincompMain>, dim3(grid), dim3(LincompMain::THREADS), 0, s, a);
+  int i = 0;
+#define LL_LC_LAUNCH(bm, bn, kt, nc, np, st)                                                        \
+  if (cfg_index() == i++) {                                                                        \
+    using C = LincompCfg<bm, bn, kt, nc, np, st>;                                                  \
+    hipLaunchKernelGGL(lincomp_fused<C>, dim3(grid), dim3(C::THREADS), 0, s, a);                   \
+    return hipGetLastError();                                                                      \
+  }
+  LL_LINCOMP_CFGS(LL_LC_LAUNCH)
+#undef LL_LC_LAUNCH
+  using C = LincompCfg<64, 256, 64, 4, 4, 3>;
+  hipLaunchKernelGGL(lincomp_fused<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ struct LincompCfg {
   static_assert(NPROD > 0, "the fused kernel uses separate loading waves");
   static_assert((A_BYTES / 1024) % NPROD == 0 && (B_BYTES / 1024) % NPROD == 0, "load split");
   static_assert(LDS <= 160 * 1024, "LDS");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(STAGES >= 2 && STAGES <= 8, "stages");
   static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
   static_assert(FM * FN * 16 * 2 <= 160, "accumulators + U must leave room for fragments");
 };
@@ -158,7 +158,9 @@ __device__ __forceinline__ void lc_issue(const LincompKArgs& p, const LcPos& s, 
   const bool fa = kin && m0 + Cfg::BM <= p.Mo;
   const bool fb = kin && n0 + Cfg::BN <= p.D;
   load_tile<Cfg::BM, Cfg::KT, false, Cfg::LOADERS>(oa, sa, fa, m0, k0, slot, lw, lane, va);
-  load_tile<Cfg::BN, Cfg::KT, false, Cfg::LOADERS>(ob, sb, fb, n0, k0, slot + Cfg::A_BYTES, lw, lane, vb);
+  // user and item rows are read once: non-temporal hint
+  load_tile<Cfg::BN, Cfg::KT, false, Cfg::LOADERS, SliceStream, true>(ob, sb, fb, n0, k0, slot + Cfg::A_BYTES, lw,
+                                                                       lane, vb);
 }
 
 // Swap with the neighbouring lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
@@ -229,15 +231,20 @@ __device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& 
   }
 }
 
-template <class Cfg>
-__device__ __forceinline__ void lc_wait(int n) {
-  if constexpr (Cfg::STAGES <= 2) {
+// s_waitcnt vmcnt(min(n, MAX) * LPW) for a wave-uniform n >= 0: at most n
+// slices of this wave's loads may stay in flight.
+template <class Cfg, int MAX>
+__device__ __forceinline__ void lc_wait_upto(int n) {
+  if constexpr (MAX <= 0) {
     wait_vmcnt<0>();
   } else {
-    if (n <= 0) wait_vmcnt<0>();
-    else if (n == 1 || Cfg::STAGES == 3) wait_vmcnt<Cfg::LPW>();
-    else wait_vmcnt<(Cfg::STAGES - 2) * Cfg::LPW>();
+    if (n >= MAX) wait_vmcnt<MAX * Cfg::LPW>();
+    else lc_wait_upto<Cfg, MAX - 1>(n);
   }
+}
+template <class Cfg>
+__device__ __forceinline__ void lc_wait(int n) {
+  lc_wait_upto<Cfg, Cfg::STAGES - 1>(n);
 }
 
 template <class Cfg>

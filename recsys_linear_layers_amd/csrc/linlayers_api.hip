@@ -164,8 +164,6 @@ void fill_operand_args(OperandArgs* oa, const void* ptr, const OperandPlan& op, 
     oa->extent = op.kmajor ? (rows - 1) * op.ld + K : (K - 1) * op.ld + rows;
   }
   oa->rows = (int32_t)rows;
-  oa->bo = 0;
-  oa->bi = 0;
 }
 
 }  // namespace
@@ -356,8 +354,6 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
   k.M = (int32_t)d.M;
   k.N = (int32_t)d.N;
   k.c_bf16 = cbf;
-  k.bdiv = 1;
-  k.batches = 1;
   k.splits = p->splits;
   k.kiters = p->kiters;
   k.kps = p->kps;
