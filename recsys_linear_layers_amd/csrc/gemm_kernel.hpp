@@ -64,6 +64,7 @@ struct GemmKArgs {
   float* partial;     // split-K partials [splits][M][N], or null
   int32_t M, N;
   int32_t c_bf16;
+  int32_t c_fast;               // 1: no partial, ldcn == 1, ldcm even, C 4-byte aligned (epilogue_fast)
   int32_t splits, kiters, kps;  // kiters, kps in units of KT
   int32_t tiles_m, tiles_n, group_m;
   int32_t total;
@@ -96,7 +97,12 @@ struct GemmCfg {
   static_assert(STAGES >= 2, "stages");
   static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
-  static_assert(FM * FN * 16 <= 128, "accumulators must fit beside the fragments in 256 VGPRs");
+  // More accumulators than fit beside the fragments in 256 VGPRs are kept in
+  // AGPRs explicitly: the MFMAs are then inline asm with AGPR accumulator
+  // operands (left to itself the compiler places fragments in AGPRs and
+  // spills accumulators).
+  static constexpr bool AGPR_ACC = FM * FN * 16 > 128;
+  static_assert(!AGPR_ACC || WAVES_PER_EU == 1, "AGPR accumulators need one wave per SIMD");
 };
 
 // ---------------------------------------------------------------------------
@@ -411,14 +417,64 @@ __device__ __forceinline__ void load_frags(const char LL_LDS* slot, int kk, int 
                            : frag_mnmajor<Cfg::BN>(sB, wn0 + 32 * j, kk, lane);
 }
 
-// One k16 step over the wave's FM x FN blocks of 32x32.
+// One k16 step over the wave's FM x FN blocks of 32x32.  `first`
+// (wave-uniform) starts the tile's sums: the MFMA then takes 0 as its C
+// operand.  Without AGPR_ACC the accumulators are zeroed separately and
+// `first` is ignored.
+//
+// AGPR_ACC: volatile inline asm on AGPR accumulators, so the MFMAs keep
+// program order with the kernel's other volatile asm (LDS DMA, the padding
+// before the epilogue).  The compiler does not pad hazards in front of an
+// asm MFMA: a VALU write of a fragment register (a v_mov assembling the two
+// halves of a transposed fragment) needs 2 wait states before an MFMA reads
+// it, so each MFMA carries an s_nop 1, which costs nothing while the previous
+// MFMA occupies the matrix pipe.  Back-to-back MFMAs accumulating into the
+// same registers need no padding.
 template <class Cfg>
-__device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+__device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN], bool first) {
+  if constexpr (Cfg::AGPR_ACC) {
+    if (first) {
 #pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i)
+      for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < Cfg::FN; ++j)
+          asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                       : "=a"(acc[i][j])
+                       : "v"(f.a[i]), "v"(f.b[j]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+          asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+a"(acc[i][j])
+                       : "v"(f.a[i]), "v"(f.b[j]));
+    }
+  } else {
+    (void)first;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Between the last MFMA of a tile and reads of its result: the longest
+// MFMA-write -> VALU-read requirement is below 20 wait states.  Each block
+// passes through a volatile asm that takes it as an in/out AGPR operand, so
+// no read of any block can be scheduled before the padding (AGPR_ACC only;
+// the compiler pads builtin MFMAs itself).
+template <class Cfg>
+__device__ __forceinline__ void acc_hazard_pad(f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+  if constexpr (Cfg::AGPR_ACC) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+        if (i + j > 0) asm volatile("" : "+a"(acc[i][j]));
+  }
 }
 
 template <int FM, int FN>
@@ -435,12 +491,68 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
+// Swap with the neighbouring lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ float swap_pair(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF,
+                                                               false));
+}
+
+// Epilogue for a tile that lies wholly inside C, with C row-major
+// (ldcn == 1) and no split-K.  Row bases are wave-uniform (scalar
+// registers); each lane keeps one 32-bit element offset.  bf16 C: the lane
+// pair holding columns d, d+1 swaps values so that each lane writes one
+// 4-byte (d, d+1) pair per row - whole 128-byte lines, half the stores.
+template <class Cfg>
+__device__ __forceinline__ void epilogue_fast(const GemmKArgs& p, const TileInfo& ti,
+                                              const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wm0, int wn0,
+                                              int lane) {
+  const int row0 = ti.m0 + wm0;  // wave-uniform
+  const int half = lane >> 5;
+  if (p.c_bf16) {
+    const bool odd = lane & 1;
+    const int col = ti.n0 + wn0 + (lane & 30);
+    // lane-dependent part: row offset 4*half (+2 for the odd lane), column
+    const int loff = (4 * half + (odd ? 2 : 0)) * (int)p.ldcm + col;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint16_t* rowp = (uint16_t*)p.c + (int64_t)(row0 + 32 * i + 8 * g) * p.ldcm;
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
+          const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          // the even lane sends rows 2, 3 and receives the odd lane's rows 0, 1
+          // (column d+1); the odd lane sends rows 0, 1 and receives rows 2, 3
+          const float s0 = swap_pair(odd ? v0 : v2);
+          const float s1 = swap_pair(odd ? v1 : v3);
+          const float a0 = odd ? s0 : v0, a1 = odd ? v2 : s0;
+          const float b0 = odd ? s1 : v1, b1 = odd ? v3 : s1;
+          const uint32_t pa = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
+          const uint32_t pb = (uint32_t)f32_to_bf16_bits(b0) | ((uint32_t)f32_to_bf16_bits(b1) << 16);
+          *(uint32_t*)(rowp + loff + 32 * j) = pa;
+          *(uint32_t*)(rowp + p.ldcm + loff + 32 * j) = pb;
+        }
+      }
+  } else {
+    const int loff = 4 * half * (int)p.ldcm + ti.n0 + wn0 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float* rowp = (float*)p.c + (int64_t)(row0 + 32 * i + 8 * (r >> 2) + (r & 3)) * p.ldcm;
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) rowp[loff + 32 * j] = acc[i][j][r];
+      }
+  }
+}
+
 // Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds
 // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 block.
 template <class Cfg>
-__device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
-                                         const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wm0, int wn0,
-                                         int lane) {
+__device__ __forceinline__ void epilogue_any(const GemmKArgs& p, const TileInfo& ti,
+                                             const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wm0, int wn0,
+                                             int lane) {
   const int colb = ti.n0 + wn0 + (lane & 31);
   const int rowb = ti.m0 + wm0 + 4 * (lane >> 5);
   if (p.partial) {
@@ -466,15 +578,29 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = rowb + 32 * i + 8 * (r >> 2) + (r & 3);
+        const float v = acc[i][j][r];
         if (row < p.M && col < p.N) {
           const int64_t o = (int64_t)row * p.ldcm + (int64_t)col * p.ldcn;
           if (p.c_bf16)
-            ((uint16_t*)p.c)[o] = f32_to_bf16_bits(acc[i][j][r]);
+            ((uint16_t*)p.c)[o] = f32_to_bf16_bits(v);
           else
-            ((float*)p.c)[o] = acc[i][j][r];
+            ((float*)p.c)[o] = v;
         }
       }
     }
+}
+
+// The fast path needs: no split-K partial, unit column stride, the tile
+// inside C, and (bf16) 4-byte aligned column pairs, i.e. an even row stride
+// and an even base offset.  p.c_fast carries the host's check of the
+// stride/alignment conditions.
+template <class Cfg>
+__device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
+                                         const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wm0, int wn0, int lane) {
+  if (p.c_fast && ti.m0 + Cfg::BM <= p.M && ti.n0 + Cfg::BN <= p.N)
+    epilogue_fast<Cfg>(p, ti, acc, wm0, wn0, lane);
+  else
+    epilogue_any<Cfg>(p, ti, acc, wm0, wn0, lane);
 }
 
 template <class Cfg>
@@ -488,6 +614,205 @@ __device__ __forceinline__ void wait_slices(int n) {
   }
 }
 
+// Compute-side position in the workgroup's sequence of slices.
+template <class Cfg>
+struct CompPos {
+  int ct, ck;  // work item, slice
+  TileInfo ti;
+  __device__ __forceinline__ void start(const GemmKArgs& p, int first) {
+    ct = first;
+    ti = decode_tile<Cfg>(p, ct);
+    ck = ti.kb;
+  }
+  __device__ __forceinline__ bool tile_first() const { return ck == ti.kb; }
+  __device__ __forceinline__ bool tile_end() const { return ck + 1 == ti.ke; }
+  __device__ __forceinline__ bool has_next(const GemmKArgs& p, int stride) const {
+    return !tile_end() || ct + stride < p.total;
+  }
+  __device__ __forceinline__ void advance(const GemmKArgs& p, int stride) {
+    if (tile_end()) {
+      ct += stride;
+      ti = decode_tile<Cfg>(p, ct);
+      ck = ti.kb;
+    } else {
+      ++ck;
+    }
+  }
+};
+
+// Loading role (separate loading waves): fill the ring, then per slice wait
+// until the next slice has landed, meet the computing waves at the barrier
+// and refill the slot they have just released.
+template <class Cfg>
+__device__ __forceinline__ void producer_loop(const GemmKArgs& p, char LL_LDS* smem, int first, int stride,
+                                              int lw, int lane) {
+  constexpr int S = Cfg::STAGES;
+  const uint32_t va = TileGeom<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR>::lane_off(lw, lane, (int)p.a.ld);
+  const uint32_t vb = TileGeom<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR>::lane_off(lw, lane, (int)p.b.ld);
+  Loader<Cfg> ld;
+  ld.start(p, first);
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (ld.valid(p)) {
+      ld.issue(p, smem + s * Cfg::SLOT, lw, lane, va, vb);
+      ld.advance(p, stride);
+      ++issued;
+    }
+  }
+  wait_slices<Cfg>(issued - 1);
+  lds_barrier();
+  CompPos<Cfg> cc;
+  cc.start(p, first);
+  int j = 0, slot = 0;
+  while (true) {
+    const bool has_next = cc.has_next(p, stride);
+    if (has_next) wait_slices<Cfg>(issued - j - 2);
+    lds_barrier();
+    if (ld.valid(p)) {
+      ld.issue(p, smem + slot * Cfg::SLOT, lw, lane, va, vb);
+      ld.advance(p, stride);
+      ++issued;
+    }
+    if (!has_next) break;
+    cc.advance(p, stride);
+    ++j;
+    slot = slot + 1 == S ? 0 : slot + 1;
+  }
+}
+
+// Computing role (separate computing waves): fragments from LDS, MFMAs, and
+// the epilogue; one barrier per slice, placed before its last k16 step.
+// Fragments are double-buffered (the next k16 step's reads overlap this
+// step's MFMAs) unless the configuration runs three waves per SIMD, where the
+// register budget only allows one buffer and the second computing wave on
+// the SIMD covers the LDS latency instead.
+template <class Cfg>
+__device__ __forceinline__ void consumer_loop(const GemmKArgs& p, char LL_LDS* smem, int first, int stride,
+                                              int cw, int lane) {
+  constexpr int S = Cfg::STAGES;
+  constexpr int KS = Cfg::KS;
+  constexpr int NB = Cfg::WAVES_PER_EU >= 3 ? 1 : 2;  // fragment buffers
+  const int wm0 = (cw / Cfg::WN) * (Cfg::BM / Cfg::WM);
+  const int wn0 = (cw % Cfg::WN) * (Cfg::BN / Cfg::WN);
+  f32x16 acc[Cfg::FM][Cfg::FN];
+  if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+  Frags<Cfg> f[NB];
+  lds_barrier();
+  load_frags<Cfg>(smem, 0, wm0, wn0, lane, f[0]);
+  CompPos<Cfg> cc;
+  cc.start(p, first);
+  int slot = 0;
+  while (true) {
+    char LL_LDS* cur = smem + slot * Cfg::SLOT;
+    const bool tile_first = cc.tile_first();
+    const bool tile_end = cc.tile_end();
+    const bool has_next = cc.has_next(p, stride);
+    const int nslot = slot + 1 == S ? 0 : slot + 1;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if constexpr (NB == 2) {
+        if (kk + 1 < KS) {
+          load_frags<Cfg>(cur, kk + 1, wm0, wn0, lane, f[(kk + 1) & 1]);
+        } else {
+          lds_barrier();
+          if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
+        }
+        mfma_step<Cfg>(f[kk & 1], acc, kk == 0 && tile_first);
+      } else {
+        mfma_step<Cfg>(f[0], acc, kk == 0 && tile_first);
+        if (kk + 1 < KS) {
+          load_frags<Cfg>(cur, kk + 1, wm0, wn0, lane, f[0]);
+        } else {
+          lds_barrier();
+          if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
+        }
+      }
+    }
+    if (tile_end) {
+      acc_hazard_pad<Cfg>(acc);
+      epilogue<Cfg>(p, cc.ti, acc, wm0, wn0, lane);
+      if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+    }
+    if (!has_next) break;
+    cc.advance(p, stride);
+    slot = nslot;
+  }
+}
+
+// Every wave both loads its share of each slice and computes.
+template <class Cfg>
+__device__ __forceinline__ void coop_loop(const GemmKArgs& p, char LL_LDS* smem, int first, int stride, int wave,
+                                          int lane) {
+  constexpr int S = Cfg::STAGES;
+  constexpr int KS = Cfg::KS;
+  const int wm0 = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
+  const int wn0 = (wave % Cfg::WN) * (Cfg::BN / Cfg::WN);
+  const uint32_t va = TileGeom<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR>::lane_off(wave, lane, (int)p.a.ld);
+  const uint32_t vb = TileGeom<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR>::lane_off(wave, lane, (int)p.b.ld);
+  Loader<Cfg> ld;
+  ld.start(p, first);
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (ld.valid(p)) {
+      ld.issue(p, smem + s * Cfg::SLOT, wave, lane, va, vb);
+      ld.advance(p, stride);
+      ++issued;
+    }
+  }
+  wait_slices<Cfg>(issued - 1);
+  lds_barrier();
+
+  f32x16 acc[Cfg::FM][Cfg::FN];
+  if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+  Frags<Cfg> f[2];
+  load_frags<Cfg>(smem, 0, wm0, wn0, lane, f[0]);
+
+  bool drain = false;  // this wave issued global stores since its last full wait
+  int j = 0;           // slices consumed so far
+  int slot = 0;        // ring slot of slice j
+  CompPos<Cfg> cc;
+  cc.start(p, first);
+  while (true) {
+    char LL_LDS* cur = smem + slot * Cfg::SLOT;
+    const bool tile_first = cc.tile_first();
+    const bool tile_end = cc.tile_end();
+    const bool has_next = cc.has_next(p, stride);
+    const int nslot = slot + 1 == S ? 0 : slot + 1;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) {
+        load_frags<Cfg>(cur, kk + 1, wm0, wn0, lane, f[(kk + 1) & 1]);
+      } else {
+        // Slice boundary: slice j+1 must have landed; slice j's LDS is free.
+        if (has_next) {
+          wait_slices<Cfg>(drain ? 0 : issued - j - 2);
+          drain = false;
+        }
+        lds_barrier();
+        if (ld.valid(p)) {
+          ld.issue(p, cur, wave, lane, va, vb);
+          ld.advance(p, stride);
+          ++issued;
+        }
+        if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
+      }
+      mfma_step<Cfg>(f[kk & 1], acc, kk == 0 && tile_first);
+    }
+    if (tile_end) {
+      acc_hazard_pad<Cfg>(acc);
+      epilogue<Cfg>(p, cc.ti, acc, wm0, wn0, lane);
+      drain = true;
+      if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+    }
+    if (!has_next) break;
+    cc.advance(p, stride);
+    ++j;
+    slot = nslot;
+  }
+}
+
 template <class Cfg>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_EU, Cfg::WAVES_PER_EU)))
@@ -495,92 +820,18 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   static_assert(Cfg::STAGES <= 4, "wait_slices covers up to 4 stages");
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS];
   char LL_LDS* smem = (char LL_LDS*)smem_raw;
-  constexpr int S = Cfg::STAGES;
-  constexpr int KS = Cfg::KS;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const bool is_cons = Cfg::NPROD == 0 || wave < Cfg::NCONS;
-  const bool is_prod = Cfg::NPROD == 0 || wave >= Cfg::NCONS;
-  const int lw = Cfg::NPROD == 0 ? wave : wave - Cfg::NCONS;
-  const int cw = is_cons ? wave : 0;
-  const int wm0 = (cw / Cfg::WN) * (Cfg::BM / Cfg::WM);
-  const int wn0 = (cw % Cfg::WN) * (Cfg::BN / Cfg::WN);
-  const uint32_t va = TileGeom<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR>::lane_off(lw, lane, (int)p.a.ld);
-  const uint32_t vb = TileGeom<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR>::lane_off(lw, lane, (int)p.b.ld);
-
   const int stride = gridDim.x;
   const int first = xcd_remap(blockIdx.x, gridDim.x);
   if (first >= p.total) return;  // uniform over the workgroup
-
-  Loader<Cfg> ld;
-  ld.start(p, first);
-
-  // Prologue: fill every slot of the ring.
-  int issued = 0;
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    if (ld.valid(p)) {
-      if (is_prod) ld.issue(p, smem + s * Cfg::SLOT, lw, lane, va, vb);
-      ld.advance(p, stride);
-      ++issued;
-    }
-  }
-  if (is_prod) wait_slices<Cfg>(issued - 1);
-  lds_barrier();
-
-  f32x16 acc[Cfg::FM][Cfg::FN];
-  zero_acc(acc);
-  Frags<Cfg> f[2];
-  if (is_cons) load_frags<Cfg>(smem, 0, wm0, wn0, lane, f[0]);
-
-  bool drain = false;  // this wave issued global stores since its last full wait
-  int j = 0;           // slices consumed so far
-  int slot = 0;        // ring slot of slice j
-  int ct = first;      // work item being computed
-  TileInfo cti = decode_tile<Cfg>(p, ct);
-  int ck = cti.kb;
-  while (true) {
-    char LL_LDS* cur = smem + slot * Cfg::SLOT;
-    const bool tile_end = ck + 1 == cti.ke;
-    const bool has_next = !tile_end || ct + stride < p.total;
-    const int nslot = slot + 1 == S ? 0 : slot + 1;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      if (kk + 1 < KS) {
-        if (is_cons) load_frags<Cfg>(cur, kk + 1, wm0, wn0, lane, f[(kk + 1) & 1]);
-      } else {
-        // Slice boundary: slice j+1 must have landed; slice j's LDS is free.
-        if (is_prod && has_next) {
-          wait_slices<Cfg>(drain ? 0 : issued - j - 2);
-          drain = false;
-        }
-        lds_barrier();
-        if (ld.valid(p)) {
-          if (is_prod) ld.issue(p, cur, lw, lane, va, vb);
-          ld.advance(p, stride);
-          ++issued;
-        }
-        if (is_cons && has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
-      }
-      if (is_cons) mfma_step<Cfg>(f[kk & 1], acc);
-    }
-    if (tile_end) {
-      if (is_cons) {
-        epilogue<Cfg>(p, cti, acc, wm0, wn0, lane);
-        drain = true;
-      }
-      zero_acc(acc);
-    }
-    if (!has_next) break;
-    if (tile_end) {
-      ct += stride;
-      cti = decode_tile<Cfg>(p, ct);
-      ck = cti.kb;
-    } else {
-      ++ck;
-    }
-    ++j;
-    slot = nslot;
+  if constexpr (Cfg::NPROD > 0) {
+    if (wave >= Cfg::NCONS)
+      producer_loop<Cfg>(p, smem, first, stride, wave - Cfg::NCONS, lane);
+    else
+      consumer_loop<Cfg>(p, smem, first, stride, wave, lane);
+  } else {
+    coop_loop<Cfg>(p, smem, first, stride, wave, lane);
   }
 }
 

@@ -15,6 +15,7 @@ namespace ll {
 #define LL_GEMM_KINDS(X)                                                                              \
   X(KIND_SQ8_K64, 256, 256, 64, 2, 4, 0, 2)    /* 8 waves (2 per SIMD) 128x64 each */               \
   X(KIND_SQ8_K32, 256, 256, 32, 2, 4, 0, 4)    /* same, 4 x 32 KB slots */                          \
+  X(KIND_WIDE8_PC, 256, 128, 64, 2, 4, 4, 3)   /* 8 computing 128x32 + 4 loading waves */           \
   X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 3)    /* 4 computing 128x64 + 4 loading waves */           \
   X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 3)  /* 4 waves 128x64, load + compute */                 \
   X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 3)    /* skinny M: 4 computing 64x128 + 4 loading */       \

@@ -60,6 +60,7 @@ struct LincompCfg {
   static constexpr int LOADERS = NPROD;
   static constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / NPROD;
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
+  static constexpr bool AGPR_ACC = false;
   static_assert(NPROD > 0, "the fused kernel uses separate loading waves");
   static_assert((A_BYTES / 1024) % NPROD == 0 && (B_BYTES / 1024) % NPROD == 0, "load split");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -161,12 +162,6 @@ __device__ __forceinline__ void lc_issue(const LincompKArgs& p, const LcPos& s, 
   // user and item rows are read once: non-temporal hint
   load_tile<Cfg::BN, Cfg::KT, false, Cfg::LOADERS, SliceStream, true>(ob, sb, fb, n0, k0, slot + Cfg::A_BYTES, lw,
                                                                        lane, vb);
-}
-
-// Swap with the neighbouring lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
-__device__ __forceinline__ float swap_pair(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF,
-                                                               false));
 }
 
 // Store the wave's FM x FN blocks of Y for candidate (r, c).  Accumulator
@@ -323,7 +318,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         lds_barrier();
         if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, 0, wn0, lane, f[0]);
       }
-      mfma_step<Cfg>(f[kk & 1], acc);
+      mfma_step<Cfg>(f[kk & 1], acc, false);
     }
     if (p.dedup && cc.user_end(p)) {
 #pragma unroll

@@ -217,8 +217,8 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   if (s != LL_OK) return s;
   p.cus = info->cus;
 
-  // Tile shape: skinny M uses 128-row tiles; tiny problems use 128x128 tiles;
-  // everything else 256x256 tiles.
+  // Tile shape: skinny M uses 128x256 tiles; tiny problems use 128x128
+  // tiles; everything else 256x128 tiles with separate loading waves.
   const int64_t M = d->M, N = d->N;
   int kind;
   if (M <= 128 && N >= 1024)
@@ -226,9 +226,10 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   else if (M * N <= 1024ll * 1024)
     kind = KIND_SMALL_COOP;
   else
-    kind = KIND_SQ8_K64;
+    kind = KIND_WIDE_PC;
   if (d->flags & LL_FLAG_COOPERATIVE) {
-    if (kind_info(kind).nprod > 0) kind = KIND_WIDE_COOP;
+    if (kind == KIND_WIDE_PC) kind = KIND_SQ8_K64;
+    else if (kind_info(kind).nprod > 0) kind = KIND_WIDE_COOP;
   } else if (d->flags & LL_FLAG_PRODUCER_CONSUMER) {
     if (kind_info(kind).nprod == 0) kind = KIND_WIDE_PC;
   }
@@ -367,6 +368,8 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
     k.c = C;
     k.ldcm = d.stride_cm;
     k.ldcn = d.stride_cn;
+    k.c_fast = d.stride_cn == 1 && d.stride_cm % 2 == 0 && ((uintptr_t)C & 3) == 0 &&
+               d.stride_cm * (d.M + 256) < (1ll << 31);
   }
   e = launch_gemm(p->layout, p->kind, k, p->grid, st);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
