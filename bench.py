@@ -168,8 +168,10 @@ def cpu_baseline_lincomp(name: str, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # Short kernels (the 4096^3 GEMM runs ~0.12 ms) need tens of warm-up
+    # launches before clocks settle; 5 warm-up steps measured ~20% low.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gemm_4096",
                     choices=sorted(GEMM_NAMES | LINCOMP_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -177,6 +179,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, --steps times "
                          "(calibrates the HBM byte counters of a profiler run); prints its own line")
+    ap.add_argument("--stream-probe-mib", type=int, default=0,
+                    help="only run a streaming reduction that reads 4x and writes 1x this many MiB "
+                         "(the read/write mix of linear compression), --steps times; prints its own line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -200,6 +205,19 @@ def main():
                           "GB/s": round(2 * n / (ev * 1e-3) / 1e9, 1)}))
         return
 
+    if args.stream_probe_mib:
+        # out[i] = x[0][i] + x[1][i] + x[2][i] + x[3][i]: 4 bytes read per byte
+        # written, a plain streaming pass with no reuse.
+        n = (args.stream_probe_mib << 20) // 4
+        x = torch.ones((4, n), dtype=torch.float32, device="cuda")
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        wall, ev = _time_launches(lambda: torch.sum(x, dim=0, out=y), args.steps, args.warmup, stream)
+        rd, wr = 16 * n, 4 * n
+        print(json.dumps({"probe": "stream 4 reads : 1 write", "bytes_read": rd, "bytes_written": wr,
+                          "ms": round(ev, 4), "GB/s": round((rd + wr) / (ev * 1e-3) / 1e9, 1)}))
+        return
+
     head = args.workload
     if head in LINCOMP_NAMES:
         r = bench_lincomp(head, args.steps, args.warmup)
@@ -210,7 +228,8 @@ def main():
         config = dict(workload=head, requests=c.R, candidates_per_request=c.C, user_rows=c.Nu,
                       item_rows=c.Ni, dim=c.D, out_rows=c.Mo, y_dtype="bf16",
                       algorithmic_bytes=c.algorithmic_bytes)
-        plan = "two launches: user block per request, then per-candidate GEMM with fp32 bias"
+        plan = ("one persistent launch: per request the user block's product once, kept in registers "
+                "and reused as every candidate's starting sums; 4 loading + 4 computing waves")
     else:
         r = bench_gemm(head, args.steps, args.warmup)
         c = r["case"]

@@ -169,7 +169,7 @@ class GemmPlan:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        if h and _lib is not None:  # _lib is None once the interpreter tears the module down
             _lib.gemm_plan_destroy(h)
             self.handle = None
 
