@@ -101,7 +101,13 @@ struct GemmCfg {
   // AGPRs explicitly: the MFMAs are then inline asm with AGPR accumulator
   // operands (left to itself the compiler places fragments in AGPRs and
   // spills accumulators).
-  static constexpr bool AGPR_ACC = FM * FN * 16 > 128;
+  static constexpr bool AGPR_ACC = FM * FN * 16 > 128 && WAVES_PER_EU == 1 && NPROD == 0;
+  // Fragment buffers of a computing wave: two (the next k16 step's reads
+  // overlap this step's MFMAs) unless accumulators plus two buffers would
+  // not fit the wave's register budget (512 / waves per SIMD, less about 24
+  // for addresses and loop state); then one, and the other computing waves
+  // on the SIMD cover the LDS latency.
+  static constexpr int FRAG_BUFS = FM * FN * 16 + 2 * 4 * (FM + FN) + 24 <= 512 / WAVES_PER_EU / 8 * 8 ? 2 : 1;
   static_assert(!AGPR_ACC || WAVES_PER_EU == 1, "AGPR accumulators need one wave per SIMD");
 };
 
@@ -603,15 +609,21 @@ __device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
     epilogue_any<Cfg>(p, ti, acc, wm0, wn0, lane);
 }
 
-template <class Cfg>
-__device__ __forceinline__ void wait_slices(int n) {
-  if constexpr (Cfg::STAGES <= 2) {
+// s_waitcnt vmcnt(n * LPW) for a wave-uniform 0 <= n < STAGES (n >= MAX
+// waits for MAX * LPW): the wave's loads of the n slices issued after the
+// one waited for may stay in flight.
+template <class Cfg, int MAX>
+__device__ __forceinline__ void wait_slices_upto(int n) {
+  if constexpr (MAX <= 0) {
     wait_vmcnt<0>();
   } else {
-    if (n <= 0) wait_vmcnt<0>();
-    else if (n == 1 || Cfg::STAGES == 3) wait_vmcnt<Cfg::LPW>();
-    else wait_vmcnt<(Cfg::STAGES - 2) * Cfg::LPW>();
+    if (n >= MAX) wait_vmcnt<MAX * Cfg::LPW>();
+    else wait_slices_upto<Cfg, MAX - 1>(n);
   }
+}
+template <class Cfg>
+__device__ __forceinline__ void wait_slices(int n) {
+  wait_slices_upto<Cfg, Cfg::STAGES - 1>(n);
 }
 
 // Compute-side position in the workgroup's sequence of slices.
@@ -692,7 +704,7 @@ __device__ __forceinline__ void consumer_loop(const GemmKArgs& p, char LL_LDS* s
                                               int cw, int lane) {
   constexpr int S = Cfg::STAGES;
   constexpr int KS = Cfg::KS;
-  constexpr int NB = Cfg::WAVES_PER_EU >= 3 ? 1 : 2;  // fragment buffers
+  constexpr int NB = Cfg::FRAG_BUFS;
   const int wm0 = (cw / Cfg::WN) * (Cfg::BM / Cfg::WM);
   const int wn0 = (cw % Cfg::WN) * (Cfg::BN / Cfg::WN);
   f32x16 acc[Cfg::FM][Cfg::FN];
@@ -817,7 +829,6 @@ template <class Cfg>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_EU, Cfg::WAVES_PER_EU)))
     gemm_persistent(const GemmKArgs p) {
-  static_assert(Cfg::STAGES <= 4, "wait_slices covers up to 4 stages");
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS];
   char LL_LDS* smem = (char LL_LDS*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
