@@ -33,6 +33,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256"}
 LINCOMP_NAMES = {"lincomp_256x128"}
+# The same workload given in the layer's original form: every candidate's
+# stacked input [user rows; item rows] materialised (no reuse possible).
+STACKED_NAMES = {"lincomp_256x128_stacked": "lincomp_256x128"}
 
 
 def _kernel_source_hash() -> str:
@@ -119,6 +122,29 @@ def bench_lincomp(name: str, steps: int, warmup: int):
     gbs = c.algorithmic_bytes / (ev * 1e-3) / 1e9
     return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3), gbs=gbs,
                 tflops=c.flops / (ev * 1e-3) / 1e12)
+
+
+def bench_lincomp_stacked(name: str, steps: int, warmup: int):
+    """Times linear compression on the materialised stacked input X
+    [R][C][Nu+Ni][D] and, on the same data, the user-once form; reports the
+    ratio of the two (the speedup of computing the user block once)."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    import synth
+    from synth.device import lincomp_operands
+    c = synth.lincomp_workload(STACKED_NAMES[name])
+    user, item, W = lincomp_operands(c)
+    X = torch.cat([user[:, None].expand(c.R, c.C, c.Nu, c.D), item], dim=2).contiguous()
+    Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    _log(f"{name}: timing the stacked input")
+    wall, ev = _time_launches(lambda: ll.lincomp_stacked(X, W, c.Nu, out=Y), steps, warmup, stream)
+    _log(f"{name}: timing the user-once form on the same data")
+    _, ev_dedup = _time_launches(lambda: ll.lincomp(user, item, W, out=Y), steps, warmup, stream)
+    stacked_bytes = X.numel() * 2 + W.numel() * 2 + Y.numel() * 2
+    return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3),
+                gbs=stacked_bytes / (ev * 1e-3) / 1e9, stacked_bytes=stacked_bytes,
+                dedup_ms=ev_dedup, speedup=ev / ev_dedup)
 
 
 def cpu_baseline_gemm(name: str, target_s: float = 12.0):
@@ -243,11 +269,19 @@ def main():
 
     also = []
     if not args.no_also:
-        for name in ["ffn_up", "ffn_down", "lincomp_256x128", "edge", "skinny_splitk", "gemm_4096"]:
+        for name in ["ffn_up", "ffn_down", "lincomp_256x128", "lincomp_256x128_stacked", "edge",
+                     "skinny_splitk", "gemm_4096"]:
             if name == head:
                 continue
             torch.cuda.empty_cache()
-            if name in LINCOMP_NAMES:
+            if name in STACKED_NAMES:
+                x = bench_lincomp_stacked(name, args.steps, args.warmup)
+                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
+                                 unit="requests/s", hbm_gbs=round(x["gbs"], 1),
+                                 hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4), bytes=x["stacked_bytes"],
+                                 user_once_ms=round(x["dedup_ms"], 4),
+                                 user_once_speedup=round(x["speedup"], 3)))
+            elif name in LINCOMP_NAMES:
                 x = bench_lincomp(name, args.steps, args.warmup)
                 also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
                                  unit="requests/s", hbm_gbs=round(x["gbs"], 1),

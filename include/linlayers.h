@@ -124,16 +124,21 @@ ll_status gemm_plan_destroy(gemm_plan* plan);
 /*
  * Linear compression.  Sizes: R requests, C candidates per request, Nu user
  * rows, Ni item rows, D columns (embedding width), Mo compressed rows.
- *   user[r][n][d] = user[r*su_r + n*su_n + d]            (0 <= n < Nu), bf16
+ *   user[r][c][n][d] = user[r*su_r + c*su_c + n*su_n + d] (0 <= n < Nu), bf16
  *   item[r][c][n][d] = item[r*si_r + c*si_c + n*si_n + d] (0 <= n < Ni), bf16
  *   W[n][m] = W[n*sw_n + m]                               (0 <= n < Nu+Ni), bf16
  *   Y[r][c][m][d] = Y[r*sy_r + c*sy_c + m*sy_m + d], y_type LL_BF16 or LL_F32
- * Y[r][c][m][d] = sum_{n<Nu} W[n][m] user[r][n][d] + sum_{n<Ni} W[Nu+n][m] item[r][c][n][d],
- * accumulated in fp32; the first sum is computed once per request and kept
- * in fp32 (never rounded to bf16) until the final result is rounded.
+ * Y[r][c][m][d] = sum_{n<Nu} W[n][m] user[r][c][n][d] + sum_{n<Ni} W[Nu+n][m] item[r][c][n][d],
+ * accumulated in fp32.  su_c == 0: the user rows are one block per request,
+ * shared by all its candidates (the request's repeated features); the first
+ * sum is then computed once per request and kept in fp32 (never rounded to
+ * bf16) until the final result is rounded.  su_c != 0: every candidate
+ * carries its own user rows (a materialised stacked input [user; item] per
+ * candidate, the layer's original form); each candidate then computes both
+ * sums, in the same order, so equal rows give bit-identical results.
  * The last dimension of every tensor is contiguous; user, item and W must be
- * 16-byte aligned and su_n, si_n, sw_n multiples of 8; D and Mo multiples
- * of 8.
+ * 16-byte aligned and every stride a non-negative multiple of 8 (su_n, si_n,
+ * sw_n, sy_m at least the row length); D and Mo multiples of 8.
  * flags: 0 = user block once per request (default); LL_LINCOMP_NO_DEDUP =
  * treat the user rows as if they were repeated for every candidate (each
  * candidate recomputes the user contribution; the result is the same sum).
@@ -142,7 +147,7 @@ ll_status gemm_plan_destroy(gemm_plan* plan);
 
 typedef struct {
   int64_t R, C, Nu, Ni, D, Mo;
-  int64_t su_r, su_n;
+  int64_t su_r, su_c, su_n;
   int64_t si_r, si_c, si_n;
   int64_t sw_n;
   int64_t sy_r, sy_c, sy_m;

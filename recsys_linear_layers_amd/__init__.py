@@ -46,7 +46,7 @@ class GemmDesc(ctypes.Structure):
 
 class LincompDesc(ctypes.Structure):
     _fields_ = [("R", _i64), ("C", _i64), ("Nu", _i64), ("Ni", _i64), ("D", _i64), ("Mo", _i64),
-                ("su_r", _i64), ("su_n", _i64),
+                ("su_r", _i64), ("su_c", _i64), ("su_n", _i64),
                 ("si_r", _i64), ("si_c", _i64), ("si_n", _i64),
                 ("sw_n", _i64),
                 ("sy_r", _i64), ("sy_c", _i64), ("sy_m", _i64),
@@ -207,16 +207,25 @@ def gemm(A, B, out=None, out_dtype=None, flags: int = 0):
 
 
 def lincomp_desc_for(user, item, W, Y, flags: int = 0) -> LincompDesc:
-    R, Nu, D = user.shape
+    """user is [R][Nu][D] (one block per request) or [R][C][Nu][D] (rows per
+    candidate, e.g. the first Nu rows of a materialised input)."""
     R2, C, Ni, D2 = item.shape
+    if user.dim() == 4:
+        if user.shape[1] != C:
+            raise ValueError("lincomp shape mismatch")
+        R, _, Nu, D = user.shape
+        su_r, su_c, su_n = user.stride(0), user.stride(1), user.stride(2)
+    else:
+        R, Nu, D = user.shape
+        su_r, su_c, su_n = user.stride(0), 0, user.stride(1)
     Nin, Mo = W.shape
     if R2 != R or D2 != D or Nin != Nu + Ni or tuple(Y.shape) != (R, C, Mo, D):
         raise ValueError("lincomp shape mismatch")
     for t in (user, item, W, Y):
         if t.stride(-1) != 1:
             raise ValueError("last dimension must be contiguous")
-    su, si, sw, sy = user.stride(), item.stride(), W.stride(), Y.stride()
-    return LincompDesc(R, C, Nu, Ni, D, Mo, su[0], su[1], si[0], si[1], si[2], sw[0],
+    si, sw, sy = item.stride(), W.stride(), Y.stride()
+    return LincompDesc(R, C, Nu, Ni, D, Mo, su_r, su_c, su_n, si[0], si[1], si[2], sw[0],
                        sy[0], sy[1], sy[2], _dtype_code(Y.dtype), flags)
 
 
@@ -224,10 +233,11 @@ _lc_ws: dict = {}
 
 
 def lincomp(user, item, W, out=None, out_dtype=None, flags: int = 0):
-    """Y[r, c] = W^T . [user[r]; item[r, c]] for bf16 tensors user [R][Nu][D],
-    item [R][C][Ni][D], W [Nu+Ni][Mo]; returns Y [R][C][Mo][D]."""
+    """Y[r, c] = W^T . [user[r]; item[r, c]] for bf16 tensors user [R][Nu][D]
+    (or [R][C][Nu][D], rows per candidate), item [R][C][Ni][D], W [Nu+Ni][Mo];
+    returns Y [R][C][Mo][D]."""
     torch = _torch()
-    R, Nu, D = user.shape
+    R, D = user.shape[0], user.shape[-1]
     C = item.shape[1]
     Mo = W.shape[1]
     if out is None:
@@ -243,3 +253,11 @@ def lincomp(user, item, W, out=None, out_dtype=None, flags: int = 0):
     lincomp_run(desc, user.data_ptr(), item.data_ptr(), W.data_ptr(), out.data_ptr(), ws.data_ptr(),
                 ws.numel(), stream)
     return out
+
+
+
+def lincomp_stacked(X, W, Nu: int, out=None, out_dtype=None):
+    """The layer's original form: X [R][C][Nu+Ni][D] holds every candidate's
+    stacked input [user rows; item rows] in full.  Y[r, c] = W^T . X[r, c];
+    each candidate computes its user rows' contribution itself."""
+    return lincomp(X[:, :, :Nu], X[:, :, Nu:], W, out=out, out_dtype=out_dtype)

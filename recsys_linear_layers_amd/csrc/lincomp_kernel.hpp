@@ -16,7 +16,8 @@
 //    B = item[r][c]).  The consumer waves keep U[r] in registers at the end
 //    of the user slices and start every candidate's accumulators from it, so
 //    U never goes through memory and is never rounded.
-//    Without dedup the user slices are repeated before every candidate and
+//    Without dedup (asked for, or user rows given per candidate) the user
+//    slices of the current candidate are streamed before its item slices and
 //    the accumulators start from zero (the stacked-input form).
 //  * Loading waves (NPROD) only stream slices HBM -> LDS with direct-to-LDS
 //    loads; computing waves only read fragments, run MFMAs and store Y.  The
@@ -37,7 +38,7 @@ struct LincompKArgs {
   const uint16_t* item;
   const uint16_t* W;
   void* Y;
-  int64_t su_r, su_n, si_r, si_c, si_n, sw_n, sy_r, sy_c, sy_m;
+  int64_t su_r, su_c, su_n, si_r, si_c, si_n, sw_n, sy_r, sy_c, sy_m;
   int64_t user_extent, item_extent, w_extent;  // elements addressable from each base pointer
   int32_t R, C, Nu, Ni, D, Mo;
   int32_t tiles_m, tiles_n, chunk, nchunks;    // candidates per work item, work items per request
@@ -148,7 +149,7 @@ __device__ __forceinline__ void lc_issue(const LincompKArgs& p, const LcPos& s, 
   sb.soff = 0;
   if (s.user) {
     ob.ld = p.su_n;
-    const int64_t borg = (int64_t)s.r * p.su_r + (int64_t)k0 * p.su_n + n0;
+    const int64_t borg = (int64_t)s.r * p.su_r + (int64_t)s.c * p.su_c + (int64_t)k0 * p.su_n + n0;
     sb.rs = make_rsrc(p.user + borg, clamp_records(p.user_extent - borg));
   } else {
     ob.ld = p.si_n;

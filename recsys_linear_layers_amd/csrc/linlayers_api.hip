@@ -394,12 +394,12 @@ static ll_status lincomp_check(const lincomp_desc* d) {
   if (d->flags & ~(uint32_t)LL_LINCOMP_NO_DEDUP) return fail(LL_ERR_INVALID_ARG, "unknown flag bits");
   if (d->y_type != LL_BF16 && d->y_type != LL_F32) return fail(LL_ERR_UNSUPPORTED, "Y must be LL_BF16 or LL_F32");
   if (d->D % 8 || d->Mo % 8) return fail(LL_ERR_INVALID_ARG, "D and Mo must be multiples of 8");
-  if (d->su_n % 8 || d->si_n % 8 || d->sw_n % 8 || d->su_r % 8 || d->si_r % 8 || d->si_c % 8 ||
+  if (d->su_n % 8 || d->si_n % 8 || d->sw_n % 8 || d->su_r % 8 || d->su_c % 8 || d->si_r % 8 || d->si_c % 8 ||
       d->sy_r % 8 || d->sy_c % 8 || d->sy_m % 8)
     return fail(LL_ERR_INVALID_ARG, "every row and batch stride must be a multiple of 8");
   if (d->su_n < d->D || d->si_n < d->D || d->sw_n < d->Mo || d->sy_m < d->D)
     return fail(LL_ERR_INVALID_ARG, "row strides shorter than the rows");
-  if (d->su_r < 0 || d->si_r < 0 || d->si_c < 0 || d->sy_r < 0 || d->sy_c < 0)
+  if (d->su_r < 0 || d->su_c < 0 || d->si_r < 0 || d->si_c < 0 || d->sy_r < 0 || d->sy_c < 0)
     return fail(LL_ERR_INVALID_ARG, "negative stride");
   if (d->Mo >= (1 << 30) || d->D >= (1 << 30) || d->R * d->C >= (1ll << 30))
     return fail(LL_ERR_UNSUPPORTED, "Mo, D and R*C must be below 2^30");
@@ -435,6 +435,7 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
                                                               (d->Mo - 1) * d->sy_m + d->D) * ysz)};
   if (overlaps(sy, Span{(uintptr_t)W, (uintptr_t)W + (uintptr_t)((d->Nu + d->Ni - 1) * d->sw_n + d->Mo) * 2}) ||
       (d->Nu > 0 && overlaps(sy, Span{(uintptr_t)user, (uintptr_t)user + (uintptr_t)(((d->R - 1) * d->su_r +
+                                                                                      (d->C - 1) * d->su_c +
                                                                                       (d->Nu - 1) * d->su_n + d->D) * 2)})) ||
       (d->Ni > 0 && overlaps(sy, Span{(uintptr_t)item, (uintptr_t)item + (uintptr_t)(((d->R - 1) * d->si_r +
                                                                                       (d->C - 1) * d->si_c +
@@ -449,6 +450,7 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
   k.W = (const uint16_t*)W;
   k.Y = Y;
   k.su_r = d->su_r;
+  k.su_c = d->su_c;
   k.su_n = d->su_n;
   k.si_r = d->si_r;
   k.si_c = d->si_c;
@@ -457,7 +459,7 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
   k.sy_r = d->sy_r;
   k.sy_c = d->sy_c;
   k.sy_m = d->sy_m;
-  k.user_extent = d->Nu > 0 ? (d->R - 1) * d->su_r + (d->Nu - 1) * d->su_n + d->D : 0;
+  k.user_extent = d->Nu > 0 ? (d->R - 1) * d->su_r + (d->C - 1) * d->su_c + (d->Nu - 1) * d->su_n + d->D : 0;
   k.item_extent = d->Ni > 0 ? (d->R - 1) * d->si_r + (d->C - 1) * d->si_c + (d->Ni - 1) * d->si_n + d->D : 0;
   k.w_extent = (d->Nu + d->Ni - 1) * d->sw_n + d->Mo;
   k.R = (int32_t)d->R;
@@ -484,7 +486,8 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
   if (total >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "too many work items");
   k.total = (int32_t)total;
   k.y_bf16 = d->y_type == LL_BF16;
-  k.dedup = !(d->flags & LL_LINCOMP_NO_DEDUP);
+  // Per-candidate user rows (su_c != 0) leave nothing to share.
+  k.dedup = !(d->flags & LL_LINCOMP_NO_DEDUP) && d->su_c == 0;
   const int grid = (int)std::min<int64_t>(total, info->cus);
   hipError_t e = launch_lincomp(k, grid, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "lincomp launch");

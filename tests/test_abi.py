@@ -103,7 +103,7 @@ def test_valid_plan_needs_a_device():
 def _lc(**kw):
     import recsys_linear_layers_amd as ll
     R, C, Nu, Ni, D, Mo = 2, 3, 256, 256, 256, 64
-    base = dict(R=R, C=C, Nu=Nu, Ni=Ni, D=D, Mo=Mo, su_r=Nu * D, su_n=D, si_r=C * Ni * D, si_c=Ni * D,
+    base = dict(R=R, C=C, Nu=Nu, Ni=Ni, D=D, Mo=Mo, su_r=Nu * D, su_c=0, su_n=D, si_r=C * Ni * D, si_c=Ni * D,
                 si_n=D, sw_n=Mo, sy_r=C * Mo * D, sy_c=Mo * D, sy_m=D, y_type=ll.LL_BF16, flags=0)
     base.update(kw)
     return ll.LincompDesc(**base)
@@ -117,7 +117,7 @@ def test_lincomp_workspace_and_checks():
     assert ll.lincomp_workspace_size(_lc(Nu=0)) == 0
     n = ctypes.c_size_t()
     for kw in (dict(R=-1), dict(D=12), dict(su_n=12), dict(flags=8), dict(y_type=5), dict(si_c=4),
-               dict(sw_n=8), dict(sy_m=260)):
+               dict(sw_n=8), dict(sy_m=260), dict(su_c=4), dict(su_c=-8)):
         st = ll._lib.lincomp_workspace_size(ctypes.byref(_lc(**kw)), ctypes.byref(n))
         assert st != ll.LL_OK, kw
     st = ll._lib.lincomp_run(None, None, None, None, None, None, 0, None)

@@ -23,8 +23,24 @@ def _run(case, y_dtype="bf16", flags=0):
     return to_f64(Y)
 
 
-def _check(case, pairs=None, y_dtype="bf16", flags=0):
-    Y = _run(case, y_dtype, flags)
+def _run_stacked(case, y_dtype="bf16"):
+    """The layer's original input: every candidate's [user rows; item rows]
+    materialised in one tensor X [R][C][Nu+Ni][D]."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    R, C, D, Mo, Nu = case.R, case.C, case.D, case.Mo, case.Nu
+    user, item, W = lincomp_operands(case)
+    X = torch.cat([user[:, None].expand(R, C, Nu, D), item], dim=2).contiguous()
+    del item
+    dt = torch.bfloat16 if y_dtype == "bf16" else torch.float32
+    Y = torch.full((R, C, Mo, D), float("nan"), dtype=dt, device="cuda")
+    ll.lincomp_stacked(X, W, Nu, out=Y)
+    torch.cuda.synchronize()
+    return to_f64(Y)
+
+
+def _check(case, pairs=None, y_dtype="bf16", flags=0, stacked=False):
+    Y = _run_stacked(case, y_dtype) if stacked else _run(case, y_dtype, flags)
     pairs = pairs or [(r, c) for r in range(case.R) for c in range(case.C)]
     ref, S = oracle.lincomp_case(case, pairs)
     got = np.stack([Y[r, c] for r, c in pairs])
@@ -64,6 +80,25 @@ def test_no_dedup_mode_matches_dedup():
     a = _run(c)
     b = _check(c, flags=ll.LL_LINCOMP_NO_DEDUP)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("Nu,Ni,D,Mo", [(256, 256, 256, 64), (40, 24, 72, 24), (0, 64, 64, 16)])
+def test_stacked_input_matches_oracle_and_dedup(Nu, Ni, D, Mo):
+    # Per-candidate user rows: no sharing, every candidate computes both sums
+    # in the dedup path's order, so the results must be bit-identical.
+    c = synth.lincomp_case(3, 5, Nu, Ni, D, Mo, seed=60 + Nu + Ni, name=f"stacked{Nu}_{Ni}_{D}_{Mo}")
+    a = _run(c)
+    b = _check(c, stacked=True)
+    assert np.array_equal(a, b)
+    _check(c, y_dtype="f32", stacked=True)
+
+
+def test_full_workload_stacked_sampled_candidates():
+    c = synth.lincomp_workload("lincomp_256x128")
+    rng = np.random.default_rng(1)
+    pairs = [(0, 0), (c.R - 1, c.C - 1)]
+    pairs += [(int(r), int(k)) for r, k in zip(rng.integers(0, c.R, 16), rng.integers(0, c.C, 16))]
+    _check(c, pairs, stacked=True)
 
 
 def test_full_workload_sampled_candidates():
