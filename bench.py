@@ -36,6 +36,8 @@ LINCOMP_NAMES = {"lincomp_256x128"}
 # The same workload given in the layer's original form: every candidate's
 # stacked input [user rows; item rows] materialised (no reuse possible).
 STACKED_NAMES = {"lincomp_256x128_stacked": "lincomp_256x128"}
+# Ragged requests: 256 requests with a lognormal mix of candidate counts.
+RAGGED_NAMES = {"lincomp_ragged_256"}
 
 
 def _kernel_source_hash() -> str:
@@ -145,6 +147,22 @@ def bench_lincomp_stacked(name: str, steps: int, warmup: int):
     return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3),
                 gbs=stacked_bytes / (ev * 1e-3) / 1e9, stacked_bytes=stacked_bytes,
                 dedup_ms=ev_dedup, speedup=ev / ev_dedup)
+
+
+def bench_lincomp_ragged(name: str, steps: int, warmup: int):
+    import torch
+    import recsys_linear_layers_amd as ll
+    import synth
+    from synth.device import ragged_operands
+    _log(f"{name}: generating inputs")
+    c = synth.lincomp_ragged_workload(name)
+    user, item, W, offsets = ragged_operands(c)
+    Y = torch.empty((c.Ctot, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    _log(f"{name}: timing")
+    wall, ev = _time_launches(lambda: ll.lincomp_ragged(user, item, W, offsets, out=Y), steps, warmup, stream)
+    gbs = c.algorithmic_bytes / (ev * 1e-3) / 1e9
+    return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3), gbs=gbs)
 
 
 def cpu_baseline_gemm(name: str, target_s: float = 12.0):
@@ -269,12 +287,20 @@ def main():
 
     also = []
     if not args.no_also:
-        for name in ["ffn_up", "ffn_down", "lincomp_256x128", "lincomp_256x128_stacked", "edge",
-                     "skinny_splitk", "gemm_4096"]:
+        for name in ["ffn_up", "ffn_down", "lincomp_256x128", "lincomp_256x128_stacked", "lincomp_ragged_256",
+                     "edge", "skinny_splitk", "gemm_4096"]:
             if name == head:
                 continue
             torch.cuda.empty_cache()
-            if name in STACKED_NAMES:
+            if name in RAGGED_NAMES:
+                x = bench_lincomp_ragged(name, args.steps, args.warmup)
+                c = x["case"]
+                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
+                                 unit="requests/s", candidates=c.Ctot,
+                                 candidates_per_request=[int(c.lengths.min()), round(float(c.lengths.mean()), 1),
+                                                         int(c.lengths.max())],
+                                 hbm_gbs=round(x["gbs"], 1), hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4)))
+            elif name in STACKED_NAMES:
                 x = bench_lincomp_stacked(name, args.steps, args.warmup)
                 also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
                                  unit="requests/s", hbm_gbs=round(x["gbs"], 1),

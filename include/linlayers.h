@@ -170,6 +170,38 @@ ll_status lincomp_run(const lincomp_desc* desc, const void* user, const void* it
                       const void* W, void* Y, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/*
+ * Linear compression over ragged requests (page "Meta accélère un noyau GPU
+ * d'un facteur 4 avec TLX", sections "Comment le chargement des données gêne
+ * le calcul" and "Par où commencer dans votre équipe": the number of
+ * candidates scored per request varies).  Request r owns the candidates
+ * offsets[r] .. offsets[r+1]-1 of a flat candidate axis of length Ctot:
+ *   user[r][n][d] = user[r*su_r + n*su_n + d]   (0 <= n < Nu), bf16
+ *   item[g][n][d] = item[g*si_c + n*si_n + d]   (0 <= g < Ctot, 0 <= n < Ni), bf16
+ *   W as for lincomp_run; Y[g][m][d] = Y[g*sy_c + m*sy_m + d], y_type
+ * Y[g] = sum_{n<Nu} W[n][m] user[r(g)][n][d] + sum_{n<Ni} W[Nu+n][m] item[g][n][d],
+ * with the user sum formed once per (request, work item) and kept in fp32.
+ * offsets: device array of R+1 int64, non-decreasing, offsets[0] = 0,
+ * offsets[R] = Ctot (read on the device; values outside [0, Ctot] are
+ * clamped, and malformed offsets give unspecified rows of Y but no access
+ * outside the buffers).  Candidates of empty requests do not exist; every
+ * g in [0, Ctot) is written.  Alignment and stride rules as for
+ * lincomp_run.  No workspace.  R == 0 or Ctot == 0: nothing is written.
+ * Errors as for lincomp_run, plus LL_ERR_INVALID_ARG for a null offsets.
+ */
+typedef struct {
+  int64_t R, Ctot, Nu, Ni, D, Mo;
+  int64_t su_r, su_n;
+  int64_t si_c, si_n;
+  int64_t sw_n;
+  int64_t sy_c, sy_m;
+  int32_t y_type; /* ll_dtype */
+  uint32_t flags; /* LL_LINCOMP_NO_DEDUP or 0 */
+} lincomp_ragged_desc;
+
+ll_status lincomp_ragged_run(const lincomp_ragged_desc* desc, const int64_t* offsets, const void* user,
+                             const void* item, const void* W, void* Y, void* stream);
+
 /* Static, human-readable name of a status code ("LL_OK", ...). */
 const char* ll_status_string(ll_status s);
 

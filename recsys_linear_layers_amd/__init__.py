@@ -53,6 +53,15 @@ class LincompDesc(ctypes.Structure):
                 ("y_type", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
+class LincompRaggedDesc(ctypes.Structure):
+    _fields_ = [("R", _i64), ("Ctot", _i64), ("Nu", _i64), ("Ni", _i64), ("D", _i64), ("Mo", _i64),
+                ("su_r", _i64), ("su_n", _i64),
+                ("si_c", _i64), ("si_n", _i64),
+                ("sw_n", _i64),
+                ("sy_c", _i64), ("sy_m", _i64),
+                ("y_type", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
 _lib.ll_status_string.restype = ctypes.c_char_p
 _lib.ll_status_string.argtypes = [ctypes.c_int]
 _lib.ll_last_error.restype = ctypes.c_char_p
@@ -64,8 +73,9 @@ _lib.gemm_run.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.gemm_plan_destroy.argtypes = [_vp]
 _lib.lincomp_workspace_size.argtypes = [ctypes.POINTER(LincompDesc), ctypes.POINTER(ctypes.c_size_t)]
 _lib.lincomp_run.argtypes = [ctypes.POINTER(LincompDesc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.lincomp_ragged_run.argtypes = [ctypes.POINTER(LincompRaggedDesc), _vp, _vp, _vp, _vp, _vp, _vp]
 for _f in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run",
-           "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run"):
+           "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "lincomp_ragged_run"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -122,6 +132,11 @@ def lincomp_workspace_size(desc: LincompDesc) -> int:
     n = ctypes.c_size_t()
     _check(_lib.lincomp_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "lincomp_workspace_size")
     return n.value
+
+
+def lincomp_ragged_run(desc: LincompRaggedDesc, offsets: int, user: int, item: int, W: int, Y: int,
+                       stream: int = 0) -> None:
+    _check(_lib.lincomp_ragged_run(ctypes.byref(desc), offsets, user, item, W, Y, stream), "lincomp_ragged_run")
 
 
 def lincomp_run(desc: LincompDesc, user: int, item: int, W: int, Y: int, workspace: int, ws_bytes: int,
@@ -261,3 +276,31 @@ def lincomp_stacked(X, W, Nu: int, out=None, out_dtype=None):
     stacked input [user rows; item rows] in full.  Y[r, c] = W^T . X[r, c];
     each candidate computes its user rows' contribution itself."""
     return lincomp(X[:, :, :Nu], X[:, :, Nu:], W, out=out, out_dtype=out_dtype)
+
+
+def lincomp_ragged(user, item, W, offsets, out=None, out_dtype=None, flags: int = 0):
+    """Ragged requests: user [R][Nu][D], item [Ctot][Ni][D], W [Nu+Ni][Mo] (bf16),
+    offsets int64 [R+1] on the device (request r owns candidates
+    offsets[r] .. offsets[r+1]-1); returns Y [Ctot][Mo][D]."""
+    torch = _torch()
+    R, Nu, D = user.shape
+    Ctot, Ni, D2 = item.shape
+    Nin, Mo = W.shape
+    if D2 != D or Nin != Nu + Ni or tuple(offsets.shape) != (R + 1,) or offsets.dtype != torch.int64:
+        raise ValueError("lincomp_ragged shape mismatch")
+    if out is None:
+        out = torch.empty((Ctot, Mo, D), dtype=out_dtype or torch.bfloat16, device=user.device)
+    if tuple(out.shape) != (Ctot, Mo, D):
+        raise ValueError("lincomp_ragged output shape mismatch")
+    for t in (user, item, W, out):
+        if t.stride(-1) != 1:
+            raise ValueError("last dimension must be contiguous")
+    if not offsets.is_contiguous():
+        raise ValueError("offsets must be contiguous")
+    su, si, sw, sy = user.stride(), item.stride(), W.stride(), out.stride()
+    desc = LincompRaggedDesc(R, Ctot, Nu, Ni, D, Mo, su[0], su[1], si[0], si[1], sw[0], sy[0], sy[1],
+                             _dtype_code(out.dtype), flags)
+    stream = torch.cuda.current_stream(user.device).cuda_stream
+    lincomp_ragged_run(desc, offsets.data_ptr(), user.data_ptr(), item.data_ptr(), W.data_ptr(),
+                       out.data_ptr(), stream)
+    return out

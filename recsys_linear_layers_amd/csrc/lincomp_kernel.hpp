@@ -45,6 +45,12 @@ struct LincompKArgs {
   int32_t nu_sl, ni_sl;                        // slices per user / per candidate phase (>= 1 for Ni)
   int32_t total;                               // work items
   int32_t y_bf16, dedup;
+  // Ragged requests (offsets != nullptr): C is the total candidate count, the
+  // candidates of request r are offsets[r] .. offsets[r+1]-1 (global indices
+  // into item and Y, whose request strides are 0), and the candidates are cut
+  // into nranges equal contiguous ranges, one per work item (per output tile).
+  const int64_t* offsets;
+  int32_t nranges;
 };
 
 template <int BM_, int BN_, int KT_, int WN_, int NPROD_, int STAGES_>
@@ -73,11 +79,25 @@ struct LincompCfg {
 // Position in a work item's slice sequence.  Both roles walk the same
 // sequence with their own copy.
 struct LcPos {
-  int t;        // work item
-  int r, c, c1; // request, current candidate, end of the item's candidates
-  int m0, n0;   // output tile origin (Mo, D)
-  bool user;    // current slice belongs to the user phase
-  int ks;       // slice index within the phase
+  int t;         // work item
+  int r, c, c1;  // request, current candidate, end of the item's candidates
+  int rend;      // end of the current request's candidates within the item
+  int m0, n0;    // output tile origin (Mo, D)
+  bool user;     // current slice belongs to the user phase
+  int ks;        // slice index within the phase
+
+  // offsets[q] clamped to [0, C]: malformed offsets give wrong rows, never an
+  // access outside the buffers.
+  __device__ static __forceinline__ int off_at(const LincompKArgs& p, int q) {
+    const int64_t v = p.offsets[q];
+    return (int)(v < 0 ? 0 : (v > p.C ? (int64_t)p.C : v));
+  }
+  // First candidate index >= c that starts a later request than r.
+  __device__ __forceinline__ void next_request(const LincompKArgs& p) {
+    while (r + 1 < p.R && off_at(p, r + 1) <= c) ++r;
+    const int e = min(off_at(p, r + 1), c1);
+    rend = e > c ? e : c + 1;  // progress even on malformed offsets
+  }
 
   __device__ __forceinline__ void start(const LincompKArgs& p, int t_) {
     t = t_;
@@ -85,20 +105,38 @@ struct LcPos {
     const int tiles = p.tiles_m * p.tiles_n;
     const int tin = t % tiles;
     const int rc = t / tiles;
-    r = rc / p.nchunks;
-    const int ch = rc - r * p.nchunks;
-    c = ch * p.chunk;
-    c1 = min(c + p.chunk, p.C);
     m0 = tin / p.tiles_n;  // tile indices along Mo and D
     n0 = tin - m0 * p.tiles_n;
     ks = 0;
     user = p.nu_sl > 0;
+    if (p.offsets) {
+      c = (int)((int64_t)rc * p.C / p.nranges);
+      c1 = (int)((int64_t)(rc + 1) * p.C / p.nranges);
+      // request of candidate c: the last r with offsets[r] <= c
+      int lo = 0, hi = p.R - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off_at(p, mid) <= c) lo = mid;
+        else hi = mid - 1;
+      }
+      r = lo;
+      next_request(p);
+      return;
+    }
+    r = rc / p.nchunks;
+    const int ch = rc - r * p.nchunks;
+    c = ch * p.chunk;
+    c1 = min(c + p.chunk, p.C);
+    rend = c1;
   }
   __device__ __forceinline__ bool valid(const LincompKArgs& p) const { return t < p.total; }
   // Last slice of the user phase (dedup: U is complete after it).
   __device__ __forceinline__ bool user_end(const LincompKArgs& p) const { return user && ks + 1 == p.nu_sl; }
   // Last slice of a candidate (its result is complete after it).
   __device__ __forceinline__ bool cand_end(const LincompKArgs& p) const { return !user && ks + 1 == p.ni_sl; }
+  // Last slice of the request's candidates in this item (the next candidate,
+  // if any, needs a new U).
+  __device__ __forceinline__ bool req_end(const LincompKArgs& p) const { return cand_end(p) && c + 1 >= rend; }
   __device__ __forceinline__ bool item_end(const LincompKArgs& p) const { return cand_end(p) && c + 1 == c1; }
   __device__ __forceinline__ void advance(const LincompKArgs& p, int stride) {
     if (user) {
@@ -111,7 +149,12 @@ struct LcPos {
     if (++ks < p.ni_sl) return;
     ks = 0;
     if (++c < c1) {
-      user = !p.dedup && p.nu_sl > 0;
+      if (c >= rend) {  // ragged: the next request starts
+        next_request(p);
+        user = p.nu_sl > 0;
+      } else {
+        user = !p.dedup && p.nu_sl > 0;
+      }
       return;
     }
     start(p, t + stride);
@@ -329,7 +372,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     }
     if (cc.cand_end(p)) {
       lc_epilogue<Cfg>(p, cc, acc, wn0, lane);
-      if (p.dedup) {
+      if (p.dedup && !cc.req_end(p)) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll

@@ -387,7 +387,7 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
 // Linear compression
 // ---------------------------------------------------------------------------
 
-static ll_status lincomp_check(const lincomp_desc* d) {
+static ll_status lincomp_check(const lincomp_desc* d, bool ragged = false) {
   if (!d) return fail(LL_ERR_INVALID_ARG, "null desc");
   if (d->R < 0 || d->C < 0 || d->Nu < 0 || d->Ni < 0 || d->D < 0 || d->Mo < 0)
     return fail(LL_ERR_INVALID_ARG, "negative size");
@@ -401,8 +401,10 @@ static ll_status lincomp_check(const lincomp_desc* d) {
     return fail(LL_ERR_INVALID_ARG, "row strides shorter than the rows");
   if (d->su_r < 0 || d->su_c < 0 || d->si_r < 0 || d->si_c < 0 || d->sy_r < 0 || d->sy_c < 0)
     return fail(LL_ERR_INVALID_ARG, "negative stride");
-  if (d->Mo >= (1 << 30) || d->D >= (1 << 30) || d->R * d->C >= (1ll << 30))
-    return fail(LL_ERR_UNSUPPORTED, "Mo, D and R*C must be below 2^30");
+  if (d->Mo >= (1 << 30) || d->D >= (1 << 30) || (ragged ? d->C : d->R * d->C) >= (1ll << 30) ||
+      d->R >= (1ll << 30))
+    return fail(LL_ERR_UNSUPPORTED, ragged ? "Mo, D, R and Ctot must be below 2^30"
+                                           : "Mo, D and R*C must be below 2^30");
   if (d->su_n * 2 * kBK >= (1ll << 31) || d->si_n * 2 * kBK >= (1ll << 31) || d->sw_n * 2 * kBK >= (1ll << 31))
     return fail(LL_ERR_UNSUPPORTED, "row strides too large");
   return LL_OK;
@@ -416,11 +418,12 @@ ll_status lincomp_workspace_size(const lincomp_desc* d, size_t* bytes) {
   return ok();
 }
 
-ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item, const void* W, void* Y,
-                      void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
-  ll_status s = lincomp_check(d);
+// Shared by the per-request and the ragged entry points.  offsets != nullptr:
+// ragged (d->C is the total candidate count; d's request strides of item and
+// Y and the per-candidate user stride are 0).
+static ll_status lincomp_launch(const lincomp_desc* d, const int64_t* offsets, const void* user, const void* item,
+                                const void* W, void* Y, void* stream) {
+  ll_status s = lincomp_check(d, offsets != nullptr);
   if (s != LL_OK) return s;
   if (d->R == 0 || d->C == 0 || d->Mo == 0 || d->D == 0) return ok();
   if (!Y || !W || (d->Nu > 0 && !user) || (d->Ni > 0 && !item)) return fail(LL_ERR_INVALID_ARG, "null pointer");
@@ -474,15 +477,28 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
   // A candidate with no item rows still needs one (all-zero) slice so that its
   // result (the user contribution alone) is written.
   k.ni_sl = d->Ni > 0 ? (int32_t)((d->Ni + lk.kt - 1) / lk.kt) : 1;
-  // Candidates per work item: one workgroup per CU, and the user block is
-  // recomputed only once per work item.
   const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n;
-  const int64_t per_req = std::max<int64_t>(1, (info->cus + d->R * tiles - 1) / (d->R * tiles));
-  int64_t chunk = (d->C + per_req - 1) / per_req;
-  if (chunk < 1) chunk = 1;
-  k.chunk = (int32_t)chunk;
-  k.nchunks = (int32_t)((d->C + chunk - 1) / chunk);
-  const int64_t total = tiles * d->R * k.nchunks;
+  int64_t total;
+  if (offsets) {
+    // Equal contiguous ranges of the flat candidate axis, one per CU and
+    // output tile: the work is balanced whatever the request lengths; a range
+    // recomputes the user block of each request it touches (at most one more
+    // than the requests it holds whole).
+    k.offsets = offsets;
+    k.nranges = (int32_t)std::max<int64_t>(1, std::min<int64_t>(d->C, info->cus / std::max<int64_t>(1, tiles)));
+    k.chunk = 1;
+    k.nchunks = 1;
+    total = tiles * k.nranges;
+  } else {
+    // Candidates per work item: one workgroup per CU, and the user block is
+    // recomputed only once per work item.
+    const int64_t per_req = std::max<int64_t>(1, (info->cus + d->R * tiles - 1) / (d->R * tiles));
+    int64_t chunk = (d->C + per_req - 1) / per_req;
+    if (chunk < 1) chunk = 1;
+    k.chunk = (int32_t)chunk;
+    k.nchunks = (int32_t)((d->C + chunk - 1) / chunk);
+    total = tiles * d->R * k.nchunks;
+  }
   if (total >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "too many work items");
   k.total = (int32_t)total;
   k.y_bf16 = d->y_type == LL_BF16;
@@ -492,6 +508,40 @@ ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item,
   hipError_t e = launch_lincomp(k, grid, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "lincomp launch");
   return ok();
+}
+
+ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item, const void* W, void* Y,
+                      void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return lincomp_launch(d, nullptr, user, item, W, Y, stream);
+}
+
+ll_status lincomp_ragged_run(const lincomp_ragged_desc* g, const int64_t* offsets, const void* user,
+                             const void* item, const void* W, void* Y, void* stream) {
+  if (!g) return fail(LL_ERR_INVALID_ARG, "null desc");
+  lincomp_desc d;
+  memset(&d, 0, sizeof d);
+  d.R = g->R;
+  d.C = g->Ctot;
+  d.Nu = g->Nu;
+  d.Ni = g->Ni;
+  d.D = g->D;
+  d.Mo = g->Mo;
+  d.su_r = g->su_r;
+  d.su_n = g->su_n;
+  d.si_c = g->si_c;
+  d.si_n = g->si_n;
+  d.sw_n = g->sw_n;
+  d.sy_c = g->sy_c;
+  d.sy_m = g->sy_m;
+  d.y_type = g->y_type;
+  d.flags = g->flags;
+  if (!offsets && g->R > 0 && g->Ctot > 0) {
+    ll_status s = lincomp_check(&d, true);
+    return s != LL_OK ? s : fail(LL_ERR_INVALID_ARG, "null offsets");
+  }
+  return lincomp_launch(&d, offsets ? offsets : (const int64_t*)nullptr, user, item, W, Y, stream);
 }
 
 }  // extern "C"

@@ -183,3 +183,65 @@ def lincomp_workload(name: str = "lincomp_256x128") -> LincompCase:
     if name == "lincomp_small":
         return lincomp_case(3, 5, name=name, sub=1)
     raise KeyError(name)
+
+
+class RaggedLincompCase:
+    """Ragged requests: request r owns candidates offsets[r] .. offsets[r+1]-1
+    of a flat candidate axis.  user [R][Nu][D], item [Ctot][Ni][D],
+    W [Nu+Ni][Mo], Y [Ctot][Mo][D]; dense, last dim contiguous."""
+
+    def __init__(self, name, lengths, Nu, Ni, D, Mo, user, item, W):
+        self.name, self.Nu, self.Ni, self.D, self.Mo = name, Nu, Ni, D, Mo
+        self.lengths = np.asarray(lengths, dtype=np.int64)
+        self.R = int(self.lengths.shape[0])
+        self.offsets = np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int64)
+        self.Ctot = int(self.offsets[-1])
+        self.user, self.item, self.W = user, item, W
+
+    def request_of(self, g: int) -> int:
+        """The request owning flat candidate g."""
+        return int(np.searchsorted(self.offsets, g, side="right") - 1)
+
+    @property
+    def dims(self):
+        """(R, C, Nu, Ni, D, Mo) for the per-candidate oracle, C = Ctot."""
+        return (self.R, self.Ctot, self.Nu, self.Ni, self.D, self.Mo)
+
+    @property
+    def strides(self):
+        """Element strides; the flat candidate axis has no request stride."""
+        return dict(su_r=self.Nu * self.D, su_n=self.D, si_r=0, si_c=self.Ni * self.D, si_n=self.D,
+                    sw_n=self.Mo, sy_c=self.Mo * self.D, sy_m=self.D)
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """user once per request, every item row once, W once, Y once (bf16)."""
+        return 2 * (self.R * self.Nu * self.D + self.Ctot * self.Ni * self.D
+                    + (self.Nu + self.Ni) * self.Mo + self.Ctot * self.Mo * self.D)
+
+
+def ragged_lengths(R: int, median: float, sigma: float, *, seed: int, sub: int = 0, lo: int = 1,
+                   hi: int = 1024) -> np.ndarray:
+    """Candidates per request: round(median * exp(sigma * z)), z standard
+    normal (a lognormal length mix), clipped to [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(sub, 99, 0))))
+    z = rng.standard_normal(R)
+    return np.clip(np.rint(median * np.exp(sigma * z)), lo, hi).astype(np.int64)
+
+
+def lincomp_ragged_case(lengths, Nu=256, Ni=256, D=256, Mo=64, *, x_dist=("normal", 0.0, 0.1),
+                        w_dist=("normal", 0.0, 0.05), seed=6, sub=0, name="lincomp_ragged") -> RaggedLincompCase:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    R, Ctot = int(lengths.shape[0]), int(lengths.sum())
+    user = bf16_tensor(R * Nu * D, *x_dist, seed=seed, sub=sub, tensor=0)
+    item = bf16_tensor(Ctot * Ni * D, *x_dist, seed=seed, sub=sub, tensor=1)
+    W = bf16_tensor((Nu + Ni) * Mo, *w_dist, seed=seed, sub=sub, tensor=2)
+    return RaggedLincompCase(name, lengths, Nu, Ni, D, Mo, user, item, W)
+
+
+def lincomp_ragged_workload(name: str = "lincomp_ragged_256") -> RaggedLincompCase:
+    """256 requests, lognormal candidate counts (median 112, sigma 0.5: mean
+    about 127, so the total is close to the 256 x 128 workload)."""
+    if name == "lincomp_ragged_256":
+        return lincomp_ragged_case(ragged_lengths(256, 112.0, 0.5, seed=6), seed=6, name=name)
+    raise KeyError(name)

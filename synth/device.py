@@ -30,3 +30,15 @@ def lincomp_operands(case, device="cuda"):
                      device)
     W = to_device(c.W, (c.Nu + c.Ni, c.Mo), (c.Mo, 1), device)
     return user, item, W
+
+
+def ragged_operands(case, device="cuda"):
+    """user [R][Nu][D], item [Ctot][Ni][D], W, and the int64 offsets [R+1] on the device."""
+    import torch
+    c = case
+    z = np.zeros(8, np.uint16)
+    user = to_device(c.user if c.Nu else z, (c.R, c.Nu, c.D), (c.Nu * c.D, c.D, 1), device)
+    item = to_device(c.item if (c.Ni and c.Ctot) else z, (c.Ctot, c.Ni, c.D), (c.Ni * c.D, c.D, 1), device)
+    W = to_device(c.W, (c.Nu + c.Ni, c.Mo), (c.Mo, 1), device)
+    offsets = torch.from_numpy(c.offsets.copy()).to(device)
+    return user, item, W, offsets

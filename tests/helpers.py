@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from synth.device import gemm_operands, lincomp_operands, to_device, to_f64  # noqa: F401
+from synth.device import gemm_operands, lincomp_operands, ragged_operands, to_device, to_f64  # noqa: F401
 
 
 def sample_indices(M, N, n, seed, tile=256):
