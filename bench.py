@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256"}
+GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256", "gemm_4096_f16"}
 LINCOMP_NAMES = {"lincomp_256x128"}
 # The same workload given in the layer's original form: every candidate's
 # stacked input [user rows; item rows] materialised (no reuse possible).
@@ -100,7 +100,7 @@ def bench_gemm(name: str, steps: int, warmup: int):
     case = synth.gemm_workload(name)
     A, B = gemm_operands(case)
     _log(f"{name}: timing")
-    dt = torch.bfloat16 if case.out_dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[case.out_dtype]
     C = torch.empty((case.M, case.N), dtype=dt, device="cuda")
     plan = ll.plan_for(A, B, C)
     stream = torch.cuda.current_stream()
@@ -288,7 +288,7 @@ def main():
     also = []
     if not args.no_also:
         for name in ["ffn_up", "ffn_down", "lincomp_256x128", "lincomp_256x128_stacked", "lincomp_ragged_256",
-                     "edge", "skinny_splitk", "gemm_4096"]:
+                     "edge", "skinny_splitk", "gemm_4096_f16", "gemm_4096"]:
             if name == head:
                 continue
             torch.cuda.empty_cache()

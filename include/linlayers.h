@@ -59,7 +59,7 @@ typedef enum {
   LL_ERR_NO_DEVICE = 5     /* no HIP device is visible */
 } ll_status;
 
-typedef enum { LL_BF16 = 0, LL_F32 = 1 } ll_dtype;
+typedef enum { LL_BF16 = 0, LL_F32 = 1, LL_F16 = 2 /* IEEE binary16 */ } ll_dtype;
 
 /* gemm_desc.flags */
 #define LL_FLAG_PACK_A 0x1u /* always copy A into an aligned workspace layout first */
@@ -70,10 +70,12 @@ typedef enum { LL_BF16 = 0, LL_F32 = 1 } ll_dtype;
 /*
  * GEMM problem.  A[i][k] = A[i*stride_am + k*stride_ak] (0 <= i < M, 0 <= k < K),
  * B[k][j] = B[k*stride_bk + j*stride_bn], C[i][j] = C[i*stride_cm + j*stride_cn].
- * a_type and b_type must be LL_BF16; c_type is LL_BF16 or LL_F32.
+ * a_type and b_type: both LL_BF16 or both LL_F16 (the fp16 GEMMs of the
+ * tables on "Triton 3.7 permite extender el compilador de GPU sin forks");
+ * c_type is LL_BF16, LL_F16 or LL_F32.  Products are accumulated in fp32.
  * For A and for B, one of the two strides must be 1 (row- or column-major, any
- * leading dimension); C may use any positive strides.  bf16 C is rounded to
- * nearest even.
+ * leading dimension); C may use any positive strides.  16-bit C is rounded
+ * to nearest even (fp16 overflow gives infinity).
  */
 typedef struct {
   int64_t M, N, K;

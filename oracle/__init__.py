@@ -31,6 +31,9 @@ def _load():
         lib.oracle_get_threads.restype = ctypes.c_int
         lib.oracle_gemm_rows.argtypes = [_i64] * 3 + [_p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _p]
         lib.oracle_gemm_entries.argtypes = [_i64] * 3 + [_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _p, _p, _p]
+        lib.oracle_gemm_rows_fmt.argtypes = [ctypes.c_int] + lib.oracle_gemm_rows.argtypes
+        lib.oracle_gemm_entries_fmt.argtypes = [ctypes.c_int] + lib.oracle_gemm_entries.argtypes
+        lib.oracle_widen.argtypes = [ctypes.c_int, _i64, _p, _p]
         lc = [_i64] * 6 + [_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _i64, _p, _p, _p]
         lib.oracle_lincomp_naive.argtypes = lc + [_p]
         lib.oracle_lincomp_dedup.argtypes = lc
@@ -45,7 +48,7 @@ def _ptr(a: np.ndarray):
 def _u16(a) -> np.ndarray:
     a = np.ascontiguousarray(a)
     if a.dtype != np.uint16:
-        raise TypeError("oracle inputs are bf16 bit patterns (uint16)")
+        raise TypeError("oracle inputs are 16-bit bit patterns (uint16)")
     return a.reshape(-1)
 
 
@@ -57,19 +60,31 @@ def get_threads() -> int:
     return int(_load().oracle_get_threads())
 
 
-def gemm(M, N, K, A, sam, sak, B, sbk, sbn, *, rows=None, bound=True):
-    """Rows ``rows=(row0, nrows)`` (default: all) of C = A.B and of S = sum |a*b|."""
+FORMATS = {"bf16": 0, "f16": 2}  # element formats of the 16-bit inputs
+
+
+def widen(bits, fmt="bf16") -> np.ndarray:
+    """Exact fp64 values of 16-bit patterns in format ``fmt``."""
+    bits = _u16(bits)
+    out = np.empty(bits.shape[0], dtype=np.float64)
+    _load().oracle_widen(FORMATS[fmt], bits.shape[0], _ptr(bits), _ptr(out))
+    return out
+
+
+def gemm(M, N, K, A, sam, sak, B, sbk, sbn, *, rows=None, bound=True, fmt="bf16"):
+    """Rows ``rows=(row0, nrows)`` (default: all) of C = A.B and of S = sum |a*b|;
+    A and B hold ``fmt`` ("bf16" or "f16") bit patterns."""
     lib = _load()
     A, B = _u16(A), _u16(B)
     row0, nrows = (0, M) if rows is None else rows
     C = np.empty((nrows, N), dtype=np.float64)
     S = np.empty((nrows, N), dtype=np.float64) if bound else None
-    lib.oracle_gemm_rows(M, N, K, _ptr(A), sam, sak, _ptr(B), sbk, sbn, row0, nrows,
-                         _ptr(C), _ptr(S) if bound else None)
+    lib.oracle_gemm_rows_fmt(FORMATS[fmt], M, N, K, _ptr(A), sam, sak, _ptr(B), sbk, sbn, row0, nrows,
+                             _ptr(C), _ptr(S) if bound else None)
     return (C, S) if bound else C
 
 
-def gemm_entries(M, N, K, A, sam, sak, B, sbk, sbn, rows, cols):
+def gemm_entries(M, N, K, A, sam, sak, B, sbk, sbn, rows, cols, fmt="bf16"):
     """C[rows[e], cols[e]] and S at the same entries."""
     lib = _load()
     A, B = _u16(A), _u16(B)
@@ -77,7 +92,7 @@ def gemm_entries(M, N, K, A, sam, sak, B, sbk, sbn, rows, cols):
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     out = np.empty(rows.shape[0], dtype=np.float64)
     S = np.empty(rows.shape[0], dtype=np.float64)
-    lib.oracle_gemm_entries(M, N, K, _ptr(A), sam, sak, _ptr(B), sbk, sbn, rows.shape[0],
+    lib.oracle_gemm_entries_fmt(FORMATS[fmt], M, N, K, _ptr(A), sam, sak, _ptr(B), sbk, sbn, rows.shape[0],
                             _ptr(rows), _ptr(cols), _ptr(out), _ptr(S))
     return out, S
 
@@ -127,9 +142,9 @@ def lincomp_case(case, pairs, *, bound=True, naive=True):
 
 def gemm_case(case, *, rows=None, bound=True):
     return gemm(case.M, case.N, case.K, case.A, case.sam, case.sak, case.B, case.sbk, case.sbn,
-                rows=rows, bound=bound)
+                rows=rows, bound=bound, fmt=case.in_dtype)
 
 
 def gemm_case_entries(case, rows, cols):
     return gemm_entries(case.M, case.N, case.K, case.A, case.sam, case.sak, case.B, case.sbk,
-                        case.sbn, rows, cols)
+                        case.sbn, rows, cols, fmt=case.in_dtype)

@@ -8,6 +8,9 @@ TEST INFRASTRUCTURE ONLY.  For an output element with oracle value ``ref`` and
   half-unit-in-the-last-place of an 8-significant-bit bf16 value, i.e. the
   largest error of a round-to-nearest-even conversion.  A truncating
   conversion can err by almost a whole unit and therefore fails it.
+* fp16 output: the fp32 bound plus ``2**-11 * |ref|``, the half unit of an
+  11-significant-bit fp16 value (normal range; below it the absolute 1e-6
+  covers the subnormal half unit 2**-25).
 """
 from __future__ import annotations
 
@@ -18,6 +21,8 @@ def bound(ref: np.ndarray, S: np.ndarray, out_dtype: str) -> np.ndarray:
     b = 1e-3 * np.asarray(S, dtype=np.float64) + 1e-6
     if out_dtype == "bf16":
         b = b + 2.0 ** -8 * np.abs(np.asarray(ref, dtype=np.float64))
+    elif out_dtype == "f16":
+        b = b + 2.0 ** -11 * np.abs(np.asarray(ref, dtype=np.float64))
     elif out_dtype != "f32":
         raise ValueError(out_dtype)
     return b

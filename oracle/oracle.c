@@ -20,6 +20,29 @@ static double widen(uint16_t h) {
   return (double)f;
 }
 
+/* IEEE 754 binary16 -> fp64, exact, from the format's definition: sign bit,
+ * 5-bit exponent e (bias 15), 10-bit fraction m.  e = 0: m * 2^-24
+ * (subnormal or zero); 0 < e < 31: (1024 + m) * 2^(e - 25); e = 31: infinity
+ * (m = 0) or NaN. */
+static double widen_f16(uint16_t h) {
+  const int s = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+/* Element decoding by format: ORACLE_BF16 or ORACLE_F16. */
+static double widen_fmt(int fmt, uint16_t h) { return fmt == ORACLE_F16 ? widen_f16(h) : widen(h); }
+
+void oracle_widen(int fmt, int64_t n, const uint16_t* in, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = widen_fmt(fmt, in[i]);
+}
+
 void oracle_set_threads(int n) {
 #ifdef _OPENMP
   if (n > 0) omp_set_num_threads(n);
@@ -39,10 +62,10 @@ int oracle_get_threads(void) {
 /* C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j], k ascending.  The k loop sits
  * outside the j loop so that B is read along its rows; each C[i][j] still
  * receives its terms one by one in ascending k, exactly as the definition. */
-void oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
-                      const uint16_t* A, int64_t sam, int64_t sak,
-                      const uint16_t* B, int64_t sbk, int64_t sbn,
-                      int64_t row0, int64_t nrows, double* C, double* S) {
+void oracle_gemm_rows_fmt(int fmt, int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t sam, int64_t sak,
+                          const uint16_t* B, int64_t sbk, int64_t sbn,
+                          int64_t row0, int64_t nrows, double* C, double* S) {
   (void)M;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < nrows; ++r) {
@@ -53,14 +76,42 @@ void oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
     if (s)
       for (int64_t j = 0; j < N; ++j) s[j] = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-      const double a = widen(A[i * sam + k * sak]);
+      const double a = widen_fmt(fmt, A[i * sam + k * sak]);
       const uint16_t* brow = B + k * sbk;
       for (int64_t j = 0; j < N; ++j) {
-        const double p = a * widen(brow[j * sbn]);
+        const double p = a * widen_fmt(fmt, brow[j * sbn]);
         c[j] += p;
         if (s) s[j] += fabs(p);
       }
     }
+  }
+}
+
+void oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
+                      const uint16_t* A, int64_t sam, int64_t sak,
+                      const uint16_t* B, int64_t sbk, int64_t sbn,
+                      int64_t row0, int64_t nrows, double* C, double* S) {
+  oracle_gemm_rows_fmt(ORACLE_BF16, M, N, K, A, sam, sak, B, sbk, sbn, row0, nrows, C, S);
+}
+
+void oracle_gemm_entries_fmt(int fmt, int64_t M, int64_t N, int64_t K,
+                             const uint16_t* A, int64_t sam, int64_t sak,
+                             const uint16_t* B, int64_t sbk, int64_t sbn,
+                             int64_t n, const int64_t* rows, const int64_t* cols,
+                             double* out, double* S) {
+  (void)M;
+  (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t e = 0; e < n; ++e) {
+    const int64_t i = rows[e], j = cols[e];
+    double c = 0.0, s = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double p = widen_fmt(fmt, A[i * sam + k * sak]) * widen_fmt(fmt, B[k * sbk + j * sbn]);
+      c += p;
+      s += fabs(p);
+    }
+    out[e] = c;
+    if (S) S[e] = s;
   }
 }
 
@@ -69,20 +120,7 @@ void oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
                          const uint16_t* B, int64_t sbk, int64_t sbn,
                          int64_t n, const int64_t* rows, const int64_t* cols,
                          double* out, double* S) {
-  (void)M;
-  (void)N;
-#pragma omp parallel for schedule(dynamic, 16)
-  for (int64_t e = 0; e < n; ++e) {
-    const int64_t i = rows[e], j = cols[e];
-    double c = 0.0, s = 0.0;
-    for (int64_t k = 0; k < K; ++k) {
-      const double p = widen(A[i * sam + k * sak]) * widen(B[k * sbk + j * sbn]);
-      c += p;
-      s += fabs(p);
-    }
-    out[e] = c;
-    if (S) S[e] = s;
-  }
+  oracle_gemm_entries_fmt(ORACLE_BF16, M, N, K, A, sam, sak, B, sbk, sbn, n, rows, cols, out, S);
 }
 
 /* Per candidate, as the layer is stated: build the candidate's full input X by

@@ -5,10 +5,12 @@
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
  * header, table or helper with the HIP library, and never calls it.
  *
- * Inputs are bf16 bit patterns (uint16).  Each value is widened exactly
- * (bits << 16 is the fp32 pattern; fp32 -> fp64 is exact), every product of
- * two bf16 values is exact in fp64 (8 + 8 significant bits), and each output
- * is one sum taken in ascending index order.  S (optional) is the matching
+ * Inputs are bf16 bit patterns (uint16), or for the _fmt GEMM entry points
+ * IEEE binary16 (fp16) patterns.  Each value is widened exactly (bf16: bits
+ * << 16 is the fp32 pattern; fp16: decoded from its sign, exponent and
+ * fraction fields), every product of two such values is exact in fp64 (at
+ * most 11 + 11 significant bits), and each output is one sum taken in
+ * ascending index order.  S (optional) is the matching
  * sum of |products|, which sets the acceptance bound.
  *
  * Pages: "Triton 3.7 permite extender el compilador de GPU sin forks"
@@ -25,7 +27,13 @@
 extern "C" {
 #endif
 
+#define ORACLE_BF16 0
+#define ORACLE_F16 2 /* IEEE binary16 */
+
 void oracle_set_threads(int n);
+
+/* out[i] = exact fp64 value of the fmt-format pattern in[i]. */
+void oracle_widen(int fmt, int64_t n, const uint16_t* in, double* out);
 int oracle_get_threads(void);
 
 /* Rows [row0, row0 + nrows) of C = A.B into C[nrows][N] (row-major, fp64),
@@ -34,6 +42,17 @@ void oracle_gemm_rows(int64_t M, int64_t N, int64_t K,
                       const uint16_t* A, int64_t sam, int64_t sak,
                       const uint16_t* B, int64_t sbk, int64_t sbn,
                       int64_t row0, int64_t nrows, double* C, double* S);
+
+/* The same with A and B in format fmt (ORACLE_BF16 or ORACLE_F16). */
+void oracle_gemm_rows_fmt(int fmt, int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t sam, int64_t sak,
+                          const uint16_t* B, int64_t sbk, int64_t sbn,
+                          int64_t row0, int64_t nrows, double* C, double* S);
+void oracle_gemm_entries_fmt(int fmt, int64_t M, int64_t N, int64_t K,
+                             const uint16_t* A, int64_t sam, int64_t sak,
+                             const uint16_t* B, int64_t sbk, int64_t sbn,
+                             int64_t n, const int64_t* rows, const int64_t* cols,
+                             double* out, double* S);
 
 /* n single entries (rows[e], cols[e]) of C = A.B.  S may be NULL. */
 void oracle_gemm_entries(int64_t M, int64_t N, int64_t K,

@@ -25,7 +25,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 LL_OK, LL_ERR_INVALID_ARG, LL_ERR_UNSUPPORTED, LL_ERR_WORKSPACE, LL_ERR_HIP, LL_ERR_NO_DEVICE = range(6)
-LL_BF16, LL_F32 = 0, 1
+LL_BF16, LL_F32, LL_F16 = 0, 1, 2
 LL_FLAG_PACK_A = 0x1
 LL_FLAG_PACK_B = 0x2
 LL_FLAG_PRODUCER_CONSUMER = 0x4
@@ -160,6 +160,8 @@ def _dtype_code(dt) -> int:
         return LL_BF16
     if dt == torch.float32:
         return LL_F32
+    if dt == torch.float16:
+        return LL_F16
     raise TypeError(f"unsupported dtype {dt}")
 
 
@@ -213,7 +215,8 @@ def plan_for(A, B, C, flags: int = 0) -> GemmPlan:
 
 
 def gemm(A, B, out=None, out_dtype=None, flags: int = 0):
-    """C = A @ B for 2-D bf16 CUDA (HIP) tensors with any row/column-major strides."""
+    """C = A @ B for 2-D bf16 (or both fp16) CUDA (HIP) tensors with any
+    row/column-major strides; C is bf16 (default), fp16 or fp32."""
     torch = _torch()
     if out is None:
         out = torch.empty((A.shape[0], B.shape[1]), dtype=out_dtype or torch.bfloat16, device=A.device)

@@ -8,8 +8,21 @@ hipError_t launch_gemm_kk(int kind, const GemmKArgs& a, int grid, hipStream_t s)
 hipError_t launch_gemm_kn(int kind, const GemmKArgs& a, int grid, hipStream_t s);
 hipError_t launch_gemm_mk(int kind, const GemmKArgs& a, int grid, hipStream_t s);
 hipError_t launch_gemm_mn(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_kk_f16(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_kn_f16(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_mk_f16(int kind, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_mn_f16(int kind, const GemmKArgs& a, int grid, hipStream_t s);
 
-hipError_t launch_gemm(int layout, int kind, const GemmKArgs& args, int grid, hipStream_t stream) {
+hipError_t launch_gemm(int layout, int kind, int f16, const GemmKArgs& args, int grid, hipStream_t stream) {
+  if (f16) {
+    switch (layout) {
+      case 0: return launch_gemm_kk_f16(kind, args, grid, stream);
+      case 1: return launch_gemm_kn_f16(kind, args, grid, stream);
+      case 2: return launch_gemm_mk_f16(kind, args, grid, stream);
+      case 3: return launch_gemm_mn_f16(kind, args, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (layout) {
     case 0: return launch_gemm_kk(kind, args, grid, stream);
     case 1: return launch_gemm_kn(kind, args, grid, stream);
@@ -64,7 +77,7 @@ hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int
 // C[i][j] = sum over s = 0..splits-1 (ascending) of partial[s][i][j].
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ P, int splits,
                                                             int64_t M, int64_t N, void* __restrict__ C,
-                                                            int64_t ldcm, int64_t ldcn, int c_bf16) {
+                                                            int64_t ldcm, int64_t ldcn, int c_fmt) {
   const int64_t total = M * N;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
@@ -72,45 +85,47 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     for (int s = 1; s < splits; ++s) acc += P[(int64_t)s * total + e];
     const int64_t i = e / N, j = e - i * N;
     const int64_t o = i * ldcm + j * ldcn;
-    if (c_bf16)
+    if (c_fmt == 1)
       ((uint16_t*)C)[o] = f32_to_bf16_bits(acc);
+    else if (c_fmt == 2)
+      ((uint16_t*)C)[o] = f32_to_f16_bits(acc);
     else
       ((float*)C)[o] = acc;
   }
 }
 
 hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int64_t N, void* C,
-                                int64_t ldcm, int64_t ldcn, int c_bf16, hipStream_t stream) {
+                                int64_t ldcm, int64_t ldcn, int c_fmt, hipStream_t stream) {
   const int64_t total = M * N;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
   const int grid = (int)(blocks < 16384 ? blocks : 16384);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, partial, splits, M, N, C,
-                     ldcm, ldcn, c_bf16);
+                     ldcm, ldcn, c_fmt);
   return hipGetLastError();
 }
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(void* __restrict__ C, int64_t M, int64_t N,
-                                                        int64_t ldcm, int64_t ldcn, int c_bf16) {
+                                                        int64_t ldcm, int64_t ldcn, int c_fmt) {
   const int64_t total = M * N;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t i = e / N, j = e - i * N;
     const int64_t o = i * ldcm + j * ldcn;
-    if (c_bf16)
+    if (c_fmt)
       ((uint16_t*)C)[o] = 0;
     else
       ((float*)C)[o] = 0.f;
   }
 }
 
-hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_bf16,
+hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt,
                             hipStream_t stream) {
   const int64_t total = M * N;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
   const int grid = (int)(blocks < 16384 ? blocks : 16384);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldcm, ldcn, c_bf16);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldcm, ldcn, c_fmt);
   return hipGetLastError();
 }
 

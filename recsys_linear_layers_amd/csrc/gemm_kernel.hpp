@@ -39,6 +39,7 @@
 namespace ll {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -63,15 +64,17 @@ struct GemmKArgs {
   int64_t ldcm, ldcn;
   float* partial;     // split-K partials [splits][M][N], or null
   int32_t M, N;
-  int32_t c_bf16;
+  int32_t c_fmt;                // C elements: 0 fp32, 1 bf16, 2 fp16
   int32_t c_fast;               // 1: no partial, ldcn == 1, ldcm even, C 4-byte aligned (epilogue_fast)
   int32_t splits, kiters, kps;  // kiters, kps in units of KT
   int32_t tiles_m, tiles_n, group_m;
   int32_t total;
 };
 
-template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_>
+template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,
+          bool F16_ = false>
 struct GemmCfg {
+  static constexpr bool F16 = F16_;           // A and B are fp16 (else bf16); same bytes, another MFMA
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int KT = KT_;              // k elements per ring slot (32 or 64)
   static constexpr int KS = KT / 16;          // k16 MFMA steps per slot
@@ -423,6 +426,17 @@ __device__ __forceinline__ void load_frags(const char LL_LDS* slot, int kk, int 
                            : frag_mnmajor<Cfg::BN>(sB, wn0 + 32 * j, kk, lane);
 }
 
+// One 32x32x16 MFMA with fp32 accumulation; the fragments hold bf16 or, for
+// F16, fp16 bit patterns (the LDS path moves 16-bit elements either way).
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // One k16 step over the wave's FM x FN blocks of 32x32.  `first`
 // (wave-uniform) starts the tile's sums: the MFMA then takes 0 as its C
 // operand.  Without AGPR_ACC the accumulators are zeroed separately and
@@ -439,6 +453,7 @@ __device__ __forceinline__ void load_frags(const char LL_LDS* slot, int kk, int 
 template <class Cfg>
 __device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN], bool first) {
   if constexpr (Cfg::AGPR_ACC) {
+    static_assert(!Cfg::F16, "AGPR accumulators: bf16 only");
     if (first) {
 #pragma unroll
       for (int i = 0; i < Cfg::FM; ++i)
@@ -462,7 +477,7 @@ __device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma32<Cfg::F16>(f.a[i], f.b[j], acc[i][j]);
   }
 }
 
@@ -497,6 +512,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);  // v_cvt_f16_f32: round to nearest even
+}
+
+// 16-bit C element: bf16 (fmt 1) or fp16 (fmt 2), rounded to nearest even.
+template <int FMT>
+__device__ __forceinline__ uint16_t to_c16(float v) {
+  if constexpr (FMT == 2) return f32_to_f16_bits(v);
+  else return f32_to_bf16_bits(v);
+}
+
 // Swap with the neighbouring lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
 __device__ __forceinline__ float swap_pair(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF,
@@ -508,40 +534,55 @@ __device__ __forceinline__ float swap_pair(float v) {
 // registers); each lane keeps one 32-bit element offset.  bf16 C: the lane
 // pair holding columns d, d+1 swaps values so that each lane writes one
 // 4-byte (d, d+1) pair per row - whole 128-byte lines, half the stores.
+template <class Cfg, int FMT>
+__device__ __forceinline__ void epilogue_fast16(const GemmKArgs& p, const TileInfo& ti,
+                                                const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wm0, int wn0,
+                                                int lane) {
+  const int row0 = ti.m0 + wm0;  // wave-uniform
+  const int half = lane >> 5;
+  const bool odd = lane & 1;
+  const int col = ti.n0 + wn0 + (lane & 30);
+  // lane-dependent part: row offset 4*half (+2 for the odd lane), column
+  const int loff = (4 * half + (odd ? 2 : 0)) * (int)p.ldcm + col;
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint16_t* rowp = (uint16_t*)p.c + (int64_t)(row0 + 32 * i + 8 * g) * p.ldcm;
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        // the even lane sends rows 2, 3 and receives the odd lane's rows 0, 1
+        // (column d+1); the odd lane sends rows 0, 1 and receives rows 2, 3
+        const float s0 = swap_pair(odd ? v0 : v2);
+        const float s1 = swap_pair(odd ? v1 : v3);
+        const float a0 = odd ? s0 : v0, a1 = odd ? v2 : s0;
+        const float b0 = odd ? s1 : v1, b1 = odd ? v3 : s1;
+        const uint32_t pa = (uint32_t)to_c16<FMT>(a0) | ((uint32_t)to_c16<FMT>(a1) << 16);
+        const uint32_t pb = (uint32_t)to_c16<FMT>(b0) | ((uint32_t)to_c16<FMT>(b1) << 16);
+        *(uint32_t*)(rowp + loff + 32 * j) = pa;
+        *(uint32_t*)(rowp + p.ldcm + loff + 32 * j) = pb;
+      }
+    }
+}
+
+// Epilogue for a tile that lies wholly inside C, with C row-major
+// (ldcn == 1) and no split-K.  Row bases are wave-uniform (scalar
+// registers); each lane keeps one 32-bit element offset.  16-bit C: the lane
+// pair holding columns d, d+1 swaps values so that each lane writes one
+// 4-byte (d, d+1) pair per row - whole 128-byte lines, half the stores.
 template <class Cfg>
 __device__ __forceinline__ void epilogue_fast(const GemmKArgs& p, const TileInfo& ti,
                                               const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wm0, int wn0,
                                               int lane) {
-  const int row0 = ti.m0 + wm0;  // wave-uniform
-  const int half = lane >> 5;
-  if (p.c_bf16) {
-    const bool odd = lane & 1;
-    const int col = ti.n0 + wn0 + (lane & 30);
-    // lane-dependent part: row offset 4*half (+2 for the odd lane), column
-    const int loff = (4 * half + (odd ? 2 : 0)) * (int)p.ldcm + col;
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint16_t* rowp = (uint16_t*)p.c + (int64_t)(row0 + 32 * i + 8 * g) * p.ldcm;
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-          const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          // the even lane sends rows 2, 3 and receives the odd lane's rows 0, 1
-          // (column d+1); the odd lane sends rows 0, 1 and receives rows 2, 3
-          const float s0 = swap_pair(odd ? v0 : v2);
-          const float s1 = swap_pair(odd ? v1 : v3);
-          const float a0 = odd ? s0 : v0, a1 = odd ? v2 : s0;
-          const float b0 = odd ? s1 : v1, b1 = odd ? v3 : s1;
-          const uint32_t pa = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
-          const uint32_t pb = (uint32_t)f32_to_bf16_bits(b0) | ((uint32_t)f32_to_bf16_bits(b1) << 16);
-          *(uint32_t*)(rowp + loff + 32 * j) = pa;
-          *(uint32_t*)(rowp + p.ldcm + loff + 32 * j) = pb;
-        }
-      }
+  if (p.c_fmt == 1) {
+    epilogue_fast16<Cfg, 1>(p, ti, acc, wm0, wn0, lane);
+  } else if (p.c_fmt == 2) {
+    epilogue_fast16<Cfg, 2>(p, ti, acc, wm0, wn0, lane);
   } else {
-    const int loff = 4 * half * (int)p.ldcm + ti.n0 + wn0 + (lane & 31);
+    const int row0 = ti.m0 + wm0;  // wave-uniform
+    const int loff = 4 * (lane >> 5) * (int)p.ldcm + ti.n0 + wn0 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
@@ -587,8 +628,10 @@ __device__ __forceinline__ void epilogue_any(const GemmKArgs& p, const TileInfo&
         const float v = acc[i][j][r];
         if (row < p.M && col < p.N) {
           const int64_t o = (int64_t)row * p.ldcm + (int64_t)col * p.ldcn;
-          if (p.c_bf16)
+          if (p.c_fmt == 1)
             ((uint16_t*)p.c)[o] = f32_to_bf16_bits(v);
+          else if (p.c_fmt == 2)
+            ((uint16_t*)p.c)[o] = f32_to_f16_bits(v);
           else
             ((float*)p.c)[o] = v;
         }

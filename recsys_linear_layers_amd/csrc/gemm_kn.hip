@@ -3,6 +3,7 @@
 
 #define LL_AK true
 #define LL_BK false
+#define LL_F16 false
 
 namespace ll {
 

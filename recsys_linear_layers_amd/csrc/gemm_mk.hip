@@ -3,6 +3,7 @@
 
 #define LL_AK false
 #define LL_BK true
+#define LL_F16 false
 
 namespace ll {
 

@@ -39,10 +39,11 @@ inline int layout_index(bool a_kmajor, bool b_kmajor) { return (a_kmajor ? 0 : 2
 
 // Launch switch over every kind for one operand layout (instantiated once per layout).
 #define LL_KIND_CASE(name, bm, bn, kt, wm, wn, np, st) \
-  case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK>>(a, grid, s);
+  case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK, LL_F16>>(a, grid, s);
 
-// Launch `kind` for layout `layout` on `grid` workgroups.  Returns the launch status.
-hipError_t launch_gemm(int layout, int kind, const GemmKArgs& args, int grid, hipStream_t stream);
+// Launch `kind` for layout `layout` (bf16 or, f16 != 0, fp16 operands) on
+// `grid` workgroups.  Returns the launch status.
+hipError_t launch_gemm(int layout, int kind, int f16, const GemmKArgs& args, int grid, hipStream_t stream);
 
 // Fused linear-compression kernel (lincomp_kernel.hpp).
 struct LincompKArgs;
@@ -57,8 +58,8 @@ hipError_t launch_lincomp(const LincompKArgs& args, int grid, hipStream_t stream
 hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
                               uint16_t* dst, int64_t ldp, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int64_t N, void* C,
-                                int64_t ldcm, int64_t ldcn, int c_bf16, hipStream_t stream);
-hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_bf16,
+                                int64_t ldcm, int64_t ldcn, int c_fmt, hipStream_t stream);
+hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt,
                             hipStream_t stream);
 
 }  // namespace ll

@@ -58,6 +58,7 @@ struct LincompCfg {
   static constexpr int BM = BM_, BN = BN_, KT = KT_, KS = KT / 16;
   static constexpr int WM = 1, WN = WN_;
   static constexpr int NCONS = WN, NPROD = NPROD_, STAGES = STAGES_;
+  static constexpr bool F16 = false;  // bf16 inputs
   static constexpr int WAVES = NCONS + NPROD, THREADS = WAVES * 64;
   static constexpr int FM = BM / 32, FN = BN / WN / 32;
   static constexpr bool A_KMAJOR = false, B_KMAJOR = false;  // W^T and X are both MN-major in LDS

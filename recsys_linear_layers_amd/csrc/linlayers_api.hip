@@ -195,8 +195,10 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   if (d->flags & ~known) return fail(LL_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~known);
   if ((d->flags & LL_FLAG_PRODUCER_CONSUMER) && (d->flags & LL_FLAG_COOPERATIVE))
     return fail(LL_ERR_INVALID_ARG, "LL_FLAG_PRODUCER_CONSUMER and LL_FLAG_COOPERATIVE are exclusive");
-  if (d->a_type != LL_BF16 || d->b_type != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "A and B must be LL_BF16");
-  if (d->c_type != LL_BF16 && d->c_type != LL_F32) return fail(LL_ERR_UNSUPPORTED, "C must be LL_BF16 or LL_F32");
+  if ((d->a_type != LL_BF16 && d->a_type != LL_F16) || d->b_type != d->a_type)
+    return fail(LL_ERR_UNSUPPORTED, "A and B must both be LL_BF16 or both LL_F16");
+  if (d->c_type != LL_BF16 && d->c_type != LL_F16 && d->c_type != LL_F32)
+    return fail(LL_ERR_UNSUPPORTED, "C must be LL_BF16, LL_F16 or LL_F32");
   if (d->M >= (1ll << 31) || d->N >= (1ll << 31) || d->K >= (1ll << 31))
     return fail(LL_ERR_UNSUPPORTED, "dimensions must be below 2^31");
 
@@ -324,7 +326,7 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != p->device) return fail(LL_ERR_INVALID_ARG, "plan made for device %d, current is %d", p->device, dev);
-  const int64_t csz = d.c_type == LL_BF16 ? 2 : 4;
+  const int64_t csz = d.c_type == LL_F32 ? 4 : 2;
   const Span sc = span_of(C, d.M, d.N, d.stride_cm, d.stride_cn, csz);
   if (d.K > 0) {
     if (overlaps(sc, span_of(A, d.M, d.K, d.stride_am, d.stride_ak, 2)) ||
@@ -334,9 +336,9 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
   if (p->ws_bytes > 0 && overlaps(sc, Span{(uintptr_t)ws, (uintptr_t)ws + p->ws_bytes}))
     return fail(LL_ERR_INVALID_ARG, "C overlaps the workspace");
   hipStream_t st = (hipStream_t)stream;
-  const int cbf = d.c_type == LL_BF16;
+  const int cfmt = d.c_type == LL_BF16 ? 1 : d.c_type == LL_F16 ? 2 : 0;
   if (d.K == 0) {
-    e = launch_fill_zero(C, d.M, d.N, d.stride_cm, d.stride_cn, cbf, st);
+    e = launch_fill_zero(C, d.M, d.N, d.stride_cm, d.stride_cn, cfmt, st);
     return e == hipSuccess ? ok() : hip_fail(e, "fill_zero launch");
   }
   if ((!p->a.pack && ((uintptr_t)A & 15)) || (!p->b.pack && ((uintptr_t)B & 15)))
@@ -357,7 +359,7 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
   fill_operand_args(&k.b, B, p->b, d.N, d.K, p->Kp, ws);
   k.M = (int32_t)d.M;
   k.N = (int32_t)d.N;
-  k.c_bf16 = cbf;
+  k.c_fmt = cfmt;
   k.splits = p->splits;
   k.kiters = p->kiters;
   k.kps = p->kps;
@@ -374,10 +376,10 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
     k.c_fast = d.stride_cn == 1 && d.stride_cm % 2 == 0 && ((uintptr_t)C & 3) == 0 &&
                d.stride_cm * (d.M + 256) < (1ll << 31);
   }
-  e = launch_gemm(p->layout, p->kind, k, p->grid, st);
+  e = launch_gemm(p->layout, p->kind, d.a_type == LL_F16, k, p->grid, st);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   if (p->splits > 1) {
-    e = launch_splitk_reduce(k.partial, p->splits, d.M, d.N, C, d.stride_cm, d.stride_cn, cbf, st);
+    e = launch_splitk_reduce(k.partial, p->splits, d.M, d.N, C, d.stride_cm, d.stride_cn, cfmt, st);
     if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");
   }
   return ok();

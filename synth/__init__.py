@@ -41,7 +41,13 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _draw_chunk(seed: int, key: tuple, n: int, dist: str, p0: float, p1: float) -> np.ndarray:
+def f32_to_f16_rne(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to IEEE binary16 (numpy's conversion: round to nearest,
+    ties to even); returns uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _draw_chunk(seed: int, key: tuple, n: int, dist: str, p0: float, p1: float, fmt: str = "bf16") -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=key)))
     if dist == "uniform":
         x = rng.random(n, dtype=np.float32)
@@ -54,7 +60,7 @@ def _draw_chunk(seed: int, key: tuple, n: int, dist: str, p0: float, p1: float) 
         x = rng.integers(int(p0), int(p1) + 1, size=n).astype(np.float32)
     else:
         raise ValueError(dist)
-    return f32_to_bf16_rne(x)
+    return f32_to_f16_rne(x) if fmt == "f16" else f32_to_bf16_rne(x)
 
 
 def _threads() -> int:
@@ -64,7 +70,7 @@ def _threads() -> int:
 
 
 def bf16_tensor(numel: int, dist: str, p0: float, p1: float, *, seed: int, sub: int = 0,
-                tensor: int = 0) -> np.ndarray:
+                tensor: int = 0, fmt: str = "bf16") -> np.ndarray:
     """Flat uint16 buffer of ``numel`` bf16 values drawn per the module recipe.
 
     ``dist``/``p0``/``p1``: ("uniform", lo, hi), ("normal", mean-ignored, std) or
@@ -76,7 +82,7 @@ def bf16_tensor(numel: int, dist: str, p0: float, p1: float, *, seed: int, sub: 
     def work(i: int) -> None:
         lo = i * CHUNK
         hi = min(numel, lo + CHUNK)
-        out[lo:hi] = _draw_chunk(seed, (sub, tensor, i), hi - lo, dist, p0, p1)
+        out[lo:hi] = _draw_chunk(seed, (sub, tensor, i), hi - lo, dist, p0, p1, fmt)
 
     if nchunks <= 1:
         for i in range(nchunks):
@@ -95,11 +101,12 @@ def bf16_tensor(numel: int, dist: str, p0: float, p1: float, *, seed: int, sub: 
 class GemmCase:
     """C = A.B with A[i,k] = A_buf[i*sam + k*sak], B[k,j] = B_buf[k*sbk + j*sbn]."""
 
-    def __init__(self, name, M, N, K, A, sam, sak, B, sbk, sbn, out_dtype):
+    def __init__(self, name, M, N, K, A, sam, sak, B, sbk, sbn, out_dtype, in_dtype="bf16"):
         self.name, self.M, self.N, self.K = name, M, N, K
         self.A, self.sam, self.sak = A, sam, sak
         self.B, self.sbk, self.sbn = B, sbk, sbn
-        self.out_dtype = out_dtype  # "f32" or "bf16"
+        self.out_dtype = out_dtype  # "f32", "bf16" or "f16"
+        self.in_dtype = in_dtype    # format of A and B: "bf16" or "f16"
 
     @property
     def flops(self) -> float:
@@ -107,20 +114,21 @@ class GemmCase:
 
 
 def gemm_case(M, N, K, *, dist=("uniform", -1.0, 1.0), b_dist=None, seed=0, sub=0,
-              b_col_major=False, lda=None, ldb=None, out_dtype="f32", name="gemm") -> GemmCase:
-    """Row-major A [M][lda>=K]; B row-major [K][ldb>=N] or column-major [N][ldb>=K]."""
+              b_col_major=False, lda=None, ldb=None, out_dtype="f32", in_dtype="bf16", name="gemm") -> GemmCase:
+    """Row-major A [M][lda>=K]; B row-major [K][ldb>=N] or column-major [N][ldb>=K];
+    A and B in ``in_dtype`` ("bf16" or "f16")."""
     b_dist = b_dist or dist
     lda = K if lda is None else lda
-    A = bf16_tensor(M * lda, *dist, seed=seed, sub=sub, tensor=0)
+    A = bf16_tensor(M * lda, *dist, seed=seed, sub=sub, tensor=0, fmt=in_dtype)
     if b_col_major:
         ldb = K if ldb is None else ldb
-        B = bf16_tensor(N * ldb, *b_dist, seed=seed, sub=sub, tensor=1)
+        B = bf16_tensor(N * ldb, *b_dist, seed=seed, sub=sub, tensor=1, fmt=in_dtype)
         sbk, sbn = 1, ldb
     else:
         ldb = N if ldb is None else ldb
-        B = bf16_tensor(K * ldb, *b_dist, seed=seed, sub=sub, tensor=1)
+        B = bf16_tensor(K * ldb, *b_dist, seed=seed, sub=sub, tensor=1, fmt=in_dtype)
         sbk, sbn = ldb, 1
-    return GemmCase(name, M, N, K, A, lda, 1, B, sbk, sbn, out_dtype)
+    return GemmCase(name, M, N, K, A, lda, 1, B, sbk, sbn, out_dtype, in_dtype)
 
 
 GEMM_WORKLOADS = {
@@ -135,6 +143,9 @@ GEMM_WORKLOADS = {
                                     out_dtype="f32")),
     "skinny_splitk": (128, 8192, 65536, dict(dist=("uniform", -1.0, 1.0), seed=5, sub=1,
                                              out_dtype="f32")),
+    # fp16 operands and output (the pages' GEMM tables are fp16)
+    "gemm_4096_f16": (4096, 4096, 4096, dict(dist=("normal", 0.0, 1.0), seed=7, out_dtype="f16",
+                                             in_dtype="f16")),
 }
 
 

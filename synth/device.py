@@ -5,10 +5,11 @@ from __future__ import annotations
 import numpy as np
 
 
-def to_device(buf: np.ndarray, shape, strides, device="cuda"):
-    """A bf16 tensor viewing `buf` (uint16 bf16 patterns) with element strides."""
+def to_device(buf: np.ndarray, shape, strides, device="cuda", fmt="bf16"):
+    """A bf16 (or fmt "f16": fp16) tensor viewing `buf` (uint16 patterns) with element strides."""
     import torch
-    flat = torch.from_numpy(np.ascontiguousarray(buf).view(np.int16)).to(device).view(torch.bfloat16)
+    dt = torch.float16 if fmt == "f16" else torch.bfloat16
+    flat = torch.from_numpy(np.ascontiguousarray(buf).view(np.int16)).to(device).view(dt)
     return flat.as_strided(tuple(shape), tuple(strides))
 
 
@@ -17,8 +18,9 @@ def to_f64(t) -> np.ndarray:
 
 
 def gemm_operands(case, device="cuda"):
-    A = to_device(case.A, (case.M, case.K), (case.sam, case.sak), device)
-    B = to_device(case.B, (case.K, case.N), (case.sbk, case.sbn), device)
+    fmt = getattr(case, "in_dtype", "bf16")
+    A = to_device(case.A, (case.M, case.K), (case.sam, case.sak), device, fmt)
+    B = to_device(case.B, (case.K, case.N), (case.sbk, case.sbn), device, fmt)
     return A, B
 
 

@@ -21,7 +21,7 @@ def _run(case, flags=0, c_layout="row", out=None):
     import torch
     ll = _ll()
     A, B = gemm_operands(case)
-    dt = torch.float32 if case.out_dtype == "f32" else torch.bfloat16
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[case.out_dtype]
     if out is None:
         if c_layout == "row":
             C = torch.full((case.M, case.N), float("nan"), dtype=dt, device="cuda")
@@ -182,3 +182,65 @@ def test_skinny_split_k_integer_exact():
     rows, cols = sample_indices(M, N, 2048, 4)
     ref, _ = oracle.gemm_case_entries(c, rows, cols)
     assert np.array_equal(got[rows, cols], ref)
+
+
+# ---------------------------------------------------------------------------
+# fp16 operands (same data path, v_mfma_f32_32x32x16_f16)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(7, 9, 13), (200, 136, 72), (257, 263, 300), (130, 1030, 520)])
+@pytest.mark.parametrize("la,lb", [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")])
+def test_f16_small_shapes_every_layout(M, N, K, la, lb):
+    seed = M * 7919 + N * 31 + K
+    c = synth.gemm_case(M, N, K, seed=seed, b_col_major=(lb == "col"), out_dtype="f32", in_dtype="f16")
+    if la == "col":
+        c.A = synth.bf16_tensor(M * K, "uniform", -1.0, 1.0, seed=seed, tensor=5, fmt="f16")
+        c.sam, c.sak = 1, M
+    for out in ("f32", "f16", "bf16"):
+        c.out_dtype = out
+        _full_check(c)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (257, 263, 300)])
+def test_f16_integer_inputs_bit_exact(M, N, K):
+    c = synth.gemm_case(M, N, K, dist=("int", -4, 4), seed=M + N + K + 7, in_dtype="f16")
+    C = _run(c)
+    ref, _ = oracle.gemm_case(c)
+    assert np.array_equal(to_f64(C), ref)
+
+
+def test_f16_epilogue_rounds_to_nearest_even():
+    # integer-valued sums, exact in fp32, rounded once to fp16
+    c = synth.gemm_case(256, 256, 256, dist=("int", -8, 8), seed=98, out_dtype="f16", in_dtype="f16")
+    C = _run(c)
+    ref, _ = oracle.gemm_case(c)
+    want = synth.f32_to_f16_rne(ref.astype(np.float32))
+    import torch
+    got = C.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_f16_split_k_and_k_zero():
+    import torch
+    ll = _ll()
+    c = synth.gemm_case(128, 1024, 8192, seed=97, out_dtype="f16", in_dtype="f16")
+    _full_check(c)
+    A = torch.zeros((5, 0), dtype=torch.float16, device="cuda")
+    B = torch.zeros((0, 7), dtype=torch.float16, device="cuda")
+    C = torch.full((5, 7), 3.0, dtype=torch.float16, device="cuda")
+    ll.gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 0)
+
+
+def test_mixed_operand_types_rejected():
+    import torch
+    ll = _ll()
+    A = torch.zeros((8, 8), dtype=torch.float16, device="cuda")
+    B = torch.zeros((8, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ll.LLError):
+        ll.gemm(A, B)
+
+
+def test_gemm_4096_f16_sampled():
+    _sampled_check(synth.gemm_workload("gemm_4096_f16"), strip_rows=16)

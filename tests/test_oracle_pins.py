@@ -292,3 +292,89 @@ def test_golden_fixture():
     Bb = synth.f32_to_bf16_rne(B.astype(np.float32)).reshape(-1)
     Co, _ = oracle.gemm(M, N, K, Ab, K, 1, Bb, N, 1)
     assert np.array_equal(Co, C)
+
+
+# ---------------------------------------------------------------------------
+# fp16 operands
+# ---------------------------------------------------------------------------
+
+def test_f16_widening_matches_numpy_for_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = oracle.widen(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("bits,value", [(0x3C00, 1.0), (0xC000, -2.0), (0x7BFF, 65504.0), (0x0001, 2.0 ** -24),
+                                        (0x0400, 2.0 ** -14), (0x03FF, 1023 * 2.0 ** -24), (0x3555, 1365 / 4096),
+                                        (0x8000, -0.0), (0x7C00, float("inf"))])
+def test_f16_widening_closed_forms(bits, value):
+    got = oracle.widen(np.array([bits], dtype=np.uint16), "f16")[0]
+    assert got == value and np.signbit(got) == np.signbit(value)
+
+
+def _mixed_f16(rng, n):
+    """fp16 patterns with random sign, exponent in [-20, 12] (subnormals included) and mantissa."""
+    m = rng.random(n, dtype=np.float32) + np.float32(1.0)
+    e = rng.integers(-20, 13, n).astype(np.float32)
+    s = np.where(rng.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+    return synth.f32_to_f16_rne(s * m * np.exp2(e))
+
+
+def test_f16_bruteforce_exact_rationals():
+    rng = np.random.default_rng(4321)
+    for M in range(1, 7):
+        for N in range(1, 7):
+            for K in range(1, 9):
+                la, lb = rng.choice(["row", "col"]), rng.choice(["row", "col"])
+                na, sam, sak = _layout(rng, M, K, la)
+                nb, sbk, sbn = _layout(rng, K, N, lb)
+                A = _mixed_f16(rng, na)
+                B = _mixed_f16(rng, nb)
+                C, S = oracle.gemm(M, N, K, A, sam, sak, B, sbk, sbn, fmt="f16")
+                fa = [Fraction(float(v)) for v in A.view(np.float16)]
+                fb = [Fraction(float(v)) for v in B.view(np.float16)]
+                for i in range(M):
+                    for j in range(N):
+                        terms = [fa[i * sam + k * sak] * fb[k * sbk + j * sbn] for k in range(K)]
+                        exact = sum(terms, Fraction(0))
+                        sabs = sum((abs(t) for t in terms), Fraction(0))
+                        tol = K * U53 * float(sabs) * 1.0001
+                        assert abs(Fraction(C[i, j]) - exact) <= Fraction(tol), (M, N, K, i, j)
+                        assert abs(Fraction(S[i, j]) - sabs) <= Fraction(tol), (M, N, K, i, j)
+
+
+def test_f16_entries_agree_with_rows():
+    c = synth.gemm_case(37, 29, 70, seed=5, in_dtype="f16", dist=("normal", 0, 1.0))
+    C, S = oracle.gemm_case(c)
+    rows = np.array([0, 36, 5, 17], dtype=np.int64)
+    cols = np.array([0, 28, 3, 11], dtype=np.int64)
+    e, Se = oracle.gemm_case_entries(c, rows, cols)
+    assert np.array_equal(e, C[rows, cols]) and np.array_equal(Se, S[rows, cols])
+
+
+def test_f16_case_is_not_read_as_bf16():
+    # the same bits decoded as bf16 give other values: the format reaches the oracle
+    c = synth.gemm_case(8, 8, 8, seed=6, in_dtype="f16", dist=("normal", 0, 1.0))
+    C16, _ = oracle.gemm_case(c)
+    Cb, _ = oracle.gemm(8, 8, 8, c.A, c.sam, c.sak, c.B, c.sbk, c.sbn, fmt="bf16")
+    A = c.A.view(np.float16).astype(np.float64).reshape(8, 8)
+    B = c.B.view(np.float16).astype(np.float64).reshape(8, 8)
+    assert np.allclose(C16, A @ B, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(Cb, C16)
+
+
+def test_f16_acceptance_passes_rne_fails_truncation():
+    rng = np.random.default_rng(9)
+    ref = rng.standard_normal(4096) * 100.0
+    S = np.zeros_like(ref)
+    rne = ref.astype(np.float32).astype(np.float16).astype(np.float64)
+    assert acceptance.check(rne, ref, S, "f16")[0]
+    # truncation toward zero: clear the bits below fp16's last place
+    r32 = ref.astype(np.float32)
+    f16 = r32.astype(np.float16)
+    up = np.abs(f16.astype(np.float32)) > np.abs(r32)
+    trunc = np.where(up, np.nextafter(f16, np.float16(0)), f16).astype(np.float64)
+    assert not acceptance.check(trunc, ref, S, "f16")[0]
