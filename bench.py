@@ -38,6 +38,9 @@ LINCOMP_NAMES = {"lincomp_256x128"}
 STACKED_NAMES = {"lincomp_256x128_stacked": "lincomp_256x128"}
 # Ragged requests: 256 requests with a lognormal mix of candidate counts.
 RAGGED_NAMES = {"lincomp_ragged_256"}
+# FFN up-projection with its bias and GELU fused into the GEMM's epilogue,
+# against the same GEMM followed by separate bias-add and GELU passes.
+EPILOGUE_NAMES = {"ffn_up_bias_gelu": "ffn_up"}
 
 
 def _kernel_source_hash() -> str:
@@ -165,6 +168,33 @@ def bench_lincomp_ragged(name: str, steps: int, warmup: int):
     return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3), gbs=gbs)
 
 
+def bench_gemm_epilogue(name: str, steps: int, warmup: int):
+    import torch
+    import recsys_linear_layers_amd as ll
+    import synth
+    from synth.device import gemm_operands
+    case = synth.gemm_workload(EPILOGUE_NAMES[name])
+    A, B = gemm_operands(case)
+    bias = torch.randn(case.N, dtype=torch.float32, device="cuda") * 0.5
+    C = torch.empty((case.M, case.N), dtype=torch.bfloat16, device="cuda")
+    fused = ll.plan_for(A, B, C, 0, ll.LL_EPI_BIAS | ll.LL_EPI_GELU)
+    plain = ll.plan_for(A, B, C)
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    _log(f"{name}: timing the fused epilogue")
+    _, ev_fused = _time_launches(lambda: fused.run(A, B, C, h, bias=bias), steps, warmup, stream)
+    b16 = bias.to(torch.bfloat16)
+
+    def unfused():
+        plain.run(A, B, C, h)
+        torch.nn.functional.gelu(C + b16)
+
+    _log(f"{name}: timing GEMM + separate bias and GELU passes")
+    _, ev_unfused = _time_launches(unfused, steps, warmup, stream)
+    return dict(case=case, fused_ms=ev_fused, unfused_ms=ev_unfused, plan=fused.describe(),
+                tflops=case.flops / (ev_fused * 1e-3) / 1e12)
+
+
 def cpu_baseline_gemm(name: str, target_s: float = 12.0):
     """The oracle on the first rows of C, sized to about target_s of CPU time."""
     import oracle
@@ -287,12 +317,19 @@ def main():
 
     also = []
     if not args.no_also:
-        for name in ["ffn_up", "ffn_down", "lincomp_256x128", "lincomp_256x128_stacked", "lincomp_ragged_256",
+        for name in ["ffn_up", "ffn_down", "ffn_up_bias_gelu", "lincomp_256x128", "lincomp_256x128_stacked",
+                     "lincomp_ragged_256",
                      "edge", "skinny_splitk", "gemm_4096_f16", "gemm_4096"]:
             if name == head:
                 continue
             torch.cuda.empty_cache()
-            if name in RAGGED_NAMES:
+            if name in EPILOGUE_NAMES:
+                x = bench_gemm_epilogue(name, args.steps, args.warmup)
+                also.append(dict(workload=name, ms=round(x["fused_ms"], 4), value=round(x["tflops"], 1),
+                                 unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                 unfused_ms=round(x["unfused_ms"], 4),
+                                 fused_speedup=round(x["unfused_ms"] / x["fused_ms"], 3), plan=x["plan"]))
+            elif name in RAGGED_NAMES:
                 x = bench_lincomp_ragged(name, args.steps, args.warmup)
                 c = x["case"]
                 also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),

@@ -77,11 +77,29 @@ typedef enum { LL_BF16 = 0, LL_F32 = 1, LL_F16 = 2 /* IEEE binary16 */ } ll_dtyp
  * leading dimension); C may use any positive strides.  16-bit C is rounded
  * to nearest even (fp16 overflow gives infinity).
  */
+/*
+ * gemm_desc.epilogue: what happens to each fp32 sum z = (A.B)[i][j] before it
+ * is converted to c_type (page "Meta accélère un noyau GPU d'un facteur 4 avec
+ * TLX", section "Par où commencer dans votre équipe": fuse steps, then
+ * measure again).  LL_EPI_BIAS adds bias[j] (fp32, one per column of C,
+ * passed to gemm_run_ex); then the activation, evaluated in fp32:
+ *   LL_EPI_RELU  max(z, 0)
+ *   LL_EPI_GELU  z * Phi(z) = z/2 * (1 + erf(z / sqrt(2)))  (the exact form)
+ *   LL_EPI_SILU  z / (1 + exp(-z))
+ * 0: C = A.B as before.  Unknown bits -> LL_ERR_INVALID_ARG.
+ */
+#define LL_EPI_BIAS 0x1u
+#define LL_EPI_RELU 0x10u
+#define LL_EPI_GELU 0x20u
+#define LL_EPI_SILU 0x30u
+#define LL_EPI_ACT_MASK 0xF0u
+
 typedef struct {
   int64_t M, N, K;
   int64_t stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn;
   int32_t a_type, b_type, c_type; /* ll_dtype values */
   uint32_t flags;                 /* LL_FLAG_* ; unknown bits -> LL_ERR_INVALID_ARG */
+  uint32_t epilogue;              /* LL_EPI_* ; 0 for a plain product */
 } gemm_desc;
 
 typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
@@ -120,6 +138,15 @@ ll_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
  */
 ll_status gemm_run(const gemm_plan* plan, const void* A, const void* B, void* C,
                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gemm_run for a plan whose epilogue adds a bias: `bias` is a device array of
+ * N fp32 values (4-byte aligned), read once per output tile.  A plan without
+ * LL_EPI_BIAS ignores `bias`; gemm_run on a plan with LL_EPI_BIAS, or a null
+ * bias here, is LL_ERR_INVALID_ARG.  Otherwise as gemm_run.
+ */
+ll_status gemm_run_ex(const gemm_plan* plan, const void* A, const void* B, void* C, const float* bias,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 ll_status gemm_plan_destroy(gemm_plan* plan);
 

@@ -34,6 +34,7 @@ def _load():
         lib.oracle_gemm_rows_fmt.argtypes = [ctypes.c_int] + lib.oracle_gemm_rows.argtypes
         lib.oracle_gemm_entries_fmt.argtypes = [ctypes.c_int] + lib.oracle_gemm_entries.argtypes
         lib.oracle_widen.argtypes = [ctypes.c_int, _i64, _p, _p]
+        lib.oracle_epilogue.argtypes = [ctypes.c_int, _i64, _i64, _p, _p, _p]
         lc = [_i64] * 6 + [_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _i64, _p, _p, _p]
         lib.oracle_lincomp_naive.argtypes = lc + [_p]
         lib.oracle_lincomp_dedup.argtypes = lc
@@ -148,3 +149,32 @@ def gemm_case(case, *, rows=None, bound=True):
 def gemm_case_entries(case, rows, cols):
     return gemm_entries(case.M, case.N, case.K, case.A, case.sam, case.sak, case.B, case.sbk,
                         case.sbn, rows, cols, fmt=case.in_dtype)
+
+
+ACTS = {None: 0, "relu": 1, "gelu": 2, "silu": 3}
+
+
+def epilogue(C, S, bias, act, cols=None):
+    """act(C + bias) in fp64 and S + |bias| (new arrays).  C, S: [rows][N], or
+    1-D values at columns ``cols`` (sampled entries); bias: fp32 [N] or None."""
+    lib = _load()
+    C = np.array(C, dtype=np.float64, copy=True)
+    S = np.array(S, dtype=np.float64, copy=True) if S is not None else None
+    if cols is not None:
+        b = None if bias is None else np.ascontiguousarray(np.asarray(bias, dtype=np.float32)[np.asarray(cols)])
+        for k in range(C.shape[0]):
+            bk = None if b is None else b[k:k + 1]
+            ck = C[k:k + 1]
+            sk = S[k:k + 1] if S is not None else None
+            lib.oracle_epilogue(ACTS[act], 1, 1, _ptr(ck), _ptr(sk) if sk is not None else None,
+                                _ptr(bk) if bk is not None else None)
+            C[k] = ck[0]
+            if S is not None:
+                S[k] = sk[0]
+        return C, S
+    C = np.ascontiguousarray(C)
+    rows, N = C.shape
+    b = None if bias is None else np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+    lib.oracle_epilogue(ACTS[act], rows, N, _ptr(C), _ptr(S) if S is not None else None,
+                        _ptr(b) if b is not None else None)
+    return C, S

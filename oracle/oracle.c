@@ -205,3 +205,26 @@ void oracle_lincomp_dedup(int64_t R, int64_t C, int64_t Nu, int64_t Ni, int64_t 
     free(V);
   }
 }
+
+/* GEMM epilogue on n values of one row of C, in place, as stated: x = c +
+ * bias[j]; then ReLU max(x, 0), GELU x * Phi(x) = x/2 (1 + erf(x / sqrt 2)),
+ * or SiLU x / (1 + exp(-x)), all in fp64.  S[j] (the bound's sum of
+ * |terms|) gains |bias[j]|: the bias is one more term of the sum.  GELU is
+ * evaluated as x/2 erfc(-x / sqrt 2), the same value, so that large
+ * negative x keeps its relative accuracy. */
+void oracle_epilogue(int act, int64_t rows, int64_t N, double* C, double* S, const float* bias) {
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < N; ++j) {
+      const double b = bias ? (double)bias[j] : 0.0;
+      const double x = C[i * N + j] + b;
+      double y = x;
+      if (act == ORACLE_ACT_RELU)
+        y = x > 0.0 ? x : 0.0;
+      else if (act == ORACLE_ACT_GELU)
+        y = 0.5 * x * erfc(-x / sqrt(2.0)); /* = x/2 (1 + erf(x / sqrt 2)), without cancellation for x < 0 */
+      else if (act == ORACLE_ACT_SILU)
+        y = x / (1.0 + exp(-x));
+      C[i * N + j] = y;
+      if (S) S[i * N + j] += fabs(b);
+    }
+}

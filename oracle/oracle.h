@@ -54,6 +54,16 @@ void oracle_gemm_entries_fmt(int fmt, int64_t M, int64_t N, int64_t K,
                              int64_t n, const int64_t* rows, const int64_t* cols,
                              double* out, double* S);
 
+/* GEMM epilogue, in place on C[rows][N] (fp64): x = C + bias[j] (bias may be
+ * NULL), then the activation act (ORACLE_ACT_*), in fp64.  S (may be NULL)
+ * gains |bias[j]|.  Page "Meta accelere un noyau GPU d'un facteur 4 avec
+ * TLX", section on where to start (fuse steps, measure again). */
+#define ORACLE_ACT_NONE 0
+#define ORACLE_ACT_RELU 1
+#define ORACLE_ACT_GELU 2
+#define ORACLE_ACT_SILU 3
+void oracle_epilogue(int act, int64_t rows, int64_t N, double* C, double* S, const float* bias);
+
 /* n single entries (rows[e], cols[e]) of C = A.B.  S may be NULL. */
 void oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
                          const uint16_t* A, int64_t sam, int64_t sak,

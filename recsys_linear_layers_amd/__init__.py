@@ -26,6 +26,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 LL_OK, LL_ERR_INVALID_ARG, LL_ERR_UNSUPPORTED, LL_ERR_WORKSPACE, LL_ERR_HIP, LL_ERR_NO_DEVICE = range(6)
 LL_BF16, LL_F32, LL_F16 = 0, 1, 2
+LL_EPI_BIAS, LL_EPI_RELU, LL_EPI_GELU, LL_EPI_SILU = 0x1, 0x10, 0x20, 0x30
+ACTIVATIONS = {None: 0, "relu": LL_EPI_RELU, "gelu": LL_EPI_GELU, "silu": LL_EPI_SILU}
 LL_FLAG_PACK_A = 0x1
 LL_FLAG_PACK_B = 0x2
 LL_FLAG_PRODUCER_CONSUMER = 0x4
@@ -41,7 +43,7 @@ class GemmDesc(ctypes.Structure):
                 ("stride_am", _i64), ("stride_ak", _i64), ("stride_bk", _i64), ("stride_bn", _i64),
                 ("stride_cm", _i64), ("stride_cn", _i64),
                 ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32), ("c_type", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("epilogue", ctypes.c_uint32)]
 
 
 class LincompDesc(ctypes.Structure):
@@ -70,11 +72,12 @@ _lib.gemm_plan_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(GemmDesc)]
 _lib.gemm_plan_workspace_size.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
 _lib.gemm_plan_describe.argtypes = [_vp, ctypes.c_char_p, ctypes.c_size_t]
 _lib.gemm_run.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.gemm_run_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.gemm_plan_destroy.argtypes = [_vp]
 _lib.lincomp_workspace_size.argtypes = [ctypes.POINTER(LincompDesc), ctypes.POINTER(ctypes.c_size_t)]
 _lib.lincomp_run.argtypes = [ctypes.POINTER(LincompDesc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.lincomp_ragged_run.argtypes = [ctypes.POINTER(LincompRaggedDesc), _vp, _vp, _vp, _vp, _vp, _vp]
-for _f in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run",
+for _f in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run", "gemm_run_ex",
            "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "lincomp_ragged_run"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -122,6 +125,11 @@ def gemm_plan_describe(plan: int) -> str:
 
 def gemm_run(plan: int, A: int, B: int, C: int, workspace: int, ws_bytes: int, stream: int) -> None:
     _check(_lib.gemm_run(plan, A, B, C, workspace, ws_bytes, stream), "gemm_run")
+
+
+def gemm_run_ex(plan: int, A: int, B: int, C: int, bias: int, workspace: int, ws_bytes: int,
+                stream: int = 0) -> None:
+    _check(_lib.gemm_run_ex(plan, A, B, C, bias, workspace, ws_bytes, stream), "gemm_run_ex")
 
 
 def gemm_plan_destroy(plan: int) -> None:
@@ -178,11 +186,16 @@ class GemmPlan:
     def describe(self) -> str:
         return gemm_plan_describe(self.handle)
 
-    def run(self, A, B, C, stream: int | None = None) -> None:
+    def run(self, A, B, C, stream: int | None = None, bias=None) -> None:
         if stream is None:
             stream = _torch().cuda.current_stream(A.device).cuda_stream
-        gemm_run(self.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), self.workspace.data_ptr(),
-                 self.ws_bytes, stream)
+        if bias is not None or (self.desc.epilogue & LL_EPI_BIAS):
+            gemm_run_ex(self.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(),
+                        bias.data_ptr() if bias is not None else None, self.workspace.data_ptr(),
+                        self.ws_bytes, stream)
+        else:
+            gemm_run(self.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), self.workspace.data_ptr(),
+                     self.ws_bytes, stream)
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -194,18 +207,18 @@ class GemmPlan:
 _plans: dict = {}
 
 
-def gemm_desc_for(A, B, C, flags: int = 0) -> GemmDesc:
+def gemm_desc_for(A, B, C, flags: int = 0, epilogue: int = 0) -> GemmDesc:
     M, K = A.shape
     K2, N = B.shape
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
     sa, sb, sc = A.stride(), B.stride(), C.stride()
     return GemmDesc(M, N, K, sa[0], sa[1], sb[0], sb[1], sc[0], sc[1],
-                    _dtype_code(A.dtype), _dtype_code(B.dtype), _dtype_code(C.dtype), flags)
+                    _dtype_code(A.dtype), _dtype_code(B.dtype), _dtype_code(C.dtype), flags, epilogue)
 
 
-def plan_for(A, B, C, flags: int = 0) -> GemmPlan:
-    desc = gemm_desc_for(A, B, C, flags)
+def plan_for(A, B, C, flags: int = 0, epilogue: int = 0) -> GemmPlan:
+    desc = gemm_desc_for(A, B, C, flags, epilogue)
     key = (A.device.index, tuple(getattr(desc, f) for f, _ in GemmDesc._fields_))
     plan = _plans.get(key)
     if plan is None:
@@ -214,13 +227,20 @@ def plan_for(A, B, C, flags: int = 0) -> GemmPlan:
     return plan
 
 
-def gemm(A, B, out=None, out_dtype=None, flags: int = 0):
-    """C = A @ B for 2-D bf16 (or both fp16) CUDA (HIP) tensors with any
-    row/column-major strides; C is bf16 (default), fp16 or fp32."""
+def gemm(A, B, out=None, out_dtype=None, flags: int = 0, bias=None, act=None):
+    """C = act(A @ B + bias) for 2-D bf16 (or both fp16) CUDA (HIP) tensors with
+    any row/column-major strides; C is bf16 (default), fp16 or fp32.  bias:
+    optional fp32 [N]; act: None, "relu", "gelu" (exact) or "silu", applied
+    to the fp32 sums in the GEMM's epilogue."""
     torch = _torch()
     if out is None:
         out = torch.empty((A.shape[0], B.shape[1]), dtype=out_dtype or torch.bfloat16, device=A.device)
-    plan_for(A, B, out, flags).run(A, B, out)
+    epilogue = ACTIVATIONS[act]
+    if bias is not None:
+        if bias.dtype != torch.float32 or tuple(bias.shape) != (B.shape[1],) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 tensor of N values")
+        epilogue |= LL_EPI_BIAS
+    plan_for(A, B, out, flags, epilogue).run(A, B, out, bias=bias)
     return out
 
 

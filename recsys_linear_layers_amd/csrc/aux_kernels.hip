@@ -32,9 +32,33 @@ hipError_t launch_gemm(int layout, int kind, int f16, const GemmKArgs& args, int
   }
 }
 
+hipError_t launch_gemm_epi_kk(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_epi_kn(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_epi_mk(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_epi_mn(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_epi_kk_f16(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_epi_kn_f16(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_epi_mk_f16(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_epi_mn_f16(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s);
+
+hipError_t launch_gemm_epi(int layout, int kind, int f16, int epi, const GemmKArgs& args, int grid,
+                           hipStream_t stream) {
+  switch (layout * 2 + (f16 ? 1 : 0)) {
+    case 0: return launch_gemm_epi_kk(kind, epi, args, grid, stream);
+    case 1: return launch_gemm_epi_kk_f16(kind, epi, args, grid, stream);
+    case 2: return launch_gemm_epi_kn(kind, epi, args, grid, stream);
+    case 3: return launch_gemm_epi_kn_f16(kind, epi, args, grid, stream);
+    case 4: return launch_gemm_epi_mk(kind, epi, args, grid, stream);
+    case 5: return launch_gemm_epi_mk_f16(kind, epi, args, grid, stream);
+    case 6: return launch_gemm_epi_mn(kind, epi, args, grid, stream);
+    case 7: return launch_gemm_epi_mn_f16(kind, epi, args, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 const KindInfo& kind_info(int kind) {
-#define LL_KIND_INFO(name, bm, bn, kt, wm, wn, np, st) \
-  {bm, bn, kt, (wm * wn + np) * 64, st * (bm + bn) * kt * 2, st, np, #name},
+#define LL_KIND_INFO(name, bm, bn, kt, wm, wn, np, st, ep) \
+  {bm, bn, kt, (wm * wn + np) * 64, st * (bm + bn) * kt * 2, st, np, ep, #name},
   static const KindInfo table[KIND_COUNT] = {LL_GEMM_KINDS(LL_KIND_INFO)};
 #undef LL_KIND_INFO
   return table[kind];
@@ -75,57 +99,71 @@ hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int
 }
 
 // C[i][j] = sum over s = 0..splits-1 (ascending) of partial[s][i][j].
+// Bias and activation of the GEMM epilogue, selected at run time (these
+// kernels are element-wise).
+__device__ __forceinline__ float epi_rt(float z, float b, int act) {
+  switch (act) {
+    case 1: return epi<1>(z, b);
+    case 2: return epi<2>(z, b);
+    case 3: return epi<3>(z, b);
+    default: return epi<0>(z, b);
+  }
+}
+
+__device__ __forceinline__ void store_c(void* C, int64_t o, float v, int c_fmt) {
+  if (c_fmt == 1)
+    ((uint16_t*)C)[o] = f32_to_bf16_bits(v);
+  else if (c_fmt == 2)
+    ((uint16_t*)C)[o] = f32_to_f16_bits(v);
+  else
+    ((float*)C)[o] = v;
+}
+
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ P, int splits,
                                                             int64_t M, int64_t N, void* __restrict__ C,
-                                                            int64_t ldcm, int64_t ldcn, int c_fmt) {
+                                                            int64_t ldcm, int64_t ldcn, int c_fmt,
+                                                            const float* __restrict__ bias, int act) {
   const int64_t total = M * N;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     float acc = P[e];
     for (int s = 1; s < splits; ++s) acc += P[(int64_t)s * total + e];
     const int64_t i = e / N, j = e - i * N;
-    const int64_t o = i * ldcm + j * ldcn;
-    if (c_fmt == 1)
-      ((uint16_t*)C)[o] = f32_to_bf16_bits(acc);
-    else if (c_fmt == 2)
-      ((uint16_t*)C)[o] = f32_to_f16_bits(acc);
-    else
-      ((float*)C)[o] = acc;
+    store_c(C, i * ldcm + j * ldcn, epi_rt(acc, bias ? bias[j] : 0.f, act), c_fmt);
   }
 }
 
 hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int64_t N, void* C,
-                                int64_t ldcm, int64_t ldcn, int c_fmt, hipStream_t stream) {
+                                int64_t ldcm, int64_t ldcn, int c_fmt, const float* bias, int act,
+                                hipStream_t stream) {
   const int64_t total = M * N;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
   const int grid = (int)(blocks < 16384 ? blocks : 16384);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, partial, splits, M, N, C,
-                     ldcm, ldcn, c_fmt);
+                     ldcm, ldcn, c_fmt, bias, act);
   return hipGetLastError();
 }
 
+// K == 0: every sum is empty, so C = epilogue(0).
 __global__ void __launch_bounds__(256) fill_zero_kernel(void* __restrict__ C, int64_t M, int64_t N,
-                                                        int64_t ldcm, int64_t ldcn, int c_fmt) {
+                                                        int64_t ldcm, int64_t ldcn, int c_fmt,
+                                                        const float* __restrict__ bias, int act) {
   const int64_t total = M * N;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t i = e / N, j = e - i * N;
-    const int64_t o = i * ldcm + j * ldcn;
-    if (c_fmt)
-      ((uint16_t*)C)[o] = 0;
-    else
-      ((float*)C)[o] = 0.f;
+    store_c(C, i * ldcm + j * ldcn, epi_rt(0.f, bias ? bias[j] : 0.f, act), c_fmt);
   }
 }
 
-hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt,
-                            hipStream_t stream) {
+hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt, const float* bias,
+                            int act, hipStream_t stream) {
   const int64_t total = M * N;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
   const int grid = (int)(blocks < 16384 ? blocks : 16384);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldcm, ldcn, c_fmt);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldcm, ldcn, c_fmt, bias, act);
   return hipGetLastError();
 }
 

@@ -65,6 +65,8 @@ struct GemmKArgs {
   float* partial;     // split-K partials [splits][M][N], or null
   int32_t M, N;
   int32_t c_fmt;                // C elements: 0 fp32, 1 bf16, 2 fp16
+  const float* bias;            // per-column addend (fp32, N values), or null
+  int32_t act;                  // activation after the bias: 0 none, 1 ReLU, 2 GELU (erf form), 3 SiLU
   int32_t c_fast;               // 1: no partial, ldcn == 1, ldcm even, C 4-byte aligned (epilogue_fast)
   int32_t splits, kiters, kps;  // kiters, kps in units of KT
   int32_t tiles_m, tiles_n, group_m;
@@ -72,9 +74,14 @@ struct GemmKArgs {
 };
 
 template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,
-          bool F16_ = false>
+          bool F16_ = false, int EPI_ = 0>
 struct GemmCfg {
   static constexpr bool F16 = F16_;           // A and B are fp16 (else bf16); same bytes, another MFMA
+  // Fused epilogue, fixed per instantiation (a run-time choice among
+  // activations costs the whole kernel its registers): 0 none; else the
+  // per-column bias (if given) and activation EPI-1 (0 identity, 1 ReLU,
+  // 2 GELU, 3 SiLU) on every sum before it is stored.
+  static constexpr int EPI = EPI_;
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int KT = KT_;              // k elements per ring slot (32 or 64)
   static constexpr int KS = KT / 16;          // k16 MFMA steps per slot
@@ -516,6 +523,37 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);  // v_cvt_f16_f32: round to nearest even
 }
 
+// erf(u) for u >= 0 by the rational approximation of Abramowitz and Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (absolute error at most
+// 1.5e-7): 1 - (a1 t + ... + a5 t^5) exp(-u^2), t = 1 / (1 + p u).  Branch
+// free, so that an unrolled epilogue over every accumulator stays compact.
+__device__ __forceinline__ float erf_as(float u) {
+  const float t = __frcp_rn(1.f + 0.3275911f * u);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  return 1.f - poly * __expf(-u * u);
+}
+
+// Epilogue arithmetic on one fp32 sum z plus its column's bias b: the
+// activation ACT of z + b, in fp32.  GELU is the exact form z * Phi(z) =
+// z/2 (1 + erf(z / sqrt 2)); SiLU z / (1 + exp(-z)).
+template <int ACT>
+__device__ __forceinline__ float epi(float z, float b) {
+  const float x = z + b;
+  if constexpr (ACT == 1) {
+    return x > 0.f ? x : 0.f;
+  } else if constexpr (ACT == 2) {
+    const float e = erf_as(fabsf(x) * 0.70710678118654752f);
+    return 0.5f * x * (1.f + (x < 0.f ? -e : e));
+  } else if constexpr (ACT == 3) {
+    return x * __frcp_rn(1.f + __expf(-x));
+  } else {
+    return x;
+  }
+}
+
+__device__ __forceinline__ float bias_at(const GemmKArgs& p, int col) { return p.bias ? p.bias[col] : 0.f; }
+
 // 16-bit C element: bf16 (fmt 1) or fp16 (fmt 2), rounded to nearest even.
 template <int FMT>
 __device__ __forceinline__ uint16_t to_c16(float v) {
@@ -643,9 +681,30 @@ __device__ __forceinline__ void epilogue_any(const GemmKArgs& p, const TileInfo&
 // inside C, and (bf16) 4-byte aligned column pairs, i.e. an even row stride
 // and an even base offset.  p.c_fast carries the host's check of the
 // stride/alignment conditions.
+// Bias and activation, in place on the accumulators before the store (the
+// accumulators are cleared after the epilogue anyway).  Columns past N take
+// no bias (those elements are not stored).
+template <class Cfg, int ACT>
+__device__ __forceinline__ void apply_epi(const GemmKArgs& p, const TileInfo& ti, f32x16 (&acc)[Cfg::FM][Cfg::FN],
+                                          int wn0, int lane) {
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int col = ti.n0 + wn0 + (lane & 31) + 32 * j;
+    const float b = col < p.N ? bias_at(p, col) : 0.f;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = epi<ACT>(acc[i][j][r], b);
+  }
+}
+
+// Split-K partials stay raw sums (the reduce applies bias and activation).
 template <class Cfg>
-__device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti,
-                                         const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wm0, int wn0, int lane) {
+__device__ __forceinline__ void epilogue(const GemmKArgs& p, const TileInfo& ti, f32x16 (&acc)[Cfg::FM][Cfg::FN],
+                                         int wm0, int wn0, int lane) {
+  if constexpr (Cfg::EPI > 0) {
+    if (!p.partial) apply_epi<Cfg, Cfg::EPI - 1>(p, ti, acc, wn0, lane);
+  }
   if (p.c_fast && ti.m0 + Cfg::BM <= p.M && ti.n0 + Cfg::BN <= p.N)
     epilogue_fast<Cfg>(p, ti, acc, wm0, wn0, lane);
   else

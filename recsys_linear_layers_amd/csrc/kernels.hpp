@@ -12,14 +12,16 @@ namespace ll {
 // computing waves each own a (BM/WM) x (BN/WN) block of the tile; NPROD > 0
 // adds that many loading waves, NPROD == 0 makes every wave load and compute.
 // KT is the k depth of one ring slot.
-#define LL_GEMM_KINDS(X)                                                                              \
-  X(KIND_SQ8_K64, 256, 256, 64, 2, 4, 0, 2)    /* 8 waves (2 per SIMD) 128x64 each */               \
-  X(KIND_SQ8_K32, 256, 256, 32, 2, 4, 0, 4)    /* same, 4 x 32 KB slots */                          \
-  X(KIND_WIDE8_PC, 256, 128, 64, 2, 4, 4, 3)   /* 8 computing 128x32 + 4 loading waves */           \
-  X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 3)    /* 4 computing 128x64 + 4 loading waves */           \
-  X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 3)  /* 4 waves 128x64, load + compute */                 \
-  X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 3)    /* skinny M: 4 computing 64x128 + 4 loading */       \
-  X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 3) /* small problems: 4 waves 64x64 */
+// X(name, BM, BN, KT, computing-wave grid WM x WN, loading waves, ring slots,
+//   has fused-epilogue instantiations)
+#define LL_GEMM_KINDS(X)                                                                                 \
+  X(KIND_SQ8_K64, 256, 256, 64, 2, 4, 0, 2, 0)    /* 8 waves (2 per SIMD) 128x64 each */               \
+  X(KIND_SQ8_K32, 256, 256, 32, 2, 4, 0, 4, 0)    /* same, 4 x 32 KB slots */                          \
+  X(KIND_WIDE8_PC, 256, 128, 64, 2, 4, 4, 3, 0)   /* 8 computing 128x32 + 4 loading waves */           \
+  X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 3, 1)    /* 4 computing 128x64 + 4 loading waves */           \
+  X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 3, 0)  /* 4 waves 128x64, load + compute */                 \
+  X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 3, 1)    /* skinny M: 4 computing 64x128 + 4 loading */       \
+  X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 3, 0) /* small problems: 4 waves 64x64 */
 
 enum KernelKind {
 #define LL_KIND_ENUM(name, ...) name,
@@ -30,6 +32,7 @@ enum KernelKind {
 
 struct KindInfo {
   int bm, bn, kt, threads, lds, stages, nprod;
+  int epi;  // has fused-epilogue instantiations
   const char* name;
 };
 const KindInfo& kind_info(int kind);
@@ -38,12 +41,18 @@ const KindInfo& kind_info(int kind);
 inline int layout_index(bool a_kmajor, bool b_kmajor) { return (a_kmajor ? 0 : 2) | (b_kmajor ? 0 : 1); }
 
 // Launch switch over every kind for one operand layout (instantiated once per layout).
-#define LL_KIND_CASE(name, bm, bn, kt, wm, wn, np, st) \
+#define LL_KIND_CASE(name, bm, bn, kt, wm, wn, np, st, ep) \
   case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK, LL_F16>>(a, grid, s);
+#define LL_KIND_CASE_EPI(name, bm, bn, kt, wm, wn, np, st, ep) \
+  case name: return launch_epi<bm, bn, kt, wm, wn, np, st, ep>(a, epi, grid, s);
 
 // Launch `kind` for layout `layout` (bf16 or, f16 != 0, fp16 operands) on
 // `grid` workgroups.  Returns the launch status.
 hipError_t launch_gemm(int layout, int kind, int f16, const GemmKArgs& args, int grid, hipStream_t stream);
+// The same with fused epilogue `epi` (1 + activation code: 1 bias only, 2
+// ReLU, 3 GELU, 4 SiLU); only kinds marked in LL_GEMM_KINDS have these.
+hipError_t launch_gemm_epi(int layout, int kind, int f16, int epi, const GemmKArgs& args, int grid,
+                           hipStream_t stream);
 
 // Fused linear-compression kernel (lincomp_kernel.hpp).
 struct LincompKArgs;
@@ -58,8 +67,10 @@ hipError_t launch_lincomp(const LincompKArgs& args, int grid, hipStream_t stream
 hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
                               uint16_t* dst, int64_t ldp, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int64_t N, void* C,
-                                int64_t ldcm, int64_t ldcn, int c_fmt, hipStream_t stream);
-hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt,
+                                int64_t ldcm, int64_t ldcn, int c_fmt, const float* bias, int act,
+                                hipStream_t stream);
+hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt, const float* bias,
+                            int act,
                             hipStream_t stream);
 
 }  // namespace ll

@@ -108,6 +108,7 @@ struct gemm_plan {
   OperandPlan a, b;
   int64_t Kp;       // K rounded up to a multiple of 8
   int splits;
+  int epi;          // fused-epilogue instantiation (0: none, or the split-K reduce applies it)
   int kiters, kps;
   int tiles_m, tiles_n, total, grid, group_m;
   size_t ws_partial_off;
@@ -193,6 +194,9 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     return fail(LL_ERR_INVALID_ARG, "strides must be >= 1");
   const uint32_t known = LL_FLAG_PACK_A | LL_FLAG_PACK_B | LL_FLAG_PRODUCER_CONSUMER | LL_FLAG_COOPERATIVE;
   if (d->flags & ~known) return fail(LL_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~known);
+  const uint32_t act = d->epilogue & LL_EPI_ACT_MASK;
+  if ((d->epilogue & ~(LL_EPI_BIAS | LL_EPI_ACT_MASK)) || act > LL_EPI_SILU)
+    return fail(LL_ERR_INVALID_ARG, "unknown epilogue 0x%x", d->epilogue);
   if ((d->flags & LL_FLAG_PRODUCER_CONSUMER) && (d->flags & LL_FLAG_COOPERATIVE))
     return fail(LL_ERR_INVALID_ARG, "LL_FLAG_PRODUCER_CONSUMER and LL_FLAG_COOPERATIVE are exclusive");
   if ((d->a_type != LL_BF16 && d->a_type != LL_F16) || d->b_type != d->a_type)
@@ -244,6 +248,13 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
       if (strcmp(env, kind_info(i).name) == 0) kind = i;
     if (env[0] >= '0' && env[0] <= '9' && atoi(env) < KIND_COUNT) kind = atoi(env);
   }
+  // A fused epilogue runs in the kinds instantiated with it (the
+  // producer/consumer tiles of the same orientation rule).
+  if (d->epilogue && !kind_info(kind).epi) {
+    if (d->flags & LL_FLAG_COOPERATIVE)
+      return fail(LL_ERR_UNSUPPORTED, "fused epilogues run in the producer/consumer kernels only");
+    kind = M > N ? KIND_TALL_PC : KIND_WIDE_PC;
+  }
   p.kind = kind;
   const KindInfo& ki = kind_info(kind);
   p.tiles_m = (int)((M + ki.bm - 1) / ki.bm);
@@ -264,6 +275,8 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   }
   p.kps = (p.kiters + splits - 1) / splits;
   splits = p.kiters > 0 ? (p.kiters + p.kps - 1) / p.kps : 1;  // every split gets >= 1 k-step
+  // Split-K partials are raw sums; the reduce then applies the epilogue.
+  p.epi = (d->epilogue && splits == 1) ? (int)((d->epilogue & LL_EPI_ACT_MASK) >> 4) + 1 : 0;
   p.splits = splits;
   p.total = (int)(tiles * splits);
   p.grid = (int)(p.total < slots ? p.total : slots);
@@ -302,9 +315,9 @@ ll_status gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
                                "A:M-major,B:N-major"};
   snprintf(buf, len,
            "kernel=%s layout=%s packA=%d packB=%d tiles=%dx%d splitk=%d kiters=%d grid=%d cus=%d "
-           "group_m=%d ws=%zu",
+           "group_m=%d ws=%zu epilogue=0x%x fused=%d",
            k.name, lay[p->layout], (int)p->a.pack, (int)p->b.pack, p->tiles_m, p->tiles_n, p->splits,
-           p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes);
+           p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes, p->d.epilogue, p->epi);
   return ok();
 }
 
@@ -313,8 +326,27 @@ ll_status gemm_plan_destroy(gemm_plan* p) {
   return ok();
 }
 
+static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B, void* C, const float* bias,
+                               void* ws, size_t ws_bytes, void* stream);
+
+ll_status gemm_run_ex(const gemm_plan* p, const void* A, const void* B, void* C, const float* bias, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!p) return fail(LL_ERR_INVALID_ARG, "null plan");
+  const bool has_bias = p->d.epilogue & LL_EPI_BIAS;
+  if (has_bias && !bias) return fail(LL_ERR_INVALID_ARG, "the plan's epilogue adds a bias: bias is null");
+  if (has_bias && ((uintptr_t)bias & 3)) return fail(LL_ERR_INVALID_ARG, "bias must be 4-byte aligned");
+  return gemm_run_impl(p, A, B, C, has_bias ? bias : nullptr, ws, ws_bytes, stream);
+}
+
 ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, void* ws, size_t ws_bytes,
                    void* stream) {
+  if (p && (p->d.epilogue & LL_EPI_BIAS))
+    return fail(LL_ERR_INVALID_ARG, "the plan's epilogue adds a bias: use gemm_run_ex");
+  return gemm_run_impl(p, A, B, C, nullptr, ws, ws_bytes, stream);
+}
+
+static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B, void* C, const float* bias,
+                               void* ws, size_t ws_bytes, void* stream) {
   if (!p) return fail(LL_ERR_INVALID_ARG, "null plan");
   const gemm_desc& d = p->d;
   if (d.M == 0 || d.N == 0) return ok();
@@ -337,8 +369,9 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
     return fail(LL_ERR_INVALID_ARG, "C overlaps the workspace");
   hipStream_t st = (hipStream_t)stream;
   const int cfmt = d.c_type == LL_BF16 ? 1 : d.c_type == LL_F16 ? 2 : 0;
+  const int act = (int)((d.epilogue & LL_EPI_ACT_MASK) >> 4);  // 0 none, 1 ReLU, 2 GELU, 3 SiLU
   if (d.K == 0) {
-    e = launch_fill_zero(C, d.M, d.N, d.stride_cm, d.stride_cn, cfmt, st);
+    e = launch_fill_zero(C, d.M, d.N, d.stride_cm, d.stride_cn, cfmt, bias, act, st);
     return e == hipSuccess ? ok() : hip_fail(e, "fill_zero launch");
   }
   if ((!p->a.pack && ((uintptr_t)A & 15)) || (!p->b.pack && ((uintptr_t)B & 15)))
@@ -360,6 +393,8 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
   k.M = (int32_t)d.M;
   k.N = (int32_t)d.N;
   k.c_fmt = cfmt;
+  k.bias = bias;
+  k.act = act;
   k.splits = p->splits;
   k.kiters = p->kiters;
   k.kps = p->kps;
@@ -376,10 +411,11 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
     k.c_fast = d.stride_cn == 1 && d.stride_cm % 2 == 0 && ((uintptr_t)C & 3) == 0 &&
                d.stride_cm * (d.M + 256) < (1ll << 31);
   }
-  e = launch_gemm(p->layout, p->kind, d.a_type == LL_F16, k, p->grid, st);
+  e = p->epi ? launch_gemm_epi(p->layout, p->kind, d.a_type == LL_F16, p->epi, k, p->grid, st)
+             : launch_gemm(p->layout, p->kind, d.a_type == LL_F16, k, p->grid, st);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   if (p->splits > 1) {
-    e = launch_splitk_reduce(k.partial, p->splits, d.M, d.N, C, d.stride_cm, d.stride_cn, cfmt, st);
+    e = launch_splitk_reduce(k.partial, p->splits, d.M, d.N, C, d.stride_cm, d.stride_cn, cfmt, bias, act, st);
     if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");
   }
   return ok();

@@ -378,3 +378,54 @@ def test_f16_acceptance_passes_rne_fails_truncation():
     up = np.abs(f16.astype(np.float32)) > np.abs(r32)
     trunc = np.where(up, np.nextafter(f16, np.float16(0)), f16).astype(np.float64)
     assert not acceptance.check(trunc, ref, S, "f16")[0]
+
+
+# ---------------------------------------------------------------------------
+# GEMM epilogue: bias and activation
+# ---------------------------------------------------------------------------
+
+def test_epilogue_activations_match_scipy():
+    from scipy.special import expit, ndtr
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(2000) * 3.0, np.linspace(-40, 40, 801), [0.0, -0.0, 1e-300]])
+    C = x.reshape(1, -1)
+    for act, ref in [("relu", np.maximum(x, 0.0)), ("gelu", x * ndtr(x)), ("silu", x * expit(x)), (None, x)]:
+        got, _ = oracle.epilogue(C, None, None, act)
+        np.testing.assert_allclose(got[0], ref, rtol=1e-12, atol=1e-300)  # two fp64 libraries for Phi
+
+
+def test_epilogue_bias_is_added_exactly_and_counted_in_S():
+    rng = np.random.default_rng(22)
+    C = rng.standard_normal((3, 7))
+    S = np.abs(C) * 2
+    bias = rng.standard_normal(7).astype(np.float32)
+    got, S2 = oracle.epilogue(C, S, bias, None)
+    assert np.array_equal(got, C + bias.astype(np.float64))
+    assert np.array_equal(S2, S + np.abs(bias.astype(np.float64)))
+    # sampled entries take their column's bias
+    cols = np.array([6, 0, 3])
+    g1, _ = oracle.epilogue(C[0, cols], S[0, cols], bias, "gelu", cols=cols)
+    g2, _ = oracle.epilogue(C, S, bias, "gelu")
+    assert np.array_equal(g1, g2[0, cols])
+
+
+def test_epilogue_closed_forms():
+    C = np.array([[0.0, 1.0, -1.0, 50.0, -50.0]])
+    g, _ = oracle.epilogue(C, None, None, "gelu")
+    assert g[0, 0] == 0.0 and g[0, 3] == 50.0 and abs(g[0, 4]) < 1e-300 * 1e300 * 1e-500 + 1e-200
+    assert abs(g[0, 1] - 0.8413447460685429) < 1e-15 and abs(g[0, 2] + 0.15865525393145707) < 1e-15
+    s, _ = oracle.epilogue(C, None, None, "silu")
+    assert s[0, 0] == 0.0 and abs(s[0, 1] - 1 / (1 + np.exp(-1.0))) < 1e-16 and s[0, 3] == 50.0
+
+
+def test_activation_bound_is_what_the_slope_allows():
+    # a sum off by e moves GELU by at most 1.13 e: a shifted sum at the bound passes, 3x the bound fails
+    rng = np.random.default_rng(23)
+    z = rng.standard_normal(5000) * 2
+    S = np.abs(z) * 10 + 1
+    e = 1e-3 * S + 1e-6
+    ref, _ = oracle.epilogue(z.reshape(1, -1), None, None, "gelu")
+    near, _ = oracle.epilogue((z + e).reshape(1, -1), None, None, "gelu")
+    far, _ = oracle.epilogue((z + 3 * e).reshape(1, -1), None, None, "gelu")
+    assert acceptance.check(near[0], ref[0], S, "f32", "gelu")[0]
+    assert not acceptance.check(far[0], ref[0], S, "f32", "gelu")[0]
