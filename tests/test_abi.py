@@ -17,9 +17,9 @@ def _declared():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run",
-              "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "ll_status_string",
-              "ll_last_error"):
+    for n in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run", "gemm_run_ex",
+              "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "lincomp_ragged_run",
+              "ll_status_string", "ll_last_error"):
         assert n in names
 
 
@@ -75,6 +75,13 @@ def _has_gpu():
     (dict(stride_am=64, stride_ak=2), "LL_ERR_UNSUPPORTED"),
     (dict(stride_bk=3, stride_bn=5), "LL_ERR_UNSUPPORTED"),
     (dict(M=1 << 31), "LL_ERR_UNSUPPORTED"),
+    (dict(N=1 << 31), "LL_ERR_UNSUPPORTED"),
+    (dict(K=1 << 23, stride_am=1 << 23), "LL_ERR_UNSUPPORTED"),   # K too large for 32-bit tile offsets
+    (dict(a_type=2), "LL_ERR_UNSUPPORTED"),                        # fp16 A with bf16 B
+    (dict(a_type=2, b_type=2, c_type=3), "LL_ERR_UNSUPPORTED"),
+    (dict(epilogue=0x2), "LL_ERR_INVALID_ARG"),
+    (dict(epilogue=0x40), "LL_ERR_INVALID_ARG"),
+    (dict(epilogue=0x100), "LL_ERR_INVALID_ARG"),
 ])
 def test_plan_argument_checks(kw, expect):
     import recsys_linear_layers_amd as ll
@@ -122,3 +129,32 @@ def test_lincomp_workspace_and_checks():
         assert st != ll.LL_OK, kw
     st = ll._lib.lincomp_run(None, None, None, None, None, None, 0, None)
     assert st == ll.LL_ERR_INVALID_ARG
+
+
+def _rg(**kw):
+    import recsys_linear_layers_amd as ll
+    R, Ctot, Nu, Ni, D, Mo = 3, 10, 64, 64, 64, 16
+    base = dict(R=R, Ctot=Ctot, Nu=Nu, Ni=Ni, D=D, Mo=Mo, su_r=Nu * D, su_n=D, si_c=Ni * D, si_n=D, sw_n=Mo,
+                sy_c=Mo * D, sy_m=D, y_type=ll.LL_BF16, flags=0)
+    base.update(kw)
+    return ll.LincompRaggedDesc(**base)
+
+
+def test_ragged_argument_checks():
+    import recsys_linear_layers_amd as ll
+    run = ll._lib.lincomp_ragged_run
+    assert run(None, None, None, None, None, None, None) == ll.LL_ERR_INVALID_ARG
+    # null offsets with candidates to compute
+    assert run(ctypes.byref(_rg()), None, 16, 16, 16, 16, None) == ll.LL_ERR_INVALID_ARG
+    assert "offsets" in ll.ll_last_error()
+    for kw in (dict(R=-1), dict(D=12), dict(si_c=4), dict(su_r=-8), dict(flags=8), dict(y_type=7),
+               dict(sy_m=32)):
+        st = run(ctypes.byref(_rg(**kw)), 16, 16, 16, 16, 16, None)
+        assert st != ll.LL_OK, kw
+    # nothing to compute: no device needed
+    assert run(ctypes.byref(_rg(R=0, Ctot=0)), None, None, None, None, None, None) == ll.LL_OK
+
+
+def test_gemm_run_ex_null_plan():
+    import recsys_linear_layers_amd as ll
+    assert ll._lib.gemm_run_ex(None, None, None, None, None, None, 0, None) == ll.LL_ERR_INVALID_ARG
