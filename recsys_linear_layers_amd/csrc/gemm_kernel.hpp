@@ -107,18 +107,13 @@ struct GemmCfg {
   static_assert(STAGES >= 2, "stages");
   static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
-  // More accumulators than fit beside the fragments in 256 VGPRs are kept in
-  // AGPRs explicitly: the MFMAs are then inline asm with AGPR accumulator
-  // operands (left to itself the compiler places fragments in AGPRs and
-  // spills accumulators).
-  static constexpr bool AGPR_ACC = FM * FN * 16 > 128 && WAVES_PER_EU == 1 && NPROD == 0;
   // Fragment buffers of a computing wave: two (the next k16 step's reads
   // overlap this step's MFMAs) unless accumulators plus two buffers would
   // not fit the wave's register budget (512 / waves per SIMD, less about 24
   // for addresses and loop state); then one, and the other computing waves
   // on the SIMD cover the LDS latency.
   static constexpr int FRAG_BUFS = FM * FN * 16 + 2 * 4 * (FM + FN) + 24 <= 512 / WAVES_PER_EU / 8 * 8 ? 2 : 1;
-  static_assert(!AGPR_ACC || WAVES_PER_EU == 1, "AGPR accumulators need one wave per SIMD");
+  static_assert(FM * FN * 16 <= 128 || WAVES_PER_EU == 1, "accumulators beyond 128 registers need the full file");
 };
 
 // ---------------------------------------------------------------------------
@@ -444,65 +439,15 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// One k16 step over the wave's FM x FN blocks of 32x32.  `first`
-// (wave-uniform) starts the tile's sums: the MFMA then takes 0 as its C
-// operand.  Without AGPR_ACC the accumulators are zeroed separately and
-// `first` is ignored.
-//
-// AGPR_ACC: volatile inline asm on AGPR accumulators, so the MFMAs keep
-// program order with the kernel's other volatile asm (LDS DMA, the padding
-// before the epilogue).  The compiler does not pad hazards in front of an
-// asm MFMA: a VALU write of a fragment register (a v_mov assembling the two
-// halves of a transposed fragment) needs 2 wait states before an MFMA reads
-// it, so each MFMA carries an s_nop 1, which costs nothing while the previous
-// MFMA occupies the matrix pipe.  Back-to-back MFMAs accumulating into the
-// same registers need no padding.
+// One k16 step over the wave's FM x FN blocks of 32x32 (the accumulators are
+// cleared separately when a tile starts).
 template <class Cfg>
-__device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN], bool first) {
-  if constexpr (Cfg::AGPR_ACC) {
-    static_assert(!Cfg::F16, "AGPR accumulators: bf16 only");
-    if (first) {
+__device__ __forceinline__ void mfma_step(const Frags<Cfg>& f, f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
+  for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                       : "=a"(acc[i][j])
-                       : "v"(f.a[i]), "v"(f.b[j]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                       : "+a"(acc[i][j])
-                       : "v"(f.a[i]), "v"(f.b[j]));
-    }
-  } else {
-    (void)first;
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j)
-        acc[i][j] = mfma32<Cfg::F16>(f.a[i], f.b[j], acc[i][j]);
-  }
-}
-
-// Between the last MFMA of a tile and reads of its result: the longest
-// MFMA-write -> VALU-read requirement is below 20 wait states.  Each block
-// passes through a volatile asm that takes it as an in/out AGPR operand, so
-// no read of any block can be scheduled before the padding (AGPR_ACC only;
-// the compiler pads builtin MFMAs itself).
-template <class Cfg>
-__device__ __forceinline__ void acc_hazard_pad(f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
-  if constexpr (Cfg::AGPR_ACC) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j)
-        if (i + j > 0) asm volatile("" : "+a"(acc[i][j]));
-  }
+    for (int j = 0; j < Cfg::FN; ++j)
+      acc[i][j] = mfma32<Cfg::F16>(f.a[i], f.b[j], acc[i][j]);
 }
 
 template <int FM, int FN>
@@ -738,7 +683,6 @@ struct CompPos {
     ti = decode_tile<Cfg>(p, ct);
     ck = ti.kb;
   }
-  __device__ __forceinline__ bool tile_first() const { return ck == ti.kb; }
   __device__ __forceinline__ bool tile_end() const { return ck + 1 == ti.ke; }
   __device__ __forceinline__ bool has_next(const GemmKArgs& p, int stride) const {
     return !tile_end() || ct + stride < p.total;
@@ -810,7 +754,7 @@ __device__ __forceinline__ void consumer_loop(const GemmKArgs& p, char LL_LDS* s
   const int wm0 = (cw / Cfg::WN) * (Cfg::BM / Cfg::WM);
   const int wn0 = (cw % Cfg::WN) * (Cfg::BN / Cfg::WN);
   f32x16 acc[Cfg::FM][Cfg::FN];
-  if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+  zero_acc(acc);
   Frags<Cfg> f[NB];
   lds_barrier();
   load_frags<Cfg>(smem, 0, wm0, wn0, lane, f[0]);
@@ -819,7 +763,6 @@ __device__ __forceinline__ void consumer_loop(const GemmKArgs& p, char LL_LDS* s
   int slot = 0;
   while (true) {
     char LL_LDS* cur = smem + slot * Cfg::SLOT;
-    const bool tile_first = cc.tile_first();
     const bool tile_end = cc.tile_end();
     const bool has_next = cc.has_next(p, stride);
     const int nslot = slot + 1 == S ? 0 : slot + 1;
@@ -832,9 +775,9 @@ __device__ __forceinline__ void consumer_loop(const GemmKArgs& p, char LL_LDS* s
           lds_barrier();
           if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
         }
-        mfma_step<Cfg>(f[kk & 1], acc, kk == 0 && tile_first);
+        mfma_step<Cfg>(f[kk & 1], acc);
       } else {
-        mfma_step<Cfg>(f[0], acc, kk == 0 && tile_first);
+        mfma_step<Cfg>(f[0], acc);
         if (kk + 1 < KS) {
           load_frags<Cfg>(cur, kk + 1, wm0, wn0, lane, f[0]);
         } else {
@@ -844,9 +787,8 @@ __device__ __forceinline__ void consumer_loop(const GemmKArgs& p, char LL_LDS* s
       }
     }
     if (tile_end) {
-      acc_hazard_pad<Cfg>(acc);
       epilogue<Cfg>(p, cc.ti, acc, wm0, wn0, lane);
-      if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+      zero_acc(acc);
     }
     if (!has_next) break;
     cc.advance(p, stride);
@@ -879,7 +821,7 @@ __device__ __forceinline__ void coop_loop(const GemmKArgs& p, char LL_LDS* smem,
   lds_barrier();
 
   f32x16 acc[Cfg::FM][Cfg::FN];
-  if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+  zero_acc(acc);
   Frags<Cfg> f[2];
   load_frags<Cfg>(smem, 0, wm0, wn0, lane, f[0]);
 
@@ -890,7 +832,6 @@ __device__ __forceinline__ void coop_loop(const GemmKArgs& p, char LL_LDS* smem,
   cc.start(p, first);
   while (true) {
     char LL_LDS* cur = smem + slot * Cfg::SLOT;
-    const bool tile_first = cc.tile_first();
     const bool tile_end = cc.tile_end();
     const bool has_next = cc.has_next(p, stride);
     const int nslot = slot + 1 == S ? 0 : slot + 1;
@@ -912,13 +853,12 @@ __device__ __forceinline__ void coop_loop(const GemmKArgs& p, char LL_LDS* smem,
         }
         if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, wm0, wn0, lane, f[0]);
       }
-      mfma_step<Cfg>(f[kk & 1], acc, kk == 0 && tile_first);
+      mfma_step<Cfg>(f[kk & 1], acc);
     }
     if (tile_end) {
-      acc_hazard_pad<Cfg>(acc);
       epilogue<Cfg>(p, cc.ti, acc, wm0, wn0, lane);
       drain = true;
-      if constexpr (!Cfg::AGPR_ACC) zero_acc(acc);
+      zero_acc(acc);
     }
     if (!has_next) break;
     cc.advance(p, stride);

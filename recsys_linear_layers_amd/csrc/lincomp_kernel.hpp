@@ -68,7 +68,6 @@ struct LincompCfg {
   static constexpr int LOADERS = NPROD;
   static constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / NPROD;
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
-  static constexpr bool AGPR_ACC = false;
   static_assert(NPROD > 0, "the fused kernel uses separate loading waves");
   static_assert((A_BYTES / 1024) % NPROD == 0 && (B_BYTES / 1024) % NPROD == 0, "load split");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -363,7 +362,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         lds_barrier();
         if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, 0, wn0, lane, f[0]);
       }
-      mfma_step<Cfg>(f[kk & 1], acc, false);
+      mfma_step<Cfg>(f[kk & 1], acc);
     }
     if (p.dedup && cc.user_end(p)) {
 #pragma unroll
