@@ -1,0 +1,83 @@
+"""Contracts of the C ABI on the GPU: overlap rejection, workspace checks, and
+concurrent runs of one plan on two streams (plans are immutable; each run
+brings its own workspace)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import gemm_operands, lincomp_operands, to_f64
+from oracle import acceptance
+
+pytestmark = pytest.mark.gpu
+
+
+def test_c_overlapping_an_operand_is_rejected():
+    import torch
+    import recsys_linear_layers_amd as ll
+    buf = torch.zeros(2 * 64 * 64, dtype=torch.bfloat16, device="cuda")
+    A = buf[: 64 * 64].view(64, 64)
+    B = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    C = buf[32 * 64: 96 * 64].view(64, 64)  # shares half its rows with A
+    with pytest.raises(ll.LLError) as e:
+        ll.gemm(A, B, out=C)
+    assert e.value.status == ll.LL_ERR_INVALID_ARG
+
+
+def test_y_overlapping_an_input_is_rejected():
+    import torch
+    import recsys_linear_layers_amd as ll
+    c = synth.lincomp_case(2, 3, 64, 64, 64, 16, seed=80, name="ov")
+    user, item, W = lincomp_operands(c)
+    Y = item.reshape(-1)[: 2 * 3 * 16 * 64].view(2, 3, 16, 64)  # Y inside item
+    with pytest.raises(ll.LLError) as e:
+        ll.lincomp(user, item, W, out=Y)
+    assert e.value.status == ll.LL_ERR_INVALID_ARG
+
+
+def test_split_k_workspace_too_small_is_rejected():
+    import torch
+    import recsys_linear_layers_amd as ll
+    A = torch.zeros((128, 65536), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((65536, 1024), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((128, 1024), dtype=torch.float32, device="cuda")
+    plan = ll.plan_for(A, B, C)
+    assert plan.ws_bytes > 0 and "splitk=1 " not in plan.describe()
+    with pytest.raises(ll.LLError) as e:
+        ll.gemm_run(plan.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), plan.workspace.data_ptr(),
+                    plan.ws_bytes - 1, 0)
+    assert e.value.status == ll.LL_ERR_WORKSPACE
+
+
+def test_one_plan_two_streams_concurrently():
+    import torch
+    import recsys_linear_layers_amd as ll
+    # split-K shape, so each run needs its own workspace
+    c = synth.gemm_case(128, 1024, 8192, seed=81, out_dtype="f32")
+    A, B = gemm_operands(c)
+    C1 = torch.full((128, 1024), float("nan"), dtype=torch.float32, device="cuda")
+    C2 = torch.full((128, 1024), float("nan"), dtype=torch.float32, device="cuda")
+    plan = ll.plan_for(A, B, C1)
+    ws2 = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ll.gemm_run(plan.handle, A.data_ptr(), B.data_ptr(), C1.data_ptr(), plan.workspace.data_ptr(),
+                    plan.ws_bytes, s1.cuda_stream)
+        ll.gemm_run(plan.handle, A.data_ptr(), B.data_ptr(), C2.data_ptr(), ws2.data_ptr(), plan.ws_bytes,
+                    s2.cuda_stream)
+    torch.cuda.synchronize()
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(to_f64(C1), ref, S, "f32", "stream 1")
+    assert torch.equal(C1, C2)  # same plan, same order of sums: bit-identical
+
+
+def test_plan_describe_reports_the_choice():
+    import torch
+    import recsys_linear_layers_amd as ll
+    A = torch.zeros((4096, 4096), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((4096, 4096), dtype=torch.bfloat16, device="cuda")
+    d = ll.plan_for(A, A, C).describe()
+    assert "kernel=KIND_WIDE_PC" in d and "splitk=1" in d
+    d = ll.plan_for(A, A, C, 0, ll.LL_EPI_GELU).describe()
+    assert "fused=3" in d
