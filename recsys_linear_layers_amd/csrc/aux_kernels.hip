@@ -65,36 +65,62 @@ const KindInfo& kind_info(int kind) {
 }
 
 // dst[r][k] = src[r*s_r + k*s_k] for k < K, 0 for K <= k < ldp.  One thread per
-// 8-element (16-byte) chunk of dst.
+// 8-element (16-byte) chunk of dst; rows along grid y.  When the source row
+// is contiguous (s_k == 1) an interior chunk is read with aligned 32-bit
+// loads: four words if its first element is 4-byte aligned, else the five
+// words covering elements k0-1 .. k0+8, shifted by one element.  The first
+// and last chunk of a row use element loads, so no load leaves the row.
+__device__ __forceinline__ uint32_t pair16(uint32_t lo_word, uint32_t hi_word) {
+  return (lo_word >> 16) | (hi_word << 16);  // elements 1 of lo_word and 0 of hi_word
+}
+
 __global__ void __launch_bounds__(256) pack_kmajor_kernel(const uint16_t* __restrict__ src, int64_t s_r,
                                                           int64_t s_k, int64_t rows, int64_t K,
                                                           uint16_t* __restrict__ dst, int64_t ldp) {
   const int64_t chunks_per_row = ldp / 8;
-  const int64_t total = rows * chunks_per_row;
-  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
-       c += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = c / chunks_per_row;
-    const int64_t k0 = (c - r * chunks_per_row) * 8;
-    uint16_t v[8];
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const uint16_t* row = src + r * s_r;
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < chunks_per_row;
+         c += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t k0 = c * 8;
+      uint4 o;
+      if (s_k == 1 && k0 > 0 && k0 + 8 < K) {
+        const uintptr_t a = (uintptr_t)(row + k0);
+        if ((a & 3) == 0) {
+          const uint32_t* w = (const uint32_t*)a;
+          o.x = w[0];
+          o.y = w[1];
+          o.z = w[2];
+          o.w = w[3];
+        } else {
+          const uint32_t* w = (const uint32_t*)(a - 2);  // elements k0-1, k0 | k0+1, k0+2 | ...
+          const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3], w4 = w[4];
+          o.x = pair16(w0, w1);
+          o.y = pair16(w1, w2);
+          o.z = pair16(w2, w3);
+          o.w = pair16(w3, w4);
+        }
+      } else {
+        uint16_t v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < K) ? src[r * s_r + (k0 + e) * s_k] : (uint16_t)0;
-    uint4 o;
-    o.x = v[0] | ((uint32_t)v[1] << 16);
-    o.y = v[2] | ((uint32_t)v[3] << 16);
-    o.z = v[4] | ((uint32_t)v[5] << 16);
-    o.w = v[6] | ((uint32_t)v[7] << 16);
-    *(uint4*)(dst + r * ldp + k0) = o;
+        for (int e = 0; e < 8; ++e) v[e] = (k0 + e < K) ? row[(k0 + e) * s_k] : (uint16_t)0;
+        o.x = v[0] | ((uint32_t)v[1] << 16);
+        o.y = v[2] | ((uint32_t)v[3] << 16);
+        o.z = v[4] | ((uint32_t)v[5] << 16);
+        o.w = v[6] | ((uint32_t)v[7] << 16);
+      }
+      *(uint4*)(dst + r * ldp + k0) = o;
+    }
   }
 }
 
 hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
                               uint16_t* dst, int64_t ldp, hipStream_t stream) {
-  const int64_t total = rows * (ldp / 8);
-  if (total == 0) return hipSuccess;
-  const int64_t blocks = (total + 255) / 256;
-  const int grid = (int)(blocks < 65536 ? blocks : 65536);
-  hipLaunchKernelGGL(pack_kmajor_kernel, dim3(grid), dim3(256), 0, stream, src, s_r, s_k, rows, K, dst,
-                     ldp);
+  const int64_t chunks = ldp / 8;
+  if (rows == 0 || chunks == 0) return hipSuccess;
+  const int64_t bx = (chunks + 255) / 256;
+  const dim3 grid((unsigned)(bx < 64 ? bx : 64), (unsigned)(rows < 65535 ? rows : 65535));
+  hipLaunchKernelGGL(pack_kmajor_kernel, grid, dim3(256), 0, stream, src, s_r, s_k, rows, K, dst, ldp);
   return hipGetLastError();
 }
 
