@@ -106,6 +106,10 @@ struct GemmCfg {
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(STAGES >= 2, "stages");
   static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
+  // An M/N-contiguous operand tile is loaded in 1-KB instructions that each
+  // cover whole k-rows, so its width must divide 512 elements; kinds that
+  // break this (a 192-row tile) exist only for K-contiguous operands.
+  static constexpr bool VALID = (A_KMAJOR || 64 % (BM / 8) == 0) && (B_KMAJOR || 64 % (BN / 8) == 0);
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
   // Fragment buffers of a computing wave: two (the next k16 step's reads
   // overlap this step's MFMAs) unless accumulators plus two buffers would
@@ -216,7 +220,7 @@ struct TileGeom {
   static constexpr int CH = R / 8;               // MN-major: 16-byte chunks per k-row
   static constexpr int RPQ = KMAJ ? 64 / CPR : 64 / CH;
   static constexpr int PER = KMAJ ? (CPR == 8 ? 8 : 1) : (RPQ >= 4 ? 1 : 4 / RPQ);
-  static_assert(KMAJ || CH <= 64, "MN-major tile too wide");
+  static_assert(KMAJ || (CH <= 64 && 64 % CH == 0), "MN-major tile rows must split a 1-KB load evenly");
   // Per-lane byte offset of instruction q (q mod PER) relative to its first row.
   __device__ static __forceinline__ uint32_t lane_off(int q, int lane, int ld) {
     const int qq = PER == 1 ? 0 : q % PER;

@@ -9,8 +9,12 @@ namespace ll {
 
 template <class Cfg>
 static hipError_t launch_cfg(const GemmKArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_persistent<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, s, a);
-  return hipGetLastError();
+  if constexpr (!Cfg::VALID) {
+    return hipErrorInvalidValue;  // the plan never selects such a kind for this layout
+  } else {
+    hipLaunchKernelGGL(gemm_persistent<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+    return hipGetLastError();
+  }
 }
 
 hipError_t launch_gemm_mk_f16(int kind, const GemmKArgs& a, int grid, hipStream_t s) {

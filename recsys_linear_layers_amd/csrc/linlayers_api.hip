@@ -236,6 +236,24 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     kind = KIND_SMALL_COOP;
   else
     kind = M > N ? KIND_TALL_PC : KIND_WIDE_PC;
+  // Tile-count quantisation: a persistent grid runs ceil(tiles / CUs) passes
+  // of tiles, so on mid-size problems a larger tile that covers the problem
+  // in fewer passes wins despite more work per tile (4000x3000: 252 tiles of
+  // 192x256 in one pass against 384 of 128x256 in two).  The 192x256 kind
+  // (K-contiguous A only) replaces the 256x128 / 128x256 kinds when its
+  // passes times tile area is at least 3% smaller and neither would split K.
+  if (!(d->flags & (LL_FLAG_COOPERATIVE | LL_FLAG_PRODUCER_CONSUMER)) && !d->epilogue && p.a.kmajor &&
+      (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
+    auto passes = [&](int k) -> int64_t {
+      const KindInfo& ki = kind_info(k);
+      const int64_t t = ((M + ki.bm - 1) / ki.bm) * ((N + ki.bn - 1) / ki.bn);
+      return t * 2 <= p.cus ? -1 : (t + p.cus - 1) / p.cus;  // -1: the plan would split K
+    };
+    const int64_t pb = passes(kind), pt = passes(KIND_T192_PC);
+    const KindInfo& kb = kind_info(kind);
+    const KindInfo& kt = kind_info(KIND_T192_PC);
+    if (pb > 0 && pt > 0 && pt * kt.bm * kt.bn * 100 < pb * kb.bm * kb.bn * 97) kind = KIND_T192_PC;
+  }
   if (d->flags & LL_FLAG_COOPERATIVE) {
     if (kind == KIND_WIDE_PC) kind = KIND_SQ8_K64;
     else if (kind_info(kind).nprod > 0) kind = KIND_WIDE_COOP;
@@ -254,6 +272,14 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     if (d->flags & LL_FLAG_COOPERATIVE)
       return fail(LL_ERR_UNSUPPORTED, "fused epilogues run in the producer/consumer kernels only");
     kind = M > N ? KIND_TALL_PC : KIND_WIDE_PC;
+  }
+  {
+    // A tile whose M/N-contiguous operand rows do not divide a 1-KB load (192
+    // elements) exists only for K-contiguous operands (a forced kind may ask).
+    const KindInfo& kv = kind_info(kind);
+    if ((!p.a.kmajor && 64 % (kv.bm / 8) != 0) || (!p.b.kmajor && 64 % (kv.bn / 8) != 0))
+      return fail(LL_ERR_UNSUPPORTED, "kernel %s needs K-contiguous operands for its %dx%d tile", kv.name, kv.bm,
+                  kv.bn);
   }
   p.kind = kind;
   const KindInfo& ki = kind_info(kind);
