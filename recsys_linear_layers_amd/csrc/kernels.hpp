@@ -22,7 +22,7 @@ namespace ll {
   X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 3, 0)  /* 4 waves 128x64, load + compute */                 \
   X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 3, 1)    /* skinny M: 4 computing 64x128 + 4 loading */       \
   X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 3, 0) /* small problems: 4 waves 64x64 */                \
-  X(KIND_T192_PC, 192, 256, 64, 2, 4, 4, 2, 0)    /* 8 computing 96x64 + 4 loading; K-contiguous A */
+  X(KIND_T192_PC, 192, 256, 64, 2, 4, 4, 2, 1)    /* 8 computing 96x64 + 4 loading; K-contiguous A */
 
 enum KernelKind {
 #define LL_KIND_ENUM(name, ...) name,

@@ -242,7 +242,7 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   // 192x256 in one pass against 384 of 128x256 in two).  The 192x256 kind
   // (K-contiguous A only) replaces the 256x128 / 128x256 kinds when its
   // passes times tile area is at least 3% smaller and neither would split K.
-  if (!(d->flags & (LL_FLAG_COOPERATIVE | LL_FLAG_PRODUCER_CONSUMER)) && !d->epilogue && p.a.kmajor &&
+  if (!(d->flags & (LL_FLAG_COOPERATIVE | LL_FLAG_PRODUCER_CONSUMER)) && p.a.kmajor &&
       (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
     auto passes = [&](int k) -> int64_t {
       const KindInfo& ki = kind_info(k);

@@ -77,7 +77,7 @@ def test_rule_selection(M, N, K, want):
     assert (KIND in d) == want, d
 
 
-def test_rule_needs_k_contiguous_a_and_no_epilogue_or_forced_mode():
+def test_rule_needs_k_contiguous_a_and_no_forced_mode():
     ll = _ll()
     # M = 2904 keeps a column-major A direct (M-contiguous); with M not a
     # multiple of 8 it would be packed into a K-contiguous copy, where the rule applies
@@ -86,7 +86,8 @@ def test_rule_needs_k_contiguous_a_and_no_epilogue_or_forced_mode():
     assert KIND in _describe(2900, 2900, 136, a_col=True)
     assert KIND in _describe(2900, 2900, 136, b_col=True)
     assert KIND in _describe(2900, 2900, 136, in_t=ll.LL_F16, c_t=ll.LL_F16)
-    assert KIND not in _describe(2900, 2900, 136, epilogue=ll.LL_EPI_GELU)
+    assert KIND in _describe(2900, 2900, 136, epilogue=ll.LL_EPI_GELU)
+    assert KIND in _describe(2900, 2900, 136, epilogue=ll.LL_EPI_BIAS | ll.LL_EPI_SILU)
     assert KIND not in _describe(2900, 2900, 136, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
     assert KIND not in _describe(2900, 2900, 136, flags=ll.LL_FLAG_COOPERATIVE)
 
@@ -144,3 +145,36 @@ def test_forced_on_column_major_a_is_refused(forced_kind):
         _describe(304, 300, 64, a_col=True)   # M % 8 == 0: A stays M-contiguous (no pack)
     assert e.value.status == ll.LL_ERR_UNSUPPORTED
     assert "K-contiguous" in ll.ll_last_error()
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu", "silu"])
+def test_selected_fused_epilogue(act):
+    """Bias + activation fused into the 192x256 kind, on a shape the rule selects."""
+    import torch
+    ll = _ll()
+    c = synth.gemm_case(2900, 2900, 136, seed=194, dist=("normal", 0.0, 1.0), out_dtype="bf16")
+    A, B = gemm_operands(c)
+    bias = torch.linspace(-2.0, 2.0, c.N, dtype=torch.float32, device="cuda")
+    C = torch.full((c.M, c.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ll.gemm(A, B, out=C, bias=bias, act=act)
+    torch.cuda.synchronize()
+    epi = ll.LL_EPI_BIAS | {"relu": ll.LL_EPI_RELU, "gelu": ll.LL_EPI_GELU, "silu": ll.LL_EPI_SILU}[act]
+    assert KIND in ll.plan_for(A, B, C, 0, epi).describe()
+    ref, S = oracle.gemm_case(c)
+    ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+    acceptance.assert_close(to_f64(C), ref, S, "bf16", f"2900x2900x136 bias+{act}", act=act)
+
+
+def test_forced_fused_epilogue_small(forced_kind):
+    import torch
+    ll = _ll()
+    c = synth.gemm_case(257, 263, 300, seed=195, dist=("normal", 0.0, 1.0), out_dtype="f32")
+    A, B = gemm_operands(c)
+    bias = torch.linspace(-1.0, 1.0, c.N, dtype=torch.float32, device="cuda")
+    C = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
+    ll.gemm(A, B, out=C, bias=bias, act="gelu")
+    torch.cuda.synchronize()
+    assert KIND in ll.plan_for(A, B, C, 0, ll.LL_EPI_BIAS | ll.LL_EPI_GELU).describe()
+    ref, S = oracle.gemm_case(c)
+    ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), "gelu")
+    acceptance.assert_close(to_f64(C), ref, S, "f32", "257x263x300 bias+gelu forced", act="gelu")
