@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256", "gemm_4096_f16"}
+GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256", "gemm_4096_f16", "gemm_3000"}
+# workloads also timed with the kind the plan chose before its tile-count rule
+TILE_RULE_NAMES = {"gemm_3000": "KIND_WIDE_PC"}
 LINCOMP_NAMES = {"lincomp_256x128"}
 # The same workload given in the layer's original form: every candidate's
 # stacked input [user rows; item rows] materialised (no reuse possible).
@@ -94,7 +96,9 @@ def _time_launches(fn, steps: int, warmup: int, stream):
     return wall, start.elapsed_time(end) / steps
 
 
-def bench_gemm(name: str, steps: int, warmup: int):
+def bench_gemm(name: str, steps: int, warmup: int, force_kind: str | None = None):
+    """force_kind: time the plan with this kernel kind instead of the plan's own
+    choice (LL_GEMM_KIND, read when a plan is made; the forced plan is not kept)."""
     import torch
     import recsys_linear_layers_amd as ll
     import synth
@@ -102,10 +106,17 @@ def bench_gemm(name: str, steps: int, warmup: int):
     _log(f"{name}: generating inputs")
     case = synth.gemm_workload(name)
     A, B = gemm_operands(case)
-    _log(f"{name}: timing")
+    _log(f"{name}: timing" + (f" with {force_kind}" if force_kind else ""))
     dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[case.out_dtype]
     C = torch.empty((case.M, case.N), dtype=dt, device="cuda")
-    plan = ll.plan_for(A, B, C)
+    if force_kind:
+        os.environ["LL_GEMM_KIND"] = force_kind
+        try:
+            plan = ll.GemmPlan(ll.gemm_desc_for(A, B, C), A.device)
+        finally:
+            del os.environ["LL_GEMM_KIND"]
+    else:
+        plan = ll.plan_for(A, B, C)
     stream = torch.cuda.current_stream()
     wall, ev = _time_launches(lambda: plan.run(A, B, C, stream.cuda_stream), steps, warmup, stream)
     tflops = case.flops / (ev * 1e-3) / 1e12
@@ -319,11 +330,19 @@ def main():
     if not args.no_also:
         for name in ["ffn_up", "ffn_down", "ffn_up_bias_gelu", "lincomp_256x128", "lincomp_256x128_stacked",
                      "lincomp_ragged_256",
-                     "edge", "skinny_splitk", "gemm_4096_f16", "gemm_4096"]:
+                     "edge", "skinny_splitk", "gemm_3000", "gemm_4096_f16", "gemm_4096"]:
             if name == head:
                 continue
             torch.cuda.empty_cache()
-            if name in EPILOGUE_NAMES:
+            if name in TILE_RULE_NAMES:
+                x = bench_gemm(name, args.steps, args.warmup)
+                y = bench_gemm(name, args.steps, args.warmup, force_kind=TILE_RULE_NAMES[name])
+                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["tflops"], 1),
+                                 unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                 without_rule_ms=round(y["kernel_ms"], 4),
+                                 tile_rule_speedup=round(y["kernel_ms"] / x["kernel_ms"], 3), plan=x["plan"],
+                                 plan_without_rule=y["plan"]))
+            elif name in EPILOGUE_NAMES:
                 x = bench_gemm_epilogue(name, args.steps, args.warmup)
                 also.append(dict(workload=name, ms=round(x["fused_ms"], 4), value=round(x["tflops"], 1),
                                  unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),

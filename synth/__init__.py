@@ -143,6 +143,9 @@ GEMM_WORKLOADS = {
                                     out_dtype="f32")),
     "skinny_splitk": (128, 8192, 65536, dict(dist=("uniform", -1.0, 1.0), seed=5, sub=1,
                                              out_dtype="f32")),
+    # mid-size: 288 tiles of 256x128 leave a second pass 1/8 full; the plan's
+    # tile-count rule takes 192 tiles of 192x256 in one pass instead
+    "gemm_3000": (3000, 3000, 3000, dict(dist=("normal", 0.0, 1.0), seed=11, out_dtype="bf16")),
     # fp16 operands and output (the pages' GEMM tables are fp16)
     "gemm_4096_f16": (4096, 4096, 4096, dict(dist=("normal", 0.0, 1.0), seed=7, out_dtype="f16",
                                              in_dtype="f16")),

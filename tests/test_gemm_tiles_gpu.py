@@ -64,6 +64,7 @@ def _run(case, flags=0):
 
 @pytest.mark.parametrize("M,N,K,want", [
     (2900, 2900, 136, True),      # 276 tiles of 256x128 (2 passes) vs 192 of 192x256 (1 pass)
+    (3000, 3000, 3000, True),     # 288 tiles of 256x128 (2 passes) vs 192 of 192x256 (1 pass)
     (4000, 3000, 1000, True),     # 384 of 128x256 (2 passes) vs 252 of 192x256 (1 pass)
     (4096, 4096, 4096, False),    # 512 tiles of 256x128: 2 whole passes
     (16384, 28672, 8192, False),  # FFN up
@@ -100,6 +101,20 @@ def test_selected_full_parity(out):
     assert KIND in desc, desc
     ref, S = oracle.gemm_case(c)
     acceptance.assert_close(to_f64(C), ref, S, out, f"2900x2900x136 {out}")
+
+
+def test_gemm_3000_workload_sampled():
+    """The benchmark's mid-size workload, at its full size, in the kind the rule picks."""
+    c = synth.gemm_workload("gemm_3000")
+    C, desc = _run(c)
+    assert KIND in desc, desc
+    got = to_f64(C)
+    rows, cols = sample_indices(c.M, c.N, 4096, seed=4, tile=192)
+    ref, S = oracle.gemm_case_entries(c, rows, cols)
+    acceptance.assert_close(got[rows, cols], ref, S, "bf16", "gemm_3000 samples")
+    for r0 in (0, 2880, c.M - 8):   # first rows, the last row of tiles, the ragged end
+        ref, S = oracle.gemm_case(c, rows=(r0, 8))
+        acceptance.assert_close(got[r0:r0 + 8], ref, S, "bf16", f"gemm_3000 strip {r0}")
 
 
 def test_selected_mid_shape_sampled():
