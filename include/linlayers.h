@@ -108,6 +108,16 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * Validate `desc` and choose the kernel configuration (tile shape, stage
  * count, wave roles, split-K factor, grid) for the CURRENT HIP device.
  * On success *out receives a new plan.
+ * Tile choice: 256x128 or 128x256 tiles with separate loading waves (the
+ * 256-long side along the shorter of M and N); 128x256 for M <= 128; 128x128
+ * for M*N <= 2^20.  The persistent grid runs ceil(tiles / CUs) passes of
+ * tiles, so when A is K-contiguous (or packed) and 192x256 tiles cover the
+ * problem in passes x tile area at least 3% smaller, without a K split,
+ * those are used instead.  K is split when the tiles fill fewer than half of
+ * the CUs.  The environment variable LL_GEMM_KIND (a kernel name as printed
+ * by gemm_plan_describe, or its index) forces a kernel for configuration
+ * sweeps; a forced 192-row tile with an M-contiguous A gives
+ * LL_ERR_UNSUPPORTED.
  * Errors: LL_ERR_INVALID_ARG (null out/desc, negative size, zero or negative
  * stride, unknown flag bits), LL_ERR_UNSUPPORTED (dtype, neither stride of A
  * or of B equal to 1, device not gfx950), LL_ERR_NO_DEVICE, LL_ERR_HIP.
