@@ -4,7 +4,8 @@
  *
  * Operations (definitions from the pages this library follows):
  *
- *  - gemm_*   : C = A.B with bf16 A and B, fp32 accumulation, fp32 or bf16 C.
+ *  - gemm_*   : C = act(A.B + bias) with bf16 (or fp16) A and B, fp32
+ *               accumulation, fp32, bf16 or fp16 C; bias and activation optional.
  *               The problem is stated as on the page "Triton 3.7 permite
  *               extender el compilador de GPU sin forks" (listings in the
  *               sections "NVIDIA H100 (Hopper): GEMM persistente" and
@@ -135,8 +136,8 @@ ll_status gemm_plan_workspace_size(const gemm_plan* plan, size_t* bytes);
 ll_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
 
 /*
- * C = A.B on `stream`.  A, B: bf16 device buffers; C: device buffer of
- * c_type.  Unless the plan packs an operand (LL_FLAG_PACK_*, or a layout that
+ * C = A.B on `stream`.  A, B: device buffers of a_type (bf16 or fp16); C:
+ * device buffer of c_type.  Unless the plan packs an operand (LL_FLAG_PACK_*, or a layout that
  * needs it: leading dimension not a multiple of 8, K-contiguous operand with
  * K not a multiple of 8, M- or N-contiguous operand whose M or N is not a
  * multiple of 8), that operand's pointer must be 16-byte aligned.
@@ -145,6 +146,9 @@ ll_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
  * misaligned operand, C overlapping A or B, current device differs from the
  * plan's), LL_ERR_WORKSPACE (ws_bytes below gemm_plan_workspace_size or a
  * null workspace with a non-zero requirement), LL_ERR_HIP (launch failure).
+ * The call only launches kernels on `stream` (pack, GEMM, split-K reduce or
+ * the K == 0 fill): it allocates nothing and records no memset or copy, so
+ * it may be captured into a HIP graph; replays reuse the captured pointers.
  */
 ll_status gemm_run(const gemm_plan* plan, const void* A, const void* B, void* C,
                    void* workspace, size_t ws_bytes, void* stream);
@@ -204,6 +208,8 @@ ll_status lincomp_workspace_size(const lincomp_desc* desc, size_t* bytes);
  * Errors: LL_ERR_INVALID_ARG (null desc/pointer, negative size, stride or
  * alignment rule above broken, Y overlapping an input), LL_ERR_UNSUPPORTED
  * (y_type, device), LL_ERR_WORKSPACE, LL_ERR_NO_DEVICE, LL_ERR_HIP.
+ * The call launches one kernel on `stream` and allocates nothing, so it may
+ * be captured into a HIP graph.
  */
 ll_status lincomp_run(const lincomp_desc* desc, const void* user, const void* item,
                       const void* W, void* Y, void* workspace, size_t ws_bytes,

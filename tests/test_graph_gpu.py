@@ -1,0 +1,93 @@
+"""Launches captured in a HIP graph replay the eager results bit for bit.
+
+The library's run calls launch kernels only (no allocation, no memset), so a
+caller can capture them on its stream.  Each graph is replayed several times
+with unrelated eager work and synchronisations in between, and every replay is
+compared with the eager result of the same call (same kernels, same order of
+summation, so the results are identical)."""
+import pytest
+
+import synth
+from synth.device import gemm_operands, lincomp_operands
+
+pytestmark = pytest.mark.gpu
+
+
+def _ll():
+    import recsys_linear_layers_amd as ll
+    return ll
+
+
+def _replay_check(run, out, replays=3):
+    """run() launches on torch's current stream and writes `out`."""
+    import torch
+    run()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up off the default stream before capture
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    x = torch.randn(512, 512, device="cuda")
+    for i in range(replays):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), eager.view(torch.uint8)), f"replay {i} differs"
+        x = x @ x.t() / 512.0          # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+def _gemm_case_run(case, flags=0, bias=None, act=None):
+    import torch
+    ll = _ll()
+    A, B = gemm_operands(case)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[case.out_dtype]
+    C = torch.empty((case.M, case.N), dtype=dt, device="cuda")
+    epi = ll.ACTIVATIONS[act] | (ll.LL_EPI_BIAS if bias is not None else 0)
+    plan = ll.plan_for(A, B, C, flags, epi)   # plan and workspace made before capture
+    return plan, (lambda: plan.run(A, B, C, bias=bias)), C
+
+
+def test_gemm_graph_replay():
+    plan, run, C = _gemm_case_run(synth.gemm_case(1000, 1500, 700, seed=31, dist=("normal", 0.0, 1.0),
+                                                  out_dtype="bf16"))
+    _replay_check(run, C)
+
+
+def test_gemm_split_k_graph_replay():
+    # two kernels per call: partial tiles, then the ordered reduce
+    plan, run, C = _gemm_case_run(synth.gemm_case(128, 2048, 8192, seed=32, out_dtype="f32"))
+    assert "splitk=1 " not in plan.describe()
+    _replay_check(run, C)
+
+
+def test_gemm_packed_graph_replay():
+    # odd leading dimensions: pack kernels run before the GEMM in the same call
+    plan, run, C = _gemm_case_run(synth.gemm_case(777, 555, 333, seed=33, b_col_major=True, lda=335, ldb=337,
+                                                  out_dtype="f32"))
+    assert "packA=1" in plan.describe() and "packB=1" in plan.describe()
+    _replay_check(run, C)
+
+
+def test_gemm_fused_epilogue_graph_replay():
+    import torch
+    bias = torch.linspace(-1.0, 1.0, 1500, dtype=torch.float32, device="cuda")
+    plan, run, C = _gemm_case_run(synth.gemm_case(1000, 1500, 700, seed=34, out_dtype="bf16"), bias=bias,
+                                  act="gelu")
+    _replay_check(run, C)
+
+
+def test_lincomp_graph_replay():
+    import torch
+    ll = _ll()
+    c = synth.lincomp_case(8, 5, 256, 256, 256, 64, seed=35)
+    user, item, W = lincomp_operands(c)
+    Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    _replay_check(lambda: ll.lincomp(user, item, W, out=Y), Y)
