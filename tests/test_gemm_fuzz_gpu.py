@@ -1,0 +1,78 @@
+"""Seeded random GEMM cases on the GPU against the fp64 oracle, element by
+element: sizes, operand layouts and leading dimensions, input and output
+types, epilogue and plan flags all drawn at random, so that combinations the
+parametrised tests do not list are covered too.  Every draw is reproducible
+from the case index."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import to_f64
+from oracle import acceptance
+from synth.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 160
+
+
+def _draw(i):
+    rng = np.random.default_rng(1000 + i)
+    small = rng.random() < 0.3
+    M = int(rng.integers(1, 40 if small else 521))
+    N = int(rng.integers(1, 40 if small else 521))
+    K = int(rng.integers(1, 40 if small else 801))
+    in_dtype = str(rng.choice(["bf16", "f16"]))
+    out = str(rng.choice(["f32", in_dtype]))
+    a_col, b_col = bool(rng.random() < 0.4), bool(rng.random() < 0.4)
+    pad_a, pad_b = int(rng.choice([0, 0, 1, 3, 8])), int(rng.choice([0, 0, 2, 5, 8]))
+    act = rng.choice([None, None, "relu", "gelu", "silu"])
+    bias = bool(rng.random() < 0.5) or act is not None and rng.random() < 0.5
+    flags = int(rng.choice([0, 0, 0, 0x1, 0x2, 0x3, 0x4, 0x8]))
+    return dict(M=M, N=N, K=K, in_dtype=in_dtype, out=out, a_col=a_col, b_col=b_col, pad_a=pad_a,
+                pad_b=pad_b, act=act, bias=bias, flags=flags, seed=2000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    import torch
+    import recsys_linear_layers_amd as ll
+    d = _draw(i)
+    M, N, K = d["M"], d["N"], d["K"]
+    what = f"case {i}: {d}"
+    # A: row-major [M][lda] or column-major [K][lda]; B: row-major [K][ldb] or column-major [N][ldb]
+    if d["a_col"]:
+        lda = M + d["pad_a"]
+        A_bits = synth.bf16_tensor(K * lda, "uniform", -1.0, 1.0, seed=d["seed"], tensor=0, fmt=d["in_dtype"])
+        sam, sak = 1, lda
+    else:
+        lda = K + d["pad_a"]
+        A_bits = synth.bf16_tensor(M * lda, "uniform", -1.0, 1.0, seed=d["seed"], tensor=0, fmt=d["in_dtype"])
+        sam, sak = lda, 1
+    if d["b_col"]:
+        ldb = K + d["pad_b"]
+        B_bits = synth.bf16_tensor(N * ldb, "uniform", -1.0, 1.0, seed=d["seed"], tensor=1, fmt=d["in_dtype"])
+        sbk, sbn = 1, ldb
+    else:
+        ldb = N + d["pad_b"]
+        B_bits = synth.bf16_tensor(K * ldb, "uniform", -1.0, 1.0, seed=d["seed"], tensor=1, fmt=d["in_dtype"])
+        sbk, sbn = ldb, 1
+    A = to_device(A_bits, (M, K), (sam, sak), "cuda", d["in_dtype"])
+    B = to_device(B_bits, (K, N), (sbk, sbn), "cuda", d["in_dtype"])
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[d["out"]]
+    C = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    bias = None
+    if d["bias"]:
+        bias = torch.from_numpy(np.random.default_rng(d["seed"]).standard_normal(N).astype(np.float32)).cuda()
+    if d["flags"] & ll.LL_FLAG_COOPERATIVE and (bias is not None or d["act"] is not None):
+        with pytest.raises(ll.LLError) as e:
+            ll.gemm(A, B, out=C, flags=d["flags"], bias=bias, act=d["act"])
+        assert e.value.status == ll.LL_ERR_UNSUPPORTED, what
+        return
+    ll.gemm(A, B, out=C, flags=d["flags"], bias=bias, act=d["act"])
+    torch.cuda.synchronize()
+    ref, S = oracle.gemm(M, N, K, A_bits, sam, sak, B_bits, sbk, sbn, fmt=d["in_dtype"])
+    if bias is not None or d["act"] is not None:
+        ref, S = oracle.epilogue(ref, S, None if bias is None else bias.cpu().numpy(), d["act"])
+    acceptance.assert_close(to_f64(C), ref, S, d["out"], what, act=d["act"])
