@@ -32,8 +32,11 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256", "gemm_4096_f16", "gemm_3000"}
-# workloads also timed with the kind the plan chose before its tile-count rule
-TILE_RULE_NAMES = {"gemm_3000": "KIND_WIDE_PC"}
+# workloads also timed with the kind the plan would choose without its tile
+# rules (the 192x256 tile-count rule on gemm_3000, the 256x256 rule on the
+# others)
+TILE_RULE_NAMES = {"gemm_3000": "KIND_WIDE_PC", "gemm_4096": "KIND_WIDE_PC", "ffn_up": "KIND_WIDE_PC",
+                   "gemm_4096_f16": "KIND_WIDE_PC"}
 LINCOMP_NAMES = {"lincomp_256x128"}
 # The same workload given in the layer's original form: every candidate's
 # stacked input [user rows; item rows] materialised (no reuse possible).
@@ -304,6 +307,7 @@ def main():
         return
 
     head = args.workload
+    rule_context = {}
     if head in LINCOMP_NAMES:
         r = bench_lincomp(head, args.steps, args.warmup)
         c = r["case"]
@@ -325,6 +329,11 @@ def main():
                       b_layout="column-major" if c.sbk == 1 else "row-major",
                       c_dtype=c.out_dtype, flops=c.flops)
         plan = r["plan"]
+        if head in TILE_RULE_NAMES:
+            y = bench_gemm(head, args.steps, args.warmup, force_kind=TILE_RULE_NAMES[head])
+            rule_context = dict(without_rule_ms=round(y["kernel_ms"], 4), without_rule_tflops=round(y["tflops"], 1),
+                                tile_rule_speedup=round(y["kernel_ms"] / r["kernel_ms"], 3),
+                                plan_without_rule=y["plan"])
 
     also = []
     if not args.no_also:
@@ -385,7 +394,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": config, "roofline": roof, "cpu_baseline": cpu,
-        "kernel_ms": round(r["kernel_ms"], 4), "plan": plan, "also": also,
+        "kernel_ms": round(r["kernel_ms"], 4), "plan": plan, **rule_context, "also": also,
         "kernel_source_hash": _kernel_source_hash(),
     }
     print(json.dumps(out))

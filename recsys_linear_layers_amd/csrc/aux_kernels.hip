@@ -57,7 +57,7 @@ hipError_t launch_gemm_epi(int layout, int kind, int f16, int epi, const GemmKAr
 }
 
 const KindInfo& kind_info(int kind) {
-#define LL_KIND_INFO(name, bm, bn, kt, wm, wn, np, st, ep) \
+#define LL_KIND_INFO(name, bm, bn, kt, wm, wn, np, lw, st, ep) \
   {bm, bn, kt, (wm * wn + np) * 64, st * (bm + bn) * kt * 2, st, np, ep, #name},
   static const KindInfo table[KIND_COUNT] = {LL_GEMM_KINDS(LL_KIND_INFO)};
 #undef LL_KIND_INFO

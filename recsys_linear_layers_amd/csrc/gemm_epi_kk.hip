@@ -18,16 +18,16 @@ static hipError_t launch_cfg(const GemmKArgs& a, int grid, hipStream_t s) {
   }
 }
 
-template <int BM, int BN, int KT, int WM, int WN, int NP, int ST, int EP>
+template <int BM, int BN, int KT, int WM, int WN, int NP, int LW, int ST, int EP>
 static hipError_t launch_epi(const GemmKArgs& a, int epi, int grid, hipStream_t s) {
   if constexpr (EP == 0) {
     return hipErrorInvalidValue;
   } else {
     switch (epi) {
-      case 1: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 1>>(a, grid, s);
-      case 2: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 2>>(a, grid, s);
-      case 3: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 3>>(a, grid, s);
-      case 4: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 4>>(a, grid, s);
+      case 1: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 1, LW>>(a, grid, s);
+      case 2: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 2, LW>>(a, grid, s);
+      case 3: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 3, LW>>(a, grid, s);
+      case 4: return launch_cfg<GemmCfg<BM, BN, KT, WM, WN, NP, ST, LL_AK, LL_BK, LL_F16, 4, LW>>(a, grid, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -26,8 +26,9 @@
 //    current slice's LDS (its last fragments are already in registers), so the
 //    slice's slot is refilled at once and the next slice's first fragments are
 //    read while the last k16 step's MFMAs run.  With NPROD > 0 the loading
-//    and computing roles are separate waves; with NPROD == 0 every wave does
-//    both.  The ring runs across tile boundaries of the persistent loop.
+//    and computing roles are separate waves; with NPROD == 0 every wave
+//    computes and the first NLW waves (all if NLW == 0) also load.  The ring
+//    runs across tile boundaries of the persistent loop.
 //  * Persistent grid over (k-split, tile) work items in grouped
 //    (GROUP_M) order, with workgroup ids remapped so that the consecutive
 //    work items that share operand panels land on the same XCD (and its L2).
@@ -74,7 +75,7 @@ struct GemmKArgs {
 };
 
 template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,
-          bool F16_ = false, int EPI_ = 0>
+          bool F16_ = false, int EPI_ = 0, int NLW_ = 0>
 struct GemmCfg {
   static constexpr bool F16 = F16_;           // A and B are fp16 (else bf16); same bytes, another MFMA
   // Fused epilogue, fixed per instantiation (a run-time choice among
@@ -87,7 +88,11 @@ struct GemmCfg {
   static constexpr int KS = KT / 16;          // k16 MFMA steps per slot
   static constexpr int WM = WM_, WN = WN_;    // computing-wave grid
   static constexpr int NCONS = WM * WN;
-  static constexpr int NPROD = NPROD_;        // 0: every wave loads and computes
+  static constexpr int NPROD = NPROD_;        // 0: every wave computes, and loads unless NLW says otherwise
+  // With NPROD == 0: only waves 0 .. NLW-1 issue loads (0: every wave).  One
+  // loading wave per SIMD leaves its partner wave free to run MFMAs while the
+  // loading wave stalls issuing loads.
+  static constexpr int NLW = NLW_;
   static constexpr int STAGES = STAGES_;
   static constexpr bool A_KMAJOR = AK_;       // A stored K-contiguous (row-major A)
   static constexpr bool B_KMAJOR = BK_;       // B stored K-contiguous (column-major B)
@@ -97,7 +102,8 @@ struct GemmCfg {
   static constexpr int A_BYTES = BM * KT * 2, B_BYTES = BN * KT * 2;
   static constexpr int SLOT = A_BYTES + B_BYTES;
   static constexpr int LDS = STAGES * SLOT;
-  static constexpr int LOADERS = NPROD ? NPROD : NCONS;
+  static constexpr int LOADERS = NPROD ? NPROD : (NLW ? NLW : NCONS);
+  static_assert(NLW == 0 || (NPROD == 0 && NLW <= NCONS), "loading subset of computing waves");
   static constexpr int QA = A_BYTES / 1024, QB = B_BYTES / 1024;  // 1-KB loads per slot
   static constexpr int LPW = (QA + QB) / LOADERS;                  // per loading wave
   static_assert(KT == 32 || KT == 64, "KT");
@@ -800,7 +806,9 @@ __device__ __forceinline__ void consumer_loop(const GemmKArgs& p, char LL_LDS* s
   }
 }
 
-// Every wave both loads its share of each slice and computes.
+// Every wave computes; waves below Cfg::LOADERS also load their share of
+// each slice (all of them unless Cfg::NLW picks a subset).  Waves that do not
+// load never wait on vmcnt.
 template <class Cfg>
 __device__ __forceinline__ void coop_loop(const GemmKArgs& p, char LL_LDS* smem, int first, int stride, int wave,
                                           int lane) {
@@ -810,18 +818,19 @@ __device__ __forceinline__ void coop_loop(const GemmKArgs& p, char LL_LDS* smem,
   const int wn0 = (wave % Cfg::WN) * (Cfg::BN / Cfg::WN);
   const uint32_t va = TileGeom<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR>::lane_off(wave, lane, (int)p.a.ld);
   const uint32_t vb = TileGeom<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR>::lane_off(wave, lane, (int)p.b.ld);
+  const bool loader = wave < Cfg::LOADERS;  // wave-uniform
   Loader<Cfg> ld;
   ld.start(p, first);
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    if (ld.valid(p)) {
+    if (loader && ld.valid(p)) {
       ld.issue(p, smem + s * Cfg::SLOT, wave, lane, va, vb);
       ld.advance(p, stride);
       ++issued;
     }
   }
-  wait_slices<Cfg>(issued - 1);
+  if (loader) wait_slices<Cfg>(issued - 1);
   lds_barrier();
 
   f32x16 acc[Cfg::FM][Cfg::FN];
@@ -845,12 +854,12 @@ __device__ __forceinline__ void coop_loop(const GemmKArgs& p, char LL_LDS* smem,
         load_frags<Cfg>(cur, kk + 1, wm0, wn0, lane, f[(kk + 1) & 1]);
       } else {
         // Slice boundary: slice j+1 must have landed; slice j's LDS is free.
-        if (has_next) {
+        if (has_next && loader) {
           wait_slices<Cfg>(drain ? 0 : issued - j - 2);
           drain = false;
         }
         lds_barrier();
-        if (ld.valid(p)) {
+        if (loader && ld.valid(p)) {
           ld.issue(p, cur, wave, lane, va, vb);
           ld.advance(p, stride);
           ++issued;

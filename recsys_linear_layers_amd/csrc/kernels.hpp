@@ -8,21 +8,22 @@
 
 namespace ll {
 
-// Tile configurations: X(name, BM, BN, KT, WM, WN, NPROD, STAGES).  WM x WN
-// computing waves each own a (BM/WM) x (BN/WN) block of the tile; NPROD > 0
-// adds that many loading waves, NPROD == 0 makes every wave load and compute.
-// KT is the k depth of one ring slot.
-// X(name, BM, BN, KT, computing-wave grid WM x WN, loading waves, ring slots,
-//   has fused-epilogue instantiations)
-#define LL_GEMM_KINDS(X)                                                                                 \
-  X(KIND_SQ8_K64, 256, 256, 64, 2, 4, 0, 2, 0)    /* 8 waves (2 per SIMD) 128x64 each */               \
-  X(KIND_SQ8_K32, 256, 256, 32, 2, 4, 0, 4, 0)    /* same, 4 x 32 KB slots */                          \
-  X(KIND_WIDE8_PC, 256, 128, 64, 2, 4, 4, 3, 0)   /* 8 computing 128x32 + 4 loading waves */           \
-  X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 3, 1)    /* 4 computing 128x64 + 4 loading waves */           \
-  X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 3, 0)  /* 4 waves 128x64, load + compute */                 \
-  X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 3, 1)    /* skinny M: 4 computing 64x128 + 4 loading */       \
-  X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 3, 0) /* small problems: 4 waves 64x64 */                \
-  X(KIND_T192_PC, 192, 256, 64, 2, 4, 4, 2, 1)    /* 8 computing 96x64 + 4 loading; K-contiguous A */
+// Tile configurations: X(name, BM, BN, KT, WM, WN, NPROD, NLW, STAGES, EPI).
+// WM x WN computing waves each own a (BM/WM) x (BN/WN) block of the tile;
+// NPROD > 0 adds that many loading waves; with NPROD == 0 the computing waves
+// load too, the first NLW of them (all if NLW == 0).  KT is the k depth of one
+// ring slot; STAGES the ring's slot count; EPI marks kinds with fused-epilogue
+// instantiations.
+#define LL_GEMM_KINDS(X)                                                                                   \
+  X(KIND_SQ8_K64, 256, 256, 64, 2, 4, 0, 0, 2, 0)    /* 8 waves (2 per SIMD) 128x64 each */              \
+  X(KIND_SQ8_K32, 256, 256, 32, 2, 4, 0, 0, 4, 0)    /* same, 4 x 32 KB slots */                         \
+  X(KIND_WIDE8_PC, 256, 128, 64, 2, 4, 4, 0, 3, 0)   /* 8 computing 128x32 + 4 loading waves */          \
+  X(KIND_WIDE_PC, 256, 128, 64, 2, 2, 4, 0, 3, 1)    /* 4 computing 128x64 + 4 loading waves */          \
+  X(KIND_WIDE_COOP, 256, 128, 64, 2, 2, 0, 0, 3, 0)  /* 4 waves 128x64, load + compute */                \
+  X(KIND_TALL_PC, 128, 256, 64, 2, 2, 4, 0, 3, 1)    /* skinny M: 4 computing 64x128 + 4 loading */      \
+  X(KIND_SMALL_COOP, 128, 128, 64, 2, 2, 0, 0, 3, 0) /* small problems: 4 waves 64x64 */                 \
+  X(KIND_T192_PC, 192, 256, 64, 2, 4, 4, 0, 2, 1)    /* 8 computing 96x64 + 4 loading; K-contiguous A */ \
+  X(KIND_SQ8_LW4, 256, 256, 64, 4, 2, 0, 4, 2, 0)    /* 8 waves 64x128, one per SIMD also loads */
 
 enum KernelKind {
 #define LL_KIND_ENUM(name, ...) name,
@@ -42,10 +43,10 @@ const KindInfo& kind_info(int kind);
 inline int layout_index(bool a_kmajor, bool b_kmajor) { return (a_kmajor ? 0 : 2) | (b_kmajor ? 0 : 1); }
 
 // Launch switch over every kind for one operand layout (instantiated once per layout).
-#define LL_KIND_CASE(name, bm, bn, kt, wm, wn, np, st, ep) \
-  case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK, LL_F16>>(a, grid, s);
-#define LL_KIND_CASE_EPI(name, bm, bn, kt, wm, wn, np, st, ep) \
-  case name: return launch_epi<bm, bn, kt, wm, wn, np, st, ep>(a, epi, grid, s);
+#define LL_KIND_CASE(name, bm, bn, kt, wm, wn, np, lw, st, ep) \
+  case name: return launch_cfg<GemmCfg<bm, bn, kt, wm, wn, np, st, LL_AK, LL_BK, LL_F16, 0, lw>>(a, grid, s);
+#define LL_KIND_CASE_EPI(name, bm, bn, kt, wm, wn, np, lw, st, ep) \
+  case name: return launch_epi<bm, bn, kt, wm, wn, np, lw, st, ep>(a, epi, grid, s);
 
 // Launch `kind` for layout `layout` (bf16 or, f16 != 0, fp16 operands) on
 // `grid` workgroups.  Returns the launch status.

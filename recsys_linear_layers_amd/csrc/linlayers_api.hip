@@ -242,17 +242,32 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   // 192x256 in one pass against 384 of 128x256 in two).  The 192x256 kind
   // (K-contiguous A only) replaces the 256x128 / 128x256 kinds when its
   // passes times tile area is at least 3% smaller and neither would split K.
-  if (!(d->flags & (LL_FLAG_COOPERATIVE | LL_FLAG_PRODUCER_CONSUMER)) && p.a.kmajor &&
-      (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
-    auto passes = [&](int k) -> int64_t {
-      const KindInfo& ki = kind_info(k);
-      const int64_t t = ((M + ki.bm - 1) / ki.bm) * ((N + ki.bn - 1) / ki.bn);
-      return t * 2 <= p.cus ? -1 : (t + p.cus - 1) / p.cus;  // -1: the plan would split K
-    };
+  auto passes = [&](int k) -> int64_t {
+    const KindInfo& ki = kind_info(k);
+    const int64_t t = ((M + ki.bm - 1) / ki.bm) * ((N + ki.bn - 1) / ki.bn);
+    return t * 2 <= p.cus ? -1 : (t + p.cus - 1) / p.cus;  // -1: the plan would split K
+  };
+  const bool free_choice = !(d->flags & (LL_FLAG_COOPERATIVE | LL_FLAG_PRODUCER_CONSUMER));
+  if (free_choice && p.a.kmajor && (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
     const int64_t pb = passes(kind), pt = passes(KIND_T192_PC);
     const KindInfo& kb = kind_info(kind);
     const KindInfo& kt = kind_info(KIND_T192_PC);
     if (pb > 0 && pt > 0 && pt * kt.bm * kt.bn * 100 < pb * kb.bm * kb.bn * 97) kind = KIND_T192_PC;
+  }
+  // Square 256x256 tiles with 8 computing waves, one per SIMD also loading
+  // (KIND_SQ8_LW4), in place of 256x128: a third fewer bytes per flop through
+  // each CU's load path, and one tile per CU instead of two at 4096^2.  With
+  // A K-contiguous and B N-contiguous it was ahead of the 256x128 kind on
+  // every shape measured where that kind is chosen (4096^3 by 15%, FFN-up by
+  // 6%, 8192^3 by 1%; 4096^2 x 16384 2% behind) and behind 128x256 on tall
+  // shapes (FFN-down by 7%), so it replaces only the 256x128 choice, only
+  // without a fused epilogue, and only when its passes times tile area is no
+  // larger (it would leave CUs idle otherwise).
+  if (free_choice && kind == KIND_WIDE_PC && !d->epilogue && p.a.kmajor && !p.b.kmajor) {
+    const int64_t pw = passes(KIND_WIDE_PC), ps = passes(KIND_SQ8_LW4);
+    const KindInfo& kw = kind_info(KIND_WIDE_PC);
+    const KindInfo& ks = kind_info(KIND_SQ8_LW4);
+    if (pw > 0 && ps > 0 && ps * ks.bm * ks.bn <= pw * kw.bm * kw.bn) kind = KIND_SQ8_LW4;
   }
   if (d->flags & LL_FLAG_COOPERATIVE) {
     if (kind == KIND_WIDE_PC) kind = KIND_SQ8_K64;
