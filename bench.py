@@ -256,10 +256,12 @@ def cpu_baseline_lincomp(name: str, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # Short kernels (the 4096^3 GEMM runs ~0.12 ms) need tens of warm-up
-    # launches before clocks settle; 5 warm-up steps measured ~20% low.
+    # Short kernels need tens of milliseconds of back-to-back work before the
+    # clocks settle: the 4096^3 GEMM (~0.12 ms per call) measured ~20% low
+    # after 5 warm-up calls, ~9% low after 50, and within 1% of its steady
+    # rate after 300 or 1000.
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="gemm_4096",
                     choices=sorted(GEMM_NAMES | LINCOMP_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
