@@ -36,9 +36,32 @@ def _draw(i):
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(i):
+    _check(i, _draw(i))
+
+
+N_SQUARE = 40
+
+
+@pytest.mark.parametrize("i", range(N_SQUARE))
+def test_random_case_square_kind(i, monkeypatch):
+    """The 256x256 kind with one loading wave per SIMD, forced on random
+    cases (no fused epilogue: that kind has none, and the plan would fall back
+    to another)."""
+    import recsys_linear_layers_amd as ll
+    d = _draw(N_CASES + i)
+    d["act"], d["bias"] = None, False
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ8_LW4")
+    try:
+        _check(N_CASES + i, d, want_kind="KIND_SQ8_LW4")
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+
+
+def _check(i, d, want_kind=None):
     import torch
     import recsys_linear_layers_amd as ll
-    d = _draw(i)
     M, N, K = d["M"], d["N"], d["K"]
     what = f"case {i}: {d}"
     # A: row-major [M][lda] or column-major [K][lda]; B: row-major [K][ldb] or column-major [N][ldb]
@@ -72,6 +95,8 @@ def test_random_case(i):
         return
     ll.gemm(A, B, out=C, flags=d["flags"], bias=bias, act=d["act"])
     torch.cuda.synchronize()
+    if want_kind is not None:
+        assert f"kernel={want_kind} " in ll.plan_for(A, B, C, d["flags"]).describe(), what
     ref, S = oracle.gemm(M, N, K, A_bits, sam, sak, B_bits, sbk, sbn, fmt=d["in_dtype"])
     if bias is not None or d["act"] is not None:
         ref, S = oracle.epilogue(ref, S, None if bias is None else bias.cpu().numpy(), d["act"])
