@@ -253,6 +253,36 @@ def cpu_baseline_lincomp(name: str, target_s: float = 12.0):
                 sample=f"fp64 per-candidate oracle, first {n} candidates, {dt:.1f} s")
 
 
+def vendor_context(steps: int, warmup: int):
+    """torch.matmul on the GEMM workloads' shapes, operands of the same types
+    and scales drawn on the device, timed like the library (same warm-up and
+    step counts, one event pair around the timed calls)."""
+    import torch
+    import synth
+    out = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    for name in ["gemm_4096", "ffn_up", "ffn_down", "gemm_3000", "gemm_4096_f16", "skinny_splitk"]:
+        M, N, K, kw = synth.GEMM_WORKLOADS[name]
+        in_t = {"bf16": torch.bfloat16, "f16": torch.float16}[kw.get("in_dtype", "bf16")]
+        def draw(rows, cols, dist):
+            if dist[0] == "uniform":
+                return (torch.rand(rows, cols, device="cuda", generator=gen) * (dist[2] - dist[1]) + dist[1]).to(in_t)
+            return (torch.randn(rows, cols, device="cuda", generator=gen) * dist[2] + dist[1]).to(in_t)
+        A = draw(M, K, kw["dist"])
+        B = draw(K, N, kw.get("b_dist") or kw["dist"])
+        # torch.matmul writes C in its inputs' type: an fp32-output workload is
+        # timed with a bf16/fp16 C (noted in the result)
+        C = torch.empty(M, N, device="cuda", dtype=in_t)
+        _log(f"vendor context: {name}")
+        _, ev = _time_launches(lambda: torch.matmul(A, B, out=C), steps, warmup, torch.cuda.current_stream())
+        out.append(dict(workload=name, ms=round(ev, 4), tflops=round(2.0 * M * N * K / (ev * 1e-3) / 1e12, 1),
+                        c_dtype=str(C.dtype).replace("torch.", ""), library_c_dtype=kw.get("out_dtype", "f32")))
+        del A, B, C
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +299,8 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, --steps times "
                          "(calibrates the HBM byte counters of a profiler run); prints its own line")
+    ap.add_argument("--vendor-context", action="store_true",
+                    help="time torch.matmul (the vendor GEMM) on the GEMM workloads' shapes instead, for context")
     ap.add_argument("--stream-probe-mib", type=int, default=0,
                     help="only run a streaming reduction that reads 4x and writes 1x this many MiB "
                          "(the read/write mix of linear compression), --steps times; prints its own line")
@@ -306,6 +338,11 @@ def main():
         rd, wr = 16 * n, 4 * n
         print(json.dumps({"probe": "stream 4 reads : 1 write", "bytes_read": rd, "bytes_written": wr,
                           "ms": round(ev, 4), "GB/s": round((rd + wr) / (ev * 1e-3) / 1e9, 1)}))
+        return
+
+    if args.vendor_context:
+        print(json.dumps({"probe": "vendor GEMM (torch.matmul), context only", "steps": args.steps,
+                          "warmup": args.warmup, "results": vendor_context(args.steps, args.warmup)}))
         return
 
     head = args.workload
