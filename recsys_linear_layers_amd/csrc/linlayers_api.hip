@@ -258,11 +258,11 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   // (KIND_SQ8_LW4), in place of 256x128: a third fewer bytes per flop through
   // each CU's load path, and one tile per CU instead of two at 4096^2.  With
   // A K-contiguous and B N-contiguous it was ahead of the 256x128 kind on
-  // every shape measured where that kind is chosen (4096^3 by 15%, FFN-up by
-  // 6%, 8192^3 by 1%; 4096^2 x 16384 2% behind) and behind 128x256 on tall
-  // shapes (FFN-down by 7%), so it replaces only the 256x128 choice, only
-  // without a fused epilogue, and only when its passes times tile area is no
-  // larger (it would leave CUs idle otherwise).
+  // most shapes measured where that kind is chosen (4096^3 by 1-4%, FFN-up by
+  // 3-6%, 8192x8192x28672 by 3.5%; 4096^2 x 16384 2% behind) and behind
+  // 128x256 on tall shapes (FFN-down by 7%), so it replaces only the 256x128
+  // choice, only without a fused epilogue, and only when its passes times tile
+  // area is no larger (it would leave CUs idle otherwise).
   if (free_choice && kind == KIND_WIDE_PC && !d->epilogue && p.a.kmajor && !p.b.kmajor) {
     const int64_t pw = passes(KIND_WIDE_PC), ps = passes(KIND_SQ8_LW4);
     const KindInfo& kw = kind_info(KIND_WIDE_PC);
