@@ -146,8 +146,11 @@ ll_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
  * M == 0 or N == 0: nothing is written.  K == 0: C is set to zero.
  * Errors: LL_ERR_INVALID_ARG (null plan/pointer with a non-empty problem,
  * misaligned operand, C overlapping A or B, current device differs from the
- * plan's), LL_ERR_WORKSPACE (ws_bytes below gemm_plan_workspace_size or a
- * null workspace with a non-zero requirement), LL_ERR_HIP (launch failure).
+ * plan's), LL_ERR_WORKSPACE (ws_bytes below gemm_plan_workspace_size, a
+ * null workspace with a non-zero requirement, or a workspace not 256-byte
+ * aligned), LL_ERR_HIP (launch failure).  Packed copies live in the
+ * workspace with rows padded to whole 128-byte lines: A K-contiguous
+ * [M][ldp], B N-contiguous [K][ldp].
  * The call only launches kernels on `stream` (pack, GEMM, split-K reduce or
  * the K == 0 fill): it allocates nothing and records no memset or copy, so
  * it may be captured into a HIP graph; replays reuse the captured pointers.

@@ -124,6 +124,77 @@ hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int
   return hipGetLastError();
 }
 
+// dst[k][r] = src[r*s_r + k*s_k] for r < rows, 0 for rows <= r < ldp; k < K;
+// ldp a multiple of 64 and dst 16-byte aligned.  The N-contiguous packed copy
+// of B.  Each workgroup moves one 64 (k) x 64 (r) block through LDS: reads run
+// along whichever source stride is 1 (a transpose when the source is
+// K-contiguous, a copy when it is N-contiguous); a K-contiguous source row may
+// start at any 2-byte offset, so its interior is read as aligned 32-bit words.
+// Writes are 16-byte chunks along r.  Blocks along k are strided over grid y,
+// so any K fits the grid.
+__global__ void __launch_bounds__(256) pack_mnmajor_kernel(const uint16_t* __restrict__ src, int64_t s_r,
+                                                           int64_t s_k, int64_t rows, int64_t K,
+                                                           uint16_t* __restrict__ dst, int64_t ldp) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [k][r]; 144-byte rows, 16-byte aligned
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const bool along_k = s_k == 1;
+  const int t = threadIdx.x;
+  for (int64_t k0 = (int64_t)blockIdx.y * 64; k0 < K; k0 += (int64_t)gridDim.y * 64) {
+    if (along_k) {
+      // thread: row rr = t / 4, elements kk0 .. kk0+15 with kk0 = 16 * (t % 4).  Away from
+      // the row's first element and from K, nine aligned words cover them (shifted by one
+      // element when they start at an odd element); elsewhere element by element.
+      const int rr = t >> 2, kk0 = (t & 3) * 16;
+      const int64_t r = r0 + rr, k = k0 + kk0;
+      if (r < rows && k >= 1 && k + 18 <= K) {
+        const int64_t o = r * s_r + k;
+        const int sh = (int)(((uintptr_t)(src + o) >> 1) & 1);  // word-aligned start: o - sh
+        const uint32_t* w = (const uint32_t*)(src + (o - sh));
+        uint32_t v[9];
+#pragma unroll
+        for (int j = 0; j < 9; ++j) v[j] = w[j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int i = j + sh;
+          tile[kk0 + j][rr] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+        }
+      } else {
+#pragma unroll 4
+        for (int j = 0; j < 16; ++j)
+          tile[kk0 + j][rr] = (r < rows && k + j < K) ? src[r * s_r + k + j] : (uint16_t)0;
+      }
+    } else {
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const int e = i * 256 + t;
+        const int rr = e & 63, kk = e >> 6;
+        const int64_t r = r0 + rr, k = k0 + kk;
+        tile[kk][rr] = (r < rows && k < K) ? src[r * s_r + k * s_k] : (uint16_t)0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + t;  // 16-byte chunk: k-row c / 8, elements 8 * (c % 8) ..
+      const int kk = c >> 3, rr = (c & 7) * 8;
+      const int64_t k = k0 + kk;
+      if (k < K) *(uint4*)(dst + k * ldp + r0 + rr) = *(const uint4*)&tile[kk][rr];
+    }
+    __syncthreads();  // the tile is refilled for the next block along k
+  }
+}
+
+hipError_t launch_pack_mnmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
+                               uint16_t* dst, int64_t ldp, hipStream_t stream) {
+  if (K == 0 || ldp == 0) return hipSuccess;
+  if (ldp % 64 != 0 || ((uintptr_t)dst & 15)) return hipErrorInvalidValue;
+  const int64_t bx = ldp / 64, by = (K + 63) / 64;
+  if (bx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)bx, (unsigned)(by < 65535 ? by : 65535));
+  hipLaunchKernelGGL(pack_mnmajor_kernel, grid, dim3(256), 0, stream, src, s_r, s_k, rows, K, dst, ldp);
+  return hipGetLastError();
+}
+
 // C[i][j] = sum over s = 0..splits-1 (ascending) of partial[s][i][j].
 // Bias and activation of the GEMM epilogue, selected at run time (these
 // kernels are element-wise).

@@ -68,6 +68,8 @@ hipError_t launch_lincomp(const LincompKArgs& args, int grid, hipStream_t stream
 // Auxiliary kernels.
 hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
                               uint16_t* dst, int64_t ldp, hipStream_t stream);
+hipError_t launch_pack_mnmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,
+                               uint16_t* dst, int64_t ldp, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int64_t N, void* C,
                                 int64_t ldcm, int64_t ldcn, int c_fmt, const float* bias, int act,
                                 hipStream_t stream);

@@ -90,8 +90,11 @@ bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // One operand as the kernel sees it.
 struct OperandPlan {
-  bool kmajor;      // K-contiguous in memory (after packing, always true)
-  bool pack;        // copied into the workspace as K-major [rows][Kp]
+  bool kmajor;      // K-contiguous as the kernel reads it (the original layout, or the packed copy's)
+  bool pack;        // copied into the workspace (layout below)
+  bool pack_mn;     // the packed copy is [K][ldp] (rows contiguous), else [rows][ldp] (K contiguous)
+  int64_t ldp;      // row stride of the packed copy: its row length rounded up to 64 elements, so
+                    // that every packed row starts on a 128-byte line
   int64_t ld;       // leading dimension of the direct view
   int64_t s_r, s_k; // original strides (rows = M or N)
   size_t ws_off;    // workspace offset of the packed copy
@@ -117,9 +120,13 @@ struct gemm_plan {
 
 namespace {
 
-// Decide how an operand with logical extent rows x K and strides (s_r, s_k) is fed.
+// Decide how an operand with logical extent rows x K and strides (s_r, s_k) is
+// fed.  A packed copy is K-major [rows][ldp], or with prefer_mn rows-contiguous
+// [K][ldp]: B is packed that way, because the 128x256 and 256x256 tiles
+// load an N-contiguous B faster (64 k-rows of whole lines per slice instead
+// of 256 rows) and the 256x128 tile is indifferent to it.
 ll_status plan_operand(const char* name, int64_t rows, int64_t K, int64_t s_r, int64_t s_k, bool force_pack,
-                       OperandPlan* op) {
+                       bool prefer_mn, OperandPlan* op) {
   op->s_r = s_r;
   op->s_k = s_k;
   if (s_k == 1) {
@@ -138,7 +145,9 @@ ll_status plan_operand(const char* name, int64_t rows, int64_t K, int64_t s_r, i
   else
     direct = direct && rows % 8 == 0 && op->ld * 2 * kBK < (1ll << 31);
   op->pack = !direct;
-  if (op->pack) op->kmajor = true;
+  op->pack_mn = op->pack && prefer_mn && round_up(rows, 64) * 2 * kBK < (1ll << 31);
+  op->ldp = round_up(op->pack_mn ? rows : K, 64);
+  if (op->pack) op->kmajor = !op->pack_mn;
   return LL_OK;
 }
 
@@ -153,11 +162,16 @@ int occupancy_for(int kind) {
 
 void fill_operand_args(OperandArgs* oa, const void* ptr, const OperandPlan& op, int64_t rows, int64_t K,
                        int64_t Kp, const void* ws) {
-  if (op.pack) {
+  if (op.pack && op.pack_mn) {
     oa->ptr = (const uint16_t*)((const char*)ws + op.ws_off);
-    oa->ld = Kp;
+    oa->ld = op.ldp;
+    oa->kvalid = (int32_t)K;
+    oa->extent = K * op.ldp;
+  } else if (op.pack) {
+    oa->ptr = (const uint16_t*)((const char*)ws + op.ws_off);
+    oa->ld = op.ldp;
     oa->kvalid = (int32_t)Kp;
-    oa->extent = rows * Kp;
+    oa->extent = rows * op.ldp;
   } else {
     oa->ptr = (const uint16_t*)ptr;
     oa->ld = op.ld;
@@ -209,13 +223,13 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   gemm_plan p;
   memset(&p, 0, sizeof p);
   p.d = *d;
-  ll_status s = plan_operand("A", d->M, d->K, d->stride_am, d->stride_ak, d->flags & LL_FLAG_PACK_A, &p.a);
+  ll_status s = plan_operand("A", d->M, d->K, d->stride_am, d->stride_ak, d->flags & LL_FLAG_PACK_A, false, &p.a);
   if (s != LL_OK) return s;
-  s = plan_operand("B", d->N, d->K, d->stride_bn, d->stride_bk, d->flags & LL_FLAG_PACK_B, &p.b);
+  s = plan_operand("B", d->N, d->K, d->stride_bn, d->stride_bk, d->flags & LL_FLAG_PACK_B, true, &p.b);
   if (s != LL_OK) return s;
   // Any K-contiguous operand needs K padded to a multiple of 8; packed copies carry zeros there.
   p.Kp = round_up(d->K, 8);
-  if (p.Kp * 2 * 256 >= (1ll << 31)) return fail(LL_ERR_UNSUPPORTED, "K too large");
+  if (round_up(d->K, 64) * 2 * 256 >= (1ll << 31)) return fail(LL_ERR_UNSUPPORTED, "K too large");
   p.layout = layout_index(p.a.kmajor, p.b.kmajor);
 
   const DeviceInfo* info = nullptr;
@@ -327,11 +341,11 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   size_t off = 0;
   if (p.a.pack) {
     p.a.ws_off = off;
-    off = align256(off + (size_t)(M * p.Kp * 2));
+    off = align256(off + (size_t)(M * p.a.ldp * 2));
   }
   if (p.b.pack) {
     p.b.ws_off = off;
-    off = align256(off + (size_t)(N * p.Kp * 2));
+    off = align256(off + (size_t)((p.b.pack_mn ? d->K : N) * p.b.ldp * 2));
   }
   p.ws_partial_off = off;
   if (splits > 1) off = align256(off + (size_t)splits * M * N * 4);
@@ -395,6 +409,8 @@ static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B,
   if (d.K > 0 && (!A || !B)) return fail(LL_ERR_INVALID_ARG, "null A or B");
   if (ws_bytes < p->ws_bytes || (p->ws_bytes > 0 && !ws))
     return fail(LL_ERR_WORKSPACE, "workspace %zu bytes, plan needs %zu", ws_bytes, p->ws_bytes);
+  if (p->ws_bytes > 0 && ((uintptr_t)ws & 255))
+    return fail(LL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -419,12 +435,13 @@ static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B,
     return fail(LL_ERR_INVALID_ARG, "A and B must be 16-byte aligned unless packed (LL_FLAG_PACK_A/B)");
   if (p->a.pack) {
     e = launch_pack_kmajor((const uint16_t*)A, p->a.s_r, p->a.s_k, d.M, d.K,
-                           (uint16_t*)((char*)ws + p->a.ws_off), p->Kp, st);
+                           (uint16_t*)((char*)ws + p->a.ws_off), p->a.ldp, st);
     if (e != hipSuccess) return hip_fail(e, "pack A launch");
   }
   if (p->b.pack) {
-    e = launch_pack_kmajor((const uint16_t*)B, p->b.s_r, p->b.s_k, d.N, d.K,
-                           (uint16_t*)((char*)ws + p->b.ws_off), p->Kp, st);
+    uint16_t* dst = (uint16_t*)((char*)ws + p->b.ws_off);
+    e = p->b.pack_mn ? launch_pack_mnmajor((const uint16_t*)B, p->b.s_r, p->b.s_k, d.N, d.K, dst, p->b.ldp, st)
+                     : launch_pack_kmajor((const uint16_t*)B, p->b.s_r, p->b.s_k, d.N, d.K, dst, p->b.ldp, st);
     if (e != hipSuccess) return hip_fail(e, "pack B launch");
   }
   GemmKArgs k;

@@ -49,6 +49,23 @@ def test_split_k_workspace_too_small_is_rejected():
     assert e.value.status == ll.LL_ERR_WORKSPACE
 
 
+def test_misaligned_workspace_is_rejected():
+    import torch
+    import recsys_linear_layers_amd as ll
+    # column-major B with an odd leading dimension: packed (N-contiguous) into the workspace
+    A = torch.zeros((300, 520), dtype=torch.bfloat16, device="cuda")
+    Bt = torch.zeros((260, 521), dtype=torch.bfloat16, device="cuda")[:, :520]
+    B = Bt.t()
+    C = torch.zeros((300, 260), dtype=torch.float32, device="cuda")
+    plan = ll.plan_for(A, B, C)
+    assert plan.ws_bytes > 0 and "packB=1" in plan.describe() and "B:N-major" in plan.describe()
+    ws = torch.empty(plan.ws_bytes + 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ll.LLError) as e:
+        ll.gemm_run(plan.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), ws.data_ptr() + 16, plan.ws_bytes, 0)
+    assert e.value.status == ll.LL_ERR_WORKSPACE
+    assert "aligned" in ll.ll_last_error()
+
+
 def test_one_plan_two_streams_concurrently():
     import torch
     import recsys_linear_layers_amd as ll
