@@ -128,6 +128,29 @@ def test_misaligned_operand_is_rejected_without_pack():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("offset", [0, 1, 2, 3])
+@pytest.mark.parametrize("ldb", [300, 301])
+def test_packed_b_from_any_2_byte_offset(offset, ldb):
+    """Column-major B packed N-contiguous from a view that starts at any
+    2-byte offset: the pack reads a row's interior as 4-byte-aligned words
+    and must shift by the view's own address, not by the element index."""
+    import torch
+    ll = _ll()
+    M, N, K = 130, 70, 290
+    seed = 91 + offset * 7 + ldb
+    c = synth.gemm_case(M, N, K, seed=seed, b_col_major=True, ldb=ldb, out_dtype="f32")
+    B_bits = np.concatenate([np.zeros(offset, dtype=np.uint16), c.B])
+    base = torch.from_numpy(B_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    B = torch.as_strided(base, (K, N), (1, ldb), offset)
+    A, _ = gemm_operands(c)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ll.gemm(A, B, out=C, flags=ll.LL_FLAG_PACK_B)
+    torch.cuda.synchronize()
+    assert "B:N-major" in ll.plan_for(A, B, C, ll.LL_FLAG_PACK_B).describe()
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(to_f64(C), ref, S, "f32", f"packed B offset {offset} ldb {ldb}")
+
+
 def _sampled_check(case, n=4096, strip_rows=8, seed=1, flags=0):
     C = _run(case, flags=flags)
     got = to_f64(C)
