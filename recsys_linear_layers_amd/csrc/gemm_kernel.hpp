@@ -261,6 +261,11 @@ __device__ __forceinline__ void load_tile(const OperandArgs& op, const Stream& o
   } else {
     // Lanes outside the matrix: offset beyond num_records (the whole offset
     // sits in voff here, soffset is 0, so it cannot wrap back into range).
+    // The empty asm makes the lane index opaque, so that these per-load
+    // offsets (used only for tiles at the matrix edge) are computed here
+    // rather than hoisted out of the main loop, where they held a dozen
+    // registers for its whole length and made the 256x256 kind spill.
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int i = 0; i < G::NQ / NL; ++i) {
       const int q = lw + i * NL;
