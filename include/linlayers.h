@@ -117,7 +117,9 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * those are used instead.  Where 256x128 remains, A is K-contiguous, B is
  * N-contiguous and no epilogue is fused, 256x256 tiles (eight computing
  * waves, one per SIMD also loading) replace it when they need no more passes
- * x tile area.  K is split when the tiles fill fewer than half of the CUs.  The environment variable LL_GEMM_KIND (a kernel name as printed
+ * x tile area; for K > 8192 the 128x256 tiles take their place again under
+ * the same conditions.  K is split when the tiles fill fewer than half of the
+ * CUs.  The environment variable LL_GEMM_KIND (a kernel name as printed
  * by gemm_plan_describe, or its index) forces a kernel for configuration
  * sweeps; a forced 192-row tile with an M-contiguous A gives
  * LL_ERR_UNSUPPORTED.

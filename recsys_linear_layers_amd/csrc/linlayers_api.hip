@@ -283,6 +283,19 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     const KindInfo& ks = kind_info(KIND_SQ8_LW4);
     if (pw > 0 && ps > 0 && ps * ks.bm * ks.bn <= pw * kw.bm * kw.bn) kind = KIND_SQ8_LW4;
   }
+  // Long K: beyond K = 8192 the 128x256 kind was ahead of the 256x256 and the
+  // 256x128 kinds on square and wide shapes too, not only on tall ones
+  // (8192^2 x 12288 .. 28672 by 4-7.5%, 8192 x 16384 x 28672 by 4%, 4096^2 x
+  // 16384 by 3%; 8192^2 x 16384 1% behind), while at K <= 8192 it is not
+  // (FFN-up 4% behind the 256x256 kind).  Same layout and epilogue conditions
+  // as above, and again no more passes times tile area.
+  if (free_choice && !d->epilogue && p.a.kmajor && !p.b.kmajor && d->K > 8192 &&
+      (kind == KIND_WIDE_PC || kind == KIND_SQ8_LW4)) {
+    const int64_t pk = passes(kind), pt = passes(KIND_TALL_PC);
+    const KindInfo& kk = kind_info(kind);
+    const KindInfo& kt = kind_info(KIND_TALL_PC);
+    if (pk > 0 && pt > 0 && pt * kt.bm * kt.bn <= pk * kk.bm * kk.bn) kind = KIND_TALL_PC;
+  }
   if (d->flags & LL_FLAG_COOPERATIVE) {
     if (kind == KIND_WIDE_PC) kind = KIND_SQ8_K64;
     else if (kind_info(kind).nprod > 0) kind = KIND_WIDE_COOP;

@@ -67,6 +67,9 @@ def _run(case, flags=0):
     (4096, 4096, 4096, True),     # 256 tiles of 256x256 (1 pass) vs 512 of 256x128 (2 passes)
     (16384, 28672, 8192, True),   # FFN up: 7 passes vs 14
     (16384, 8192, 28672, False),  # FFN down: M > N keeps 128x256
+    (8192, 8192, 28672, False),   # K > 8192: 128x256
+    (8192, 16384, 24576, False),  # K > 8192: 128x256
+    (8192, 8192, 8192, True),     # K = 8192 keeps 256x256
     (4000, 4000, 136, True),      # ragged: 256 tiles vs 512
     (4096, 2048, 8192, False),    # M > N
     (2048, 4096, 8192, False),    # 128 tiles of 256x256 would split K; 256x128 fills the CUs
@@ -77,6 +80,15 @@ def _run(case, flags=0):
 def test_rule_selection(M, N, K, want):
     d = _describe(M, N, K)
     assert (KIND in d) == want, d
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 28672), (4096, 4096, 16384), (8192, 16384, 24576)])
+def test_long_k_rule_picks_128x256(M, N, K):
+    ll = _ll()
+    assert "kernel=KIND_TALL_PC " in _describe(M, N, K)
+    # with a fused epilogue, another layout or a forced mode the rule stays out
+    assert "kernel=KIND_TALL_PC " not in _describe(M, N, K, epilogue=ll.LL_EPI_GELU)
+    assert "kernel=KIND_TALL_PC " not in _describe(M, N, K, b_col=True)
 
 
 def test_rule_conditions():
