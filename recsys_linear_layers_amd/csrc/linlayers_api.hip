@@ -272,8 +272,8 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   // (KIND_SQ8_LW4), in place of 256x128: a third fewer bytes per flop through
   // each CU's load path, and one tile per CU instead of two at 4096^2.  With
   // A K-contiguous and B N-contiguous it was ahead of the 256x128 kind on
-  // most shapes measured where that kind is chosen (4096^3 by 1-4%, FFN-up by
-  // 3-6%, 8192x8192x28672 by 3.5%; 4096^2 x 16384 2% behind) and behind
+  // most shapes measured where that kind is chosen (FFN-up by 2-6%, 8192^3 by
+  // up to 1%; 4096^3 within 2% either way; 4096^2 x 16384 2% behind) and behind
   // 128x256 on tall shapes (FFN-down by 7%), so it replaces only the 256x128
   // choice, only without a fused epilogue, and only when its passes times tile
   // area is no larger (it would leave CUs idle otherwise).
