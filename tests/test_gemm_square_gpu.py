@@ -91,6 +91,22 @@ def test_long_k_rule_picks_128x256(M, N, K):
     assert "kernel=KIND_TALL_PC " not in _describe(M, N, K, b_col=True)
 
 
+def test_long_k_selected_sampled():
+    """A square long-K shape the rule sends to the 128x256 kind, at full size:
+    sampled entries (the corners and the last tile row and column included)
+    and row strips against the oracle."""
+    c = synth.gemm_case(4096, 4096, 16384, seed=259, dist=("normal", 0.0, 1.0), out_dtype="bf16")
+    C, desc = _run(c)
+    assert "kernel=KIND_TALL_PC " in desc, desc
+    got = to_f64(C)
+    rows, cols = sample_indices(c.M, c.N, 2048, seed=6, tile=256)
+    ref, S = oracle.gemm_case_entries(c, rows, cols)
+    acceptance.assert_close(got[rows, cols], ref, S, "bf16", "4096x4096x16384 samples")
+    for r0 in (0, c.M - 8):
+        ref, S = oracle.gemm_case(c, rows=(r0, 8))
+        acceptance.assert_close(got[r0:r0 + 8], ref, S, "bf16", f"4096x4096x16384 strip {r0}")
+
+
 def test_rule_conditions():
     ll = _ll()
     assert KIND in _describe(4096, 4096, 4096, in_t=ll.LL_F16, c_t=ll.LL_F16)
