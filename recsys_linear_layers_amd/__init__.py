@@ -174,14 +174,28 @@ def _dtype_code(dt) -> int:
 
 
 class GemmPlan:
-    """Owns one gemm_plan and a workspace tensor on the plan's device."""
+    """Owns one gemm_plan and its workspaces on the plan's device: one per
+    stream the plan runs on, so that runs on different streams never share
+    packed copies or split-K partials (the C ABI asks concurrent runs for
+    distinct workspaces)."""
 
     def __init__(self, desc: GemmDesc, device):
         self.desc = desc
         self.handle = gemm_plan_create(desc)
         self.ws_bytes = gemm_plan_workspace_size(self.handle)
+        self.device = device
         torch = _torch()
-        self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+        self._ws = {}
+        # workspace of the stream current at creation (also what callers of
+        # the raw C-ABI mirrors may pass)
+        self.workspace = self.workspace_for(torch.cuda.current_stream(device).cuda_stream)
+
+    def workspace_for(self, stream: int):
+        ws = self._ws.get(stream)
+        if ws is None:
+            ws = _torch().empty(max(self.ws_bytes, 1), dtype=_torch().uint8, device=self.device)
+            self._ws[stream] = ws
+        return ws
 
     def describe(self) -> str:
         return gemm_plan_describe(self.handle)
@@ -189,13 +203,12 @@ class GemmPlan:
     def run(self, A, B, C, stream: int | None = None, bias=None) -> None:
         if stream is None:
             stream = _torch().cuda.current_stream(A.device).cuda_stream
+        ws = self.workspace_for(stream)
         if bias is not None or (self.desc.epilogue & LL_EPI_BIAS):
             gemm_run_ex(self.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(),
-                        bias.data_ptr() if bias is not None else None, self.workspace.data_ptr(),
-                        self.ws_bytes, stream)
+                        bias.data_ptr() if bias is not None else None, ws.data_ptr(), self.ws_bytes, stream)
         else:
-            gemm_run(self.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), self.workspace.data_ptr(),
-                     self.ws_bytes, stream)
+            gemm_run(self.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), ws.data_ptr(), self.ws_bytes, stream)
 
     def __del__(self):
         h = getattr(self, "handle", None)

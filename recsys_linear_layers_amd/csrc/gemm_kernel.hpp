@@ -405,7 +405,10 @@ struct Loader {
   __device__ __forceinline__ void issue(const GemmKArgs& p, char LL_LDS* slot, int lw, int lane, uint32_t va,
                                         uint32_t vb) const {
     const int k0 = k * Cfg::KT;
-    const bool fast = rows_in && k0 + Cfg::KT <= p.a.kvalid;  // kvalid is the same for both operands
+    // The two operands' k extents differ when one is a packed K-contiguous
+    // copy (zero columns up to K rounded to 8) and the other is read in place
+    // (exactly K): the unmasked path is taken only where both hold the slice.
+    const bool fast = rows_in && k0 + Cfg::KT <= min(p.a.kvalid, p.b.kvalid);
     load_tile<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR, Cfg::LOADERS>(p.a, a, fast, m0, k0, slot, lw, lane, va);
     load_tile<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR, Cfg::LOADERS>(p.b, bo, fast, n0, k0, slot + Cfg::A_BYTES, lw,
                                                               lane, vb);

@@ -139,13 +139,18 @@ ll_status plan_operand(const char* name, int64_t rows, int64_t K, int64_t s_r, i
     return fail(LL_ERR_UNSUPPORTED, "%s: neither stride is 1 (strides %lld, %lld)", name, (long long)s_r,
                 (long long)s_k);
   }
+  // One slice of a tile spans at most 256 rows (K-contiguous) or kBK k-rows
+  // (rows contiguous) of the operand.  Keeping that span below 2^30 bytes keeps
+  // every offset the loads form (a slice base below 2^30, re-based beyond it,
+  // plus the span) below the descriptor's num_records clamp, so in-range data
+  // is never read as out of range.
   bool direct = !force_pack && op->ld % 8 == 0;
   if (op->kmajor)
-    direct = direct && K % 8 == 0 && op->ld * 2 * 256 < (1ll << 31);
+    direct = direct && K % 8 == 0 && op->ld * 2 * 256 < (1ll << 30);
   else
-    direct = direct && rows % 8 == 0 && op->ld * 2 * kBK < (1ll << 31);
+    direct = direct && rows % 8 == 0 && op->ld * 2 * kBK < (1ll << 30);
   op->pack = !direct;
-  op->pack_mn = op->pack && prefer_mn && round_up(rows, 64) * 2 * kBK < (1ll << 31);
+  op->pack_mn = op->pack && prefer_mn && round_up(rows, 64) * 2 * kBK < (1ll << 30);
   op->ldp = round_up(op->pack_mn ? rows : K, 64);
   if (op->pack) op->kmajor = !op->pack_mn;
   return LL_OK;
@@ -175,7 +180,7 @@ void fill_operand_args(OperandArgs* oa, const void* ptr, const OperandPlan& op, 
   } else {
     oa->ptr = (const uint16_t*)ptr;
     oa->ld = op.ld;
-    oa->kvalid = (int32_t)(op.kmajor ? K : K);
+    oa->kvalid = (int32_t)K;
     oa->extent = op.kmajor ? (rows - 1) * op.ld + K : (K - 1) * op.ld + rows;
   }
   oa->rows = (int32_t)rows;
@@ -229,7 +234,7 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   if (s != LL_OK) return s;
   // Any K-contiguous operand needs K padded to a multiple of 8; packed copies carry zeros there.
   p.Kp = round_up(d->K, 8);
-  if (round_up(d->K, 64) * 2 * 256 >= (1ll << 31)) return fail(LL_ERR_UNSUPPORTED, "K too large");
+  if (round_up(d->K, 64) * 2 * 256 >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "K too large");
   p.layout = layout_index(p.a.kmajor, p.b.kmajor);
 
   const DeviceInfo* info = nullptr;
@@ -382,9 +387,9 @@ ll_status gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
   static const char* lay[4] = {"A:K-major,B:K-major", "A:K-major,B:N-major", "A:M-major,B:K-major",
                                "A:M-major,B:N-major"};
   snprintf(buf, len,
-           "kernel=%s layout=%s packA=%d packB=%d tiles=%dx%d splitk=%d kiters=%d grid=%d cus=%d "
+           "kernel=%s tile=%dx%d layout=%s packA=%d packB=%d tiles=%dx%d splitk=%d kiters=%d grid=%d cus=%d "
            "group_m=%d ws=%zu epilogue=0x%x fused=%d",
-           k.name, lay[p->layout], (int)p->a.pack, (int)p->b.pack, p->tiles_m, p->tiles_n, p->splits,
+           k.name, k.bm, k.bn, lay[p->layout], (int)p->a.pack, (int)p->b.pack, p->tiles_m, p->tiles_n, p->splits,
            p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes, p->d.epilogue, p->epi);
   return ok();
 }

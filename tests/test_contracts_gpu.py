@@ -89,6 +89,33 @@ def test_one_plan_two_streams_concurrently():
     assert torch.equal(C1, C2)  # same plan, same order of sums: bit-identical
 
 
+@pytest.mark.parametrize("shape,b_col", [((128, 1024, 8192), False), ((300, 260, 520), True)])
+def test_gemm_convenience_on_two_streams(shape, b_col):
+    """ll.gemm on two streams at once with one cached plan (a split-K shape,
+    and a column-major B with an odd leading dimension that is packed): each
+    stream gets its own workspace, so neither run reads the other's partials or
+    packed copy."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    M, N, K = shape
+    cases = [synth.gemm_case(M, N, K, seed=82 + i, out_dtype="f32", b_col_major=b_col,
+                             ldb=(K + 1 if b_col else None)) for i in range(2)]
+    ops = [gemm_operands(c) for c in cases]
+    outs = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for _ in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for (A, B), C, st in zip(ops, outs, streams):
+            with torch.cuda.stream(st):
+                ll.gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    d = ll.plan_for(ops[0][0], ops[0][1], outs[0]).describe()
+    assert ("splitk=1 " not in d) if not b_col else ("packB=1" in d), d
+    for c, C in zip(cases, outs):
+        ref, S = oracle.gemm_case(c)
+        acceptance.assert_close(to_f64(C), ref, S, "f32", f"{c.name} seed on its own stream")
+
+
 def test_plan_describe_reports_the_choice():
     import torch
     import recsys_linear_layers_amd as ll

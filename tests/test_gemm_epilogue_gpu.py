@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import gemm_operands, sample_indices, to_f64
+from helpers import gemm_operands, per_tile_indices, plan_tile, sample_indices, strip_starts, to_f64
 from oracle import acceptance
 
 pytestmark = pytest.mark.gpu
@@ -125,10 +125,26 @@ def test_errors():
 
 
 def test_ffn_up_bias_gelu_sampled():
+    """Full size: 4096 seeded entries (with the last tile row and column), one
+    entry in every output tile of the plan's grid, a seeded 64-row strip and
+    the first and last rows."""
+    import torch
+    import recsys_linear_layers_amd as ll
     c = synth.gemm_workload("ffn_up")
     bias = _bias(c.N, 41, 0.5)
     got = _run(c, bias, "gelu")
-    rows, cols = sample_indices(c.M, c.N, 2048, seed=42)
+    A, B = gemm_operands(c)
+    C = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+    tile = plan_tile(ll.plan_for(A, B, C, 0, ll.LL_EPI_BIAS | ll.LL_EPI_GELU).describe())
+    del A, B, C
+    rows, cols = sample_indices(c.M, c.N, 4096, seed=42, tile=tile)
+    tr, tc = per_tile_indices(c.M, c.N, tile, 43)
+    rows, cols = np.concatenate([rows, tr]), np.concatenate([cols, tc])
     ref, S = oracle.gemm_case_entries(c, rows, cols)
     ref, S = oracle.epilogue(ref, S, bias, "gelu", cols=cols)
-    acceptance.assert_close(got[rows, cols], ref, S, "bf16", "ffn_up gelu", act="gelu")
+    acceptance.assert_close(got[rows, cols], ref, S, "bf16", f"ffn_up gelu samples (tile {tile})", act="gelu")
+    for r0, nr in strip_starts(c.M, 64, 44):
+        ref, S = oracle.gemm_case(c, rows=(r0, nr))
+        ref, S = oracle.epilogue(ref, S, bias, "gelu")
+        acceptance.assert_close(got[r0:r0 + nr], ref, S, "bf16", f"ffn_up gelu rows {r0}..{r0 + nr - 1}",
+                                act="gelu")

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import gemm_operands, sample_indices, to_f64
+from helpers import gemm_operands, per_tile_indices, plan_tile, sample_indices, strip_starts, to_f64
 from oracle import acceptance
 
 pytestmark = pytest.mark.gpu
@@ -151,29 +151,95 @@ def test_packed_b_from_any_2_byte_offset(offset, ldb):
     acceptance.assert_close(to_f64(C), ref, S, "f32", f"packed B offset {offset} ldb {ldb}")
 
 
-def _sampled_check(case, n=4096, strip_rows=8, seed=1, flags=0):
-    C = _run(case, flags=flags)
+def _sampled_check(case, n=4096, strip_rows=64, seed=1, flags=0):
+    """Full-size parity: n seeded entries (with the corners and the last tile
+    row and column), one seeded entry in every output tile of the plan's tile
+    grid, a seeded strip of strip_rows rows, and the first and last rows, each
+    against the oracle."""
+    import torch
+    ll = _ll()
+    A, B = gemm_operands(case)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[case.out_dtype]
+    C = torch.full((case.M, case.N), float("nan"), dtype=dt, device="cuda")
+    ll.gemm(A, B, out=C, flags=flags)
+    torch.cuda.synchronize()
+    tile = plan_tile(ll.plan_for(A, B, C, flags).describe())
+    del A, B
     got = to_f64(C)
-    rows, cols = sample_indices(case.M, case.N, n, seed)
+    del C
+    rows, cols = sample_indices(case.M, case.N, n, seed, tile=tile)
+    tr, tc = per_tile_indices(case.M, case.N, tile, seed + 1)
+    rows, cols = np.concatenate([rows, tr]), np.concatenate([cols, tc])
     ref, S = oracle.gemm_case_entries(case, rows, cols)
-    acceptance.assert_close(got[rows, cols], ref, S, case.out_dtype, f"{case.name} samples")
-    for r0 in (0, case.M - strip_rows):
-        ref, S = oracle.gemm_case(case, rows=(r0, strip_rows))
-        acceptance.assert_close(got[r0:r0 + strip_rows], ref, S, case.out_dtype, f"{case.name} strip {r0}")
+    acceptance.assert_close(got[rows, cols], ref, S, case.out_dtype, f"{case.name} samples (tile {tile})")
+    for r0, nr in strip_starts(case.M, strip_rows, seed + 2):
+        ref, S = oracle.gemm_case(case, rows=(r0, nr))
+        acceptance.assert_close(got[r0:r0 + nr], ref, S, case.out_dtype, f"{case.name} rows {r0}..{r0 + nr - 1}")
     return got
 
 
 def test_gemm_4096_bf16_out():
-    _sampled_check(synth.gemm_workload("gemm_4096"), strip_rows=16)
+    _sampled_check(synth.gemm_workload("gemm_4096"))
 
 
 @pytest.mark.parametrize("name", ["ffn_up", "ffn_down"])
 def test_ffn_shapes(name):
-    _sampled_check(synth.gemm_workload(name), n=2048, strip_rows=2)
+    _sampled_check(synth.gemm_workload(name))
+
+
+def test_descriptor_rebase_past_1gib():
+    """A row-major B whose k-range per work item spans more than 1 GiB (the
+    loader re-opens its buffer descriptor at the current slice once the
+    running offset passes 2^30): 2048 x 28672 x 24576, B 1.41 GB, no K split."""
+    c = synth.gemm_case(2048, 28672, 24576, dist=("normal", 0.0, 1.0), b_dist=("normal", 0.0, 0.02),
+                        seed=12, out_dtype="bf16", name="rebase_1gib")
+    slice_bytes = 64 * c.sbk * 2
+    assert slice_bytes * (c.K // 64) > 1 << 30
+    import torch
+    A, B = gemm_operands(c)
+    d = _ll().plan_for(A, B, torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")).describe()
+    del A, B
+    assert "splitk=1 " in d and "packB=0" in d and "B:N-major" in d, d
+    _sampled_check(c, strip_rows=16)
+
+
+@pytest.mark.parametrize("M,N,K,kind", [(384, 520, 1017, None), (2048, 2048, 4095, "KIND_SQ8_LW4"),
+                                        (1000, 1032, 2043, "KIND_WIDE_PC"), (520, 1032, 1982, "KIND_TALL_PC"),
+                                        (1000, 1032, 2044, "KIND_T192_PC"), (520, 264, 1021, "KIND_WIDE_COOP")])
+def test_packed_a_with_direct_b_reads_no_row_past_k(M, N, K, kind, monkeypatch):
+    """K = 57..63 mod 64 with a row-major A (packed: K is not a multiple of 8, its
+    copy carries zero columns up to K rounded to 8, a whole number of 64-deep
+    slices) and a row-major B read in place: B is a view of the first K rows of a
+    buffer whose later rows are NaN.  The last slice must take the masked load
+    path, since B holds only K rows; any read of a row past K shows as NaN."""
+    import torch
+    ll = _ll()
+    assert K % 64 >= 57 and K % 8 != 0
+    c = synth.gemm_case(M, N, K, seed=K + M, out_dtype="f32", name="k_tail")
+    A, _ = gemm_operands(c)
+    Bfull = torch.full((K + 16, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Bfull[:K] = gemm_operands(c)[1]
+    B = Bfull[:K]
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ll._plans.clear()
+    if kind:
+        monkeypatch.setenv("LL_GEMM_KIND", kind)
+    try:
+        ll.gemm(A, B, out=C)
+        torch.cuda.synchronize()
+        desc = ll.plan_for(A, B, C).describe()
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+    assert "packA=1" in desc and "packB=0" in desc, desc
+    if kind:
+        assert f"kernel={kind} " in desc, desc
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(to_f64(C), ref, S, "f32", f"{M}x{N}x{K} {desc}")
 
 
 def test_edge_shape_column_major_b():
-    _sampled_check(synth.gemm_workload("edge"), strip_rows=4)
+    _sampled_check(synth.gemm_workload("edge"))
 
 
 def test_edge_shape_integer_exact_samples():
@@ -192,7 +258,7 @@ def test_skinny_split_k():
     c = synth.gemm_workload("skinny_splitk")
     A, B = gemm_operands(c)
     assert "splitk=1 " not in ll.plan_for(A, B, torch.empty((c.M, c.N), device="cuda")).describe()
-    got = _sampled_check(c, strip_rows=2)
+    got = _sampled_check(c)
     again = to_f64(_run(c))
     assert np.array_equal(got, again), "split-K result must be run-to-run deterministic"
 
@@ -266,4 +332,4 @@ def test_mixed_operand_types_rejected():
 
 
 def test_gemm_4096_f16_sampled():
-    _sampled_check(synth.gemm_workload("gemm_4096_f16"), strip_rows=16)
+    _sampled_check(synth.gemm_workload("gemm_4096_f16"))
