@@ -5,14 +5,23 @@ linear-compression requests/s (fraction of HBM bandwidth) on one MI355X.
 
 One step is one call of the library on the headline workload (default: the
 4096^3 GEMM with bf16 output).  Inputs are seeded synthetic bf16 (the
-``synth`` module), resident in HBM before timing starts.  W untimed warm-up
-steps, then K timed steps between two device synchronisations; the kernel's
-average duration comes from HIP events recorded around every launch on the
-stream the library launches on.  Prints ONE JSON line.  The other
-configurations are reported in the same line under "also".
+``synth`` module), resident in HBM before timing starts.  Every workload gets
+W untimed warm-up calls, then K timed calls between two device
+synchronisations, each call bracketed by its own pair of HIP events on the
+stream the library launches on; the mean and the median of those per-call
+durations are reported, and the mean is what throughput is computed from.
+The other configurations (FFN shapes, linear compression and its variants,
+edge and skinny shapes) run first and the headline last, so that the headline
+is timed at the clocks the chip holds under sustained work rather than at
+the clocks it ramps up from after idling through input generation.  Prints
+ONE JSON line; linear compression, the second half of the metric, has its
+own object ("lincomp") with its own roofline and CPU baseline.
 
-CPU baseline: the fp64 oracle, timed on a bounded sample of the headline
-workload (rows of C) on this host's cores; it is a reported baseline, not the
+CPU baseline: the fp64 oracle (the original, plain implementation) on this
+host's cores, after all GPU timing: the whole headline problem, and per
+configuration the whole problem where it takes seconds, or a bounded sample
+(C3: a seeded 64-row strip plus the first and last rows, with the time for the
+full shape extrapolated and labelled so).  It is a reported baseline, not the
 target.
 """
 from __future__ import annotations
@@ -21,7 +30,10 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import re
+import statistics
+import subprocess
 import sys
 import time
 
@@ -76,165 +88,251 @@ def _log(msg: str) -> None:
 
 
 def _time_launches(fn, steps: int, warmup: int, stream):
-    """Returns (wall ms per step, event-measured ms per step).
-
-    The K timed steps are enqueued back to back between one pair of HIP
-    events recorded on `stream` (the stream the library launches on), so the
-    per-step figure is the kernels' average duration plus any gap between
-    them; the host stays ahead of the device for kernels this long.
-    """
+    """W untimed calls, then K timed calls between two device synchronisations,
+    each bracketed by a pair of HIP events recorded on `stream` (the stream the
+    library launches on).  Returns dict(wall_ms: host time per call across the
+    timed region, ms: mean event-measured duration per call, median_ms)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
+        starts[i].record(stream)
         fn()
-    end.record(stream)
+        ends[i].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return wall, start.elapsed_time(end) / steps
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return dict(wall_ms=wall, ms=statistics.fmean(per), median_ms=statistics.median(per))
 
 
-def bench_gemm(name: str, steps: int, warmup: int, force_kind: str | None = None):
-    """force_kind: time the plan with this kernel kind instead of the plan's own
-    choice (LL_GEMM_KIND, read when a plan is made; the forced plan is not kept)."""
+_CASES: dict = {}
+
+
+def _case(name: str):
+    """Host inputs of a workload, generated once and shared by its GPU leg and
+    its CPU baseline (dropped by _drop_case)."""
+    import synth
+    if name not in _CASES:
+        if name in LINCOMP_NAMES:
+            _CASES[name] = synth.lincomp_workload(name)
+        elif name in RAGGED_NAMES:
+            _CASES[name] = synth.lincomp_ragged_workload(name)
+        else:
+            _CASES[name] = synth.gemm_workload(name)
+    return _CASES[name]
+
+
+def _drop_case(name: str) -> None:
+    _CASES.pop(name, None)
+
+
+# Every workload is prepared first (inputs copied to HBM, plans made), then
+# all are timed back to back, so that no timed call follows a host-side pause.
+
+def prep_gemm(name: str, force_kind: str | None = None) -> dict:
+    """Device operands, output and plan of a GEMM workload.  force_kind: make the
+    plan with this kernel kind instead of the plan's own choice (LL_GEMM_KIND,
+    read when a plan is made; the forced plan is not cached)."""
     import torch
     import recsys_linear_layers_amd as ll
-    import synth
     from synth.device import gemm_operands
-    _log(f"{name}: generating inputs")
-    case = synth.gemm_workload(name)
+    _log(f"{name}: preparing inputs")
+    case = _case(name)
     A, B = gemm_operands(case)
-    _log(f"{name}: timing" + (f" with {force_kind}" if force_kind else ""))
     dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[case.out_dtype]
     C = torch.empty((case.M, case.N), dtype=dt, device="cuda")
+    plans = {None: ll.plan_for(A, B, C)}
     if force_kind:
         os.environ["LL_GEMM_KIND"] = force_kind
         try:
-            plan = ll.GemmPlan(ll.gemm_desc_for(A, B, C), A.device)
+            plans[force_kind] = ll.GemmPlan(ll.gemm_desc_for(A, B, C), A.device)
         finally:
             del os.environ["LL_GEMM_KIND"]
-    else:
-        plan = ll.plan_for(A, B, C)
+    return dict(case=case, A=A, B=B, C=C, plans=plans)
+
+
+def time_gemm(p: dict, steps: int, warmup: int, kind: str | None = None) -> dict:
+    import torch
+    case, A, B, C, plan = p["case"], p["A"], p["B"], p["C"], p["plans"][kind]
+    _log(f"{case.name}: timing" + (f" with {kind}" if kind else ""))
     stream = torch.cuda.current_stream()
-    wall, ev = _time_launches(lambda: plan.run(A, B, C, stream.cuda_stream), steps, warmup, stream)
-    tflops = case.flops / (ev * 1e-3) / 1e12
-    return dict(case=case, wall_ms=wall, kernel_ms=ev, tflops=tflops, plan=plan.describe())
+    t = _time_launches(lambda: plan.run(A, B, C, stream.cuda_stream), steps, warmup, stream)
+    return dict(case=case, wall_ms=t["wall_ms"], kernel_ms=t["ms"], median_ms=t["median_ms"],
+                tflops=case.flops / (t["ms"] * 1e-3) / 1e12, plan=plan.describe())
 
 
-def bench_lincomp(name: str, steps: int, warmup: int):
+def prep_lincomp(name: str) -> dict:
+    import torch
+    from synth.device import lincomp_operands
+    _log(f"{name}: preparing inputs")
+    c = _case(name)
+    user, item, W = lincomp_operands(c)
+    Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    return dict(case=c, user=user, item=item, W=W, Y=Y)
+
+
+def time_lincomp(p: dict, steps: int, warmup: int) -> dict:
     import torch
     import recsys_linear_layers_amd as ll
-    import synth
-    from synth.device import lincomp_operands
-    _log(f"{name}: generating inputs")
-    c = synth.lincomp_workload(name)
-    user, item, W = lincomp_operands(c)
-    _log(f"{name}: timing")
-    Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    c, user, item, W, Y = p["case"], p["user"], p["item"], p["W"], p["Y"]
+    _log(f"{c.name}: timing")
     stream = torch.cuda.current_stream()
-    wall, ev = _time_launches(lambda: ll.lincomp(user, item, W, out=Y), steps, warmup, stream)
-    gbs = c.algorithmic_bytes / (ev * 1e-3) / 1e9
-    return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3), gbs=gbs,
-                tflops=c.flops / (ev * 1e-3) / 1e12)
+    t = _time_launches(lambda: ll.lincomp(user, item, W, out=Y), steps, warmup, stream)
+    ev = t["ms"]
+    return dict(case=c, wall_ms=t["wall_ms"], kernel_ms=ev, median_ms=t["median_ms"], req_s=c.R / (ev * 1e-3),
+                gbs=c.algorithmic_bytes / (ev * 1e-3) / 1e9, tflops=c.flops / (ev * 1e-3) / 1e12)
 
 
-def bench_lincomp_stacked(name: str, steps: int, warmup: int):
-    """Times linear compression on the materialised stacked input X
-    [R][C][Nu+Ni][D] and, on the same data, the user-once form; reports the
-    ratio of the two (the speedup of computing the user block once)."""
+def prep_stacked(lc: dict) -> dict:
+    """The workload's materialised stacked input X [R][C][Nu+Ni][D] (every
+    candidate's [user rows; item rows]), built on the device from the
+    user-once workload's operands."""
+    import torch
+    c = lc["case"]
+    X = torch.cat([lc["user"][:, None].expand(c.R, c.C, c.Nu, c.D), lc["item"]], dim=2).contiguous()
+    return dict(lc, X=X)
+
+
+def time_stacked(p: dict, steps: int, warmup: int) -> dict:
+    """Times linear compression on the stacked input and, on the same data, the
+    user-once form; reports the ratio of the two (the speedup of computing the
+    user block once)."""
     import torch
     import recsys_linear_layers_amd as ll
-    import synth
-    from synth.device import lincomp_operands
-    c = synth.lincomp_workload(STACKED_NAMES[name])
-    user, item, W = lincomp_operands(c)
-    X = torch.cat([user[:, None].expand(c.R, c.C, c.Nu, c.D), item], dim=2).contiguous()
-    Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    c, X, W, Y = p["case"], p["X"], p["W"], p["Y"]
     stream = torch.cuda.current_stream()
-    _log(f"{name}: timing the stacked input")
-    wall, ev = _time_launches(lambda: ll.lincomp_stacked(X, W, c.Nu, out=Y), steps, warmup, stream)
-    _log(f"{name}: timing the user-once form on the same data")
-    _, ev_dedup = _time_launches(lambda: ll.lincomp(user, item, W, out=Y), steps, warmup, stream)
+    _log(f"{c.name}: timing the stacked input")
+    t = _time_launches(lambda: ll.lincomp_stacked(X, W, c.Nu, out=Y), steps, warmup, stream)
+    _log(f"{c.name}: timing the user-once form on the same data")
+    td = _time_launches(lambda: ll.lincomp(p["user"], p["item"], W, out=Y), steps, warmup, stream)
+    ev = t["ms"]
     stacked_bytes = X.numel() * 2 + W.numel() * 2 + Y.numel() * 2
-    return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3),
+    return dict(case=c, wall_ms=t["wall_ms"], kernel_ms=ev, median_ms=t["median_ms"], req_s=c.R / (ev * 1e-3),
                 gbs=stacked_bytes / (ev * 1e-3) / 1e9, stacked_bytes=stacked_bytes,
-                dedup_ms=ev_dedup, speedup=ev / ev_dedup)
+                dedup_ms=td["ms"], speedup=ev / td["ms"])
 
 
-def bench_lincomp_ragged(name: str, steps: int, warmup: int):
+def prep_ragged(name: str) -> dict:
     import torch
-    import recsys_linear_layers_amd as ll
-    import synth
     from synth.device import ragged_operands
-    _log(f"{name}: generating inputs")
-    c = synth.lincomp_ragged_workload(name)
+    _log(f"{name}: preparing inputs")
+    c = _case(name)
     user, item, W, offsets = ragged_operands(c)
     Y = torch.empty((c.Ctot, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
-    _log(f"{name}: timing")
-    wall, ev = _time_launches(lambda: ll.lincomp_ragged(user, item, W, offsets, out=Y), steps, warmup, stream)
-    gbs = c.algorithmic_bytes / (ev * 1e-3) / 1e9
-    return dict(case=c, wall_ms=wall, kernel_ms=ev, req_s=c.R / (ev * 1e-3), gbs=gbs)
+    return dict(case=c, user=user, item=item, W=W, offsets=offsets, Y=Y)
 
 
-def bench_gemm_epilogue(name: str, steps: int, warmup: int):
+def time_ragged(p: dict, steps: int, warmup: int) -> dict:
     import torch
     import recsys_linear_layers_amd as ll
-    import synth
-    from synth.device import gemm_operands
-    case = synth.gemm_workload(EPILOGUE_NAMES[name])
-    A, B = gemm_operands(case)
-    bias = torch.randn(case.N, dtype=torch.float32, device="cuda") * 0.5
+    c = p["case"]
+    stream = torch.cuda.current_stream()
+    _log(f"{c.name}: timing")
+    t = _time_launches(lambda: ll.lincomp_ragged(p["user"], p["item"], p["W"], p["offsets"], out=p["Y"]),
+                       steps, warmup, stream)
+    ev = t["ms"]
+    return dict(case=c, wall_ms=t["wall_ms"], kernel_ms=ev, median_ms=t["median_ms"], req_s=c.R / (ev * 1e-3),
+                gbs=c.algorithmic_bytes / (ev * 1e-3) / 1e9)
+
+
+def prep_epilogue(g: dict) -> dict:
+    """The FFN up-projection's operands with a per-column fp32 bias and GELU
+    fused into the GEMM, against the plain GEMM followed by separate bias-add
+    and GELU passes."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    A, B, case = g["A"], g["B"], g["case"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(41)
+    bias = torch.randn(case.N, dtype=torch.float32, device="cuda", generator=gen) * 0.5
     C = torch.empty((case.M, case.N), dtype=torch.bfloat16, device="cuda")
-    fused = ll.plan_for(A, B, C, 0, ll.LL_EPI_BIAS | ll.LL_EPI_GELU)
-    plain = ll.plan_for(A, B, C)
+    return dict(case=case, A=A, B=B, C=C, bias=bias, b16=bias.to(torch.bfloat16),
+                fused=ll.plan_for(A, B, C, 0, ll.LL_EPI_BIAS | ll.LL_EPI_GELU), plain=ll.plan_for(A, B, C))
+
+
+def time_epilogue(p: dict, steps: int, warmup: int) -> dict:
+    import torch
+    A, B, C, case = p["A"], p["B"], p["C"], p["case"]
     stream = torch.cuda.current_stream()
     h = stream.cuda_stream
-    _log(f"{name}: timing the fused epilogue")
-    _, ev_fused = _time_launches(lambda: fused.run(A, B, C, h, bias=bias), steps, warmup, stream)
-    b16 = bias.to(torch.bfloat16)
+    _log(f"{case.name}: timing the fused bias + GELU epilogue")
+    tf = _time_launches(lambda: p["fused"].run(A, B, C, h, bias=p["bias"]), steps, warmup, stream)
 
     def unfused():
-        plain.run(A, B, C, h)
-        torch.nn.functional.gelu(C + b16)
+        p["plain"].run(A, B, C, h)
+        torch.nn.functional.gelu(C + p["b16"])
 
-    _log(f"{name}: timing GEMM + separate bias and GELU passes")
-    _, ev_unfused = _time_launches(unfused, steps, warmup, stream)
-    return dict(case=case, fused_ms=ev_fused, unfused_ms=ev_unfused, plan=fused.describe(),
-                tflops=case.flops / (ev_fused * 1e-3) / 1e12)
+    _log(f"{case.name}: timing GEMM + separate bias and GELU passes")
+    tu = _time_launches(unfused, steps, warmup, stream)
+    return dict(case=case, fused_ms=tf["ms"], median_ms=tf["median_ms"], unfused_ms=tu["ms"],
+                plan=p["fused"].describe(), tflops=case.flops / (tf["ms"] * 1e-3) / 1e12)
 
 
-def cpu_baseline_gemm(name: str, target_s: float = 12.0):
-    """The oracle on the first rows of C, sized to about target_s of CPU time."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on this host's cores
+# ---------------------------------------------------------------------------
+
+def host_info() -> dict:
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        m = re.search(r"^Model name:\s*(.+)$", out, re.M)
+        model = m.group(1).strip() if m else None
+    except Exception:
+        pass
+    if model is None:
+        try:
+            m = re.search(r"^model name\s*:\s*(.+)$", open("/proc/cpuinfo").read(), re.M)
+            model = m.group(1).strip() if m else platform.processor()
+        except OSError:
+            model = platform.processor()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     import oracle
-    import synth
-    case = synth.gemm_workload(name)
-    rows, dt = 1, 0.0
-    while rows < case.M:
+    return dict(cpu_model=model, os_cpu_count=os.cpu_count(), usable_cpus=affinity,
+                oracle_threads=oracle.get_threads())
+
+
+def cpu_baseline_gemm(name: str, strip_rows: int | None = None):
+    """The value-only oracle on the whole product (strip_rows None), or on a
+    seeded strip of strip_rows rows plus the first and last rows, with the
+    time for the whole shape extrapolated by row count and labelled so."""
+    import numpy as np
+    import oracle
+    case = _case(name)
+    if strip_rows is None:
         t0 = time.perf_counter()
-        oracle.gemm_case(case, rows=(0, rows), bound=False)
+        oracle.gemm_case(case, bound=False)
         dt = time.perf_counter() - t0
-        if dt > 0.5:
-            break
-        rows *= 2
-    rows = int(max(1, min(case.M, rows * target_s / max(dt, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.gemm_case(case, rows=(0, rows), bound=False)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * case.N * case.K
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=oracle.get_threads(), kind="oracle",
-                sample=f"fp64 oracle, rows 0..{rows - 1} of C ({rows}x{case.N}x{case.K}), {dt:.1f} s")
+        return dict(workload=name, value=case.flops / dt / 1e12, unit="TFLOP/s", cores=oracle.get_threads(),
+                    kind="oracle", seconds=round(dt, 3),
+                    sample=f"fp64 oracle, whole C ({case.M}x{case.N}x{case.K})")
+    start = int(np.random.default_rng(3).integers(0, case.M - strip_rows))
+    rows_done, dt = 0, 0.0
+    for r0, n in ((start, strip_rows), (0, 1), (case.M - 1, 1)):
+        t0 = time.perf_counter()
+        oracle.gemm_case(case, rows=(r0, n), bound=False)
+        dt += time.perf_counter() - t0
+        rows_done += n
+    flops = 2.0 * rows_done * case.N * case.K
+    return dict(workload=name, value=flops / dt / 1e12, unit="TFLOP/s", cores=oracle.get_threads(), kind="oracle",
+                seconds=round(dt, 3), extrapolated_full_s=round(dt * case.M / rows_done, 1),
+                sample=f"fp64 oracle, rows {start}..{start + strip_rows - 1}, 0 and {case.M - 1} of C "
+                       f"({rows_done}x{case.N}x{case.K}); extrapolated_full_s scales the measured time by "
+                       f"{case.M}/{rows_done} rows (extrapolated, not measured)")
 
 
-def cpu_baseline_lincomp(name: str, target_s: float = 12.0):
+def cpu_baseline_lincomp(name: str, target_s: float = 8.0):
+    """The per-candidate (original, non-deduplicated) oracle on the first
+    candidates of the workload, sized to about target_s of CPU time."""
     import oracle
-    import synth
-    c = synth.lincomp_workload(name)
+    c = _case(name)
     n, dt = 1, 0.0
     while n < c.R * c.C:
         t0 = time.perf_counter()
@@ -248,15 +346,16 @@ def cpu_baseline_lincomp(name: str, target_s: float = 12.0):
     t0 = time.perf_counter()
     oracle.lincomp_case(c, pairs, bound=False)
     dt = time.perf_counter() - t0
-    # requests/s at this candidate rate
-    return dict(value=(n / c.C) / dt, unit="requests/s", cores=oracle.get_threads(), kind="oracle",
-                sample=f"fp64 per-candidate oracle, first {n} candidates, {dt:.1f} s")
+    return dict(workload=name, value=(n / c.C) / dt, unit="requests/s", cores=oracle.get_threads(),
+                kind="oracle", seconds=round(dt, 3),
+                sample=f"fp64 per-candidate oracle (each candidate's stacked input [user; item] "
+                       f"materialised), first {n} of {c.R * c.C} candidates = {n / c.C:.1f} requests")
 
 
 def vendor_context(steps: int, warmup: int):
     """torch.matmul on the GEMM workloads' shapes, operands of the same types
     and scales drawn on the device, timed like the library (same warm-up and
-    step counts, one event pair around the timed calls)."""
+    step counts, per-call events)."""
     import torch
     import synth
     out = []
@@ -265,6 +364,7 @@ def vendor_context(steps: int, warmup: int):
     for name in ["gemm_4096", "ffn_up", "ffn_down", "gemm_3000", "gemm_4096_f16", "skinny_splitk"]:
         M, N, K, kw = synth.GEMM_WORKLOADS[name]
         in_t = {"bf16": torch.bfloat16, "f16": torch.float16}[kw.get("in_dtype", "bf16")]
+
         def draw(rows, cols, dist):
             if dist[0] == "uniform":
                 return (torch.rand(rows, cols, device="cuda", generator=gen) * (dist[2] - dist[1]) + dist[1]).to(in_t)
@@ -275,23 +375,98 @@ def vendor_context(steps: int, warmup: int):
         # timed with a bf16/fp16 C (noted in the result)
         C = torch.empty(M, N, device="cuda", dtype=in_t)
         _log(f"vendor context: {name}")
-        _, ev = _time_launches(lambda: torch.matmul(A, B, out=C), steps, warmup, torch.cuda.current_stream())
-        out.append(dict(workload=name, ms=round(ev, 4), tflops=round(2.0 * M * N * K / (ev * 1e-3) / 1e12, 1),
+        t = _time_launches(lambda: torch.matmul(A, B, out=C), steps, warmup, torch.cuda.current_stream())
+        out.append(dict(workload=name, ms=round(t["ms"], 4), median_ms=round(t["median_ms"], 4),
+                        tflops=round(2.0 * M * N * K / (t["ms"] * 1e-3) / 1e12, 1),
                         c_dtype=str(C.dtype).replace("torch.", ""), library_c_dtype=kw.get("out_dtype", "f32")))
         del A, B, C
         torch.cuda.empty_cache()
     return out
 
 
+# Legs timed before the headline, in this order (the long FFN calls first);
+# the configurations whose oracle is timed too are listed in CPU_LEGS.
+ALSO_ORDER = ["ffn_up", "ffn_down", "ffn_up_bias_gelu", "lincomp_256x128", "lincomp_256x128_stacked",
+              "lincomp_ragged_256", "edge", "skinny_splitk", "gemm_256", "gemm_3000", "gemm_4096_f16", "gemm_4096"]
+# workload -> strip rows (None: the whole problem)
+CPU_LEGS = {"gemm_256": None, "ffn_up": 64, "ffn_down": 64, "edge": None, "skinny_splitk": None}
+
+
+def prep_leg(name: str, preps: dict) -> dict:
+    """Inputs and plans of one workload (reusing another workload's device
+    operands where it is defined on them)."""
+    if name in EPILOGUE_NAMES:
+        base = EPILOGUE_NAMES[name]
+        if base not in preps:
+            preps[base] = prep_gemm(base)
+        return prep_epilogue(preps[base])
+    if name in STACKED_NAMES:
+        base = STACKED_NAMES[name]
+        if base not in preps:
+            preps[base] = prep_lincomp(base)
+        return prep_stacked(preps[base])
+    if name in RAGGED_NAMES:
+        return prep_ragged(name)
+    if name in LINCOMP_NAMES:
+        return prep_lincomp(name)
+    return prep_gemm(name, TILE_RULE_NAMES.get(name))
+
+
+def time_leg(name: str, p: dict, steps: int, warmup: int) -> tuple[dict, dict]:
+    """Time one non-headline workload; returns (its entry of "also", the raw result)."""
+    if name in EPILOGUE_NAMES:
+        x = time_epilogue(p, steps, warmup)
+        return dict(workload=name, ms=round(x["fused_ms"], 4), median_ms=round(x["median_ms"], 4),
+                    value=round(x["tflops"], 1), unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
+                    unfused_ms=round(x["unfused_ms"], 4), fused_speedup=round(x["unfused_ms"] / x["fused_ms"], 3),
+                    plan=x["plan"]), x
+    if name in STACKED_NAMES:
+        x = time_stacked(p, steps, warmup)
+        return dict(workload=name, ms=round(x["kernel_ms"], 4), median_ms=round(x["median_ms"], 4),
+                    value=round(x["req_s"], 1), unit="requests/s", hbm_gbs=round(x["gbs"], 1),
+                    hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4), bytes=x["stacked_bytes"],
+                    user_once_ms=round(x["dedup_ms"], 4), user_once_speedup=round(x["speedup"], 3)), x
+    if name in RAGGED_NAMES:
+        x = time_ragged(p, steps, warmup)
+        c = x["case"]
+        return dict(workload=name, ms=round(x["kernel_ms"], 4), median_ms=round(x["median_ms"], 4),
+                    value=round(x["req_s"], 1), unit="requests/s", candidates=c.Ctot,
+                    candidates_per_request=[int(c.lengths.min()), round(float(c.lengths.mean()), 1),
+                                            int(c.lengths.max())],
+                    hbm_gbs=round(x["gbs"], 1), hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4)), x
+    if name in LINCOMP_NAMES:
+        x = time_lincomp(p, steps, warmup)
+        return dict(workload=name, ms=round(x["kernel_ms"], 4), median_ms=round(x["median_ms"], 4),
+                    value=round(x["req_s"], 1), unit="requests/s", hbm_gbs=round(x["gbs"], 1),
+                    hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4)), x
+    x = time_gemm(p, steps, warmup)
+    entry = dict(workload=name, ms=round(x["kernel_ms"], 4), median_ms=round(x["median_ms"], 4),
+                 value=round(x["tflops"], 1), unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
+                 plan=x["plan"])
+    if name in TILE_RULE_NAMES:
+        y = time_gemm(p, steps, warmup, TILE_RULE_NAMES[name])
+        entry.update(without_rule_ms=round(y["kernel_ms"], 4),
+                     tile_rule_speedup=round(y["kernel_ms"] / x["kernel_ms"], 3), plan_without_rule=y["plan"])
+    return entry, x
+
+
+def lincomp_object(x: dict, cpu: dict | None, name: str) -> dict:
+    """The linear-compression half of the metric: requests/s with its HBM roofline."""
+    c = x["case"]
+    return dict(metric="linear-compression requests/s", value=round(x["req_s"], 1), unit="requests/s",
+                workload=name, ms_per_call=round(x["kernel_ms"], 4), median_ms=round(x["median_ms"], 4),
+                config=dict(requests=c.R, candidates_per_request=c.C, user_rows=c.Nu, item_rows=c.Ni, dim=c.D,
+                            out_rows=c.Mo, y_dtype="bf16", algorithmic_bytes=c.algorithmic_bytes),
+                roofline=dict(bound="hbm", achieved=x["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=x["gbs"] / PEAK_HBM_GBS, traffic=_traffic_from_profiles(name)),
+                cpu_baseline=cpu)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # Short kernels need tens of milliseconds of back-to-back work before the
-    # clocks settle: the 4096^3 GEMM (~0.12 ms per call) measured ~20% low
-    # after 5 warm-up calls, ~9% low after 50, and within 1% of its steady
-    # rate after 300 or 1000.
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gemm_4096",
                     choices=sorted(GEMM_NAMES | LINCOMP_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -322,9 +497,9 @@ def main():
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         stream = torch.cuda.current_stream()
-        wall, ev = _time_launches(lambda: dst.copy_(src), args.steps, args.warmup, stream)
-        print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ev, 4),
-                          "GB/s": round(2 * n / (ev * 1e-3) / 1e9, 1)}))
+        t = _time_launches(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+        print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": round(t["ms"], 4),
+                          "median_ms": round(t["median_ms"], 4), "GB/s": round(2 * n / (t["ms"] * 1e-3) / 1e9, 1)}))
         return
 
     if args.stream_probe_mib:
@@ -334,10 +509,10 @@ def main():
         x = torch.ones((4, n), dtype=torch.float32, device="cuda")
         y = torch.empty(n, dtype=torch.float32, device="cuda")
         stream = torch.cuda.current_stream()
-        wall, ev = _time_launches(lambda: torch.sum(x, dim=0, out=y), args.steps, args.warmup, stream)
+        t = _time_launches(lambda: torch.sum(x, dim=0, out=y), args.steps, args.warmup, stream)
         rd, wr = 16 * n, 4 * n
         print(json.dumps({"probe": "stream 4 reads : 1 write", "bytes_read": rd, "bytes_written": wr,
-                          "ms": round(ev, 4), "GB/s": round((rd + wr) / (ev * 1e-3) / 1e9, 1)}))
+                          "ms": round(t["ms"], 4), "GB/s": round((rd + wr) / (t["ms"] * 1e-3) / 1e9, 1)}))
         return
 
     if args.vendor_context:
@@ -346,9 +521,27 @@ def main():
         return
 
     head = args.workload
+    cpu_on = not args.no_cpu_baseline
+    names = [] if args.no_also else [n for n in ALSO_ORDER if n != head]
+
+    # 1. Every workload's inputs into HBM and its plans made, before any timing.
+    preps = {}
+    for name in names + [head]:
+        if name not in preps:
+            preps[name] = prep_leg(name, preps)
+    torch.cuda.synchronize()
+
+    # 2. Every other configuration, back to back, then the headline.
+    also, lc = [], None
+    for name in names:
+        entry, x = time_leg(name, preps[name], args.steps, args.warmup)
+        also.append(entry)
+        if name in LINCOMP_NAMES:
+            lc = x
     rule_context = {}
     if head in LINCOMP_NAMES:
-        r = bench_lincomp(head, args.steps, args.warmup)
+        r = time_lincomp(preps[head], args.steps, args.warmup)
+        lc = r
         c = r["case"]
         metric, unit, value = "linear-compression requests/s", "requests/s", r["req_s"]
         roof = dict(bound="hbm", achieved=r["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
@@ -359,7 +552,7 @@ def main():
         plan = ("one persistent launch: per request the user block's product once, kept in registers "
                 "and reused as every candidate's starting sums; 4 loading + 4 computing waves")
     else:
-        r = bench_gemm(head, args.steps, args.warmup)
+        r = time_gemm(preps[head], args.steps, args.warmup)
         c = r["case"]
         metric, unit, value = "bf16 GEMM TFLOP/s", "TFLOP/s", r["tflops"]
         roof = dict(bound="mfma", achieved=r["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
@@ -369,73 +562,56 @@ def main():
                       c_dtype=c.out_dtype, flops=c.flops)
         plan = r["plan"]
         if head in TILE_RULE_NAMES:
-            y = bench_gemm(head, args.steps, args.warmup, force_kind=TILE_RULE_NAMES[head])
+            y = time_gemm(preps[head], args.steps, args.warmup, TILE_RULE_NAMES[head])
             rule_context = dict(without_rule_ms=round(y["kernel_ms"], 4), without_rule_tflops=round(y["tflops"], 1),
                                 tile_rule_speedup=round(y["kernel_ms"] / r["kernel_ms"], 3),
                                 plan_without_rule=y["plan"])
+    preps.clear()
+    torch.cuda.empty_cache()
+    for name in list(_CASES):
+        if not (cpu_on and (name in CPU_LEGS or name in LINCOMP_NAMES or name == head)):
+            _drop_case(name)
 
-    also = []
-    if not args.no_also:
-        for name in ["ffn_up", "ffn_down", "ffn_up_bias_gelu", "lincomp_256x128", "lincomp_256x128_stacked",
-                     "lincomp_ragged_256",
-                     "edge", "skinny_splitk", "gemm_3000", "gemm_4096_f16", "gemm_4096"]:
-            if name == head:
+    # 3. CPU baselines, after all GPU timing.
+    cpu, cpus, host, lc_cpu = None, [], None, None
+    if cpu_on:
+        _log("cpu baselines (oracle)")
+        host = host_info()
+        if head in LINCOMP_NAMES:
+            cpu = lc_cpu = cpu_baseline_lincomp(head)
+        else:
+            cpu = cpu_baseline_gemm(head)
+            if lc is not None:
+                lc_cpu = cpu_baseline_lincomp(lc["case"].name)
+        gpu_by_name = {a["workload"]: a for a in also}
+        for name, strip in CPU_LEGS.items():
+            if name == head or name not in gpu_by_name:
                 continue
-            torch.cuda.empty_cache()
-            if name in TILE_RULE_NAMES:
-                x = bench_gemm(name, args.steps, args.warmup)
-                y = bench_gemm(name, args.steps, args.warmup, force_kind=TILE_RULE_NAMES[name])
-                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["tflops"], 1),
-                                 unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
-                                 without_rule_ms=round(y["kernel_ms"], 4),
-                                 tile_rule_speedup=round(y["kernel_ms"] / x["kernel_ms"], 3), plan=x["plan"],
-                                 plan_without_rule=y["plan"]))
-            elif name in EPILOGUE_NAMES:
-                x = bench_gemm_epilogue(name, args.steps, args.warmup)
-                also.append(dict(workload=name, ms=round(x["fused_ms"], 4), value=round(x["tflops"], 1),
-                                 unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
-                                 unfused_ms=round(x["unfused_ms"], 4),
-                                 fused_speedup=round(x["unfused_ms"] / x["fused_ms"], 3), plan=x["plan"]))
-            elif name in RAGGED_NAMES:
-                x = bench_lincomp_ragged(name, args.steps, args.warmup)
-                c = x["case"]
-                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
-                                 unit="requests/s", candidates=c.Ctot,
-                                 candidates_per_request=[int(c.lengths.min()), round(float(c.lengths.mean()), 1),
-                                                         int(c.lengths.max())],
-                                 hbm_gbs=round(x["gbs"], 1), hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4)))
-            elif name in STACKED_NAMES:
-                x = bench_lincomp_stacked(name, args.steps, args.warmup)
-                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
-                                 unit="requests/s", hbm_gbs=round(x["gbs"], 1),
-                                 hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4), bytes=x["stacked_bytes"],
-                                 user_once_ms=round(x["dedup_ms"], 4),
-                                 user_once_speedup=round(x["speedup"], 3)))
-            elif name in LINCOMP_NAMES:
-                x = bench_lincomp(name, args.steps, args.warmup)
-                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["req_s"], 1),
-                                 unit="requests/s", hbm_gbs=round(x["gbs"], 1),
-                                 hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4)))
-            else:
-                x = bench_gemm(name, args.steps, args.warmup)
-                also.append(dict(workload=name, ms=round(x["kernel_ms"], 4), value=round(x["tflops"], 1),
-                                 unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
-                                 plan=x["plan"]))
-            del x
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        _log("cpu baseline (oracle)")
-        cpu = cpu_baseline_lincomp(head) if head in LINCOMP_NAMES else cpu_baseline_gemm(head)
+            b = cpu_baseline_gemm(name, strip)
+            g = gpu_by_name[name]
+            b["gpu_value"] = g["value"]
+            b["gpu_over_cpu"] = round(g["value"] / b["value"], 1)
+            cpus.append(b)
+            _drop_case(name)
+        cpu = dict(cpu, sample=cpu["sample"])
+        cpu.pop("workload", None)
 
     out = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": config, "roofline": roof, "cpu_baseline": cpu,
-        "kernel_ms": round(r["kernel_ms"], 4), "plan": plan, **rule_context, "also": also,
-        "kernel_source_hash": _kernel_source_hash(),
+        "kernel_ms": round(r["kernel_ms"], 4), "kernel_median_ms": round(r["median_ms"], 4),
+        "timed_after": [a["workload"] for a in also],
+        "plan": plan, **rule_context,
     }
+    if lc is not None and head not in LINCOMP_NAMES:
+        out["lincomp"] = lincomp_object(lc, lc_cpu, lc["case"].name)
+    out["also"] = also
+    if cpu_on:
+        out["cpu_baselines"] = cpus
+        out["host"] = host
+    out["kernel_source_hash"] = _kernel_source_hash()
     print(json.dumps(out))
 
 
