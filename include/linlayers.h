@@ -169,6 +169,29 @@ ll_status gemm_run(const gemm_plan* plan, const void* A, const void* B, void* C,
 ll_status gemm_run_ex(const gemm_plan* plan, const void* A, const void* B, void* C, const float* bias,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * gemm_run_ex without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The plan's workspace (packed operand copies,
+ * split-K partials) is taken from a device array inside the library, one per
+ * GPU, LL_NOALLOC_SCRATCH_BYTES long, which each GPU the library runs on
+ * holds from the library's load until the process ends.  The call allocates
+ * and frees nothing and calls no allocating library routine; its first call
+ * on a device looks up that device's array address once.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other host threads) race on it and give undefined
+ * results; serialise them.  Each call writes every workspace byte it reads
+ * before reading it, so nothing left by an earlier call matters.
+ * bias: as for gemm_run_ex (required iff the plan's epilogue adds one,
+ * ignored otherwise).  Results are identical to gemm_run_ex's.
+ * Errors: LL_ERR_WORKSPACE if the plan needs more than
+ * LL_NOALLOC_SCRATCH_BYTES (gemm_plan_workspace_size tells; nothing is
+ * launched), otherwise as gemm_run_ex.
+ */
+#define LL_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB */
+ll_status gemm_run_noalloc(const gemm_plan* plan, const void* A, const void* B, void* C, const float* bias,
+                           void* stream);
+
 ll_status gemm_plan_destroy(gemm_plan* plan);
 
 /*

@@ -73,12 +73,13 @@ _lib.gemm_plan_workspace_size.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
 _lib.gemm_plan_describe.argtypes = [_vp, ctypes.c_char_p, ctypes.c_size_t]
 _lib.gemm_run.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.gemm_run_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.gemm_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.gemm_plan_destroy.argtypes = [_vp]
 _lib.lincomp_workspace_size.argtypes = [ctypes.POINTER(LincompDesc), ctypes.POINTER(ctypes.c_size_t)]
 _lib.lincomp_run.argtypes = [ctypes.POINTER(LincompDesc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.lincomp_ragged_run.argtypes = [ctypes.POINTER(LincompRaggedDesc), _vp, _vp, _vp, _vp, _vp, _vp]
 for _f in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run", "gemm_run_ex",
-           "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "lincomp_ragged_run"):
+           "gemm_run_noalloc", "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "lincomp_ragged_run"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -130,6 +131,13 @@ def gemm_run(plan: int, A: int, B: int, C: int, workspace: int, ws_bytes: int, s
 def gemm_run_ex(plan: int, A: int, B: int, C: int, bias: int, workspace: int, ws_bytes: int,
                 stream: int = 0) -> None:
     _check(_lib.gemm_run_ex(plan, A, B, C, bias, workspace, ws_bytes, stream), "gemm_run_ex")
+
+
+LL_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gemm_run_noalloc(plan: int, A: int, B: int, C: int, bias: int | None = None, stream: int = 0) -> None:
+    _check(_lib.gemm_run_noalloc(plan, A, B, C, bias, stream), "gemm_run_noalloc")
 
 
 def gemm_plan_destroy(plan: int) -> None:

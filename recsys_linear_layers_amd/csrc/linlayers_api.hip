@@ -418,6 +418,61 @@ ll_status gemm_run(const gemm_plan* p, const void* A, const void* B, void* C, vo
   return gemm_run_impl(p, A, B, C, nullptr, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free GEMM: the plan's workspace (packed operand copies, split-K
+// partials) lives in a file-scope device array instead of a caller buffer.
+// Each device holds its own copy of the array from module load until the
+// process ends; its address on a device comes from hipGetSymbolAddress, taken
+// once per device with that device current (the array's name in host code is
+// a host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+static __device__ __align__(256) unsigned char scratch[LL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+ll_status scratch_on_device(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || ((uintptr_t)ptr & 255)) return fail(LL_ERR_HIP, "scratch array address %p not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+ll_status gemm_run_noalloc(const gemm_plan* p, const void* A, const void* B, void* C, const float* bias,
+                           void* stream) {
+  if (!p) return fail(LL_ERR_INVALID_ARG, "null plan");
+  if (p->ws_bytes > (size_t)LL_NOALLOC_SCRATCH_BYTES)
+    return fail(LL_ERR_WORKSPACE, "plan needs %zu bytes of workspace; gemm_run_noalloc holds at most %zu",
+                p->ws_bytes, (size_t)LL_NOALLOC_SCRATCH_BYTES);
+  const bool has_bias = p->d.epilogue & LL_EPI_BIAS;
+  if (has_bias && !bias) return fail(LL_ERR_INVALID_ARG, "the plan's epilogue adds a bias: bias is null");
+  if (has_bias && ((uintptr_t)bias & 3)) return fail(LL_ERR_INVALID_ARG, "bias must be 4-byte aligned");
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device) return fail(LL_ERR_INVALID_ARG, "plan made for device %d, current is %d", p->device, dev);
+  void* ws = nullptr;
+  if (p->ws_bytes > 0) {
+    const ll_status s = scratch_on_device(dev, &ws);
+    if (s != LL_OK) return s;
+  }
+  return gemm_run_impl(p, A, B, C, has_bias ? bias : nullptr, ws, ws ? (size_t)LL_NOALLOC_SCRATCH_BYTES : 0,
+                       stream);
+}
+
 static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B, void* C, const float* bias,
                                void* ws, size_t ws_bytes, void* stream) {
   if (!p) return fail(LL_ERR_INVALID_ARG, "null plan");

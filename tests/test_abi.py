@@ -95,6 +95,7 @@ def test_plan_null_arguments():
     h = ctypes.c_void_p()
     assert ll._lib.gemm_plan_create(ctypes.byref(h), None) == ll.LL_ERR_INVALID_ARG
     assert ll._lib.gemm_run(None, None, None, None, None, 0, None) == ll.LL_ERR_INVALID_ARG
+    assert ll._lib.gemm_run_noalloc(None, None, None, None, None, None) == ll.LL_ERR_INVALID_ARG
     assert ll._lib.gemm_plan_workspace_size(None, None) == ll.LL_ERR_INVALID_ARG
 
 
