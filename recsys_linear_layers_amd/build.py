@@ -37,14 +37,38 @@ def _run(cmd, verbose):
         print(out, file=sys.stderr)
 
 
+# gemm_inst.hip is compiled once per operand layout (A K- or M-contiguous, B K-
+# or N-contiguous), operand type (bf16, fp16) and epilogue (plain, fused), each
+# unit defining the launch function that aux_kernels.hip dispatches to.
+LAYOUTS = {"kk": (1, 1), "kn": (1, 0), "mk": (0, 1), "mn": (0, 0)}
+
+
+def _units():
+    """(source, object, extra flags) for every compile unit."""
+    units = []
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        if os.path.basename(src) == "gemm_inst.hip":
+            continue
+        units.append((src, os.path.join(BUILD, os.path.basename(src)[:-4] + ".o"), []))
+    inst = os.path.join(CSRC, "gemm_inst.hip")
+    for epi in (0, 1):
+        for lay, (ak, bk) in LAYOUTS.items():
+            for f16 in (0, 1):
+                name = "launch_gemm_" + ("epi_" if epi else "") + lay + ("_f16" if f16 else "")
+                defs = [f"-DLL_AK={ak}", f"-DLL_BK={bk}", f"-DLL_F16={f16}", f"-DLL_EPI={epi}",
+                        f"-DLL_LAUNCH={name}"]
+                units.append((inst, os.path.join(BUILD, name + ".o"), defs))
+    return units
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in sources]
+    units = _units()
     jobs = jobs or min(8, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]], verbose),
-                    zip(sources, objs)))
+        list(ex.map(lambda u: _run([HIPCC, *FLAGS, *u[2], "-c", u[0], "-o", u[1]], verbose), units))
+    # objects of sources that no longer exist are not linked
+    objs = [u[1] for u in units]
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -1,5 +1,6 @@
 // Auxiliary kernels: operand packing, split-K reduction, zero fill, and the
-// launch table over the per-layout instantiation units.
+// launch table over the instantiation units of gemm_inst.hip (one per operand
+// layout, operand type and epilogue).
 #include "kernels.hpp"
 
 namespace ll {

@@ -1,10 +1,16 @@
-// Instantiations of the persistent GEMM with a fused epilogue (bias and
-// activation), bf16 operands, A K-contiguous, B K-contiguous.
+// Instantiations of the persistent GEMM for one operand layout and operand
+// type, with or without fused epilogues.  build.py compiles this file once
+// per combination, defining:
+//   LL_AK      1: A K-contiguous, 0: A M-contiguous
+//   LL_BK      1: B K-contiguous, 0: B N-contiguous
+//   LL_F16     1: fp16 operands, 0: bf16
+//   LL_EPI     1: the fused-epilogue instantiations (bias, activation), 0: plain
+//   LL_LAUNCH  name of the launch function this unit defines
 #include "kernels.hpp"
 
-#define LL_AK true
-#define LL_BK true
-#define LL_F16 false
+#if !defined(LL_AK) || !defined(LL_BK) || !defined(LL_F16) || !defined(LL_EPI) || !defined(LL_LAUNCH)
+#error "gemm_inst.hip is compiled with -DLL_AK=.. -DLL_BK=.. -DLL_F16=.. -DLL_EPI=.. -DLL_LAUNCH=.."
+#endif
 
 namespace ll {
 
@@ -18,6 +24,7 @@ static hipError_t launch_cfg(const GemmKArgs& a, int grid, hipStream_t s) {
   }
 }
 
+#if LL_EPI
 template <int BM, int BN, int KT, int WM, int WN, int NP, int LW, int ST, int EP>
 static hipError_t launch_epi(const GemmKArgs& a, int epi, int grid, hipStream_t s) {
   if constexpr (EP == 0) {
@@ -33,11 +40,19 @@ static hipError_t launch_epi(const GemmKArgs& a, int epi, int grid, hipStream_t 
   }
 }
 
-hipError_t launch_gemm_epi_kk(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s) {
+hipError_t LL_LAUNCH(int kind, int epi, const GemmKArgs& a, int grid, hipStream_t s) {
   switch (kind) {
     LL_GEMM_KINDS(LL_KIND_CASE_EPI)
     default: return hipErrorInvalidValue;
   }
 }
+#else
+hipError_t LL_LAUNCH(int kind, const GemmKArgs& a, int grid, hipStream_t s) {
+  switch (kind) {
+    LL_GEMM_KINDS(LL_KIND_CASE)
+    default: return hipErrorInvalidValue;
+  }
+}
+#endif
 
 }  // namespace ll
