@@ -1,0 +1,201 @@
+// 256x256 GEMM kind with four waves of 128x128, one per SIMD, whose k-loop is
+// a hand-ordered instruction stream (KIND_SQ4_HO).
+//
+// What is computed: C = A.B (fp32 accumulation) as in gemm_kernel.hpp, for A
+// K-contiguous and B N-contiguous (row-major A and B, the layout the listings
+// on "Triton 3.7 permite extender el compilador de GPU sin forks" state, and
+// that of the FFN and square benchmark shapes), K a multiple of 64.
+//
+// Why a separate kind: a 128x128 wave tile reads a third less LDS per flop
+// than the 64x128 tiles of the eight-wave kinds (256 rows x 64 k x 2 B of
+// fragments per 2 x 128 x 128 x 64 flops), but it needs 256 fp32
+// accumulators per lane, so it runs one wave per SIMD, and then no partner
+// wave covers a wait: every fragment wait, load-issue stall and barrier wait
+// idles the matrix unit.  The k-loop is therefore one inline-asm statement
+// (gemm_sq4_loop.inc, written by gen_sq4_loop.py) that fixes the position of
+// each wait, fragment read, direct-to-LDS load and barrier among the MFMAs;
+// the accumulators live in a[0:255] for the whole work item.
+//
+// Everything around the loop is ordinary code: per work item the tile's
+// per-lane load offsets (lanes outside the matrix get an offset beyond the
+// descriptor's num_records, so the hardware writes zeros), the first two
+// slices' loads, and after the loop the epilogue, which reads the
+// accumulators one 32x32 block at a time and stores them with the shared
+// epilogue code.
+#pragma once
+
+#include "gemm_kernel.hpp"
+#include "gemm_sq4_loop.inc"
+
+namespace ll {
+
+struct Sq4 {
+  static constexpr int BM = 256, BN = 256, KT = 64, THREADS = 256;
+  static constexpr int SLOT = 65536, B_OFF = 32768, LDS = 2 * SLOT;
+};
+
+// One 32x32 accumulator block, as the shared epilogue code sees a tile of one
+// block (the interior test uses the whole 256x256 tile).
+struct Sq4Block {
+  static constexpr int FM = 1, FN = 1, BM = 256, BN = 256, EPI = 0;
+};
+
+#define LL_SQ4_READ_FN(I, J)                                                                              \
+  __device__ __forceinline__ f32x16 sq4_read_acc_##I##_##J() {                                             \
+    float r[16];                                                                                          \
+    asm volatile(LL_SQ4_READ_ACC_##I##_##J                                                                \
+                 : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]),     \
+                   "=v"(r[7]), "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), \
+                   "=v"(r[14]), "=v"(r[15]));                                                              \
+    f32x16 v;                                                                                             \
+    for (int k = 0; k < 16; ++k) v[k] = r[k];                                                             \
+    return v;                                                                                             \
+  }
+LL_SQ4_READ_FN(0, 0) LL_SQ4_READ_FN(0, 1) LL_SQ4_READ_FN(0, 2) LL_SQ4_READ_FN(0, 3)
+LL_SQ4_READ_FN(1, 0) LL_SQ4_READ_FN(1, 1) LL_SQ4_READ_FN(1, 2) LL_SQ4_READ_FN(1, 3)
+LL_SQ4_READ_FN(2, 0) LL_SQ4_READ_FN(2, 1) LL_SQ4_READ_FN(2, 2) LL_SQ4_READ_FN(2, 3)
+LL_SQ4_READ_FN(3, 0) LL_SQ4_READ_FN(3, 1) LL_SQ4_READ_FN(3, 2) LL_SQ4_READ_FN(3, 3)
+#undef LL_SQ4_READ_FN
+
+template <int I, int J>
+__device__ __forceinline__ f32x16 sq4_read_acc() {
+#define LL_SQ4_PICK(i, j) \
+  if constexpr (I == i && J == j) return sq4_read_acc_##i##_##j();
+  LL_SQ4_PICK(0, 0) LL_SQ4_PICK(0, 1) LL_SQ4_PICK(0, 2) LL_SQ4_PICK(0, 3)
+  LL_SQ4_PICK(1, 0) LL_SQ4_PICK(1, 1) LL_SQ4_PICK(1, 2) LL_SQ4_PICK(1, 3)
+  LL_SQ4_PICK(2, 0) LL_SQ4_PICK(2, 1) LL_SQ4_PICK(2, 2) LL_SQ4_PICK(2, 3)
+  LL_SQ4_PICK(3, 0) LL_SQ4_PICK(3, 1) LL_SQ4_PICK(3, 2) LL_SQ4_PICK(3, 3)
+#undef LL_SQ4_PICK
+}
+
+template <int I, int J>
+__device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0,
+                                                int lane) {
+  f32x16 acc[1][1];
+  acc[0][0] = sq4_read_acc<I, J>();
+  epilogue<Sq4Block>(p, ti, acc, wm0 + 32 * I, wn0 + 32 * J, lane);
+}
+
+// This wave's 8 A and 8 B direct-to-LDS loads of one slice into `slot`.
+// Load q = wave + 4 i of an operand tile covers A rows 8q..8q+7 (K-contiguous,
+// 128 bytes each) or B k-rows 2q, 2q+1 (512 bytes each) and lands at
+// slot + q * 1024 (B tile at +32 KB).
+__device__ __forceinline__ void sq4_issue(i32x4 ra, i32x4 rb, const uint32_t (&va)[8], const uint32_t (&vb)[8],
+                                          uint32_t ldsw, int slot, uint32_t soa, uint32_t sob) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    dma16s(ra, ldsw + slot * Sq4::SLOT + i * 4096, va[i], soa);
+    dma16s(rb, ldsw + slot * Sq4::SLOT + Sq4::B_OFF + i * 4096, vb[i], sob);
+  }
+}
+
+template <bool F16>
+__global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+    gemm_sq4(const GemmKArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::LDS];
+  char LL_LDS* smem = (char LL_LDS*)smem_raw;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int stride = gridDim.x;
+  const int first = xcd_remap(blockIdx.x, gridDim.x);
+  if (first >= p.total) return;  // uniform over the workgroup
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const uint32_t base = lds_u32(smem);
+
+  // LDS addresses of this lane's fragment reads.  A block i (32 rows) at k16
+  // step kk: blocks i and i+2 share the swizzle (rows 64 apart), so one
+  // address per (slot, kk, i parity) serves both (+8192).  B fragment j:
+  // the swizzle depends on the k-row modulo 4 only, so step kk is +8192*kk
+  // and the second half (k-rows +4) +2048 from the step-0 address.
+  uint32_t fa[2][4][2], fb[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int row = wm0 + 32 * par + (lane & 31);
+        const int lc = kk * 2 + (lane >> 5);
+        fa[s][kk][par] = base + s * Sq4::SLOT + row * 128 + ((lc ^ swz_k<8>(row)) << 4);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = lane >> 4, sl = lane & 15;
+      const int mn = wn0 + 32 * j + 16 * (g & 1) + 4 * (sl & 3);
+      const int kr = 8 * (g >> 1) + (sl >> 2);
+      const int lc = mn >> 3, half = (mn & 7) * 2;
+      fb[s][j] = base + s * Sq4::SLOT + Sq4::B_OFF + kr * 512 + ((lc ^ swz_mn<32>(kr)) << 4) + half;
+    }
+  }
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(base + wave * 1024);
+  const int lda = (int)p.a.ld, ldb = (int)p.b.ld;
+  const uint32_t incb = 64u * 2u * (uint32_t)ldb;
+
+  for (int t = first; t < p.total; t += stride) {
+    const TileInfo ti = decode_tile<Sq4>(p, t);
+    int n = ti.ke - ti.kb;
+    uint32_t va[8], vb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = wave + 4 * i;
+      const int row = q * 8 + (lane >> 3);
+      const int lca = (lane & 7) ^ swz_k<8>(row);
+      va[i] = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda + lca * 8) * 2u : kOOB;
+      const int kr = q * 2 + (lane >> 5);
+      const int lcb = (lane & 31) ^ swz_mn<32>(kr);
+      vb[i] = ti.n0 + lcb * 8 < p.b.rows ? (uint32_t)(kr * ldb + lcb * 8) * 2u : kOOB;
+    }
+    const int64_t oa = (int64_t)ti.m0 * p.a.ld + (int64_t)ti.kb * Sq4::KT;
+    const int64_t ob = (int64_t)ti.kb * Sq4::KT * p.b.ld + ti.n0;
+    const i32x4 ra = make_rsrc(p.a.ptr + oa, clamp_records(p.a.extent - oa));
+    const i32x4 rb = make_rsrc(p.b.ptr + ob, clamp_records(p.b.extent - ob));
+
+    sq4_issue(ra, rb, va, vb, ldsw, 0, 0u, 0u);
+    if (n > 1) sq4_issue(ra, rb, va, vb, ldsw, 1, 2u * Sq4::KT, incb);
+    wait_vmcnt<0>();  // also covers the previous work item's stores
+    lds_barrier();
+    int m0v = 0;  // M0 is rewritten by the loop's loads
+
+#define LL_SQ4_OPERANDS                                                                                        \
+  : [n] "+s"(n), [m0] "+{m0}"(m0v)                                                                             \
+  : [a0] "s"(ra[0]), [a1] "s"(ra[1]), [a2] "s"(ra[2]), [a3] "s"(ra[3]), [b0] "s"(rb[0]),                     \
+    [b1] "s"(rb[1]), [b2] "s"(rb[2]), [b3] "s"(rb[3]), [incb] "s"(incb), [ldsw] "s"(ldsw),                    \
+    [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]),                  \
+    [va5] "v"(va[5]), [va6] "v"(va[6]), [va7] "v"(va[7]), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]),                  \
+    [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [vb4] "v"(vb[4]), [vb5] "v"(vb[5]), [vb6] "v"(vb[6]),                  \
+    [vb7] "v"(vb[7]), [fa_0_0_0] "v"(fa[0][0][0]), [fa_0_0_1] "v"(fa[0][0][1]), [fa_0_1_0] "v"(fa[0][1][0]), \
+    [fa_0_1_1] "v"(fa[0][1][1]), [fa_0_2_0] "v"(fa[0][2][0]), [fa_0_2_1] "v"(fa[0][2][1]),                     \
+    [fa_0_3_0] "v"(fa[0][3][0]), [fa_0_3_1] "v"(fa[0][3][1]), [fa_1_0_0] "v"(fa[1][0][0]),                     \
+    [fa_1_0_1] "v"(fa[1][0][1]), [fa_1_1_0] "v"(fa[1][1][0]), [fa_1_1_1] "v"(fa[1][1][1]),                     \
+    [fa_1_2_0] "v"(fa[1][2][0]), [fa_1_2_1] "v"(fa[1][2][1]), [fa_1_3_0] "v"(fa[1][3][0]),                     \
+    [fa_1_3_1] "v"(fa[1][3][1]), [fb_0_0] "v"(fb[0][0]), [fb_0_1] "v"(fb[0][1]), [fb_0_2] "v"(fb[0][2]),       \
+    [fb_0_3] "v"(fb[0][3]), [fb_1_0] "v"(fb[1][0]), [fb_1_1] "v"(fb[1][1]), [fb_1_2] "v"(fb[1][2]),            \
+    [fb_1_3] "v"(fb[1][3])                                                                                     \
+  : LL_SQ4_CLOBBERS
+    if constexpr (F16)
+      asm volatile(LL_SQ4_LOOP_F16 LL_SQ4_OPERANDS);
+    else
+      asm volatile(LL_SQ4_LOOP_BF16 LL_SQ4_OPERANDS);
+#undef LL_SQ4_OPERANDS
+
+    lds_barrier();  // every wave is done reading the ring before it is refilled
+    sq4_store_block<0, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<0, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<0, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<0, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_block<1, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<1, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<1, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<1, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_block<2, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<2, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<2, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<2, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_block<3, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<3, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<3, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<3, 3>(p, ti, wm0, wn0, lane);
+  }
+}
+
+}  // namespace ll

@@ -29,6 +29,9 @@ enum KernelKind {
 #define LL_KIND_ENUM(name, ...) name,
   LL_GEMM_KINDS(LL_KIND_ENUM)
 #undef LL_KIND_ENUM
+  // 256x256 tile, four waves of 128x128 (one per SIMD), hand-ordered k-loop
+  // (gemm_sq4.hpp); A K-contiguous, B N-contiguous, K a multiple of 64.
+  KIND_SQ4_HO,
   KIND_COUNT
 };
 
@@ -55,6 +58,10 @@ hipError_t launch_gemm(int layout, int kind, int f16, const GemmKArgs& args, int
 // ReLU, 3 GELU, 4 SiLU); only kinds marked in LL_GEMM_KINDS have these.
 hipError_t launch_gemm_epi(int layout, int kind, int f16, int epi, const GemmKArgs& args, int grid,
                            hipStream_t stream);
+
+// The hand-ordered 256x256 kind (gemm_sq4.hip): layout 1 (A K-contiguous,
+// B N-contiguous) only.
+hipError_t launch_gemm_sq4(int layout, int f16, const GemmKArgs& args, int grid, hipStream_t stream);
 
 // Fused linear-compression kernel (lincomp_kernel.hpp).
 struct LincompKArgs;

@@ -327,6 +327,11 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     if ((!p.a.kmajor && 64 % (kv.bm / 8) != 0) || (!p.b.kmajor && 64 % (kv.bn / 8) != 0))
       return fail(LL_ERR_UNSUPPORTED, "kernel %s needs K-contiguous operands for its %dx%d tile", kv.name, kv.bm,
                   kv.bn);
+    // The hand-ordered kind reads A K-contiguous and B N-contiguous (as given
+    // or packed) in whole 64-deep slices.
+    if (kind == KIND_SQ4_HO && (!p.a.kmajor || p.b.kmajor || d->K % 64 != 0))
+      return fail(LL_ERR_UNSUPPORTED, "kernel %s needs A K-contiguous, B N-contiguous and K a multiple of 64",
+                  kv.name);
   }
   p.kind = kind;
   const KindInfo& ki = kind_info(kind);

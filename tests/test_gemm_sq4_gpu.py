@@ -1,0 +1,111 @@
+"""The hand-ordered 256x256 kind (four waves of 128x128, KIND_SQ4_HO) forced on
+shapes of every kind of edge, against the fp64 oracle: ragged M and N, one,
+two, three and many 64-deep slices, split K, bf16 and fp16 operands, every
+output type, packed operands, integer inputs bit for bit, and full size."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import gemm_operands, per_tile_indices, plan_tile, sample_indices, strip_starts, to_f64
+from oracle import acceptance
+
+pytestmark = pytest.mark.gpu
+KIND = "KIND_SQ4_HO"
+
+
+def _run(case, monkeypatch, flags=0):
+    import torch
+    import recsys_linear_layers_amd as ll
+    A, B = gemm_operands(case)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[case.out_dtype]
+    C = torch.full((case.M, case.N), float("nan"), dtype=dt, device="cuda")
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", KIND)
+    try:
+        ll.gemm(A, B, out=C, flags=flags)
+        torch.cuda.synchronize()
+        d = ll.plan_for(A, B, C, flags).describe()
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+    assert f"kernel={KIND} " in d, d
+    return to_f64(C), d
+
+
+SHAPES = [(256, 256, 64), (256, 256, 128), (256, 256, 192), (256, 512, 1024), (300, 520, 640),
+          (1000, 1032, 2048), (513, 264, 320), (8, 8, 64), (40, 24, 448), (1536, 1280, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_shapes(M, N, K, out, monkeypatch):
+    c = synth.gemm_case(M, N, K, seed=M * 7 + N * 3 + K, out_dtype=out, dist=("normal", 0.0, 1.0))
+    got, d = _run(c, monkeypatch)
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(got, ref, S, out, f"{M}x{N}x{K} {d}")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (520, 264, 1024), (300, 1032, 640)])
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_f16_operands(M, N, K, out, monkeypatch):
+    c = synth.gemm_case(M, N, K, seed=M + N + K + 5, out_dtype=out, in_dtype="f16")
+    got, d = _run(c, monkeypatch)
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(got, ref, S, out, f"f16 {M}x{N}x{K} {d}")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (520, 776, 1984), (128, 4096, 16384)])
+def test_integer_inputs_bit_exact(M, N, K, monkeypatch):
+    # the last shape splits K (16 tiles on 256 CUs): partials plus the ordered reduce
+    c = synth.gemm_case(M, N, K, dist=("int", -4, 4), seed=M + N + K + 9)
+    got, d = _run(c, monkeypatch)
+    ref, _ = oracle.gemm_case(c)
+    assert np.array_equal(got, ref), d
+
+
+def test_packed_a(monkeypatch):
+    # a column-major A is packed K-contiguous; B stays N-contiguous
+    M, N, K = 300, 520, 640
+    c = synth.gemm_case(M, N, K, seed=77, out_dtype="f32")
+    c.A = synth.bf16_tensor(M * K, "uniform", -1.0, 1.0, seed=77, tensor=5)
+    c.sam, c.sak = 1, M
+    got, d = _run(c, monkeypatch)
+    assert "packA=1" in d
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(got, ref, S, "f32", d)
+
+
+def test_refused_where_it_does_not_apply(monkeypatch):
+    import torch
+    import recsys_linear_layers_amd as ll
+    monkeypatch.setenv("LL_GEMM_KIND", KIND)
+    try:
+        A = torch.zeros((256, 200), dtype=torch.bfloat16, device="cuda")  # K not a multiple of 64
+        B = torch.zeros((200, 256), dtype=torch.bfloat16, device="cuda")
+        C = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+        with pytest.raises(ll.LLError) as e:
+            ll.GemmPlan(ll.gemm_desc_for(A, B, C), A.device)
+        assert e.value.status == ll.LL_ERR_UNSUPPORTED
+        Bc = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda").t()  # B K-contiguous
+        A2 = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(ll.LLError) as e:
+            ll.GemmPlan(ll.gemm_desc_for(A2, Bc, C), A2.device)
+        assert e.value.status == ll.LL_ERR_UNSUPPORTED
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+
+
+@pytest.mark.parametrize("name", ["gemm_4096", "ffn_up"])
+def test_full_size_sampled(name, monkeypatch):
+    c = synth.gemm_workload(name)
+    got, d = _run(c, monkeypatch)
+    tile = plan_tile(d)
+    rows, cols = sample_indices(c.M, c.N, 4096, 5, tile=tile)
+    tr, tc = per_tile_indices(c.M, c.N, tile, 6)
+    rows, cols = np.concatenate([rows, tr]), np.concatenate([cols, tc])
+    ref, S = oracle.gemm_case_entries(c, rows, cols)
+    acceptance.assert_close(got[rows, cols], ref, S, c.out_dtype, f"{name} samples {d}")
+    for r0, nr in strip_starts(c.M, 64, 7):
+        ref, S = oracle.gemm_case(c, rows=(r0, nr))
+        acceptance.assert_close(got[r0:r0 + nr], ref, S, c.out_dtype, f"{name} rows {r0}.. {d}")
