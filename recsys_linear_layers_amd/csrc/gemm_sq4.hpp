@@ -76,16 +76,21 @@ __device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileIn
   epilogue<Sq4Block>(p, ti, acc, wm0 + 32 * I, wn0 + 32 * J, lane);
 }
 
-// This wave's 8 A and 8 B direct-to-LDS loads of one slice into `slot`.
-// Load q = wave + 4 i of an operand tile covers A rows 8q..8q+7 (K-contiguous,
-// 128 bytes each) or B k-rows 2q, 2q+1 (512 bytes each) and lands at
-// slot + q * 1024 (B tile at +32 KB).
+// The first `count` of this wave's 16 direct-to-LDS loads of one slice into
+// `slot`, in the loop's order (A 0, B 0, A 1, B 1, ...).  Load q = wave + 4 i
+// of an operand tile covers A rows 8q..8q+7 (K-contiguous, 128 bytes each) or
+// B k-rows 2q, 2q+1 (512 bytes each) and lands at slot + q * 1024 (B tile at
+// +32 KB).
+template <int COUNT>
 __device__ __forceinline__ void sq4_issue(i32x4 ra, i32x4 rb, const uint32_t (&va)[8], const uint32_t (&vb)[8],
                                           uint32_t ldsw, int slot, uint32_t soa, uint32_t sob) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    dma16s(ra, ldsw + slot * Sq4::SLOT + i * 4096, va[i], soa);
-    dma16s(rb, ldsw + slot * Sq4::SLOT + Sq4::B_OFF + i * 4096, vb[i], sob);
+  for (int k = 0; k < COUNT; ++k) {
+    const int i = k >> 1;
+    if (k & 1)
+      dma16s(rb, ldsw + slot * Sq4::SLOT + Sq4::B_OFF + i * 4096, vb[i], sob);
+    else
+      dma16s(ra, ldsw + slot * Sq4::SLOT + i * 4096, va[i], soa);
   }
 }
 
@@ -150,8 +155,11 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     const i32x4 ra = make_rsrc(p.a.ptr + oa, clamp_records(p.a.extent - oa));
     const i32x4 rb = make_rsrc(p.b.ptr + ob, clamp_records(p.b.extent - ob));
 
-    sq4_issue(ra, rb, va, vb, ldsw, 0, 0u, 0u);
-    if (n > 1) sq4_issue(ra, rb, va, vb, ldsw, 1, 2u * Sq4::KT, incb);
+    // slice 0, and of slice 1 the loads the loop would have issued after the
+    // barrier of the slice before (all 16, or the first LL_SQ4_L3 when the
+    // loop spreads the rest over the next slice's first steps)
+    sq4_issue<16>(ra, rb, va, vb, ldsw, 0, 0u, 0u);
+    if (n > 1) sq4_issue<LL_SQ4_L3>(ra, rb, va, vb, ldsw, 1, 2u * Sq4::KT, incb);
     wait_vmcnt<0>();  // also covers the previous work item's stores
     lds_barrier();
     int m0v = 0;  // M0 is rewritten by the loop's loads

@@ -47,7 +47,10 @@ OUT = os.path.join(HERE, "gemm_sq4_loop.inc")
 
 FBASE = 192         # first fragment VGPR
 READ_SPAN = 10      # MFMAs of steps 0..2 over which the next step's 12 reads are spread
-BAR_AFTER = 2       # MFMAs of step 3 issued before the load wait and barrier
+BAR_AFTER = 0       # MFMAs of step 3 issued before the load wait and barrier
+L3 = 8              # loads of slice j+2 issued in step 3 of slice j; the rest go to steps 0..2 of slice j+1
+CARRY_STEPS = 3     # how many of steps 0..2 of slice j+1 share the rest
+CARRY_SPAN = 14     # MFMAs over which a step's reads and carried loads are spread
 SLOT = 65536
 B_OFF = 32768
 
@@ -100,8 +103,14 @@ def loads(slot):
     return out
 
 
+# Move both descriptors on by one slice: the 64-bit base up, num_records (the
+# operand's bytes from the base; the plan keeps every operand this kind reads
+# below 2 GB, so it is exact) down by the same amount, floored at 0 - a base
+# moved past the operand then reads zeros instead of memory beyond it.
 ADVANCE = ["s_add_u32 s88, s88, 128", "s_addc_u32 s89, s89, 0",
-           "s_add_u32 s92, s92, %[incb]", "s_addc_u32 s93, s93, 0"]
+           "s_sub_u32 s90, s90, 128", "s_cselect_b32 s90, 0, s90",
+           "s_add_u32 s92, s92, %[incb]", "s_addc_u32 s93, s93, 0",
+           "s_sub_u32 s94, s94, %[incb]", "s_cselect_b32 s94, 0, s94"]
 
 
 def interleave(mf, ops, span):
@@ -116,9 +125,32 @@ def interleave(mf, ops, span):
     return out
 
 
-def step(op, slot, kk, buf):
-    """k16 step kk (0..2) of a slice in `slot`: MFMAs on `buf`, reads of step kk+1."""
-    return ["s_waitcnt lgkmcnt(0)"] + interleave(mfmas(op, buf), reads(slot, kk + 1, 1 - buf), READ_SPAN)
+def carried(slot, kk):
+    """Loads of the next slice (into the other slot) issued in step kk (0..2):
+    the 16 - L3 that step 3 of the previous slice left, spread over the first
+    CARRY_STEPS steps; the descriptors advance once, right after the last of
+    them (every path through a slice advances them exactly once)."""
+    rest = loads(1 - slot)[L3:]
+    assert rest and 1 <= CARRY_STEPS <= 3
+    per = [rest[k::CARRY_STEPS] for k in range(CARRY_STEPS)] + [[]] * (3 - CARRY_STEPS)
+    last = max(k for k in range(3) if per[k])
+    return per[kk] + ([ADVANCE] if kk == last else [])
+
+
+def step(op, slot, kk, buf, carry):
+    """k16 step kk (0..2) of a slice in `slot`: MFMAs on `buf`, reads of step kk+1,
+    and (carry) this step's share of the next slice's remaining loads."""
+    rd = reads(slot, kk + 1, 1 - buf)
+    ops = rd
+    if carry:
+        ld = carried(slot, kk)
+        ops = []
+        for k in range(max(len(rd), len(ld))):
+            if k < len(rd):
+                ops.append(rd[k])
+            if k < len(ld):
+                ops.append(ld[k])
+    return ["s_waitcnt lgkmcnt(0)"] + interleave(mfmas(op, buf), ops, READ_SPAN if not carry else CARRY_SPAN)
 
 
 def step3(op, slot, kind):
@@ -131,14 +163,15 @@ def step3(op, slot, kind):
     rd = reads(1 - slot, 0, 0)
     ops = []
     if kind == "load":
-        ld = loads(slot)
+        ld = loads(slot)[:L3]
         # alternate fragment reads (needed first) with loads (longest latency)
         for k in range(max(len(rd), len(ld))):
             if k < len(rd):
                 ops.append(rd[k])
             if k < len(ld):
                 ops.append(ld[k])
-        ops.append(ADVANCE)
+        if L3 == 16:
+            ops.append(ADVANCE)
     else:
         ops = rd
     out += interleave(mf[BAR_AFTER:], ops, len(mf) - BAR_AFTER - 2)
@@ -151,14 +184,23 @@ def loop(op):
     # slice 2, the first slice the loop loads
     L += ["s_mov_b32 s88, %[a0]", "s_mov_b32 s89, %[a1]", "s_mov_b32 s90, %[a2]", "s_mov_b32 s91, %[a3]",
           "s_mov_b32 s92, %[b0]", "s_mov_b32 s93, %[b1]", "s_mov_b32 s94, %[b2]", "s_mov_b32 s95, %[b3]"]
-    L += ADVANCE + ADVANCE
+    # with every load of a slice in step 3 the loop's first load is of slice
+    # 2; otherwise the rest of slice 1 (whose first L3 loads the prologue
+    # issued) comes first, in the first slice's steps 0..2
+    L += ADVANCE + ADVANCE if L3 == 16 else ADVANCE
     L += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(256)]
     L += ["s_nop 4"]
     L += [x for r in reads(0, 0, 0) for x in r]
     for slot in (0, 1):
         L += [f"L_top{slot}_%=:"]
+        if L3 < 16:
+            L += ["s_cmp_lt_u32 %[n], 2", f"s_cbranch_scc1 L_noc{slot}_%="]
+            for kk in range(3):
+                L += step(op, slot, kk, kk % 2, True)
+            L += [f"s_branch L_st3{slot}_%=", f"L_noc{slot}_%=:"]
         for kk in range(3):
-            L += step(op, slot, kk, kk % 2)
+            L += step(op, slot, kk, kk % 2, False)
+        L += [f"L_st3{slot}_%=:"]
         L += ["s_cmp_eq_u32 %[n], 1", f"s_cbranch_scc1 L_last{slot}_%=",
               "s_cmp_eq_u32 %[n], 2", f"s_cbranch_scc1 L_nold{slot}_%="]
         L += step3(op, slot, "load")
@@ -200,6 +242,8 @@ def main():
     for i in range(4):
         for j in range(4):
             parts.append(f"#define LL_SQ4_READ_ACC_{i}_{j} \\\n" + read_acc(i, j) + "\n")
+    parts.append(f"// loads of a slice issued after the barrier of the slice two before; the\n"
+                 f"// prologue issues this many of slice 1\n#define LL_SQ4_L3 {L3}\n")
     parts.append("#define LL_SQ4_CLOBBERS " + clobbers() + "\n")
     text = "\n".join(parts)
     with open(OUT, "w") as f:

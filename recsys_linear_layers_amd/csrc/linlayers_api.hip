@@ -267,6 +267,15 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     return t * 2 <= p.cus ? -1 : (t + p.cus - 1) / p.cus;  // -1: the plan would split K
   };
   const bool free_choice = !(d->flags & (LL_FLAG_COOPERATIVE | LL_FLAG_PRODUCER_CONSUMER));
+  // The hand-ordered kind moves its buffer descriptors along k and shrinks
+  // their num_records with them, which is exact only while each operand, as
+  // the kernel reads it, spans less than 2 GB from its base.
+  auto span_bytes = [&](const OperandPlan& op, int64_t rows) -> int64_t {
+    if (op.pack) return (op.pack_mn ? d->K : rows) * op.ldp * 2;
+    return (op.kmajor ? (rows - 1) * op.ld + d->K : (d->K - 1) * op.ld + rows) * 2;
+  };
+  const bool sq4_fits = p.a.kmajor && !p.b.kmajor && d->K % 64 == 0 && span_bytes(p.a, M) < 0x7FFFFFF0ll &&
+                        span_bytes(p.b, N) < 0x7FFFFFF0ll;
   if (free_choice && p.a.kmajor && (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
     const int64_t pb = passes(kind), pt = passes(KIND_T192_PC);
     const KindInfo& kb = kind_info(kind);
@@ -301,6 +310,19 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     const KindInfo& kt = kind_info(KIND_TALL_PC);
     if (pk > 0 && pt > 0 && pt * kt.bm * kt.bn <= pk * kk.bm * kk.bn) kind = KIND_TALL_PC;
   }
+  // The hand-ordered 256x256 kind (four 128x128 waves, gemm_sq4.hpp) was
+  // ahead of every kind above wherever it applies: A K-contiguous, B
+  // N-contiguous, K a multiple of 64, no fused epilogue (measured on the same
+  // operands: 4096^3 +5%, FFN-up +3%, FFN-down +14% over 128x256, 8192^3 +8%,
+  // 4096^2 x 16384 +7% over 128x256).  Like the other rules it takes over
+  // only when its passes times tile area is no larger and neither choice
+  // would split K.
+  if (free_choice && !d->epilogue && sq4_fits &&
+      (kind == KIND_WIDE_PC || kind == KIND_TALL_PC || kind == KIND_SQ8_LW4 || kind == KIND_T192_PC)) {
+    const int64_t pc = passes(kind), ph = passes(KIND_SQ4_HO);
+    const KindInfo& kc = kind_info(kind);
+    if (pc > 0 && ph > 0 && ph * 256 * 256 <= pc * kc.bm * kc.bn) kind = KIND_SQ4_HO;
+  }
   if (d->flags & LL_FLAG_COOPERATIVE) {
     if (kind == KIND_WIDE_PC) kind = KIND_SQ8_K64;
     else if (kind_info(kind).nprod > 0) kind = KIND_WIDE_COOP;
@@ -329,8 +351,9 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
                   kv.bn);
     // The hand-ordered kind reads A K-contiguous and B N-contiguous (as given
     // or packed) in whole 64-deep slices.
-    if (kind == KIND_SQ4_HO && (!p.a.kmajor || p.b.kmajor || d->K % 64 != 0))
-      return fail(LL_ERR_UNSUPPORTED, "kernel %s needs A K-contiguous, B N-contiguous and K a multiple of 64",
+    if (kind == KIND_SQ4_HO && !sq4_fits)
+      return fail(LL_ERR_UNSUPPORTED,
+                  "kernel %s needs A K-contiguous, B N-contiguous, K a multiple of 64 and operands below 2 GB",
                   kv.name);
   }
   p.kind = kind;

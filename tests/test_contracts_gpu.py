@@ -122,6 +122,6 @@ def test_plan_describe_reports_the_choice():
     A = torch.zeros((4096, 4096), dtype=torch.bfloat16, device="cuda")
     C = torch.zeros((4096, 4096), dtype=torch.bfloat16, device="cuda")
     d = ll.plan_for(A, A, C).describe()
-    assert "kernel=KIND_SQ8_LW4" in d and "splitk=1" in d
+    assert "kernel=KIND_SQ4_HO" in d and "splitk=1" in d
     d = ll.plan_for(A, A, C, 0, ll.LL_EPI_GELU).describe()
     assert "fused=3" in d and "kernel=KIND_WIDE_PC" in d

@@ -59,6 +59,30 @@ def test_random_case_square_kind(i, monkeypatch):
         ll._plans.clear()
 
 
+N_SQ4 = 40
+
+
+@pytest.mark.parametrize("i", range(N_SQ4))
+def test_random_case_hand_ordered_kind(i, monkeypatch):
+    """The hand-ordered 256x256 kind forced on random cases it applies to: A
+    row-major (any leading dimension: a misaligned one is packed K-contiguous),
+    B row-major (same, packed N-contiguous), K a multiple of 64, no fused
+    epilogue."""
+    import recsys_linear_layers_amd as ll
+    d = _draw(N_CASES + N_SQUARE + i)
+    rng = np.random.default_rng(5000 + i)
+    d["K"] = 64 * int(rng.integers(1, 13))
+    d["a_col"], d["b_col"] = False, False
+    d["act"], d["bias"], d["flags"] = None, False, 0
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
+    try:
+        _check(N_CASES + N_SQUARE + i, d, want_kind="KIND_SQ4_HO")
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+
+
 def _check(i, d, want_kind=None):
     import torch
     import recsys_linear_layers_amd as ll

@@ -96,6 +96,35 @@ def test_refused_where_it_does_not_apply(monkeypatch):
         monkeypatch.delenv("LL_GEMM_KIND", raising=False)
 
 
+def _describe(M, N, K, a_col=False, b_col=False, in_t=0, c_t=0, flags=0, epilogue=0):
+    import recsys_linear_layers_amd as ll
+    sam, sak = (1, M) if a_col else (K, 1)
+    sbk, sbn = (1, K) if b_col else (N, 1)
+    h = ll.gemm_plan_create(ll.GemmDesc(M, N, K, sam, sak, sbk, sbn, N, 1, in_t, in_t, c_t, flags, epilogue))
+    try:
+        return ll.gemm_plan_describe(h)
+    finally:
+        ll.gemm_plan_destroy(h)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (16384, 28672, 8192), (16384, 8192, 28672),
+                                   (8192, 8192, 8192), (4096, 4096, 16384), (4000, 4000, 640)])
+def test_selected_on_square_and_ffn_shapes(M, N, K):
+    assert f"kernel={KIND} " in _describe(M, N, K)
+
+
+def test_selection_conditions():
+    import recsys_linear_layers_amd as ll
+    assert f"kernel={KIND} " in _describe(4096, 4096, 4096, in_t=ll.LL_F16, c_t=ll.LL_F16)
+    assert f"kernel={KIND} " in _describe(4096, 4096, 4096, c_t=ll.LL_F32)
+    for kw in (dict(b_col=True), dict(a_col=True), dict(epilogue=ll.LL_EPI_GELU), dict(epilogue=ll.LL_EPI_BIAS),
+               dict(flags=ll.LL_FLAG_PRODUCER_CONSUMER), dict(flags=ll.LL_FLAG_COOPERATIVE)):
+        assert f"kernel={KIND} " not in _describe(4096, 4096, 4096, **kw), kw
+    assert f"kernel={KIND} " not in _describe(4096, 4096, 4104)        # K % 64 != 0
+    assert f"kernel={KIND} " not in _describe(2048, 4096, 8192)        # 128 tiles would split K
+    assert f"kernel={KIND} " not in _describe(128, 8192, 65536)        # skinny
+
+
 @pytest.mark.parametrize("name", ["gemm_4096", "ffn_up"])
 def test_full_size_sampled(name, monkeypatch):
     c = synth.gemm_workload(name)

@@ -2,10 +2,11 @@
 
 The plan puts it in place of the 256x128 producer/consumer tile when A is
 K-contiguous, B is N-contiguous, there is no fused epilogue, and its tiles
-cover the problem in no more passes times tile area.  Parity against the fp64
-oracle on a ragged shape that selects it, the selection on the benchmark
-shapes, and the kind forced on small ragged shapes in every operand layout,
-both input types, split-K and K = 0."""
+cover the problem in no more passes times tile area; where K is a multiple of
+64 the hand-ordered 256x256 kind (four 128x128 waves) takes its place again.
+Parity against the fp64 oracle on ragged shapes that select it, the selection
+on the benchmark shapes, and the kind forced on small ragged shapes in every
+operand layout, both input types, split-K and K = 0."""
 import numpy as np
 import pytest
 
@@ -63,27 +64,31 @@ def _run(case, flags=0):
     return C, desc
 
 
+SQ4 = "KIND_SQ4_HO"
+
+
 @pytest.mark.parametrize("M,N,K,want", [
-    (4096, 4096, 4096, True),     # 256 tiles of 256x256 (1 pass) vs 512 of 256x128 (2 passes)
-    (16384, 28672, 8192, True),   # FFN up: 7 passes vs 14
-    (16384, 8192, 28672, False),  # FFN down: M > N keeps 128x256
-    (8192, 8192, 28672, False),   # K > 8192: 128x256
-    (8192, 16384, 24576, False),  # K > 8192: 128x256
-    (8192, 8192, 8192, True),     # K = 8192 keeps 256x256
-    (4000, 4000, 136, True),      # ragged: 256 tiles vs 512
-    (4096, 2048, 8192, False),    # M > N
-    (2048, 4096, 8192, False),    # 128 tiles of 256x256 would split K; 256x128 fills the CUs
-    (3000, 3000, 3000, False),    # the 192x256 tile-count rule
-    (8191, 5003, 4099, False),    # edge: B column-major (packed K-contiguous)
-    (128, 8192, 65536, False),    # skinny: split-K
+    (4096, 4096, 4096, SQ4),         # K a multiple of 64: the hand-ordered kind
+    (16384, 28672, 8192, SQ4),       # FFN up
+    (16384, 8192, 28672, SQ4),       # FFN down
+    (8192, 8192, 28672, SQ4),
+    (8192, 8192, 8192, SQ4),
+    (4096, 4096, 4104, KIND),        # K not a multiple of 64: 256 tiles of 256x256 vs 512 of 256x128
+    (4000, 4000, 136, KIND),         # ragged
+    (16384, 28672, 8136, KIND),      # FFN up with K % 64 = 8
+    (4096, 2048, 8192, "KIND_TALL_PC"),   # 128 tiles of 256x256 would split K; M > N
+    (2048, 4096, 8192, "KIND_WIDE_PC"),   # same, M < N
+    (3000, 3000, 3000, "KIND_T192_PC"),   # the 192x256 tile-count rule
+    (128, 8192, 65536, "KIND_TALL_PC"),   # skinny: split-K
 ])
 def test_rule_selection(M, N, K, want):
     d = _describe(M, N, K)
-    assert (KIND in d) == want, d
+    assert f"kernel={want} " in d, d
 
 
-@pytest.mark.parametrize("M,N,K", [(8192, 8192, 28672), (4096, 4096, 16384), (8192, 16384, 24576)])
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 28680), (4096, 4096, 16392), (8192, 16384, 24584)])
 def test_long_k_rule_picks_128x256(M, N, K):
+    # K > 8192 and not a multiple of 64 (else the hand-ordered kind takes it)
     ll = _ll()
     assert "kernel=KIND_TALL_PC " in _describe(M, N, K)
     # with a fused epilogue, another layout or a forced mode the rule stays out
@@ -95,28 +100,29 @@ def test_long_k_selected_sampled():
     """A square long-K shape the rule sends to the 128x256 kind, at full size:
     sampled entries (the corners and the last tile row and column included)
     and row strips against the oracle."""
-    c = synth.gemm_case(4096, 4096, 16384, seed=259, dist=("normal", 0.0, 1.0), out_dtype="bf16")
+    c = synth.gemm_case(4096, 4096, 16392, seed=259, dist=("normal", 0.0, 1.0), out_dtype="bf16")
     C, desc = _run(c)
     assert "kernel=KIND_TALL_PC " in desc, desc
     got = to_f64(C)
     rows, cols = sample_indices(c.M, c.N, 2048, seed=6, tile=256)
     ref, S = oracle.gemm_case_entries(c, rows, cols)
-    acceptance.assert_close(got[rows, cols], ref, S, "bf16", "4096x4096x16384 samples")
+    acceptance.assert_close(got[rows, cols], ref, S, "bf16", "4096x4096x16392 samples")
     for r0 in (0, c.M - 8):
         ref, S = oracle.gemm_case(c, rows=(r0, 8))
-        acceptance.assert_close(got[r0:r0 + 8], ref, S, "bf16", f"4096x4096x16384 strip {r0}")
+        acceptance.assert_close(got[r0:r0 + 8], ref, S, "bf16", f"4096x4096x16392 strip {r0}")
 
 
 def test_rule_conditions():
     ll = _ll()
-    assert KIND in _describe(4096, 4096, 4096, in_t=ll.LL_F16, c_t=ll.LL_F16)
-    assert KIND in _describe(4096, 4096, 4096, c_t=ll.LL_F32)
-    assert KIND not in _describe(4096, 4096, 4096, b_col=True)   # B K-contiguous
-    assert KIND not in _describe(4096, 4096, 4096, a_col=True)   # A M-contiguous
-    assert KIND not in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_GELU)
-    assert KIND not in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_BIAS)
-    assert KIND not in _describe(4096, 4096, 4096, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
-    assert KIND not in _describe(4096, 4096, 4096, flags=ll.LL_FLAG_COOPERATIVE)
+    K = 4104  # not a multiple of 64, so the hand-ordered kind stays out
+    assert KIND in _describe(4096, 4096, K, in_t=ll.LL_F16, c_t=ll.LL_F16)
+    assert KIND in _describe(4096, 4096, K, c_t=ll.LL_F32)
+    assert KIND not in _describe(4096, 4096, K, b_col=True)   # B K-contiguous
+    assert KIND not in _describe(4096, 4096, K, a_col=True)   # A M-contiguous
+    assert KIND not in _describe(4096, 4096, K, epilogue=ll.LL_EPI_GELU)
+    assert KIND not in _describe(4096, 4096, K, epilogue=ll.LL_EPI_BIAS)
+    assert KIND not in _describe(4096, 4096, K, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
+    assert KIND not in _describe(4096, 4096, K, flags=ll.LL_FLAG_COOPERATIVE)
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
