@@ -15,7 +15,7 @@ hipError_t launch_gemm_mk_f16(int kind, const GemmKArgs& a, int grid, hipStream_
 hipError_t launch_gemm_mn_f16(int kind, const GemmKArgs& a, int grid, hipStream_t s);
 
 hipError_t launch_gemm(int layout, int kind, int f16, const GemmKArgs& args, int grid, hipStream_t stream) {
-  if (kind == KIND_SQ4_HO) return launch_gemm_sq4(layout, f16, args, grid, stream);
+  if (kind == KIND_SQ4_HO) return launch_gemm_sq4(layout, f16, 0, args, grid, stream);
   if (f16) {
     switch (layout) {
       case 0: return launch_gemm_kk_f16(kind, args, grid, stream);
@@ -45,6 +45,7 @@ hipError_t launch_gemm_epi_mn_f16(int kind, int epi, const GemmKArgs& a, int gri
 
 hipError_t launch_gemm_epi(int layout, int kind, int f16, int epi, const GemmKArgs& args, int grid,
                            hipStream_t stream) {
+  if (kind == KIND_SQ4_HO) return launch_gemm_sq4(layout, f16, epi, args, grid, stream);
   switch (layout * 2 + (f16 ? 1 : 0)) {
     case 0: return launch_gemm_epi_kk(kind, epi, args, grid, stream);
     case 1: return launch_gemm_epi_kk_f16(kind, epi, args, grid, stream);
@@ -62,7 +63,7 @@ const KindInfo& kind_info(int kind) {
 #define LL_KIND_INFO(name, bm, bn, kt, wm, wn, np, lw, st, ep) \
   {bm, bn, kt, (wm * wn + np) * 64, st * (bm + bn) * kt * 2, st, np, ep, #name},
   static const KindInfo table[KIND_COUNT] = {LL_GEMM_KINDS(LL_KIND_INFO)
-                                             {256, 256, 64, 256, 2 * 65536, 2, 0, 0, "KIND_SQ4_HO"}};
+                                             {256, 256, 64, 256, 2 * 65536, 2, 0, 1, "KIND_SQ4_HO"}};
 #undef LL_KIND_INFO
   return table[kind];
 }

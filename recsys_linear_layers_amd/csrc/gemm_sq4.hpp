@@ -35,9 +35,12 @@ struct Sq4 {
 };
 
 // One 32x32 accumulator block, as the shared epilogue code sees a tile of one
-// block (the interior test uses the whole 256x256 tile).
+// block (the interior test uses the whole 256x256 tile).  EPI: 0 plain, else
+// the per-column bias (if given) and activation EPI-1 on every sum before it
+// is stored (as GemmCfg::EPI).
+template <int EPI_>
 struct Sq4Block {
-  static constexpr int FM = 1, FN = 1, BM = 256, BN = 256, EPI = 0;
+  static constexpr int FM = 1, FN = 1, BM = 256, BN = 256, EPI = EPI_;
 };
 
 #define LL_SQ4_READ_FN(I, J)                                                                              \
@@ -68,12 +71,12 @@ __device__ __forceinline__ f32x16 sq4_read_acc() {
 #undef LL_SQ4_PICK
 }
 
-template <int I, int J>
+template <int EPI, int I, int J>
 __device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0,
                                                 int lane) {
   f32x16 acc[1][1];
   acc[0][0] = sq4_read_acc<I, J>();
-  epilogue<Sq4Block>(p, ti, acc, wm0 + 32 * I, wn0 + 32 * J, lane);
+  epilogue<Sq4Block<EPI>>(p, ti, acc, wm0 + 32 * I, wn0 + 32 * J, lane);
 }
 
 // The first `count` of this wave's 16 direct-to-LDS loads of one slice into
@@ -94,7 +97,7 @@ __device__ __forceinline__ void sq4_issue(i32x4 ra, i32x4 rb, const uint32_t (&v
   }
 }
 
-template <bool F16>
+template <bool F16, int EPI>
 __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_sq4(const GemmKArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::LDS];
@@ -187,22 +190,22 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
 #undef LL_SQ4_OPERANDS
 
     lds_barrier();  // every wave is done reading the ring before it is refilled
-    sq4_store_block<0, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<0, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<0, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<0, 3>(p, ti, wm0, wn0, lane);
-    sq4_store_block<1, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<1, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<1, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<1, 3>(p, ti, wm0, wn0, lane);
-    sq4_store_block<2, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<2, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<2, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<2, 3>(p, ti, wm0, wn0, lane);
-    sq4_store_block<3, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<3, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<3, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<3, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 0, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 0, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 0, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 0, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 1, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 1, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 1, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 1, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 2, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 2, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 2, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 2, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 3, 0>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 3, 1>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 3, 2>(p, ti, wm0, wn0, lane);
+    sq4_store_block<EPI, 3, 3>(p, ti, wm0, wn0, lane);
   }
 }
 

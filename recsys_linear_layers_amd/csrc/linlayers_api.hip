@@ -312,12 +312,12 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   }
   // The hand-ordered 256x256 kind (four 128x128 waves, gemm_sq4.hpp) was
   // ahead of every kind above wherever it applies: A K-contiguous, B
-  // N-contiguous, K a multiple of 64, no fused epilogue (measured on the same
-  // operands: 4096^3 +5%, FFN-up +3%, FFN-down +14% over 128x256, 8192^3 +8%,
-  // 4096^2 x 16384 +7% over 128x256).  Like the other rules it takes over
-  // only when its passes times tile area is no larger and neither choice
-  // would split K.
-  if (free_choice && !d->epilogue && sq4_fits &&
+  // N-contiguous, K a multiple of 64 (measured on the same operands: 4096^3
+  // +5%, FFN-up +3%, FFN-down +14% over 128x256, 8192^3 +8%, 4096^2 x 16384
+  // +7% over 128x256), with or without a fused epilogue.  Like the other
+  // rules it takes over only when its passes times tile area is no larger
+  // and neither choice would split K.
+  if (free_choice && sq4_fits &&
       (kind == KIND_WIDE_PC || kind == KIND_TALL_PC || kind == KIND_SQ8_LW4 || kind == KIND_T192_PC)) {
     const int64_t pc = passes(kind), ph = passes(KIND_SQ4_HO);
     const KindInfo& kc = kind_info(kind);

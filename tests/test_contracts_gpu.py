@@ -124,4 +124,4 @@ def test_plan_describe_reports_the_choice():
     d = ll.plan_for(A, A, C).describe()
     assert "kernel=KIND_SQ4_HO" in d and "splitk=1" in d
     d = ll.plan_for(A, A, C, 0, ll.LL_EPI_GELU).describe()
-    assert "fused=3" in d and "kernel=KIND_WIDE_PC" in d
+    assert "fused=3" in d and "kernel=KIND_SQ4_HO" in d

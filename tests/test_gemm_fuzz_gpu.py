@@ -66,14 +66,14 @@ N_SQ4 = 40
 def test_random_case_hand_ordered_kind(i, monkeypatch):
     """The hand-ordered 256x256 kind forced on random cases it applies to: A
     row-major (any leading dimension: a misaligned one is packed K-contiguous),
-    B row-major (same, packed N-contiguous), K a multiple of 64, no fused
-    epilogue."""
+    B row-major (same, packed N-contiguous), K a multiple of 64; bias and
+    activation as drawn."""
     import recsys_linear_layers_amd as ll
     d = _draw(N_CASES + N_SQUARE + i)
     rng = np.random.default_rng(5000 + i)
     d["K"] = 64 * int(rng.integers(1, 13))
     d["a_col"], d["b_col"] = False, False
-    d["act"], d["bias"], d["flags"] = None, False, 0
+    d["flags"] = 0
     ll._plans.clear()
     monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
     try:

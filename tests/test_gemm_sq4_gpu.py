@@ -117,12 +117,42 @@ def test_selection_conditions():
     import recsys_linear_layers_amd as ll
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, in_t=ll.LL_F16, c_t=ll.LL_F16)
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, c_t=ll.LL_F32)
-    for kw in (dict(b_col=True), dict(a_col=True), dict(epilogue=ll.LL_EPI_GELU), dict(epilogue=ll.LL_EPI_BIAS),
+    assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_GELU)
+    assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_BIAS | ll.LL_EPI_SILU)
+    for kw in (dict(b_col=True), dict(a_col=True),
                dict(flags=ll.LL_FLAG_PRODUCER_CONSUMER), dict(flags=ll.LL_FLAG_COOPERATIVE)):
         assert f"kernel={KIND} " not in _describe(4096, 4096, 4096, **kw), kw
     assert f"kernel={KIND} " not in _describe(4096, 4096, 4104)        # K % 64 != 0
     assert f"kernel={KIND} " not in _describe(2048, 4096, 8192)        # 128 tiles would split K
     assert f"kernel={KIND} " not in _describe(128, 8192, 65536)        # skinny
+
+
+@pytest.mark.parametrize("act", [None, "relu", "gelu", "silu"])
+@pytest.mark.parametrize("M,N,K,out", [(300, 520, 640, "f32"), (513, 264, 320, "bf16"), (256, 256, 64, "f32"),
+                                       (128, 4096, 16384, "bf16")])
+def test_fused_bias_activation(act, M, N, K, out, monkeypatch):
+    """Per-column bias and ReLU / GELU / SiLU on the fp32 sums before the store;
+    the last shape splits K (the ordered reduce applies the epilogue)."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    c = synth.gemm_case(M, N, K, seed=M + 2 * N + 3 * K, out_dtype=out, dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    bias = torch.from_numpy(np.random.default_rng(M + N).standard_normal(N).astype(np.float32)).cuda()
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[out]
+    C = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", KIND)
+    try:
+        ll.gemm(A, B, out=C, bias=bias, act=act)
+        torch.cuda.synchronize()
+        d = ll.plan_for(A, B, C, 0, ll.LL_EPI_BIAS | ll.ACTIVATIONS[act]).describe()
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+    assert f"kernel={KIND} " in d, d
+    ref, S = oracle.gemm_case(c)
+    ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+    acceptance.assert_close(to_f64(C), ref, S, out, f"{M}x{N}x{K} bias+{act} {d}", act=act)
 
 
 @pytest.mark.parametrize("name", ["gemm_4096", "ffn_up"])
