@@ -58,6 +58,9 @@ RAGGED_NAMES = {"lincomp_ragged_256"}
 # FFN up-projection with its bias and GELU fused into the GEMM's epilogue,
 # against the same GEMM followed by separate bias-add and GELU passes.
 EPILOGUE_NAMES = {"ffn_up_bias_gelu": "ffn_up"}
+# Linear compression with a per-compressed-row bias and GELU fused into its
+# epilogue, against the plain layer followed by separate bias-add and GELU passes.
+LC_EPILOGUE_NAMES = {"lincomp_256x128_bias_gelu": "lincomp_256x128"}
 
 
 def _kernel_source_hash() -> str:
@@ -272,6 +275,34 @@ def time_epilogue(p: dict, steps: int, warmup: int) -> dict:
                 plan=p["fused"].describe(), tflops=case.flops / (tf["ms"] * 1e-3) / 1e12)
 
 
+def prep_lc_epilogue(lc: dict) -> dict:
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(43)
+    c = lc["case"]
+    bias = torch.randn(c.Mo, dtype=torch.float32, device="cuda", generator=gen) * 0.5
+    return dict(lc, bias=bias, b16=bias.to(torch.bfloat16)[:, None])
+
+
+def time_lc_epilogue(p: dict, steps: int, warmup: int) -> dict:
+    import torch
+    import recsys_linear_layers_amd as ll
+    c, user, item, W, Y = p["case"], p["user"], p["item"], p["W"], p["Y"]
+    stream = torch.cuda.current_stream()
+    _log(f"{c.name}: timing the fused bias + GELU epilogue")
+    tf = _time_launches(lambda: ll.lincomp(user, item, W, out=Y, bias=p["bias"], act="gelu"), steps, warmup, stream)
+
+    def unfused():
+        ll.lincomp(user, item, W, out=Y)
+        torch.nn.functional.gelu(Y + p["b16"])
+
+    _log(f"{c.name}: timing the layer + separate bias and GELU passes")
+    tu = _time_launches(unfused, steps, warmup, stream)
+    ev = tf["ms"]
+    return dict(case=c, fused_ms=ev, median_ms=tf["median_ms"], unfused_ms=tu["ms"], req_s=c.R / (ev * 1e-3),
+                gbs=c.algorithmic_bytes / (ev * 1e-3) / 1e9)
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on this host's cores
 # ---------------------------------------------------------------------------
@@ -387,7 +418,8 @@ def vendor_context(steps: int, warmup: int):
 # Legs timed before the headline, in this order (the long FFN calls first);
 # the configurations whose oracle is timed too are listed in CPU_LEGS.
 ALSO_ORDER = ["ffn_up", "ffn_down", "ffn_up_bias_gelu", "lincomp_256x128", "lincomp_256x128_stacked",
-              "lincomp_ragged_256", "edge", "skinny_splitk", "gemm_256", "gemm_3000", "gemm_4096_f16", "gemm_4096"]
+              "lincomp_256x128_bias_gelu", "lincomp_ragged_256", "edge", "skinny_splitk", "gemm_256", "gemm_3000",
+              "gemm_4096_f16", "gemm_4096"]
 # workload -> strip rows (None: the whole problem)
 CPU_LEGS = {"gemm_256": None, "ffn_up": 64, "ffn_down": 64, "edge": None, "skinny_splitk": None}
 
@@ -405,6 +437,11 @@ def prep_leg(name: str, preps: dict) -> dict:
         if base not in preps:
             preps[base] = prep_lincomp(base)
         return prep_stacked(preps[base])
+    if name in LC_EPILOGUE_NAMES:
+        base = LC_EPILOGUE_NAMES[name]
+        if base not in preps:
+            preps[base] = prep_lincomp(base)
+        return prep_lc_epilogue(preps[base])
     if name in RAGGED_NAMES:
         return prep_ragged(name)
     if name in LINCOMP_NAMES:
@@ -420,6 +457,12 @@ def time_leg(name: str, p: dict, steps: int, warmup: int) -> tuple[dict, dict]:
                     value=round(x["tflops"], 1), unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
                     unfused_ms=round(x["unfused_ms"], 4), fused_speedup=round(x["unfused_ms"] / x["fused_ms"], 3),
                     plan=x["plan"]), x
+    if name in LC_EPILOGUE_NAMES:
+        x = time_lc_epilogue(p, steps, warmup)
+        return dict(workload=name, ms=round(x["fused_ms"], 4), median_ms=round(x["median_ms"], 4),
+                    value=round(x["req_s"], 1), unit="requests/s", hbm_gbs=round(x["gbs"], 1),
+                    hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4), unfused_ms=round(x["unfused_ms"], 4),
+                    fused_speedup=round(x["unfused_ms"] / x["fused_ms"], 3)), x
     if name in STACKED_NAMES:
         x = time_stacked(p, steps, warmup)
         return dict(workload=name, ms=round(x["kernel_ms"], 4), median_ms=round(x["median_ms"], 4),

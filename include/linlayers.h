@@ -218,6 +218,16 @@ ll_status gemm_plan_destroy(gemm_plan* plan);
  */
 #define LL_LINCOMP_NO_DEDUP 0x1u
 
+/*
+ * epilogue: what happens to each fp32 sum Y[r][c][m][d] before it is
+ * converted to y_type, fused into the layer (page "Meta accélère un noyau GPU
+ * d'un facteur 4 avec TLX", section "Par où commencer dans votre équipe":
+ * fuse steps, then measure again).  The LL_EPI_* bits of gemm_desc:
+ * LL_EPI_BIAS adds bias[m] (fp32, one per compressed row, Mo values, passed
+ * to lincomp_run_ex / lincomp_ragged_run_ex), then the activation LL_EPI_RELU,
+ * LL_EPI_GELU (z * Phi(z), the exact form) or LL_EPI_SILU, in fp32.
+ * 0: Y = W^T . X as before.  Unknown bits -> LL_ERR_INVALID_ARG.
+ */
 typedef struct {
   int64_t R, C, Nu, Ni, D, Mo;
   int64_t su_r, su_c, su_n;
@@ -226,6 +236,7 @@ typedef struct {
   int64_t sy_r, sy_c, sy_m;
   int32_t y_type; /* ll_dtype */
   uint32_t flags;
+  uint32_t epilogue; /* LL_EPI_* ; 0 for the plain layer */
 } lincomp_desc;
 
 /* Bytes of device workspace lincomp_run needs for `desc` (may be 0).
@@ -244,6 +255,16 @@ ll_status lincomp_workspace_size(const lincomp_desc* desc, size_t* bytes);
 ll_status lincomp_run(const lincomp_desc* desc, const void* user, const void* item,
                       const void* W, void* Y, void* workspace, size_t ws_bytes,
                       void* stream);
+
+/*
+ * lincomp_run for a descriptor whose epilogue adds a bias: `bias` is a device
+ * array of Mo fp32 values, 16-byte aligned, bias[m] added to every Y[.][.][m][.].
+ * A descriptor without LL_EPI_BIAS ignores `bias`; lincomp_run on a descriptor
+ * with LL_EPI_BIAS, or a null or misaligned bias here, is LL_ERR_INVALID_ARG.
+ * Otherwise as lincomp_run.
+ */
+ll_status lincomp_run_ex(const lincomp_desc* desc, const void* user, const void* item, const void* W,
+                         const float* bias, void* Y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Linear compression over ragged requests (page "Meta accélère un noyau GPU
@@ -272,10 +293,15 @@ typedef struct {
   int64_t sy_c, sy_m;
   int32_t y_type; /* ll_dtype */
   uint32_t flags; /* LL_LINCOMP_NO_DEDUP or 0 */
+  uint32_t epilogue; /* LL_EPI_* as for lincomp_desc */
 } lincomp_ragged_desc;
 
 ll_status lincomp_ragged_run(const lincomp_ragged_desc* desc, const int64_t* offsets, const void* user,
                              const void* item, const void* W, void* Y, void* stream);
+
+/* lincomp_ragged_run with the bias of an LL_EPI_BIAS epilogue (as lincomp_run_ex). */
+ll_status lincomp_ragged_run_ex(const lincomp_ragged_desc* desc, const int64_t* offsets, const void* user,
+                                const void* item, const void* W, const float* bias, void* Y, void* stream);
 
 /* Static, human-readable name of a status code ("LL_OK", ...). */
 const char* ll_status_string(ll_status s);

@@ -178,3 +178,24 @@ def epilogue(C, S, bias, act, cols=None):
     lib.oracle_epilogue(ACTS[act], rows, N, _ptr(C), _ptr(S) if S is not None else None,
                         _ptr(b) if b is not None else None)
     return C, S
+
+
+def lincomp_epilogue(Y, S, bias, act):
+    """The fused epilogue of linear compression in fp64: act(Y[p][m][d] +
+    bias[m]) for every candidate p, with S[p][m][d] + |bias[m]| (page "Meta
+    accélère un noyau GPU d'un facteur 4 avec TLX", section "Par où commencer
+    dans votre équipe": fuse steps, then measure again).  The bias is one
+    value per compressed row m, so each candidate's [Mo][D] block is seen as
+    [D][Mo] (rows d, columns m) by the GEMM epilogue above, whose bias runs
+    along columns; the arithmetic is that function's.  Y, S: [P][Mo][D];
+    bias: fp32 [Mo] or None; S may be None."""
+    Y = np.asarray(Y, dtype=np.float64)
+    P, Mo, D = Y.shape
+    Yt = np.ascontiguousarray(Y.transpose(0, 2, 1)).reshape(P * D, Mo)
+    St = None if S is None else np.ascontiguousarray(np.asarray(S, dtype=np.float64).transpose(0, 2, 1)).reshape(
+        P * D, Mo)
+    Yo, So = epilogue(Yt, St, bias, act)
+    Yo = Yo.reshape(P, D, Mo).transpose(0, 2, 1)
+    So = None if So is None else So.reshape(P, D, Mo).transpose(0, 2, 1)
+    return np.ascontiguousarray(Yo), (None if So is None else np.ascontiguousarray(So))
+

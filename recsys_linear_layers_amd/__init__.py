@@ -52,7 +52,7 @@ class LincompDesc(ctypes.Structure):
                 ("si_r", _i64), ("si_c", _i64), ("si_n", _i64),
                 ("sw_n", _i64),
                 ("sy_r", _i64), ("sy_c", _i64), ("sy_m", _i64),
-                ("y_type", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("y_type", ctypes.c_int32), ("flags", ctypes.c_uint32), ("epilogue", ctypes.c_uint32)]
 
 
 class LincompRaggedDesc(ctypes.Structure):
@@ -61,7 +61,7 @@ class LincompRaggedDesc(ctypes.Structure):
                 ("si_c", _i64), ("si_n", _i64),
                 ("sw_n", _i64),
                 ("sy_c", _i64), ("sy_m", _i64),
-                ("y_type", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("y_type", ctypes.c_int32), ("flags", ctypes.c_uint32), ("epilogue", ctypes.c_uint32)]
 
 
 _lib.ll_status_string.restype = ctypes.c_char_p
@@ -78,8 +78,11 @@ _lib.gemm_plan_destroy.argtypes = [_vp]
 _lib.lincomp_workspace_size.argtypes = [ctypes.POINTER(LincompDesc), ctypes.POINTER(ctypes.c_size_t)]
 _lib.lincomp_run.argtypes = [ctypes.POINTER(LincompDesc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.lincomp_ragged_run.argtypes = [ctypes.POINTER(LincompRaggedDesc), _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.lincomp_run_ex.argtypes = [ctypes.POINTER(LincompDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.lincomp_ragged_run_ex.argtypes = [ctypes.POINTER(LincompRaggedDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 for _f in ("gemm_plan_create", "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_run", "gemm_run_ex",
-           "gemm_run_noalloc", "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "lincomp_ragged_run"):
+           "gemm_run_noalloc", "gemm_plan_destroy", "lincomp_workspace_size", "lincomp_run", "lincomp_ragged_run",
+           "lincomp_run_ex", "lincomp_ragged_run_ex"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -158,6 +161,18 @@ def lincomp_ragged_run(desc: LincompRaggedDesc, offsets: int, user: int, item: i
 def lincomp_run(desc: LincompDesc, user: int, item: int, W: int, Y: int, workspace: int, ws_bytes: int,
                 stream: int) -> None:
     _check(_lib.lincomp_run(ctypes.byref(desc), user, item, W, Y, workspace, ws_bytes, stream), "lincomp_run")
+
+
+def lincomp_run_ex(desc: LincompDesc, user: int, item: int, W: int, bias: int | None, Y: int, workspace: int,
+                   ws_bytes: int, stream: int) -> None:
+    _check(_lib.lincomp_run_ex(ctypes.byref(desc), user, item, W, bias, Y, workspace, ws_bytes, stream),
+           "lincomp_run_ex")
+
+
+def lincomp_ragged_run_ex(desc: LincompRaggedDesc, offsets: int, user: int, item: int, W: int, bias: int | None,
+                          Y: int, stream: int = 0) -> None:
+    _check(_lib.lincomp_ragged_run_ex(ctypes.byref(desc), offsets, user, item, W, bias, Y, stream),
+           "lincomp_ragged_run_ex")
 
 
 # ---------------------------------------------------------------------------
@@ -265,7 +280,17 @@ def gemm(A, B, out=None, out_dtype=None, flags: int = 0, bias=None, act=None):
     return out
 
 
-def lincomp_desc_for(user, item, W, Y, flags: int = 0) -> LincompDesc:
+def _lc_epilogue(bias, act, Mo) -> int:
+    torch = _torch()
+    epilogue = ACTIVATIONS[act]
+    if bias is not None:
+        if bias.dtype != torch.float32 or tuple(bias.shape) != (Mo,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 tensor of Mo values")
+        epilogue |= LL_EPI_BIAS
+    return epilogue
+
+
+def lincomp_desc_for(user, item, W, Y, flags: int = 0, epilogue: int = 0) -> LincompDesc:
     """user is [R][Nu][D] (one block per request) or [R][C][Nu][D] (rows per
     candidate, e.g. the first Nu rows of a materialised input)."""
     R2, C, Ni, D2 = item.shape
@@ -285,23 +310,25 @@ def lincomp_desc_for(user, item, W, Y, flags: int = 0) -> LincompDesc:
             raise ValueError("last dimension must be contiguous")
     si, sw, sy = item.stride(), W.stride(), Y.stride()
     return LincompDesc(R, C, Nu, Ni, D, Mo, su_r, su_c, su_n, si[0], si[1], si[2], sw[0],
-                       sy[0], sy[1], sy[2], _dtype_code(Y.dtype), flags)
+                       sy[0], sy[1], sy[2], _dtype_code(Y.dtype), flags, epilogue)
 
 
 _lc_ws: dict = {}
 
 
-def lincomp(user, item, W, out=None, out_dtype=None, flags: int = 0):
-    """Y[r, c] = W^T . [user[r]; item[r, c]] for bf16 tensors user [R][Nu][D]
-    (or [R][C][Nu][D], rows per candidate), item [R][C][Ni][D], W [Nu+Ni][Mo];
-    returns Y [R][C][Mo][D]."""
+def lincomp(user, item, W, out=None, out_dtype=None, flags: int = 0, bias=None, act=None):
+    """Y[r, c] = act(W^T . [user[r]; item[r, c]] + bias) for bf16 tensors user
+    [R][Nu][D] (or [R][C][Nu][D], rows per candidate), item [R][C][Ni][D], W
+    [Nu+Ni][Mo]; returns Y [R][C][Mo][D].  bias: optional fp32 [Mo], one per
+    compressed row; act: None, "relu", "gelu" (exact) or "silu", applied to
+    the fp32 sums before they are rounded."""
     torch = _torch()
     R, D = user.shape[0], user.shape[-1]
     C = item.shape[1]
     Mo = W.shape[1]
     if out is None:
         out = torch.empty((R, C, Mo, D), dtype=out_dtype or torch.bfloat16, device=user.device)
-    desc = lincomp_desc_for(user, item, W, out, flags)
+    desc = lincomp_desc_for(user, item, W, out, flags, _lc_epilogue(bias, act, Mo))
     need = lincomp_workspace_size(desc)
     key = user.device.index
     ws = _lc_ws.get(key)
@@ -309,20 +336,20 @@ def lincomp(user, item, W, out=None, out_dtype=None, flags: int = 0):
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=user.device)
         _lc_ws[key] = ws
     stream = torch.cuda.current_stream(user.device).cuda_stream
-    lincomp_run(desc, user.data_ptr(), item.data_ptr(), W.data_ptr(), out.data_ptr(), ws.data_ptr(),
-                ws.numel(), stream)
+    lincomp_run_ex(desc, user.data_ptr(), item.data_ptr(), W.data_ptr(),
+                   bias.data_ptr() if bias is not None else None, out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
     return out
 
 
 
-def lincomp_stacked(X, W, Nu: int, out=None, out_dtype=None):
+def lincomp_stacked(X, W, Nu: int, out=None, out_dtype=None, bias=None, act=None):
     """The layer's original form: X [R][C][Nu+Ni][D] holds every candidate's
-    stacked input [user rows; item rows] in full.  Y[r, c] = W^T . X[r, c];
-    each candidate computes its user rows' contribution itself."""
-    return lincomp(X[:, :, :Nu], X[:, :, Nu:], W, out=out, out_dtype=out_dtype)
+    stacked input [user rows; item rows] in full.  Y[r, c] = act(W^T . X[r, c]
+    + bias); each candidate computes its user rows' contribution itself."""
+    return lincomp(X[:, :, :Nu], X[:, :, Nu:], W, out=out, out_dtype=out_dtype, bias=bias, act=act)
 
 
-def lincomp_ragged(user, item, W, offsets, out=None, out_dtype=None, flags: int = 0):
+def lincomp_ragged(user, item, W, offsets, out=None, out_dtype=None, flags: int = 0, bias=None, act=None):
     """Ragged requests: user [R][Nu][D], item [Ctot][Ni][D], W [Nu+Ni][Mo] (bf16),
     offsets int64 [R+1] on the device (request r owns candidates
     offsets[r] .. offsets[r+1]-1); returns Y [Ctot][Mo][D]."""
@@ -343,8 +370,8 @@ def lincomp_ragged(user, item, W, offsets, out=None, out_dtype=None, flags: int 
         raise ValueError("offsets must be contiguous")
     su, si, sw, sy = user.stride(), item.stride(), W.stride(), out.stride()
     desc = LincompRaggedDesc(R, Ctot, Nu, Ni, D, Mo, su[0], su[1], si[0], si[1], sw[0], sy[0], sy[1],
-                             _dtype_code(out.dtype), flags)
+                             _dtype_code(out.dtype), flags, _lc_epilogue(bias, act, Mo))
     stream = torch.cuda.current_stream(user.device).cuda_stream
-    lincomp_ragged_run(desc, offsets.data_ptr(), user.data_ptr(), item.data_ptr(), W.data_ptr(),
-                       out.data_ptr(), stream)
+    lincomp_ragged_run_ex(desc, offsets.data_ptr(), user.data_ptr(), item.data_ptr(), W.data_ptr(),
+                          bias.data_ptr() if bias is not None else None, out.data_ptr(), stream)
     return out

@@ -48,8 +48,8 @@ OUT = os.path.join(HERE, "gemm_sq4_loop.inc")
 FBASE = 192         # first fragment VGPR
 READ_SPAN = 10      # MFMAs of steps 0..2 over which the next step's 12 reads are spread
 BAR_AFTER = 0       # MFMAs of step 3 issued before the load wait and barrier
-L3 = 8              # loads of slice j+2 issued in step 3 of slice j; the rest go to steps 0..2 of slice j+1
-CARRY_STEPS = 3     # how many of steps 0..2 of slice j+1 share the rest
+L3 = 6              # loads of slice j+2 issued in step 3 of slice j; the rest go to steps 0..2 of slice j+1
+CARRY_STEPS = 2     # how many of steps 0..2 of slice j+1 share the rest
 CARRY_SPAN = 14     # MFMAs over which a step's reads and carried loads are spread
 SLOT = 65536
 B_OFF = 32768

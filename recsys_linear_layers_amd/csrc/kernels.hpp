@@ -70,7 +70,9 @@ struct LincompKind {
   const char* name;
 };
 const LincompKind& lincomp_kind();
-hipError_t launch_lincomp(const LincompKArgs& args, int grid, hipStream_t stream);
+// act: activation of the fused epilogue (0 none, 1 ReLU, 2 GELU, 3 SiLU); the
+// bias, if any, is args.bias.
+hipError_t launch_lincomp(const LincompKArgs& args, int act, int grid, hipStream_t stream);
 
 // Auxiliary kernels.
 hipError_t launch_pack_kmajor(const uint16_t* src, int64_t s_r, int64_t s_k, int64_t rows, int64_t K,

@@ -35,7 +35,30 @@ const LincompKind& lincomp_kind() {
   return kinds[i >= 0 && i < n ? i : 0];
 }
 
-hipError_t launch_lincomp(const LincompKArgs& a, int grid, hipStream_t s) {
+hipError_t launch_lincomp(const LincompKArgs& a, int act, int grid, hipStream_t s) {
+  // A fused epilogue runs in the default configuration (one instantiation per
+  // activation, with and without a bias); the sweep configurations are plain.
+  if (act != 0 || a.bias || cfg_index() == 0) {
+    const int v = act * 2 + (a.bias ? 1 : 0);
+    switch (v) {
+#define LL_LC_EPI(n, b)                                                                       \
+  case n * 2 + b: {                                                                           \
+    using C = LincompCfg<64, 256, 64, 4, 4, 3, n, b>;                                         \
+    hipLaunchKernelGGL(lincomp_fused<C>, dim3(grid), dim3(C::THREADS), 0, s, a);              \
+    return hipGetLastError();                                                                 \
+  }
+      LL_LC_EPI(0, 0)
+      LL_LC_EPI(0, 1)
+      LL_LC_EPI(1, 0)
+      LL_LC_EPI(1, 1)
+      LL_LC_EPI(2, 0)
+      LL_LC_EPI(2, 1)
+      LL_LC_EPI(3, 0)
+      LL_LC_EPI(3, 1)
+#undef LL_LC_EPI
+      default: return hipErrorInvalidValue;
+    }
+  }
   int i = 0;
 #define LL_LC_LAUNCH(bm, bn, kt, nc, np, st)                                                        \
   if (cfg_index() == i++) {                                                                        \

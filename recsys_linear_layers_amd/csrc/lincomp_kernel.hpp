@@ -38,7 +38,7 @@ struct LincompKArgs {
   const uint16_t* item;
   const uint16_t* W;
   void* Y;
-  int64_t su_r, su_c, su_n, si_r, si_c, si_n, sw_n, sy_r, sy_c, sy_m;
+  int32_t su_r, su_c, su_n, si_r, si_c, si_n, sw_n, sy_r, sy_c, sy_m;  // element strides (< 2^31)
   int64_t user_extent, item_extent, w_extent;  // elements addressable from each base pointer
   int32_t R, C, Nu, Ni, D, Mo;
   int32_t tiles_m, tiles_n, chunk, nchunks;    // candidates per work item, work items per request
@@ -51,10 +51,17 @@ struct LincompKArgs {
   // into nranges equal contiguous ranges, one per work item (per output tile).
   const int64_t* offsets;
   int32_t nranges;
+  // Fused epilogue: bias[m] (Mo fp32 values, 16-byte aligned) added to every
+  // sum of compressed row m before the activation (LincompCfg::ACT); null: none.
+  const float* bias;
 };
 
-template <int BM_, int BN_, int KT_, int WN_, int NPROD_, int STAGES_>
+template <int BM_, int BN_, int KT_, int WN_, int NPROD_, int STAGES_, int ACT_ = 0, bool BIAS_ = false>
 struct LincompCfg {
+  // activation on every sum (plus its row's bias, BIAS) before it is stored:
+  // 0 none, 1 ReLU, 2 GELU (erf form), 3 SiLU
+  static constexpr int ACT = ACT_;
+  static constexpr bool BIAS = BIAS_;
   static constexpr int BM = BM_, BN = BN_, KT = KT_, KS = KT / 16;
   static constexpr int WM = 1, WN = WN_;
   static constexpr int NCONS = WN, NPROD = NPROD_, STAGES = STAGES_;
@@ -208,65 +215,111 @@ __device__ __forceinline__ void lc_issue(const LincompKArgs& p, const LcPos& s, 
                                                                        lane, vb);
 }
 
-// Store the wave's FM x FN blocks of Y for candidate (r, c).  Accumulator
-// layout of v_mfma_f32_32x32x16: register q of lane l holds row
-// 8*(q/4) + 4*(l/32) + q%4, column l%32 of the 32x32 block.
+// Bias of the four compressed rows m .. m+3 (m a multiple of 4; Mo is a
+// multiple of 8, so the four are all in range or all out), one 16-byte load;
+// zeros without a bias.
+template <bool BIAS>
+__device__ __forceinline__ f32x4 lc_bias4(const LincompKArgs& p, int m) {
+  f32x4 b = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (BIAS) {
+    if (m < p.Mo) b = *(const f32x4*)(p.bias + m);
+  }
+  return b;
+}
+
+// One group of a bf16 Y block: values v0..v3 of rows q%4 = 0..3 at this
+// lane's column.  Lane pair (2i, 2i+1) holds columns d, d+1 of the same rows:
+// the even lane sends rows 2, 3 and receives the odd lane's rows 0, 1
+// (column d+1), the odd lane sends rows 0, 1 and receives rows 2, 3 (column
+// d), and each lane stores the (d, d+1) pairs of its two rows.  Y + off is
+// this lane's first row of the group (row ra) at column d; sym is the row
+// stride.
+__device__ __forceinline__ void lc_store_group(const LincompKArgs& p, uint16_t* Y, int off, int sym, int ra, int dd,
+                                               bool odd, float v0, float v1, float v2, float v3) {
+  const float s0 = swap_pair(odd ? v0 : v2);
+  const float s1 = swap_pair(odd ? v1 : v3);
+  float a0, a1, b0, b1;  // row ra: (a0 at d, a1 at d+1); row ra+1: (b0, b1)
+  if (!odd) {
+    a0 = v0; a1 = s0;
+    b0 = v1; b1 = s1;
+  } else {
+    a0 = s0; a1 = v2;
+    b0 = s1; b1 = v3;
+  }
+  const uint32_t pa = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
+  const uint32_t pb = (uint32_t)f32_to_bf16_bits(b0) | ((uint32_t)f32_to_bf16_bits(b1) << 16);
+  if (dd < p.D) {  // D is a multiple of 8, so dd < D implies dd + 1 < D
+    if (ra < p.Mo) *(uint32_t*)(Y + off) = pa;
+    if (ra + 1 < p.Mo) *(uint32_t*)(Y + off + sym) = pb;
+  }
+}
+
+// Stores the wave's FM x FN blocks of Y for candidate (r, c).  Accumulator
+// layout of v_mfma_f32_32x32x16: register q of lane l holds row 8*(q/4) +
+// 4*(l/32) + q%4, column l%32 of the 32x32 block.  The block is addressed
+// from a wave-uniform base with one 32-bit element offset per lane (the host
+// keeps Mo * sy_m below 2^30) and row steps that are wave-uniform multiples
+// of sy_m.
+//  * Plain layer: block after block, each group by group (storing the two
+//    column blocks of a row group back to back was 9% slower on the 256 x 128
+//    workload).
+//  * Fused epilogue (each value's row bias, then the activation, four values
+//    at a time just before they are rounded): group by group across the
+//    column blocks, so that one 16-byte bias load serves the four rows of a
+//    group for every block and the activation's temporaries stay few.
 template <class Cfg>
-__device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& s,
-                                            const f32x16 (&acc)[Cfg::FM][Cfg::FN], int wn0, int lane) {
+__device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& s, f32x16 (&acc)[Cfg::FM][Cfg::FN],
+                                            int wn0, int lane) {
+  constexpr bool any_epi = Cfg::ACT != 0 || Cfg::BIAS;
   const int64_t yoff = (int64_t)s.r * p.sy_r + (int64_t)s.c * p.sy_c;
+  const int sym = (int)p.sy_m;
   const int mb = s.m0 * Cfg::BM + 4 * (lane >> 5);
   const int db = s.n0 * Cfg::BN + wn0 + (lane & 31);
   if (p.y_bf16) {
-    // Lane pair (2i, 2i+1) holds columns d, d+1 of the same rows.  After the
-    // swap the even lane owns rows q%4 in {0,1} and the odd lane rows {2,3},
-    // each as a (d, d+1) pair.
     uint16_t* Y = (uint16_t*)p.Y + yoff;
     const bool odd = lane & 1;
     const int d = db - (lane & 1);
+    const int r0 = mb + (odd ? 2 : 0);  // this lane's first row
+    const int loff = r0 * sym + d;
+    if constexpr (!any_epi) {
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
+      for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j)
+        for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            lc_store_group(p, Y, loff + (32 * i + 8 * g) * sym + 32 * j, sym, r0 + 32 * i + 8 * g, d + 32 * j, odd,
+                           acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          // even lane sends rows 2,3, odd lane sends rows 0,1
-          // The even lane sends rows 2, 3 and receives the odd lane's rows 0, 1
-          // (column d+1); the odd lane sends rows 0, 1 and receives rows 2, 3
-          // (column d).
-          const float s0 = swap_pair(odd ? v0 : v2);
-          const float s1 = swap_pair(odd ? v1 : v3);
-          float a0, a1, b0, b1;  // row ra: (a0 at d, a1 at d+1); row ra+1: (b0, b1)
-          if (!odd) {
-            a0 = v0; a1 = s0;
-            b0 = v1; b1 = s1;
-          } else {
-            a0 = s0; a1 = v2;
-            b0 = s1; b1 = v3;
-          }
-          const int ra = mb + 32 * i + 8 * g + (odd ? 2 : 0);
-          const int dd = d + 32 * j;
-          const uint32_t pa = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
-          const uint32_t pb = (uint32_t)f32_to_bf16_bits(b0) | ((uint32_t)f32_to_bf16_bits(b1) << 16);
-          if (dd < p.D) {  // D is a multiple of 8, so dd < D implies dd + 1 < D
-            if (ra < p.Mo) *(uint32_t*)(Y + (int64_t)ra * p.sy_m + dd) = pa;
-            if (ra + 1 < p.Mo) *(uint32_t*)(Y + (int64_t)(ra + 1) * p.sy_m + dd) = pb;
-          }
+          const f32x4 b = lc_bias4<Cfg::BIAS>(p, mb + 32 * i + 8 * g);
+#pragma unroll
+          for (int j = 0; j < Cfg::FN; ++j)
+            lc_store_group(p, Y, loff + (32 * i + 8 * g) * sym + 32 * j, sym, r0 + 32 * i + 8 * g, d + 32 * j, odd,
+                           epi<Cfg::ACT>(acc[i][j][4 * g], b[0]), epi<Cfg::ACT>(acc[i][j][4 * g + 1], b[1]),
+                           epi<Cfg::ACT>(acc[i][j][4 * g + 2], b[2]), epi<Cfg::ACT>(acc[i][j][4 * g + 3], b[3]));
         }
+    }
   } else {
     float* Y = (float*)p.Y + yoff;
+    const int loff = mb * sym + db;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j)
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 b = lc_bias4<Cfg::BIAS>(p, mb + 32 * i + 8 * g);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m = mb + 32 * i + 8 * (q >> 2) + (q & 3);
-          const int d = db + 32 * j;
-          if (m < p.Mo && d < p.D) Y[(int64_t)m * p.sy_m + d] = acc[i][j][q];
-        }
+        for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = mb + 32 * i + 8 * g + r;
+            const float v = any_epi ? epi<Cfg::ACT>(acc[i][j][4 * g + r], b[r]) : acc[i][j][4 * g + r];
+            if (m < p.Mo && db + 32 * j < p.D) Y[loff + (32 * i + 8 * g + r) * sym + 32 * j] = v;
+          }
+      }
   }
 }
 
@@ -306,9 +359,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const uint32_t va = TileGeom<Cfg::BM, Cfg::KT, false>::lane_off(lw, lane, (int)p.sw_n);
     const uint32_t vbu = TileGeom<Cfg::BN, Cfg::KT, false>::lane_off(lw, lane, (int)p.su_n);
     const uint32_t vbi = TileGeom<Cfg::BN, Cfg::KT, false>::lane_off(lw, lane, (int)p.si_n);
-    LcPos ld, cc;
+    LcPos ld;
     ld.start(p, first);
-    cc.start(p, first);
     int issued = 0;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -322,7 +374,8 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     lds_barrier();
     int j = 0, slot = 0;
     while (true) {
-      const bool has_next = !cc.item_end(p) || cc.t + stride < p.total;
+      // slice j+1 exists if it was issued already or more slices are left
+      const bool has_next = j + 1 < issued || ld.valid(p);
       if (has_next) lc_wait<Cfg>(issued - j - 2);
       lds_barrier();
       if (ld.valid(p)) {
@@ -331,7 +384,6 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         ++issued;
       }
       if (!has_next) break;
-      cc.advance(p, stride);
       ++j;
       slot = slot + 1 == S ? 0 : slot + 1;
     }
@@ -343,9 +395,12 @@ __global__ void __launch_bounds__(Cfg::THREADS)
   f32x16 acc[Cfg::FM][Cfg::FN], u[Cfg::FM][Cfg::FN];
   zero_acc(acc);
   zero_acc(u);
-  Frags<Cfg> f[2];
+  // One fragment buffer: the next k16 step's reads follow this step's MFMAs
+  // (the computing waves are far from busy in this HBM-bound layer, and the
+  // 32 VGPRs of a second buffer pushed the kernel into spilling).
+  Frags<Cfg> f;
   lds_barrier();
-  load_frags<Cfg>(smem, 0, 0, wn0, lane, f[0]);
+  load_frags<Cfg>(smem, 0, 0, wn0, lane, f);
   LcPos cc;
   cc.start(p, first);
   int slot = 0;
@@ -356,13 +411,13 @@ __global__ void __launch_bounds__(Cfg::THREADS)
     const int nslot = slot + 1 == S ? 0 : slot + 1;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
+      mfma_step<Cfg>(f, acc);
       if (kk + 1 < KS) {
-        load_frags<Cfg>(cur, kk + 1, 0, wn0, lane, f[(kk + 1) & 1]);
+        load_frags<Cfg>(cur, kk + 1, 0, wn0, lane, f);
       } else {
         lds_barrier();
-        if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, 0, wn0, lane, f[0]);
+        if (has_next) load_frags<Cfg>(smem + nslot * Cfg::SLOT, 0, 0, wn0, lane, f);
       }
-      mfma_step<Cfg>(f[kk & 1], acc);
     }
     if (p.dedup && cc.user_end(p)) {
 #pragma unroll

@@ -589,6 +589,8 @@ static ll_status lincomp_check(const lincomp_desc* d, bool ragged = false) {
   if (d->R < 0 || d->C < 0 || d->Nu < 0 || d->Ni < 0 || d->D < 0 || d->Mo < 0)
     return fail(LL_ERR_INVALID_ARG, "negative size");
   if (d->flags & ~(uint32_t)LL_LINCOMP_NO_DEDUP) return fail(LL_ERR_INVALID_ARG, "unknown flag bits");
+  if ((d->epilogue & ~(LL_EPI_BIAS | LL_EPI_ACT_MASK)) || (d->epilogue & LL_EPI_ACT_MASK) > LL_EPI_SILU)
+    return fail(LL_ERR_INVALID_ARG, "unknown epilogue 0x%x", d->epilogue);
   if (d->y_type != LL_BF16 && d->y_type != LL_F32) return fail(LL_ERR_UNSUPPORTED, "Y must be LL_BF16 or LL_F32");
   if (d->D % 8 || d->Mo % 8) return fail(LL_ERR_INVALID_ARG, "D and Mo must be multiples of 8");
   if (d->su_n % 8 || d->si_n % 8 || d->sw_n % 8 || d->su_r % 8 || d->su_c % 8 || d->si_r % 8 || d->si_c % 8 ||
@@ -604,6 +606,11 @@ static ll_status lincomp_check(const lincomp_desc* d, bool ragged = false) {
                                            : "Mo, D and R*C must be below 2^30");
   if (d->su_n * 2 * kBK >= (1ll << 31) || d->si_n * 2 * kBK >= (1ll << 31) || d->sw_n * 2 * kBK >= (1ll << 31))
     return fail(LL_ERR_UNSUPPORTED, "row strides too large");
+  // the kernel keeps every stride in 32 bits
+  for (int64_t st : {d->su_r, d->su_c, d->su_n, d->si_r, d->si_c, d->si_n, d->sw_n, d->sy_r, d->sy_c, d->sy_m})
+    if (st >= (1ll << 31)) return fail(LL_ERR_UNSUPPORTED, "strides must be below 2^31 elements");
+  // one candidate's Y block is addressed with 32-bit element offsets
+  if ((d->Mo + 1) * d->sy_m >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "Mo * sy_m too large");
   return LL_OK;
 }
 
@@ -619,9 +626,15 @@ ll_status lincomp_workspace_size(const lincomp_desc* d, size_t* bytes) {
 // ragged (d->C is the total candidate count; d's request strides of item and
 // Y and the per-candidate user stride are 0).
 static ll_status lincomp_launch(const lincomp_desc* d, const int64_t* offsets, const void* user, const void* item,
-                                const void* W, void* Y, void* stream) {
+                                const void* W, const float* bias, void* Y, void* stream) {
   ll_status s = lincomp_check(d, offsets != nullptr);
   if (s != LL_OK) return s;
+  if (d->epilogue & LL_EPI_BIAS) {
+    if (!bias) return fail(LL_ERR_INVALID_ARG, "the epilogue adds a bias: bias is null");
+    if ((uintptr_t)bias & 15) return fail(LL_ERR_INVALID_ARG, "bias must be 16-byte aligned");
+  } else {
+    bias = nullptr;
+  }
   if (d->R == 0 || d->C == 0 || d->Mo == 0 || d->D == 0) return ok();
   if (!Y || !W || (d->Nu > 0 && !user) || (d->Ni > 0 && !item)) return fail(LL_ERR_INVALID_ARG, "null pointer");
   if (((uintptr_t)user & 15) || ((uintptr_t)item & 15) || ((uintptr_t)W & 15) || ((uintptr_t)Y & 15))
@@ -649,16 +662,16 @@ static ll_status lincomp_launch(const lincomp_desc* d, const int64_t* offsets, c
   k.item = (const uint16_t*)item;
   k.W = (const uint16_t*)W;
   k.Y = Y;
-  k.su_r = d->su_r;
-  k.su_c = d->su_c;
-  k.su_n = d->su_n;
-  k.si_r = d->si_r;
-  k.si_c = d->si_c;
-  k.si_n = d->si_n;
-  k.sw_n = d->sw_n;
-  k.sy_r = d->sy_r;
-  k.sy_c = d->sy_c;
-  k.sy_m = d->sy_m;
+  k.su_r = (int32_t)d->su_r;
+  k.su_c = (int32_t)d->su_c;
+  k.su_n = (int32_t)d->su_n;
+  k.si_r = (int32_t)d->si_r;
+  k.si_c = (int32_t)d->si_c;
+  k.si_n = (int32_t)d->si_n;
+  k.sw_n = (int32_t)d->sw_n;
+  k.sy_r = (int32_t)d->sy_r;
+  k.sy_c = (int32_t)d->sy_c;
+  k.sy_m = (int32_t)d->sy_m;
   k.user_extent = d->Nu > 0 ? (d->R - 1) * d->su_r + (d->C - 1) * d->su_c + (d->Nu - 1) * d->su_n + d->D : 0;
   k.item_extent = d->Ni > 0 ? (d->R - 1) * d->si_r + (d->C - 1) * d->si_c + (d->Ni - 1) * d->si_n + d->D : 0;
   k.w_extent = (d->Nu + d->Ni - 1) * d->sw_n + d->Mo;
@@ -701,21 +714,36 @@ static ll_status lincomp_launch(const lincomp_desc* d, const int64_t* offsets, c
   k.y_bf16 = d->y_type == LL_BF16;
   // Per-candidate user rows (su_c != 0) leave nothing to share.
   k.dedup = !(d->flags & LL_LINCOMP_NO_DEDUP) && d->su_c == 0;
+  k.bias = bias;
   const int grid = (int)std::min<int64_t>(total, info->cus);
-  hipError_t e = launch_lincomp(k, grid, (hipStream_t)stream);
+  hipError_t e = launch_lincomp(k, (int)((d->epilogue & LL_EPI_ACT_MASK) >> 4), grid, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "lincomp launch");
   return ok();
 }
 
 ll_status lincomp_run(const lincomp_desc* d, const void* user, const void* item, const void* W, void* Y,
                       void* ws, size_t ws_bytes, void* stream) {
+  if (d && (d->epilogue & LL_EPI_BIAS))
+    return fail(LL_ERR_INVALID_ARG, "the epilogue adds a bias: use lincomp_run_ex");
+  return lincomp_run_ex(d, user, item, W, nullptr, Y, ws, ws_bytes, stream);
+}
+
+ll_status lincomp_run_ex(const lincomp_desc* d, const void* user, const void* item, const void* W,
+                         const float* bias, void* Y, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
-  return lincomp_launch(d, nullptr, user, item, W, Y, stream);
+  return lincomp_launch(d, nullptr, user, item, W, bias, Y, stream);
 }
 
 ll_status lincomp_ragged_run(const lincomp_ragged_desc* g, const int64_t* offsets, const void* user,
                              const void* item, const void* W, void* Y, void* stream) {
+  if (g && (g->epilogue & LL_EPI_BIAS))
+    return fail(LL_ERR_INVALID_ARG, "the epilogue adds a bias: use lincomp_ragged_run_ex");
+  return lincomp_ragged_run_ex(g, offsets, user, item, W, nullptr, Y, stream);
+}
+
+ll_status lincomp_ragged_run_ex(const lincomp_ragged_desc* g, const int64_t* offsets, const void* user,
+                                const void* item, const void* W, const float* bias, void* Y, void* stream) {
   if (!g) return fail(LL_ERR_INVALID_ARG, "null desc");
   lincomp_desc d;
   memset(&d, 0, sizeof d);
@@ -734,11 +762,12 @@ ll_status lincomp_ragged_run(const lincomp_ragged_desc* g, const int64_t* offset
   d.sy_m = g->sy_m;
   d.y_type = g->y_type;
   d.flags = g->flags;
+  d.epilogue = g->epilogue;
   if (!offsets && g->R > 0 && g->Ctot > 0) {
     ll_status s = lincomp_check(&d, true);
     return s != LL_OK ? s : fail(LL_ERR_INVALID_ARG, "null offsets");
   }
-  return lincomp_launch(&d, offsets ? offsets : (const int64_t*)nullptr, user, item, W, Y, stream);
+  return lincomp_launch(&d, offsets ? offsets : (const int64_t*)nullptr, user, item, W, bias, Y, stream);
 }
 
 }  // extern "C"

@@ -429,3 +429,30 @@ def test_activation_bound_is_what_the_slope_allows():
     far, _ = oracle.epilogue((z + 3 * e).reshape(1, -1), None, None, "gelu")
     assert acceptance.check(near[0], ref[0], S, "f32", "gelu")[0]
     assert not acceptance.check(far[0], ref[0], S, "f32", "gelu")[0]
+
+
+def test_lincomp_epilogue_bias_runs_along_compressed_rows():
+    """W = [E; 0] selects user rows exactly (integer inputs), so
+    act(Y + bias) has a closed form per (m, d): relu(user[r][sel(m)][d] + b[m]).
+    A bias applied along d instead of m, or not at all, fails it."""
+    R, C, Nu, Ni, D, Mo = 2, 3, 8, 4, 24, 8
+    c = synth.lincomp_case(R, C, Nu, Ni, D, Mo, x_dist=("int", -3, 3), seed=91, name="epi_sel")
+    sel = np.array([5, 0, 7, 2, 2, 6, 1, 3])
+    W = np.zeros((Nu + Ni, Mo), dtype=np.float32)
+    W[sel, np.arange(Mo)] = 1.0
+    c.W = synth.f32_to_bf16_rne(W.reshape(-1))
+    bias = (np.arange(Mo, dtype=np.float32) - 3.5) * 2.0
+    pairs = [(r, k) for r in range(R) for k in range(C)]
+    Y, S = oracle.lincomp_case(c, pairs)
+    got, Sb = oracle.lincomp_epilogue(Y, S, bias, "relu")
+    user = synth.bf16_to_f32(c.user).astype(np.float64).reshape(R, Nu, D)
+    want = np.stack([np.maximum(user[r][sel] + bias[:, None], 0.0) for r, _ in pairs])
+    assert np.array_equal(got, want)
+    assert np.array_equal(Sb, S + np.abs(bias)[None, :, None])
+    wrong = np.stack([np.maximum(user[r][sel] + np.resize(bias, D)[None, :], 0.0) for r, _ in pairs])
+    assert not np.array_equal(got, wrong)
+    none, _ = oracle.lincomp_epilogue(Y, S, None, "relu")
+    assert not np.array_equal(got, none)
+    # no activation and no bias is the identity
+    ident, Si = oracle.lincomp_epilogue(Y, S, None, None)
+    assert np.array_equal(ident, Y) and np.array_equal(Si, S)
