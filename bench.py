@@ -6,10 +6,12 @@ linear-compression requests/s (fraction of HBM bandwidth) on one MI355X.
 One step is one call of the library on the headline workload (default: the
 4096^3 GEMM with bf16 output).  Inputs are seeded synthetic bf16 (the
 ``synth`` module), resident in HBM before timing starts.  Every workload gets
-W untimed warm-up calls, then K timed calls between two device
-synchronisations, each call bracketed by its own pair of HIP events on the
-stream the library launches on; the mean and the median of those per-call
-durations are reported, and the mean is what throughput is computed from.
+W untimed warm-up calls, then K timed calls back to back between two device
+synchronisations, with one pair of HIP events on the stream the library
+launches on around the K calls: their mean is what throughput is computed
+from.  A second pass of K calls, each bracketed by its own pair of events,
+gives the median (per-call events put packets of their own between the
+kernels, so that pass is not the one the mean comes from).
 The other configurations (FFN shapes, linear compression and its variants,
 edge and skinny shapes) run first and the headline last, so that the headline
 is timed at the clocks the chip holds under sustained work rather than at
@@ -91,25 +93,37 @@ def _log(msg: str) -> None:
 
 
 def _time_launches(fn, steps: int, warmup: int, stream):
-    """W untimed calls, then K timed calls between two device synchronisations,
-    each bracketed by a pair of HIP events recorded on `stream` (the stream the
-    library launches on).  Returns dict(wall_ms: host time per call across the
-    timed region, ms: mean event-measured duration per call, median_ms)."""
+    """W untimed calls, then the timed region: K calls back to back between two
+    device synchronisations, with one pair of HIP events recorded on `stream`
+    (the stream the library launches on) around them and nothing else in the
+    stream between the calls.  Then, in a second pass of K calls, a pair of
+    events around each call gives the spread (median); those per-call events
+    add their own packets between the kernels, so the mean comes from the
+    first pass.  Returns dict(ms: mean per call over the timed region,
+    wall_ms: host time per call across the timed region, median_ms and
+    per_call_mean_ms: from the per-call pass)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    mean = e0.elapsed_time(e1) / steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
     per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    return dict(wall_ms=wall, ms=statistics.fmean(per), median_ms=statistics.median(per))
+    return dict(wall_ms=wall, ms=mean, median_ms=statistics.median(per), per_call_mean_ms=statistics.fmean(per))
 
 
 _CASES: dict = {}
@@ -165,7 +179,7 @@ def time_gemm(p: dict, steps: int, warmup: int, kind: str | None = None) -> dict
     stream = torch.cuda.current_stream()
     t = _time_launches(lambda: plan.run(A, B, C, stream.cuda_stream), steps, warmup, stream)
     return dict(case=case, wall_ms=t["wall_ms"], kernel_ms=t["ms"], median_ms=t["median_ms"],
-                tflops=case.flops / (t["ms"] * 1e-3) / 1e12, plan=plan.describe())
+                per_call_mean_ms=t["per_call_mean_ms"], tflops=case.flops / (t["ms"] * 1e-3) / 1e12, plan=plan.describe())
 
 
 def prep_lincomp(name: str) -> dict:
@@ -186,7 +200,8 @@ def time_lincomp(p: dict, steps: int, warmup: int) -> dict:
     stream = torch.cuda.current_stream()
     t = _time_launches(lambda: ll.lincomp(user, item, W, out=Y), steps, warmup, stream)
     ev = t["ms"]
-    return dict(case=c, wall_ms=t["wall_ms"], kernel_ms=ev, median_ms=t["median_ms"], req_s=c.R / (ev * 1e-3),
+    return dict(case=c, wall_ms=t["wall_ms"], kernel_ms=ev, median_ms=t["median_ms"],
+                per_call_mean_ms=t["per_call_mean_ms"], req_s=c.R / (ev * 1e-3),
                 gbs=c.algorithmic_bytes / (ev * 1e-3) / 1e9, tflops=c.flops / (ev * 1e-3) / 1e12)
 
 
@@ -415,6 +430,78 @@ def vendor_context(steps: int, warmup: int):
     return out
 
 
+def _probe_lib():
+    """libllprobes.so: the practical-ceiling probes (include/llprobes.h)."""
+    import ctypes
+    path = os.path.join(ROOT, "recsys_linear_layers_amd", "libllprobes.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (run recsys_linear_layers_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    lib.ll_probe_mfma_only.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_void_p]
+    return lib
+
+
+def _probe_call(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with status {rc}")
+
+
+def mfma_probe(steps: int, warmup: int, grid: int = 1024, iters: int = 20000) -> dict:
+    """bf16 MFMA issue with no memory traffic: grid workgroups of 4 waves, one
+    per SIMD, each wave iters x 16 independent 32x32x16 MFMAs; once on small
+    constant operands and once on random bf16 fragments (the multipliers
+    switch as with a GEMM's data, and the chip's power limit sets the clock
+    accordingly)."""
+    import torch
+    lib = _probe_lib()
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    frag = torch.randn(8 * 256 * 8, generator=gen, device="cuda").to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    flops = grid * 4 * iters * 16 * 32768
+    res = {"probe": "mfma_only (v_mfma_f32_32x32x16_bf16 back to back, no memory traffic)", "grid": grid,
+           "iters": iters, "flops_per_call": flops}
+    for key, ptr in (("constant_operands", None), ("random_operands", frag.data_ptr())):
+        _log(f"mfma probe ({key}): {grid} workgroups x {iters} iterations")
+        t = _time_launches(lambda: _probe_call(lib.ll_probe_mfma_only(grid, iters, ptr, out.data_ptr(),
+                                                                      stream.cuda_stream), "ll_probe_mfma_only"),
+                           steps, warmup, stream)
+        tf = flops / (t["ms"] * 1e-3) / 1e12
+        res[key] = {"ms": round(t["ms"], 4), "median_ms": round(t["median_ms"], 4), "TFLOP/s": round(tf, 1),
+                    "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return res
+
+
+def hbm_probe(mib: int, steps: int, warmup: int) -> dict:
+    """Streaming through HBM with 16-byte accesses: a copy (1 read : 1 write)
+    and 4 streams read per stream written, mib MiB per stream, at several
+    grid sizes; the best of each is the ceiling."""
+    import torch
+    lib = _probe_lib()
+    n16 = (mib << 20) // 16
+    x = torch.ones(4 * n16 * 4, dtype=torch.int32, device="cuda")
+    y = torch.empty(n16 * 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {"probe": "hbm streaming (16-byte loads and stores, no reuse)", "mib_per_stream": mib}
+    for streams, key in ((1, "copy"), (4, "read4_write1")):
+        nbytes = (streams + 1) * n16 * 16
+        runs = []
+        for grid in (1024, 2048, 4096, 8192):
+            _log(f"hbm probe: {key}, grid {grid}")
+            t = _time_launches(lambda: _probe_call(lib.ll_probe_stream(streams, x.data_ptr(), y.data_ptr(), n16, grid,
+                                                                       stream.cuda_stream), "ll_probe_stream"),
+                               steps, warmup, stream)
+            runs.append(dict(grid=grid, ms=round(t["ms"], 4), median_ms=round(t["median_ms"], 4),
+                             gbs=round(nbytes / (t["ms"] * 1e-3) / 1e9, 1)))
+        best = max(runs, key=lambda r: r["gbs"])
+        res[key] = dict(bytes_per_call=nbytes, best_gbs=best["gbs"], best_grid=best["grid"],
+                        frac_of_peak=round(best["gbs"] / PEAK_HBM_GBS, 4), runs=runs)
+    return res
+
+
 # Legs timed before the headline, in this order (the long FFN calls first);
 # the configurations whose oracle is timed too are listed in CPU_LEGS.
 ALSO_ORDER = ["ffn_up", "ffn_down", "ffn_up_bias_gelu", "lincomp_256x128", "lincomp_256x128_stacked",
@@ -519,6 +606,12 @@ def main():
                          "(calibrates the HBM byte counters of a profiler run); prints its own line")
     ap.add_argument("--vendor-context", action="store_true",
                     help="time torch.matmul (the vendor GEMM) on the GEMM workloads' shapes instead, for context")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the MFMA-issue ceiling probe (bf16 MFMAs back to back, no memory traffic), "
+                         "--steps times; prints its own line")
+    ap.add_argument("--hbm-probe-mib", type=int, default=0,
+                    help="only run the HBM streaming ceiling probes (a copy, and 4 streams read per stream "
+                         "written) over this many MiB per stream, --steps times per grid size; prints its own line")
     ap.add_argument("--stream-probe-mib", type=int, default=0,
                     help="only run a streaming reduction that reads 4x and writes 1x this many MiB "
                          "(the read/write mix of linear compression), --steps times; prints its own line")
@@ -556,6 +649,14 @@ def main():
         rd, wr = 16 * n, 4 * n
         print(json.dumps({"probe": "stream 4 reads : 1 write", "bytes_read": rd, "bytes_written": wr,
                           "ms": round(t["ms"], 4), "GB/s": round((rd + wr) / (t["ms"] * 1e-3) / 1e9, 1)}))
+        return
+
+    if args.mfma_probe:
+        print(json.dumps(mfma_probe(args.steps, args.warmup)))
+        return
+
+    if args.hbm_probe_mib:
+        print(json.dumps(hbm_probe(args.hbm_probe_mib, args.steps, args.warmup)))
         return
 
     if args.vendor_context:
@@ -645,6 +746,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": config, "roofline": roof, "cpu_baseline": cpu,
         "kernel_ms": round(r["kernel_ms"], 4), "kernel_median_ms": round(r["median_ms"], 4),
+        "kernel_per_call_mean_ms": round(r["per_call_mean_ms"], 4),
         "timed_after": [a["workload"] for a in also],
         "plan": plan, **rule_context,
     }

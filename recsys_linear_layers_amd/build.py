@@ -1,6 +1,7 @@
-"""Compile the HIP sources under csrc/ for gfx950 into liblinlayers.so (in-tree).
+"""Compile the HIP sources under csrc/ for gfx950 into liblinlayers.so (in-tree),
+and the measurement probes under probes/ into libllprobes.so.
 
-Each .hip file is compiled to an object in parallel, then linked into one
+Each .hip file is compiled to an object in parallel, then linked into its
 shared library next to this file.
 """
 from __future__ import annotations
@@ -15,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblinlayers.so")
+PROBES = os.path.join(HERE, "probes")
+PROBE_LIB = os.path.join(HERE, "libllprobes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
@@ -61,17 +64,26 @@ def _units():
     return units
 
 
+def _probe_units():
+    return [(src, os.path.join(BUILD, "probe_" + os.path.basename(src)[:-4] + ".o"), [])
+            for src in sorted(glob.glob(os.path.join(PROBES, "*.hip")))]
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    units = _units()
+    units, probes = _units(), _probe_units()
     jobs = jobs or min(8, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda u: _run([HIPCC, *FLAGS, *u[2], "-c", u[0], "-o", u[1]], verbose), units))
+        list(ex.map(lambda u: _run([HIPCC, *FLAGS, *u[2], "-c", u[0], "-o", u[1]], verbose), units + probes))
     # objects of sources that no longer exist are not linked
-    objs = [u[1] for u in units]
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    _link([u[1] for u in units], LIB, verbose)
+    _link([u[1] for u in probes], PROBE_LIB, verbose)
     return LIB
 
 

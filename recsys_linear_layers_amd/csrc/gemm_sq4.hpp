@@ -79,6 +79,88 @@ __device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileIn
   epilogue<Sq4Block<EPI>>(p, ti, acc, wm0 + 32 * I, wn0 + 32 * J, lane);
 }
 
+// Staged store of a wave's 128x128 block of 16-bit C through 32 KB of LDS
+// (the ring is free once every wave has left the k-loop).  Per 32x32
+// accumulator block the lane pair holding columns d, d+1 swaps values, so
+// that each lane holds 4-byte column pairs of two rows, and writes them into a
+// row-major [128][128] image (256-byte rows) whose 16-byte chunks are
+// XOR-swizzled by ((row >> 1) & 3) << 2: the four rows one write instruction
+// covers then fall on four different 64-byte groups of banks.  Each 16-byte
+// read then takes four whole rows back and each lane stores 16 bytes, so a
+// wave stores its block with 32 instructions of whole 128-byte lines instead
+// of 128 of 4 bytes per lane.
+__device__ __forceinline__ uint32_t sq4_stage_off(int row, int cb) {
+  return (uint32_t)(row * 256 + ((((cb >> 4) ^ (((row >> 1) & 3) << 2))) << 4) + (cb & 15));
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t sq4_pack16(float lo, float hi) {
+  return (uint32_t)to_c16<FMT>(lo) | ((uint32_t)to_c16<FMT>(hi) << 16);
+}
+
+template <int EPI, int FMT, int I, int J>
+__device__ __forceinline__ void sq4_stage_block(const GemmKArgs& p, const TileInfo& ti, int wn0, int lane,
+                                                char LL_LDS* img) {
+  f32x16 acc[1][1];
+  acc[0][0] = sq4_read_acc<I, J>();
+  if constexpr (EPI > 0) apply_epi<Sq4Block<EPI>, EPI - 1>(p, ti, acc, wn0 + 32 * J, lane);
+  const bool odd = lane & 1;
+  // even lane: rows +0, +1 of its group; odd lane: rows +2, +3 (see epilogue_fast16)
+  const int ra = 32 * I + 4 * (lane >> 5) + (odd ? 2 : 0);
+  const int cb = 64 * J + 2 * (lane & 30);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float v0 = acc[0][0][4 * g + 0], v1 = acc[0][0][4 * g + 1];
+    const float v2 = acc[0][0][4 * g + 2], v3 = acc[0][0][4 * g + 3];
+    const float s0 = swap_pair(odd ? v0 : v2);
+    const float s1 = swap_pair(odd ? v1 : v3);
+    const float a0 = odd ? s0 : v0, a1 = odd ? v2 : s0;
+    const float b0 = odd ? s1 : v1, b1 = odd ? v3 : s1;
+    *(uint32_t LL_LDS*)(img + sq4_stage_off(ra + 8 * g, cb)) = sq4_pack16<FMT>(a0, a1);
+    *(uint32_t LL_LDS*)(img + sq4_stage_off(ra + 8 * g + 1, cb)) = sq4_pack16<FMT>(b0, b1);
+  }
+}
+
+template <int EPI, int FMT>
+__device__ __forceinline__ void sq4_stage_all(const GemmKArgs& p, const TileInfo& ti, int wn0, int lane,
+                                              char LL_LDS* img) {
+  sq4_stage_block<EPI, FMT, 0, 0>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 0, 1>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 0, 2>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 0, 3>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 1, 0>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 1, 1>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 1, 2>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 1, 3>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 2, 0>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 2, 1>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 2, 2>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 2, 3>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 3, 0>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 3, 1>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 3, 2>(p, ti, wn0, lane, img);
+  sq4_stage_block<EPI, FMT, 3, 3>(p, ti, wn0, lane, img);
+}
+
+// The image back, four rows per read, each lane storing 16 bytes of a row.
+// Element offsets fit in 32 bits (the fast-epilogue condition bounds
+// ldcm * (M + 256) below 2^31), so each lane keeps one offset that steps by
+// four rows.
+__device__ __forceinline__ void sq4_flush(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0, int lane,
+                                          const char LL_LDS* img) {
+  const int rl = lane >> 4, c = lane & 15;
+  const int32_t step = 4 * (int32_t)p.ldcm;
+  int32_t off = (ti.m0 + wm0 + rl) * (int32_t)p.ldcm + ti.n0 + wn0 + c * 8;
+  uint16_t* const cb = (uint16_t*)p.c;
+#pragma unroll
+  for (int q = 0; q < 32; ++q) {
+    const int row = 4 * q + rl;
+    const i32x4 v = *(const i32x4 LL_LDS*)(img + row * 256 + ((c ^ (((row >> 1) & 3) << 2)) << 4));
+    *(i32x4*)(cb + (uint32_t)off) = v;
+    off += step;
+  }
+}
+
 // The first `count` of this wave's 16 direct-to-LDS loads of one slice into
 // `slot`, in the loop's order (A 0, B 0, A 1, B 1, ...).  Load q = wave + 4 i
 // of an operand tile covers A rows 8q..8q+7 (K-contiguous, 128 bytes each) or
@@ -189,7 +271,23 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       asm volatile(LL_SQ4_LOOP_BF16 LL_SQ4_OPERANDS);
 #undef LL_SQ4_OPERANDS
 
-    lds_barrier();  // every wave is done reading the ring before it is refilled
+    lds_barrier();  // every wave is done reading the ring before it is reused
+    // a whole tile inside a 16-bit row-major C with 16-byte aligned rows:
+    // staged through LDS (uniform over the workgroup)
+    const bool staged = p.c_fast && p.c_fmt != 0 && ti.m0 + Sq4::BM <= p.M && ti.n0 + Sq4::BN <= p.N &&
+                        ((uintptr_t)p.c & 15) == 0 && (p.ldcm & 7) == 0;
+    if (staged) {
+      char LL_LDS* img = smem + wave * 32768;
+      if (p.c_fmt == 1)
+        sq4_stage_all<EPI, 1>(p, ti, wn0, lane, img);
+      else
+        sq4_stage_all<EPI, 2>(p, ti, wn0, lane, img);
+      sq4_flush(p, ti, wm0, wn0, lane, img);
+      // the next work item's loads land all over the LDS the other waves
+      // may still be reading
+      if (t + stride < p.total) lds_barrier();
+      continue;
+    }
     sq4_store_block<EPI, 0, 0>(p, ti, wm0, wn0, lane);
     sq4_store_block<EPI, 0, 1>(p, ti, wm0, wn0, lane);
     sq4_store_block<EPI, 0, 2>(p, ti, wm0, wn0, lane);

@@ -1,0 +1,112 @@
+// Practical-ceiling probes (include/llprobes.h): MFMA issue with no memory
+// traffic, and plain HBM streaming with 16-byte accesses.  Measurement only:
+// nothing here computes a library operation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/llprobes.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 16 independent accumulators per wave (the 128x128 block of four 32x32
+// tiles by four that a GEMM wave holds): an MFMA's result is next needed 16
+// MFMAs later, far past its latency, so issue never waits on a dependency.
+// Accumulator (i, j) takes A fragment i and B fragment j, as in a GEMM's
+// k16 step.  Operands either come from `frag` (eight 16-byte fragments per
+// lane, e.g. random bf16 patterns: the multipliers switch as with real data)
+// or, with frag null, are small constants that barely switch (the issue
+// rate with the least power).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_only_kernel(int iters, const uint4* __restrict__ frag, float* out) {
+  bf16x8 a[4], b[4];
+  if (frag) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __builtin_bit_cast(bf16x8, frag[i * 256 + threadIdx.x]);
+      b[i] = __builtin_bit_cast(bf16x8, frag[(4 + i) * 256 + threadIdx.x]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[i][e] = (__bf16)(float)((threadIdx.x + e) & 7);
+        b[i][e] = (__bf16)(float)((3 * threadIdx.x + e) & 7);
+      }
+  }
+  f32x16 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j >> 2], b[j & 3], acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[j][e];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// Grid-stride over n16 elements, U elements per thread per pass with all of
+// a pass's loads issued before its stores.
+template <int S>
+__global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
+                                                     int64_t n16) {
+  constexpr int U = 4;
+  const int64_t step = (int64_t)gridDim.x * 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += step) {
+    uint4 v[U][S];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * 256;
+#pragma unroll
+      for (int s = 0; s < S; ++s) v[u][s] = i < n16 ? x[s * n16 + i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * 256;
+      if (i < n16) {
+        uint4 r = v[u][0];
+#pragma unroll
+        for (int s = 1; s < S; ++s) {
+          r.x ^= v[u][s].x;
+          r.y ^= v[u][s].y;
+          r.z ^= v[u][s].z;
+          r.w ^= v[u][s].w;
+        }
+        y[i] = r;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int ll_probe_mfma_only(int grid, int iters, const void* operands, float* out, void* stream) {
+  if (grid < 1 || grid > (1 << 20) || iters < 0 || iters > (1 << 24) || !out) return -1;
+  if ((uintptr_t)operands & 15) return -1;
+  mfma_only_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(iters, (const uint4*)operands, out);
+  return (int)hipGetLastError();
+}
+
+extern "C" int ll_probe_stream(int streams, const void* x, void* y, int64_t n16, int grid, void* stream) {
+  if ((streams != 1 && streams != 4) || n16 < 0 || grid < 1 || grid > (1 << 20)) return -1;
+  if (n16 == 0) return 0;
+  if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return -1;
+  const uintptr_t xb = (uintptr_t)x, xe = xb + (uintptr_t)(streams * n16 * 16);
+  const uintptr_t yb = (uintptr_t)y, ye = yb + (uintptr_t)(n16 * 16);
+  if (xb < ye && yb < xe) return -1;
+  const uint4* xp = (const uint4*)x;
+  uint4* yp = (uint4*)y;
+  if (streams == 1)
+    stream_kernel<1><<<grid, 256, 0, (hipStream_t)stream>>>(xp, yp, n16);
+  else
+    stream_kernel<4><<<grid, 256, 0, (hipStream_t)stream>>>(xp, yp, n16);
+  return (int)hipGetLastError();
+}

@@ -159,3 +159,38 @@ def test_ragged_argument_checks():
 def test_gemm_run_ex_null_plan():
     import recsys_linear_layers_amd as ll
     assert ll._lib.gemm_run_ex(None, None, None, None, None, None, 0, None) == ll.LL_ERR_INVALID_ARG
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "llprobes.h")
+PROBE_LIB = os.path.join(ROOT, "recsys_linear_layers_amd", "libllprobes.so")
+
+
+def _probe_lib():
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.ll_probe_mfma_only.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_void_p]
+    return lib
+
+
+def test_probe_library_exports_every_declared_symbol():
+    names = re.findall(r"^int\s+(\w+)\s*\(", open(PROBE_HEADER).read(), re.M)
+    assert sorted(names) == ["ll_probe_mfma_only", "ll_probe_stream"]
+    lib = ctypes.CDLL(PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_probes_reject_bad_arguments_on_the_host():
+    """Every rejected call returns -1 before any HIP call is made."""
+    lib = _probe_lib()
+    assert lib.ll_probe_mfma_only(0, 10, None, 256, None) == -1    # grid < 1
+    assert lib.ll_probe_mfma_only(1, -1, None, 256, None) == -1    # iters < 0
+    assert lib.ll_probe_mfma_only(1, 10, None, None, None) == -1   # no output
+    assert lib.ll_probe_mfma_only(1, 10, 4100, 256, None) == -1    # misaligned operands
+    assert lib.ll_probe_stream(2, 4096, 1 << 20, 16, 1, None) == -1  # streams not 1 or 4
+    assert lib.ll_probe_stream(1, 4096, 1 << 20, -1, 1, None) == -1  # n16 < 0
+    assert lib.ll_probe_stream(1, 4096, 1 << 20, 16, 0, None) == -1  # grid < 1
+    assert lib.ll_probe_stream(1, 4100, 1 << 20, 16, 1, None) == -1  # misaligned x
+    assert lib.ll_probe_stream(4, 4096, 4096 + 16 * 16, 16, 1, None) == -1  # y inside x
+    assert lib.ll_probe_stream(1, None, None, 0, 1, None) == 0     # nothing to do

@@ -168,3 +168,72 @@ def test_full_size_sampled(name, monkeypatch):
     for r0, nr in strip_starts(c.M, 64, 7):
         ref, S = oracle.gemm_case(c, rows=(r0, nr))
         acceptance.assert_close(got[r0:r0 + nr], ref, S, c.out_dtype, f"{name} rows {r0}.. {d}")
+
+
+def _run_into(A, B, C, monkeypatch, bias=None, act=None):
+    import torch
+    import recsys_linear_layers_amd as ll
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", KIND)
+    try:
+        ll.gemm(A, B, out=C, bias=bias, act=act)
+        torch.cuda.synchronize()
+        ep = (ll.LL_EPI_BIAS if bias is not None else 0) | ll.ACTIVATIONS[act]
+        d = ll.plan_for(A, B, C, 0, ep).describe()
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+    assert f"kernel={KIND} " in d, d
+    return d
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+@pytest.mark.parametrize("act", [None, "gelu"])
+def test_staged_epilogue_matches_direct_stores(out, act, monkeypatch):
+    """Whole tiles of a 16-bit C whose rows are 16-byte aligned leave through
+    an LDS image with 16-byte stores; with a row stride that is not a multiple
+    of 8 elements every tile takes the direct 4-byte stores.  Both give the
+    same bits.  4600 x 4352: 18 x 17 = 306 tiles on 256 workgroups (a second
+    work item for 50 of them, after the barrier that guards the image), the
+    last tile row ragged (direct stores beside staged tiles); checked against
+    the oracle in full."""
+    import torch
+    in_dtype = "f16" if out == "f16" else "bf16"
+    M, N, K = 4600, 4352, 128
+    c = synth.gemm_case(M, N, K, seed=91 + (act is None), out_dtype=out, in_dtype=in_dtype,
+                        dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[out]
+    bias = None
+    if act:
+        bias = torch.from_numpy(np.random.default_rng(92).standard_normal(N).astype(np.float32)).cuda()
+    C1 = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    big = torch.full((M, N + 4), float("nan"), dtype=dt, device="cuda")
+    C2 = big[:, :N]
+    d1 = _run_into(A, B, C1, monkeypatch, bias, act)
+    d2 = _run_into(A, B, C2, monkeypatch, bias, act)
+    g1, g2 = to_f64(C1), to_f64(C2)
+    assert np.array_equal(g1, g2), (d1, d2)
+    assert torch.isnan(big[:, N:].float()).all()  # the padding columns are untouched
+    ref, S = oracle.gemm_case(c)
+    if act:
+        ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+    acceptance.assert_close(g1, ref, S, out, f"staged {M}x{N}x{K} {out} act={act} {d1}", act=act)
+
+
+def test_staged_epilogue_needs_16_byte_aligned_c(monkeypatch):
+    """A C that starts 8 bytes into an allocation (rows 16-byte aligned apart
+    from that) takes the direct stores and matches an aligned C."""
+    import torch
+    M, N, K = 512, 768, 192
+    c = synth.gemm_case(M, N, K, seed=93, out_dtype="bf16", dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    C1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    flat = torch.full((M * N + 8,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    C2 = flat[4:4 + M * N].view(M, N)
+    assert C2.data_ptr() % 16 == 8
+    _run_into(A, B, C1, monkeypatch)
+    _run_into(A, B, C2, monkeypatch)
+    assert np.array_equal(to_f64(C1), to_f64(C2))
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(to_f64(C1), ref, S, "bf16", "aligned C")
