@@ -118,11 +118,17 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * N-contiguous and no epilogue is fused, 256x256 tiles (eight computing
  * waves, one per SIMD also loading) replace it when they need no more passes
  * x tile area; for K > 8192 the 128x256 tiles take their place again under
- * the same conditions.  K is split when the tiles fill fewer than half of the
- * CUs.  The environment variable LL_GEMM_KIND (a kernel name as printed
- * by gemm_plan_describe, or its index) forces a kernel for configuration
- * sweeps; a forced 192-row tile with an M-contiguous A gives
- * LL_ERR_UNSUPPORTED.
+ * the same conditions.  Last, with A K-contiguous and B N-contiguous (direct
+ * or packed), K a multiple of 64 and each operand spanning under 2 GB from
+ * its base, any of those four kinds gives way to KIND_SQ4_HO (256x256 tiles,
+ * four waves of 128x128, one per SIMD, each loading and computing in one
+ * hand-ordered instruction stream) when that needs no more passes x tile
+ * area; with or without a fused epilogue.  K is split when the tiles fill
+ * fewer than half of the CUs.  The environment variable LL_GEMM_KIND (a
+ * kernel name as printed by gemm_plan_describe, or its index) forces a
+ * kernel for configuration sweeps; a forced kernel that cannot take the
+ * operands (a 192-row tile with an M-contiguous A, KIND_SQ4_HO outside the
+ * conditions above) gives LL_ERR_UNSUPPORTED.
  * Errors: LL_ERR_INVALID_ARG (null out/desc, negative size, zero or negative
  * stride, unknown flag bits), LL_ERR_UNSUPPORTED (dtype, neither stride of A
  * or of B equal to 1, device not gfx950), LL_ERR_NO_DEVICE, LL_ERR_HIP.
