@@ -91,3 +91,32 @@ def test_lincomp_graph_replay():
     user, item, W = lincomp_operands(c)
     Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
     _replay_check(lambda: ll.lincomp(user, item, W, out=Y), Y)
+
+
+def test_hand_ordered_kind_graph_replay():
+    # 5100 x 5120 selects the hand-ordered 256x256 kind: 400 work items on 256
+    # workgroups (second items after the barrier that guards the staged C
+    # image), a ragged last tile row (direct stores) beside staged tiles
+    plan, run, C = _gemm_case_run(synth.gemm_case(5100, 5120, 256, seed=36, dist=("normal", 0.0, 1.0),
+                                                  out_dtype="bf16"))
+    assert "kernel=KIND_SQ4_HO " in plan.describe(), plan.describe()
+    _replay_check(run, C)
+
+
+def test_hand_ordered_kind_fused_graph_replay():
+    import torch
+    bias = torch.linspace(-2.0, 2.0, 5120, dtype=torch.float32, device="cuda")
+    plan, run, C = _gemm_case_run(synth.gemm_case(5100, 5120, 256, seed=37, dist=("normal", 0.0, 1.0),
+                                                  out_dtype="bf16"), bias=bias, act="silu")
+    assert "kernel=KIND_SQ4_HO " in plan.describe(), plan.describe()
+    _replay_check(run, C)
+
+
+def test_lincomp_epilogue_graph_replay():
+    import torch
+    ll = _ll()
+    c = synth.lincomp_case(8, 5, 256, 256, 256, 64, seed=38)
+    user, item, W = lincomp_operands(c)
+    bias = torch.linspace(-1.0, 1.0, 64, dtype=torch.float32, device="cuda")
+    Y = torch.empty((c.R, c.C, c.Mo, c.D), dtype=torch.bfloat16, device="cuda")
+    _replay_check(lambda: ll.lincomp(user, item, W, out=Y, bias=bias, act="gelu"), Y)
