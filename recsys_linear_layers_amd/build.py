@@ -40,6 +40,26 @@ def _run(cmd, verbose):
         print(out, file=sys.stderr)
 
 
+# Units built with the compiler's default machine scheduler instead: the
+# linear-compression kernels are bound by HBM, not by their instruction
+# schedule, and iterative-ilp spilled their fused-epilogue instantiations
+# (bias + GELU 34 registers against 10).
+DEFAULT_SCHED = {"lincomp.hip"}
+
+
+def _flags(src):
+    if os.path.basename(src) not in DEFAULT_SCHED:
+        return FLAGS
+    out, i = [], 0
+    while i < len(FLAGS):
+        if FLAGS[i] == "-mllvm" and FLAGS[i + 1].startswith("-amdgpu-sched-strategy="):
+            i += 2
+            continue
+        out.append(FLAGS[i])
+        i += 1
+    return out
+
+
 # gemm_inst.hip is compiled once per operand layout (A K- or M-contiguous, B K-
 # or N-contiguous), operand type (bf16, fp16) and epilogue (plain, fused), each
 # unit defining the launch function that aux_kernels.hip dispatches to.
@@ -80,7 +100,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     units, probes = _units(), _probe_units()
     jobs = jobs or min(8, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda u: _run([HIPCC, *FLAGS, *u[2], "-c", u[0], "-o", u[1]], verbose), units + probes))
+        list(ex.map(lambda u: _run([HIPCC, *_flags(u[0]), *u[2], "-c", u[0], "-o", u[1]], verbose), units + probes))
     # objects of sources that no longer exist are not linked
     _link([u[1] for u in units], LIB, verbose)
     _link([u[1] for u in probes], PROBE_LIB, verbose)

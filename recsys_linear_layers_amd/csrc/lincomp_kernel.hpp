@@ -45,6 +45,7 @@ struct LincompKArgs {
   int32_t nu_sl, ni_sl;                        // slices per user / per candidate phase (>= 1 for Ni)
   int32_t total;                               // work items
   int32_t y_bf16, dedup;
+  int32_t y_stage;  // bf16 Y, base and strides multiples of 16 bytes: whole-tile stores go through LDS
   // Ragged requests (offsets != nullptr): C is the total candidate count, the
   // candidates of request r are offsets[r] .. offsets[r+1]-1 (global indices
   // into item and Y, whose request strides are 0), and the candidates are cut
@@ -72,12 +73,17 @@ struct LincompCfg {
   static constexpr int A_BYTES = BM * KT * 2, B_BYTES = BN * KT * 2;
   static constexpr int SLOT = A_BYTES + B_BYTES;
   static constexpr int LDS = STAGES * SLOT;
+  // bf16 Y leaves through a per-wave LDS image after the ring (lc_flush)
+  // where the image fits: 64 columns (128-byte rows) per wave
+  static constexpr int IMG = BM * (BN / WN) * 2;
+  static constexpr bool STAGE_Y = BN / WN == 64 && LDS + NCONS * IMG <= 160 * 1024;
+  static constexpr int LDS_ALL = LDS + (STAGE_Y ? NCONS * IMG : 0);
   static constexpr int LOADERS = NPROD;
   static constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / NPROD;
   static constexpr int WAVES_PER_EU = (WAVES + 3) / 4;
   static_assert(NPROD > 0, "the fused kernel uses separate loading waves");
   static_assert((A_BYTES / 1024) % NPROD == 0 && (B_BYTES / 1024) % NPROD == 0, "load split");
-  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(LDS_ALL <= 160 * 1024, "LDS");
   static_assert(STAGES >= 2 && STAGES <= 8, "stages");
   static_assert(LPW * (STAGES - 1) < 64, "vmcnt range");
   static_assert(FM * FN * 16 * 2 <= 160, "accumulators + U must leave room for fragments");
@@ -254,6 +260,57 @@ __device__ __forceinline__ void lc_store_group(const LincompKArgs& p, uint16_t* 
   }
 }
 
+// Staged bf16 Y: the wave's BM x 64 block goes into its own LDS image and
+// back out in whole 128-byte lines, 16 bytes per lane (8 rows of a 64-column
+// segment per store instruction instead of 4 half lines per instruction).
+// The image has 128-byte rows; row q sits at physical row q ^ ((q >> 1) & 1)
+// and its 16-byte chunk c at c ^ (((q >> 2) & 1) << 2).  A pair write covers
+// rows 8k + {0,2,4,6} (or {1,3,5,7}) x 64 bytes and lands on all 64 banks
+// once; a 16-byte read of 16 lanes covers two whole rows of opposite bank
+// halves.  Each wave only reads back what it wrote, in order, so no barrier
+// is needed; the next candidate's writes follow this one's reads in the same
+// wave.
+__device__ __forceinline__ uint32_t lc_img_off(int q, int cb) {
+  return (uint32_t)(((q ^ ((q >> 1) & 1)) << 7) + ((((cb >> 4) ^ (((q >> 2) & 1) << 2))) << 4) + (cb & 15));
+}
+
+// One group of staged values: v0..v3 of rows q%4 = 0..3 at this lane's
+// column, lane-pair swapped as in lc_store_group; the pair of row q goes to
+// LDS byte address wa, that of row q+1 to wb.
+__device__ __forceinline__ void lc_stage_group(uint32_t wa, uint32_t wb, bool odd, float v0, float v1, float v2,
+                                               float v3) {
+  const float s0 = swap_pair(odd ? v0 : v2);
+  const float s1 = swap_pair(odd ? v1 : v3);
+  float a0, a1, b0, b1;  // row q: (a0 at d, a1 at d+1); row q+1: (b0, b1)
+  if (!odd) {
+    a0 = v0; a1 = s0;
+    b0 = v1; b1 = s1;
+  } else {
+    a0 = s0; a1 = v2;
+    b0 = s1; b1 = v3;
+  }
+  *(uint32_t LL_LDS*)(uintptr_t)wa = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
+  *(uint32_t LL_LDS*)(uintptr_t)wb = (uint32_t)f32_to_bf16_bits(b0) | ((uint32_t)f32_to_bf16_bits(b1) << 16);
+}
+
+// The image back, eight rows per 16-byte read, and out to Y (Yw: the wave's
+// block origin, sym its row stride).  Rows 8k + rl keep the lane's physical
+// row and chunk swizzle of row rl, so the reads step by 1 KB.
+template <int BM>
+__device__ __forceinline__ void lc_flush(uint16_t* Yw, int sym, int lane, uint32_t img) {
+  const int rl = lane >> 3, c = lane & 7;
+  const uint32_t ra = img + lc_img_off(rl, c * 16);
+  int off = rl * sym + c * 8;
+#pragma unroll 2
+  for (int k = 0; k < BM / 8; ++k) {
+    const i32x4 v = *(const i32x4 LL_LDS*)(uintptr_t)(ra + k * 1024);
+    // Y is written once and not read again by this kernel: non-temporal
+    // (with whole lines, 3-4% faster than cached stores of the same lines)
+    __builtin_nontemporal_store(v, (i32x4*)(Yw + off));
+    off += 8 * sym;
+  }
+}
+
 // Stores the wave's FM x FN blocks of Y for candidate (r, c).  Accumulator
 // layout of v_mfma_f32_32x32x16: register q of lane l holds row 8*(q/4) +
 // 4*(l/32) + q%4, column l%32 of the 32x32 block.  The block is addressed
@@ -269,12 +326,48 @@ __device__ __forceinline__ void lc_store_group(const LincompKArgs& p, uint16_t* 
 //    group for every block and the activation's temporaries stay few.
 template <class Cfg>
 __device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& s, f32x16 (&acc)[Cfg::FM][Cfg::FN],
-                                            int wn0, int lane) {
+                                            int wn0, int lane, char LL_LDS* img) {
   constexpr bool any_epi = Cfg::ACT != 0 || Cfg::BIAS;
   const int64_t yoff = (int64_t)s.r * p.sy_r + (int64_t)s.c * p.sy_c;
   const int sym = (int)p.sy_m;
   const int mb = s.m0 * Cfg::BM + 4 * (lane >> 5);
   const int db = s.n0 * Cfg::BN + wn0 + (lane & 31);
+  // the wave's whole block inside Y, 16-byte aligned rows (p.y_stage: the
+  // base and the strides are multiples of 16 bytes; wave-uniform)
+  if (Cfg::STAGE_Y && p.y_stage && s.m0 * Cfg::BM + Cfg::BM <= p.Mo && s.n0 * Cfg::BN + wn0 + 64 <= p.D) {
+    const bool odd = lane & 1;
+    const int q0 = 4 * (lane >> 5) + (odd ? 2 : 0);  // this lane's first row, 0, 2, 4 or 6
+    const int cb = 2 * (lane & 30);                   // byte of its column pair in a 64-column block
+    const uint32_t im = lds_u32(img);
+    // rows q0 + 32 i + 8 g (+1) keep the swizzle of rows q0 (+1): two base
+    // addresses per column block, constant offsets per (i, g)
+    uint32_t wa[Cfg::FN], wb[Cfg::FN];
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      wa[j] = im + lc_img_off(q0, cb + 64 * j);
+      wb[j] = im + lc_img_off(q0 + 1, cb + 64 * j);
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 b = lc_bias4<Cfg::BIAS>(p, mb + 32 * i + 8 * g);
+        const uint32_t ro = (32 * i + 8 * g) * 128;
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          if constexpr (any_epi)
+            lc_stage_group(wa[j] + ro, wb[j] + ro, odd, epi<Cfg::ACT>(v0, b[0]), epi<Cfg::ACT>(v1, b[1]),
+                           epi<Cfg::ACT>(v2, b[2]), epi<Cfg::ACT>(v3, b[3]));
+          else
+            lc_stage_group(wa[j] + ro, wb[j] + ro, odd, v0, v1, v2, v3);
+        }
+      }
+    lc_flush<Cfg::BM>((uint16_t*)p.Y + yoff + (int64_t)(s.m0 * Cfg::BM) * sym + s.n0 * Cfg::BN + wn0, sym, lane,
+                      im);
+    return;
+  }
   if (p.y_bf16) {
     uint16_t* Y = (uint16_t*)p.Y + yoff;
     const bool odd = lane & 1;
@@ -343,7 +436,7 @@ template <class Cfg>
 __global__ void __launch_bounds__(Cfg::THREADS)
     __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_EU, Cfg::WAVES_PER_EU)))
     lincomp_fused(const LincompKArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS_ALL];
   char LL_LDS* smem = (char LL_LDS*)smem_raw;
   constexpr int S = Cfg::STAGES;
   constexpr int KS = Cfg::KS;
@@ -392,6 +485,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
 
   // ---------------- computing waves ----------------
   const int wn0 = wave * (Cfg::BN / Cfg::WN);
+  char LL_LDS* img = smem + Cfg::LDS + (Cfg::STAGE_Y ? wave * Cfg::IMG : 0);
   f32x16 acc[Cfg::FM][Cfg::FN], u[Cfg::FM][Cfg::FN];
   zero_acc(acc);
   zero_acc(u);
@@ -426,7 +520,7 @@ __global__ void __launch_bounds__(Cfg::THREADS)
         for (int jj = 0; jj < Cfg::FN; ++jj) u[i][jj] = acc[i][jj];
     }
     if (cc.cand_end(p)) {
-      lc_epilogue<Cfg>(p, cc, acc, wn0, lane);
+      lc_epilogue<Cfg>(p, cc, acc, wn0, lane, img);
       if (p.dedup && !cc.req_end(p)) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)

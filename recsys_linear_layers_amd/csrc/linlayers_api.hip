@@ -712,6 +712,9 @@ static ll_status lincomp_launch(const lincomp_desc* d, const int64_t* offsets, c
   if (total >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "too many work items");
   k.total = (int32_t)total;
   k.y_bf16 = d->y_type == LL_BF16;
+  // Y and its strides are 16-byte multiples (checked above): bf16 Y tiles
+  // that lie wholly inside Y leave through LDS in whole lines
+  k.y_stage = k.y_bf16;
   // Per-candidate user rows (su_c != 0) leave nothing to share.
   k.dedup = !(d->flags & LL_LINCOMP_NO_DEDUP) && d->su_c == 0;
   k.bias = bias;
