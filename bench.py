@@ -438,8 +438,8 @@ def _probe_lib():
         raise RuntimeError(f"{path} is not built (run recsys_linear_layers_amd/build.py)")
     lib = ctypes.CDLL(path)
     lib.ll_probe_mfma_only.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                    ctypes.c_void_p]
+    lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -477,8 +477,9 @@ def mfma_probe(steps: int, warmup: int, grid: int = 1024, iters: int = 20000) ->
 
 def hbm_probe(mib: int, steps: int, warmup: int) -> dict:
     """Streaming through HBM with 16-byte accesses: a copy (1 read : 1 write)
-    and 4 streams read per stream written, mib MiB per stream, at several
-    grid sizes; the best of each is the ceiling."""
+    and 4 streams read per stream written, mib MiB per stream, with plain and
+    with non-temporal loads and stores, at several grid sizes; the best of
+    each pass is its ceiling."""
     import torch
     lib = _probe_lib()
     n16 = (mib << 20) // 16
@@ -488,17 +489,18 @@ def hbm_probe(mib: int, steps: int, warmup: int) -> dict:
     res = {"probe": "hbm streaming (16-byte loads and stores, no reuse)", "mib_per_stream": mib}
     for streams, key in ((1, "copy"), (4, "read4_write1")):
         nbytes = (streams + 1) * n16 * 16
-        runs = []
-        for grid in (1024, 2048, 4096, 8192):
-            _log(f"hbm probe: {key}, grid {grid}")
-            t = _time_launches(lambda: _probe_call(lib.ll_probe_stream(streams, x.data_ptr(), y.data_ptr(), n16, grid,
-                                                                       stream.cuda_stream), "ll_probe_stream"),
-                               steps, warmup, stream)
-            runs.append(dict(grid=grid, ms=round(t["ms"], 4), median_ms=round(t["median_ms"], 4),
-                             gbs=round(nbytes / (t["ms"] * 1e-3) / 1e9, 1)))
-        best = max(runs, key=lambda r: r["gbs"])
-        res[key] = dict(bytes_per_call=nbytes, best_gbs=best["gbs"], best_grid=best["grid"],
-                        frac_of_peak=round(best["gbs"] / PEAK_HBM_GBS, 4), runs=runs)
+        for hints, hk in ((0, "plain"), (3, "nontemporal")):
+            runs = []
+            for grid in (1024, 4096, 16384):
+                _log(f"hbm probe: {key}, {hk}, grid {grid}")
+                t = _time_launches(lambda: _probe_call(lib.ll_probe_stream(streams, hints, x.data_ptr(), y.data_ptr(),
+                                                                           n16, grid, stream.cuda_stream),
+                                                       "ll_probe_stream"), steps, warmup, stream)
+                runs.append(dict(grid=grid, ms=round(t["ms"], 4), median_ms=round(t["median_ms"], 4),
+                                 gbs=round(nbytes / (t["ms"] * 1e-3) / 1e9, 1)))
+            best = max(runs, key=lambda r: r["gbs"])
+            res[f"{key}_{hk}"] = dict(bytes_per_call=nbytes, best_gbs=best["gbs"], best_grid=best["grid"],
+                                      frac_of_peak=round(best["gbs"] / PEAK_HBM_GBS, 4), runs=runs)
     return res
 
 
@@ -611,7 +613,8 @@ def main():
                          "--steps times; prints its own line")
     ap.add_argument("--hbm-probe-mib", type=int, default=0,
                     help="only run the HBM streaming ceiling probes (a copy, and 4 streams read per stream "
-                         "written) over this many MiB per stream, --steps times per grid size; prints its own line")
+                         "written, plain and non-temporal) over this many MiB per stream, --steps times per grid "
+                         "size; prints its own line")
     ap.add_argument("--stream-probe-mib", type=int, default=0,
                     help="only run a streaming reduction that reads 4x and writes 1x this many MiB "
                          "(the read/write mix of linear compression), --steps times; prints its own line")

@@ -43,9 +43,10 @@ int ll_probe_mfma_only(int grid, int iters, const void* operands, float* out, vo
 /* y[i] = x[0][i] ^ x[1][i] ^ ... ^ x[streams-1][i] over n16 16-byte elements
  * per stream: x holds `streams` consecutive arrays of n16 16-byte elements
  * (streams * n16 * 16 bytes read), y holds n16 (n16 * 16 bytes written).
- * streams: 1 (a copy) or 4.  x and y 16-byte aligned, not overlapping.
+ * streams: 1 (a copy) or 4.  hints: bit 0 non-temporal loads, bit 1
+ * non-temporal stores.  x and y 16-byte aligned, not overlapping.
  * grid: workgroups of 256 threads, in [1, 2^20]; n16 >= 0. */
-int ll_probe_stream(int streams, const void* x, void* y, int64_t n16, int grid, void* stream);
+int ll_probe_stream(int streams, int hints, const void* x, void* y, int64_t n16, int grid, void* stream);
 
 #ifdef __cplusplus
 }

@@ -263,15 +263,17 @@ __device__ __forceinline__ void lc_store_group(const LincompKArgs& p, uint16_t* 
 // Staged bf16 Y: the wave's BM x 64 block goes into its own LDS image and
 // back out in whole 128-byte lines, 16 bytes per lane (8 rows of a 64-column
 // segment per store instruction instead of 4 half lines per instruction).
-// The image has 128-byte rows; row q sits at physical row q ^ ((q >> 1) & 1)
-// and its 16-byte chunk c at c ^ (((q >> 2) & 1) << 2).  A pair write covers
-// rows 8k + {0,2,4,6} (or {1,3,5,7}) x 64 bytes and lands on all 64 banks
-// once; a 16-byte read of 16 lanes covers two whole rows of opposite bank
-// halves.  Each wave only reads back what it wrote, in order, so no barrier
-// is needed; the next candidate's writes follow this one's reads in the same
-// wave.
+// The image has 128-byte rows; row q sits at physical row q ^ ((q >> 2) & 1)
+// and its 16-byte chunk c at c ^ (((q >> 1) & 1) << 2).  A pair write covers
+// rows 8k + {0,2,4,6} (or {1,3,5,7}) x 64 bytes: the four land in four
+// different 64-byte bank windows of 256 bytes, and the two rows of each half
+// wave in different halves of 128 bytes, so neither a 64-bank nor a 32-bank
+// pass conflicts; a 16-byte read covers whole rows, two adjacent ones of
+// opposite parity per 16 lanes.  Each wave only reads back what it wrote, in
+// order, so no barrier is needed; the next candidate's writes follow this
+// one's reads in the same wave.
 __device__ __forceinline__ uint32_t lc_img_off(int q, int cb) {
-  return (uint32_t)(((q ^ ((q >> 1) & 1)) << 7) + ((((cb >> 4) ^ (((q >> 2) & 1) << 2))) << 4) + (cb & 15));
+  return (uint32_t)(((q ^ ((q >> 2) & 1)) << 7) + ((((cb >> 4) ^ (((q >> 1) & 1) << 2))) << 4) + (cb & 15));
 }
 
 // One group of staged values: v0..v3 of rows q%4 = 0..3 at this lane's

@@ -54,36 +54,57 @@ void mfma_only_kernel(int iters, const uint4* __restrict__ frag, float* out) {
 }
 
 // Grid-stride over n16 elements, U elements per thread per pass with all of
-// a pass's loads issued before its stores.
-template <int S>
-__global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
+// a pass's loads issued before its stores; NT: bit 0 non-temporal loads, bit 1
+// non-temporal stores.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int S, int NT>
+__global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ x, u32x4* __restrict__ y,
                                                      int64_t n16) {
   constexpr int U = 4;
   const int64_t step = (int64_t)gridDim.x * 256 * U;
   for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += step) {
-    uint4 v[U][S];
+    u32x4 v[U][S];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * 256;
 #pragma unroll
-      for (int s = 0; s < S; ++s) v[u][s] = i < n16 ? x[s * n16 + i] : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < S; ++s) {
+        if (i < n16) {
+          if constexpr (NT & 1)
+            v[u][s] = __builtin_nontemporal_load(x + s * n16 + i);
+          else
+            v[u][s] = x[s * n16 + i];
+        } else {
+          v[u][s] = u32x4{0, 0, 0, 0};
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * 256;
       if (i < n16) {
-        uint4 r = v[u][0];
+        u32x4 r = v[u][0];
 #pragma unroll
-        for (int s = 1; s < S; ++s) {
-          r.x ^= v[u][s].x;
-          r.y ^= v[u][s].y;
-          r.z ^= v[u][s].z;
-          r.w ^= v[u][s].w;
-        }
-        y[i] = r;
+        for (int s = 1; s < S; ++s) r ^= v[u][s];
+        if constexpr (NT & 2)
+          __builtin_nontemporal_store(r, y + i);
+        else
+          y[i] = r;
       }
     }
   }
+}
+
+template <int S>
+hipError_t launch_stream(int hints, const u32x4* x, u32x4* y, int64_t n16, int grid, hipStream_t st) {
+  switch (hints) {
+    case 0: stream_kernel<S, 0><<<grid, 256, 0, st>>>(x, y, n16); break;
+    case 1: stream_kernel<S, 1><<<grid, 256, 0, st>>>(x, y, n16); break;
+    case 2: stream_kernel<S, 2><<<grid, 256, 0, st>>>(x, y, n16); break;
+    default: stream_kernel<S, 3><<<grid, 256, 0, st>>>(x, y, n16); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -95,18 +116,17 @@ extern "C" int ll_probe_mfma_only(int grid, int iters, const void* operands, flo
   return (int)hipGetLastError();
 }
 
-extern "C" int ll_probe_stream(int streams, const void* x, void* y, int64_t n16, int grid, void* stream) {
-  if ((streams != 1 && streams != 4) || n16 < 0 || grid < 1 || grid > (1 << 20)) return -1;
+extern "C" int ll_probe_stream(int streams, int hints, const void* x, void* y, int64_t n16, int grid, void* stream) {
+  if ((streams != 1 && streams != 4) || hints < 0 || hints > 3 || n16 < 0 || grid < 1 || grid > (1 << 20))
+    return -1;
   if (n16 == 0) return 0;
   if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return -1;
   const uintptr_t xb = (uintptr_t)x, xe = xb + (uintptr_t)(streams * n16 * 16);
   const uintptr_t yb = (uintptr_t)y, ye = yb + (uintptr_t)(n16 * 16);
   if (xb < ye && yb < xe) return -1;
-  const uint4* xp = (const uint4*)x;
-  uint4* yp = (uint4*)y;
-  if (streams == 1)
-    stream_kernel<1><<<grid, 256, 0, (hipStream_t)stream>>>(xp, yp, n16);
-  else
-    stream_kernel<4><<<grid, 256, 0, (hipStream_t)stream>>>(xp, yp, n16);
-  return (int)hipGetLastError();
+  const u32x4* xp = (const u32x4*)x;
+  u32x4* yp = (u32x4*)y;
+  const hipError_t e = streams == 1 ? launch_stream<1>(hints, xp, yp, n16, grid, (hipStream_t)stream)
+                                    : launch_stream<4>(hints, xp, yp, n16, grid, (hipStream_t)stream);
+  return (int)e;
 }

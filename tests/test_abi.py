@@ -168,8 +168,8 @@ PROBE_LIB = os.path.join(ROOT, "recsys_linear_layers_amd", "libllprobes.so")
 def _probe_lib():
     lib = ctypes.CDLL(PROBE_LIB)
     lib.ll_probe_mfma_only.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                    ctypes.c_void_p]
+    lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -188,9 +188,10 @@ def test_probes_reject_bad_arguments_on_the_host():
     assert lib.ll_probe_mfma_only(1, -1, None, 256, None) == -1    # iters < 0
     assert lib.ll_probe_mfma_only(1, 10, None, None, None) == -1   # no output
     assert lib.ll_probe_mfma_only(1, 10, 4100, 256, None) == -1    # misaligned operands
-    assert lib.ll_probe_stream(2, 4096, 1 << 20, 16, 1, None) == -1  # streams not 1 or 4
-    assert lib.ll_probe_stream(1, 4096, 1 << 20, -1, 1, None) == -1  # n16 < 0
-    assert lib.ll_probe_stream(1, 4096, 1 << 20, 16, 0, None) == -1  # grid < 1
-    assert lib.ll_probe_stream(1, 4100, 1 << 20, 16, 1, None) == -1  # misaligned x
-    assert lib.ll_probe_stream(4, 4096, 4096 + 16 * 16, 16, 1, None) == -1  # y inside x
-    assert lib.ll_probe_stream(1, None, None, 0, 1, None) == 0     # nothing to do
+    assert lib.ll_probe_stream(2, 0, 4096, 1 << 20, 16, 1, None) == -1  # streams not 1 or 4
+    assert lib.ll_probe_stream(1, 4, 4096, 1 << 20, 16, 1, None) == -1  # unknown hint bits
+    assert lib.ll_probe_stream(1, 0, 4096, 1 << 20, -1, 1, None) == -1  # n16 < 0
+    assert lib.ll_probe_stream(1, 0, 4096, 1 << 20, 16, 0, None) == -1  # grid < 1
+    assert lib.ll_probe_stream(1, 0, 4100, 1 << 20, 16, 1, None) == -1  # misaligned x
+    assert lib.ll_probe_stream(4, 3, 4096, 4096 + 16 * 16, 16, 1, None) == -1  # y inside x
+    assert lib.ll_probe_stream(1, 3, None, None, 0, 1, None) == 0     # nothing to do
