@@ -51,6 +51,8 @@ BAR_AFTER = 0       # MFMAs of step 3 issued before the load wait and barrier
 L3 = 6              # loads of slice j+2 issued in step 3 of slice j; the rest go to steps 0..2 of slice j+1
 CARRY_STEPS = 2     # how many of steps 0..2 of slice j+1 share the rest
 CARRY_SPAN = 14     # MFMAs over which a step's reads and carried loads are spread
+B_FIRST = 0         # load order within a slice: 0 A0, B0, A1, B1, ...; 1 B0, A0, B1, A1, ...
+CARRY_BLOCKS = 0    # 0: step k takes every CARRY_STEPS-th carried load; 1: contiguous runs of them
 SLOT = 65536
 B_OFF = 32768
 
@@ -93,13 +95,15 @@ def reads(slot, kk, buf):
 
 
 def loads(slot):
-    """The wave's 16 direct-to-LDS loads of one slice into `slot` (M0 set per load)."""
+    """The wave's 16 direct-to-LDS loads of one slice into `slot` (M0 set per
+    load), A and B alternating, the first of each pair per B_FIRST."""
     out = []
     for i in range(8):
-        out.append([f"s_add_u32 m0, %[ldsw], {slot * SLOT + i * 4096}", "s_nop 0",
-                    f"buffer_load_dwordx4 %[va{i}], s[88:91], 0 offen lds"])
-        out.append([f"s_add_u32 m0, %[ldsw], {slot * SLOT + B_OFF + i * 4096}", "s_nop 0",
-                    f"buffer_load_dwordx4 %[vb{i}], s[92:95], 0 offen lds"])
+        a = [f"s_add_u32 m0, %[ldsw], {slot * SLOT + i * 4096}", "s_nop 0",
+             f"buffer_load_dwordx4 %[va{i}], s[88:91], 0 offen lds"]
+        b = [f"s_add_u32 m0, %[ldsw], {slot * SLOT + B_OFF + i * 4096}", "s_nop 0",
+             f"buffer_load_dwordx4 %[vb{i}], s[92:95], 0 offen lds"]
+        out += [b, a] if B_FIRST else [a, b]
     return out
 
 
@@ -132,7 +136,11 @@ def carried(slot, kk):
     them (every path through a slice advances them exactly once)."""
     rest = loads(1 - slot)[L3:]
     assert rest and 1 <= CARRY_STEPS <= 3
-    per = [rest[k::CARRY_STEPS] for k in range(CARRY_STEPS)] + [[]] * (3 - CARRY_STEPS)
+    if CARRY_BLOCKS:
+        cut = [len(rest) * k // CARRY_STEPS for k in range(CARRY_STEPS + 1)]
+        per = [rest[cut[k]:cut[k + 1]] for k in range(CARRY_STEPS)] + [[]] * (3 - CARRY_STEPS)
+    else:
+        per = [rest[k::CARRY_STEPS] for k in range(CARRY_STEPS)] + [[]] * (3 - CARRY_STEPS)
     last = max(k for k in range(3) if per[k])
     return per[kk] + ([ADVANCE] if kk == last else [])
 
@@ -243,7 +251,8 @@ def main():
         for j in range(4):
             parts.append(f"#define LL_SQ4_READ_ACC_{i}_{j} \\\n" + read_acc(i, j) + "\n")
     parts.append(f"// loads of a slice issued after the barrier of the slice two before; the\n"
-                 f"// prologue issues this many of slice 1\n#define LL_SQ4_L3 {L3}\n")
+                 f"// prologue issues this many of slice 1\n#define LL_SQ4_L3 {L3}\n"
+                 f"// the loads of a slice alternate A and B, B first if 1\n#define LL_SQ4_B_FIRST {B_FIRST}\n")
     parts.append("#define LL_SQ4_CLOBBERS " + clobbers() + "\n")
     text = "\n".join(parts)
     with open(OUT, "w") as f:

@@ -54,7 +54,7 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
     pending, completed, visible = set(), set(), set()
     # prologue (C++): slice 0 whole and the first L3 loads of slice 1 (order
     # A0, B0, A1, B1, ...), then a wait for all of them and a barrier
-    order = [("A", k // 2) if k % 2 == 0 else ("B", k // 2) for k in range(16)]
+    order = [("A" if (k % 2 == 0) != bool(g.B_FIRST) else "B", k // 2) for k in range(16)]
     issued[0] = set(PIECES)
     if n > 1:
         issued[1] = set(order[:g.L3])
@@ -152,7 +152,9 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
     assert a_off // 128 == b_adv and b_adv in (n, n + 1) or n <= 2
 
 
-SPLITS = [dict(L3=16)] + [dict(L3=l3, CARRY_STEPS=c) for l3 in (12, 10, 8, 6, 4) for c in (1, 2, 3)]
+SPLITS = [dict(L3=16)] + [dict(L3=l3, CARRY_STEPS=c) for l3 in (12, 10, 8, 6, 4) for c in (1, 2, 3)] + \
+         [dict(L3=l3, CARRY_STEPS=c, B_FIRST=b, CARRY_BLOCKS=k) for l3 in (8, 6, 4) for c in (2, 3)
+          for b in (0, 1) for k in (0, 1) if b or k]
 
 
 @pytest.mark.parametrize("params", SPLITS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
