@@ -274,8 +274,14 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     if (op.pack) return (op.pack_mn ? d->K : rows) * op.ldp * 2;
     return (op.kmajor ? (rows - 1) * op.ld + d->K : (d->K - 1) * op.ld + rows) * 2;
   };
-  const bool sq4_fits = p.a.kmajor && !p.b.kmajor && d->K % 64 == 0 && span_bytes(p.a, M) < 0x7FFFFFF0ll &&
-                        span_bytes(p.b, N) < 0x7FFFFFF0ll;
+  // The hand-ordered kind loads whole 64-deep slices with no k mask.  With K
+  // not a multiple of 64 that is still exact when A is a packed copy (zero
+  // columns up to ldp, K rounded up to 64): the last slice's B rows past K
+  // lie beyond B's descriptor range and read as zeros, and they meet A's
+  // zero columns.  A read in place would meet them with its next row's
+  // values, and an Inf or NaN there would reach C.
+  const bool sq4_fits = p.a.kmajor && !p.b.kmajor && (d->K % 64 == 0 || p.a.pack) &&
+                        span_bytes(p.a, M) < 0x7FFFFFF0ll && span_bytes(p.b, N) < 0x7FFFFFF0ll;
   if (free_choice && p.a.kmajor && (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
     const int64_t pb = passes(kind), pt = passes(KIND_T192_PC);
     const KindInfo& kb = kind_info(kind);
@@ -353,7 +359,8 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     // or packed) in whole 64-deep slices.
     if (kind == KIND_SQ4_HO && !sq4_fits)
       return fail(LL_ERR_UNSUPPORTED,
-                  "kernel %s needs A K-contiguous, B N-contiguous, K a multiple of 64 and operands below 2 GB",
+                  "kernel %s needs A K-contiguous, B N-contiguous, K a multiple of 64 (or A packed) and operands "
+                  "below 2 GB",
                   kv.name);
   }
   p.kind = kind;

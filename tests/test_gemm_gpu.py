@@ -204,6 +204,7 @@ def test_descriptor_rebase_past_1gib():
 
 
 @pytest.mark.parametrize("M,N,K,kind", [(384, 520, 1017, None), (2048, 2048, 4095, "KIND_SQ8_LW4"),
+                                        (2048, 2048, 4095, "KIND_SQ4_HO"), (1000, 1032, 2043, "KIND_SQ4_HO"),
                                         (1000, 1032, 2043, "KIND_WIDE_PC"), (520, 1032, 1982, "KIND_TALL_PC"),
                                         (1000, 1032, 2044, "KIND_T192_PC"), (520, 264, 1021, "KIND_WIDE_COOP")])
 def test_packed_a_with_direct_b_reads_no_row_past_k(M, N, K, kind, monkeypatch):

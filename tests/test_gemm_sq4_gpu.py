@@ -76,6 +76,18 @@ def test_packed_a(monkeypatch):
     acceptance.assert_close(got, ref, S, "f32", d)
 
 
+@pytest.mark.parametrize("M,N,K,lda", [(520, 264, 1091, 1093), (300, 776, 200, 201), (256, 256, 72, 73)])
+def test_k_tail_with_packed_a(M, N, K, lda, monkeypatch):
+    """K not a multiple of 64 with an A whose odd row stride makes the plan
+    pack it (zero columns up to K rounded to 64): the last slice reads B rows
+    past K as zeros through the descriptor range."""
+    c = synth.gemm_case(M, N, K, seed=M + N + K + 11, lda=lda, out_dtype="bf16", dist=("normal", 0.0, 1.0))
+    got, d = _run(c, monkeypatch)
+    assert "packA=1" in d, d
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(got, ref, S, "bf16", f"k tail {M}x{N}x{K} lda={lda} {d}")
+
+
 def test_refused_where_it_does_not_apply(monkeypatch):
     import torch
     import recsys_linear_layers_amd as ll
