@@ -572,8 +572,14 @@ def time_leg(name: str, p: dict, steps: int, warmup: int) -> tuple[dict, dict]:
                     value=round(x["req_s"], 1), unit="requests/s", hbm_gbs=round(x["gbs"], 1),
                     hbm_frac=round(x["gbs"] / PEAK_HBM_GBS, 4)), x
     x = time_gemm(p, steps, warmup)
+    c = x["case"]
+    # compulsory bytes: A and B read once, C written once (the bound of the
+    # skinny split-K shape, whose arithmetic intensity is under the ridge)
+    cb = c.M * c.K * 2 + c.K * c.N * 2 + c.M * c.N * {"bf16": 2, "f16": 2, "f32": 4}[c.out_dtype]
+    gbs = cb / (x["kernel_ms"] * 1e-3) / 1e9
     entry = dict(workload=name, ms=round(x["kernel_ms"], 4), median_ms=round(x["median_ms"], 4),
                  value=round(x["tflops"], 1), unit="TFLOP/s", mfma_frac=round(x["tflops"] / PEAK_BF16_TFLOPS, 4),
+                 compulsory_bytes=cb, hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
                  plan=x["plan"])
     if name in TILE_RULE_NAMES:
         y = time_gemm(p, steps, warmup, TILE_RULE_NAMES[name])
