@@ -221,14 +221,26 @@ __device__ __forceinline__ void lc_issue(const LincompKArgs& p, const LcPos& s, 
                                                                        lane, vb);
 }
 
-// Bias of the four compressed rows m .. m+3 (m a multiple of 4; Mo is a
-// multiple of 8, so the four are all in range or all out), one 16-byte load;
-// zeros without a bias.
+// Bias of the four compressed rows of a lane's group: rows m8 + 4 half ..
+// + 3, where m8 (a multiple of 8, uniform over the wave) is the group's first
+// row and half = lane / 32; zeros without a bias.  The eight values of rows
+// m8 .. m8 + 7 come through scalar loads (the address is wave-uniform and the
+// bias is read-only): a vector load here would count with the wave's Y
+// stores, and waiting for it would wait for every store issued before it.
+// Mo is a multiple of 8, so the eight rows are all in range or all out.
 template <bool BIAS>
-__device__ __forceinline__ f32x4 lc_bias4(const LincompKArgs& p, int m) {
+__device__ __forceinline__ f32x4 lc_bias4(const LincompKArgs& p, int m8, int half) {
   f32x4 b = {0.f, 0.f, 0.f, 0.f};
   if constexpr (BIAS) {
-    if (m < p.Mo) b = *(const f32x4*)(p.bias + m);
+    if (m8 < p.Mo) {
+      typedef const float __attribute__((address_space(4)))* cptr;
+      const cptr q = (cptr)(p.bias + m8);
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = q[k];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[r] = half ? v[4 + r] : v[r];
+    }
   }
   return b;
 }
@@ -353,7 +365,7 @@ __device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& 
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 b = lc_bias4<Cfg::BIAS>(p, mb + 32 * i + 8 * g);
+        const f32x4 b = lc_bias4<Cfg::BIAS>(p, s.m0 * Cfg::BM + 32 * i + 8 * g, lane >> 5);
         const uint32_t ro = (32 * i + 8 * g) * 128;
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) {
@@ -390,7 +402,7 @@ __device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& 
       for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 b = lc_bias4<Cfg::BIAS>(p, mb + 32 * i + 8 * g);
+          const f32x4 b = lc_bias4<Cfg::BIAS>(p, s.m0 * Cfg::BM + 32 * i + 8 * g, lane >> 5);
 #pragma unroll
           for (int j = 0; j < Cfg::FN; ++j)
             lc_store_group(p, Y, loff + (32 * i + 8 * g) * sym + 32 * j, sym, r0 + 32 * i + 8 * g, d + 32 * j, odd,
@@ -405,7 +417,7 @@ __device__ __forceinline__ void lc_epilogue(const LincompKArgs& p, const LcPos& 
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 b = lc_bias4<Cfg::BIAS>(p, mb + 32 * i + 8 * g);
+        const f32x4 b = lc_bias4<Cfg::BIAS>(p, s.m0 * Cfg::BM + 32 * i + 8 * g, lane >> 5);
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j)
 #pragma unroll
