@@ -57,6 +57,7 @@ struct OperandArgs {
   int32_t rows;         // extent along M (A) or N (B)
   int32_t kvalid;       // k extent holding data; K-major operands: a multiple of 8
   int64_t extent;       // elements addressable from ptr (clamps num_records)
+  int32_t once;         // each element is loaded by one work item only (non-temporal loads)
 };
 
 struct GemmKArgs {
@@ -409,9 +410,20 @@ struct Loader {
     // copy (zero columns up to K rounded to 8) and the other is read in place
     // (exactly K): the unmasked path is taken only where both hold the slice.
     const bool fast = rows_in && k0 + Cfg::KT <= min(p.a.kvalid, p.b.kvalid);
-    load_tile<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR, Cfg::LOADERS>(p.a, a, fast, m0, k0, slot, lw, lane, va);
-    load_tile<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR, Cfg::LOADERS>(p.b, bo, fast, n0, k0, slot + Cfg::A_BYTES, lw,
-                                                              lane, vb);
+    // an operand read by one work item only (one tile row or column) is
+    // streamed with the non-temporal hint, so it does not push reused data
+    // out of L2 (uniform branch)
+    if (p.a.once)
+      load_tile<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR, Cfg::LOADERS, OpStream, true>(p.a, a, fast, m0, k0, slot, lw, lane,
+                                                                             va);
+    else
+      load_tile<Cfg::BM, Cfg::KT, Cfg::A_KMAJOR, Cfg::LOADERS>(p.a, a, fast, m0, k0, slot, lw, lane, va);
+    if (p.b.once)
+      load_tile<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR, Cfg::LOADERS, OpStream, true>(p.b, bo, fast, n0, k0,
+                                                                             slot + Cfg::A_BYTES, lw, lane, vb);
+    else
+      load_tile<Cfg::BN, Cfg::KT, Cfg::B_KMAJOR, Cfg::LOADERS>(p.b, bo, fast, n0, k0, slot + Cfg::A_BYTES, lw,
+                                                                lane, vb);
   }
 
   __device__ __forceinline__ void advance(const GemmKArgs& p, int stride) {

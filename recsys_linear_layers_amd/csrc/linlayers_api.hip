@@ -568,6 +568,9 @@ static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B,
   k.tiles_n = p->tiles_n;
   k.group_m = p->group_m;
   k.total = p->total;
+  // an operand that only one row (column) of tiles reads is loaded once
+  k.a.once = p->tiles_n == 1;
+  k.b.once = p->tiles_m == 1;
   if (p->splits > 1) {
     k.partial = (float*)((char*)ws + p->ws_partial_off);
   } else {
