@@ -83,6 +83,33 @@ def test_random_case_hand_ordered_kind(i, monkeypatch):
         ll._plans.clear()
 
 
+N_SQ4_TAIL = 30
+
+
+@pytest.mark.parametrize("i", range(N_SQ4_TAIL))
+def test_random_case_hand_ordered_k_tail(i, monkeypatch):
+    """The hand-ordered kind forced on random cases whose K is not a multiple
+    of 64, with A packed (it reads whole 64-deep slices, which is exact only
+    against a packed A's zero columns).  Sizes reach past four tiles so that
+    interior tiles take the staged epilogue when N allows 16-byte rows; bias
+    and activation as drawn."""
+    import recsys_linear_layers_amd as ll
+    d = _draw(N_CASES + N_SQUARE + N_SQ4 + i)
+    rng = np.random.default_rng(7000 + i)
+    d["M"] = int(rng.integers(1, 1100))
+    d["N"] = 8 * int(rng.integers(1, 138)) if rng.random() < 0.6 else int(rng.integers(1, 1100))
+    d["K"] = 64 * int(rng.integers(0, 9)) + int(rng.integers(1, 64))
+    d["a_col"], d["b_col"] = False, False
+    d["flags"] = ll.LL_FLAG_PACK_A
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
+    try:
+        _check(N_CASES + N_SQUARE + N_SQ4 + i, d, want_kind="KIND_SQ4_HO")
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+
+
 def _check(i, d, want_kind=None):
     import torch
     import recsys_linear_layers_amd as ll
