@@ -258,6 +258,16 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(void* __restrict__ C, in
   }
 }
 
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt, const float* bias,
                             int act, hipStream_t stream) {
   const int64_t total = M * N;

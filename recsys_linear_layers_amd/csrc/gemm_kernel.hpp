@@ -73,6 +73,9 @@ struct GemmKArgs {
   int32_t splits, kiters, kps;  // kiters, kps in units of KT
   int32_t tiles_m, tiles_n, group_m;
   int32_t total;
+  // Hand-ordered kind only: per-XCD round counters (8 x 32 words, zeroed
+  // before the launch), or null for no round barrier.
+  uint32_t* sync;
 };
 
 template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,

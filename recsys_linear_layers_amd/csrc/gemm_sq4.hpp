@@ -34,6 +34,10 @@ struct Sq4 {
   static constexpr int SLOT = 65536, B_OFF = 32768, LDS = 2 * SLOT;
 };
 
+// Longest wait at a round barrier, in ticks of the 100 MHz clock (30 us; the
+// drift it corrects is a few us per round).
+constexpr uint64_t kSyncWaitTicks = 3000;
+
 // One 32x32 accumulator block, as the shared epilogue code sees a tile of one
 // block (the interior test uses the whole 256x256 tile).  EPI: 0 plain, else
 // the per-column bias (if given) and activation EPI-1 on every sum before it
@@ -224,7 +228,30 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
   const int lda = (int)p.a.ld, ldb = (int)p.b.ld;
   const uint32_t incb = 64u * 2u * (uint32_t)ldb;
 
-  for (int t = first; t < p.total; t += stride) {
+  // Round barrier per XCD.  Work item t runs in round (t - first) / stride,
+  // and the 32 workgroups of an XCD share panels only within a round.  Left
+  // alone they drift apart by up to a whole tile over many rounds, and then
+  // each fetches its panels' slices past L2 for itself.  So a workgroup
+  // counts itself in after its k-loop and, before the next round's first
+  // loads, waits until every workgroup of its XCD has done the same.  The
+  // wait is bounded (kSyncWaitTicks of the 100 MHz clock), so a workgroup
+  // that is not resident costs time but never blocks; the counts change no
+  // arithmetic.
+  uint32_t* const cnt = p.sync ? p.sync + (blockIdx.x & 7) * 32 : nullptr;
+  const uint32_t per_xcd = gridDim.x >> 3;
+  uint32_t round = 0;
+  for (int t = first; t < p.total; t += stride, ++round) {
+    if (cnt && round > 0) {
+      if (wave == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while ((uint32_t)__builtin_amdgcn_readfirstlane(
+                   (int)__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < per_xcd * round) {
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncWaitTicks) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      lds_barrier();
+    }
     const TileInfo ti = decode_tile<Sq4>(p, t);
     int n = ti.ke - ti.kb;
     uint32_t va[8], vb[8];
@@ -275,6 +302,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
 #undef LL_SQ4_OPERANDS
 
     lds_barrier();  // every wave is done reading the ring before it is reused
+    if (cnt && wave == 0 && lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // a whole tile inside a 16-bit row-major C with 16-byte aligned rows:
     // staged through LDS (uniform over the workgroup)
     const bool staged = p.c_fast && p.c_fmt != 0 && ti.m0 + Sq4::BM <= p.M && ti.n0 + Sq4::BN <= p.N &&

@@ -77,6 +77,16 @@ ll_status current_device(int* dev, const DeviceInfo** info) {
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The hand-ordered kind's round counters: one per XCD, 128 bytes apart.
+constexpr int kRoundSyncWords = 8 * 32;
+// Fewest rounds (passes of the persistent grid over its tiles) for which the
+// plan turns the round barrier on.  Measured with and without it, same
+// process: FFN-up (28 rounds) +2.2%, the same with bias + GELU +0.1%,
+// 16384^2 x 4096 (16) +0.1%; 8 rounds and fewer -0.1 to -0.8% (8192^2 x
+// 1024, 4 short rounds, the most).  The drift it removes builds up over
+// many rounds.
+constexpr int kRoundSyncMinRounds = 20;
+
 // Byte extent [lo, hi) touched by a 2-D strided view of `rows` x `cols` elements.
 struct Span {
   uintptr_t lo, hi;
@@ -114,7 +124,9 @@ struct gemm_plan {
   int epi;          // fused-epilogue instantiation (0: none, or the split-K reduce applies it)
   int kiters, kps;
   int tiles_m, tiles_n, total, grid, group_m;
+  int round_sync;   // hand-ordered kind: round barrier per XCD (counters in the workspace)
   size_t ws_partial_off;
+  size_t ws_sync_off;
   size_t ws_bytes;
 };
 
@@ -390,6 +402,17 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   p.grid = (int)(p.total < slots ? p.total : slots);
   if (p.grid < 1) p.grid = 1;
   p.group_m = 8;
+  // Round barrier per XCD for the hand-ordered kind (gemm_sq4.hpp): on
+  // FFN-up (28 rounds of 256 tiles) it cut the bytes fetched past L2 from
+  // 16.9 to 12.1 GB and the time by 2.2-2.3%.  It needs the grid to be whole
+  // XCDs (the work-item remap) and many rounds (kRoundSyncMinRounds).
+  // LL_GEMM_ROUND_SYNC=0 / 1 overrides the choice (measurement).
+  {
+    const int rounds = p.grid > 0 ? (p.total + p.grid - 1) / p.grid : 0;
+    p.round_sync = kind == KIND_SQ4_HO && p.grid % 8 == 0 && rounds >= kRoundSyncMinRounds;
+    if (const char* env = getenv("LL_GEMM_ROUND_SYNC"))
+      p.round_sync = env[0] == '1' && kind == KIND_SQ4_HO && p.grid % 8 == 0 && rounds >= 2;
+  }
 
   size_t off = 0;
   if (p.a.pack) {
@@ -402,6 +425,8 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   }
   p.ws_partial_off = off;
   if (splits > 1) off = align256(off + (size_t)splits * M * N * 4);
+  p.ws_sync_off = off;
+  if (p.round_sync) off = align256(off + kRoundSyncWords * 4);
   p.ws_bytes = off;
 
   gemm_plan* h = new (std::nothrow) gemm_plan(p);
@@ -423,9 +448,9 @@ ll_status gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
                                "A:M-major,B:N-major"};
   snprintf(buf, len,
            "kernel=%s tile=%dx%d layout=%s packA=%d packB=%d tiles=%dx%d splitk=%d kiters=%d grid=%d cus=%d "
-           "group_m=%d ws=%zu epilogue=0x%x fused=%d",
+           "group_m=%d ws=%zu epilogue=0x%x fused=%d round_sync=%d",
            k.name, k.bm, k.bn, lay[p->layout], (int)p->a.pack, (int)p->b.pack, p->tiles_m, p->tiles_n, p->splits,
-           p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes, p->d.epilogue, p->epi);
+           p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes, p->d.epilogue, p->epi, p->round_sync);
   return ok();
 }
 
@@ -579,6 +604,11 @@ static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B,
     k.ldcn = d.stride_cn;
     k.c_fast = d.stride_cn == 1 && d.stride_cm % 2 == 0 && ((uintptr_t)C & 3) == 0 &&
                d.stride_cm * (d.M + 256) < (1ll << 31);
+  }
+  if (p->round_sync) {
+    k.sync = (uint32_t*)((char*)ws + p->ws_sync_off);
+    e = launch_clear_words(k.sync, kRoundSyncWords, st);
+    if (e != hipSuccess) return hip_fail(e, "round counter clear launch");
   }
   e = p->epi ? launch_gemm_epi(p->layout, p->kind, d.a_type == LL_F16, p->epi, k, p->grid, st)
              : launch_gemm(p->layout, p->kind, d.a_type == LL_F16, k, p->grid, st);

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import gemm_operands, lincomp_operands, to_f64
+from helpers import gemm_operands, lincomp_operands, strip_starts, to_f64
 from oracle import acceptance
 
 pytestmark = pytest.mark.gpu
@@ -125,3 +125,33 @@ def test_plan_describe_reports_the_choice():
     assert "kernel=KIND_SQ4_HO" in d and "splitk=1" in d
     d = ll.plan_for(A, A, C, 0, ll.LL_EPI_GELU).describe()
     assert "fused=3" in d and "kernel=KIND_SQ4_HO" in d
+
+
+def test_round_barrier_plans_on_two_streams(monkeypatch):
+    """Two hand-ordered GEMMs with round barriers at once, on two streams: the
+    second kernel's workgroups wait for CUs the first holds, so their round
+    waits may run out.  The wait is bounded and changes no arithmetic: both
+    results equal a run alone."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    M, N, K = 8192, 8192, 512
+    c = synth.gemm_case(M, N, K, seed=99, out_dtype="bf16", dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    outs = [torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "1")
+    plan = ll.GemmPlan(ll.gemm_desc_for(A, B, outs[0]), A.device)
+    monkeypatch.delenv("LL_GEMM_ROUND_SYNC")
+    assert "kernel=KIND_SQ4_HO " in plan.describe() and "round_sync=1" in plan.describe(), plan.describe()
+    plan.run(A, B, outs[2])
+    torch.cuda.synchronize()
+    wss = [torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        for C, ws, st in zip(outs[:2], wss, streams):
+            ll.gemm_run(plan.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), ws.data_ptr(), plan.ws_bytes,
+                        st.cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[2])
+    for r0, nr in strip_starts(M, 64, 100):
+        ref, S = oracle.gemm_case(c, rows=(r0, nr))
+        acceptance.assert_close(to_f64(outs[2][r0:r0 + nr]), ref, S, "bf16", f"rows {r0}..")

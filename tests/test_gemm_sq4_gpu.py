@@ -249,3 +249,76 @@ def test_staged_epilogue_needs_16_byte_aligned_c(monkeypatch):
     assert np.array_equal(to_f64(C1), to_f64(C2))
     ref, S = oracle.gemm_case(c)
     acceptance.assert_close(to_f64(C1), ref, S, "bf16", "aligned C")
+
+
+def test_round_barrier_selection(monkeypatch):
+    """Plans of the hand-ordered kind with 20 rounds of tiles or more keep
+    each XCD's workgroups a round apart at most (round_sync=1), with their
+    counters in the workspace; fewer rounds and other kinds do not, and the
+    override turns it on from two rounds or off."""
+    import recsys_linear_layers_amd as ll
+    for M, N, K in [(16384, 28672, 8192), (16384, 20480, 1024)]:       # 28 and 20 rounds
+        d = _describe(M, N, K)
+        assert f"kernel={KIND} " in d and "round_sync=1" in d, d
+        assert int(d.split(" ws=")[1].split()[0]) >= 1024, d
+    for M, N, K in [(4096, 4096, 4096), (16384, 8192, 28672), (8192, 8192, 8192), (16384, 16384, 4096)]:
+        d = _describe(M, N, K)                                         # 1, 8, 4 and 16 rounds
+        assert f"kernel={KIND} " in d and "round_sync=0" in d and " ws=0 " in d, d
+    d = _describe(16384, 28672, 8192, b_col=True)                      # another kind
+    assert f"kernel={KIND} " not in d and "round_sync=0" in d, d
+    monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "0")
+    d = _describe(16384, 28672, 8192)
+    assert "round_sync=0" in d and " ws=0 " in d, d
+    monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "1")
+    assert "round_sync=1" in _describe(8192, 8192, 1024)
+    assert "round_sync=0" in _describe(4096, 4096, 4096)              # still needs two rounds
+
+
+def _run_sync(A, B, C, sync, monkeypatch, bias=None, act=None):
+    import torch
+    import recsys_linear_layers_amd as ll
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "1" if sync else "0")
+    monkeypatch.setenv("LL_GEMM_KIND", KIND)
+    try:
+        ll.gemm(A, B, out=C, bias=bias, act=act)
+        torch.cuda.synchronize()
+        ep = (ll.LL_EPI_BIAS if bias is not None else 0) | ll.ACTIVATIONS[act]
+        d = ll.plan_for(A, B, C, 0, ep).describe()
+    finally:
+        monkeypatch.delenv("LL_GEMM_ROUND_SYNC", raising=False)
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+    assert f"kernel={KIND} " in d and f"round_sync={int(sync)}" in d, d
+    return d
+
+
+@pytest.mark.parametrize("act", [None, "gelu"])
+def test_round_barrier_changes_no_bits(act, monkeypatch):
+    """The round barrier only delays loads: with and without it the bits are
+    the same.  8192 x 8704: 32 x 34 = 1088 tiles, four full rounds and a
+    fifth of 64 tiles; checked against the oracle on 64-row strips and
+    samples, plain and with bias + GELU."""
+    import torch
+    M, N, K = 8192, 8704, 256
+    c = synth.gemm_case(M, N, K, seed=95 + (act is None), out_dtype="bf16", dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    bias = None
+    if act:
+        bias = torch.from_numpy(np.random.default_rng(96).standard_normal(N).astype(np.float32)).cuda()
+    C1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    C2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d1 = _run_sync(A, B, C1, True, monkeypatch, bias, act)
+    _run_sync(A, B, C2, False, monkeypatch, bias, act)
+    assert torch.equal(C1, C2), d1
+    got = to_f64(C1)
+    rows, cols = sample_indices(M, N, 2048, 97, tile=(256, 256))
+    ref, S = oracle.gemm_case_entries(c, rows, cols)
+    if act:
+        ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act, cols=cols)
+    acceptance.assert_close(got[rows, cols], ref, S, "bf16", f"samples {d1}", act=act)
+    for r0, nr in strip_starts(M, 64, 98)[:3]:
+        ref, S = oracle.gemm_case(c, rows=(r0, nr))
+        if act:
+            ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+        acceptance.assert_close(got[r0:r0 + nr], ref, S, "bf16", f"rows {r0}.. {d1}", act=act)
