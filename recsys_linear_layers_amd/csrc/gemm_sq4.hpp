@@ -14,14 +14,16 @@
 // idles the matrix unit.  The k-loop is therefore one inline-asm statement
 // (gemm_sq4_loop.inc, written by gen_sq4_loop.py) that fixes the position of
 // each wait, fragment read, direct-to-LDS load and barrier among the MFMAs;
-// the accumulators live in a[0:255] for the whole work item.
+// the accumulators live in a[0:255] for the whole work item.  Its MFMA is
+// the 16x16x32 one (8 x 8 blocks per wave): for the same flops it moves half
+// the accumulator bytes of the 32x32x16 one, and the power-limited clock is
+// higher for it.
 //
 // Everything around the loop is ordinary code: per work item the tile's
 // per-lane load offsets (lanes outside the matrix get an offset beyond the
 // descriptor's num_records, so the hardware writes zeros), the first two
 // slices' loads, and after the loop the epilogue, which reads the
-// accumulators one 32x32 block at a time and stores them with the shared
-// epilogue code.
+// accumulators one 16x16 block at a time.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -38,63 +40,94 @@ struct Sq4 {
 // drift it corrects is a few us per round).
 constexpr uint64_t kSyncWaitTicks = 3000;
 
-// One 32x32 accumulator block, as the shared epilogue code sees a tile of one
-// block (the interior test uses the whole 256x256 tile).  EPI: 0 plain, else
-// the per-column bias (if given) and activation EPI-1 on every sum before it
-// is stored (as GemmCfg::EPI).
-template <int EPI_>
-struct Sq4Block {
-  static constexpr int FM = 1, FN = 1, BM = 256, BN = 256, EPI = EPI_;
-};
-
-#define LL_SQ4_READ_FN(I, J)                                                                              \
-  __device__ __forceinline__ f32x16 sq4_read_acc_##I##_##J() {                                             \
-    float r[16];                                                                                          \
-    asm volatile(LL_SQ4_READ_ACC_##I##_##J                                                                \
-                 : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]),     \
-                   "=v"(r[7]), "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), \
-                   "=v"(r[14]), "=v"(r[15]));                                                              \
-    f32x16 v;                                                                                             \
-    for (int k = 0; k < 16; ++k) v[k] = r[k];                                                             \
-    return v;                                                                                             \
+// Accumulator block n (16x16; row block n / 8, column block n % 8 of the
+// wave's 128x128): register r of lane l holds row 4 * (l / 16) + r, column
+// l % 16 of the block (the output layout of v_mfma_f32_16x16x32).
+#define LL_SQ4_ACC_FN(N)                                                                            \
+  __device__ __forceinline__ f32x4 sq4_acc_##N() {                                                  \
+    float r0, r1, r2, r3;                                                                          \
+    asm volatile(LL_SQ4_READ_ACC_##N : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3));                    \
+    return f32x4{r0, r1, r2, r3};                                                                  \
   }
-LL_SQ4_READ_FN(0, 0) LL_SQ4_READ_FN(0, 1) LL_SQ4_READ_FN(0, 2) LL_SQ4_READ_FN(0, 3)
-LL_SQ4_READ_FN(1, 0) LL_SQ4_READ_FN(1, 1) LL_SQ4_READ_FN(1, 2) LL_SQ4_READ_FN(1, 3)
-LL_SQ4_READ_FN(2, 0) LL_SQ4_READ_FN(2, 1) LL_SQ4_READ_FN(2, 2) LL_SQ4_READ_FN(2, 3)
-LL_SQ4_READ_FN(3, 0) LL_SQ4_READ_FN(3, 1) LL_SQ4_READ_FN(3, 2) LL_SQ4_READ_FN(3, 3)
-#undef LL_SQ4_READ_FN
+LL_SQ4_BLOCKS(LL_SQ4_ACC_FN)
+#undef LL_SQ4_ACC_FN
 
-template <int I, int J>
-__device__ __forceinline__ f32x16 sq4_read_acc() {
-#define LL_SQ4_PICK(i, j) \
-  if constexpr (I == i && J == j) return sq4_read_acc_##i##_##j();
-  LL_SQ4_PICK(0, 0) LL_SQ4_PICK(0, 1) LL_SQ4_PICK(0, 2) LL_SQ4_PICK(0, 3)
-  LL_SQ4_PICK(1, 0) LL_SQ4_PICK(1, 1) LL_SQ4_PICK(1, 2) LL_SQ4_PICK(1, 3)
-  LL_SQ4_PICK(2, 0) LL_SQ4_PICK(2, 1) LL_SQ4_PICK(2, 2) LL_SQ4_PICK(2, 3)
-  LL_SQ4_PICK(3, 0) LL_SQ4_PICK(3, 1) LL_SQ4_PICK(3, 2) LL_SQ4_PICK(3, 3)
-#undef LL_SQ4_PICK
+template <int N>
+__device__ __forceinline__ f32x4 sq4_acc() {
+#define LL_SQ4_ACC_PICK(n) \
+  if constexpr (N == n) return sq4_acc_##n();
+  LL_SQ4_BLOCKS(LL_SQ4_ACC_PICK)
+#undef LL_SQ4_ACC_PICK
 }
 
-template <int EPI, int I, int J>
-__device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0,
-                                                int lane) {
-  f32x16 acc[1][1];
-  acc[0][0] = sq4_read_acc<I, J>();
-  epilogue<Sq4Block<EPI>>(p, ti, acc, wm0 + 32 * I, wn0 + 32 * J, lane);
+// The bias of the 8 columns this lane holds in the wave's 128 (one per column
+// block), read once per tile; columns past N take none (they are not stored).
+template <int EPI>
+__device__ __forceinline__ void sq4_bias(const GemmKArgs& p, const TileInfo& ti, int wn0, int lane, float (&b)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int col = ti.n0 + wn0 + 16 * j + (lane & 15);
+    b[j] = (EPI > 0 && col < p.N) ? bias_at(p, col) : 0.f;
+  }
+}
+
+// Direct stores of block N: split-K partials (raw sums), or C of any type and
+// layout with bias and activation, element by element with bounds checks
+// (ragged tiles, fp32 C, C that the staged path does not take).
+template <int EPI, int N>
+__device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0, int lane,
+                                                const float (&bias)[8]) {
+  constexpr int I = N >> 3, J = N & 7;
+  f32x4 v = sq4_acc<N>();
+  const int col = ti.n0 + wn0 + 16 * J + (lane & 15);
+  const int row0 = ti.m0 + wm0 + 16 * I + 4 * (lane >> 4);
+  if (p.partial) {
+    float* P = p.partial + (int64_t)ti.ks * p.M * p.N;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (row0 + r < p.M && col < p.N) P[(int64_t)(row0 + r) * p.N + col] = v[r];
+    return;
+  }
+  if constexpr (EPI > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = epi<EPI - 1>(v[r], bias[J]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + r;
+    if (row < p.M && col < p.N) {
+      const int64_t o = (int64_t)row * p.ldcm + (int64_t)col * p.ldcn;
+      if (p.c_fmt == 1)
+        ((uint16_t*)p.c)[o] = f32_to_bf16_bits(v[r]);
+      else if (p.c_fmt == 2)
+        ((uint16_t*)p.c)[o] = f32_to_f16_bits(v[r]);
+      else
+        ((float*)p.c)[o] = v[r];
+    }
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void sq4_store_all(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0, int lane) {
+  float bias[8];
+  sq4_bias<EPI>(p, ti, wn0, lane, bias);
+#define LL_SQ4_STORE(n) sq4_store_block<EPI, n>(p, ti, wm0, wn0, lane, bias);
+  LL_SQ4_BLOCKS(LL_SQ4_STORE)
+#undef LL_SQ4_STORE
 }
 
 // Staged store of a wave's 128x128 block of 16-bit C through 32 KB of LDS
-// (the ring is free once every wave has left the k-loop).  Per 32x32
+// (the ring is free once every wave has left the k-loop).  Per 16x16
 // accumulator block the lane pair holding columns d, d+1 swaps values, so
 // that each lane holds 4-byte column pairs of two rows, and writes them into a
 // row-major [128][128] image (256-byte rows) whose 16-byte chunks are
-// XOR-swizzled by ((row >> 1) & 3) << 2: the four rows one write instruction
-// covers then fall on four different 64-byte groups of banks.  Each 16-byte
-// read then takes four whole rows back and each lane stores 16 bytes, so a
-// wave stores its block with 32 instructions of whole 128-byte lines instead
-// of 128 of 4 bytes per lane.
+// XOR-swizzled by ((row >> 1) & 7) << 1: the eight rows one write instruction
+// covers (32 bytes each) then fall on eight different 32-byte groups of
+// banks.  Each 16-byte read then takes four whole rows back and each lane
+// stores 16 bytes, so a wave stores its block with 32 instructions of whole
+// 128-byte lines instead of 256 of 2 bytes per lane.
 __device__ __forceinline__ uint32_t sq4_stage_off(int row, int cb) {
-  return (uint32_t)(row * 256 + ((((cb >> 4) ^ (((row >> 1) & 3) << 2))) << 4) + (cb & 15));
+  return (uint32_t)(row * 256 + ((((cb >> 4) ^ (((row >> 1) & 7) << 1))) << 4) + (cb & 15));
 }
 
 template <int FMT>
@@ -102,48 +135,36 @@ __device__ __forceinline__ uint32_t sq4_pack16(float lo, float hi) {
   return (uint32_t)to_c16<FMT>(lo) | ((uint32_t)to_c16<FMT>(hi) << 16);
 }
 
-template <int EPI, int FMT, int I, int J>
-__device__ __forceinline__ void sq4_stage_block(const GemmKArgs& p, const TileInfo& ti, int wn0, int lane,
-                                                char LL_LDS* img) {
-  f32x16 acc[1][1];
-  acc[0][0] = sq4_read_acc<I, J>();
-  if constexpr (EPI > 0) apply_epi<Sq4Block<EPI>, EPI - 1>(p, ti, acc, wn0 + 32 * J, lane);
-  const bool odd = lane & 1;
-  // even lane: rows +0, +1 of its group; odd lane: rows +2, +3 (see epilogue_fast16)
-  const int ra = 32 * I + 4 * (lane >> 5) + (odd ? 2 : 0);
-  const int cb = 64 * J + 2 * (lane & 30);
+template <int EPI, int FMT, int N>
+__device__ __forceinline__ void sq4_stage_block(int lane, const float (&bias)[8], char LL_LDS* img) {
+  constexpr int I = N >> 3, J = N & 7;
+  f32x4 v = sq4_acc<N>();
+  if constexpr (EPI > 0) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const float v0 = acc[0][0][4 * g + 0], v1 = acc[0][0][4 * g + 1];
-    const float v2 = acc[0][0][4 * g + 2], v3 = acc[0][0][4 * g + 3];
-    const float s0 = swap_pair(odd ? v0 : v2);
-    const float s1 = swap_pair(odd ? v1 : v3);
-    const float a0 = odd ? s0 : v0, a1 = odd ? v2 : s0;
-    const float b0 = odd ? s1 : v1, b1 = odd ? v3 : s1;
-    *(uint32_t LL_LDS*)(img + sq4_stage_off(ra + 8 * g, cb)) = sq4_pack16<FMT>(a0, a1);
-    *(uint32_t LL_LDS*)(img + sq4_stage_off(ra + 8 * g + 1, cb)) = sq4_pack16<FMT>(b0, b1);
+    for (int r = 0; r < 4; ++r) v[r] = epi<EPI - 1>(v[r], bias[J]);
   }
+  const bool odd = lane & 1;
+  // lanes 2c, 2c+1 hold columns d, d+1 of rows 4g..4g+3 (g = lane / 16); the
+  // even lane sends rows 2, 3 and receives the odd lane's rows 0, 1, the odd
+  // lane sends rows 0, 1 and receives rows 2, 3
+  const int ra = 16 * I + 4 * (lane >> 4) + (odd ? 2 : 0);
+  const int cb = 32 * J + 2 * (lane & 14);
+  const float s0 = swap_pair(odd ? v[0] : v[2]);
+  const float s1 = swap_pair(odd ? v[1] : v[3]);
+  const float a0 = odd ? s0 : v[0], a1 = odd ? v[2] : s0;
+  const float b0 = odd ? s1 : v[1], b1 = odd ? v[3] : s1;
+  *(uint32_t LL_LDS*)(img + sq4_stage_off(ra, cb)) = sq4_pack16<FMT>(a0, a1);
+  *(uint32_t LL_LDS*)(img + sq4_stage_off(ra + 1, cb)) = sq4_pack16<FMT>(b0, b1);
 }
 
 template <int EPI, int FMT>
 __device__ __forceinline__ void sq4_stage_all(const GemmKArgs& p, const TileInfo& ti, int wn0, int lane,
                                               char LL_LDS* img) {
-  sq4_stage_block<EPI, FMT, 0, 0>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 0, 1>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 0, 2>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 0, 3>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 1, 0>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 1, 1>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 1, 2>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 1, 3>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 2, 0>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 2, 1>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 2, 2>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 2, 3>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 3, 0>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 3, 1>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 3, 2>(p, ti, wn0, lane, img);
-  sq4_stage_block<EPI, FMT, 3, 3>(p, ti, wn0, lane, img);
+  float bias[8];
+  sq4_bias<EPI>(p, ti, wn0, lane, bias);
+#define LL_SQ4_STAGE(n) sq4_stage_block<EPI, FMT, n>(lane, bias, img);
+  LL_SQ4_BLOCKS(LL_SQ4_STAGE)
+#undef LL_SQ4_STAGE
 }
 
 // The image back, four rows per read, each lane storing 16 bytes of a row.
@@ -159,7 +180,7 @@ __device__ __forceinline__ void sq4_flush(const GemmKArgs& p, const TileInfo& ti
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int row = 4 * q + rl;
-    const i32x4 v = *(const i32x4 LL_LDS*)(img + row * 256 + ((c ^ (((row >> 1) & 3) << 2)) << 4));
+    const i32x4 v = *(const i32x4 LL_LDS*)(img + row * 256 + ((c ^ (((row >> 1) & 7) << 1)) << 4));
     // C is not read again by this kernel: non-temporal (same box: +1.3% at
     // 4096^3, +1.5% at 8192^3, FFN shapes within noise)
     __builtin_nontemporal_store(v, (i32x4*)(cb + (uint32_t)off));
@@ -199,27 +220,30 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
   const uint32_t base = lds_u32(smem);
 
-  // LDS addresses of this lane's fragment reads.  A block i (32 rows) at k16
-  // step kk: blocks i and i+2 share the swizzle (rows 64 apart), so one
-  // address per (slot, kk, i parity) serves both (+8192).  B fragment j:
-  // the swizzle depends on the k-row modulo 4 only, so step kk is +8192*kk
-  // and the second half (k-rows +4) +2048 from the step-0 address.
-  uint32_t fa[2][4][2], fb[2][4];
+  // LDS addresses of this lane's fragment reads (16x16x32 operands: lane l
+  // takes row / column l % 16 and k = 8 * (l / 16) .. + 7 of the step's 32).
+  // A block i (16 rows) at k32 step kk: blocks i and i+4 share the swizzle
+  // (rows 64 apart), so one address per (slot, kk, i % 4) serves both
+  // (+8192).  B fragment j (16 columns): two transposing reads, each giving
+  // a lane 4 k of its column; the swizzle depends on the k-row modulo 4
+  // only, so step kk is +16384*kk and the second half (k-rows +4) +2048
+  // from the step-0 address.
+  uint32_t fa[2][2][4], fb[2][8];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        const int row = wm0 + 32 * par + (lane & 31);
-        const int lc = kk * 2 + (lane >> 5);
-        fa[s][kk][par] = base + s * Sq4::SLOT + row * 128 + ((lc ^ swz_k<8>(row)) << 4);
+      for (int q = 0; q < 4; ++q) {
+        const int row = wm0 + 16 * q + (lane & 15);
+        const int lc = kk * 4 + (lane >> 4);
+        fa[s][kk][q] = base + s * Sq4::SLOT + row * 128 + ((lc ^ swz_k<8>(row)) << 4);
       }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const int g = lane >> 4, sl = lane & 15;
-      const int mn = wn0 + 32 * j + 16 * (g & 1) + 4 * (sl & 3);
-      const int kr = 8 * (g >> 1) + (sl >> 2);
+      const int mn = wn0 + 16 * j + 4 * (sl & 3);
+      const int kr = 8 * g + (sl >> 2);
       const int lc = mn >> 3, half = (mn & 7) * 2;
       fb[s][j] = base + s * Sq4::SLOT + Sq4::B_OFF + kr * 512 + ((lc ^ swz_mn<32>(kr)) << 4) + half;
     }
@@ -279,21 +303,23 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     lds_barrier();
     int m0v = 0;  // M0 is rewritten by the loop's loads
 
-#define LL_SQ4_OPERANDS                                                                                        \
-  : [n] "+s"(n), [m0] "+{m0}"(m0v)                                                                             \
-  : [a0] "s"(ra[0]), [a1] "s"(ra[1]), [a2] "s"(ra[2]), [a3] "s"(ra[3]), [b0] "s"(rb[0]),                     \
+#define LL_SQ4_OPERANDS                                                                                       \
+  : [n] "+s"(n), [m0] "+{m0}"(m0v)                                                                            \
+  : [a0] "s"(ra[0]), [a1] "s"(ra[1]), [a2] "s"(ra[2]), [a3] "s"(ra[3]), [b0] "s"(rb[0]),                      \
     [b1] "s"(rb[1]), [b2] "s"(rb[2]), [b3] "s"(rb[3]), [incb] "s"(incb), [ldsw] "s"(ldsw),                    \
-    [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]),                  \
-    [va5] "v"(va[5]), [va6] "v"(va[6]), [va7] "v"(va[7]), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]),                  \
-    [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [vb4] "v"(vb[4]), [vb5] "v"(vb[5]), [vb6] "v"(vb[6]),                  \
-    [vb7] "v"(vb[7]), [fa_0_0_0] "v"(fa[0][0][0]), [fa_0_0_1] "v"(fa[0][0][1]), [fa_0_1_0] "v"(fa[0][1][0]), \
-    [fa_0_1_1] "v"(fa[0][1][1]), [fa_0_2_0] "v"(fa[0][2][0]), [fa_0_2_1] "v"(fa[0][2][1]),                     \
-    [fa_0_3_0] "v"(fa[0][3][0]), [fa_0_3_1] "v"(fa[0][3][1]), [fa_1_0_0] "v"(fa[1][0][0]),                     \
-    [fa_1_0_1] "v"(fa[1][0][1]), [fa_1_1_0] "v"(fa[1][1][0]), [fa_1_1_1] "v"(fa[1][1][1]),                     \
-    [fa_1_2_0] "v"(fa[1][2][0]), [fa_1_2_1] "v"(fa[1][2][1]), [fa_1_3_0] "v"(fa[1][3][0]),                     \
-    [fa_1_3_1] "v"(fa[1][3][1]), [fb_0_0] "v"(fb[0][0]), [fb_0_1] "v"(fb[0][1]), [fb_0_2] "v"(fb[0][2]),       \
-    [fb_0_3] "v"(fb[0][3]), [fb_1_0] "v"(fb[1][0]), [fb_1_1] "v"(fb[1][1]), [fb_1_2] "v"(fb[1][2]),            \
-    [fb_1_3] "v"(fb[1][3])                                                                                     \
+    [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]),                 \
+    [va5] "v"(va[5]), [va6] "v"(va[6]), [va7] "v"(va[7]), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]),                 \
+    [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [vb4] "v"(vb[4]), [vb5] "v"(vb[5]), [vb6] "v"(vb[6]),                 \
+    [vb7] "v"(vb[7]), [fa_0_0_0] "v"(fa[0][0][0]), [fa_0_0_1] "v"(fa[0][0][1]), [fa_0_0_2] "v"(fa[0][0][2]),  \
+    [fa_0_0_3] "v"(fa[0][0][3]), [fa_0_1_0] "v"(fa[0][1][0]), [fa_0_1_1] "v"(fa[0][1][1]),                    \
+    [fa_0_1_2] "v"(fa[0][1][2]), [fa_0_1_3] "v"(fa[0][1][3]), [fa_1_0_0] "v"(fa[1][0][0]),                    \
+    [fa_1_0_1] "v"(fa[1][0][1]), [fa_1_0_2] "v"(fa[1][0][2]), [fa_1_0_3] "v"(fa[1][0][3]),                    \
+    [fa_1_1_0] "v"(fa[1][1][0]), [fa_1_1_1] "v"(fa[1][1][1]), [fa_1_1_2] "v"(fa[1][1][2]),                    \
+    [fa_1_1_3] "v"(fa[1][1][3]), [fb_0_0] "v"(fb[0][0]), [fb_0_1] "v"(fb[0][1]), [fb_0_2] "v"(fb[0][2]),      \
+    [fb_0_3] "v"(fb[0][3]), [fb_0_4] "v"(fb[0][4]), [fb_0_5] "v"(fb[0][5]), [fb_0_6] "v"(fb[0][6]),           \
+    [fb_0_7] "v"(fb[0][7]), [fb_1_0] "v"(fb[1][0]), [fb_1_1] "v"(fb[1][1]), [fb_1_2] "v"(fb[1][2]),           \
+    [fb_1_3] "v"(fb[1][3]), [fb_1_4] "v"(fb[1][4]), [fb_1_5] "v"(fb[1][5]), [fb_1_6] "v"(fb[1][6]),           \
+    [fb_1_7] "v"(fb[1][7])                                                                                    \
   : LL_SQ4_CLOBBERS
     if constexpr (F16)
       asm volatile(LL_SQ4_LOOP_F16 LL_SQ4_OPERANDS);
@@ -319,22 +345,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       if (t + stride < p.total) lds_barrier();
       continue;
     }
-    sq4_store_block<EPI, 0, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 0, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 0, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 0, 3>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 1, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 1, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 1, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 1, 3>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 2, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 2, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 2, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 2, 3>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 3, 0>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 3, 1>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 3, 2>(p, ti, wm0, wn0, lane);
-    sq4_store_block<EPI, 3, 3>(p, ti, wm0, wn0, lane);
+    sq4_store_all<EPI>(p, ti, wm0, wn0, lane);
   }
 }
 

@@ -5,26 +5,30 @@ with four waves of 128x128 (KIND_SQ4_HO), ordered by hand.
 
 The k-loop of one work item is a single inline-asm statement, so that where
 every wait, LDS fragment read, direct-to-LDS load and barrier sits relative to
-the 16 MFMAs of a k16 step is fixed here rather than by the compiler's
-scheduler.  Registers (per wave, one wave per SIMD):
+the 64 MFMAs of a k32 step is fixed here rather than by the compiler's
+scheduler.  The MFMA is the 16x16x32 one: for the same flops it moves half
+the accumulator bytes of the 32x32x16 one, and under the chip's power limit
+it holds a higher clock.  Registers (per wave, one wave per SIMD):
 
-* a[0:255]: the 128x128 fp32 accumulators; block (i, j) (32x32, i rows,
-  j columns) is a[16*(4i+j) : 16*(4i+j)+15].
-* v[192:223] / v[224:255]: two fragment buffers F0 / F1, each 4 A fragments
-  (4 VGPRs each: 32 rows x 16 k, bf16/fp16) then 4 B fragments.
+* a[0:255]: the 128x128 fp32 accumulators; block (i, j) (16x16, i rows,
+  j columns, 0..7 each) is a[4*(8i+j) : 4*(8i+j)+3].
+* v[128:191] / v[192:255]: two fragment buffers F0 / F1, each 8 A fragments
+  (4 VGPRs each: 16 rows x 32 k, bf16/fp16) then 8 B fragments (32 k x 16
+  columns).
 * s[88:91] / s[92:95]: private copies of the A / B buffer descriptors, whose
   base advances by one k-slice per issued slice (64-bit SALU add).
 
 Ring: two LDS slots of 64 KB (A tile [256][64] K-contiguous, then B tile
 [64][256] N-contiguous, both swizzled as the loaders write them).  Slice j is
-in slot j%2.  Per slice, k16 steps 0..2 each wait for their fragments, then
-issue 16 MFMAs with the next step's 12 fragment reads spread between them.
-Step 3 waits for its fragments (every read of slot j%2 is then done), issues
-a few MFMAs, waits until this wave's loads of slice j+1 have landed and meets
-the other waves at the barrier; after it, slice j+1 is in LDS for every wave
-and slot j%2 is free, so the rest of step 3's MFMAs are interleaved with the
-reads of slice j+1's first step and the 16 loads of slice j+2 into slot j%2.
-The last slice has no barrier; the one before it issues no loads.
+in slot j%2.  Per slice, k32 step 0 waits for its fragments, then issues 64
+MFMAs with step 1's 24 fragment reads spread between them.  Step 1 waits for
+its fragments (every read of slot j%2 is then done), issues a few MFMAs,
+waits until this wave's loads of slice j+1 have landed and meets the other
+waves at the barrier; after it, slice j+1 is in LDS for every wave and slot
+j%2 is free, so the rest of step 1's MFMAs are interleaved with the reads of
+slice j+1's first step and the first loads of slice j+2 into slot j%2; the
+rest of slice j+2's loads go between step 0's MFMAs of slice j+1.  The last
+slice has no barrier; the one before it issues no loads.
 
 Operands the statement expects (names as in gemm_sq4.hpp):
   n (+s)                slices of the work item, >= 1
@@ -33,10 +37,10 @@ Operands the statement expects (names as in gemm_sq4.hpp):
   ldsw (s)              LDS byte address of slot 0 plus 1024 * wave
   m0 (+{m0})            M0, rewritten by the loads
   va0..va7, vb0..vb7 (v) per-lane offsets of the wave's 8 A and 8 B loads
-  fa_S_K_P (v)          LDS address of A fragments of slot S, k16 step K,
-                        32-row block parity P (block i+2 at +8192)
+  fa_S_K_P (v)          LDS address of A fragments of slot S, k32 step K,
+                        16-row block i with i % 4 == P (block i+4 at +8192)
   fb_S_J (v)            LDS address of B fragment J of slot S at step 0
-                        (step K at +8192*K, the second half at +2048)
+                        (step K at +16384*K, the second half at +2048)
 """
 from __future__ import annotations
 
@@ -45,12 +49,17 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(HERE, "gemm_sq4_loop.inc")
 
-FBASE = 192         # first fragment VGPR
-READ_SPAN = 10      # MFMAs of steps 0..2 over which the next step's 12 reads are spread
-BAR_AFTER = 0       # MFMAs of step 3 issued before the load wait and barrier
-L3 = 6              # loads of slice j+2 issued in step 3 of slice j; the rest go to steps 0..2 of slice j+1
-CARRY_STEPS = 2     # how many of steps 0..2 of slice j+1 share the rest
-CARRY_SPAN = 14     # MFMAs over which a step's reads and carried loads are spread
+STEPS = 2           # k32 steps per 64-deep slice
+MFMAS = 64          # MFMAs per step (8 x 8 blocks of 16x16)
+READS = 24          # fragment reads per step: 8 A (ds_read_b128), 16 B (two ds_read_b64_tr_b16 each)
+B_STEP = 16384      # LDS bytes between a B fragment's steps (32 k-rows of 512 bytes)
+FBASE = 128         # first fragment VGPR
+FBUF = 64           # VGPRs per fragment buffer
+READ_SPAN = 40      # MFMAs of step 0 over which step 1's reads are spread
+BAR_AFTER = 8       # MFMAs of step 1 issued before the load wait and barrier
+L3 = 10             # loads of slice j+2 issued in step 1 of slice j; the rest go to step 0 of slice j+1
+CARRY_STEPS = 1     # how many of the steps before the last of slice j+1 share the rest
+CARRY_SPAN = 52     # MFMAs over which a step's reads and carried loads are spread
 B_FIRST = 0         # load order within a slice: 0 A0, B0, A1, B1, ...; 1 B0, A0, B1, A1, ...
 CARRY_BLOCKS = 0    # 0: step k takes every CARRY_STEPS-th carried load; 1: contiguous runs of them
 SLOT = 65536
@@ -58,36 +67,36 @@ B_OFF = 32768
 
 
 def fa(buf, i):
-    return FBASE + 32 * buf + 4 * i
+    return FBASE + FBUF * buf + 4 * i
 
 
 def fb(buf, j):
-    return FBASE + 32 * buf + 16 + 4 * j
+    return FBASE + FBUF * buf + 32 + 4 * j
 
 
 def acc(i, j):
-    return 16 * (4 * i + j)
+    return 4 * (8 * i + j)
 
 
 def mfmas(op, buf):
     out = []
-    for i in range(4):
-        for j in range(4):
+    for i in range(8):
+        for j in range(8):
             a = acc(i, j)
-            out.append(f"{op} a[{a}:{a + 15}], v[{fa(buf, i)}:{fa(buf, i) + 3}], "
-                       f"v[{fb(buf, j)}:{fb(buf, j) + 3}], a[{a}:{a + 15}]")
+            out.append(f"{op} a[{a}:{a + 3}], v[{fa(buf, i)}:{fa(buf, i) + 3}], "
+                       f"v[{fb(buf, j)}:{fb(buf, j) + 3}], a[{a}:{a + 3}]")
     return out
 
 
 def reads(slot, kk, buf):
-    """The 12 fragment reads of k16 step kk from `slot` into buffer `buf`."""
+    """The 24 fragment reads of k32 step kk from `slot` into buffer `buf`."""
     out = []
-    for i in range(4):
-        off = (i >> 1) * 8192
+    for i in range(8):
+        off = (i >> 2) * 8192
         o = f" offset:{off}" if off else ""
-        out.append([f"ds_read_b128 v[{fa(buf, i)}:{fa(buf, i) + 3}], %[fa_{slot}_{kk}_{i & 1}]{o}"])
-    for j in range(4):
-        lo, hi = kk * 8192, kk * 8192 + 2048
+        out.append([f"ds_read_b128 v[{fa(buf, i)}:{fa(buf, i) + 3}], %[fa_{slot}_{kk}_{i & 3}]{o}"])
+    for j in range(8):
+        lo, hi = kk * B_STEP, kk * B_STEP + 2048
         o = f" offset:{lo}" if lo else ""
         out.append([f"ds_read_b64_tr_b16 v[{fb(buf, j)}:{fb(buf, j) + 1}], %[fb_{slot}_{j}]{o}"])
         out.append([f"ds_read_b64_tr_b16 v[{fb(buf, j) + 2}:{fb(buf, j) + 3}], %[fb_{slot}_{j}] offset:{hi}"])
@@ -130,24 +139,27 @@ def interleave(mf, ops, span):
 
 
 def carried(slot, kk):
-    """Loads of the next slice (into the other slot) issued in step kk (0..2):
-    the 16 - L3 that step 3 of the previous slice left, spread over the first
-    CARRY_STEPS steps; the descriptors advance once, right after the last of
-    them (every path through a slice advances them exactly once)."""
+    """Loads of the next slice (into the other slot) issued in step kk (one of
+    the STEPS - 1 steps before the last): the 16 - L3 that the last step of
+    the previous slice left, spread over the first CARRY_STEPS steps; the
+    descriptors advance once, right after the last of them (every path
+    through a slice advances them exactly once)."""
     rest = loads(1 - slot)[L3:]
-    assert rest and 1 <= CARRY_STEPS <= 3
+    early = STEPS - 1
+    assert rest and 1 <= CARRY_STEPS <= early
     if CARRY_BLOCKS:
         cut = [len(rest) * k // CARRY_STEPS for k in range(CARRY_STEPS + 1)]
-        per = [rest[cut[k]:cut[k + 1]] for k in range(CARRY_STEPS)] + [[]] * (3 - CARRY_STEPS)
+        per = [rest[cut[k]:cut[k + 1]] for k in range(CARRY_STEPS)] + [[]] * (early - CARRY_STEPS)
     else:
-        per = [rest[k::CARRY_STEPS] for k in range(CARRY_STEPS)] + [[]] * (3 - CARRY_STEPS)
-    last = max(k for k in range(3) if per[k])
+        per = [rest[k::CARRY_STEPS] for k in range(CARRY_STEPS)] + [[]] * (early - CARRY_STEPS)
+    last = max(k for k in range(early) if per[k])
     return per[kk] + ([ADVANCE] if kk == last else [])
 
 
 def step(op, slot, kk, buf, carry):
-    """k16 step kk (0..2) of a slice in `slot`: MFMAs on `buf`, reads of step kk+1,
-    and (carry) this step's share of the next slice's remaining loads."""
+    """Step kk (before the last) of a slice in `slot`: MFMAs on `buf`, reads of
+    step kk+1, and (carry) this step's share of the next slice's remaining
+    loads."""
     rd = reads(slot, kk + 1, 1 - buf)
     ops = rd
     if carry:
@@ -161,10 +173,11 @@ def step(op, slot, kk, buf, carry):
     return ["s_waitcnt lgkmcnt(0)"] + interleave(mfmas(op, buf), ops, READ_SPAN if not carry else CARRY_SPAN)
 
 
-def step3(op, slot, kind):
-    """Step 3 (fragments in F1).  kind: "last" (no next slice), "noload" (next
-    slice, nothing more to load), "load" (next slice, and load slice j+2)."""
-    mf = mfmas(op, 1)
+def step_last(op, slot, kind):
+    """The last step of a slice (fragments in buffer (STEPS - 1) % 2).  kind:
+    "last" (no next slice), "noload" (next slice, nothing more to load),
+    "load" (next slice, and load slice j+2)."""
+    mf = mfmas(op, (STEPS - 1) % 2)
     if kind == "last":
         return ["s_waitcnt lgkmcnt(0)"] + mf
     out = ["s_waitcnt lgkmcnt(0)"] + mf[:BAR_AFTER] + ["s_waitcnt vmcnt(0)", "s_barrier"]
@@ -192,9 +205,9 @@ def loop(op):
     # slice 2, the first slice the loop loads
     L += ["s_mov_b32 s88, %[a0]", "s_mov_b32 s89, %[a1]", "s_mov_b32 s90, %[a2]", "s_mov_b32 s91, %[a3]",
           "s_mov_b32 s92, %[b0]", "s_mov_b32 s93, %[b1]", "s_mov_b32 s94, %[b2]", "s_mov_b32 s95, %[b3]"]
-    # with every load of a slice in step 3 the loop's first load is of slice
-    # 2; otherwise the rest of slice 1 (whose first L3 loads the prologue
-    # issued) comes first, in the first slice's steps 0..2
+    # with every load of a slice in the last step the loop's first load is of
+    # slice 2; otherwise the rest of slice 1 (whose first L3 loads the
+    # prologue issued) comes first, in the first slice's earlier steps
     L += ADVANCE + ADVANCE if L3 == 16 else ADVANCE
     L += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(256)]
     L += ["s_nop 4"]
@@ -203,24 +216,25 @@ def loop(op):
         L += [f"L_top{slot}_%=:"]
         if L3 < 16:
             L += ["s_cmp_lt_u32 %[n], 2", f"s_cbranch_scc1 L_noc{slot}_%="]
-            for kk in range(3):
+            for kk in range(STEPS - 1):
                 L += step(op, slot, kk, kk % 2, True)
             L += [f"s_branch L_st3{slot}_%=", f"L_noc{slot}_%=:"]
-        for kk in range(3):
+        for kk in range(STEPS - 1):
             L += step(op, slot, kk, kk % 2, False)
         L += [f"L_st3{slot}_%=:"]
         L += ["s_cmp_eq_u32 %[n], 1", f"s_cbranch_scc1 L_last{slot}_%=",
               "s_cmp_eq_u32 %[n], 2", f"s_cbranch_scc1 L_nold{slot}_%="]
-        L += step3(op, slot, "load")
+        L += step_last(op, slot, "load")
         L += ["s_sub_u32 %[n], %[n], 1", f"s_branch L_top{1 - slot}_%="]
         L += [f"L_nold{slot}_%=:"]
-        L += step3(op, slot, "noload")
+        L += step_last(op, slot, "noload")
         L += ["s_sub_u32 %[n], %[n], 1", f"s_branch L_top{1 - slot}_%="]
         L += [f"L_last{slot}_%=:"]
-        L += step3(op, slot, "last")
+        L += step_last(op, slot, "last")
         L += ["s_branch L_done_%="]
     # the accumulators are read with v_accvgpr_read after this statement:
-    # at least 18 wait states after the last 32x32 MFMA that writes them
+    # more wait states after the last MFMA that writes them than any MFMA
+    # needs (24 against at most 18)
     L += ["L_done_%=:", "s_nop 7", "s_nop 7", "s_nop 7"]
     return L
 
@@ -229,9 +243,9 @@ def cstring(lines):
     return " \\\n".join(f'  "{ln}\\n\\t"' for ln in lines)
 
 
-def read_acc(i, j):
-    a = acc(i, j)
-    return cstring([f"v_accvgpr_read_b32 %{r}, a{a + r}" for r in range(16)])
+def read_acc(n):
+    """Accumulator block n = 8i + j into the statement's outputs %0..%3."""
+    return cstring([f"v_accvgpr_read_b32 %{r}, a{4 * n + r}" for r in range(4)])
 
 
 def clobbers():
@@ -245,11 +259,12 @@ def main():
              "// kind with four 128x128 waves as one hand-ordered instruction stream",
              "// (see gen_sq4_loop.py for the register plan and the order).",
              "#pragma once", ""]
-    parts.append("#define LL_SQ4_LOOP_BF16 \\\n" + cstring(loop("v_mfma_f32_32x32x16_bf16")) + "\n")
-    parts.append("#define LL_SQ4_LOOP_F16 \\\n" + cstring(loop("v_mfma_f32_32x32x16_f16")) + "\n")
-    for i in range(4):
-        for j in range(4):
-            parts.append(f"#define LL_SQ4_READ_ACC_{i}_{j} \\\n" + read_acc(i, j) + "\n")
+    parts.append("#define LL_SQ4_LOOP_BF16 \\\n" + cstring(loop("v_mfma_f32_16x16x32_bf16")) + "\n")
+    parts.append("#define LL_SQ4_LOOP_F16 \\\n" + cstring(loop("v_mfma_f32_16x16x32_f16")) + "\n")
+    for n in range(64):
+        parts.append(f"#define LL_SQ4_READ_ACC_{n} \\\n" + read_acc(n) + "\n")
+    parts.append("// X(n) for every accumulator block n = 8 * row block + column block\n#define LL_SQ4_BLOCKS(X) " +
+                 " ".join(f"X({n})" for n in range(64)) + "\n")
     parts.append(f"// loads of a slice issued after the barrier of the slice two before; the\n"
                  f"// prologue issues this many of slice 1\n#define LL_SQ4_L3 {L3}\n"
                  f"// the loads of a slice alternate A and B, B first if 1\n#define LL_SQ4_B_FIRST {B_FIRST}\n")

@@ -12,11 +12,11 @@ stream) shows for every slice count and every load split that:
   that slot held has completed and a barrier has followed;
 * a fragment read finds every load of its slice completed and published by a
   barrier, reads the slot its slice went to, and the reads come in the order
-  slice 0 step 0, 1, 2, 3, slice 1 step 0, ...;
+  slice 0 step 0, 1, slice 1 step 0, ... (two k32 steps per slice);
 * the descriptors move by exactly one slice per slice, so num_records stays
   the operand's bytes from the base;
-* there is one barrier per slice but the last, 64 MFMAs per slice, and no load
-  is still outstanding at the end.
+* there is one barrier per slice but the last, 128 MFMAs per slice (two k32
+  steps of 64), and no load is still outstanding at the end.
 """
 import importlib.util
 import os
@@ -27,7 +27,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEN = os.path.join(ROOT, "recsys_linear_layers_amd", "csrc", "gen_sq4_loop.py")
 INC = os.path.join(ROOT, "recsys_linear_layers_amd", "csrc", "gemm_sq4_loop.inc")
-OP = "v_mfma_f32_32x32x16_bf16"
+OP = "v_mfma_f32_16x16x32_bf16"
 
 
 def _gen(**params):
@@ -101,7 +101,7 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
             want_m0 = (s % 2) * g.SLOT + (g.B_OFF if which == "B" else 0) + i * 4096
             assert m0 == want_m0, (s, which, i, m0, want_m0)
             if s >= 2:
-                assert released >= 4 * (s - 2) + 4, f"slot of slice {s - 2} refilled before its reads were released"
+                assert released >= g.STEPS * (s - 1), f"slot of slice {s - 2} refilled before its reads were released"
             issued[s].add((which, i))
             pending.add((s, (which, i)))
         elif ln == "s_waitcnt vmcnt(0)":
@@ -112,10 +112,10 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
         elif ln == "s_barrier":
             barriers += 1
             visible |= completed
-            released = reads_done // 12
+            released = reads_done // g.READS
         elif ln.startswith("ds_read"):
-            grp = reads_issued // 12
-            s, kk = grp // 4, grp % 4
+            grp = reads_issued // g.READS
+            s, kk = grp // g.STEPS, grp % g.STEPS
             m = re.search(r"%\[f([ab])_(\d)_(\d)(?:_(\d))?\](?: offset:(\d+))?", ln)
             assert m, ln
             slot = int(m.group(2))
@@ -123,7 +123,7 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
             if m.group(1) == "a":
                 assert int(m.group(3)) == kk, (ln, kk)
             else:
-                assert off // 8192 == kk, (ln, kk)
+                assert off // g.B_STEP == kk, (ln, kk)
             assert slot == s % 2, (ln, s)
             missing = [p for p in PIECES if (s, p) not in visible]
             assert not missing, f"read of slice {s} step {kk} before {missing} were published"
@@ -147,14 +147,14 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
     for s in range(n):
         assert issued.get(s) == set(PIECES), f"slice {s}: {sorted(set(PIECES) - issued.get(s, set()))} never loaded"
     assert not pending, "loads still outstanding at the end"
-    assert reads_issued == 48 * n and mfmas == 64 * n and barriers == n - 1
+    assert reads_issued == g.READS * g.STEPS * n and mfmas == g.MFMAS * g.STEPS * n and barriers == n - 1
     # the descriptors end at most one slice past the last loaded one
     assert a_off // 128 == b_adv and b_adv in (n, n + 1) or n <= 2
 
 
-SPLITS = [dict(L3=16)] + [dict(L3=l3, CARRY_STEPS=c) for l3 in (12, 10, 8, 6, 4) for c in (1, 2, 3)] + \
-         [dict(L3=l3, CARRY_STEPS=c, B_FIRST=b, CARRY_BLOCKS=k) for l3 in (8, 6, 4) for c in (2, 3)
-          for b in (0, 1) for k in (0, 1) if b or k]
+SPLITS = [dict(L3=16)] + [dict(L3=l3) for l3 in (14, 12, 10, 8, 6, 4, 2)] + \
+         [dict(L3=l3, B_FIRST=1) for l3 in (8, 6, 4)] + \
+         [dict(L3=6, READ_SPAN=r, CARRY_SPAN=c) for r, c in ((16, 24), (63, 63), (1, 1))]
 
 
 @pytest.mark.parametrize("params", SPLITS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
@@ -171,7 +171,7 @@ def test_committed_parameters_emulate():
 
 def test_emulation_catches_a_double_advance():
     """The emulation rejects a stream whose descriptors move twice in a slice."""
-    g = _gen(L3=8, CARRY_STEPS=3)
+    g = _gen(L3=8)
     real = g.carried
     g.carried = lambda slot, kk: real(slot, kk) + ([g.ADVANCE] if kk == 0 else [])
     with pytest.raises(AssertionError):
