@@ -122,9 +122,10 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * or packed), K a multiple of 64 and each operand spanning under 2 GB from
  * its base, any of those four kinds gives way to KIND_SQ4_HO (256x256 tiles,
  * four waves of 128x128, one per SIMD, each loading and computing in one
- * hand-ordered instruction stream) when that needs no more passes x tile
- * area; with or without a fused epilogue.  K is split when the tiles fill
- * fewer than half of the CUs.  KIND_SQ4_HO plans with 20 rounds or more
+ * hand-ordered instruction stream) when that needs at most 1.25x their
+ * passes x tile area (it runs ~1.3x as fast per pass and area); with or
+ * without a fused epilogue.  K is split when the tiles fill
+ * fewer than half of the CUs.  KIND_SQ4_HO plans with 8 rounds or more
  * (passes of the grid over the tiles) on a grid of whole XCDs also keep each
  * XCD's workgroups within a round of one another (round_sync=1 in the
  * description; LL_GEMM_ROUND_SYNC=0, or 1 for two rounds or more, overrides): a bounded wait between

@@ -81,11 +81,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kRoundSyncWords = 8 * 32;
 // Fewest rounds (passes of the persistent grid over its tiles) for which the
 // plan turns the round barrier on.  Measured with and without it, same
-// process: FFN-up (28 rounds) +2.2%, the same with bias + GELU +0.1%,
-// 16384^2 x 4096 (16) +0.1%; 8 rounds and fewer -0.1 to -0.8% (8192^2 x
-// 1024, 4 short rounds, the most).  The drift it removes builds up over
-// many rounds.
-constexpr int kRoundSyncMinRounds = 20;
+// process: FFN-up (28 rounds) +4.0%, the same with bias + GELU +0.7%,
+// 16384^2 x 4096 (16) +0.6%, 16384 x 8192 x 8192 (8) +0.5%, FFN-down (8)
+// +0.2%; 4 rounds -0.8 to -1.4% (8192^2 x 1024, short rounds, the most),
+// 2 rounds -0.3 to -0.4%.  The drift it removes builds up over rounds.
+constexpr int kRoundSyncMinRounds = 8;
 
 // Byte extent [lo, hi) touched by a 2-D strided view of `rows` x `cols` elements.
 struct Span {
@@ -328,18 +328,20 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     const KindInfo& kt = kind_info(KIND_TALL_PC);
     if (pk > 0 && pt > 0 && pt * kt.bm * kt.bn <= pk * kk.bm * kk.bn) kind = KIND_TALL_PC;
   }
-  // The hand-ordered 256x256 kind (four 128x128 waves, gemm_sq4.hpp) was
+  // The hand-ordered 256x256 kind (four 128x128 waves, gemm_sq4.hpp) is
   // ahead of every kind above wherever it applies: A K-contiguous, B
-  // N-contiguous, K a multiple of 64 (measured on the same operands: 4096^3
-  // +5%, FFN-up +3%, FFN-down +14% over 128x256, 8192^3 +8%, 4096^2 x 16384
-  // +7% over 128x256), with or without a fused epilogue.  Like the other
-  // rules it takes over only when its passes times tile area is no larger
-  // and neither choice would split K.
+  // N-contiguous, K a multiple of 64 or A packed, with or without a fused
+  // epilogue.  Per pass and tile area it runs ~1.3x as fast as the others,
+  // so it takes over when its passes times tile area is at most 1.25x theirs
+  // and neither choice would split K.  Measured against the kind the area
+  // rule alone picks, same operands: at 1.11x (8448^2 x 4096) +18%, 1.14x
+  // (12288 x 4608 x 8192) +16%, 1.2x (8191 x 5003 x 4099, both packed) +10%;
+  // at 1.33x (4608^2 x 4096, 6144^2 x 4096, 4608 x 8192 x 4096) -4 to -9%.
   if (free_choice && sq4_fits &&
       (kind == KIND_WIDE_PC || kind == KIND_TALL_PC || kind == KIND_SQ8_LW4 || kind == KIND_T192_PC)) {
     const int64_t pc = passes(kind), ph = passes(KIND_SQ4_HO);
     const KindInfo& kc = kind_info(kind);
-    if (pc > 0 && ph > 0 && ph * 256 * 256 <= pc * kc.bm * kc.bn) kind = KIND_SQ4_HO;
+    if (pc > 0 && ph > 0 && ph * 256 * 256 * 4 <= pc * kc.bm * kc.bn * 5) kind = KIND_SQ4_HO;
   }
   if (d->flags & LL_FLAG_COOPERATIVE) {
     if (kind == KIND_WIDE_PC) kind = KIND_SQ8_K64;
@@ -404,7 +406,7 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   p.group_m = 8;
   // Round barrier per XCD for the hand-ordered kind (gemm_sq4.hpp): on
   // FFN-up (28 rounds of 256 tiles) it cut the bytes fetched past L2 from
-  // 16.9 to 12.1 GB and the time by 2.2-2.3%.  It needs the grid to be whole
+  // 16.9 to 12.1 GB and the time by 2-4%.  It needs the grid to be whole
   // XCDs (the work-item remap) and many rounds (kRoundSyncMinRounds).
   // LL_GEMM_ROUND_SYNC=0 / 1 overrides the choice (measurement).
   {

@@ -125,6 +125,20 @@ def test_selected_on_square_and_ffn_shapes(M, N, K):
     assert f"kernel={KIND} " in _describe(M, N, K)
 
 
+@pytest.mark.parametrize("M,N,K,b_col,want", [
+    (8448, 8448, 4096, False, True),    # 5 passes of 256x256 against 9 of 256x128: 1.11x the area
+    (12288, 4608, 8192, False, True),   # 4 against 7 of 128x256: 1.14x
+    (8191, 5003, 4099, True, True),     # the edge shape, both operands packed: 3 against 5, 1.2x
+    (4608, 4608, 4096, False, False),   # 2 against 3 of 256x128: 1.33x
+    (6144, 6144, 4096, False, False),   # 3 against 3 of 192x256: 1.33x
+])
+def test_selected_up_to_a_quarter_more_area(M, N, K, b_col, want):
+    """The hand-ordered kind runs ~1.3x as fast per pass and tile area as the
+    other kinds, so it is chosen while it needs at most 1.25x their passes
+    times tile area."""
+    assert (f"kernel={KIND} " in _describe(M, N, K, b_col=b_col)) == want
+
+
 def test_selection_conditions():
     import recsys_linear_layers_amd as ll
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, in_t=ll.LL_F16, c_t=ll.LL_F16)
@@ -252,17 +266,17 @@ def test_staged_epilogue_needs_16_byte_aligned_c(monkeypatch):
 
 
 def test_round_barrier_selection(monkeypatch):
-    """Plans of the hand-ordered kind with 20 rounds of tiles or more keep
+    """Plans of the hand-ordered kind with 8 rounds of tiles or more keep
     each XCD's workgroups a round apart at most (round_sync=1), with their
     counters in the workspace; fewer rounds and other kinds do not, and the
     override turns it on from two rounds or off."""
     import recsys_linear_layers_amd as ll
-    for M, N, K in [(16384, 28672, 8192), (16384, 20480, 1024)]:       # 28 and 20 rounds
+    for M, N, K in [(16384, 28672, 8192), (16384, 8192, 28672), (16384, 16384, 4096)]:   # 28, 8, 16 rounds
         d = _describe(M, N, K)
         assert f"kernel={KIND} " in d and "round_sync=1" in d, d
         assert int(d.split(" ws=")[1].split()[0]) >= 1024, d
-    for M, N, K in [(4096, 4096, 4096), (16384, 8192, 28672), (8192, 8192, 8192), (16384, 16384, 4096)]:
-        d = _describe(M, N, K)                                         # 1, 8, 4 and 16 rounds
+    for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 8192, 1024), (4096, 8192, 8192)]:
+        d = _describe(M, N, K)                                         # 1, 4, 4 and 2 rounds
         assert f"kernel={KIND} " in d and "round_sync=0" in d and " ws=0 " in d, d
     d = _describe(16384, 28672, 8192, b_col=True)                      # another kind
     assert f"kernel={KIND} " not in d and "round_sync=0" in d, d
@@ -271,6 +285,7 @@ def test_round_barrier_selection(monkeypatch):
     assert "round_sync=0" in d and " ws=0 " in d, d
     monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "1")
     assert "round_sync=1" in _describe(8192, 8192, 1024)
+    assert "round_sync=1" in _describe(4096, 8192, 8192)
     assert "round_sync=0" in _describe(4096, 4096, 4096)              # still needs two rounds
 
 
