@@ -438,6 +438,7 @@ def _probe_lib():
         raise RuntimeError(f"{path} is not built (run recsys_linear_layers_amd/build.py)")
     lib = ctypes.CDLL(path)
     lib.ll_probe_mfma_only.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ll_probe_mfma16_only.argtypes = lib.ll_probe_mfma_only.argtypes
     lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_int, ctypes.c_void_p]
     return lib
@@ -450,10 +451,10 @@ def _probe_call(rc: int, what: str) -> None:
 
 def mfma_probe(steps: int, warmup: int, grid: int = 1024, iters: int = 20000) -> dict:
     """bf16 MFMA issue with no memory traffic: grid workgroups of 4 waves, one
-    per SIMD, each wave iters x 16 independent 32x32x16 MFMAs; once on small
-    constant operands and once on random bf16 fragments (the multipliers
-    switch as with a GEMM's data, and the chip's power limit sets the clock
-    accordingly)."""
+    per SIMD, each wave iters x 16 independent 32x32x16 MFMAs (or iters x 64
+    of 16x16x32, twice the flops); once on small constant operands and once on
+    random bf16 fragments (the multipliers switch as with a GEMM's data, and
+    the chip's power limit sets the clock accordingly)."""
     import torch
     lib = _probe_lib()
     out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
@@ -461,17 +462,19 @@ def mfma_probe(steps: int, warmup: int, grid: int = 1024, iters: int = 20000) ->
     gen.manual_seed(5)
     frag = torch.randn(8 * 256 * 8, generator=gen, device="cuda").to(torch.bfloat16)
     stream = torch.cuda.current_stream()
-    flops = grid * 4 * iters * 16 * 32768
-    res = {"probe": "mfma_only (v_mfma_f32_32x32x16_bf16 back to back, no memory traffic)", "grid": grid,
-           "iters": iters, "flops_per_call": flops}
-    for key, ptr in (("constant_operands", None), ("random_operands", frag.data_ptr())):
-        _log(f"mfma probe ({key}): {grid} workgroups x {iters} iterations")
-        t = _time_launches(lambda: _probe_call(lib.ll_probe_mfma_only(grid, iters, ptr, out.data_ptr(),
-                                                                      stream.cuda_stream), "ll_probe_mfma_only"),
-                           steps, warmup, stream)
-        tf = flops / (t["ms"] * 1e-3) / 1e12
-        res[key] = {"ms": round(t["ms"], 4), "median_ms": round(t["median_ms"], 4), "TFLOP/s": round(tf, 1),
-                    "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    res = {"probe": "mfma_only (bf16 MFMAs back to back, no memory traffic)", "grid": grid, "iters": iters}
+    for shape, fn, flops in (("32x32x16", "ll_probe_mfma_only", grid * 4 * iters * 16 * 32768),
+                             ("16x16x32", "ll_probe_mfma16_only", grid * 4 * iters * 64 * 16384)):
+        call = getattr(lib, fn)
+        sub = {"instruction": f"v_mfma_f32_{shape}_bf16", "flops_per_call": flops}
+        for key, ptr in (("constant_operands", None), ("random_operands", frag.data_ptr())):
+            _log(f"mfma probe {shape} ({key}): {grid} workgroups x {iters} iterations")
+            t = _time_launches(lambda: _probe_call(call(grid, iters, ptr, out.data_ptr(), stream.cuda_stream), fn),
+                               steps, warmup, stream)
+            tf = flops / (t["ms"] * 1e-3) / 1e12
+            sub[key] = {"ms": round(t["ms"], 4), "median_ms": round(t["median_ms"], 4), "TFLOP/s": round(tf, 1),
+                        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        res[shape] = sub
     return res
 
 

@@ -8,9 +8,11 @@
  *
  *  - MFMA issue: waves that do nothing but back-to-back bf16 matrix
  *    multiply-accumulates (v_mfma_f32_32x32x16_bf16, the instruction of the
- *    library's bf16 GEMM and linear compression), with no memory traffic and
- *    no dependency stalls.  Its rate, at the clock the chip holds while doing
- *    it, bounds any bf16 kernel on this GPU.
+ *    library's producer/consumer GEMM kinds and linear compression, or
+ *    v_mfma_f32_16x16x32_bf16, that of its hand-ordered GEMM kind), with no
+ *    memory traffic and no dependency stalls.  Its rate, at the clock the
+ *    chip holds while doing it, bounds any bf16 kernel on this GPU built on
+ *    that instruction.
  *  - HBM streaming: a plain copy (one stream read, one written) and a pass
  *    that reads four streams and writes one (the 4:1 read:write byte mix of
  *    the linear-compression workload), 16-byte accesses, no reuse.
@@ -39,6 +41,13 @@ extern "C" {
  * out: grid * 256 floats (each lane's accumulator sum, so the work is not
  * dead).  grid in [1, 2^20], iters in [0, 2^24]. */
 int ll_probe_mfma_only(int grid, int iters, const void* operands, float* out, void* stream);
+
+/* As ll_probe_mfma_only with v_mfma_f32_16x16x32_bf16 (the instruction of
+ * the library's 256x256 hand-ordered GEMM kind): each wave keeps 64
+ * independent 16x16 accumulators and issues iters x 64 MFMAs of 16384 flops:
+ * grid * 4 * iters * 64 * 16384 flops per call (twice ll_probe_mfma_only's
+ * at the same iters).  Same arguments, limits and errors. */
+int ll_probe_mfma16_only(int grid, int iters, const void* operands, float* out, void* stream);
 
 /* y[i] = x[0][i] ^ x[1][i] ^ ... ^ x[streams-1][i] over n16 16-byte elements
  * per stream: x holds `streams` consecutive arrays of n16 16-byte elements

@@ -10,6 +10,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // 16 independent accumulators per wave (the 128x128 block of four 32x32
 // tiles by four that a GEMM wave holds): an MFMA's result is next needed 16
@@ -50,6 +51,44 @@ void mfma_only_kernel(int iters, const uint4* __restrict__ frag, float* out) {
   for (int j = 0; j < 16; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) s += acc[j][e];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// The same with the 16x16x32 MFMA (the library's hand-ordered GEMM loop's):
+// the 128x128 block as 8 x 8 accumulators of 16x16, 64 independent MFMAs per
+// iteration (16384 flops each, twice the 32x32 probe's flops per
+// iteration), A fragment i and B fragment j for accumulator (i, j).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma16_only_kernel(int iters, const uint4* __restrict__ frag, float* out) {
+  bf16x8 a[8], b[8];
+  if (frag) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = __builtin_bit_cast(bf16x8, frag[(i & 3) * 256 + threadIdx.x]);
+      b[i] = __builtin_bit_cast(bf16x8, frag[(4 + (i & 3)) * 256 + ((threadIdx.x + 32 * (i >> 2)) & 255)]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[i][e] = (__bf16)(float)((threadIdx.x + e + i) & 7);
+        b[i][e] = (__bf16)(float)((3 * threadIdx.x + e + i) & 7);
+      }
+  }
+  f32x4 acc[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) acc[j] = f32x4{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j >> 3], b[j & 7], acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 64; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += acc[j][e];
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -113,6 +152,13 @@ extern "C" int ll_probe_mfma_only(int grid, int iters, const void* operands, flo
   if (grid < 1 || grid > (1 << 20) || iters < 0 || iters > (1 << 24) || !out) return -1;
   if ((uintptr_t)operands & 15) return -1;
   mfma_only_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(iters, (const uint4*)operands, out);
+  return (int)hipGetLastError();
+}
+
+extern "C" int ll_probe_mfma16_only(int grid, int iters, const void* operands, float* out, void* stream) {
+  if (grid < 1 || grid > (1 << 20) || iters < 0 || iters > (1 << 24) || !out) return -1;
+  if ((uintptr_t)operands & 15) return -1;
+  mfma16_only_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(iters, (const uint4*)operands, out);
   return (int)hipGetLastError();
 }
 

@@ -168,6 +168,7 @@ PROBE_LIB = os.path.join(ROOT, "recsys_linear_layers_amd", "libllprobes.so")
 def _probe_lib():
     lib = ctypes.CDLL(PROBE_LIB)
     lib.ll_probe_mfma_only.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ll_probe_mfma16_only.argtypes = lib.ll_probe_mfma_only.argtypes
     lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_int, ctypes.c_void_p]
     return lib
@@ -175,7 +176,7 @@ def _probe_lib():
 
 def test_probe_library_exports_every_declared_symbol():
     names = re.findall(r"^int\s+(\w+)\s*\(", open(PROBE_HEADER).read(), re.M)
-    assert sorted(names) == ["ll_probe_mfma_only", "ll_probe_stream"]
+    assert sorted(names) == ["ll_probe_mfma16_only", "ll_probe_mfma_only", "ll_probe_stream"]
     lib = ctypes.CDLL(PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -184,10 +185,11 @@ def test_probe_library_exports_every_declared_symbol():
 def test_probes_reject_bad_arguments_on_the_host():
     """Every rejected call returns -1 before any HIP call is made."""
     lib = _probe_lib()
-    assert lib.ll_probe_mfma_only(0, 10, None, 256, None) == -1    # grid < 1
-    assert lib.ll_probe_mfma_only(1, -1, None, 256, None) == -1    # iters < 0
-    assert lib.ll_probe_mfma_only(1, 10, None, None, None) == -1   # no output
-    assert lib.ll_probe_mfma_only(1, 10, 4100, 256, None) == -1    # misaligned operands
+    for f in (lib.ll_probe_mfma_only, lib.ll_probe_mfma16_only):
+        assert f(0, 10, None, 256, None) == -1    # grid < 1
+        assert f(1, -1, None, 256, None) == -1    # iters < 0
+        assert f(1, 10, None, None, None) == -1   # no output
+        assert f(1, 10, 4100, 256, None) == -1    # misaligned operands
     assert lib.ll_probe_stream(2, 0, 4096, 1 << 20, 16, 1, None) == -1  # streams not 1 or 4
     assert lib.ll_probe_stream(1, 4, 4096, 1 << 20, 16, 1, None) == -1  # unknown hint bits
     assert lib.ll_probe_stream(1, 0, 4096, 1 << 20, -1, 1, None) == -1  # n16 < 0
