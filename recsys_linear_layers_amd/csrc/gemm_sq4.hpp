@@ -36,6 +36,16 @@ struct Sq4 {
   static constexpr int SLOT = 65536, B_OFF = 32768, LDS = 2 * SLOT;
 };
 
+// Chunk swizzle of the B tile's k-rows (512 bytes, 32 chunks of 16 bytes
+// each): chunk c of k-row kr sits at c ^ sq4_swz_b(kr).  A transposing B
+// read serves 32 lanes at a time, and those take k-rows kr..kr+3 and
+// kr+8..kr+11 at the same 16 columns; bits 0-1 of kr spread the first four
+// over four bank groups and bit 3 moves the other four to four more, so the
+// pass touches every bank once.  Bits 2 and 5 are left alone: the second
+// half of a fragment (k-rows +4) and the next k32 step (k-rows +32) then sit
+// at constant offsets from the first.
+__device__ __forceinline__ int sq4_swz_b(int kr) { return ((kr & 3) << 2) | (((kr >> 3) & 1) << 1); }
+
 // Longest wait at a round barrier, in ticks of the 100 MHz clock (30 us; the
 // drift it corrects is a few us per round).
 constexpr uint64_t kSyncWaitTicks = 3000;
@@ -225,8 +235,8 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
   // A block i (16 rows) at k32 step kk: blocks i and i+4 share the swizzle
   // (rows 64 apart), so one address per (slot, kk, i % 4) serves both
   // (+8192).  B fragment j (16 columns): two transposing reads, each giving
-  // a lane 4 k of its column; the swizzle depends on the k-row modulo 4
-  // only, so step kk is +16384*kk and the second half (k-rows +4) +2048
+  // a lane 4 k of its column; the swizzle (sq4_swz_b) ignores k-row bits 2
+  // and 5, so step kk is +16384*kk and the second half (k-rows +4) +2048
   // from the step-0 address.
   uint32_t fa[2][2][4], fb[2][8];
 #pragma unroll
@@ -245,7 +255,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       const int mn = wn0 + 16 * j + 4 * (sl & 3);
       const int kr = 8 * g + (sl >> 2);
       const int lc = mn >> 3, half = (mn & 7) * 2;
-      fb[s][j] = base + s * Sq4::SLOT + Sq4::B_OFF + kr * 512 + ((lc ^ swz_mn<32>(kr)) << 4) + half;
+      fb[s][j] = base + s * Sq4::SLOT + Sq4::B_OFF + kr * 512 + ((lc ^ sq4_swz_b(kr)) << 4) + half;
     }
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(base + wave * 1024);
@@ -286,7 +296,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       const int lca = (lane & 7) ^ swz_k<8>(row);
       va[i] = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda + lca * 8) * 2u : kOOB;
       const int kr = q * 2 + (lane >> 5);
-      const int lcb = (lane & 31) ^ swz_mn<32>(kr);
+      const int lcb = (lane & 31) ^ sq4_swz_b(kr);
       vb[i] = ti.n0 + lcb * 8 < p.b.rows ? (uint32_t)(kr * ldb + lcb * 8) * 2u : kOOB;
     }
     const int64_t oa = (int64_t)ti.m0 * p.a.ld + (int64_t)ti.kb * Sq4::KT;
