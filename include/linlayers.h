@@ -130,7 +130,13 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * XCD's workgroups within a round of one another (round_sync=1 in the
  * description; LL_GEMM_ROUND_SYNC=0, or 1 for two rounds or more, overrides): a bounded wait between
  * rounds, so that tiles sharing A and B panels read them from L2 together;
- * its counters take 1 KB of workspace.  The environment variable LL_GEMM_KIND (a
+ * its counters take 1 KB of workspace.  When a KIND_SQ4_HO plan's last round
+ * would hold at most half as many tiles as the grid has workgroups (and K
+ * has at least 32 slices of 64), those tiles are split 2-4 ways along K
+ * (tail=<tiles>x<splits> in the description; LL_GEMM_TAIL_SPLIT=0 turns it
+ * off): each split leaves a 256x256 fp32 partial in the workspace, and a
+ * reduce kernel adds them in ascending split order, then applies the
+ * epilogue.  The environment variable LL_GEMM_KIND (a
  * kernel name as printed by gemm_plan_describe, or its index) forces a
  * kernel for configuration sweeps; a forced kernel that cannot take the
  * operands (a 192-row tile with an M-contiguous A, KIND_SQ4_HO outside the
@@ -164,10 +170,11 @@ ll_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
  * null workspace with a non-zero requirement, or a workspace not 256-byte
  * aligned), LL_ERR_HIP (launch failure).  Packed copies live in the
  * workspace with rows padded to whole 128-byte lines: A K-contiguous
- * [M][ldp], B N-contiguous [K][ldp]; so do split-K partials and the round
- * counters of plans with round_sync=1 (zeroed by the call itself).
+ * [M][ldp], B N-contiguous [K][ldp]; so do split-K partials, the round
+ * counters of plans with round_sync=1 (zeroed by the call itself) and the
+ * partial tiles of a K-split last round.
  * The call only launches kernels on `stream` (pack, counter clear, GEMM,
- * split-K reduce or the K == 0 fill): it allocates nothing and records no memset or copy, so
+ * split-K or tail reduce, or the K == 0 fill): it allocates nothing and records no memset or copy, so
  * it may be captured into a HIP graph; replays reuse the captured pointers.
  */
 ll_status gemm_run(const gemm_plan* plan, const void* A, const void* B, void* C,
@@ -186,7 +193,7 @@ ll_status gemm_run_ex(const gemm_plan* plan, const void* A, const void* B, void*
  * gemm_run_ex without a caller workspace, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  The plan's workspace (packed operand copies,
- * split-K partials, round counters) is taken from a device array inside the library, one per
+ * split-K partials, round counters, tail partials) is taken from a device array inside the library, one per
  * GPU, LL_NOALLOC_SCRATCH_BYTES long, which each GPU the library runs on
  * holds from the library's load until the process ends.  The call allocates
  * and frees nothing and calls no allocating library routine; its first call

@@ -246,6 +246,43 @@ hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int
   return hipGetLastError();
 }
 
+// The hand-ordered kind's last-round tiles that were split along K: tile
+// tail_first + i (grouped order, 256x256) sums its splits' partials
+// P[(i * splits + s)][256][256] in ascending s, then bias, activation and the
+// C conversion.  Workgroup b takes rows 4 (b % 64) .. + 3 of tile b / 64,
+// each thread four consecutive columns.
+__global__ void __launch_bounds__(256) tail_reduce_kernel(const float* __restrict__ P, int splits, int tail_first,
+                                                          int tiles_m, int tiles_n, int group_m, int64_t M,
+                                                          int64_t N, void* __restrict__ C, int64_t ldcm,
+                                                          int64_t ldcn, int c_fmt, const float* __restrict__ bias,
+                                                          int act) {
+  const int i = blockIdx.x >> 6;
+  const int rl = 4 * (blockIdx.x & 63) + (threadIdx.x >> 6);
+  const int cl = 4 * (threadIdx.x & 63);
+  int tm, tn;
+  grouped_tile(tail_first + i, tiles_m, tiles_n, group_m, tm, tn);
+  const int64_t row = (int64_t)tm * 256 + rl;
+  const int64_t col0 = (int64_t)tn * 256 + cl;
+  if (row >= M || col0 >= N) return;
+  const float* q = P + (int64_t)i * splits * 65536 + rl * 256 + cl;
+  f32x4 acc = *(const f32x4*)q;
+  for (int s = 1; s < splits; ++s) acc += *(const f32x4*)(q + (int64_t)s * 65536);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t col = col0 + e;
+    if (col < N) store_c(C, row * ldcm + col * ldcn, epi_rt(acc[e], bias ? bias[col] : 0.f, act), c_fmt);
+  }
+}
+
+hipError_t launch_tail_reduce(const float* partial, int splits, int tail_first, int tail_tiles, int tiles_m,
+                              int tiles_n, int group_m, int64_t M, int64_t N, void* C, int64_t ldcm, int64_t ldcn,
+                              int c_fmt, const float* bias, int act, hipStream_t stream) {
+  if (tail_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(tail_tiles * 64), dim3(256), 0, stream, partial, splits, tail_first,
+                     tiles_m, tiles_n, group_m, M, N, C, ldcm, ldcn, c_fmt, bias, act);
+  return hipGetLastError();
+}
+
 // K == 0: every sum is empty, so C = epilogue(0).
 __global__ void __launch_bounds__(256) fill_zero_kernel(void* __restrict__ C, int64_t M, int64_t N,
                                                         int64_t ldcm, int64_t ldcn, int c_fmt,

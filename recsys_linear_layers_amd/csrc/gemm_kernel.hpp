@@ -76,6 +76,13 @@ struct GemmKArgs {
   // Hand-ordered kind only: per-XCD round counters (8 x 32 words, zeroed
   // before the launch), or null for no round barrier.
   uint32_t* sync;
+  // Hand-ordered kind only: work items from tail_first on split the tiles of
+  // a last round that would leave CUs idle tail_splits ways along K
+  // (tail_kps slices each, the last split the rest) and leave raw fp32
+  // partials in tail_partial ([item - tail_first][256][256]); a reduce
+  // kernel finishes those tiles.  tail_first == total: no tail split.
+  int32_t tail_first, tail_splits, tail_kps;
+  float* tail_partial;
 };
 
 template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,
@@ -337,6 +344,18 @@ struct TileInfo {
   int ks, m0, n0, kb, ke;
 };
 
+// Tile tin (0 .. tiles_m * tiles_n - 1) in grouped order: groups of group_m
+// tile rows, column by column within a group.
+__device__ __forceinline__ void grouped_tile(int tin, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int gid = tin / per_group;
+  const int first_m = gid * group_m;
+  const int gsz = min(tiles_m - first_m, group_m);
+  const int w = tin - gid * per_group;
+  tm = first_m + w % gsz;
+  tn = w / gsz;
+}
+
 template <class Cfg>
 __device__ __forceinline__ TileInfo decode_tile(const GemmKArgs& p, int t) {
   const int tiles = p.tiles_m * p.tiles_n;
@@ -346,13 +365,10 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmKArgs& p, int t) {
   ti.ks = rest;
   ti.kb = rest * p.kps;
   ti.ke = min(ti.kb + p.kps, p.kiters);
-  const int per_group = p.group_m * p.tiles_n;
-  const int gid = tin / per_group;
-  const int first_m = gid * p.group_m;
-  const int gsz = min(p.tiles_m - first_m, p.group_m);
-  const int w = tin - gid * per_group;
-  ti.m0 = (first_m + w % gsz) * Cfg::BM;
-  ti.n0 = (w / gsz) * Cfg::BN;
+  int tm, tn;
+  grouped_tile(tin, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  ti.m0 = tm * Cfg::BM;
+  ti.n0 = tn * Cfg::BN;
   return ti;
 }
 

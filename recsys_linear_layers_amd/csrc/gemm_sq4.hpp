@@ -117,6 +117,40 @@ __device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileIn
   }
 }
 
+// Work item t: a whole tile, or (from p.tail_first on) one K split of a tile
+// of the last round, whose raw fp32 sums go to slot t - p.tail_first of
+// p.tail_partial (slot -1 for a whole tile).
+__device__ __forceinline__ TileInfo sq4_decode(const GemmKArgs& p, int t, int& slot) {
+  if (t < p.tail_first) {
+    slot = -1;
+    return decode_tile<Sq4>(p, t);
+  }
+  slot = t - p.tail_first;
+  TileInfo ti = decode_tile<Sq4>(p, p.tail_first + slot / p.tail_splits);
+  ti.ks = slot % p.tail_splits;
+  ti.kb = ti.ks * p.tail_kps;
+  ti.ke = min(ti.kb + p.tail_kps, p.kiters);
+  return ti;
+}
+
+// A K split's raw sums into its [256][256] fp32 partial tile (every element,
+// also those past M or N: the reduce reads only those inside C).
+template <int N>
+__device__ __forceinline__ void sq4_tail_block(float* part, int wm0, int wn0, int lane) {
+  constexpr int I = N >> 3, J = N & 7;
+  const f32x4 v = sq4_acc<N>();
+  float* q = part + (wm0 + 16 * I + 4 * (lane >> 4)) * 256 + wn0 + 16 * J + (lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) q[r * 256] = v[r];
+}
+
+__device__ __forceinline__ void sq4_tail_all(const GemmKArgs& p, int slot, int wm0, int wn0, int lane) {
+  float* part = p.tail_partial + (int64_t)slot * (Sq4::BM * Sq4::BN);
+#define LL_SQ4_TAIL(n) sq4_tail_block<n>(part, wm0, wn0, lane);
+  LL_SQ4_BLOCKS(LL_SQ4_TAIL)
+#undef LL_SQ4_TAIL
+}
+
 template <int EPI>
 __device__ __forceinline__ void sq4_store_all(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0, int lane) {
   float bias[8];
@@ -286,7 +320,8 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       }
       lds_barrier();
     }
-    const TileInfo ti = decode_tile<Sq4>(p, t);
+    int slot;
+    const TileInfo ti = sq4_decode(p, t, slot);
     int n = ti.ke - ti.kb;
     uint32_t va[8], vb[8];
 #pragma unroll
@@ -339,6 +374,10 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
 
     lds_barrier();  // every wave is done reading the ring before it is reused
     if (cnt && wave == 0 && lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (slot >= 0) {  // a K split of a last-round tile: raw sums for the reduce
+      sq4_tail_all(p, slot, wm0, wn0, lane);
+      continue;
+    }
     // a whole tile inside a 16-bit row-major C with 16-byte aligned rows:
     // staged through LDS (uniform over the workgroup)
     const bool staged = p.c_fast && p.c_fmt != 0 && ti.m0 + Sq4::BM <= p.M && ti.n0 + Sq4::BN <= p.N &&

@@ -85,6 +85,10 @@ hipError_t launch_splitk_reduce(const float* partial, int splits, int64_t M, int
 hipError_t launch_fill_zero(void* C, int64_t M, int64_t N, int64_t ldcm, int64_t ldcn, int c_fmt, const float* bias,
                             int act,
                             hipStream_t stream);
+// Finishes the hand-ordered kind's K-split last-round tiles (tail_reduce_kernel).
+hipError_t launch_tail_reduce(const float* partial, int splits, int tail_first, int tail_tiles, int tiles_m,
+                              int tiles_n, int group_m, int64_t M, int64_t N, void* C, int64_t ldcm, int64_t ldcn,
+                              int c_fmt, const float* bias, int act, hipStream_t stream);
 // Zeroes n 32-bit words with one workgroup (a kernel, so that it may sit in a captured graph).
 hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream);
 

@@ -77,6 +77,15 @@ ll_status current_device(int* dev, const DeviceInfo** info) {
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The hand-ordered kind's tail split: at most this many K splits per tile of
+// a last round that is at most half full, each of at least this many slices.
+// Measured with and without it, same process: the edge shape (128 tiles, 2
+// splits) +8.8%, 8448^2 x 4096 (65 x 3) +10.6%, 12288 x 4608 x 8192 (96 x
+// 2) +8.9%, 4352 x 4096 x 4096 (16 x 4) +18.4%; with 8-slice splits
+// (8448^2 x 1024) -3.6%, the partials' traffic outweighing the time saved.
+constexpr int kTailMaxSplits = 4;
+constexpr int kTailMinSlices = 16;
+
 // The hand-ordered kind's round counters: one per XCD, 128 bytes apart.
 constexpr int kRoundSyncWords = 8 * 32;
 // Fewest rounds (passes of the persistent grid over its tiles) for which the
@@ -125,8 +134,10 @@ struct gemm_plan {
   int kiters, kps;
   int tiles_m, tiles_n, total, grid, group_m;
   int round_sync;   // hand-ordered kind: round barrier per XCD (counters in the workspace)
+  int tail_tiles, tail_splits, tail_kps, tail_first;  // hand-ordered kind: K-split last round
   size_t ws_partial_off;
   size_t ws_sync_off;
+  size_t ws_tail_off;
   size_t ws_bytes;
 };
 
@@ -404,6 +415,33 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   p.grid = (int)(p.total < slots ? p.total : slots);
   if (p.grid < 1) p.grid = 1;
   p.group_m = 8;
+  // Tail split for the hand-ordered kind: when the last round of a
+  // persistent grid holds at most half as many tiles as there are
+  // workgroups, the rest of the chip would idle through it.  Those tiles are
+  // split along K instead (s ways, s * tiles <= grid), their splits write raw
+  // fp32 partials to the workspace, and a reduce kernel sums them in
+  // ascending order and applies the epilogue.  The round then takes about
+  // 1/s of its time.  LL_GEMM_TAIL_SPLIT=0 turns it off (measurement).
+  p.tail_tiles = 0;
+  p.tail_splits = 1;
+  p.tail_kps = p.kiters;
+  p.tail_first = p.total;
+  if (kind == KIND_SQ4_HO && splits == 1 && tiles > p.grid && p.kiters >= 2 * kTailMinSlices) {
+    const int64_t last = tiles % p.grid;
+    const char* env = getenv("LL_GEMM_TAIL_SPLIT");
+    if (last > 0 && last * 2 <= p.grid && !(env && env[0] == '0')) {
+      int s = (int)std::min<int64_t>(std::min<int64_t>(p.grid / last, kTailMaxSplits), p.kiters / kTailMinSlices);
+      const int kps = s > 0 ? (p.kiters + s - 1) / s : p.kiters;
+      if (s >= 2) s = (p.kiters + kps - 1) / kps;  // every split gets >= 1 slice (>= kTailMinSlices but the last)
+      if (s >= 2) {
+        p.tail_tiles = (int)last;
+        p.tail_splits = s;
+        p.tail_kps = kps;
+        p.tail_first = (int)(tiles - last);
+        p.total = p.tail_first + (int)last * s;
+      }
+    }
+  }
   // Round barrier per XCD for the hand-ordered kind (gemm_sq4.hpp): on
   // FFN-up (28 rounds of 256 tiles) it cut the bytes fetched past L2 from
   // 16.9 to 12.1 GB and the time by 2-4%.  It needs the grid to be whole
@@ -429,6 +467,8 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   if (splits > 1) off = align256(off + (size_t)splits * M * N * 4);
   p.ws_sync_off = off;
   if (p.round_sync) off = align256(off + kRoundSyncWords * 4);
+  p.ws_tail_off = off;
+  if (p.tail_tiles > 0) off = align256(off + (size_t)p.tail_tiles * p.tail_splits * 256 * 256 * 4);
   p.ws_bytes = off;
 
   gemm_plan* h = new (std::nothrow) gemm_plan(p);
@@ -450,9 +490,10 @@ ll_status gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
                                "A:M-major,B:N-major"};
   snprintf(buf, len,
            "kernel=%s tile=%dx%d layout=%s packA=%d packB=%d tiles=%dx%d splitk=%d kiters=%d grid=%d cus=%d "
-           "group_m=%d ws=%zu epilogue=0x%x fused=%d round_sync=%d",
+           "group_m=%d ws=%zu epilogue=0x%x fused=%d round_sync=%d tail=%dx%d",
            k.name, k.bm, k.bn, lay[p->layout], (int)p->a.pack, (int)p->b.pack, p->tiles_m, p->tiles_n, p->splits,
-           p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes, p->d.epilogue, p->epi, p->round_sync);
+           p->kiters, p->grid, p->cus, p->group_m, p->ws_bytes, p->d.epilogue, p->epi, p->round_sync, p->tail_tiles,
+           p->tail_splits);
   return ok();
 }
 
@@ -607,6 +648,10 @@ static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B,
     k.c_fast = d.stride_cn == 1 && d.stride_cm % 2 == 0 && ((uintptr_t)C & 3) == 0 &&
                d.stride_cm * (d.M + 256) < (1ll << 31);
   }
+  k.tail_first = p->tail_first;
+  k.tail_splits = p->tail_splits;
+  k.tail_kps = p->tail_kps;
+  if (p->tail_tiles > 0) k.tail_partial = (float*)((char*)ws + p->ws_tail_off);
   if (p->round_sync) {
     k.sync = (uint32_t*)((char*)ws + p->ws_sync_off);
     e = launch_clear_words(k.sync, kRoundSyncWords, st);
@@ -615,6 +660,11 @@ static ll_status gemm_run_impl(const gemm_plan* p, const void* A, const void* B,
   e = p->epi ? launch_gemm_epi(p->layout, p->kind, d.a_type == LL_F16, p->epi, k, p->grid, st)
              : launch_gemm(p->layout, p->kind, d.a_type == LL_F16, k, p->grid, st);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  if (p->tail_tiles > 0) {
+    e = launch_tail_reduce(k.tail_partial, p->tail_splits, p->tail_first, p->tail_tiles, p->tiles_m, p->tiles_n,
+                           p->group_m, d.M, d.N, C, d.stride_cm, d.stride_cn, cfmt, bias, act, st);
+    if (e != hipSuccess) return hip_fail(e, "tail reduce launch");
+  }
   if (p->splits > 1) {
     e = launch_splitk_reduce(k.partial, p->splits, d.M, d.N, C, d.stride_cm, d.stride_cn, cfmt, bias, act, st);
     if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");

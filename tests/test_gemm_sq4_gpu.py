@@ -2,6 +2,8 @@
 shapes of every kind of edge, against the fp64 oracle: ragged M and N, one,
 two, three and many 64-deep slices, split K, bf16 and fp16 operands, every
 output type, packed operands, integer inputs bit for bit, and full size."""
+import re
+
 import numpy as np
 import pytest
 
@@ -337,3 +339,118 @@ def test_round_barrier_changes_no_bits(act, monkeypatch):
         if act:
             ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
         acceptance.assert_close(got[r0:r0 + nr], ref, S, "bf16", f"rows {r0}.. {d1}", act=act)
+
+
+def _grouped(tin, tiles_m, tiles_n, group_m=8):
+    """Tile (row, column) of grouped-order tile index tin, as the plan orders tiles."""
+    per = group_m * tiles_n
+    g, w = divmod(tin, per)
+    first = g * group_m
+    gsz = min(tiles_m - first, group_m)
+    return first + w % gsz, w // gsz
+
+
+def _tail_tiles(d, M, N):
+    m = re.search(r"\btail=(\d+)x(\d+)", d)
+    tiles_m, tiles_n = -(-M // 256), -(-N // 256)
+    nt = int(m.group(1))
+    first = tiles_m * tiles_n - nt
+    return [_grouped(first + i, tiles_m, tiles_n) for i in range(nt)], int(m.group(2))
+
+
+def test_tail_split_selection():
+    """A last round at most half full is split along K (up to 4 ways, at
+    least 16 slices a split, splits x tiles within the grid); whole rounds,
+    short K and other kinds are left alone."""
+    import recsys_linear_layers_amd as ll
+    assert " tail=128x2" in _describe(8191, 5003, 4099, b_col=True)   # 640 tiles: 2 rounds + 128
+    assert " tail=65x3" in _describe(8448, 8448, 4096)                   # 1089 tiles: 4 rounds + 65
+    for M, N, K in [(4096, 4096, 4096), (16384, 28672, 8192), (8192, 8192, 8192)]:
+        assert " tail=0x1" in _describe(M, N, K)                         # whole rounds
+    d = _describe(8448, 8448, 1984)                                      # 31 slices: splits would be short
+    assert f"kernel={KIND} " in d and " tail=0x1" in d, d
+    d = _describe(8191, 5003, 4099, b_col=True)
+    assert int(d.split(" ws=")[1].split()[0]) >= 128 * 2 * 256 * 256 * 4, d
+
+
+def _run_tail(A, B, C, monkeypatch, split, bias=None, act=None):
+    import torch
+    import recsys_linear_layers_amd as ll
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", KIND)
+    if not split:
+        monkeypatch.setenv("LL_GEMM_TAIL_SPLIT", "0")
+    try:
+        ll.gemm(A, B, out=C, bias=bias, act=act)
+        torch.cuda.synchronize()
+        ep = (ll.LL_EPI_BIAS if bias is not None else 0) | ll.ACTIVATIONS[act]
+        d = ll.plan_for(A, B, C, 0, ep).describe()
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        monkeypatch.delenv("LL_GEMM_TAIL_SPLIT", raising=False)
+        ll._plans.clear()
+    assert f"kernel={KIND} " in d, d
+    return d
+
+
+@pytest.mark.parametrize("out,act", [("bf16", None), ("bf16", "gelu"), ("f32", None), ("f32", "silu")])
+def test_tail_split_against_oracle(out, act, monkeypatch):
+    """4300 x 4100 x 4096: 17 x 17 = 289 tiles, a last round of 33 split four
+    ways (16 slices each), the ragged last tile row among them.  Every tail
+    tile is checked on 64 sampled entries and a full row strip, every other
+    tile on one entry; fp32 C with a row stride of N + 8."""
+    import torch
+    M, N, K = 4300, 4100, 4096
+    c = synth.gemm_case(M, N, K, seed=311 + (act is not None) + 2 * (out == "f32"), out_dtype=out,
+                        dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    bias = None
+    if act:
+        bias = torch.from_numpy(np.random.default_rng(312).standard_normal(N).astype(np.float32)).cuda()
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[out]
+    big = torch.full((M, N + 8), float("nan"), dtype=dt, device="cuda")
+    C = big[:, :N] if out == "f32" else torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    d = _run_tail(A, B, C, monkeypatch, True, bias, act)
+    assert " tail=33x4" in d, d
+    got = to_f64(C)
+    tails, _ = _tail_tiles(d, M, N)
+    rng = np.random.default_rng(313)
+    rows, cols = per_tile_indices(M, N, (256, 256), 314)
+    rows, cols = list(rows), list(cols)
+    for tm, tn in tails:
+        h, w = min(256, M - 256 * tm), min(256, N - 256 * tn)
+        rows += list(256 * tm + rng.integers(0, h, 64))
+        cols += list(256 * tn + rng.integers(0, w, 64))
+    rows, cols = np.array(rows), np.array(cols)
+    ref, S = oracle.gemm_case_entries(c, rows, cols)
+    if act:
+        ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act, cols=cols)
+    acceptance.assert_close(got[rows, cols], ref, S, out, f"tail samples {d}", act=act)
+    for tm in sorted({tm for tm, _ in tails}):
+        r0 = 256 * tm + 5 if 256 * tm + 5 < M else 256 * tm
+        nr = min(4, M - r0)
+        ref, S = oracle.gemm_case(c, rows=(r0, nr))
+        if act:
+            ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+        acceptance.assert_close(got[r0:r0 + nr], ref, S, out, f"tail rows {r0}.. {d}", act=act)
+    if out == "f32":
+        assert torch.isnan(big[:, N:]).all()   # the padding columns are untouched
+
+
+def test_tail_split_integer_inputs_bit_exact(monkeypatch):
+    """With small integer inputs every partial sum is exact: the K-split tail
+    tiles give the same bits as the unsplit kernel, and the oracle's."""
+    import torch
+    M, N, K = 4352, 4096, 2048
+    c = synth.gemm_case(M, N, K, dist=("int", -4, 4), seed=315, out_dtype="f32")
+    A, B = gemm_operands(c)
+    C1 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    C2 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    d1 = _run_tail(A, B, C1, monkeypatch, True)
+    d2 = _run_tail(A, B, C2, monkeypatch, False)
+    assert " tail=16x2" in d1 and " tail=0x1" in d2, (d1, d2)
+    assert torch.equal(C1, C2)
+    tails, _ = _tail_tiles(d1, M, N)
+    tm, tn = tails[-1]
+    ref, _ = oracle.gemm_case(c, rows=(256 * tm, 8))
+    assert np.array_equal(to_f64(C1)[256 * tm:256 * tm + 8], ref)

@@ -2,7 +2,8 @@
 workspace in a device array inside the library) against gemm_run_ex with the
 plan's own workspace, through the C ABI: results must be bit-identical (same
 kernels, same order of sums), on two calls in a row, the second smaller, for
-split-K partials and packed operand copies; plus the size limit."""
+split-K partials, packed operand copies and the round counters of the
+hand-ordered kind; plus the size limit."""
 import ctypes
 
 import numpy as np
@@ -73,6 +74,31 @@ def test_packed_operands_two_calls_second_smaller():
         return c
     _check(case(1030, 777, 1301, 304, "noalloc_pack_big"), want="packA=1 packB=1")
     _check(case(300, 260, 519, 305, "noalloc_pack_small"), act="gelu", bias_seed=306, want="packA=1 packB=1")
+
+
+def test_round_counters_two_calls_second_smaller(monkeypatch):
+    # the hand-ordered kind with its round barrier: the counters sit in the
+    # workspace and each call clears them first (2 rounds each: 306, then 289 tiles)
+    monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
+    monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "1")
+    big = synth.gemm_case(4608, 4352, 128, seed=307, out_dtype="bf16", dist=("normal", 0.0, 1.0),
+                          name="noalloc_rounds_big")
+    small = synth.gemm_case(4352, 4160, 64, seed=308, out_dtype="bf16", dist=("normal", 0.0, 1.0),
+                            name="noalloc_rounds_small")
+    _check(big, want="round_sync=1")
+    _check(small, act="silu", bias_seed=309, want="round_sync=1")
+
+
+def test_tail_split_two_calls_second_smaller(monkeypatch):
+    # the hand-ordered kind's K-split last round: partial tiles in the
+    # workspace, then the reduce (289 tiles: 33 split 4 ways, then 2 ways)
+    monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
+    big = synth.gemm_case(4352, 4160, 4096, seed=317, out_dtype="bf16", dist=("normal", 0.0, 1.0),
+                          name="noalloc_tail_big")
+    small = synth.gemm_case(4352, 4160, 2048, seed=318, out_dtype="f32", dist=("normal", 0.0, 1.0),
+                            name="noalloc_tail_small")
+    _check(big, want="tail=33x4")
+    _check(small, act="gelu", bias_seed=319, want="tail=33x2")
 
 
 def test_plan_beyond_the_scratch_size_is_refused():
