@@ -86,6 +86,21 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kTailMaxSplits = 4;
 constexpr int kTailMinSlices = 16;
 
+// K splits of the tail of a hand-ordered plan with `tiles` tiles on `grid`
+// workgroups and `kiters` 64-deep slices: 1 (no tail split) unless there is
+// a whole round and a last round at most half full.
+int tail_splits_for(int64_t tiles, int64_t grid, int kiters) {
+  if (grid <= 0 || tiles <= grid || kiters < 2 * kTailMinSlices) return 1;
+  const int64_t last = tiles % grid;
+  if (last == 0 || last * 2 > grid) return 1;
+  const char* env = getenv("LL_GEMM_TAIL_SPLIT");
+  if (env && env[0] == '0') return 1;
+  int s = (int)std::min<int64_t>(std::min<int64_t>(grid / last, kTailMaxSplits), kiters / kTailMinSlices);
+  if (s < 2) return 1;
+  const int kps = (kiters + s - 1) / s;
+  return (kiters + kps - 1) / kps;  // every split gets >= 1 slice (>= kTailMinSlices but the last)
+}
+
 // The hand-ordered kind's round counters: one per XCD, 128 bytes apart.
 constexpr int kRoundSyncWords = 8 * 32;
 // Fewest rounds (passes of the persistent grid over its tiles) for which the
@@ -344,15 +359,26 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   // N-contiguous, K a multiple of 64 or A packed, with or without a fused
   // epilogue.  Per pass and tile area it runs ~1.3x as fast as the others,
   // so it takes over when its passes times tile area is at most 1.25x theirs
-  // and neither choice would split K.  Measured against the kind the area
-  // rule alone picks, same operands: at 1.11x (8448^2 x 4096) +18%, 1.14x
-  // (12288 x 4608 x 8192) +16%, 1.2x (8191 x 5003 x 4099, both packed) +10%;
-  // at 1.33x (4608^2 x 4096, 6144^2 x 4096, 4608 x 8192 x 4096) -4 to -9%.
+  // and neither choice would split K; a last round it splits along K (the
+  // tail split below) counts as 1/s of a pass.  Measured against the kind
+  // the area rule alone picks, same operands, before the tail split existed:
+  // at 1.11x (8448^2 x 4096) +18%, 1.14x (12288 x 4608 x 8192) +16%, 1.2x
+  // (8191 x 5003 x 4099, both packed) +10%; at 1.33x (4608^2 x 4096, 6144^2 x
+  // 4096, 4608 x 8192 x 4096) -4 to -9%.  With it those three run +19%,
+  // +3.5% and +5.5% (their last rounds split 3, 4 and 4 ways), 4608^2 x 8192
+  // +33%, 4352^2 x 2048 +3.4%; 4352^2 x 1024 (too short to split) -1.3%.
   if (free_choice && sq4_fits &&
       (kind == KIND_WIDE_PC || kind == KIND_TALL_PC || kind == KIND_SQ8_LW4 || kind == KIND_T192_PC)) {
     const int64_t pc = passes(kind), ph = passes(KIND_SQ4_HO);
     const KindInfo& kc = kind_info(kind);
-    if (pc > 0 && ph > 0 && ph * 256 * 256 * 4 <= pc * kc.bm * kc.bn * 5) kind = KIND_SQ4_HO;
+    if (pc > 0 && ph > 0) {
+      // passes in twelfths: whole rounds, and a split last round at 1/s
+      const int64_t tiles_h = ((M + 255) / 256) * ((N + 255) / 256);
+      const int kiters_h = (int)((round_up(d->K, 64) + 63) / 64);
+      const int s = tail_splits_for(tiles_h, p.cus, kiters_h);
+      const int64_t ph12 = s > 1 ? 12 * (tiles_h / p.cus) + 12 / s : 12 * ph;
+      if (ph12 * 256 * 256 * 4 <= 12 * pc * kc.bm * kc.bn * 5) kind = KIND_SQ4_HO;
+    }
   }
   if (d->flags & LL_FLAG_COOPERATIVE) {
     if (kind == KIND_WIDE_PC) kind = KIND_SQ8_K64;
@@ -426,20 +452,15 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   p.tail_splits = 1;
   p.tail_kps = p.kiters;
   p.tail_first = p.total;
-  if (kind == KIND_SQ4_HO && splits == 1 && tiles > p.grid && p.kiters >= 2 * kTailMinSlices) {
-    const int64_t last = tiles % p.grid;
-    const char* env = getenv("LL_GEMM_TAIL_SPLIT");
-    if (last > 0 && last * 2 <= p.grid && !(env && env[0] == '0')) {
-      int s = (int)std::min<int64_t>(std::min<int64_t>(p.grid / last, kTailMaxSplits), p.kiters / kTailMinSlices);
-      const int kps = s > 0 ? (p.kiters + s - 1) / s : p.kiters;
-      if (s >= 2) s = (p.kiters + kps - 1) / kps;  // every split gets >= 1 slice (>= kTailMinSlices but the last)
-      if (s >= 2) {
-        p.tail_tiles = (int)last;
-        p.tail_splits = s;
-        p.tail_kps = kps;
-        p.tail_first = (int)(tiles - last);
-        p.total = p.tail_first + (int)last * s;
-      }
+  if (kind == KIND_SQ4_HO && splits == 1) {
+    const int s = tail_splits_for(tiles, p.grid, p.kiters);
+    if (s >= 2) {
+      const int64_t last = tiles % p.grid;
+      p.tail_tiles = (int)last;
+      p.tail_splits = s;
+      p.tail_kps = (p.kiters + s - 1) / s;
+      p.tail_first = (int)(tiles - last);
+      p.total = p.tail_first + (int)last * s;
     }
   }
   // Round barrier per XCD for the hand-ordered kind (gemm_sq4.hpp): on

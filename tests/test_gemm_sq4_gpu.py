@@ -131,13 +131,14 @@ def test_selected_on_square_and_ffn_shapes(M, N, K):
     (8448, 8448, 4096, False, True),    # 5 passes of 256x256 against 9 of 256x128: 1.11x the area
     (12288, 4608, 8192, False, True),   # 4 against 7 of 128x256: 1.14x
     (8191, 5003, 4099, True, True),     # the edge shape, both operands packed: 3 against 5, 1.2x
-    (4608, 4608, 4096, False, False),   # 2 against 3 of 256x128: 1.33x
-    (6144, 6144, 4096, False, False),   # 3 against 3 of 192x256: 1.33x
+    (4608, 4608, 4096, False, True),    # 1 + 1/3 (last round split 3 ways) against 3 of 256x128: 0.89x
+    (6144, 6144, 4096, False, True),    # 2 + 1/4 against 3 of 192x256: 1.0x
+    (4352, 4352, 1024, False, False),   # 2 (16 slices: no split) against 3 of 256x128: 1.33x
 ])
 def test_selected_up_to_a_quarter_more_area(M, N, K, b_col, want):
     """The hand-ordered kind runs ~1.3x as fast per pass and tile area as the
     other kinds, so it is chosen while it needs at most 1.25x their passes
-    times tile area."""
+    times tile area, a last round it splits s ways along K counting 1/s."""
     assert (f"kernel={KIND} " in _describe(M, N, K, b_col=b_col)) == want
 
 
