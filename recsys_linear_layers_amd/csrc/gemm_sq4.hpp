@@ -36,6 +36,18 @@ struct Sq4 {
   static constexpr int SLOT = 65536, B_OFF = 32768, LDS = 2 * SLOT;
 };
 
+// Chunk swizzle of the A tile's rows (128 bytes, 8 chunks of 16 bytes each):
+// chunk c of row r sits at c ^ sq4_swz_a(r).  A 16-byte fragment read gives
+// lane l row l % 16 and chunk 4 kk + l / 16, and the LDS serves it in passes
+// of lanes 8p..8p+7 with 32+8p..32+8p+7: 8 rows at chunks x and x ^ 2.  The
+// four rows of each parity in such a pass then need one value from each of
+// {0, 2}, {1, 3}, {4, 6}, {5, 7}, and eight consecutive rows eight distinct
+// values: bits 0 and 1 of r swapped, and bit 1 flipped in the odd 8-row
+// half.  Period 16 rows, so blocks 64 rows apart share addresses.
+__device__ __forceinline__ int sq4_swz_a(int r) {
+  return (((r & 1) << 1) | ((r >> 1) & 1) | (r & 4)) ^ (((r >> 3) & 1) << 1);
+}
+
 // Chunk swizzle of the B tile's k-rows (512 bytes, 32 chunks of 16 bytes
 // each): chunk c of k-row kr sits at c ^ sq4_swz_b(kr).  A transposing B
 // read serves 32 lanes at a time, and those take k-rows kr..kr+3 and
@@ -281,7 +293,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       for (int q = 0; q < 4; ++q) {
         const int row = wm0 + 16 * q + (lane & 15);
         const int lc = kk * 4 + (lane >> 4);
-        fa[s][kk][q] = base + s * Sq4::SLOT + row * 128 + ((lc ^ swz_k<8>(row)) << 4);
+        fa[s][kk][q] = base + s * Sq4::SLOT + row * 128 + ((lc ^ sq4_swz_a(row)) << 4);
       }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -328,7 +340,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     for (int i = 0; i < 8; ++i) {
       const int q = wave + 4 * i;
       const int row = q * 8 + (lane >> 3);
-      const int lca = (lane & 7) ^ swz_k<8>(row);
+      const int lca = (lane & 7) ^ sq4_swz_a(row);
       va[i] = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda + lca * 8) * 2u : kOOB;
       const int kr = q * 2 + (lane >> 5);
       const int lcb = (lane & 31) ^ sq4_swz_b(kr);
