@@ -126,7 +126,8 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * passes x tile area (it runs ~1.3x as fast per pass and area); with or
  * without a fused epilogue.  K is split when the tiles fill
  * fewer than half of the CUs.  KIND_SQ4_HO plans with 8 rounds or more
- * (passes of the grid over the tiles) on a grid of whole XCDs also keep each
+ * (passes of the grid over the tiles) of K >= 8192 each, on a grid of whole
+ * XCDs, also keep each
  * XCD's workgroups within a round of one another (round_sync=1 in the
  * description; LL_GEMM_ROUND_SYNC=0, or 1 for two rounds or more, overrides): a bounded wait between
  * rounds, so that tiles sharing A and B panels read them from L2 together;

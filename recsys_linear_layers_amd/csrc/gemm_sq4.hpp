@@ -129,6 +129,12 @@ __device__ __forceinline__ void sq4_store_block(const GemmKArgs& p, const TileIn
   }
 }
 
+// The round barrier's arrival: one lane of wave 0 adds 1 to its XCD's
+// counter (a vector atomic) when cnt is set.
+__device__ __forceinline__ void sq4_count_in(uint32_t* cnt, int wave, int lane) {
+  if (cnt && wave == 0 && lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Work item t: a whole tile, or (from p.tail_first on) one K split of a tile
 // of the last round, whose raw fp32 sums go to slot t - p.tail_first of
 // p.tail_partial (slot -1 for a whole tile).
@@ -312,11 +318,12 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
   // and the 32 workgroups of an XCD share panels only within a round.  Left
   // alone they drift apart by up to a whole tile over many rounds, and then
   // each fetches its panels' slices past L2 for itself.  So a workgroup
-  // counts itself in after its k-loop and, before the next round's first
-  // loads, waits until every workgroup of its XCD has done the same.  The
-  // wait is bounded (kSyncWaitTicks of the 100 MHz clock), so a workgroup
-  // that is not resident costs time but never blocks; the counts change no
-  // arithmetic.
+  // counts itself in once its work item is done (epilogue included: an
+  // epilogue's length varies, and so would the next round's start) and,
+  // before the next round's first loads, waits until every workgroup of its
+  // XCD has done the same.  The wait is bounded (kSyncWaitTicks of the
+  // 100 MHz clock), so a workgroup that is not resident costs time but never
+  // blocks; the counts change no arithmetic.
   uint32_t* const cnt = p.sync ? p.sync + (blockIdx.x & 7) * 32 : nullptr;
   const uint32_t per_xcd = gridDim.x >> 3;
   uint32_t round = 0;
@@ -385,9 +392,9 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
 #undef LL_SQ4_OPERANDS
 
     lds_barrier();  // every wave is done reading the ring before it is reused
-    if (cnt && wave == 0 && lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (slot >= 0) {  // a K split of a last-round tile: raw sums for the reduce
       sq4_tail_all(p, slot, wm0, wn0, lane);
+      sq4_count_in(cnt, wave, lane);
       continue;
     }
     // a whole tile inside a 16-bit row-major C with 16-byte aligned rows:
@@ -401,12 +408,14 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       else
         sq4_stage_all<EPI, 2>(p, ti, wn0, lane, img);
       sq4_flush(p, ti, wm0, wn0, lane, img);
+      sq4_count_in(cnt, wave, lane);
       // the next work item's loads land all over the LDS the other waves
       // may still be reading
       if (t + stride < p.total) lds_barrier();
       continue;
     }
     sq4_store_all<EPI>(p, ti, wm0, wn0, lane);
+    sq4_count_in(cnt, wave, lane);
   }
 }
 

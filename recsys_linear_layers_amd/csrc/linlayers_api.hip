@@ -103,13 +103,16 @@ int tail_splits_for(int64_t tiles, int64_t grid, int kiters) {
 
 // The hand-ordered kind's round counters: one per XCD, 128 bytes apart.
 constexpr int kRoundSyncWords = 8 * 32;
-// Fewest rounds (passes of the persistent grid over its tiles) for which the
-// plan turns the round barrier on.  Measured with and without it, same
-// process: FFN-up (28 rounds) +4.0%, the same with bias + GELU +0.7%,
-// 16384^2 x 4096 (16) +0.6%, 16384 x 8192 x 8192 (8) +0.5%, FFN-down (8)
-// +0.2%; 4 rounds -0.8 to -1.4% (8192^2 x 1024, short rounds, the most),
-// 2 rounds -0.3 to -0.4%.  The drift it removes builds up over rounds.
+// Fewest rounds (passes of the persistent grid over its tiles), and fewest
+// 64-deep slices per tile, for which the plan turns the round barrier on.
+// Measured with and without it, same process: FFN-up (28 rounds of 128
+// slices) +4.9%, the same with bias + GELU +4.1%, FFN-down (8 of 448)
+// +0.35%, 16384 x 8192 x 8192 (8 of 128) +0.1%; shorter tiles lose:
+// 16384^2 x 4096 (16 of 64) -1.8%, 8192^2 x 4096 and 8192^3 (4) -1%,
+// 8192^2 x 1024 (4 of 16) -7%, 4096 x 8192 x 8192 (2) -1.8%.  The drift it
+// removes builds up over many long rounds; on short ones the wait costs more.
 constexpr int kRoundSyncMinRounds = 8;
+constexpr int kRoundSyncMinSlices = 128;
 
 // Byte extent [lo, hi) touched by a 2-D strided view of `rows` x `cols` elements.
 struct Span {
@@ -465,12 +468,14 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   }
   // Round barrier per XCD for the hand-ordered kind (gemm_sq4.hpp): on
   // FFN-up (28 rounds of 256 tiles) it cut the bytes fetched past L2 from
-  // 16.9 to 12.1 GB and the time by 2-4%.  It needs the grid to be whole
-  // XCDs (the work-item remap) and many rounds (kRoundSyncMinRounds).
+  // 16.9 to 12.1 GB and the time by 2-5%.  It needs the grid to be whole
+  // XCDs (the work-item remap) and many long rounds (kRoundSyncMinRounds,
+  // kRoundSyncMinSlices).
   // LL_GEMM_ROUND_SYNC=0 / 1 overrides the choice (measurement).
   {
     const int rounds = p.grid > 0 ? (p.total + p.grid - 1) / p.grid : 0;
-    p.round_sync = kind == KIND_SQ4_HO && p.grid % 8 == 0 && rounds >= kRoundSyncMinRounds;
+    p.round_sync = kind == KIND_SQ4_HO && p.grid % 8 == 0 && rounds >= kRoundSyncMinRounds &&
+                   p.kiters >= kRoundSyncMinSlices;
     if (const char* env = getenv("LL_GEMM_ROUND_SYNC"))
       p.round_sync = env[0] == '1' && kind == KIND_SQ4_HO && p.grid % 8 == 0 && rounds >= 2;
   }

@@ -269,17 +269,18 @@ def test_staged_epilogue_needs_16_byte_aligned_c(monkeypatch):
 
 
 def test_round_barrier_selection(monkeypatch):
-    """Plans of the hand-ordered kind with 8 rounds of tiles or more keep
+    """Plans of the hand-ordered kind with 8 rounds of tiles or more, each of
+    K >= 8192 (128 slices), keep
     each XCD's workgroups a round apart at most (round_sync=1), with their
     counters in the workspace; fewer rounds and other kinds do not, and the
     override turns it on from two rounds or off."""
     import recsys_linear_layers_amd as ll
-    for M, N, K in [(16384, 28672, 8192), (16384, 8192, 28672), (16384, 16384, 4096)]:   # 28, 8, 16 rounds
+    for M, N, K in [(16384, 28672, 8192), (16384, 8192, 28672), (16384, 8192, 8192)]:   # 28, 8, 8 rounds
         d = _describe(M, N, K)
         assert f"kernel={KIND} " in d and "round_sync=1" in d, d
         assert int(d.split(" ws=")[1].split()[0]) >= 1024, d
-    for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 8192, 1024), (4096, 8192, 8192)]:
-        d = _describe(M, N, K)                                         # 1, 4, 4 and 2 rounds
+    for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 4096), (4096, 8192, 8192)]:
+        d = _describe(M, N, K)                                         # 1, 4, 16 (of 64 slices) and 2 rounds
         assert f"kernel={KIND} " in d and "round_sync=0" in d and " ws=0 " in d, d
     d = _describe(16384, 28672, 8192, b_col=True)                      # another kind
     assert f"kernel={KIND} " not in d and "round_sync=0" in d, d
