@@ -137,7 +137,9 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * (tail=<tiles>x<splits> in the description; LL_GEMM_TAIL_SPLIT=0 turns it
  * off): each split leaves a 256x256 fp32 partial in the workspace, and a
  * reduce kernel adds them in ascending split order, then applies the
- * epilogue.  The environment variable LL_GEMM_KIND (a
+ * epilogue.  KIND_SQ4_HO plans whose B rows (as read) are 16384 elements or
+ * more apart, with K >= 8192, also prefetch each B slice into L2 one slice
+ * ahead (prefetch_b=1; LL_GEMM_PREFETCH_B=0 or 1 overrides).  The environment variable LL_GEMM_KIND (a
  * kernel name as printed by gemm_plan_describe, or its index) forces a
  * kernel for configuration sweeps; a forced kernel that cannot take the
  * operands (a 192-row tile with an M-contiguous A, KIND_SQ4_HO outside the

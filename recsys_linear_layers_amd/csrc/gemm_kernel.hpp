@@ -83,6 +83,10 @@ struct GemmKArgs {
   // kernel finishes those tiles.  tail_first == total: no tail split.
   int32_t tail_first, tail_splits, tail_kps;
   float* tail_partial;
+  // Hand-ordered kind only: 1 to prefetch the B slice after the next into
+  // L2 (its loop always issues the prefetch; with 0 every lane's offset is
+  // out of range and the load touches no memory).
+  int32_t b_prefetch;
 };
 
 template <int BM_, int BN_, int KT_, int WM_, int WN_, int NPROD_, int STAGES_, bool AK_, bool BK_,

@@ -34,6 +34,9 @@ namespace ll {
 struct Sq4 {
   static constexpr int BM = 256, BN = 256, KT = 64, THREADS = 256;
   static constexpr int SLOT = 65536, B_OFF = 32768, LDS = 2 * SLOT;
+  // 256 bytes per wave above the ring that the loop's L2 prefetches write
+  // into (nothing reads them)
+  static constexpr int PF_LDS = LL_SQ4_PREFETCH ? 1024 : 0;
 };
 
 // Chunk swizzle of the A tile's rows (128 bytes, 8 chunks of 16 bytes each):
@@ -272,7 +275,7 @@ __device__ __forceinline__ void sq4_issue(i32x4 ra, i32x4 rb, const uint32_t (&v
 template <bool F16, int EPI>
 __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_sq4(const GemmKArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::LDS + Sq4::PF_LDS];
   char LL_LDS* smem = (char LL_LDS*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -311,6 +314,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     }
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(base + wave * 1024);
+  const uint32_t ldsp = __builtin_amdgcn_readfirstlane(base + Sq4::LDS + wave * 256);
   const int lda = (int)p.a.ld, ldb = (int)p.b.ld;
   const uint32_t incb = 64u * 2u * (uint32_t)ldb;
 
@@ -342,7 +346,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     int slot;
     const TileInfo ti = sq4_decode(p, t, slot);
     int n = ti.ke - ti.kb;
-    uint32_t va[8], vb[8];
+    uint32_t va[8], vb[8], vpa = kOOB, vpb = kOOB;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int q = wave + 4 * i;
@@ -352,6 +356,20 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       const int kr = q * 2 + (lane >> 5);
       const int lcb = (lane & 31) ^ sq4_swz_b(kr);
       vb[i] = ti.n0 + lcb * 8 < p.b.rows ? (uint32_t)(kr * ldb + lcb * 8) * 2u : kOOB;
+    }
+    // L2 prefetch offsets, one line per lane of this wave's share of a
+    // slice: A rows 8q + t (q = wave + 4i) at their first chunk; B k-rows
+    // 2q, 2q+1, four lines of 128 bytes each.  kOOB: nothing is fetched.
+    {
+      const int q = wave + 4 * (lane >> 3);
+      if constexpr ((LL_SQ4_PREFETCH & 2) != 0) {
+        const int row = q * 8 + (lane & 7);
+        vpa = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda) * 2u : kOOB;
+      }
+      if constexpr ((LL_SQ4_PREFETCH & 1) != 0) {
+        const int kr = q * 2 + ((lane >> 2) & 1), line = lane & 3;
+        vpb = p.b_prefetch && ti.n0 + line * 64 < p.b.rows ? (uint32_t)(kr * ldb + line * 64) * 2u : kOOB;
+      }
     }
     const int64_t oa = (int64_t)ti.m0 * p.a.ld + (int64_t)ti.kb * Sq4::KT;
     const int64_t ob = (int64_t)ti.kb * Sq4::KT * p.b.ld + ti.n0;
@@ -370,7 +388,8 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
 #define LL_SQ4_OPERANDS                                                                                       \
   : [n] "+s"(n), [m0] "+{m0}"(m0v)                                                                            \
   : [a0] "s"(ra[0]), [a1] "s"(ra[1]), [a2] "s"(ra[2]), [a3] "s"(ra[3]), [b0] "s"(rb[0]),                      \
-    [b1] "s"(rb[1]), [b2] "s"(rb[2]), [b3] "s"(rb[3]), [incb] "s"(incb), [ldsw] "s"(ldsw),                    \
+    [b1] "s"(rb[1]), [b2] "s"(rb[2]), [b3] "s"(rb[3]), [incb] "s"(incb), [ldsw] "s"(ldsw), [ldsp] "s"(ldsp),  \
+    [vpa] "v"(vpa), [vpb] "v"(vpb),                                                                           \
     [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]),                 \
     [va5] "v"(va[5]), [va6] "v"(va[6]), [va7] "v"(va[7]), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]),                 \
     [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [vb4] "v"(vb[4]), [vb5] "v"(vb[5]), [vb6] "v"(vb[6]),                 \

@@ -62,6 +62,7 @@ CARRY_STEPS = 1     # how many of the steps before the last of slice j+1 share t
 CARRY_SPAN = 52     # MFMAs over which a step's reads and carried loads are spread
 B_FIRST = 0         # load order within a slice: 0 A0, B0, A1, B1, ...; 1 B0, A0, B1, A1, ...
 CARRY_BLOCKS = 0    # 0: step k takes every CARRY_STEPS-th carried load; 1: contiguous runs of them
+PREFETCH = 1        # L2 prefetch of the slice after the next, right after the descriptors advance: bit 0 B, bit 1 A
 SLOT = 65536
 B_OFF = 32768
 
@@ -126,6 +127,24 @@ ADVANCE = ["s_add_u32 s88, s88, 128", "s_addc_u32 s89, s89, 0",
            "s_sub_u32 s94, s94, %[incb]", "s_cselect_b32 s94, 0, s94"]
 
 
+def prefetch():
+    """One dword per 128-byte line of this wave's share of the slice the
+    descriptors now point at (the one after the slice being loaded), into a
+    dummy LDS area, so that the real loads of that slice find it in L2.  The
+    per-lane offsets (vpa, vpb) are range-checked against num_records, so a
+    slice past the operand's end reads nothing."""
+    out = []
+    if PREFETCH & 1:
+        out.append(["s_add_u32 m0, %[ldsp], 0", "s_nop 0", "buffer_load_dword %[vpb], s[92:95], 0 offen lds"])
+    if PREFETCH & 2:
+        out.append(["s_add_u32 m0, %[ldsp], 0", "s_nop 0", "buffer_load_dword %[vpa], s[88:91], 0 offen lds"])
+    return out
+
+
+def npf():
+    return bin(PREFETCH & 3).count("1")
+
+
 def interleave(mf, ops, span):
     """MFMAs in order, with op k placed after MFMA floor(k * span / len(ops))."""
     after = {}
@@ -153,7 +172,7 @@ def carried(slot, kk):
     else:
         per = [rest[k::CARRY_STEPS] for k in range(CARRY_STEPS)] + [[]] * (early - CARRY_STEPS)
     last = max(k for k in range(early) if per[k])
-    return per[kk] + ([ADVANCE] if kk == last else [])
+    return per[kk] + ([ADVANCE] + prefetch() if kk == last else [])
 
 
 def step(op, slot, kk, buf, carry):
@@ -180,7 +199,7 @@ def step_last(op, slot, kind):
     mf = mfmas(op, (STEPS - 1) % 2)
     if kind == "last":
         return ["s_waitcnt lgkmcnt(0)"] + mf
-    out = ["s_waitcnt lgkmcnt(0)"] + mf[:BAR_AFTER] + ["s_waitcnt vmcnt(0)", "s_barrier"]
+    out = ["s_waitcnt lgkmcnt(0)"] + mf[:BAR_AFTER] + [f"s_waitcnt vmcnt({npf()})", "s_barrier"]
     rd = reads(1 - slot, 0, 0)
     ops = []
     if kind == "load":
@@ -193,6 +212,7 @@ def step_last(op, slot, kind):
                 ops.append(ld[k])
         if L3 == 16:
             ops.append(ADVANCE)
+            ops += prefetch()
     else:
         ops = rd
     out += interleave(mf[BAR_AFTER:], ops, len(mf) - BAR_AFTER - 2)
@@ -265,6 +285,7 @@ def main():
         parts.append(f"#define LL_SQ4_READ_ACC_{n} \\\n" + read_acc(n) + "\n")
     parts.append("// X(n) for every accumulator block n = 8 * row block + column block\n#define LL_SQ4_BLOCKS(X) " +
                  " ".join(f"X({n})" for n in range(64)) + "\n")
+    parts.append(f"// L2 prefetch of the slice after the next: bit 0 B, bit 1 A\n#define LL_SQ4_PREFETCH {PREFETCH}\n")
     parts.append(f"// loads of a slice issued after the barrier of the slice two before; the\n"
                  f"// prologue issues this many of slice 1\n#define LL_SQ4_L3 {L3}\n"
                  f"// the loads of a slice alternate A and B, B first if 1\n#define LL_SQ4_B_FIRST {B_FIRST}\n")

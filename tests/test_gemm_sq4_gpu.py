@@ -456,3 +456,37 @@ def test_tail_split_integer_inputs_bit_exact(monkeypatch):
     tm, tn = tails[-1]
     ref, _ = oracle.gemm_case(c, rows=(256 * tm, 8))
     assert np.array_equal(to_f64(C1)[256 * tm:256 * tm + 8], ref)
+
+
+def test_b_prefetch_selection_and_bits(monkeypatch):
+    """B is prefetched into L2 a slice ahead when its rows are 16384 elements
+    or more apart and K >= 8192; the prefetch only warms the cache, so the
+    bits are the same with and without it."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    assert "prefetch_b=1" in _describe(16384, 28672, 8192)              # FFN up
+    for M, N, K in [(16384, 8192, 28672), (4096, 4096, 4096), (4096, 28672, 4096)]:
+        assert "prefetch_b=0" in _describe(M, N, K), (M, N, K)          # FFN down, 4096^3, short K
+    M, N, K = 2048, 16384, 1024
+    c = synth.gemm_case(M, N, K, seed=321, out_dtype="bf16", dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    outs, descs = [], []
+    for on in ("1", "0"):
+        C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ll._plans.clear()
+        monkeypatch.setenv("LL_GEMM_KIND", KIND)
+        monkeypatch.setenv("LL_GEMM_PREFETCH_B", on)
+        try:
+            ll.gemm(A, B, out=C)
+            torch.cuda.synchronize()
+            descs.append(ll.plan_for(A, B, C).describe())
+        finally:
+            monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+            monkeypatch.delenv("LL_GEMM_PREFETCH_B", raising=False)
+            ll._plans.clear()
+        outs.append(C)
+    assert "prefetch_b=1" in descs[0] and "prefetch_b=0" in descs[1], descs
+    assert torch.equal(outs[0], outs[1])
+    for r0, nr in strip_starts(M, 8, 322):
+        ref, S = oracle.gemm_case(c, rows=(r0, nr))
+        acceptance.assert_close(to_f64(outs[0][r0:r0 + nr]), ref, S, "bf16", f"rows {r0}.. {descs[0]}")

@@ -51,7 +51,8 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
     lines = g.loop(OP)
     labels = {ln[:-1]: k for k, ln in enumerate(lines) if ln.endswith(":")}
     issued = {}          # slice -> set of pieces
-    pending, completed, visible = set(), set(), set()
+    pending, completed, visible = [], set(), set()   # pending: issue order, prefetches as ("PF", slice)
+    prefetches = 0
     # prologue (C++): slice 0 whole and the first L3 loads of slice 1 (order
     # A0, B0, A1, B1, ...), then a wait for all of them and a barrier
     order = [("A" if (k % 2 == 0) != bool(g.B_FIRST) else "B", k // 2) for k in range(16)]
@@ -89,6 +90,18 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
             pass
         elif ln.startswith("s_add_u32 m0, %[ldsw], "):
             m0 = int(ln.split(", ")[-1])
+        elif ln == "s_add_u32 m0, %[ldsp], 0":
+            m0 = "pf"
+        elif ln.startswith("buffer_load_dword "):
+            m = re.match(r"buffer_load_dword %\[vp([ab])\], s\[(\d+):\d+\], 0 offen lds", ln)
+            assert m and m0 == "pf", ln
+            which = m.group(1).upper()
+            assert m.group(2) == ("88" if which == "A" else "92"), ln
+            s = a_off // 128 if which == "A" else b_adv
+            # the descriptors point at the slice after the one whose loads were issued last
+            assert all(s > t for t in issued), f"prefetch of slice {s} after its loads"
+            pending.append(("PF", s))
+            prefetches += 1
         elif ln.startswith("buffer_load_dwordx4"):
             m = re.match(r"buffer_load_dwordx4 %\[v([ab])(\d)\], s\[(\d+):\d+\], 0 offen lds", ln)
             assert m, ln
@@ -103,10 +116,12 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
             if s >= 2:
                 assert released >= g.STEPS * (s - 1), f"slot of slice {s - 2} refilled before its reads were released"
             issued[s].add((which, i))
-            pending.add((s, (which, i)))
-        elif ln == "s_waitcnt vmcnt(0)":
-            completed |= pending
-            pending.clear()
+            pending.append((s, (which, i)))
+        elif (m := re.match(r"s_waitcnt vmcnt\((\d+)\)", ln)):
+            keep = int(m.group(1))
+            done = pending[:len(pending) - keep] if keep else pending
+            completed |= {x for x in done if x[0] != "PF"}
+            pending = pending[len(done):]
         elif ln == "s_waitcnt lgkmcnt(0)":
             reads_done = reads_issued
         elif ln == "s_barrier":
@@ -146,7 +161,10 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
     assert nrec_a == max(0, ext_a - a_off) and nrec_b == max(0, ext_b - b_adv * inc_b)
     for s in range(n):
         assert issued.get(s) == set(PIECES), f"slice {s}: {sorted(set(PIECES) - issued.get(s, set()))} never loaded"
-    assert not pending, "loads still outstanding at the end"
+    assert not [x for x in pending if x[0] != "PF"], "loads still outstanding at the end"
+    # each descriptor advance inside the loop (not the one or two before it) is followed by the prefetches
+    in_loop = a_off // 128 - (2 if g.L3 == 16 else 1)
+    assert prefetches == g.npf() * in_loop, (prefetches, in_loop)
     assert reads_issued == g.READS * g.STEPS * n and mfmas == g.MFMAS * g.STEPS * n and barriers == n - 1
     # the descriptors end at most one slice past the last loaded one
     assert a_off // 128 == b_adv and b_adv in (n, n + 1) or n <= 2
@@ -154,7 +172,8 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
 
 SPLITS = [dict(L3=16)] + [dict(L3=l3) for l3 in (14, 12, 10, 8, 6, 4, 2)] + \
          [dict(L3=l3, B_FIRST=1) for l3 in (8, 6, 4)] + \
-         [dict(L3=6, READ_SPAN=r, CARRY_SPAN=c) for r, c in ((16, 24), (63, 63), (1, 1))]
+         [dict(L3=6, READ_SPAN=r, CARRY_SPAN=c) for r, c in ((16, 24), (63, 63), (1, 1))] + \
+         [dict(L3=l3, PREFETCH=pf) for l3 in (10, 16) for pf in (1, 2, 3)]
 
 
 @pytest.mark.parametrize("params", SPLITS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
