@@ -10,7 +10,7 @@ import oracle
 import synth
 from helpers import to_f64
 from oracle import acceptance
-from synth.device import to_device
+from synth.device import gemm_operands as gemm_operands_t, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -108,6 +108,74 @@ def test_random_case_hand_ordered_k_tail(i, monkeypatch):
     finally:
         monkeypatch.delenv("LL_GEMM_KIND", raising=False)
         ll._plans.clear()
+
+
+N_FEATURES = 8
+
+
+@pytest.mark.parametrize("i", range(N_FEATURES))
+def test_random_case_hand_ordered_features(i, monkeypatch):
+    """The hand-ordered kind on random shapes of more than one round of
+    256x256 tiles, with its round barrier, its K-split last round and its B
+    prefetch each forced on or off at random (bias and activation and the
+    output type drawn too); sampled against the oracle: one entry in every
+    tile, 32 in each tile of the last round, and row strips."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    from helpers import per_tile_indices, strip_starts
+    rng = np.random.default_rng(9000 + i)
+    sync, tail, pf = str(i & 1), str((i >> 1) & 1), str((i >> 2) & 1)   # every combination once
+    while True:   # with the tail split on, a last round small enough to split
+        M, N = int(rng.integers(4100, 6200)), int(rng.integers(4100, 6200))
+        if tail == "0" or 0 < (-(-M // 256) * -(-N // 256)) % 256 <= 128:
+            break
+    K = 64 * int(rng.integers(32, 65))
+    out = str(rng.choice(["bf16", "f32"]))
+    act = rng.choice([None, "relu", "gelu", "silu"])
+    use_bias = bool(rng.random() < 0.6)
+    c = synth.gemm_case(M, N, K, seed=9100 + i, out_dtype=out, dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands_t(c)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[out]
+    C = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    bias = (torch.from_numpy(rng.standard_normal(N).astype(np.float32)).cuda() if use_bias else None)
+    ll._plans.clear()
+    for k, v in (("LL_GEMM_KIND", "KIND_SQ4_HO"), ("LL_GEMM_ROUND_SYNC", sync), ("LL_GEMM_TAIL_SPLIT", tail),
+                 ("LL_GEMM_PREFETCH_B", pf)):
+        monkeypatch.setenv(k, v)
+    try:
+        ll.gemm(A, B, out=C, bias=bias, act=act)
+        torch.cuda.synchronize()
+        ep = (ll.LL_EPI_BIAS if bias is not None else 0) | ll.ACTIVATIONS[act]
+        d = ll.plan_for(A, B, C, 0, ep).describe()
+    finally:
+        for k in ("LL_GEMM_KIND", "LL_GEMM_ROUND_SYNC", "LL_GEMM_TAIL_SPLIT", "LL_GEMM_PREFETCH_B"):
+            monkeypatch.delenv(k, raising=False)
+        ll._plans.clear()
+    what = f"features case {i}: {M}x{N}x{K} {out} act={act} bias={use_bias} {d}"
+    assert "kernel=KIND_SQ4_HO " in what and f"round_sync={sync}" in d and f"prefetch_b={pf}" in d, what
+    assert ("tail=0x1" in d) == (tail == "0"), what
+    got = to_f64(C)
+    rows, cols = per_tile_indices(M, N, (256, 256), 9200 + i)
+    tiles_m, tiles_n = -(-M // 256), -(-N // 256)
+    last = (tiles_m * tiles_n) % 256
+    extra_r, extra_c = [], []
+    for t in range(tiles_m * tiles_n - last, tiles_m * tiles_n):
+        per, (gid, w) = 8 * tiles_n, divmod(t, 8 * tiles_n)
+        gsz = min(tiles_m - 8 * gid, 8)
+        tm, tn = 8 * gid + w % gsz, w // gsz
+        h, wd = min(256, M - 256 * tm), min(256, N - 256 * tn)
+        extra_r += list(256 * tm + rng.integers(0, h, 32))
+        extra_c += list(256 * tn + rng.integers(0, wd, 32))
+    rows, cols = np.concatenate([rows, extra_r]).astype(np.int64), np.concatenate([cols, extra_c]).astype(np.int64)
+    ref, S = oracle.gemm_case_entries(c, rows, cols)
+    if bias is not None or act is not None:
+        ref, S = oracle.epilogue(ref, S, None if bias is None else bias.cpu().numpy(), act, cols=cols)
+    acceptance.assert_close(got[rows, cols], ref, S, out, what, act=act)
+    for r0, nr in strip_starts(M, 4, 9300 + i):
+        ref, S = oracle.gemm_case(c, rows=(r0, nr))
+        if bias is not None or act is not None:
+            ref, S = oracle.epilogue(ref, S, None if bias is None else bias.cpu().numpy(), act)
+        acceptance.assert_close(got[r0:r0 + nr], ref, S, out, f"{what} rows {r0}..", act=act)
 
 
 def _check(i, d, want_kind=None):
