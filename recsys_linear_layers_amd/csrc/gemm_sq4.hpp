@@ -172,6 +172,56 @@ __device__ __forceinline__ void sq4_tail_all(const GemmKArgs& p, int slot, int w
 #undef LL_SQ4_TAIL
 }
 
+// Whole tiles of an fp32 C with unit column stride (any row stride): one
+// base pointer per lane, the row offsets (16 I + r) * ldcm wave-uniform and
+// the column block an immediate offset, so each element costs one store
+// (the general path above spends ~10 operations per element on 64-bit
+// offsets, bounds and the type).  Plain stores: with rows only 4-byte aligned
+// a 64-byte row piece spans two cache lines, and L2 must merge the pieces of
+// neighbouring column blocks (non-temporal stores were slower on every shape
+// but one).
+template <int EPI, int N>
+__device__ __forceinline__ void sq4_store_f32_block(float* const (&rowp)[4], float bias) {
+  f32x4 v = sq4_acc<N>();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float x = v[r];
+    if constexpr (EPI > 0) x = epi<EPI - 1>(x, bias);
+    rowp[r][16 * (N & 7)] = x;
+  }
+}
+
+template <int EPI, int I>
+__device__ __forceinline__ void sq4_store_f32_rows(const GemmKArgs& p, float* base, const float (&bias)[8]) {
+  float* const rowp[4] = {base + (int64_t)(16 * I + 0) * p.ldcm, base + (int64_t)(16 * I + 1) * p.ldcm,
+                          base + (int64_t)(16 * I + 2) * p.ldcm, base + (int64_t)(16 * I + 3) * p.ldcm};
+  sq4_store_f32_block<EPI, 8 * I + 0>(rowp, bias[0]);
+  sq4_store_f32_block<EPI, 8 * I + 1>(rowp, bias[1]);
+  sq4_store_f32_block<EPI, 8 * I + 2>(rowp, bias[2]);
+  sq4_store_f32_block<EPI, 8 * I + 3>(rowp, bias[3]);
+  sq4_store_f32_block<EPI, 8 * I + 4>(rowp, bias[4]);
+  sq4_store_f32_block<EPI, 8 * I + 5>(rowp, bias[5]);
+  sq4_store_f32_block<EPI, 8 * I + 6>(rowp, bias[6]);
+  sq4_store_f32_block<EPI, 8 * I + 7>(rowp, bias[7]);
+}
+
+template <int EPI>
+__device__ __forceinline__ void sq4_store_f32_full(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0,
+                                                   int lane) {
+  float bias[8];
+  sq4_bias<EPI>(p, ti, wn0, lane, bias);
+  float* const base =
+      (float*)p.c + (int64_t)(ti.m0 + wm0 + 4 * (lane >> 4)) * p.ldcm + ti.n0 + wn0 + (lane & 15);
+  sq4_store_f32_rows<EPI, 0>(p, base, bias);
+  sq4_store_f32_rows<EPI, 1>(p, base, bias);
+  sq4_store_f32_rows<EPI, 2>(p, base, bias);
+  sq4_store_f32_rows<EPI, 3>(p, base, bias);
+  sq4_store_f32_rows<EPI, 4>(p, base, bias);
+  sq4_store_f32_rows<EPI, 5>(p, base, bias);
+  sq4_store_f32_rows<EPI, 6>(p, base, bias);
+  sq4_store_f32_rows<EPI, 7>(p, base, bias);
+}
+
 template <int EPI>
 __device__ __forceinline__ void sq4_store_all(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0, int lane) {
   float bias[8];
@@ -433,7 +483,10 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       if (t + stride < p.total) lds_barrier();
       continue;
     }
-    sq4_store_all<EPI>(p, ti, wm0, wn0, lane);
+    if (p.c_fmt == 0 && p.ldcn == 1 && !p.partial && ti.m0 + Sq4::BM <= p.M && ti.n0 + Sq4::BN <= p.N)
+      sq4_store_f32_full<EPI>(p, ti, wm0, wn0, lane);
+    else
+      sq4_store_all<EPI>(p, ti, wm0, wn0, lane);
     sq4_count_in(cnt, wave, lane);
   }
 }

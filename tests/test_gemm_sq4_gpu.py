@@ -250,6 +250,36 @@ def test_staged_epilogue_matches_direct_stores(out, act, monkeypatch):
     acceptance.assert_close(g1, ref, S, out, f"staged {M}x{N}x{K} {out} act={act} {d1}", act=act)
 
 
+@pytest.mark.parametrize("act", [None, "relu", "gelu", "silu"])
+def test_f32_whole_tile_stores_match_general_path(act, monkeypatch):
+    """Whole tiles of an fp32 C with unit column stride take one store per
+    element from a per-lane row pointer, also for a row stride that is odd
+    (4-byte aligned rows only); a column-major C and the ragged last tile row
+    take the general per-element path.  All give the same bits, the padding
+    columns stay untouched, and the result matches the oracle in full.
+    4600 x 4352 x 128: 306 tiles on 256 workgroups."""
+    import torch
+    M, N, K = 4600, 4352, 128
+    c = synth.gemm_case(M, N, K, seed=97 + len(str(act)), out_dtype="f32", dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    bias = None
+    if act:
+        bias = torch.from_numpy(np.random.default_rng(98).standard_normal(N).astype(np.float32)).cuda()
+    C1 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    big = torch.full((M, N + 3), float("nan"), dtype=torch.float32, device="cuda")
+    C2 = big[:, :N]
+    C3 = torch.full((N, M), float("nan"), dtype=torch.float32, device="cuda").t()
+    ds = [_run_into(A, B, C, monkeypatch, bias, act) for C in (C1, C2, C3)]
+    g1, g2, g3 = to_f64(C1), to_f64(C2), to_f64(C3)
+    assert np.array_equal(g1, g2), ds
+    assert np.array_equal(g1, g3), ds
+    assert torch.isnan(big[:, N:]).all()
+    ref, S = oracle.gemm_case(c)
+    if act:
+        ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+    acceptance.assert_close(g1, ref, S, "f32", f"f32 whole tiles {M}x{N}x{K} act={act} {ds[0]}", act=act)
+
+
 def test_staged_epilogue_needs_16_byte_aligned_c(monkeypatch):
     """A C that starts 8 bytes into an allocation (rows 16-byte aligned apart
     from that) takes the direct stores and matches an aligned C."""
