@@ -518,6 +518,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  // The fp32 value is what gets rounded: without the empty asm the compiler
+  // may fold a multiply before it into v_fma_mixlo_f16, which rounds the
+  // exact product to fp16 once, and one sum would then differ by an ulp
+  // between kernels and store paths.
+  asm("" : "+v"(v));
   return __builtin_bit_cast(uint16_t, (_Float16)v);  // v_cvt_f16_f32: round to nearest even
 }
 
@@ -525,26 +530,35 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
 // Handbook of Mathematical Functions, formula 7.1.26 (absolute error at most
 // 1.5e-7): 1 - (a1 t + ... + a5 t^5) exp(-u^2), t = 1 / (1 + p u).  Branch
 // free, so that an unrolled epilogue over every accumulator stays compact.
+// Every multiply and add is spelled out (fmaf, __fmul_rn, __fadd_rn): left to
+// the compiler, whether a product is fused into an add depends on the code
+// around it, and the same sum would round differently in different kernels
+// and store paths.
 __device__ __forceinline__ float erf_as(float u) {
-  const float t = __frcp_rn(1.f + 0.3275911f * u);
-  const float poly =
-      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  return 1.f - poly * __expf(-u * u);
+  const float t = __frcp_rn(fmaf(0.3275911f, u, 1.f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  const float poly = __fmul_rn(t, q);
+  return fmaf(-poly, __expf(__fmul_rn(-u, u)), 1.f);
 }
 
 // Epilogue arithmetic on one fp32 sum z plus its column's bias b: the
 // activation ACT of z + b, in fp32.  GELU is the exact form z * Phi(z) =
-// z/2 (1 + erf(z / sqrt 2)); SiLU z / (1 + exp(-z)).
+// z/2 (1 + erf(z / sqrt 2)), as the product of z/2 and 1 + erf (exact where
+// erf is near -1), which keeps the sign of z where the result underflows;
+// SiLU z / (1 + exp(-z)).
 template <int ACT>
 __device__ __forceinline__ float epi(float z, float b) {
-  const float x = z + b;
+  const float x = __fadd_rn(z, b);
   if constexpr (ACT == 1) {
     return x > 0.f ? x : 0.f;
   } else if constexpr (ACT == 2) {
-    const float e = erf_as(fabsf(x) * 0.70710678118654752f);
-    return 0.5f * x * (1.f + (x < 0.f ? -e : e));
+    const float e = erf_as(__fmul_rn(fabsf(x), 0.70710678118654752f));
+    return __fmul_rn(__fmul_rn(0.5f, x), __fadd_rn(1.f, x < 0.f ? -e : e));
   } else if constexpr (ACT == 3) {
-    return x * __frcp_rn(1.f + __expf(-x));
+    return __fmul_rn(x, __frcp_rn(__fadd_rn(1.f, __expf(-x))));
   } else {
     return x;
   }

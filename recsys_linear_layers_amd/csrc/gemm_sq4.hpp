@@ -34,8 +34,13 @@ namespace ll {
 struct Sq4 {
   static constexpr int BM = 256, BN = 256, KT = 64, THREADS = 256;
   static constexpr int SLOT = 65536, B_OFF = 32768, LDS = 2 * SLOT;
-  // 256 bytes per wave above the ring that the loop's L2 prefetches write
-  // into (nothing reads them)
+  // after the loop each wave stages its 128x128 block of a 16-bit C in an
+  // image of 128 rows of 256 bytes plus 16 of padding, over the ring
+  static constexpr int IMG_PITCH = 272, IMG = 128 * IMG_PITCH;
+  // 256 bytes per wave above the ring and the images that the loop's L2
+  // prefetches write into (nothing reads them; kept clear of the images so
+  // that no prefetch still in flight can land in one)
+  static constexpr int PF_OFF = 4 * IMG > LDS ? 4 * IMG : LDS;
   static constexpr int PF_LDS = LL_SQ4_PREFETCH ? 1024 : 0;
 };
 
@@ -231,24 +236,19 @@ __device__ __forceinline__ void sq4_store_all(const GemmKArgs& p, const TileInfo
 #undef LL_SQ4_STORE
 }
 
-// Staged store of a wave's 128x128 block of 16-bit C through 32 KB of LDS
+// Staged store of a wave's 128x128 block of 16-bit C through an LDS image
 // (the ring is free once every wave has left the k-loop).  Per 16x16
-// accumulator block the lane pair holding columns d, d+1 swaps values, so
-// that each lane holds 4-byte column pairs of two rows, and writes them into a
-// row-major [128][128] image (256-byte rows) whose 16-byte chunks are
-// XOR-swizzled by ((row >> 1) & 7) << 1: the eight rows one write instruction
-// covers (32 bytes each) then fall on eight different 32-byte groups of
-// banks.  Each 16-byte read then takes four whole rows back and each lane
-// stores 16 bytes, so a wave stores its block with 32 instructions of whole
-// 128-byte lines instead of 256 of 2 bytes per lane.
-__device__ __forceinline__ uint32_t sq4_stage_off(int row, int cb) {
-  return (uint32_t)(row * 256 + ((((cb >> 4) ^ (((row >> 1) & 7) << 1))) << 4) + (cb & 15));
-}
-
-template <int FMT>
-__device__ __forceinline__ uint32_t sq4_pack16(float lo, float hi) {
-  return (uint32_t)to_c16<FMT>(lo) | ((uint32_t)to_c16<FMT>(hi) << 16);
-}
+// accumulator block each lane converts its column's four rows and writes
+// them as four 16-bit values into the row-major [128][128] image.  Rows are
+// 272 bytes apart, so row R starts 4 R banks further on: the four groups of
+// 16 lanes of one write (rows 4 g + r) fall on banks 16 apart, and every
+// address is one per-lane base plus an immediate.  That is eight vector ALU
+// operations per block; with one wave per SIMD nothing hides their issue
+// time, and exchanging values between lanes first, to write whole words,
+// costs ten more.  Each 16-byte read then takes whole rows back and each
+// lane stores 16 bytes, so a wave stores its block with 32 instructions of
+// whole 128-byte lines instead of 256 of 2 bytes per lane.
+__device__ __forceinline__ uint32_t sq4_stage_off(int row, int cb) { return (uint32_t)(row * Sq4::IMG_PITCH + cb); }
 
 template <int EPI, int FMT, int N>
 __device__ __forceinline__ void sq4_stage_block(int lane, const float (&bias)[8], char LL_LDS* img) {
@@ -258,18 +258,11 @@ __device__ __forceinline__ void sq4_stage_block(int lane, const float (&bias)[8]
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = epi<EPI - 1>(v[r], bias[J]);
   }
-  const bool odd = lane & 1;
-  // lanes 2c, 2c+1 hold columns d, d+1 of rows 4g..4g+3 (g = lane / 16); the
-  // even lane sends rows 2, 3 and receives the odd lane's rows 0, 1, the odd
-  // lane sends rows 0, 1 and receives rows 2, 3
-  const int ra = 16 * I + 4 * (lane >> 4) + (odd ? 2 : 0);
-  const int cb = 32 * J + 2 * (lane & 14);
-  const float s0 = swap_pair(odd ? v[0] : v[2]);
-  const float s1 = swap_pair(odd ? v[1] : v[3]);
-  const float a0 = odd ? s0 : v[0], a1 = odd ? v[2] : s0;
-  const float b0 = odd ? s1 : v[1], b1 = odd ? v[3] : s1;
-  *(uint32_t LL_LDS*)(img + sq4_stage_off(ra, cb)) = sq4_pack16<FMT>(a0, a1);
-  *(uint32_t LL_LDS*)(img + sq4_stage_off(ra + 1, cb)) = sq4_pack16<FMT>(b0, b1);
+  // lane holds column 16 J + (lane & 15) of rows 16 I + 4 g + r, g = lane / 16
+  const int row = 16 * I + 4 * (lane >> 4);
+  const int cb = 32 * J + 2 * (lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) *(uint16_t LL_LDS*)(img + sq4_stage_off(row + r, cb)) = to_c16<FMT>(v[r]);
 }
 
 template <int EPI, int FMT>
@@ -282,20 +275,22 @@ __device__ __forceinline__ void sq4_stage_all(const GemmKArgs& p, const TileInfo
 #undef LL_SQ4_STAGE
 }
 
-// The image back, four rows per read, each lane storing 16 bytes of a row.
-// Element offsets fit in 32 bits (the fast-epilogue condition bounds
-// ldcm * (M + 256) below 2^31), so each lane keeps one offset that steps by
-// four rows.
+// The image back, four rows per read, each lane storing 16 bytes of a row:
+// lanes 8p..8p+7 and 32+8p..32+8p+7, which one pass of a 16-byte LDS read
+// serves together, take chunks 0-7 and 8-15 of row 4q+p (all 64 banks once),
+// and each group of eight lanes stores a whole 128-byte line.  Element
+// offsets fit in 32 bits (the fast-epilogue condition bounds ldcm * (M + 256)
+// below 2^31), so each lane keeps one offset that steps by four rows.
 __device__ __forceinline__ void sq4_flush(const GemmKArgs& p, const TileInfo& ti, int wm0, int wn0, int lane,
                                           const char LL_LDS* img) {
-  const int rl = lane >> 4, c = lane & 15;
+  const int pr = (lane >> 3) & 3, ch = ((lane >> 5) << 3) | (lane & 7);
   const int32_t step = 4 * (int32_t)p.ldcm;
-  int32_t off = (ti.m0 + wm0 + rl) * (int32_t)p.ldcm + ti.n0 + wn0 + c * 8;
+  int32_t off = (ti.m0 + wm0 + pr) * (int32_t)p.ldcm + ti.n0 + wn0 + ch * 8;
+  const char LL_LDS* const src = img + pr * Sq4::IMG_PITCH + ch * 16;
   uint16_t* const cb = (uint16_t*)p.c;
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
-    const int row = 4 * q + rl;
-    const i32x4 v = *(const i32x4 LL_LDS*)(img + row * 256 + ((c ^ (((row >> 1) & 7) << 1)) << 4));
+    const i32x4 v = *(const i32x4 LL_LDS*)(src + q * 4 * Sq4::IMG_PITCH);
     // C is not read again by this kernel: non-temporal (same box: +1.3% at
     // 4096^3, +1.5% at 8192^3, FFN shapes within noise)
     __builtin_nontemporal_store(v, (i32x4*)(cb + (uint32_t)off));
@@ -325,7 +320,7 @@ __device__ __forceinline__ void sq4_issue(i32x4 ra, i32x4 rb, const uint32_t (&v
 template <bool F16, int EPI>
 __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_sq4(const GemmKArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::LDS + Sq4::PF_LDS];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::PF_OFF + Sq4::PF_LDS];
   char LL_LDS* smem = (char LL_LDS*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -364,7 +359,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     }
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(base + wave * 1024);
-  const uint32_t ldsp = __builtin_amdgcn_readfirstlane(base + Sq4::LDS + wave * 256);
+  const uint32_t ldsp = __builtin_amdgcn_readfirstlane(base + Sq4::PF_OFF + wave * 256);
   const int lda = (int)p.a.ld, ldb = (int)p.b.ld;
   const uint32_t incb = 64u * 2u * (uint32_t)ldb;
 
@@ -471,7 +466,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     const bool staged = p.c_fast && p.c_fmt != 0 && ti.m0 + Sq4::BM <= p.M && ti.n0 + Sq4::BN <= p.N &&
                         ((uintptr_t)p.c & 15) == 0 && (p.ldcm & 7) == 0;
     if (staged) {
-      char LL_LDS* img = smem + wave * 32768;
+      char LL_LDS* img = smem + wave * Sq4::IMG;
       if (p.c_fmt == 1)
         sq4_stage_all<EPI, 1>(p, ti, wn0, lane, img);
       else
