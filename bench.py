@@ -441,6 +441,8 @@ def _probe_lib():
     lib.ll_probe_mfma16_only.argtypes = lib.ll_probe_mfma_only.argtypes
     lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_int, ctypes.c_void_p]
+    lib.ll_probe_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_void_p]
     return lib
 
 
@@ -479,10 +481,11 @@ def mfma_probe(steps: int, warmup: int, grid: int = 1024, iters: int = 20000) ->
 
 
 def hbm_probe(mib: int, steps: int, warmup: int) -> dict:
-    """Streaming through HBM with 16-byte accesses: a copy (1 read : 1 write)
-    and 4 streams read per stream written, mib MiB per stream, with plain and
-    with non-temporal loads and stores, at several grid sizes; the best of
-    each pass is its ceiling."""
+    """Streaming through HBM with 16-byte accesses: a copy (1 read : 1 write),
+    4 streams read per stream written, and reads alone (one 16-byte result
+    written per thread), mib MiB per stream, with plain and with non-temporal
+    loads and stores, at several grid sizes; the best of each pass is its
+    ceiling."""
     import torch
     lib = _probe_lib()
     n16 = (mib << 20) // 16
@@ -503,6 +506,20 @@ def hbm_probe(mib: int, steps: int, warmup: int) -> dict:
                                  gbs=round(nbytes / (t["ms"] * 1e-3) / 1e9, 1)))
             best = max(runs, key=lambda r: r["gbs"])
             res[f"{key}_{hk}"] = dict(bytes_per_call=nbytes, best_gbs=best["gbs"], best_grid=best["grid"],
+                                      frac_of_peak=round(best["gbs"] / PEAK_HBM_GBS, 4), runs=runs)
+    yr = torch.empty(16384 * 256 * 4, dtype=torch.int32, device="cuda")
+    for hints, hk in ((0, "plain"), (1, "nontemporal")):
+        runs = []
+        for grid in (1024, 4096, 16384):
+            _log(f"hbm probe: read_only, {hk}, grid {grid}")
+            nbytes = 4 * n16 * 16 + grid * 256 * 16
+            t = _time_launches(lambda: _probe_call(lib.ll_probe_read(hints, x.data_ptr(), yr.data_ptr(), 4 * n16, grid,
+                                                                     stream.cuda_stream), "ll_probe_read"),
+                               steps, warmup, stream)
+            runs.append(dict(grid=grid, ms=round(t["ms"], 4), median_ms=round(t["median_ms"], 4),
+                             gbs=round(nbytes / (t["ms"] * 1e-3) / 1e9, 1)))
+        best = max(runs, key=lambda r: r["gbs"])
+        res[f"read_only_{hk}"] = dict(bytes_per_call=4 * n16 * 16, best_gbs=best["gbs"], best_grid=best["grid"],
                                       frac_of_peak=round(best["gbs"] / PEAK_HBM_GBS, 4), runs=runs)
     return res
 

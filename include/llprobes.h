@@ -15,7 +15,8 @@
  *    that instruction.
  *  - HBM streaming: a plain copy (one stream read, one written) and a pass
  *    that reads four streams and writes one (the 4:1 read:write byte mix of
- *    the linear-compression workload), 16-byte accesses, no reuse.
+ *    the linear-compression workload), 16-byte accesses, no reuse; and a
+ *    read-only pass (the byte mix of a skinny GEMM whose B is streamed once).
  *
  * Conventions: pointers are DEVICE pointers on the current device; the caller
  * owns every buffer; `stream` is a hipStream_t (NULL = the default stream).
@@ -56,6 +57,13 @@ int ll_probe_mfma16_only(int grid, int iters, const void* operands, float* out, 
  * non-temporal stores.  x and y 16-byte aligned, not overlapping.
  * grid: workgroups of 256 threads, in [1, 2^20]; n16 >= 0. */
 int ll_probe_stream(int streams, int hints, const void* x, void* y, int64_t n16, int grid, void* stream);
+
+/* Read-only streaming: reads x (n16 16-byte elements, n16 * 16 bytes) once;
+ * each thread XORs the elements it reads and writes that one 16-byte value
+ * to y[thread], so y holds grid * 256 16-byte elements (grid * 4096 bytes
+ * written).  hints: 1 non-temporal loads, 0 plain.  x and y 16-byte aligned,
+ * not overlapping.  grid in [1, 2^20]; n16 >= 0 (0 still writes y). */
+int ll_probe_read(int hints, const void* x, void* y, int64_t n16, int grid, void* stream);
 
 #ifdef __cplusplus
 }

@@ -135,6 +135,34 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ x
   }
 }
 
+// Read-only streaming: each thread XORs together every 16-byte element it
+// reads and writes the one result at the end (16 bytes per thread, so the
+// traffic is reads to within grid * 4 KiB).
+template <int NT>
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ x, u32x4* __restrict__ y, int64_t n16) {
+  constexpr int U = 8;
+  const int64_t step = (int64_t)gridDim.x * 256 * U;
+  u32x4 r = u32x4{0, 0, 0, 0};
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += step) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * 256;
+      if (i < n16) {
+        if constexpr (NT)
+          v[u] = __builtin_nontemporal_load(x + i);
+        else
+          v[u] = x[i];
+      } else {
+        v[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) r ^= v[u];
+  }
+  y[(int64_t)blockIdx.x * 256 + threadIdx.x] = r;
+}
+
 template <int S>
 hipError_t launch_stream(int hints, const u32x4* x, u32x4* y, int64_t n16, int grid, hipStream_t st) {
   switch (hints) {
@@ -175,4 +203,17 @@ extern "C" int ll_probe_stream(int streams, int hints, const void* x, void* y, i
   const hipError_t e = streams == 1 ? launch_stream<1>(hints, xp, yp, n16, grid, (hipStream_t)stream)
                                     : launch_stream<4>(hints, xp, yp, n16, grid, (hipStream_t)stream);
   return (int)e;
+}
+
+extern "C" int ll_probe_read(int hints, const void* x, void* y, int64_t n16, int grid, void* stream) {
+  if (hints < 0 || hints > 1 || n16 < 0 || grid < 1 || grid > (1 << 20)) return -1;
+  if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return -1;
+  const uintptr_t xb = (uintptr_t)x, xe = xb + (uintptr_t)(n16 * 16);
+  const uintptr_t yb = (uintptr_t)y, ye = yb + (uintptr_t)grid * 256 * 16;
+  if (xb < ye && yb < xe) return -1;
+  if (hints)
+    read_kernel<1><<<grid, 256, 0, (hipStream_t)stream>>>((const u32x4*)x, (u32x4*)y, n16);
+  else
+    read_kernel<0><<<grid, 256, 0, (hipStream_t)stream>>>((const u32x4*)x, (u32x4*)y, n16);
+  return (int)hipGetLastError();
 }

@@ -171,12 +171,14 @@ def _probe_lib():
     lib.ll_probe_mfma16_only.argtypes = lib.ll_probe_mfma_only.argtypes
     lib.ll_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_int, ctypes.c_void_p]
+    lib.ll_probe_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_void_p]
     return lib
 
 
 def test_probe_library_exports_every_declared_symbol():
     names = re.findall(r"^int\s+(\w+)\s*\(", open(PROBE_HEADER).read(), re.M)
-    assert sorted(names) == ["ll_probe_mfma16_only", "ll_probe_mfma_only", "ll_probe_stream"]
+    assert sorted(names) == ["ll_probe_mfma16_only", "ll_probe_mfma_only", "ll_probe_read", "ll_probe_stream"]
     lib = ctypes.CDLL(PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -197,3 +199,9 @@ def test_probes_reject_bad_arguments_on_the_host():
     assert lib.ll_probe_stream(1, 0, 4100, 1 << 20, 16, 1, None) == -1  # misaligned x
     assert lib.ll_probe_stream(4, 3, 4096, 4096 + 16 * 16, 16, 1, None) == -1  # y inside x
     assert lib.ll_probe_stream(1, 3, None, None, 0, 1, None) == 0     # nothing to do
+    assert lib.ll_probe_read(2, 4096, 1 << 20, 16, 1, None) == -1      # unknown hint bits
+    assert lib.ll_probe_read(0, 4096, 1 << 20, -1, 1, None) == -1      # n16 < 0
+    assert lib.ll_probe_read(0, 4096, 1 << 20, 16, 0, None) == -1      # grid < 1
+    assert lib.ll_probe_read(0, 4096, None, 16, 1, None) == -1         # no y
+    assert lib.ll_probe_read(0, 4104, 1 << 20, 16, 1, None) == -1      # misaligned x
+    assert lib.ll_probe_read(1, 4096, 4096 + 16 * 8, 16, 1, None) == -1  # y inside x
