@@ -526,39 +526,48 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);  // v_cvt_f16_f32: round to nearest even
 }
 
-// erf(u) for u >= 0 by the rational approximation of Abramowitz and Stegun,
+// erf(|x| / sqrt 2) by the rational approximation of Abramowitz and Stegun,
 // Handbook of Mathematical Functions, formula 7.1.26 (absolute error at most
-// 1.5e-7): 1 - (a1 t + ... + a5 t^5) exp(-u^2), t = 1 / (1 + p u).  Branch
-// free, so that an unrolled epilogue over every accumulator stays compact.
-// Every multiply and add is spelled out (fmaf, __fmul_rn, __fadd_rn): left to
-// the compiler, whether a product is fused into an add depends on the code
-// around it, and the same sum would round differently in different kernels
-// and store paths.
-__device__ __forceinline__ float erf_as(float u) {
-  const float t = __frcp_rn(fmaf(0.3275911f, u, 1.f));
+// 1.5e-7): erf(u) = 1 - (a1 t + ... + a5 t^5) exp(-u^2), t = 1 / (1 + p u),
+// here with u = |x| / sqrt 2 folded into the constants: t = 1 / (1 + (p /
+// sqrt 2) |x|) and exp(-u^2) = 2^(x^2 * (-log2(e) / 2)).  Branch free, so
+// that an unrolled epilogue over every accumulator stays compact.  The
+// reciprocal and the power of two are the hardware's (v_rcp_f32,
+// v_exp_f32: about 1 ulp, no range handling), far inside the formula's own
+// error; a correctly rounded reciprocal and a denormal-safe exp cost a dozen
+// more vector operations per element, which with one wave per SIMD nothing
+// hides.  Every multiply and add is spelled out (fmaf, __fmul_rn, __fadd_rn):
+// left to the compiler, whether a product is fused into an add depends on
+// the code around it, and the same sum would round differently in different
+// kernels and store paths.
+__device__ __forceinline__ float erf_as_scaled(float x) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.231641900f, fabsf(x), 1.f));  // 0.3275911 / sqrt 2
   float q = fmaf(t, 1.061405429f, -1.453152027f);
   q = fmaf(t, q, 1.421413741f);
   q = fmaf(t, q, -0.284496736f);
   q = fmaf(t, q, 0.254829592f);
   const float poly = __fmul_rn(t, q);
-  return fmaf(-poly, __expf(__fmul_rn(-u, u)), 1.f);
+  const float g = __builtin_amdgcn_exp2f(__fmul_rn(__fmul_rn(x, x), -0.721347520f));  // exp(-x^2 / 2)
+  return fmaf(-poly, g, 1.f);
 }
 
 // Epilogue arithmetic on one fp32 sum z plus its column's bias b: the
 // activation ACT of z + b, in fp32.  GELU is the exact form z * Phi(z) =
 // z/2 (1 + erf(z / sqrt 2)), as the product of z/2 and 1 + erf (exact where
 // erf is near -1), which keeps the sign of z where the result underflows;
-// SiLU z / (1 + exp(-z)).
+// SiLU z / (1 + exp(-z)) (exp(-z) = 2^(-z log2(e)); its overflow for very
+// negative z gives the limit, -0).
 template <int ACT>
 __device__ __forceinline__ float epi(float z, float b) {
   const float x = __fadd_rn(z, b);
   if constexpr (ACT == 1) {
     return x > 0.f ? x : 0.f;
   } else if constexpr (ACT == 2) {
-    const float e = erf_as(__fmul_rn(fabsf(x), 0.70710678118654752f));
-    return __fmul_rn(__fmul_rn(0.5f, x), __fadd_rn(1.f, x < 0.f ? -e : e));
+    const float e = erf_as_scaled(x);
+    return __fmul_rn(__fmul_rn(0.5f, x), __fadd_rn(1.f, copysignf(e, x)));
   } else if constexpr (ACT == 3) {
-    return __fmul_rn(x, __frcp_rn(__fadd_rn(1.f, __expf(-x))));
+    const float g = __builtin_amdgcn_exp2f(__fmul_rn(x, -1.442695041f));
+    return __fmul_rn(x, __builtin_amdgcn_rcpf(__fadd_rn(1.f, g)));
   } else {
     return x;
   }
