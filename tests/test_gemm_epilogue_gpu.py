@@ -86,6 +86,31 @@ def test_split_k_reduce_applies_epilogue():
     _check(c, _bias(1024, 37), "relu")
 
 
+@pytest.mark.parametrize("N", [1024, 1030])
+def test_split_k_reduce_store_paths_agree(N):
+    """With N a multiple of 4 the split-K reduce takes four columns per thread
+    and one 16-byte store into a row-major fp32 C, element stores into a
+    column-major one; with N = 1030 every element goes through the per-element
+    reduce.  Both C layouts give the same bits, matching the oracle."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    c = synth.gemm_case(128, N, 8192, seed=38, out_dtype="f32", dist=("normal", 0.0, 1.0))
+    A, B = gemm_operands(c)
+    bias = torch.from_numpy(_bias(N, 39)).cuda()
+    C1 = torch.full((128, N), float("nan"), dtype=torch.float32, device="cuda")
+    C2 = torch.full((N, 128), float("nan"), dtype=torch.float32, device="cuda").t()
+    for C in (C1, C2):
+        ll.gemm(A, B, out=C, bias=bias, act="silu")
+    torch.cuda.synchronize()
+    d = ll.plan_for(A, B, C1, 0, ll.LL_EPI_BIAS | ll.ACTIVATIONS["silu"]).describe()
+    assert "splitk=1 " not in d, d
+    g1, g2 = to_f64(C1), to_f64(C2)
+    assert np.array_equal(g1, g2), d
+    ref, S = oracle.gemm_case(c)
+    ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), "silu")
+    acceptance.assert_close(g1, ref, S, "f32", f"split-K reduce N={N} {d}", act="silu")
+
+
 def test_k_zero_gives_activation_of_bias():
     import torch
     import recsys_linear_layers_amd as ll
