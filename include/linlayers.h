@@ -124,7 +124,13 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * four waves of 128x128, one per SIMD, each loading and computing in one
  * hand-ordered instruction stream) when that needs at most 1.25x their
  * passes x tile area (it runs ~1.3x as fast per pass and area); with or
- * without a fused epilogue.  K is split when the tiles fill
+ * without a fused epilogue.  A K-contiguous B read in place (C = X W^T with W
+ * stored [N][K]) keeps KIND_SQ4_HO out; from M = 4096, with A K-contiguous and
+ * no LL_FLAG_PACK_B, LL_FLAG_PRODUCER_CONSUMER or LL_FLAG_COOPERATIVE, the
+ * plan then packs B itself into an N-contiguous workspace copy (K x N x 2
+ * bytes; packB=1 in the description) if KIND_SQ4_HO is what then runs, and
+ * reads B in place otherwise: the copy moves 4 K N bytes and, at M >= 4096,
+ * costs less than the faster kernel saves.  K is split when the tiles fill
  * fewer than half of the CUs.  KIND_SQ4_HO plans with 8 rounds or more
  * (passes of the grid over the tiles) of K >= 8192 each, on a grid of whole
  * XCDs, also keep each
@@ -206,7 +212,11 @@ ll_status gemm_run_ex(const gemm_plan* plan, const void* A, const void* B, void*
  * results; serialise them.  Each call writes every workspace byte it reads
  * before reading it, so nothing left by an earlier call matters.
  * bias: as for gemm_run_ex (required iff the plan's epilogue adds one,
- * ignored otherwise).  Results are identical to gemm_run_ex's.
+ * ignored otherwise).  Results are identical to gemm_run_ex's, except where
+ * the plan packed a K-contiguous B on its own (see gemm_plan_create) and that
+ * copy does not fit the array: the call then runs the plan's in-place choice
+ * for the same operands (another kernel: results within the same tolerance,
+ * not the same bits).
  * Errors: LL_ERR_WORKSPACE if the plan needs more than
  * LL_NOALLOC_SCRATCH_BYTES (gemm_plan_workspace_size tells; nothing is
  * launched), otherwise as gemm_run_ex.

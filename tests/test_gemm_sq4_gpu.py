@@ -127,6 +127,50 @@ def test_selected_on_square_and_ffn_shapes(M, N, K):
     assert f"kernel={KIND} " in _describe(M, N, K)
 
 
+@pytest.mark.parametrize("M,N,K,want", [(4096, 4096, 4096, True), (16384, 28672, 8192, True),
+                                     (16384, 8192, 28672, True), (8192, 2048, 8192, True),
+                                     (2048, 8192, 8192, False), (3072, 3072, 3072, False), (4096, 1024, 2048, False),
+                                     (4096, 2560, 1024, False)])
+def test_k_contiguous_b_packed_for_the_hand_ordered_kind(M, N, K, want):
+    """C = X W^T (B K-contiguous): from M = 4096 the plan packs B into an
+    N-contiguous copy when the hand-ordered kind then runs; below that, or
+    where another kind would run anyway (3072^3 and 4096 x 2560: 192x256
+    tiles; 64 tiles of 256x256: split K), B is read in place.  Asked for producer/consumer
+    kernels, B is never packed."""
+    import recsys_linear_layers_amd as ll
+    d = _describe(M, N, K, b_col=True)
+    assert (f"kernel={KIND} " in d) == want, d
+    assert ("packB=1" in d) == want, d
+    d = _describe(M, N, K, b_col=True, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
+    assert "packB=0" in d and f"kernel={KIND} " not in d, d
+
+
+def test_k_contiguous_b_packed_integer_exact(monkeypatch):
+    """The packed B and the hand-ordered kind against B read in place by the
+    producer/consumer kind: integer inputs make both exact, so the bits agree,
+    and sampled entries match the oracle."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    c = synth.gemm_case(4096, 4096, 1024, dist=("int", -4, 4), seed=341, out_dtype="f32", b_col_major=True)
+    A, B = gemm_operands(c)
+    C1 = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
+    C2 = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
+    ll._plans.clear()
+    ll.gemm(A, B, out=C1)
+    ll.gemm(A, B, out=C2, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
+    torch.cuda.synchronize()
+    d1 = ll.plan_for(A, B, C1).describe()
+    d2 = ll.plan_for(A, B, C2, ll.LL_FLAG_PRODUCER_CONSUMER).describe()
+    ll._plans.clear()
+    assert f"kernel={KIND} " in d1 and "packB=1" in d1, d1
+    assert "packB=0" in d2, d2
+    g1, g2 = to_f64(C1), to_f64(C2)
+    assert np.array_equal(g1, g2), (d1, d2)
+    rows, cols = sample_indices(c.M, c.N, 2048, 342, tile=plan_tile(d1))
+    ref, _ = oracle.gemm_case_entries(c, rows, cols)
+    assert np.array_equal(g1[rows, cols], ref)
+
+
 @pytest.mark.parametrize("M,N,K,b_col,want", [
     (8448, 8448, 4096, False, True),    # 5 passes of 256x256 against 9 of 256x128: 1.11x the area
     (12288, 4608, 8192, False, True),   # 4 against 7 of 128x256: 1.14x
@@ -148,8 +192,8 @@ def test_selection_conditions():
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, c_t=ll.LL_F32)
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_GELU)
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_BIAS | ll.LL_EPI_SILU)
-    for kw in (dict(b_col=True), dict(a_col=True),
-               dict(flags=ll.LL_FLAG_PRODUCER_CONSUMER), dict(flags=ll.LL_FLAG_COOPERATIVE)):
+    # (a K-contiguous B is packed for it from M = 4096: the test above)
+    for kw in (dict(a_col=True), dict(flags=ll.LL_FLAG_PRODUCER_CONSUMER), dict(flags=ll.LL_FLAG_COOPERATIVE)):
         assert f"kernel={KIND} " not in _describe(4096, 4096, 4096, **kw), kw
     assert f"kernel={KIND} " not in _describe(4096, 4096, 4104)        # K % 64 != 0
     assert f"kernel={KIND} " not in _describe(2048, 4096, 8192)        # 128 tiles would split K
@@ -312,8 +356,10 @@ def test_round_barrier_selection(monkeypatch):
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 4096), (4096, 8192, 8192)]:
         d = _describe(M, N, K)                                         # 1, 4, 16 (of 64 slices) and 2 rounds
         assert f"kernel={KIND} " in d and "round_sync=0" in d and " ws=0 " in d, d
-    d = _describe(16384, 28672, 8192, b_col=True)                      # another kind
+    d = _describe(16384, 28672, 8192, b_col=True, flags=ll.LL_FLAG_PRODUCER_CONSUMER)   # another kind
     assert f"kernel={KIND} " not in d and "round_sync=0" in d, d
+    d = _describe(16384, 28672, 8192, b_col=True)                      # B packed for the hand-ordered kind
+    assert f"kernel={KIND} " in d and "packB=1" in d and "round_sync=1" in d, d
     monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "0")
     d = _describe(16384, 28672, 8192)
     assert "round_sync=0" in d and " ws=0 " in d, d
