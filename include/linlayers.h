@@ -118,19 +118,15 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * N-contiguous and no epilogue is fused, 256x256 tiles (eight computing
  * waves, one per SIMD also loading) replace it when they need no more passes
  * x tile area; for K > 8192 the 128x256 tiles take their place again under
- * the same conditions.  Last, with A K-contiguous and B N-contiguous (direct
- * or packed), K a multiple of 64 and each operand spanning under 2 GB from
- * its base, any of those four kinds gives way to KIND_SQ4_HO (256x256 tiles,
+ * the same conditions.  Last, with A K-contiguous (direct or packed), B
+ * N-contiguous or K-contiguous (C = X W^T with W stored [N][K]; direct or
+ * packed), K a multiple of 64 (or A packed, and B too when K-contiguous) and
+ * each operand spanning under 2 GB from its base, any of those four kinds
+ * gives way to KIND_SQ4_HO (256x256 tiles,
  * four waves of 128x128, one per SIMD, each loading and computing in one
  * hand-ordered instruction stream) when that needs at most 1.25x their
  * passes x tile area (it runs ~1.3x as fast per pass and area); with or
- * without a fused epilogue.  A K-contiguous B read in place (C = X W^T with W
- * stored [N][K]) keeps KIND_SQ4_HO out; from M = 4096, with A K-contiguous and
- * no LL_FLAG_PACK_B, LL_FLAG_PRODUCER_CONSUMER or LL_FLAG_COOPERATIVE, the
- * plan then packs B itself into an N-contiguous workspace copy (K x N x 2
- * bytes; packB=1 in the description) if KIND_SQ4_HO is what then runs, and
- * reads B in place otherwise: the copy moves 4 K N bytes and, at M >= 4096,
- * costs less than the faster kernel saves.  K is split when the tiles fill
+ * without a fused epilogue.  K is split when the tiles fill
  * fewer than half of the CUs.  KIND_SQ4_HO plans with 8 rounds or more
  * (passes of the grid over the tiles) of K >= 8192 each, on a grid of whole
  * XCDs, also keep each
@@ -143,9 +139,9 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * (tail=<tiles>x<splits> in the description; LL_GEMM_TAIL_SPLIT=0 turns it
  * off): each split leaves a 256x256 fp32 partial in the workspace, and a
  * reduce kernel adds them in ascending split order, then applies the
- * epilogue.  KIND_SQ4_HO plans whose B rows (as read) are 16384 elements or
- * more apart, with K >= 8192, also prefetch each B slice into L2 one slice
- * ahead (prefetch_b=1; LL_GEMM_PREFETCH_B=0 or 1 overrides).  The environment variable LL_GEMM_KIND (a
+ * epilogue.  KIND_SQ4_HO plans whose B is wide (an N-contiguous B's rows, as
+ * read, 16384 elements or more apart; a K-contiguous B with N >= 16384), with
+ * K >= 8192, also prefetch each B slice into L2 one slice ahead (prefetch_b=1; LL_GEMM_PREFETCH_B=0 or 1 overrides).  The environment variable LL_GEMM_KIND (a
  * kernel name as printed by gemm_plan_describe, or its index) forces a
  * kernel for configuration sweeps; a forced kernel that cannot take the
  * operands (a 192-row tile with an M-contiguous A, KIND_SQ4_HO outside the
@@ -212,11 +208,7 @@ ll_status gemm_run_ex(const gemm_plan* plan, const void* A, const void* B, void*
  * results; serialise them.  Each call writes every workspace byte it reads
  * before reading it, so nothing left by an earlier call matters.
  * bias: as for gemm_run_ex (required iff the plan's epilogue adds one,
- * ignored otherwise).  Results are identical to gemm_run_ex's, except where
- * the plan packed a K-contiguous B on its own (see gemm_plan_create) and that
- * copy does not fit the array: the call then runs the plan's in-place choice
- * for the same operands (another kernel: results within the same tolerance,
- * not the same bits).
+ * ignored otherwise).  Results are identical to gemm_run_ex's.
  * Errors: LL_ERR_WORKSPACE if the plan needs more than
  * LL_NOALLOC_SCRATCH_BYTES (gemm_plan_workspace_size tells; nothing is
  * launched), otherwise as gemm_run_ex.

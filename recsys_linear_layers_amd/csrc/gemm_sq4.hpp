@@ -317,7 +317,7 @@ __device__ __forceinline__ void sq4_issue(i32x4 ra, i32x4 rb, const uint32_t (&v
   }
 }
 
-template <bool F16, int EPI>
+template <bool F16, int EPI, bool BK>
 __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_sq4(const GemmKArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::PF_OFF + Sq4::PF_LDS];
@@ -337,8 +337,9 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
   // (+8192).  B fragment j (16 columns): two transposing reads, each giving
   // a lane 4 k of its column; the swizzle (sq4_swz_b) ignores k-row bits 2
   // and 5, so step kk is +16384*kk and the second half (k-rows +4) +2048
-  // from the step-0 address.
-  uint32_t fa[2][2][4], fb[2][8];
+  // from the step-0 address.  With B K-contiguous (BK) its tile is laid out
+  // and read like A's: fbk, column blocks j and j+4 at +8192.
+  uint32_t fa[2][2][4], fb[2][8], fbk[2][2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -348,6 +349,8 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
         const int row = wm0 + 16 * q + (lane & 15);
         const int lc = kk * 4 + (lane >> 4);
         fa[s][kk][q] = base + s * Sq4::SLOT + row * 128 + ((lc ^ sq4_swz_a(row)) << 4);
+        const int col = wn0 + 16 * q + (lane & 15);
+        fbk[s][kk][q] = base + s * Sq4::SLOT + Sq4::B_OFF + col * 128 + ((lc ^ sq4_swz_a(col)) << 4);
       }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -361,7 +364,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(base + wave * 1024);
   const uint32_t ldsp = __builtin_amdgcn_readfirstlane(base + Sq4::PF_OFF + wave * 256);
   const int lda = (int)p.a.ld, ldb = (int)p.b.ld;
-  const uint32_t incb = 64u * 2u * (uint32_t)ldb;
+  const uint32_t incb = BK ? 2u * Sq4::KT : 64u * 2u * (uint32_t)ldb;  // bytes of B per slice
 
   // Round barrier per XCD.  Work item t runs in round (t - first) / stride,
   // and the 32 workgroups of an XCD share panels only within a round.  Left
@@ -398,13 +401,20 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       const int row = q * 8 + (lane >> 3);
       const int lca = (lane & 7) ^ sq4_swz_a(row);
       va[i] = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda + lca * 8) * 2u : kOOB;
-      const int kr = q * 2 + (lane >> 5);
-      const int lcb = (lane & 31) ^ sq4_swz_b(kr);
-      vb[i] = ti.n0 + lcb * 8 < p.b.rows ? (uint32_t)(kr * ldb + lcb * 8) * 2u : kOOB;
+      if constexpr (BK) {  // B columns 8q.. like A rows
+        const int col = q * 8 + (lane >> 3);
+        const int lcb = (lane & 7) ^ sq4_swz_a(col);
+        vb[i] = ti.n0 + col < p.b.rows ? (uint32_t)(col * ldb + lcb * 8) * 2u : kOOB;
+      } else {
+        const int kr = q * 2 + (lane >> 5);
+        const int lcb = (lane & 31) ^ sq4_swz_b(kr);
+        vb[i] = ti.n0 + lcb * 8 < p.b.rows ? (uint32_t)(kr * ldb + lcb * 8) * 2u : kOOB;
+      }
     }
     // L2 prefetch offsets, one line per lane of this wave's share of a
     // slice: A rows 8q + t (q = wave + 4i) at their first chunk; B k-rows
-    // 2q, 2q+1, four lines of 128 bytes each.  kOOB: nothing is fetched.
+    // 2q, 2q+1, four lines of 128 bytes each (a K-contiguous B: its rows 8q
+    // + t, as A's).  kOOB: nothing is fetched.
     {
       const int q = wave + 4 * (lane >> 3);
       if constexpr ((LL_SQ4_PREFETCH & 2) != 0) {
@@ -412,12 +422,18 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
         vpa = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda) * 2u : kOOB;
       }
       if constexpr ((LL_SQ4_PREFETCH & 1) != 0) {
-        const int kr = q * 2 + ((lane >> 2) & 1), line = lane & 3;
-        vpb = p.b_prefetch && ti.n0 + line * 64 < p.b.rows ? (uint32_t)(kr * ldb + line * 64) * 2u : kOOB;
+        if constexpr (BK) {
+          const int col = q * 8 + (lane & 7);
+          vpb = p.b_prefetch && ti.n0 + col < p.b.rows ? (uint32_t)(col * ldb) * 2u : kOOB;
+        } else {
+          const int kr = q * 2 + ((lane >> 2) & 1), line = lane & 3;
+          vpb = p.b_prefetch && ti.n0 + line * 64 < p.b.rows ? (uint32_t)(kr * ldb + line * 64) * 2u : kOOB;
+        }
       }
     }
     const int64_t oa = (int64_t)ti.m0 * p.a.ld + (int64_t)ti.kb * Sq4::KT;
-    const int64_t ob = (int64_t)ti.kb * Sq4::KT * p.b.ld + ti.n0;
+    const int64_t ob = BK ? (int64_t)ti.n0 * p.b.ld + (int64_t)ti.kb * Sq4::KT
+                          : (int64_t)ti.kb * Sq4::KT * p.b.ld + ti.n0;
     const i32x4 ra = make_rsrc(p.a.ptr + oa, clamp_records(p.a.extent - oa));
     const i32x4 rb = make_rsrc(p.b.ptr + ob, clamp_records(p.b.extent - ob));
 
@@ -430,7 +446,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     lds_barrier();
     int m0v = 0;  // M0 is rewritten by the loop's loads
 
-#define LL_SQ4_OPERANDS                                                                                       \
+#define LL_SQ4_OPERANDS(FB)                                                                                   \
   : [n] "+s"(n), [m0] "+{m0}"(m0v)                                                                            \
   : [a0] "s"(ra[0]), [a1] "s"(ra[1]), [a2] "s"(ra[2]), [a3] "s"(ra[3]), [b0] "s"(rb[0]),                      \
     [b1] "s"(rb[1]), [b2] "s"(rb[2]), [b3] "s"(rb[3]), [incb] "s"(incb), [ldsw] "s"(ldsw), [ldsp] "s"(ldsp),  \
@@ -443,16 +459,33 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     [fa_0_1_2] "v"(fa[0][1][2]), [fa_0_1_3] "v"(fa[0][1][3]), [fa_1_0_0] "v"(fa[1][0][0]),                    \
     [fa_1_0_1] "v"(fa[1][0][1]), [fa_1_0_2] "v"(fa[1][0][2]), [fa_1_0_3] "v"(fa[1][0][3]),                    \
     [fa_1_1_0] "v"(fa[1][1][0]), [fa_1_1_1] "v"(fa[1][1][1]), [fa_1_1_2] "v"(fa[1][1][2]),                    \
-    [fa_1_1_3] "v"(fa[1][1][3]), [fb_0_0] "v"(fb[0][0]), [fb_0_1] "v"(fb[0][1]), [fb_0_2] "v"(fb[0][2]),      \
-    [fb_0_3] "v"(fb[0][3]), [fb_0_4] "v"(fb[0][4]), [fb_0_5] "v"(fb[0][5]), [fb_0_6] "v"(fb[0][6]),           \
-    [fb_0_7] "v"(fb[0][7]), [fb_1_0] "v"(fb[1][0]), [fb_1_1] "v"(fb[1][1]), [fb_1_2] "v"(fb[1][2]),           \
-    [fb_1_3] "v"(fb[1][3]), [fb_1_4] "v"(fb[1][4]), [fb_1_5] "v"(fb[1][5]), [fb_1_6] "v"(fb[1][6]),           \
-    [fb_1_7] "v"(fb[1][7])                                                                                    \
+    [fa_1_1_3] "v"(fa[1][1][3]), FB                                                                           \
   : LL_SQ4_CLOBBERS
-    if constexpr (F16)
-      asm volatile(LL_SQ4_LOOP_F16 LL_SQ4_OPERANDS);
-    else
-      asm volatile(LL_SQ4_LOOP_BF16 LL_SQ4_OPERANDS);
+#define LL_SQ4_FB                                                                                             \
+  [fb_0_0] "v"(fb[0][0]), [fb_0_1] "v"(fb[0][1]), [fb_0_2] "v"(fb[0][2]), [fb_0_3] "v"(fb[0][3]),             \
+      [fb_0_4] "v"(fb[0][4]), [fb_0_5] "v"(fb[0][5]), [fb_0_6] "v"(fb[0][6]), [fb_0_7] "v"(fb[0][7]),         \
+      [fb_1_0] "v"(fb[1][0]), [fb_1_1] "v"(fb[1][1]), [fb_1_2] "v"(fb[1][2]), [fb_1_3] "v"(fb[1][3]),         \
+      [fb_1_4] "v"(fb[1][4]), [fb_1_5] "v"(fb[1][5]), [fb_1_6] "v"(fb[1][6]), [fb_1_7] "v"(fb[1][7])
+#define LL_SQ4_FBK                                                                                            \
+  [fbk_0_0_0] "v"(fbk[0][0][0]), [fbk_0_0_1] "v"(fbk[0][0][1]), [fbk_0_0_2] "v"(fbk[0][0][2]),                \
+      [fbk_0_0_3] "v"(fbk[0][0][3]), [fbk_0_1_0] "v"(fbk[0][1][0]), [fbk_0_1_1] "v"(fbk[0][1][1]),            \
+      [fbk_0_1_2] "v"(fbk[0][1][2]), [fbk_0_1_3] "v"(fbk[0][1][3]), [fbk_1_0_0] "v"(fbk[1][0][0]),            \
+      [fbk_1_0_1] "v"(fbk[1][0][1]), [fbk_1_0_2] "v"(fbk[1][0][2]), [fbk_1_0_3] "v"(fbk[1][0][3]),            \
+      [fbk_1_1_0] "v"(fbk[1][1][0]), [fbk_1_1_1] "v"(fbk[1][1][1]), [fbk_1_1_2] "v"(fbk[1][1][2]),            \
+      [fbk_1_1_3] "v"(fbk[1][1][3])
+    if constexpr (BK) {
+      if constexpr (F16)
+        asm volatile(LL_SQ4_LOOP_F16_BK LL_SQ4_OPERANDS(LL_SQ4_FBK));
+      else
+        asm volatile(LL_SQ4_LOOP_BF16_BK LL_SQ4_OPERANDS(LL_SQ4_FBK));
+    } else {
+      if constexpr (F16)
+        asm volatile(LL_SQ4_LOOP_F16 LL_SQ4_OPERANDS(LL_SQ4_FB));
+      else
+        asm volatile(LL_SQ4_LOOP_BF16 LL_SQ4_OPERANDS(LL_SQ4_FB));
+    }
+#undef LL_SQ4_FB
+#undef LL_SQ4_FBK
 #undef LL_SQ4_OPERANDS
 
     lds_barrier();  // every wave is done reading the ring before it is reused
@@ -484,6 +517,21 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       sq4_store_all<EPI>(p, ti, wm0, wn0, lane);
     sq4_count_in(cnt, wave, lane);
   }
+}
+
+// Launch of one instantiation by epilogue (0: none, 1: bias only, 2-4:
+// ReLU, GELU, SiLU after the optional bias).
+template <bool F16, bool BK>
+inline hipError_t launch_sq4(int epi, const GemmKArgs& a, int grid, hipStream_t s) {
+  switch (epi) {
+    case 0: hipLaunchKernelGGL((gemm_sq4<F16, 0, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_sq4<F16, 1, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_sq4<F16, 2, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_sq4<F16, 3, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_sq4<F16, 4, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace ll

@@ -41,6 +41,12 @@ Operands the statement expects (names as in gemm_sq4.hpp):
                         16-row block i with i % 4 == P (block i+4 at +8192)
   fb_S_J (v)            LDS address of B fragment J of slot S at step 0
                         (step K at +16384*K, the second half at +2048)
+
+The _BK variant of the loop takes B K-contiguous instead (the usual layout of
+a linear layer's weight, C = X W^T): its LDS tile is [256 columns][64 k]
+like A's, each B fragment one ds_read_b128 like an A fragment (16 reads per
+step instead of 24), and it expects fbk_S_K_P in place of fb_S_J (B blocks j
+and j+4 at +8192, as for A) and incb = 128.
 """
 from __future__ import annotations
 
@@ -52,6 +58,7 @@ OUT = os.path.join(HERE, "gemm_sq4_loop.inc")
 STEPS = 2           # k32 steps per 64-deep slice
 MFMAS = 64          # MFMAs per step (8 x 8 blocks of 16x16)
 READS = 24          # fragment reads per step: 8 A (ds_read_b128), 16 B (two ds_read_b64_tr_b16 each)
+READS_BK = 16       # the same with B K-contiguous: 8 A and 8 B, all ds_read_b128
 B_STEP = 16384      # LDS bytes between a B fragment's steps (32 k-rows of 512 bytes)
 FBASE = 128         # first fragment VGPR
 FBUF = 64           # VGPRs per fragment buffer
@@ -89,13 +96,20 @@ def mfmas(op, buf):
     return out
 
 
-def reads(slot, kk, buf):
-    """The 24 fragment reads of k32 step kk from `slot` into buffer `buf`."""
+def reads(slot, kk, buf, bk=False):
+    """The 24 fragment reads of k32 step kk from `slot` into buffer `buf` (16
+    with B K-contiguous)."""
     out = []
     for i in range(8):
         off = (i >> 2) * 8192
         o = f" offset:{off}" if off else ""
         out.append([f"ds_read_b128 v[{fa(buf, i)}:{fa(buf, i) + 3}], %[fa_{slot}_{kk}_{i & 3}]{o}"])
+    if bk:
+        for j in range(8):
+            off = (j >> 2) * 8192
+            o = f" offset:{off}" if off else ""
+            out.append([f"ds_read_b128 v[{fb(buf, j)}:{fb(buf, j) + 3}], %[fbk_{slot}_{kk}_{j & 3}]{o}"])
+        return out
     for j in range(8):
         lo, hi = kk * B_STEP, kk * B_STEP + 2048
         o = f" offset:{lo}" if lo else ""
@@ -175,11 +189,11 @@ def carried(slot, kk):
     return per[kk] + ([ADVANCE] + prefetch() if kk == last else [])
 
 
-def step(op, slot, kk, buf, carry):
+def step(op, slot, kk, buf, carry, bk=False):
     """Step kk (before the last) of a slice in `slot`: MFMAs on `buf`, reads of
     step kk+1, and (carry) this step's share of the next slice's remaining
     loads."""
-    rd = reads(slot, kk + 1, 1 - buf)
+    rd = reads(slot, kk + 1, 1 - buf, bk)
     ops = rd
     if carry:
         ld = carried(slot, kk)
@@ -192,7 +206,7 @@ def step(op, slot, kk, buf, carry):
     return ["s_waitcnt lgkmcnt(0)"] + interleave(mfmas(op, buf), ops, READ_SPAN if not carry else CARRY_SPAN)
 
 
-def step_last(op, slot, kind):
+def step_last(op, slot, kind, bk=False):
     """The last step of a slice (fragments in buffer (STEPS - 1) % 2).  kind:
     "last" (no next slice), "noload" (next slice, nothing more to load),
     "load" (next slice, and load slice j+2)."""
@@ -200,7 +214,7 @@ def step_last(op, slot, kind):
     if kind == "last":
         return ["s_waitcnt lgkmcnt(0)"] + mf
     out = ["s_waitcnt lgkmcnt(0)"] + mf[:BAR_AFTER] + [f"s_waitcnt vmcnt({npf()})", "s_barrier"]
-    rd = reads(1 - slot, 0, 0)
+    rd = reads(1 - slot, 0, 0, bk)
     ops = []
     if kind == "load":
         ld = loads(slot)[:L3]
@@ -219,7 +233,7 @@ def step_last(op, slot, kind):
     return out
 
 
-def loop(op):
+def loop(op, bk=False):
     L = []
     # private descriptor copies, advanced from slice 0 (the operands) to
     # slice 2, the first slice the loop loads
@@ -231,26 +245,26 @@ def loop(op):
     L += ADVANCE + ADVANCE if L3 == 16 else ADVANCE
     L += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(256)]
     L += ["s_nop 4"]
-    L += [x for r in reads(0, 0, 0) for x in r]
+    L += [x for r in reads(0, 0, 0, bk) for x in r]
     for slot in (0, 1):
         L += [f"L_top{slot}_%=:"]
         if L3 < 16:
             L += ["s_cmp_lt_u32 %[n], 2", f"s_cbranch_scc1 L_noc{slot}_%="]
             for kk in range(STEPS - 1):
-                L += step(op, slot, kk, kk % 2, True)
+                L += step(op, slot, kk, kk % 2, True, bk)
             L += [f"s_branch L_st3{slot}_%=", f"L_noc{slot}_%=:"]
         for kk in range(STEPS - 1):
-            L += step(op, slot, kk, kk % 2, False)
+            L += step(op, slot, kk, kk % 2, False, bk)
         L += [f"L_st3{slot}_%=:"]
         L += ["s_cmp_eq_u32 %[n], 1", f"s_cbranch_scc1 L_last{slot}_%=",
               "s_cmp_eq_u32 %[n], 2", f"s_cbranch_scc1 L_nold{slot}_%="]
-        L += step_last(op, slot, "load")
+        L += step_last(op, slot, "load", bk)
         L += ["s_sub_u32 %[n], %[n], 1", f"s_branch L_top{1 - slot}_%="]
         L += [f"L_nold{slot}_%=:"]
-        L += step_last(op, slot, "noload")
+        L += step_last(op, slot, "noload", bk)
         L += ["s_sub_u32 %[n], %[n], 1", f"s_branch L_top{1 - slot}_%="]
         L += [f"L_last{slot}_%=:"]
-        L += step_last(op, slot, "last")
+        L += step_last(op, slot, "last", bk)
         L += ["s_branch L_done_%="]
     # the accumulators are read with v_accvgpr_read after this statement:
     # more wait states after the last MFMA that writes them than any MFMA
@@ -281,6 +295,9 @@ def main():
              "#pragma once", ""]
     parts.append("#define LL_SQ4_LOOP_BF16 \\\n" + cstring(loop("v_mfma_f32_16x16x32_bf16")) + "\n")
     parts.append("#define LL_SQ4_LOOP_F16 \\\n" + cstring(loop("v_mfma_f32_16x16x32_f16")) + "\n")
+    parts.append("// the same with B K-contiguous\n#define LL_SQ4_LOOP_BF16_BK \\\n" +
+                 cstring(loop("v_mfma_f32_16x16x32_bf16", True)) + "\n")
+    parts.append("#define LL_SQ4_LOOP_F16_BK \\\n" + cstring(loop("v_mfma_f32_16x16x32_f16", True)) + "\n")
     for n in range(64):
         parts.append(f"#define LL_SQ4_READ_ACC_{n} \\\n" + read_acc(n) + "\n")
     parts.append("// X(n) for every accumulator block n = 8 * row block + column block\n#define LL_SQ4_BLOCKS(X) " +

@@ -169,9 +169,6 @@ struct gemm_plan {
   size_t ws_sync_off;
   size_t ws_tail_off;
   size_t ws_bytes;
-  // A plan that packs a K-contiguous B on its own keeps the plan that reads B
-  // in place (no workspace for it), for callers whose workspace is bounded.
-  gemm_plan* alt;
 };
 
 namespace {
@@ -260,18 +257,7 @@ const char* ll_status_string(ll_status s) {
 
 const char* ll_last_error(void) { return g_last_error.c_str(); }
 
-// A K-contiguous B (C = X * W^T with W stored [N][K], the usual layout of a
-// linear layer's weight) read in place runs the producer/consumer kinds; the
-// hand-ordered kind reads B N-contiguous.  From M = 4096 a transposed copy of
-// B in the workspace (4 K N bytes moved) plus the hand-ordered kind is
-// faster (same box, bf16: 4096^3 1159 -> 1299 TFLOP/s, 8192^3 1204 -> 1387,
-// 16384 x 28672 x 8192 1166 -> 1434, 16384 x 8192 x 28672 951 -> 1413,
-// 8192 x 2048 x 8192 1192 -> 1466), while at M = 2048 the copy is not repaid
-// (2048 x 8192 x 8192 1197 -> 1131).  The plan packs B then, and only when
-// the hand-ordered kind is what runs.
-constexpr int64_t kAutoPackBMinM = 4096;
-
-static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack_b) {
+ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
   if (!out || !d) return fail(LL_ERR_INVALID_ARG, "gemm_plan_create: null argument");
   *out = nullptr;
   if (d->M < 0 || d->N < 0 || d->K < 0) return fail(LL_ERR_INVALID_ARG, "negative size");
@@ -299,13 +285,6 @@ static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack
   if (s != LL_OK) return s;
   s = plan_operand("B", d->N, d->K, d->stride_bn, d->stride_bk, d->flags & LL_FLAG_PACK_B, true, &p.b);
   if (s != LL_OK) return s;
-  const bool auto_b = auto_pack_b && !(d->flags & (LL_FLAG_COOPERATIVE | LL_FLAG_PRODUCER_CONSUMER)) &&
-                      p.a.kmajor && p.b.kmajor && !p.b.pack && d->M >= kAutoPackBMinM;
-  if (auto_b) {
-    s = plan_operand("B", d->N, d->K, d->stride_bn, d->stride_bk, true, true, &p.b);
-    if (s != LL_OK) return s;
-    if (!p.b.pack_mn) return plan_create(out, d, false);
-  }
   // Any K-contiguous operand needs K padded to a multiple of 8; packed copies carry zeros there.
   p.Kp = round_up(d->K, 8);
   if (round_up(d->K, 64) * 2 * 256 >= (1ll << 30)) return fail(LL_ERR_UNSUPPORTED, "K too large");
@@ -350,12 +329,15 @@ static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack
   };
   // The hand-ordered kind loads whole 64-deep slices with no k mask.  With K
   // not a multiple of 64 that is still exact when A is a packed copy (zero
-  // columns up to ldp, K rounded up to 64): the last slice's B rows past K
-  // lie beyond B's descriptor range and read as zeros, and they meet A's
-  // zero columns.  A read in place would meet them with its next row's
-  // values, and an Inf or NaN there would reach C.
-  const bool sq4_fits = p.a.kmajor && !p.b.kmajor && (d->K % 64 == 0 || p.a.pack) &&
-                        span_bytes(p.a, M) < 0x7FFFFFF0ll && span_bytes(p.b, N) < 0x7FFFFFF0ll;
+  // columns up to ldp, K rounded up to 64) and B is N-contiguous: the last
+  // slice's B rows past K lie beyond B's descriptor range and read as zeros,
+  // and they meet A's zero columns.  A read in place would meet them with
+  // its next row's values, and an Inf or NaN there would reach C.  A
+  // K-contiguous B (its variant with B tiles laid out like A's) read in
+  // place has the same problem, so there both operands are packed copies.
+  const bool sq4_k_ok = d->K % 64 == 0 || (p.a.pack && (!p.b.kmajor || p.b.pack));
+  const bool sq4_fits = p.a.kmajor && sq4_k_ok && span_bytes(p.a, M) < 0x7FFFFFF0ll &&
+                        span_bytes(p.b, N) < 0x7FFFFFF0ll;
   if (free_choice && p.a.kmajor && (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
     const int64_t pb = passes(kind), pt = passes(KIND_T192_PC);
     const KindInfo& kb = kind_info(kind);
@@ -392,7 +374,9 @@ static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack
   }
   // The hand-ordered 256x256 kind (four 128x128 waves, gemm_sq4.hpp) is
   // ahead of every kind above wherever it applies: A K-contiguous, B
-  // N-contiguous, K a multiple of 64 or A packed, with or without a fused
+  // N-contiguous or K-contiguous (C = X W^T, the usual layout of a linear
+  // layer's weight: a variant that lays B tiles out and reads them like A's),
+  // K a multiple of 64 or the operands packed, with or without a fused
   // epilogue.  Per pass and tile area it runs ~1.3x as fast as the others,
   // so it takes over when its passes times tile area is at most 1.25x theirs
   // and neither choice would split K; a last round it splits along K (the
@@ -435,8 +419,6 @@ static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack
       return fail(LL_ERR_UNSUPPORTED, "fused epilogues run in the producer/consumer kernels only");
     kind = M > N ? KIND_TALL_PC : KIND_WIDE_PC;
   }
-  // B packed on the plan's own initiative: only for the hand-ordered kind.
-  if (auto_b && kind != KIND_SQ4_HO) return plan_create(out, d, false);
   {
     // A tile whose M/N-contiguous operand rows do not divide a 1-KB load (192
     // elements) exists only for K-contiguous operands (a forced kind may ask).
@@ -444,12 +426,12 @@ static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack
     if ((!p.a.kmajor && 64 % (kv.bm / 8) != 0) || (!p.b.kmajor && 64 % (kv.bn / 8) != 0))
       return fail(LL_ERR_UNSUPPORTED, "kernel %s needs K-contiguous operands for its %dx%d tile", kv.name, kv.bm,
                   kv.bn);
-    // The hand-ordered kind reads A K-contiguous and B N-contiguous (as given
+    // The hand-ordered kind reads A K-contiguous and B either way (as given
     // or packed) in whole 64-deep slices.
     if (kind == KIND_SQ4_HO && !sq4_fits)
       return fail(LL_ERR_UNSUPPORTED,
-                  "kernel %s needs A K-contiguous, B N-contiguous, K a multiple of 64 (or A packed) and operands "
-                  "below 2 GB",
+                  "kernel %s needs A K-contiguous, K a multiple of 64 (or A packed, and B packed when "
+                  "K-contiguous) and operands below 2 GB",
                   kv.name);
   }
   p.kind = kind;
@@ -516,8 +498,11 @@ static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack
   }
 
   {
-    const int64_t ldb_k = p.b.pack ? p.b.ldp : p.b.ld;  // B's row stride as the kernel reads it
-    p.b_prefetch = kind == KIND_SQ4_HO && ldb_k >= kPrefetchBMinStride && p.kiters >= kPrefetchBMinSlices;
+    // B wide: an N-contiguous B's row stride as the kernel reads it (at least
+    // N), or N for a K-contiguous one.  Same box, 16384 x 28672 x 8192 with B
+    // K-contiguous: +6.3%; 16384 x 8192 x 28672 and 8192^3 -2%.
+    const int64_t b_width = p.b.kmajor ? d->N : (p.b.pack ? p.b.ldp : p.b.ld);
+    p.b_prefetch = kind == KIND_SQ4_HO && b_width >= kPrefetchBMinStride && p.kiters >= kPrefetchBMinSlices;
     if (const char* env = getenv("LL_GEMM_PREFETCH_B")) p.b_prefetch = env[0] == '1' && kind == KIND_SQ4_HO;
   }
 
@@ -540,7 +525,6 @@ static ll_status plan_create(gemm_plan** out, const gemm_desc* d, bool auto_pack
 
   gemm_plan* h = new (std::nothrow) gemm_plan(p);
   if (!h) return fail(LL_ERR_INVALID_ARG, "out of host memory");
-  if (auto_b && plan_create(&h->alt, d, false) != LL_OK) h->alt = nullptr;
   *out = h;
   return ok();
 }
@@ -565,10 +549,7 @@ ll_status gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
   return ok();
 }
 
-ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) { return plan_create(out, d, true); }
-
 ll_status gemm_plan_destroy(gemm_plan* p) {
-  if (p) delete p->alt;
   delete p;
   return ok();
 }
@@ -628,9 +609,6 @@ extern "C" {
 ll_status gemm_run_noalloc(const gemm_plan* p, const void* A, const void* B, void* C, const float* bias,
                            void* stream) {
   if (!p) return fail(LL_ERR_INVALID_ARG, "null plan");
-  // a B packed by the plan's own choice that would not fit: read it in place
-  if (p->ws_bytes > (size_t)LL_NOALLOC_SCRATCH_BYTES && p->alt && p->alt->ws_bytes <= (size_t)LL_NOALLOC_SCRATCH_BYTES)
-    p = p->alt;
   if (p->ws_bytes > (size_t)LL_NOALLOC_SCRATCH_BYTES)
     return fail(LL_ERR_WORKSPACE, "plan needs %zu bytes of workspace; gemm_run_noalloc holds at most %zu",
                 p->ws_bytes, (size_t)LL_NOALLOC_SCRATCH_BYTES);

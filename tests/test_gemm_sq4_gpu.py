@@ -101,11 +101,18 @@ def test_refused_where_it_does_not_apply(monkeypatch):
         with pytest.raises(ll.LLError) as e:
             ll.GemmPlan(ll.gemm_desc_for(A, B, C), A.device)
         assert e.value.status == ll.LL_ERR_UNSUPPORTED
-        Bc = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda").t()  # B K-contiguous
-        A2 = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda")
+        # K = 200 with A packed (row stride 201) but a K-contiguous B read in
+        # place: its rows past K would meet A's zero columns with the next
+        # row's values
+        A2 = torch.zeros((256, 201), dtype=torch.bfloat16, device="cuda")[:, :200]
+        Bc = torch.zeros((256, 200), dtype=torch.bfloat16, device="cuda").t()
         with pytest.raises(ll.LLError) as e:
             ll.GemmPlan(ll.gemm_desc_for(A2, Bc, C), A2.device)
         assert e.value.status == ll.LL_ERR_UNSUPPORTED
+        # a K-contiguous B with K a multiple of 64 is taken
+        Bk = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda").t()
+        A3 = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda")
+        assert "B:K-major" in ll.GemmPlan(ll.gemm_desc_for(A3, Bk, C), A3.device).describe()
     finally:
         monkeypatch.delenv("LL_GEMM_KIND", raising=False)
 
@@ -128,27 +135,26 @@ def test_selected_on_square_and_ffn_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,want", [(4096, 4096, 4096, True), (16384, 28672, 8192, True),
-                                     (16384, 8192, 28672, True), (8192, 2048, 8192, True),
-                                     (2048, 8192, 8192, False), (3072, 3072, 3072, False), (4096, 1024, 2048, False),
-                                     (4096, 2560, 1024, False)])
-def test_k_contiguous_b_packed_for_the_hand_ordered_kind(M, N, K, want):
-    """C = X W^T (B K-contiguous): from M = 4096 the plan packs B into an
-    N-contiguous copy when the hand-ordered kind then runs; below that, or
-    where another kind would run anyway (3072^3 and 4096 x 2560: 192x256
-    tiles; 64 tiles of 256x256: split K), B is read in place.  Asked for producer/consumer
-    kernels, B is never packed."""
+                                     (16384, 8192, 28672, True), (8192, 2048, 8192, True), (2048, 8192, 8192, True),
+                                     (3072, 3072, 3072, False), (4096, 1024, 2048, False), (4096, 2560, 1024, False)])
+def test_k_contiguous_b_selected_in_place(M, N, K, want):
+    """C = X W^T (B K-contiguous, W stored [N][K]): the hand-ordered kind takes
+    B in place, its tiles laid out and read like A's, under the same area rule
+    as for an N-contiguous B (3072^3 and 4096 x 2560: 192x256 tiles; 64 tiles
+    of 256x256: split K).  Asked for producer/consumer kernels, it stays out."""
     import recsys_linear_layers_amd as ll
     d = _describe(M, N, K, b_col=True)
     assert (f"kernel={KIND} " in d) == want, d
-    assert ("packB=1" in d) == want, d
+    assert "packB=0" in d and "B:K-major" in d, d
+    assert (f"kernel={KIND} " in _describe(M, N, K)) == want
     d = _describe(M, N, K, b_col=True, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
-    assert "packB=0" in d and f"kernel={KIND} " not in d, d
+    assert f"kernel={KIND} " not in d, d
 
 
-def test_k_contiguous_b_packed_integer_exact(monkeypatch):
-    """The packed B and the hand-ordered kind against B read in place by the
-    producer/consumer kind: integer inputs make both exact, so the bits agree,
-    and sampled entries match the oracle."""
+def test_k_contiguous_b_integer_exact():
+    """The hand-ordered kind with B K-contiguous against the producer/consumer
+    kind on the same B: integer inputs make both exact, so the bits agree, and
+    sampled entries match the oracle."""
     import torch
     import recsys_linear_layers_amd as ll
     c = synth.gemm_case(4096, 4096, 1024, dist=("int", -4, 4), seed=341, out_dtype="f32", b_col_major=True)
@@ -162,13 +168,76 @@ def test_k_contiguous_b_packed_integer_exact(monkeypatch):
     d1 = ll.plan_for(A, B, C1).describe()
     d2 = ll.plan_for(A, B, C2, ll.LL_FLAG_PRODUCER_CONSUMER).describe()
     ll._plans.clear()
-    assert f"kernel={KIND} " in d1 and "packB=1" in d1, d1
-    assert "packB=0" in d2, d2
+    assert f"kernel={KIND} " in d1 and "B:K-major" in d1 and "packB=0" in d1, d1
+    assert f"kernel={KIND} " not in d2, d2
     g1, g2 = to_f64(C1), to_f64(C2)
     assert np.array_equal(g1, g2), (d1, d2)
     rows, cols = sample_indices(c.M, c.N, 2048, 342, tile=plan_tile(d1))
     ref, _ = oracle.gemm_case_entries(c, rows, cols)
     assert np.array_equal(g1[rows, cols], ref)
+
+
+BK_SHAPES = [(256, 256, 64), (256, 256, 192), (300, 520, 640), (1000, 1032, 2048), (513, 264, 320), (8, 8, 64),
+             (40, 24, 448), (1536, 1280, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", BK_SHAPES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_shapes_b_k_contiguous(M, N, K, out, monkeypatch):
+    """The variant for a K-contiguous B forced on ragged M and N, one to many
+    slices, both output types."""
+    c = synth.gemm_case(M, N, K, seed=M * 5 + N * 7 + K, out_dtype=out, dist=("normal", 0.0, 1.0), b_col_major=True)
+    got, d = _run(c, monkeypatch)
+    assert "B:K-major" in d and "packB=0" in d, d
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(got, ref, S, out, f"B K-contiguous {M}x{N}x{K} {d}")
+
+
+@pytest.mark.parametrize("act", [None, "gelu"])
+@pytest.mark.parametrize("out,in_dtype", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16")])
+def test_b_k_contiguous_epilogue_and_f16(act, out, in_dtype, monkeypatch):
+    """Bias + activation, fp16 operands and every C type with B K-contiguous,
+    300 x 1032 x 640 (ragged M, several tiles)."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    M, N, K = 300, 1032, 640
+    c = synth.gemm_case(M, N, K, seed=343, out_dtype=out, in_dtype=in_dtype, dist=("normal", 0.0, 1.0),
+                        b_col_major=True)
+    A, B = gemm_operands(c)
+    bias = torch.from_numpy(np.random.default_rng(344).standard_normal(N).astype(np.float32)).cuda()
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out]
+    C = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    d = _run_into(A, B, C, monkeypatch, bias, act)
+    assert "B:K-major" in d, d
+    ref, S = oracle.gemm_case(c)
+    ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+    acceptance.assert_close(to_f64(C), ref, S, out, f"B K-contiguous {out} act={act} {d}", act=act)
+
+
+def test_b_k_contiguous_tail_split_and_round_barrier(monkeypatch):
+    """The K-split last round (4300 x 4100 x 4096: 33 tiles split 4 ways) and,
+    forced on, the round barrier with B K-contiguous: the same bits as without
+    them on integer inputs, and the oracle on sampled entries."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    c = synth.gemm_case(4300, 4100, 4096, dist=("int", -3, 3), seed=345, out_dtype="f32", b_col_major=True)
+    A, B = gemm_operands(c)
+    outs = []
+    for tail, sync in (("1", "0"), ("0", "0"), ("1", "1")):
+        monkeypatch.setenv("LL_GEMM_TAIL_SPLIT", tail)
+        monkeypatch.setenv("LL_GEMM_ROUND_SYNC", sync)
+        C = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
+        d = _run_into(A, B, C, monkeypatch)
+        outs.append((to_f64(C), d))
+    monkeypatch.delenv("LL_GEMM_TAIL_SPLIT", raising=False)
+    monkeypatch.delenv("LL_GEMM_ROUND_SYNC", raising=False)
+    assert " tail=33x4" in outs[0][1] and " tail=0x1" in outs[1][1], [d for _, d in outs]
+    assert "B:K-major" in outs[0][1]
+    for g, d in outs[1:]:
+        assert np.array_equal(outs[0][0], g), d
+    rows, cols = sample_indices(c.M, c.N, 2048, 346, tile=256)
+    ref, _ = oracle.gemm_case_entries(c, rows, cols)
+    assert np.array_equal(outs[0][0][rows, cols], ref)
 
 
 @pytest.mark.parametrize("M,N,K,b_col,want", [
@@ -192,7 +261,7 @@ def test_selection_conditions():
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, c_t=ll.LL_F32)
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_GELU)
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_BIAS | ll.LL_EPI_SILU)
-    # (a K-contiguous B is packed for it from M = 4096: the test above)
+    # (a K-contiguous B: test_k_contiguous_b_selected_in_place)
     for kw in (dict(a_col=True), dict(flags=ll.LL_FLAG_PRODUCER_CONSUMER), dict(flags=ll.LL_FLAG_COOPERATIVE)):
         assert f"kernel={KIND} " not in _describe(4096, 4096, 4096, **kw), kw
     assert f"kernel={KIND} " not in _describe(4096, 4096, 4104)        # K % 64 != 0
@@ -358,8 +427,8 @@ def test_round_barrier_selection(monkeypatch):
         assert f"kernel={KIND} " in d and "round_sync=0" in d and " ws=0 " in d, d
     d = _describe(16384, 28672, 8192, b_col=True, flags=ll.LL_FLAG_PRODUCER_CONSUMER)   # another kind
     assert f"kernel={KIND} " not in d and "round_sync=0" in d, d
-    d = _describe(16384, 28672, 8192, b_col=True)                      # B packed for the hand-ordered kind
-    assert f"kernel={KIND} " in d and "packB=1" in d and "round_sync=1" in d, d
+    d = _describe(16384, 28672, 8192, b_col=True)                      # B K-contiguous, in place
+    assert f"kernel={KIND} " in d and "packB=0" in d and "round_sync=1" in d, d
     monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "0")
     d = _describe(16384, 28672, 8192)
     assert "round_sync=0" in d and " ws=0 " in d, d

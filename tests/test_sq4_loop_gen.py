@@ -47,8 +47,9 @@ def test_committed_include_is_the_generators_output(tmp_path):
 PIECES = [("A", i) for i in range(8)] + [("B", i) for i in range(8)]
 
 
-def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
-    lines = g.loop(OP)
+def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
+    lines = g.loop(OP, bk)
+    nreads = g.READS_BK if bk else g.READS
     labels = {ln[:-1]: k for k, ln in enumerate(lines) if ln.endswith(":")}
     issued = {}          # slice -> set of pieces
     pending, completed, visible = [], set(), set()   # pending: issue order, prefetches as ("PF", slice)
@@ -127,15 +128,16 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
         elif ln == "s_barrier":
             barriers += 1
             visible |= completed
-            released = reads_done // g.READS
+            released = reads_done // nreads
         elif ln.startswith("ds_read"):
-            grp = reads_issued // g.READS
+            grp = reads_issued // nreads
             s, kk = grp // g.STEPS, grp % g.STEPS
-            m = re.search(r"%\[f([ab])_(\d)_(\d)(?:_(\d))?\](?: offset:(\d+))?", ln)
+            m = re.search(r"%\[f(a|b|bk)_(\d)_(\d)(?:_(\d))?\](?: offset:(\d+))?", ln)
             assert m, ln
+            assert (m.group(1) == "b") == (not bk and not ln.startswith("ds_read_b128")), ln
             slot = int(m.group(2))
             off = int(m.group(5) or 0)
-            if m.group(1) == "a":
+            if m.group(1) in ("a", "bk"):
                 assert int(m.group(3)) == kk, (ln, kk)
             else:
                 assert off // g.B_STEP == kk, (ln, kk)
@@ -165,7 +167,7 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9):
     # each descriptor advance inside the loop (not the one or two before it) is followed by the prefetches
     in_loop = a_off // 128 - (2 if g.L3 == 16 else 1)
     assert prefetches == g.npf() * in_loop, (prefetches, in_loop)
-    assert reads_issued == g.READS * g.STEPS * n and mfmas == g.MFMAS * g.STEPS * n and barriers == n - 1
+    assert reads_issued == nreads * g.STEPS * n and mfmas == g.MFMAS * g.STEPS * n and barriers == n - 1
     # the descriptors end at most one slice past the last loaded one
     assert a_off // 128 == b_adv and b_adv in (n, n + 1) or n <= 2
 
@@ -182,10 +184,20 @@ def test_emulated_loop(params, n):
     emulate(_gen(**params), n)
 
 
+@pytest.mark.parametrize("params", [dict(), dict(L3=16), dict(L3=4), dict(L3=10, PREFETCH=3)],
+                         ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()) or "committed")
+@pytest.mark.parametrize("n", range(1, 10))
+def test_emulated_loop_b_k_contiguous(params, n):
+    """The variant for a K-contiguous B (B fragments read like A's, 16 reads
+    per step), with B moving 128 bytes per slice like A."""
+    emulate(_gen(**params), n, inc_b=128, bk=True)
+
+
 def test_committed_parameters_emulate():
     g = _gen()
     for n in range(1, 12):
         emulate(g, n)
+        emulate(g, n, inc_b=128, bk=True)
 
 
 def test_emulation_catches_a_double_advance():

@@ -2,9 +2,9 @@
 workspace in a device array inside the library) against gemm_run_ex with the
 plan's own workspace, through the C ABI: results must be bit-identical (same
 kernels, same order of sums), on two calls in a row, the second smaller, for
-split-K partials, packed operand copies (also a B the plan packs on its
-own, and the in-place plan it keeps for when that copy does not fit) and the
-round counters of the hand-ordered kind; plus the size limit."""
+split-K partials, packed operand copies, the round counters and K-split
+last rounds of the hand-ordered kind (with B N- or K-contiguous); plus the
+size limit."""
 import ctypes
 
 import numpy as np
@@ -118,41 +118,14 @@ def test_plan_beyond_the_scratch_size_is_refused():
         ll.gemm_plan_destroy(h)
 
 
-def test_b_packed_by_the_plan_two_calls_second_smaller():
-    # C = X W^T layout (B K-contiguous): from M = 4096 the plan packs B itself
-    # for the hand-ordered kind; these copies fit the device array
-    big = synth.gemm_case(4096, 4096, 1024, seed=331, out_dtype="bf16", b_col_major=True, name="noalloc_nt_big")
-    small = synth.gemm_case(4096, 4096, 512, seed=332, out_dtype="f32", b_col_major=True, name="noalloc_nt_small")
-    _check(big, want="packB=1")
-    _check(small, act="silu", bias_seed=333, want="packB=1")
-
-
-def test_b_packed_by_the_plan_beyond_the_array_reads_b_in_place():
-    """4096 x 8192 x 4608 with B K-contiguous: the plan packs B (75.5 MB, more
-    than the device array holds); gemm_run_noalloc then runs the plan that
-    reads B in place.  Integer inputs make both results exact, so they agree
-    bit for bit, and sampled entries match the oracle."""
-    import torch
-    import recsys_linear_layers_amd as ll
-    from helpers import sample_indices
-    c = synth.gemm_case(4096, 8192, 4608, dist=("int", -3, 3), seed=334, out_dtype="f32", b_col_major=True,
-                        name="noalloc_nt_alt")
-    A, B = gemm_operands(c)
-    C1 = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
-    C2 = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
-    plan = ll.GemmPlan(ll.gemm_desc_for(A, B, C1), A.device)
-    d = plan.describe()
-    assert "packB=1" in d and plan.ws_bytes > ll.LL_NOALLOC_SCRATCH_BYTES, d
-    stream = torch.cuda.current_stream().cuda_stream
-    ll.gemm_run(plan.handle, A.data_ptr(), B.data_ptr(), C1.data_ptr(), plan.workspace.data_ptr(), plan.ws_bytes,
-                stream)
-    ll.gemm_run_noalloc(plan.handle, A.data_ptr(), B.data_ptr(), C2.data_ptr(), None, stream)
-    torch.cuda.synchronize()
-    g1, g2 = to_f64(C1), to_f64(C2)
-    assert np.array_equal(g1, g2), d
-    rows, cols = sample_indices(c.M, c.N, 2048, 335)
-    ref, _ = oracle.gemm_case_entries(c, rows, cols)
-    assert np.array_equal(g2[rows, cols], ref)
+def test_b_k_contiguous_tail_split_two_calls_second_smaller(monkeypatch):
+    # C = X W^T (B K-contiguous) in the hand-ordered kind, whose K-split last
+    # round keeps its partials in the device array
+    monkeypatch.delenv("LL_GEMM_TAIL_SPLIT", raising=False)
+    big = synth.gemm_case(4352, 4160, 4096, seed=331, out_dtype="bf16", b_col_major=True, name="noalloc_nt_big")
+    small = synth.gemm_case(4352, 4160, 2048, seed=332, out_dtype="f32", b_col_major=True, name="noalloc_nt_small")
+    _check(big, want="B:K-major")
+    _check(small, act="silu", bias_seed=333, want="tail=33x2")
 
 
 def test_plan_without_workspace():
