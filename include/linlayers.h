@@ -175,7 +175,8 @@ ll_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
  * null workspace with a non-zero requirement, or a workspace not 256-byte
  * aligned), LL_ERR_HIP (launch failure).  Packed copies live in the
  * workspace with rows padded to whole 128-byte lines: A K-contiguous
- * [M][ldp], B N-contiguous [K][ldp]; so do split-K partials, the round
+ * [M][ldp], B N-contiguous [K][ldp] (K-contiguous [N][ldp] when B is given
+ * K-contiguous and A is K-contiguous); so do split-K partials, the round
  * counters of plans with round_sync=1 (zeroed by the call itself) and the
  * partial tiles of a K-split last round.
  * The call only launches kernels on `stream` (pack, counter clear, GEMM,

@@ -52,13 +52,13 @@ def test_split_k_workspace_too_small_is_rejected():
 def test_misaligned_workspace_is_rejected():
     import torch
     import recsys_linear_layers_amd as ll
-    # column-major B with an odd leading dimension: packed (N-contiguous) into the workspace
+    # column-major B with an odd leading dimension: packed (K-contiguous, beside a K-contiguous A) into the workspace
     A = torch.zeros((300, 520), dtype=torch.bfloat16, device="cuda")
     Bt = torch.zeros((260, 521), dtype=torch.bfloat16, device="cuda")[:, :520]
     B = Bt.t()
     C = torch.zeros((300, 260), dtype=torch.float32, device="cuda")
     plan = ll.plan_for(A, B, C)
-    assert plan.ws_bytes > 0 and "packB=1" in plan.describe() and "B:N-major" in plan.describe()
+    assert plan.ws_bytes > 0 and "packB=1" in plan.describe() and "B:K-major" in plan.describe()
     ws = torch.empty(plan.ws_bytes + 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(ll.LLError) as e:
         ll.gemm_run(plan.handle, A.data_ptr(), B.data_ptr(), C.data_ptr(), ws.data_ptr() + 16, plan.ws_bytes, 0)

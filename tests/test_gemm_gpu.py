@@ -130,15 +130,21 @@ def test_misaligned_operand_is_rejected_without_pack():
 
 @pytest.mark.parametrize("offset", [0, 1, 2, 3])
 @pytest.mark.parametrize("ldb", [300, 301])
-def test_packed_b_from_any_2_byte_offset(offset, ldb):
-    """Column-major B packed N-contiguous from a view that starts at any
-    2-byte offset: the pack reads a row's interior as 4-byte-aligned words
-    and must shift by the view's own address, not by the element index."""
+@pytest.mark.parametrize("a_col", [False, True])
+def test_packed_b_from_any_2_byte_offset(offset, ldb, a_col):
+    """Column-major B packed from a view that starts at any 2-byte offset:
+    the packs read a row's interior as aligned words and must shift by the
+    view's own address, not by the element index.  Beside a K-contiguous A
+    the copy stays K-contiguous (the row copy); beside an M-contiguous A it
+    is transposed N-contiguous (the LDS transpose)."""
     import torch
     ll = _ll()
-    M, N, K = 130, 70, 290
-    seed = 91 + offset * 7 + ldb
+    M, N, K = 136, 70, 290
+    seed = 91 + offset * 7 + ldb + 50 * a_col
     c = synth.gemm_case(M, N, K, seed=seed, b_col_major=True, ldb=ldb, out_dtype="f32")
+    if a_col:
+        c.A = synth.bf16_tensor(M * K, "uniform", -1.0, 1.0, seed=seed, tensor=5)
+        c.sam, c.sak = 1, M
     B_bits = np.concatenate([np.zeros(offset, dtype=np.uint16), c.B])
     base = torch.from_numpy(B_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
     B = torch.as_strided(base, (K, N), (1, ldb), offset)
@@ -146,7 +152,9 @@ def test_packed_b_from_any_2_byte_offset(offset, ldb):
     C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     ll.gemm(A, B, out=C, flags=ll.LL_FLAG_PACK_B)
     torch.cuda.synchronize()
-    assert "B:N-major" in ll.plan_for(A, B, C, ll.LL_FLAG_PACK_B).describe()
+    d = ll.plan_for(A, B, C, ll.LL_FLAG_PACK_B).describe()
+    assert ("B:N-major" if a_col else "B:K-major") in d and "packB=1" in d, d
+    assert ("packA=0" in d) == a_col, d  # K = 290: a K-contiguous A is packed too
     ref, S = oracle.gemm_case(c)
     acceptance.assert_close(to_f64(C), ref, S, "f32", f"packed B offset {offset} ldb {ldb}")
 
