@@ -149,6 +149,8 @@ GEMM_WORKLOADS = {
     # fp16 operands and output (the pages' GEMM tables are fp16)
     "gemm_4096_f16": (4096, 4096, 4096, dict(dist=("normal", 0.0, 1.0), seed=7, out_dtype="f16",
                                              in_dtype="f16")),
+    # C = X W^T with W stored [N][K]: B K-contiguous (a linear layer's usual weight layout)
+    "gemm_4096_nt": (4096, 4096, 4096, dict(dist=("normal", 0.0, 1.0), seed=2, out_dtype="bf16", b_col_major=True)),
 }
 
 

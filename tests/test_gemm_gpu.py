@@ -342,3 +342,8 @@ def test_mixed_operand_types_rejected():
 
 def test_gemm_4096_f16_sampled():
     _sampled_check(synth.gemm_workload("gemm_4096_f16"))
+
+
+def test_gemm_4096_nt_sampled():
+    # B K-contiguous (C = X W^T): the hand-ordered kind's variant for such a B, in place
+    _sampled_check(synth.gemm_workload("gemm_4096_nt"))
