@@ -83,6 +83,37 @@ def test_random_case_hand_ordered_kind(i, monkeypatch):
         ll._plans.clear()
 
 
+N_SQ4_BK = 16
+
+
+@pytest.mark.parametrize("i", range(N_SQ4_BK))
+def test_random_case_hand_ordered_b_k_contiguous(i, monkeypatch):
+    """The hand-ordered kind's variant for a K-contiguous B (C = X W^T) forced
+    on random cases: B column-major with any leading dimension (a misaligned
+    one is packed, still K-contiguous), K a multiple of 64 for even i; for odd
+    i any K with both operands packed (their zero columns past K meet in the
+    last 64-deep slice); bias, activation and output type as drawn."""
+    import recsys_linear_layers_amd as ll
+    d = _draw(N_CASES + N_SQUARE + N_SQ4 + 1000 + i)
+    rng = np.random.default_rng(8000 + i)
+    d["M"] = int(rng.integers(1, 1100))
+    d["N"] = int(rng.integers(1, 1100))
+    d["a_col"], d["b_col"] = False, True
+    if i % 2 == 0:
+        d["K"] = 64 * int(rng.integers(1, 13))
+        d["flags"] = 0
+    else:
+        d["K"] = 64 * int(rng.integers(0, 9)) + int(rng.integers(1, 64))
+        d["flags"] = ll.LL_FLAG_PACK_A | ll.LL_FLAG_PACK_B
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
+    try:
+        _check(N_CASES + N_SQUARE + N_SQ4 + 1000 + i, d, want_kind="KIND_SQ4_HO", want="B:K-major")
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+
+
 N_SQ4_TAIL = 30
 
 
@@ -178,7 +209,7 @@ def test_random_case_hand_ordered_features(i, monkeypatch):
         acceptance.assert_close(got[r0:r0 + nr], ref, S, out, f"{what} rows {r0}..", act=act)
 
 
-def _check(i, d, want_kind=None):
+def _check(i, d, want_kind=None, want=None):
     import torch
     import recsys_linear_layers_amd as ll
     M, N, K = d["M"], d["N"], d["K"]
@@ -214,8 +245,10 @@ def _check(i, d, want_kind=None):
         return
     ll.gemm(A, B, out=C, flags=d["flags"], bias=bias, act=d["act"])
     torch.cuda.synchronize()
-    if want_kind is not None:
-        assert f"kernel={want_kind} " in ll.plan_for(A, B, C, d["flags"]).describe(), what
+    if want_kind is not None or want is not None:
+        desc = ll.plan_for(A, B, C, d["flags"]).describe()
+        assert want_kind is None or f"kernel={want_kind} " in desc, what
+        assert want is None or want in desc, (what, desc)
     ref, S = oracle.gemm(M, N, K, A_bits, sam, sak, B_bits, sbk, sbn, fmt=d["in_dtype"])
     if bias is not None or d["act"] is not None:
         ref, S = oracle.epilogue(ref, S, None if bias is None else bias.cpu().numpy(), d["act"])

@@ -122,22 +122,25 @@ def test_lincomp_epilogue_graph_replay():
     _replay_check(lambda: ll.lincomp(user, item, W, out=Y, bias=bias, act="gelu"), Y)
 
 
-def test_hand_ordered_round_barrier_tail_prefetch_graph_replay(monkeypatch):
+@pytest.mark.parametrize("b_col", [False, True])
+def test_hand_ordered_round_barrier_tail_prefetch_graph_replay(b_col, monkeypatch):
     # 4352 x 4096 x 2048 with the round barrier and the B prefetch forced on:
     # four kernels per call (counter clear, the GEMM, whose last round of 16
-    # tiles is split two ways along K, and the ordered tail reduce)
+    # tiles is split two ways along K, and the ordered tail reduce); B
+    # N-contiguous, or K-contiguous (the kind's variant for it)
     ll = _ll()
     ll._plans.clear()
     monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
     monkeypatch.setenv("LL_GEMM_ROUND_SYNC", "1")
     monkeypatch.setenv("LL_GEMM_PREFETCH_B", "1")
     try:
-        plan, run, C = _gemm_case_run(synth.gemm_case(4352, 4096, 2048, seed=39, dist=("normal", 0.0, 1.0),
-                                                      out_dtype="bf16"))
+        plan, run, C = _gemm_case_run(synth.gemm_case(4352, 4096, 2048, seed=39 + b_col, dist=("normal", 0.0, 1.0),
+                                                      out_dtype="bf16", b_col_major=b_col))
     finally:
         for v in ("LL_GEMM_KIND", "LL_GEMM_ROUND_SYNC", "LL_GEMM_PREFETCH_B"):
             monkeypatch.delenv(v, raising=False)
     d = plan.describe()
     assert "round_sync=1" in d and "tail=16x2" in d and "prefetch_b=1" in d, d
+    assert ("B:K-major" if b_col else "B:N-major") in d, d
     _replay_check(run, C)
     ll._plans.clear()
