@@ -118,11 +118,11 @@ typedef struct gemm_plan gemm_plan; /* opaque, host-side, immutable */
  * N-contiguous and no epilogue is fused, 256x256 tiles (eight computing
  * waves, one per SIMD also loading) replace it when they need no more passes
  * x tile area; for K > 8192 the 128x256 tiles take their place again under
- * the same conditions.  Last, with A K-contiguous (direct or packed), B
- * N-contiguous or K-contiguous (C = X W^T with W stored [N][K]; direct or
- * packed), K a multiple of 64 (or A packed, and B too when K-contiguous) and
- * each operand spanning under 2 GB from its base, any of those four kinds
- * gives way to KIND_SQ4_HO (256x256 tiles,
+ * the same conditions.  Last, with A K- or M-contiguous (C = X^T Y, a
+ * weight gradient) and B N- or K-contiguous (C = X W^T with W stored
+ * [N][K]), direct or packed, K a multiple of 64 (or every K-contiguous
+ * operand packed) and each operand spanning under 2 GB from its base, any
+ * of those four kinds gives way to KIND_SQ4_HO (256x256 tiles,
  * four waves of 128x128, one per SIMD, each loading and computing in one
  * hand-ordered instruction stream) when that needs at most 1.25x their
  * passes x tile area (it runs ~1.3x as fast per pass and area); with or

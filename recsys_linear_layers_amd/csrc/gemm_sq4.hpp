@@ -317,7 +317,7 @@ __device__ __forceinline__ void sq4_issue(i32x4 ra, i32x4 rb, const uint32_t (&v
   }
 }
 
-template <bool F16, int EPI, bool BK>
+template <bool F16, int EPI, bool BK, bool AM>
 __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_sq4(const GemmKArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[Sq4::PF_OFF + Sq4::PF_LDS];
@@ -338,8 +338,10 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
   // a lane 4 k of its column; the swizzle (sq4_swz_b) ignores k-row bits 2
   // and 5, so step kk is +16384*kk and the second half (k-rows +4) +2048
   // from the step-0 address.  With B K-contiguous (BK) its tile is laid out
-  // and read like A's: fbk, column blocks j and j+4 at +8192.
-  uint32_t fa[2][2][4], fb[2][8], fbk[2][2][4];
+  // and read like A's: fbk, column blocks j and j+4 at +8192.  With A
+  // M-contiguous (AM) its tile is laid out and read like an N-contiguous B's:
+  // fat, row block i.
+  uint32_t fa[2][2][4], fb[2][8], fbk[2][2][4], fat[2][8];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -359,12 +361,15 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       const int kr = 8 * g + (sl >> 2);
       const int lc = mn >> 3, half = (mn & 7) * 2;
       fb[s][j] = base + s * Sq4::SLOT + Sq4::B_OFF + kr * 512 + ((lc ^ sq4_swz_b(kr)) << 4) + half;
+      const int mr = wm0 + 16 * j + 4 * (sl & 3);
+      fat[s][j] = base + s * Sq4::SLOT + kr * 512 + (((mr >> 3) ^ sq4_swz_b(kr)) << 4) + (mr & 7) * 2;
     }
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(base + wave * 1024);
   const uint32_t ldsp = __builtin_amdgcn_readfirstlane(base + Sq4::PF_OFF + wave * 256);
   const int lda = (int)p.a.ld, ldb = (int)p.b.ld;
   const uint32_t incb = BK ? 2u * Sq4::KT : 64u * 2u * (uint32_t)ldb;  // bytes of B per slice
+  const uint32_t inca = AM ? 64u * 2u * (uint32_t)lda : 2u * Sq4::KT;  // and of A
 
   // Round barrier per XCD.  Work item t runs in round (t - first) / stride,
   // and the 32 workgroups of an XCD share panels only within a round.  Left
@@ -398,9 +403,15 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int q = wave + 4 * i;
-      const int row = q * 8 + (lane >> 3);
-      const int lca = (lane & 7) ^ sq4_swz_a(row);
-      va[i] = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda + lca * 8) * 2u : kOOB;
+      if constexpr (AM) {  // A k-rows 2q, 2q+1 like an N-contiguous B's
+        const int kr = q * 2 + (lane >> 5);
+        const int lca = (lane & 31) ^ sq4_swz_b(kr);
+        va[i] = ti.m0 + lca * 8 < p.a.rows ? (uint32_t)(kr * lda + lca * 8) * 2u : kOOB;
+      } else {
+        const int row = q * 8 + (lane >> 3);
+        const int lca = (lane & 7) ^ sq4_swz_a(row);
+        va[i] = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda + lca * 8) * 2u : kOOB;
+      }
       if constexpr (BK) {  // B columns 8q.. like A rows
         const int col = q * 8 + (lane >> 3);
         const int lcb = (lane & 7) ^ sq4_swz_a(col);
@@ -417,7 +428,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     // + t, as A's).  kOOB: nothing is fetched.
     {
       const int q = wave + 4 * (lane >> 3);
-      if constexpr ((LL_SQ4_PREFETCH & 2) != 0) {
+      if constexpr ((LL_SQ4_PREFETCH & 2) != 0 && !AM) {
         const int row = q * 8 + (lane & 7);
         vpa = ti.m0 + row < p.a.rows ? (uint32_t)(row * lda) * 2u : kOOB;
       }
@@ -431,7 +442,7 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
         }
       }
     }
-    const int64_t oa = (int64_t)ti.m0 * p.a.ld + (int64_t)ti.kb * Sq4::KT;
+    const int64_t oa = AM ? (int64_t)ti.kb * Sq4::KT * p.a.ld + ti.m0 : (int64_t)ti.m0 * p.a.ld + (int64_t)ti.kb * Sq4::KT;
     const int64_t ob = BK ? (int64_t)ti.n0 * p.b.ld + (int64_t)ti.kb * Sq4::KT
                           : (int64_t)ti.kb * Sq4::KT * p.b.ld + ti.n0;
     const i32x4 ra = make_rsrc(p.a.ptr + oa, clamp_records(p.a.extent - oa));
@@ -441,26 +452,34 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
     // barrier of the slice before (all 16, or the first LL_SQ4_L3 when the
     // loop spreads the rest over the next slice's first steps)
     sq4_issue<16>(ra, rb, va, vb, ldsw, 0, 0u, 0u);
-    if (n > 1) sq4_issue<LL_SQ4_L3>(ra, rb, va, vb, ldsw, 1, 2u * Sq4::KT, incb);
+    if (n > 1) sq4_issue<LL_SQ4_L3>(ra, rb, va, vb, ldsw, 1, inca, incb);
     wait_vmcnt<0>();  // also covers the previous work item's stores
     lds_barrier();
     int m0v = 0;  // M0 is rewritten by the loop's loads
 
-#define LL_SQ4_OPERANDS(FB)                                                                                   \
+#define LL_SQ4_OPERANDS(FA, FB)                                                                               \
   : [n] "+s"(n), [m0] "+{m0}"(m0v)                                                                            \
   : [a0] "s"(ra[0]), [a1] "s"(ra[1]), [a2] "s"(ra[2]), [a3] "s"(ra[3]), [b0] "s"(rb[0]),                      \
-    [b1] "s"(rb[1]), [b2] "s"(rb[2]), [b3] "s"(rb[3]), [incb] "s"(incb), [ldsw] "s"(ldsw), [ldsp] "s"(ldsp),  \
+    [b1] "s"(rb[1]), [b2] "s"(rb[2]), [b3] "s"(rb[3]), [incb] "s"(incb), [inca] "s"(inca), [ldsw] "s"(ldsw),  \
+    [ldsp] "s"(ldsp),                                                                                         \
     [vpa] "v"(vpa), [vpb] "v"(vpb),                                                                           \
     [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]),                 \
     [va5] "v"(va[5]), [va6] "v"(va[6]), [va7] "v"(va[7]), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]),                 \
     [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [vb4] "v"(vb[4]), [vb5] "v"(vb[5]), [vb6] "v"(vb[6]),                 \
-    [vb7] "v"(vb[7]), [fa_0_0_0] "v"(fa[0][0][0]), [fa_0_0_1] "v"(fa[0][0][1]), [fa_0_0_2] "v"(fa[0][0][2]),  \
-    [fa_0_0_3] "v"(fa[0][0][3]), [fa_0_1_0] "v"(fa[0][1][0]), [fa_0_1_1] "v"(fa[0][1][1]),                    \
-    [fa_0_1_2] "v"(fa[0][1][2]), [fa_0_1_3] "v"(fa[0][1][3]), [fa_1_0_0] "v"(fa[1][0][0]),                    \
-    [fa_1_0_1] "v"(fa[1][0][1]), [fa_1_0_2] "v"(fa[1][0][2]), [fa_1_0_3] "v"(fa[1][0][3]),                    \
-    [fa_1_1_0] "v"(fa[1][1][0]), [fa_1_1_1] "v"(fa[1][1][1]), [fa_1_1_2] "v"(fa[1][1][2]),                    \
-    [fa_1_1_3] "v"(fa[1][1][3]), FB                                                                           \
+    [vb7] "v"(vb[7]), FA, FB                                                                                \
   : LL_SQ4_CLOBBERS
+#define LL_SQ4_FA                                                                                             \
+  [fa_0_0_0] "v"(fa[0][0][0]), [fa_0_0_1] "v"(fa[0][0][1]), [fa_0_0_2] "v"(fa[0][0][2]),                       \
+      [fa_0_0_3] "v"(fa[0][0][3]), [fa_0_1_0] "v"(fa[0][1][0]), [fa_0_1_1] "v"(fa[0][1][1]),                   \
+      [fa_0_1_2] "v"(fa[0][1][2]), [fa_0_1_3] "v"(fa[0][1][3]), [fa_1_0_0] "v"(fa[1][0][0]),                   \
+      [fa_1_0_1] "v"(fa[1][0][1]), [fa_1_0_2] "v"(fa[1][0][2]), [fa_1_0_3] "v"(fa[1][0][3]),                   \
+      [fa_1_1_0] "v"(fa[1][1][0]), [fa_1_1_1] "v"(fa[1][1][1]), [fa_1_1_2] "v"(fa[1][1][2]),                   \
+      [fa_1_1_3] "v"(fa[1][1][3])
+#define LL_SQ4_FAT                                                                                            \
+  [fat_0_0] "v"(fat[0][0]), [fat_0_1] "v"(fat[0][1]), [fat_0_2] "v"(fat[0][2]), [fat_0_3] "v"(fat[0][3]),     \
+      [fat_0_4] "v"(fat[0][4]), [fat_0_5] "v"(fat[0][5]), [fat_0_6] "v"(fat[0][6]), [fat_0_7] "v"(fat[0][7]), \
+      [fat_1_0] "v"(fat[1][0]), [fat_1_1] "v"(fat[1][1]), [fat_1_2] "v"(fat[1][2]), [fat_1_3] "v"(fat[1][3]), \
+      [fat_1_4] "v"(fat[1][4]), [fat_1_5] "v"(fat[1][5]), [fat_1_6] "v"(fat[1][6]), [fat_1_7] "v"(fat[1][7])
 #define LL_SQ4_FB                                                                                             \
   [fb_0_0] "v"(fb[0][0]), [fb_0_1] "v"(fb[0][1]), [fb_0_2] "v"(fb[0][2]), [fb_0_3] "v"(fb[0][3]),             \
       [fb_0_4] "v"(fb[0][4]), [fb_0_5] "v"(fb[0][5]), [fb_0_6] "v"(fb[0][6]), [fb_0_7] "v"(fb[0][7]),         \
@@ -473,17 +492,29 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
       [fbk_1_0_1] "v"(fbk[1][0][1]), [fbk_1_0_2] "v"(fbk[1][0][2]), [fbk_1_0_3] "v"(fbk[1][0][3]),            \
       [fbk_1_1_0] "v"(fbk[1][1][0]), [fbk_1_1_1] "v"(fbk[1][1][1]), [fbk_1_1_2] "v"(fbk[1][1][2]),            \
       [fbk_1_1_3] "v"(fbk[1][1][3])
-    if constexpr (BK) {
+    if constexpr (AM && BK) {
       if constexpr (F16)
-        asm volatile(LL_SQ4_LOOP_F16_BK LL_SQ4_OPERANDS(LL_SQ4_FBK));
+        asm volatile(LL_SQ4_LOOP_F16_AM_BK LL_SQ4_OPERANDS(LL_SQ4_FAT, LL_SQ4_FBK));
       else
-        asm volatile(LL_SQ4_LOOP_BF16_BK LL_SQ4_OPERANDS(LL_SQ4_FBK));
+        asm volatile(LL_SQ4_LOOP_BF16_AM_BK LL_SQ4_OPERANDS(LL_SQ4_FAT, LL_SQ4_FBK));
+    } else if constexpr (AM) {
+      if constexpr (F16)
+        asm volatile(LL_SQ4_LOOP_F16_AM LL_SQ4_OPERANDS(LL_SQ4_FAT, LL_SQ4_FB));
+      else
+        asm volatile(LL_SQ4_LOOP_BF16_AM LL_SQ4_OPERANDS(LL_SQ4_FAT, LL_SQ4_FB));
+    } else if constexpr (BK) {
+      if constexpr (F16)
+        asm volatile(LL_SQ4_LOOP_F16_BK LL_SQ4_OPERANDS(LL_SQ4_FA, LL_SQ4_FBK));
+      else
+        asm volatile(LL_SQ4_LOOP_BF16_BK LL_SQ4_OPERANDS(LL_SQ4_FA, LL_SQ4_FBK));
     } else {
       if constexpr (F16)
-        asm volatile(LL_SQ4_LOOP_F16 LL_SQ4_OPERANDS(LL_SQ4_FB));
+        asm volatile(LL_SQ4_LOOP_F16 LL_SQ4_OPERANDS(LL_SQ4_FA, LL_SQ4_FB));
       else
-        asm volatile(LL_SQ4_LOOP_BF16 LL_SQ4_OPERANDS(LL_SQ4_FB));
+        asm volatile(LL_SQ4_LOOP_BF16 LL_SQ4_OPERANDS(LL_SQ4_FA, LL_SQ4_FB));
     }
+#undef LL_SQ4_FA
+#undef LL_SQ4_FAT
 #undef LL_SQ4_FB
 #undef LL_SQ4_FBK
 #undef LL_SQ4_OPERANDS
@@ -521,14 +552,14 @@ __global__ void __launch_bounds__(Sq4::THREADS) __attribute__((amdgpu_waves_per_
 
 // Launch of one instantiation by epilogue (0: none, 1: bias only, 2-4:
 // ReLU, GELU, SiLU after the optional bias).
-template <bool F16, bool BK>
+template <bool F16, bool BK, bool AM>
 inline hipError_t launch_sq4(int epi, const GemmKArgs& a, int grid, hipStream_t s) {
   switch (epi) {
-    case 0: hipLaunchKernelGGL((gemm_sq4<F16, 0, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((gemm_sq4<F16, 1, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_sq4<F16, 2, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_sq4<F16, 3, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_sq4<F16, 4, BK>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((gemm_sq4<F16, 0, BK, AM>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_sq4<F16, 1, BK, AM>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_sq4<F16, 2, BK, AM>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_sq4<F16, 3, BK, AM>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_sq4<F16, 4, BK, AM>), dim3(grid), dim3(Sq4::THREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -6,7 +6,7 @@
 namespace ll {
 
 hipError_t launch_gemm_sq4_bk(int f16, int epi, const GemmKArgs& a, int grid, hipStream_t s) {
-  return f16 ? launch_sq4<true, true>(epi, a, grid, s) : launch_sq4<false, true>(epi, a, grid, s);
+  return f16 ? launch_sq4<true, true, false>(epi, a, grid, s) : launch_sq4<false, true, false>(epi, a, grid, s);
 }
 
 }  // namespace ll

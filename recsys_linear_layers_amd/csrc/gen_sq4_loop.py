@@ -47,6 +47,11 @@ a linear layer's weight, C = X W^T): its LDS tile is [256 columns][64 k]
 like A's, each B fragment one ds_read_b128 like an A fragment (16 reads per
 step instead of 24), and it expects fbk_S_K_P in place of fb_S_J (B blocks j
 and j+4 at +8192, as for A) and incb = 128.
+
+The _AM variants take A M-contiguous (C = X^T Y, a layer's weight gradient):
+its LDS tile is [64 k][256 rows] like an N-contiguous B's, each A fragment two
+ds_read_b64_tr_b16 like a B fragment, read at fat_S_I (step K at +16384*K,
+the second half at +2048), and A's descriptor moves by inca bytes per slice.
 """
 from __future__ import annotations
 
@@ -59,6 +64,7 @@ STEPS = 2           # k32 steps per 64-deep slice
 MFMAS = 64          # MFMAs per step (8 x 8 blocks of 16x16)
 READS = 24          # fragment reads per step: 8 A (ds_read_b128), 16 B (two ds_read_b64_tr_b16 each)
 READS_BK = 16       # the same with B K-contiguous: 8 A and 8 B, all ds_read_b128
+READS_AM = 8        # more with A M-contiguous (two ds_read_b64_tr_b16 per A fragment)
 B_STEP = 16384      # LDS bytes between a B fragment's steps (32 k-rows of 512 bytes)
 FBASE = 128         # first fragment VGPR
 FBUF = 64           # VGPRs per fragment buffer
@@ -96,11 +102,17 @@ def mfmas(op, buf):
     return out
 
 
-def reads(slot, kk, buf, bk=False):
+def reads(slot, kk, buf, bk=False, am=False):
     """The 24 fragment reads of k32 step kk from `slot` into buffer `buf` (16
-    with B K-contiguous)."""
+    with B K-contiguous; 8 more with A M-contiguous)."""
     out = []
     for i in range(8):
+        if am:
+            lo, hi = kk * B_STEP, kk * B_STEP + 2048
+            o = f" offset:{lo}" if lo else ""
+            out.append([f"ds_read_b64_tr_b16 v[{fa(buf, i)}:{fa(buf, i) + 1}], %[fat_{slot}_{i}]{o}"])
+            out.append([f"ds_read_b64_tr_b16 v[{fa(buf, i) + 2}:{fa(buf, i) + 3}], %[fat_{slot}_{i}] offset:{hi}"])
+            continue
         off = (i >> 2) * 8192
         o = f" offset:{off}" if off else ""
         out.append([f"ds_read_b128 v[{fa(buf, i)}:{fa(buf, i) + 3}], %[fa_{slot}_{kk}_{i & 3}]{o}"])
@@ -139,6 +151,9 @@ ADVANCE = ["s_add_u32 s88, s88, 128", "s_addc_u32 s89, s89, 0",
            "s_sub_u32 s90, s90, 128", "s_cselect_b32 s90, 0, s90",
            "s_add_u32 s92, s92, %[incb]", "s_addc_u32 s93, s93, 0",
            "s_sub_u32 s94, s94, %[incb]", "s_cselect_b32 s94, 0, s94"]
+# the same with A M-contiguous: A moves 64 k-rows (inca bytes) per slice
+ADVANCE_AM = [x.replace("s88, s88, 128", "s88, s88, %[inca]").replace("s90, s90, 128", "s90, s90, %[inca]")
+              for x in ADVANCE]
 
 
 def prefetch():
@@ -171,7 +186,7 @@ def interleave(mf, ops, span):
     return out
 
 
-def carried(slot, kk):
+def carried(slot, kk, am=False):
     """Loads of the next slice (into the other slot) issued in step kk (one of
     the STEPS - 1 steps before the last): the 16 - L3 that the last step of
     the previous slice left, spread over the first CARRY_STEPS steps; the
@@ -186,17 +201,17 @@ def carried(slot, kk):
     else:
         per = [rest[k::CARRY_STEPS] for k in range(CARRY_STEPS)] + [[]] * (early - CARRY_STEPS)
     last = max(k for k in range(early) if per[k])
-    return per[kk] + ([ADVANCE] + prefetch() if kk == last else [])
+    return per[kk] + ([ADVANCE_AM if am else ADVANCE] + prefetch() if kk == last else [])
 
 
-def step(op, slot, kk, buf, carry, bk=False):
+def step(op, slot, kk, buf, carry, bk=False, am=False):
     """Step kk (before the last) of a slice in `slot`: MFMAs on `buf`, reads of
     step kk+1, and (carry) this step's share of the next slice's remaining
     loads."""
-    rd = reads(slot, kk + 1, 1 - buf, bk)
+    rd = reads(slot, kk + 1, 1 - buf, bk, am)
     ops = rd
     if carry:
-        ld = carried(slot, kk)
+        ld = carried(slot, kk, am)
         ops = []
         for k in range(max(len(rd), len(ld))):
             if k < len(rd):
@@ -206,7 +221,7 @@ def step(op, slot, kk, buf, carry, bk=False):
     return ["s_waitcnt lgkmcnt(0)"] + interleave(mfmas(op, buf), ops, READ_SPAN if not carry else CARRY_SPAN)
 
 
-def step_last(op, slot, kind, bk=False):
+def step_last(op, slot, kind, bk=False, am=False):
     """The last step of a slice (fragments in buffer (STEPS - 1) % 2).  kind:
     "last" (no next slice), "noload" (next slice, nothing more to load),
     "load" (next slice, and load slice j+2)."""
@@ -214,7 +229,7 @@ def step_last(op, slot, kind, bk=False):
     if kind == "last":
         return ["s_waitcnt lgkmcnt(0)"] + mf
     out = ["s_waitcnt lgkmcnt(0)"] + mf[:BAR_AFTER] + [f"s_waitcnt vmcnt({npf()})", "s_barrier"]
-    rd = reads(1 - slot, 0, 0, bk)
+    rd = reads(1 - slot, 0, 0, bk, am)
     ops = []
     if kind == "load":
         ld = loads(slot)[:L3]
@@ -225,7 +240,7 @@ def step_last(op, slot, kind, bk=False):
             if k < len(ld):
                 ops.append(ld[k])
         if L3 == 16:
-            ops.append(ADVANCE)
+            ops.append(ADVANCE_AM if am else ADVANCE)
             ops += prefetch()
     else:
         ops = rd
@@ -233,7 +248,7 @@ def step_last(op, slot, kind, bk=False):
     return out
 
 
-def loop(op, bk=False):
+def loop(op, bk=False, am=False):
     L = []
     # private descriptor copies, advanced from slice 0 (the operands) to
     # slice 2, the first slice the loop loads
@@ -242,29 +257,30 @@ def loop(op, bk=False):
     # with every load of a slice in the last step the loop's first load is of
     # slice 2; otherwise the rest of slice 1 (whose first L3 loads the
     # prologue issued) comes first, in the first slice's earlier steps
-    L += ADVANCE + ADVANCE if L3 == 16 else ADVANCE
+    adv = ADVANCE_AM if am else ADVANCE
+    L += adv + adv if L3 == 16 else adv
     L += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(256)]
     L += ["s_nop 4"]
-    L += [x for r in reads(0, 0, 0, bk) for x in r]
+    L += [x for r in reads(0, 0, 0, bk, am) for x in r]
     for slot in (0, 1):
         L += [f"L_top{slot}_%=:"]
         if L3 < 16:
             L += ["s_cmp_lt_u32 %[n], 2", f"s_cbranch_scc1 L_noc{slot}_%="]
             for kk in range(STEPS - 1):
-                L += step(op, slot, kk, kk % 2, True, bk)
+                L += step(op, slot, kk, kk % 2, True, bk, am)
             L += [f"s_branch L_st3{slot}_%=", f"L_noc{slot}_%=:"]
         for kk in range(STEPS - 1):
-            L += step(op, slot, kk, kk % 2, False, bk)
+            L += step(op, slot, kk, kk % 2, False, bk, am)
         L += [f"L_st3{slot}_%=:"]
         L += ["s_cmp_eq_u32 %[n], 1", f"s_cbranch_scc1 L_last{slot}_%=",
               "s_cmp_eq_u32 %[n], 2", f"s_cbranch_scc1 L_nold{slot}_%="]
-        L += step_last(op, slot, "load", bk)
+        L += step_last(op, slot, "load", bk, am)
         L += ["s_sub_u32 %[n], %[n], 1", f"s_branch L_top{1 - slot}_%="]
         L += [f"L_nold{slot}_%=:"]
-        L += step_last(op, slot, "noload", bk)
+        L += step_last(op, slot, "noload", bk, am)
         L += ["s_sub_u32 %[n], %[n], 1", f"s_branch L_top{1 - slot}_%="]
         L += [f"L_last{slot}_%=:"]
-        L += step_last(op, slot, "last", bk)
+        L += step_last(op, slot, "last", bk, am)
         L += ["s_branch L_done_%="]
     # the accumulators are read with v_accvgpr_read after this statement:
     # more wait states after the last MFMA that writes them than any MFMA
@@ -298,6 +314,11 @@ def main():
     parts.append("// the same with B K-contiguous\n#define LL_SQ4_LOOP_BF16_BK \\\n" +
                  cstring(loop("v_mfma_f32_16x16x32_bf16", True)) + "\n")
     parts.append("#define LL_SQ4_LOOP_F16_BK \\\n" + cstring(loop("v_mfma_f32_16x16x32_f16", True)) + "\n")
+    for bk in (False, True):
+        suf = "_AM_BK" if bk else "_AM"
+        parts.append(f"// A M-contiguous{', B K-contiguous' if bk else ''}\n#define LL_SQ4_LOOP_BF16{suf} \\\n" +
+                     cstring(loop("v_mfma_f32_16x16x32_bf16", bk, True)) + "\n")
+        parts.append(f"#define LL_SQ4_LOOP_F16{suf} \\\n" + cstring(loop("v_mfma_f32_16x16x32_f16", bk, True)) + "\n")
     for n in range(64):
         parts.append(f"#define LL_SQ4_READ_ACC_{n} \\\n" + read_acc(n) + "\n")
     parts.append("// X(n) for every accumulator block n = 8 * row block + column block\n#define LL_SQ4_BLOCKS(X) " +

@@ -63,6 +63,8 @@ hipError_t launch_gemm_epi(int layout, int kind, int f16, int epi, const GemmKAr
 // B N-contiguous) only; epi as for launch_gemm_epi (0: plain).
 hipError_t launch_gemm_sq4(int layout, int f16, int epi, const GemmKArgs& args, int grid, hipStream_t stream);
 hipError_t launch_gemm_sq4_bk(int f16, int epi, const GemmKArgs& args, int grid, hipStream_t stream);
+hipError_t launch_gemm_sq4_am(int f16, int epi, const GemmKArgs& args, int grid, hipStream_t stream);
+hipError_t launch_gemm_sq4_am_bk(int f16, int epi, const GemmKArgs& args, int grid, hipStream_t stream);
 
 // Fused linear-compression kernel (lincomp_kernel.hpp).
 struct LincompKArgs;

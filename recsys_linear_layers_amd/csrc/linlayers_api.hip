@@ -334,16 +334,13 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     return (op.kmajor ? (rows - 1) * op.ld + d->K : (d->K - 1) * op.ld + rows) * 2;
   };
   // The hand-ordered kind loads whole 64-deep slices with no k mask.  With K
-  // not a multiple of 64 that is still exact when A is a packed copy (zero
-  // columns up to ldp, K rounded up to 64) and B is N-contiguous: the last
-  // slice's B rows past K lie beyond B's descriptor range and read as zeros,
-  // and they meet A's zero columns.  A read in place would meet them with
-  // its next row's values, and an Inf or NaN there would reach C.  A
-  // K-contiguous B (its variant with B tiles laid out like A's) read in
-  // place has the same problem, so there both operands are packed copies.
-  const bool sq4_k_ok = d->K % 64 == 0 || (p.a.pack && (!p.b.kmajor || p.b.pack));
-  const bool sq4_fits = p.a.kmajor && sq4_k_ok && span_bytes(p.a, M) < 0x7FFFFFF0ll &&
-                        span_bytes(p.b, N) < 0x7FFFFFF0ll;
+  // not a multiple of 64 that is still exact when every operand reads zeros
+  // past K: a packed copy (zero columns up to ldp, K rounded up to 64), or an
+  // M/N-contiguous operand, whose k-rows past K lie beyond its descriptor
+  // range.  A K-contiguous operand read in place would give its next row's
+  // values there, and an Inf or NaN among them would reach C.
+  const bool sq4_k_ok = d->K % 64 == 0 || ((!p.a.kmajor || p.a.pack) && (!p.b.kmajor || p.b.pack));
+  const bool sq4_fits = sq4_k_ok && span_bytes(p.a, M) < 0x7FFFFFF0ll && span_bytes(p.b, N) < 0x7FFFFFF0ll;
   if (free_choice && p.a.kmajor && (kind == KIND_WIDE_PC || kind == KIND_TALL_PC)) {
     const int64_t pb = passes(kind), pt = passes(KIND_T192_PC);
     const KindInfo& kb = kind_info(kind);
@@ -379,11 +376,13 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     if (pk > 0 && pt > 0 && pt * kt.bm * kt.bn <= pk * kk.bm * kk.bn) kind = KIND_TALL_PC;
   }
   // The hand-ordered 256x256 kind (four 128x128 waves, gemm_sq4.hpp) is
-  // ahead of every kind above wherever it applies: A K-contiguous, B
-  // N-contiguous or K-contiguous (C = X W^T, the usual layout of a linear
-  // layer's weight: a variant that lays B tiles out and reads them like A's),
-  // K a multiple of 64 or the operands packed, with or without a fused
-  // epilogue.  Per pass and tile area it runs ~1.3x as fast as the others,
+  // ahead of every kind above wherever it applies: A K-contiguous or
+  // M-contiguous (C = X^T Y, a layer's weight gradient), B N-contiguous or
+  // K-contiguous (C = X W^T, the usual layout of a linear layer's weight);
+  // one variant per layout, the M-contiguous A tiles laid out and read like
+  // an N-contiguous B's and the K-contiguous B tiles like a K-contiguous A's;
+  // K a multiple of 64 or the operands reading zeros past it; with or
+  // without a fused epilogue.  Per pass and tile area it runs ~1.3x as fast as the others,
   // so it takes over when its passes times tile area is at most 1.25x theirs
   // and neither choice would split K; a last round it splits along K (the
   // tail split below) counts as 1/s of a pass.  Measured against the kind
@@ -432,12 +431,12 @@ ll_status gemm_plan_create(gemm_plan** out, const gemm_desc* d) {
     if ((!p.a.kmajor && 64 % (kv.bm / 8) != 0) || (!p.b.kmajor && 64 % (kv.bn / 8) != 0))
       return fail(LL_ERR_UNSUPPORTED, "kernel %s needs K-contiguous operands for its %dx%d tile", kv.name, kv.bm,
                   kv.bn);
-    // The hand-ordered kind reads A K-contiguous and B either way (as given
-    // or packed) in whole 64-deep slices.
+    // The hand-ordered kind reads A and B either way (as given or packed) in
+    // whole 64-deep slices.
     if (kind == KIND_SQ4_HO && !sq4_fits)
       return fail(LL_ERR_UNSUPPORTED,
-                  "kernel %s needs A K-contiguous, K a multiple of 64 (or A packed, and B packed when "
-                  "K-contiguous) and operands below 2 GB",
+                  "kernel %s needs K a multiple of 64 (or every K-contiguous operand packed) and operands below "
+                  "2 GB",
                   kv.name);
   }
   p.kind = kind;

@@ -114,6 +114,33 @@ def test_random_case_hand_ordered_b_k_contiguous(i, monkeypatch):
         ll._plans.clear()
 
 
+N_SQ4_AM = 16
+
+
+@pytest.mark.parametrize("i", range(N_SQ4_AM))
+def test_random_case_hand_ordered_a_m_contiguous(i, monkeypatch):
+    """The hand-ordered kind's variants for an M-contiguous A (C = X^T Y)
+    forced on random cases: M a multiple of 8 (A read in place), B either way
+    as drawn, any K (a K-contiguous B is then packed when K is not a multiple
+    of 64); bias, activation and output type as drawn."""
+    import recsys_linear_layers_amd as ll
+    d = _draw(N_CASES + N_SQUARE + N_SQ4 + 2000 + i)
+    rng = np.random.default_rng(8500 + i)
+    d["M"] = 8 * int(rng.integers(1, 138))
+    d["N"] = int(rng.integers(1, 1100))
+    d["K"] = int(rng.integers(1, 700))
+    d["a_col"] = True
+    d["pad_a"] = 8 * int(rng.integers(0, 3))
+    d["flags"] = ll.LL_FLAG_PACK_B if (d["b_col"] and d["K"] % 64) else 0
+    ll._plans.clear()
+    monkeypatch.setenv("LL_GEMM_KIND", "KIND_SQ4_HO")
+    try:
+        _check(N_CASES + N_SQUARE + N_SQ4 + 2000 + i, d, want_kind="KIND_SQ4_HO", want="A:M-major")
+    finally:
+        monkeypatch.delenv("LL_GEMM_KIND", raising=False)
+        ll._plans.clear()
+
+
 N_SQ4_TAIL = 30
 
 

@@ -177,6 +177,97 @@ def test_k_contiguous_b_integer_exact():
     assert np.array_equal(g1[rows, cols], ref)
 
 
+@pytest.mark.parametrize("b_col", [False, True])
+def test_m_contiguous_a_selected_in_place(b_col):
+    """C = X^T Y (A M-contiguous, a layer's weight gradient): the hand-ordered
+    kind takes A in place, its tiles laid out and read like an N-contiguous
+    B's, B either way; also with K not a multiple of 64 when B is
+    N-contiguous (both operands then read zeros past K)."""
+    import recsys_linear_layers_amd as ll
+    lay = "A:M-major,B:K-major" if b_col else "A:M-major,B:N-major"
+    for M, N, K in [(4096, 4096, 4096), (16384, 8192, 8192), (8192, 2048, 8192)]:
+        d = _describe(M, N, K, a_col=True, b_col=b_col)
+        assert f"kernel={KIND} " in d and lay in d and "packA=0" in d and "packB=0" in d, d
+    d = _describe(4096, 4096, 4104, a_col=True, b_col=b_col)
+    assert (f"kernel={KIND} " in d) == (not b_col), d     # a K-contiguous B in place needs K % 64 == 0
+    d = _describe(4096, 4096, 4096, a_col=True, b_col=b_col, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
+    assert f"kernel={KIND} " not in d, d
+
+
+AM_SHAPES = [(256, 256, 64), (256, 256, 192), (1000, 1032, 2048), (8, 8, 64), (40, 24, 448), (1536, 1280, 512),
+             (264, 520, 200), (1000, 1032, 130)]
+
+
+def _am_case(M, N, K, seed, out, b_col, in_dtype="bf16", dist=("normal", 0.0, 1.0)):
+    c = synth.gemm_case(M, N, K, seed=seed, out_dtype=out, in_dtype=in_dtype, dist=dist, b_col_major=b_col)
+    c.A = synth.bf16_tensor(M * K, dist[0], dist[1], dist[2], seed=seed, tensor=5, fmt=in_dtype)
+    c.sam, c.sak = 1, M
+    return c
+
+
+@pytest.mark.parametrize("M,N,K", AM_SHAPES)
+@pytest.mark.parametrize("b_col", [False, True])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_shapes_a_m_contiguous(M, N, K, b_col, out, monkeypatch):
+    """The variants for an M-contiguous A forced on ragged M and N, one to many
+    slices, B either way; with K not a multiple of 64 the M-contiguous A reads
+    zeros past K in place, and a K-contiguous B is packed."""
+    import recsys_linear_layers_amd as ll
+    c = _am_case(M, N, K, M * 3 + N * 5 + K + b_col, out, b_col)
+    flags = ll.LL_FLAG_PACK_B if (b_col and K % 64) else 0   # packed N-contiguous beside an M-contiguous A
+    got, d = _run(c, monkeypatch, flags)
+    assert ("A:M-major,B:K-major" if b_col and not flags else "A:M-major,B:N-major") in d and "packA=0" in d, d
+    ref, S = oracle.gemm_case(c)
+    acceptance.assert_close(got, ref, S, out, f"A M-contiguous {M}x{N}x{K} {d}")
+
+
+@pytest.mark.parametrize("act", [None, "silu"])
+@pytest.mark.parametrize("out,in_dtype", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16")])
+def test_a_m_contiguous_epilogue_and_f16(act, out, in_dtype, monkeypatch):
+    """Bias + activation, fp16 operands and every C type with A M-contiguous,
+    304 x 1032 x 640."""
+    import torch
+    M, N, K = 304, 1032, 640
+    c = _am_case(M, N, K, 351, out, False, in_dtype=in_dtype)
+    A, B = gemm_operands(c)
+    bias = torch.from_numpy(np.random.default_rng(352).standard_normal(N).astype(np.float32)).cuda()
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out]
+    C = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    d = _run_into(A, B, C, monkeypatch, bias, act)
+    assert "A:M-major" in d, d
+    ref, S = oracle.gemm_case(c)
+    ref, S = oracle.epilogue(ref, S, bias.cpu().numpy(), act)
+    acceptance.assert_close(to_f64(C), ref, S, out, f"A M-contiguous {out} act={act} {d}", act=act)
+
+
+@pytest.mark.parametrize("b_col", [False, True])
+def test_m_contiguous_a_integer_exact(b_col):
+    """A M-contiguous in the hand-ordered kind (chosen by the plan) against the
+    producer/consumer kind on the same operands: integer inputs make both
+    exact, so the bits agree; sampled entries match the oracle.  4352 x 4160
+    x 4096: the K-split last round (tail=33x4) runs too."""
+    import torch
+    import recsys_linear_layers_amd as ll
+    c = _am_case(4352, 4160, 4096, 353 + b_col, "f32", b_col, dist=("int", -3, 3))
+    A, B = gemm_operands(c)
+    C1 = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
+    C2 = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
+    ll._plans.clear()
+    ll.gemm(A, B, out=C1)
+    ll.gemm(A, B, out=C2, flags=ll.LL_FLAG_PRODUCER_CONSUMER)
+    torch.cuda.synchronize()
+    d1 = ll.plan_for(A, B, C1).describe()
+    d2 = ll.plan_for(A, B, C2, ll.LL_FLAG_PRODUCER_CONSUMER).describe()
+    ll._plans.clear()
+    assert f"kernel={KIND} " in d1 and "A:M-major" in d1 and " tail=33x4" in d1, d1
+    assert f"kernel={KIND} " not in d2, d2
+    g1, g2 = to_f64(C1), to_f64(C2)
+    assert np.array_equal(g1, g2), (d1, d2)
+    rows, cols = sample_indices(c.M, c.N, 2048, 354, tile=256)
+    ref, _ = oracle.gemm_case_entries(c, rows, cols)
+    assert np.array_equal(g1[rows, cols], ref)
+
+
 BK_SHAPES = [(256, 256, 64), (256, 256, 192), (300, 520, 640), (1000, 1032, 2048), (513, 264, 320), (8, 8, 64),
              (40, 24, 448), (1536, 1280, 512)]
 
@@ -261,8 +352,8 @@ def test_selection_conditions():
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, c_t=ll.LL_F32)
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_GELU)
     assert f"kernel={KIND} " in _describe(4096, 4096, 4096, epilogue=ll.LL_EPI_BIAS | ll.LL_EPI_SILU)
-    # (a K-contiguous B: test_k_contiguous_b_selected_in_place)
-    for kw in (dict(a_col=True), dict(flags=ll.LL_FLAG_PRODUCER_CONSUMER), dict(flags=ll.LL_FLAG_COOPERATIVE)):
+    # (a K-contiguous B or an M-contiguous A: the tests of those variants)
+    for kw in (dict(flags=ll.LL_FLAG_PRODUCER_CONSUMER), dict(flags=ll.LL_FLAG_COOPERATIVE)):
         assert f"kernel={KIND} " not in _describe(4096, 4096, 4096, **kw), kw
     assert f"kernel={KIND} " not in _describe(4096, 4096, 4104)        # K % 64 != 0
     assert f"kernel={KIND} " not in _describe(2048, 4096, 8192)        # 128 tiles would split K

@@ -47,9 +47,9 @@ def test_committed_include_is_the_generators_output(tmp_path):
 PIECES = [("A", i) for i in range(8)] + [("B", i) for i in range(8)]
 
 
-def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
-    lines = g.loop(OP, bk)
-    nreads = g.READS_BK if bk else g.READS
+def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False, am=False, inc_a=128):
+    lines = g.loop(OP, bk, am)
+    nreads = (g.READS_BK if bk else g.READS) + (g.READS_AM if am else 0)
     labels = {ln[:-1]: k for k, ln in enumerate(lines) if ln.endswith(":")}
     issued = {}          # slice -> set of pieces
     pending, completed, visible = [], set(), set()   # pending: issue order, prefetches as ("PF", slice)
@@ -64,7 +64,7 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
     visible |= completed
     reads_issued = reads_done = released = 0
     barriers = mfmas = 0
-    a_off, b_adv, m0, scc, nreg = 0, 0, None, False, n
+    a_adv, b_adv, m0, scc, nreg = 0, 0, None, False, n
     nrec_a = nrec_b = None
     pc = 0
     while pc < len(lines):
@@ -79,12 +79,12 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
             if m.group(1) == "94":
                 nrec_b = ext_b
             continue
-        if ln == "s_add_u32 s88, s88, 128":
-            a_off += 128
+        if ln == ("s_add_u32 s88, s88, %[inca]" if am else "s_add_u32 s88, s88, 128"):
+            a_adv += 1
         elif ln == "s_add_u32 s92, s92, %[incb]":
             b_adv += 1
-        elif ln == "s_sub_u32 s90, s90, 128":
-            nrec_a = max(0, nrec_a - 128)
+        elif ln == ("s_sub_u32 s90, s90, %[inca]" if am else "s_sub_u32 s90, s90, 128"):
+            nrec_a = max(0, nrec_a - inc_a)
         elif ln == "s_sub_u32 s94, s94, %[incb]":
             nrec_b = max(0, nrec_b - inc_b)
         elif ln.startswith(("s_addc_u32", "s_cselect_b32", "s_nop", "v_accvgpr_write")):
@@ -98,7 +98,7 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
             assert m and m0 == "pf", ln
             which = m.group(1).upper()
             assert m.group(2) == ("88" if which == "A" else "92"), ln
-            s = a_off // 128 if which == "A" else b_adv
+            s = a_adv if which == "A" else b_adv
             # the descriptors point at the slice after the one whose loads were issued last
             assert all(s > t for t in issued), f"prefetch of slice {s} after its loads"
             pending.append(("PF", s))
@@ -108,8 +108,7 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
             assert m, ln
             which, i = m.group(1).upper(), int(m.group(2))
             assert m.group(3) == ("88" if which == "A" else "92"), ln
-            s = a_off // 128 if which == "A" else b_adv
-            assert a_off % 128 == 0
+            s = a_adv if which == "A" else b_adv
             assert 0 <= s < n, f"load of slice {s} with n = {n}"
             assert (which, i) not in issued.setdefault(s, set()), f"slice {s} {which}{i} loaded twice"
             want_m0 = (s % 2) * g.SLOT + (g.B_OFF if which == "B" else 0) + i * 4096
@@ -132,9 +131,10 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
         elif ln.startswith("ds_read"):
             grp = reads_issued // nreads
             s, kk = grp // g.STEPS, grp % g.STEPS
-            m = re.search(r"%\[f(a|b|bk)_(\d)_(\d)(?:_(\d))?\](?: offset:(\d+))?", ln)
+            m = re.search(r"%\[f(a|b|bk|at)_(\d)_(\d)(?:_(\d))?\](?: offset:(\d+))?", ln)
             assert m, ln
-            assert (m.group(1) == "b") == (not bk and not ln.startswith("ds_read_b128")), ln
+            assert ln.startswith("ds_read_b128") == (m.group(1) in ("a", "bk")), ln
+            assert m.group(1) in (("at",) if am else ("a",)) + (("bk",) if bk else ("b",)), ln
             slot = int(m.group(2))
             off = int(m.group(5) or 0)
             if m.group(1) in ("a", "bk"):
@@ -159,17 +159,17 @@ def emulate(g, n, inc_b=4096 * 64 * 2, ext_a=10 ** 9, ext_b=10 ** 9, bk=False):
         else:
             raise AssertionError(f"instruction the emulation does not know: {ln}")
         if ln.startswith("buffer_load_dwordx4"):
-            assert nrec_a == max(0, ext_a - a_off) and nrec_b == max(0, ext_b - b_adv * inc_b)
-    assert nrec_a == max(0, ext_a - a_off) and nrec_b == max(0, ext_b - b_adv * inc_b)
+            assert nrec_a == max(0, ext_a - a_adv * inc_a) and nrec_b == max(0, ext_b - b_adv * inc_b)
+    assert nrec_a == max(0, ext_a - a_adv * inc_a) and nrec_b == max(0, ext_b - b_adv * inc_b)
     for s in range(n):
         assert issued.get(s) == set(PIECES), f"slice {s}: {sorted(set(PIECES) - issued.get(s, set()))} never loaded"
     assert not [x for x in pending if x[0] != "PF"], "loads still outstanding at the end"
     # each descriptor advance inside the loop (not the one or two before it) is followed by the prefetches
-    in_loop = a_off // 128 - (2 if g.L3 == 16 else 1)
+    in_loop = a_adv - (2 if g.L3 == 16 else 1)
     assert prefetches == g.npf() * in_loop, (prefetches, in_loop)
     assert reads_issued == nreads * g.STEPS * n and mfmas == g.MFMAS * g.STEPS * n and barriers == n - 1
     # the descriptors end at most one slice past the last loaded one
-    assert a_off // 128 == b_adv and b_adv in (n, n + 1) or n <= 2
+    assert a_adv == b_adv and b_adv in (n, n + 1) or n <= 2
 
 
 SPLITS = [dict(L3=16)] + [dict(L3=l3) for l3 in (14, 12, 10, 8, 6, 4, 2)] + \
@@ -193,17 +193,29 @@ def test_emulated_loop_b_k_contiguous(params, n):
     emulate(_gen(**params), n, inc_b=128, bk=True)
 
 
+@pytest.mark.parametrize("params", [dict(), dict(L3=16), dict(L3=4), dict(L3=10, PREFETCH=3)],
+                         ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()) or "committed")
+@pytest.mark.parametrize("bk", [False, True])
+@pytest.mark.parametrize("n", range(1, 10))
+def test_emulated_loop_a_m_contiguous(params, bk, n):
+    """The variants for an M-contiguous A (A fragments read like an
+    N-contiguous B's, A moving 64 k-rows per slice), with B either way."""
+    emulate(_gen(**params), n, inc_b=128 if bk else 4096 * 64 * 2, bk=bk, am=True, inc_a=3000 * 64 * 2)
+
+
 def test_committed_parameters_emulate():
     g = _gen()
     for n in range(1, 12):
         emulate(g, n)
         emulate(g, n, inc_b=128, bk=True)
+        emulate(g, n, am=True, inc_a=3000 * 64 * 2)
+        emulate(g, n, inc_b=128, bk=True, am=True, inc_a=3000 * 64 * 2)
 
 
 def test_emulation_catches_a_double_advance():
     """The emulation rejects a stream whose descriptors move twice in a slice."""
     g = _gen(L3=8)
     real = g.carried
-    g.carried = lambda slot, kk: real(slot, kk) + ([g.ADVANCE] if kk == 0 else [])
+    g.carried = lambda slot, kk, am=False: real(slot, kk, am) + ([g.ADVANCE] if kk == 0 else [])
     with pytest.raises(AssertionError):
         emulate(g, 6)
