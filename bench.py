@@ -46,12 +46,13 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 GEMM_NAMES = {"gemm_4096", "ffn_up", "ffn_down", "edge", "skinny_splitk", "gemm_256", "gemm_4096_f16", "gemm_3000",
-              "gemm_4096_nt"}
+              "gemm_4096_nt", "gemm_4096_tn"}
 # workloads also timed with the kind the plan would choose without its tile
 # rules (the 192x256 tile-count rule on gemm_3000, the 256x256 rule on the
 # others)
 TILE_RULE_NAMES = {"gemm_3000": "KIND_WIDE_PC", "gemm_4096": "KIND_WIDE_PC", "ffn_up": "KIND_WIDE_PC",
-                   "gemm_4096_f16": "KIND_WIDE_PC", "gemm_4096_nt": "KIND_WIDE_PC"}
+                   "gemm_4096_f16": "KIND_WIDE_PC", "gemm_4096_nt": "KIND_WIDE_PC",
+                   "gemm_4096_tn": "KIND_WIDE_PC"}
 LINCOMP_NAMES = {"lincomp_256x128"}
 # The same workload given in the layer's original form: every candidate's
 # stacked input [user rows; item rows] materialised (no reuse possible).
@@ -529,7 +530,7 @@ def hbm_probe(mib: int, steps: int, warmup: int) -> dict:
 # the configurations whose oracle is timed too are listed in CPU_LEGS.
 ALSO_ORDER = ["ffn_up", "ffn_down", "ffn_up_bias_gelu", "lincomp_256x128", "lincomp_256x128_stacked",
               "lincomp_256x128_bias_gelu", "lincomp_ragged_256", "edge", "skinny_splitk", "gemm_256", "gemm_3000",
-              "gemm_4096_f16", "gemm_4096_nt", "gemm_4096"]
+              "gemm_4096_f16", "gemm_4096_nt", "gemm_4096_tn", "gemm_4096"]
 # workload -> strip rows (None: the whole problem)
 CPU_LEGS = {"gemm_256": None, "ffn_up": 64, "ffn_down": 64, "edge": None, "skinny_splitk": None}
 

@@ -113,13 +113,20 @@ class GemmCase:
         return 2.0 * self.M * self.N * self.K
 
 
-def gemm_case(M, N, K, *, dist=("uniform", -1.0, 1.0), b_dist=None, seed=0, sub=0,
+def gemm_case(M, N, K, *, dist=("uniform", -1.0, 1.0), b_dist=None, seed=0, sub=0, a_col_major=False,
               b_col_major=False, lda=None, ldb=None, out_dtype="f32", in_dtype="bf16", name="gemm") -> GemmCase:
-    """Row-major A [M][lda>=K]; B row-major [K][ldb>=N] or column-major [N][ldb>=K];
-    A and B in ``in_dtype`` ("bf16" or "f16")."""
+    """A row-major [M][lda>=K] or column-major [K][lda>=M]; B row-major
+    [K][ldb>=N] or column-major [N][ldb>=K]; A and B in ``in_dtype`` ("bf16"
+    or "f16")."""
     b_dist = b_dist or dist
-    lda = K if lda is None else lda
-    A = bf16_tensor(M * lda, *dist, seed=seed, sub=sub, tensor=0, fmt=in_dtype)
+    if a_col_major:
+        lda = M if lda is None else lda
+        A = bf16_tensor(K * lda, *dist, seed=seed, sub=sub, tensor=0, fmt=in_dtype)
+        sam, sak = 1, lda
+    else:
+        lda = K if lda is None else lda
+        A = bf16_tensor(M * lda, *dist, seed=seed, sub=sub, tensor=0, fmt=in_dtype)
+        sam, sak = lda, 1
     if b_col_major:
         ldb = K if ldb is None else ldb
         B = bf16_tensor(N * ldb, *b_dist, seed=seed, sub=sub, tensor=1, fmt=in_dtype)
@@ -128,7 +135,7 @@ def gemm_case(M, N, K, *, dist=("uniform", -1.0, 1.0), b_dist=None, seed=0, sub=
         ldb = N if ldb is None else ldb
         B = bf16_tensor(K * ldb, *b_dist, seed=seed, sub=sub, tensor=1, fmt=in_dtype)
         sbk, sbn = ldb, 1
-    return GemmCase(name, M, N, K, A, lda, 1, B, sbk, sbn, out_dtype, in_dtype)
+    return GemmCase(name, M, N, K, A, sam, sak, B, sbk, sbn, out_dtype, in_dtype)
 
 
 GEMM_WORKLOADS = {
@@ -151,6 +158,8 @@ GEMM_WORKLOADS = {
                                              in_dtype="f16")),
     # C = X W^T with W stored [N][K]: B K-contiguous (a linear layer's usual weight layout)
     "gemm_4096_nt": (4096, 4096, 4096, dict(dist=("normal", 0.0, 1.0), seed=2, out_dtype="bf16", b_col_major=True)),
+    # C = X^T Y: A M-contiguous (a layer's weight gradient dW = dY^T X)
+    "gemm_4096_tn": (4096, 4096, 4096, dict(dist=("normal", 0.0, 1.0), seed=2, out_dtype="bf16", a_col_major=True)),
 }
 
 

@@ -347,3 +347,8 @@ def test_gemm_4096_f16_sampled():
 def test_gemm_4096_nt_sampled():
     # B K-contiguous (C = X W^T): the hand-ordered kind's variant for such a B, in place
     _sampled_check(synth.gemm_workload("gemm_4096_nt"))
+
+
+def test_gemm_4096_tn_sampled():
+    # A M-contiguous (C = X^T Y): the hand-ordered kind's variant for such an A, in place
+    _sampled_check(synth.gemm_workload("gemm_4096_tn"))
