@@ -195,6 +195,26 @@ def test_ffn_shapes(name):
     _sampled_check(synth.gemm_workload(name))
 
 
+@pytest.mark.parametrize("name,layout", [("ffn_up", "b_col_major"), ("ffn_down", "a_col_major")])
+def test_ffn_shapes_other_layouts(name, layout):
+    """The FFN shapes with B K-contiguous (the forward X W^T; ffn_up also
+    prefetches its wide B) and with A M-contiguous (a weight gradient's
+    layout): the hand-ordered kind's variants with the round barrier, one
+    entry in every tile, random entries and row strips against the oracle."""
+    import torch
+    ll = _ll()
+    M, N, K, kw = synth.GEMM_WORKLOADS[name]
+    case = synth.gemm_case(M, N, K, name=f"{name}_{layout}", **dict(kw, **{layout: True}))
+    _sampled_check(case, n=2048, strip_rows=16)
+    A, B = gemm_operands(case)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    d = ll.plan_for(A, B, C).describe()
+    want = "A:K-major,B:K-major" if layout == "b_col_major" else "A:M-major,B:N-major"
+    assert "kernel=KIND_SQ4_HO " in d and want in d and "round_sync=1" in d and "packA=0 packB=0" in d, d
+    if name == "ffn_up":
+        assert "prefetch_b=1" in d, d
+
+
 def test_descriptor_rebase_past_1gib():
     """A row-major B whose k-range per work item spans more than 1 GiB (the
     loader re-opens its buffer descriptor at the current slice once the
