@@ -409,7 +409,8 @@ def vendor_context(steps: int, warmup: int):
     out = []
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0)
-    for name in ["gemm_4096", "ffn_up", "ffn_down", "gemm_3000", "gemm_4096_f16", "skinny_splitk"]:
+    for name in ["gemm_4096", "ffn_up", "ffn_down", "gemm_3000", "gemm_4096_f16", "skinny_splitk", "gemm_4096_nt",
+                 "gemm_4096_tn"]:
         M, N, K, kw = synth.GEMM_WORKLOADS[name]
         in_t = {"bf16": torch.bfloat16, "f16": torch.float16}[kw.get("in_dtype", "bf16")]
 
@@ -417,8 +418,10 @@ def vendor_context(steps: int, warmup: int):
             if dist[0] == "uniform":
                 return (torch.rand(rows, cols, device="cuda", generator=gen) * (dist[2] - dist[1]) + dist[1]).to(in_t)
             return (torch.randn(rows, cols, device="cuda", generator=gen) * dist[2] + dist[1]).to(in_t)
-        A = draw(M, K, kw["dist"])
-        B = draw(K, N, kw.get("b_dist") or kw["dist"])
+        # column-major operands as transposed views (2-D products only)
+        A = draw(K, M, kw["dist"]).t() if kw.get("a_col_major") else draw(M, K, kw["dist"])
+        bd = kw.get("b_dist") or kw["dist"]
+        B = draw(N, K, bd).t() if kw.get("b_col_major") else draw(K, N, bd)
         # torch.matmul writes C in its inputs' type: an fp32-output workload is
         # timed with a bf16/fp16 C (noted in the result)
         C = torch.empty(M, N, device="cuda", dtype=in_t)
